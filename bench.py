@@ -1,0 +1,217 @@
+"""Benchmark of the DP-SGD per-sample clipping hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of a layer set: the
+per-example norms of every layer (dp_ghost_norm), the clip factors
+(dp_clip_factors) and the clipped, noised mean gradient of every layer
+(dp_clipped_sum_noise). Inputs are seeded synthetic tensors already resident
+in HBM; several copies are rotated so that consecutive steps do not hit the
+256 MB Infinity Cache. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "clipped examples/sec (norm+clip+noisy sum) per layer set; % of MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+CACHE_BYTES = 256 << 20
+
+
+def _algorithmic(wl, T, d, p, kind):
+    """Algorithmic flops and bytes of one call on one layer (no re-reads, no
+    intermediate buffers). ghost: unique Gram entries B*T(T+1)(d+p) + 2BT^2;
+    explicit: 2BTdp + 2Bdp; T = 1: 2B(d+p); contraction: 2BTdp."""
+    B = wl.B
+    eb = 2 if wl.dtype == "bf16" else 4
+    hb = 1 if wl.has_bias else 0
+    inp = B * T * (d + p) * eb
+    if kind == "norm":
+        if T == 1:
+            return 2.0 * B * (d + p), inp + 4 * B
+        if p * d < T * T:
+            return 2.0 * B * T * d * p + 2.0 * B * d * p, inp + 4 * B
+        return float(B) * T * (T + 1) * (d + p) + 2.0 * B * T * T, inp + 4 * B
+    flops = 2.0 * B * T * (d + hb) * p
+    return flops, inp + 4 * (d + hb) * p + 4 * B
+
+
+def run_gpu(wl, steps, warmup):
+    import torch
+    import sample_gradient_clipping_layer_amd as dpc
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    shapes = W.layer_list(wl)
+    B = wl.B
+    set_bytes = sum(B * T * (d + p) * (2 if wl.dtype == "bf16" else 4) for (T, d, p) in shapes)
+    n_sets = max(1, min(4, math.ceil(2 * CACHE_BYTES / set_bytes) + 1)) if set_bytes < 4 * CACHE_BYTES else 1
+
+    def up(x):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    sets = []
+    for s in range(n_sets):
+        layers = []
+        for l in range(len(shapes)):
+            A, G = W.make_layer(wl, l, step=s)
+            layers.append((up(A), up(G)))
+        sets.append(layers)
+    dt = dpc.DP_BF16 if wl.dtype == "bf16" else dpc.DP_F32
+    ws = []
+    for (T, d, p) in shapes:
+        nbytes = dpc.dp_workspace_bytes(dt, B, T, d, p)
+        ws.append(torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev))
+    sq = torch.empty(B, dtype=torch.float32, device=dev)
+    c = torch.empty(B, dtype=torch.float32, device=dev)
+    outs = [torch.empty(d, p, dtype=torch.float32, device=dev) for (T, d, p) in shapes]
+    bouts = [torch.empty(p, dtype=torch.float32, device=dev) if wl.has_bias else None for (T, d, p) in shapes]
+    stream = torch.cuda.current_stream()
+
+    # per-call event pairs (calls: norm per layer, clip, sum per layer)
+    ncalls = 2 * len(shapes) + 1
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ncalls)]
+          for _ in range(steps)]
+
+    def step(k, timed):
+        layers = sets[k % n_sets]
+        e = ev[k] if timed else None
+        j = 0
+        for l, (A, G) in enumerate(layers):
+            if e: e[j][0].record(stream)
+            dpc.dp_ghost_norm(A, G, sq, has_bias=wl.has_bias, accumulate=l > 0, workspace=ws[l])
+            if e: e[j][1].record(stream)
+            j += 1
+        if e: e[j][0].record(stream)
+        dpc.dp_clip_factors(sq, wl.C, c)
+        if e: e[j][1].record(stream)
+        j += 1
+        for l, (A, G) in enumerate(layers):
+            if e: e[j][0].record(stream)
+            dpc.dp_clipped_sum_noise(A, G, c, wl.C, wl.sigma, float(B), wl.seed, l, k, outs[l], bouts[l],
+                                     workspace=ws[l])
+            if e: e[j][1].record(stream)
+            j += 1
+
+    for k in range(warmup):
+        step(k, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(k, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = np.array([[a.elapsed_time(b) for (a, b) in ev[k]] for k in range(steps)])  # [steps, ncalls]
+    for o in outs:
+        assert torch.isfinite(o).all().item(), "non-finite output"
+    return wall, call_ms, shapes, n_sets
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The fp64 oracle as it stands, on the same workload: whole steps (all
+    layers: norms, clip factors, clipped sum, noise) on the host cores."""
+    from threadpoolctl import threadpool_info
+    from oracle import drivers
+
+    layers = []
+    for l in range(wl.n_layers):
+        A, G = W.make_layer(wl, l, step=0)
+        layers.append((W.as_f64(A, wl.dtype), W.as_f64(G, wl.dtype)))
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        drivers.global_clip_step(layers, wl.C, wl.sigma, wl.seed, step=n, has_bias=wl.has_bias)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    return {"value": wl.B * n / dt, "unit": "examples/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} whole step(s) of {wl.name} (B={wl.B}, all {wl.n_layers} layers, fp64 numpy, "
+                      f"materialised per-example gradients), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gpt-block-t128", choices=W.WORKLOAD_ORDER)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="print per-call times to stderr")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the clipping path on a single MI355X "
+              "(the multi-GPU design is described, not built). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    wl = W.WORKLOADS[a.workload]
+    wall, call_ms, shapes, n_sets = run_gpu(wl, a.steps, a.warmup)
+    L = len(shapes)
+    ms_per_step = 1e3 * wall / a.steps
+    value = wl.B * a.steps / wall
+
+    # dominant call by total event time
+    mean_ms = call_ms.mean(axis=0)
+    kinds = ["norm"] * L + ["clip"] + ["sum"] * L
+    by_kind = {}
+    for j, kd in enumerate(kinds):
+        by_kind[kd] = by_kind.get(kd, 0.0) + mean_ms[j]
+    dom = max(("norm", "sum"), key=lambda k: by_kind[k])
+    flops = byts = t_ms = 0.0
+    for j, kd in enumerate(kinds):
+        if kd != dom:
+            continue
+        l = j if kd == "norm" else j - L - 1
+        T, d, p = shapes[l]
+        f, b = _algorithmic(wl, T, d, p, kd)
+        flops += f
+        byts += b
+        t_ms += mean_ms[j]
+    if dom == "sum" or (wl.dtype == "bf16" and flops / byts > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3):
+        peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+        achieved = flops / (t_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None}
+    else:
+        achieved = byts / (t_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    roof["kernel"] = "dp_ghost_norm" if dom == "norm" else "dp_clipped_sum_noise"
+    roof["per_step_ms"] = round(t_ms, 4)
+    if a.breakdown:
+        names = [f"norm[{l}]" for l in range(L)] + ["clip"] + [f"sum[{l}]" for l in range(L)]
+        for nm, m in zip(names, mean_ms):
+            print(f"{nm:10s} {m * 1e3:9.2f} us", file=sys.stderr)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "examples/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "global_batch": wl.B, "seq_len": shapes[0][0],
+                   "layers": [list(s) for s in shapes] if L <= 8 else f"{L} layers",
+                   "parallelism": "single-gpu", "input_sets_rotated": n_sets},
+        "roofline": roof,
+        "events_ms_per_step": round(float(call_ms.sum(axis=1).mean()), 4),
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

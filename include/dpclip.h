@@ -1,0 +1,180 @@
+/*
+ * dpclip.h -- C ABI of libdpclip.so: the DP-SGD per-sample gradient clipping
+ * hot path on AMD Instinct MI355X (gfx950).
+ *
+ * Conventions (all entry points):
+ *  - Sizes are int64_t and must be >= 1. Tensors are device pointers to
+ *    contiguous row-major arrays, last dimension fastest. A and G share one
+ *    number type (dp_dtype). A, G and the workspace must be 16-byte aligned;
+ *    float vectors 4-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream). All device work is
+ *    enqueued asynchronously on it; nothing is synchronised. The caller keeps
+ *    every buffer alive until the stream has passed the call.
+ *  - The caller owns every buffer, including the workspace. The library keeps
+ *    no pointer after returning and has no global mutable state; calls are
+ *    re-entrant. Identical inputs give bitwise-identical outputs (fixed-order
+ *    reductions, no floating-point atomics).
+ *  - Every argument is validated before any HIP call. A failed validation
+ *    returns its code and touches nothing. HIP launch failures return
+ *    DP_ERR_HIP; no usable device returns DP_ERR_NO_DEVICE.
+ *
+ * Page keys used in the comments:
+ *  FPC  "Scaling up Differentially Private Deep Learning with Fast Per-Example
+ *       Gradient Clipping"
+ *  TTP  "Three Tools for Practical Differential Privacy"
+ *  SEDP "Scalable and Efficient Training of Large Convolutional Neural Networks
+ *       with Differential Privacy"
+ *  DDP  "Privacy-Preserving Deep Learning: A Deep Dive into DP-SGD"
+ */
+#ifndef DPCLIP_H
+#define DPCLIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DP_ABI_VERSION 1
+
+typedef int32_t dp_status;
+#define DP_OK 0
+#define DP_ERR_NULL 1      /* a required pointer is NULL */
+#define DP_ERR_SHAPE 2     /* a size is < 1 or a size product overflows the supported range */
+#define DP_ERR_DTYPE 3     /* unknown dp_dtype */
+#define DP_ERR_VALUE 4     /* a scalar is out of range (C, sigma, denom, alpha, beta, mode, kappa, ...) */
+#define DP_ERR_WORKSPACE 5 /* workspace smaller than dp_workspace_bytes() */
+#define DP_ERR_HIP 6       /* a HIP call or kernel launch failed */
+#define DP_ERR_NO_DEVICE 7 /* no gfx950 device is current */
+#define DP_ERR_ALIGN 8     /* a pointer is not aligned as required */
+
+typedef int32_t dp_dtype;
+#define DP_F32 0
+#define DP_BF16 1
+
+typedef int32_t dp_mode;
+#define DP_MODE_MIXED 0    /* layerwise decision (SEDP Sec. 4, rule (4.1)) */
+#define DP_MODE_GHOST 1    /* always the ghost norm (SEDP 'ghost' mode, App. E) */
+#define DP_MODE_EXPLICIT 2 /* always per-sample instantiation */
+
+#define DP_PATH_GHOST 1    /* <A_i A_i^T, G_i G_i^T> on per-sample Gram tiles */
+#define DP_PATH_EXPLICIT 2 /* ||A_i^T G_i||_F^2 from per-sample gradient tiles */
+#define DP_PATH_T1 3       /* T == 1 closed form ||a_i||^2 ||g_i||^2 */
+
+/*
+ * Per-example squared gradient norm of ONE layer (weight, plus bias when
+ * has_bias != 0), without materialising per-example gradients in memory.
+ *
+ * Defines: SEDP eq. (2.4)/(2.6) per-sample gradient g_i = A_i^T G_i,
+ * eq. (2.7) ghost norm ||g_i||_F^2 = <A_i A_i^T, G_i G_i^T>, Sec. 4 layerwise
+ * decision; FPC eq. (6) (outer product for T = 1) and the bias gradient
+ * b_i = sum_t G_i[t, :].
+ *
+ *  A        [B, T, d] layer inputs (for a conv: the unfolded U(a_i), d = C_in*kH*kW).
+ *  G        [B, T, p] output gradients dL/ds_i (for a conv: F^-1, spatial flattened).
+ *  dtype    DP_F32 or DP_BF16 (both tensors); accumulation is fp32.
+ *  mode     DP_MODE_*; kappa >= 1: MIXED takes the explicit path when
+ *           p*d < kappa*T*T, else ghost (tie -> ghost); T == 1 takes the
+ *           closed form unless mode is EXPLICIT.
+ *  workspace, ws_bytes  device scratch of at least dp_workspace_bytes(...)
+ *           bytes (may be NULL when that is 0). Its contents on entry are
+ *           ignored and on return undefined.
+ *  sqnorm   [B] fp32 device: overwritten (accumulate == 0) or incremented
+ *           (accumulate != 0) by the layer's squared norms, so several layers
+ *           can be summed in call order into one global norm.
+ *  path_out host int (may be NULL): receives DP_PATH_* actually taken.
+ */
+dp_status dp_ghost_norm(void* stream, const void* A, const void* G, dp_dtype dtype,
+                        int64_t B, int64_t T, int64_t d, int64_t p, int32_t has_bias,
+                        dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes,
+                        float* sqnorm, int32_t accumulate, int32_t* path_out);
+
+/*
+ * Norms and clip factors from squared norms.
+ *
+ * Defines: FPC clip_c(z) = z if ||z|| <= c else c*z/||z||; SEDP App. C
+ * C_i = min(R/||g_i||, 1); DDP g/max(1, ||g||/C).
+ *
+ *  sqnorm  [B] fp32 device (e.g. the sum over layers from dp_ghost_norm).
+ *  C       clipping bound, finite and > 0 (host value).
+ *  c       [B] fp32 device out: c_i = 1 when norm_i <= C, else C/norm_i.
+ *  norm    [B] fp32 device out, may be NULL: norm_i = sqrt(sqnorm_i), with
+ *          negative round-off clamped to 0. NaN propagates to norm_i and c_i;
+ *          an infinite norm gives c_i = 0.
+ */
+dp_status dp_clip_factors(void* stream, const float* sqnorm, int64_t B, float C,
+                          float* c, float* norm);
+
+/*
+ * Clipped, noised mean gradient of ONE layer.
+ *
+ * Defines: FPC the clipped sum with Gaussian noise added before the update
+ * (re-weighted loss, Gaussian mechanism); SEDP eq. (2.1) and Sec. 3.2
+ * (weighted gradient sum_i C_i g_i); DDP noisy aggregation.
+ *
+ *   out[m][n]   = (sum_b c[b] * sum_t A[b,t,m] G[b,t,n] + (sigma*C) * z_w[m][n]) / denom
+ *   bias_out[n] = (sum_b c[b] * sum_t G[b,t,n]          + (sigma*C) * z_b[n])    / denom
+ *
+ *  A, G, dtype, B, T, d, p  as in dp_ghost_norm.
+ *  c        [B] fp32 device clip factors (any finite values).
+ *  C, sigma bound and noise multiplier (C > 0, sigma >= 0, finite).
+ *  denom    divisor (> 0, finite); B for the plain mean.
+ *  seed, layer_id, step  select the noise: Philox4x32-10 + Box-Muller with
+ *           key (seed lo32, seed hi32), four normals per counter block.
+ *           z_w[m][n] is lane m%4 of the block at counter
+ *           ((m/4)*p + n, 2*layer_id, step, 0) (4 consecutive rows of one
+ *           column share a block); z_b[n] is lane n%4 of the block at
+ *           (n/4, 2*layer_id+1, step, 0). ceil(d/4)*p must be < 2^32.
+ *  workspace, ws_bytes  as in dp_ghost_norm.
+ *  out      [d, p] fp32 device (= A^T G layout, the transpose of a torch
+ *           weight.grad).
+ *  bias_out [p] fp32 device, or NULL for a layer without bias.
+ */
+dp_status dp_clipped_sum_noise(void* stream, const void* A, const void* G, dp_dtype dtype,
+                               int64_t B, int64_t T, int64_t d, int64_t p,
+                               const float* c, float C, float sigma, float denom,
+                               uint64_t seed, uint32_t layer_id, uint32_t step,
+                               void* workspace, size_t ws_bytes,
+                               float* out, float* bias_out);
+
+/*
+ * One update of the adaptive per-layer clipping bound of TTP:
+ *
+ *   C_l2   = init ? mean_b(norm[b]) : beta * C_prev
+ *   C_next = alpha / B * ( sum_b min(norm[b], C_l2) + sigma_l2 * C_l2 * z )
+ *
+ * where min(n, C_l2) = n / max(1, n / C_l2) is TTP's clip(||y||) and z is the
+ * normal of counter (0, 2*layer_id, step, 1) under key (seed lo32, seed hi32),
+ * lane 0. By convention `step` is the index t of the bound C_t being produced.
+ *
+ *  norm     [B] fp32 device per-example norms of the layer (previous step).
+ *  C_prev   previous bound (host); must be finite and > 0 unless init != 0.
+ *  alpha, beta > 0, sigma_l2 >= 0, finite.
+ *  C_next   fp32 device scalar out; C_l2_out fp32 device scalar out (may be NULL).
+ */
+dp_status dp_adaptive_threshold(void* stream, const float* norm, int64_t B, float C_prev,
+                                float alpha, float beta, float sigma_l2, int32_t init,
+                                uint64_t seed, uint32_t layer_id, uint32_t step,
+                                float* C_next, float* C_l2_out);
+
+/* Workspace bytes that dp_ghost_norm and dp_clipped_sum_noise need for this
+ * layer shape (the larger of the two). Returns 0 for invalid arguments. */
+size_t dp_workspace_bytes(dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64_t p,
+                          dp_mode mode, int32_t kappa);
+
+/* The DP_PATH_* that dp_ghost_norm takes for this shape, or -1 for invalid
+ * arguments. Pure host function. */
+int32_t dp_choose_path(int64_t T, int64_t d, int64_t p, dp_mode mode, int32_t kappa);
+
+/* Static string naming a status code. */
+const char* dp_status_string(dp_status status);
+
+/* DP_ABI_VERSION of the loaded library. */
+int32_t dp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DPCLIP_H */

@@ -180,3 +180,19 @@ def adaptive_threshold(norms: np.ndarray, C_prev: float, alpha: float, beta: flo
     s = float(np.sum(adaptive_clip_norm(norms, C_l2)))
     C_t = float(alpha) / B * (s + float(sigma_l2) * C_l2 * float(z))
     return C_l2, C_t
+
+
+def clipped_sum_entries(A: np.ndarray, G: np.ndarray, c: np.ndarray, rows, cols) -> np.ndarray:
+    """Selected entries S[m, n] of the clipped sum, each from its definition
+    sum_i c_i (A_i^T G_i)[m, n] = sum_i c_i sum_t A_i[t, m] G_i[t, n]
+    ([FPC] re-weighted sum; [SEDP] eq. (2.1)). For full-size checks where the
+    whole [d, p] sum is too large to materialise per example."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    c = np.asarray(c, dtype=np.float64)
+    out = np.zeros(rows.shape[0], dtype=np.float64)
+    for k in range(rows.shape[0]):
+        g_mn = np.sum(np.asarray(A[:, :, rows[k]], dtype=np.float64) * np.asarray(G[:, :, cols[k]], dtype=np.float64),
+                      axis=1)  # per-example gradient entry [B]
+        out[k] = float(np.dot(c, g_mn))
+    return out

@@ -11,9 +11,9 @@ its own norms, factors and bound, and the adaptive bound is updated after the
 step from that step's norms.
 
 Inputs are lists of (A, G) fp64 arrays (exact input values). Noise streams:
-weight noise of layer l at step t is normals(d*p, seed, l, 0, t) laid out
-row-major [d, p]; bias noise is normals(p, seed, l, 1, t); the noise of the
-adaptive bound C_t of layer l is threshold_normal(seed, l, t).
+weight noise of layer l at step t is weight_noise(d, p, seed, l, t); bias
+noise is normals(p, seed, l, 1, t); the noise of the adaptive bound C_t of
+layer l is threshold_normal(seed, l, t).
 """
 from __future__ import annotations
 
@@ -36,7 +36,7 @@ def global_clip_step(layers, C, sigma, seed, step=0, has_bias=False, denom=None,
     for lid, (A, G) in zip(layer_ids, layers):
         d, p = A.shape[2], G.shape[2]
         S, Sb = D.clipped_sum(A, G, c, has_bias)
-        z = N.normals(d * p, seed, lid, 0, step).reshape(d, p)
+        z = N.weight_noise(d, p, seed, lid, step)
         outs.append(D.noised_mean(S, z, C, sigma, denom))
         sums.append(S)
         if has_bias:
@@ -74,7 +74,7 @@ def adaptive_step(layers, C_t, sigma, alpha, beta, sigma_l2, seed, step, has_bia
         norms = np.sqrt(D.layer_sqnorms(A, G, has_bias))
         c = D.clip_factors(norms, C_t[lid])
         S, Sb = D.clipped_sum(A, G, c, has_bias)
-        z = N.normals(d * p, seed, lid, 0, step).reshape(d, p)
+        z = N.weight_noise(d, p, seed, lid, step)
         res["outs"].append(D.noised_mean(S, z, C_t[lid], sigma, denom))
         res["sums"].append(S)
         if has_bias:

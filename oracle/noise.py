@@ -14,10 +14,13 @@ key is bumped by the Weyl constants W0 = 0x9E3779B9, W1 = 0xBB67AE85 between
 rounds.
 
 Stream layout: key = (seed mod 2^32, seed div 2^32). Element e of a flat
-output of n values belongs to group j = e // 4 and takes lane e % 4 of the
-block Philox(counter = (j, 2*layer + which, step, tag), key); which = 0 for
-weight noise, 1 for bias noise; tag = 0 for gradient noise, 1 for the noise
-of the adaptive threshold (element 0 of group 0).
+stream belongs to group j = e // 4 and takes lane e % 4 of the block
+Philox(counter = (j, 2*layer + which, step, tag), key); which = 0 for weight
+noise, 1 for bias noise; tag = 0 for gradient noise, 1 for the noise of the
+adaptive threshold (element 0 of group 0). The weight noise of a [d, p]
+output groups 4 consecutive rows of one column: element (m, n) takes lane
+m % 4 of group (m // 4) * p + n (weight_noise); the bias noise of a [p]
+output is the flat stream (element n: lane n % 4 of group n // 4).
 
 Normals: one block (x0, x1, x2, x3) gives four normals by Box-Muller on the
 pairs (x0, x1) and (x2, x3):
@@ -174,3 +177,35 @@ def normals(n: int, seed: int, layer: int, which: int, step: int, tag: int = 0,
 def threshold_normal(seed: int, layer: int, step: int) -> np.float32:
     """The single normal of the adaptive-threshold noise (tag 1)."""
     return normals(1, seed, layer, 0, step, tag=1)[0]
+
+
+def normals_at(indices, seed: int, layer: int, which: int, step: int, tag: int = 0) -> np.ndarray:
+    """Elements at the given flat indices of the stream of (seed, layer,
+    which, step, tag): element e is lane e % 4 of the group e // 4."""
+    idx = np.asarray(indices, dtype=np.int64)
+    j = (idx // 4).astype(np.uint64)
+    w1 = np.full_like(j, (2 * int(layer) + int(which)) & 0xFFFFFFFF)
+    w2 = np.full_like(j, int(step) & 0xFFFFFFFF)
+    w3 = np.full_like(j, int(tag) & 0xFFFFFFFF)
+    x0, x1, x2, x3 = philox4x32_10((j, w1, w2, w3), key_of(seed))
+    z0, z1 = box_muller_f32(x0, x1)
+    z2, z3 = box_muller_f32(x2, x3)
+    z = np.stack([z0, z1, z2, z3], axis=1)
+    return z[np.arange(idx.shape[0]), idx % 4].astype(np.float32)
+
+
+def weight_noise(d: int, p: int, seed: int, layer: int, step: int) -> np.ndarray:
+    """The [d, p] weight-noise array: element (m, n) is lane m % 4 of the
+    block of group (m // 4) * p + n (which = 0, tag = 0)."""
+    nq = (d + 3) // 4
+    flat = normals(4 * nq * p, seed, layer, 0, step)      # group j = q * p + n, lanes 0..3
+    z = flat.reshape(nq, p, 4).transpose(0, 2, 1).reshape(4 * nq, p)
+    return np.ascontiguousarray(z[:d])
+
+
+def weight_noise_at(rows, cols, p: int, seed: int, layer: int, step: int) -> np.ndarray:
+    """Entries (rows[k], cols[k]) of weight_noise(d, p, ...)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    flat_idx = 4 * ((rows // 4) * p + cols) + rows % 4
+    return normals_at(flat_idx, seed, layer, 0, step)

@@ -1,0 +1,202 @@
+"""Python binding of libdpclip.so, the MI355X per-sample gradient clipping path.
+
+Argument marshalling only: torch tensors are turned into device pointers and
+sizes, the current HIP stream is passed along, and a status code other than
+DP_OK raises ``DpError``. Every step of the path runs in the library's HIP
+kernels; there is no CPU fallback, and a missing library raises on first use.
+
+The functions mirror the C ABI in ``include/dpclip.h``:
+
+    dp_ghost_norm(A, G, sqnorm, has_bias=False, mode=MODE_MIXED, kappa=1,
+                  accumulate=False, workspace=None) -> path
+    dp_clip_factors(sqnorm, C, c, norm=None)
+    dp_clipped_sum_noise(A, G, c, C, sigma, denom, seed, layer_id, step, out,
+                         bias_out=None, workspace=None)
+    dp_adaptive_threshold(norm, C_prev, alpha, beta, sigma_l2, init, seed,
+                          layer_id, step, C_next, C_l2_out=None)
+    dp_workspace_bytes(dtype, B, T, d, p, mode=MODE_MIXED, kappa=1) -> int
+    dp_choose_path(T, d, p, mode=MODE_MIXED, kappa=1) -> int
+
+A and G are contiguous [B, T, d] / [B, T, p] tensors (float32 or bfloat16) on
+the current GPU; norm, factor and output vectors are float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdpclip.so")
+
+DP_OK = 0
+DP_ERR_NULL, DP_ERR_SHAPE, DP_ERR_DTYPE, DP_ERR_VALUE = 1, 2, 3, 4
+DP_ERR_WORKSPACE, DP_ERR_HIP, DP_ERR_NO_DEVICE, DP_ERR_ALIGN = 5, 6, 7, 8
+DP_F32, DP_BF16 = 0, 1
+MODE_MIXED, MODE_GHOST, MODE_EXPLICIT = 0, 1, 2
+PATH_GHOST, PATH_EXPLICIT, PATH_T1 = 1, 2, 3
+
+EXPORTS = ("dp_ghost_norm", "dp_clip_factors", "dp_clipped_sum_noise", "dp_adaptive_threshold",
+           "dp_workspace_bytes", "dp_choose_path", "dp_status_string", "dp_abi_version")
+
+_lib = None
+
+
+class DpError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: status {status} ({msg})")
+        self.status = status
+
+
+def _declare(lib):
+    c_i64, c_i32, c_u32, c_u64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64
+    vp, fp, f = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float
+    lib.dp_ghost_norm.argtypes = [vp, vp, vp, c_i32, c_i64, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32,
+                                  vp, ctypes.c_size_t, fp, c_i32, ctypes.POINTER(c_i32)]
+    lib.dp_ghost_norm.restype = c_i32
+    lib.dp_clip_factors.argtypes = [vp, fp, c_i64, f, fp, fp]
+    lib.dp_clip_factors.restype = c_i32
+    lib.dp_clipped_sum_noise.argtypes = [vp, vp, vp, c_i32, c_i64, c_i64, c_i64, c_i64, fp, f, f, f,
+                                         c_u64, c_u32, c_u32, vp, ctypes.c_size_t, fp, fp]
+    lib.dp_clipped_sum_noise.restype = c_i32
+    lib.dp_adaptive_threshold.argtypes = [vp, fp, c_i64, f, f, f, f, c_i32, c_u64, c_u32, c_u32, fp, fp]
+    lib.dp_adaptive_threshold.restype = c_i32
+    lib.dp_workspace_bytes.argtypes = [c_i32, c_i64, c_i64, c_i64, c_i64, c_i32, c_i32]
+    lib.dp_workspace_bytes.restype = ctypes.c_size_t
+    lib.dp_choose_path.argtypes = [c_i64, c_i64, c_i64, c_i32, c_i32]
+    lib.dp_choose_path.restype = c_i32
+    lib.dp_status_string.argtypes = [c_i32]
+    lib.dp_status_string.restype = ctypes.c_char_p
+    lib.dp_abi_version.argtypes = []
+    lib.dp_abi_version.restype = c_i32
+    return lib
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sample_gradient_clipping_layer_amd._build`")
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != DP_OK:
+        raise DpError(fn, status, lib().dp_status_string(status).decode())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return DP_F32
+    if t.dtype == torch.bfloat16:
+        return DP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; float32 or bfloat16")
+
+
+def _layer(A, G):
+    if A.dim() != 3 or G.dim() != 3 or A.shape[:2] != G.shape[:2]:
+        raise ValueError(f"A [B,T,d] and G [B,T,p] expected, got {tuple(A.shape)} and {tuple(G.shape)}")
+    if A.dtype != G.dtype:
+        raise TypeError("A and G must share one dtype")
+    if not (A.is_contiguous() and G.is_contiguous()):
+        raise ValueError("A and G must be contiguous")
+    if not (A.is_cuda and G.is_cuda):
+        raise ValueError("A and G must be GPU tensors")
+    B, T, d = A.shape
+    return _dtype_code(A), int(B), int(T), int(d), int(G.shape[2])
+
+
+def _f32_vec(t, name):
+    import torch
+    if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+
+
+def dp_workspace_bytes(dtype: int, B: int, T: int, d: int, p: int, mode: int = MODE_MIXED, kappa: int = 1) -> int:
+    return int(lib().dp_workspace_bytes(dtype, B, T, d, p, mode, kappa))
+
+
+def dp_choose_path(T: int, d: int, p: int, mode: int = MODE_MIXED, kappa: int = 1) -> int:
+    return int(lib().dp_choose_path(T, d, p, mode, kappa))
+
+
+def dp_abi_version() -> int:
+    return int(lib().dp_abi_version())
+
+
+def dp_status_string(status: int) -> str:
+    return lib().dp_status_string(status).decode()
+
+
+def _workspace(workspace, dt, B, T, d, p, mode, kappa, device):
+    import torch
+    need = dp_workspace_bytes(dt, B, T, d, p, mode, kappa)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def dp_ghost_norm(A, G, sqnorm, has_bias: bool = False, mode: int = MODE_MIXED, kappa: int = 1,
+                  accumulate: bool = False, workspace=None) -> int:
+    dt, B, T, d, p = _layer(A, G)
+    _f32_vec(sqnorm, "sqnorm")
+    if sqnorm.numel() != B:
+        raise ValueError("sqnorm must have B elements")
+    ws, nbytes = _workspace(workspace, dt, B, T, d, p, mode, kappa, A.device)
+    path = ctypes.c_int32(0)
+    _check("dp_ghost_norm", lib().dp_ghost_norm(_stream(), _ptr(A), _ptr(G), dt, B, T, d, p, int(bool(has_bias)),
+                                                int(mode), int(kappa), _ptr(ws), nbytes, _ptr(sqnorm),
+                                                int(bool(accumulate)), ctypes.byref(path)))
+    return path.value
+
+
+def dp_clip_factors(sqnorm, C: float, c, norm=None):
+    _f32_vec(sqnorm, "sqnorm")
+    _f32_vec(c, "c")
+    if norm is not None:
+        _f32_vec(norm, "norm")
+    B = sqnorm.numel()
+    if c.numel() != B or (norm is not None and norm.numel() != B):
+        raise ValueError("sqnorm, c and norm must have the same length")
+    _check("dp_clip_factors", lib().dp_clip_factors(_stream(), _ptr(sqnorm), B, float(C), _ptr(c), _ptr(norm)))
+
+
+def dp_clipped_sum_noise(A, G, c, C: float, sigma: float, denom: float, seed: int, layer_id: int, step: int,
+                         out, bias_out=None, workspace=None):
+    dt, B, T, d, p = _layer(A, G)
+    _f32_vec(c, "c")
+    _f32_vec(out, "out")
+    if c.numel() != B or out.numel() != d * p:
+        raise ValueError("c must have B elements and out d*p")
+    if bias_out is not None:
+        _f32_vec(bias_out, "bias_out")
+        if bias_out.numel() != p:
+            raise ValueError("bias_out must have p elements")
+    ws, nbytes = _workspace(workspace, dt, B, T, d, p, MODE_MIXED, 1, A.device)
+    _check("dp_clipped_sum_noise", lib().dp_clipped_sum_noise(
+        _stream(), _ptr(A), _ptr(G), dt, B, T, d, p, _ptr(c), float(C), float(sigma), float(denom),
+        int(seed) & 0xFFFFFFFFFFFFFFFF, int(layer_id) & 0xFFFFFFFF, int(step) & 0xFFFFFFFF, _ptr(ws), nbytes,
+        _ptr(out), _ptr(bias_out)))
+
+
+def dp_adaptive_threshold(norm, C_prev: float, alpha: float, beta: float, sigma_l2: float, init: bool, seed: int,
+                          layer_id: int, step: int, C_next, C_l2_out=None):
+    _f32_vec(norm, "norm")
+    _f32_vec(C_next, "C_next")
+    if C_l2_out is not None:
+        _f32_vec(C_l2_out, "C_l2_out")
+    _check("dp_adaptive_threshold", lib().dp_adaptive_threshold(
+        _stream(), _ptr(norm), norm.numel(), float(C_prev), float(alpha), float(beta), float(sigma_l2),
+        int(bool(init)), int(seed) & 0xFFFFFFFFFFFFFFFF, int(layer_id) & 0xFFFFFFFF, int(step) & 0xFFFFFFFF,
+        _ptr(C_next), _ptr(C_l2_out)))

@@ -1,0 +1,208 @@
+// extern "C" entry points of libdpclip.so (declared in include/dpclip.h).
+// Every argument is validated before the first HIP call; then the kernels of
+// the chosen path are enqueued on the caller's stream, without synchronising.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/dpclip.h"
+#include "dp_launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;    // each of B, T, d+1, p below 2^31
+constexpr int64_t kMaxElems = (int64_t)1 << 50;  // B*T*(d+1), B*T*p
+constexpr int64_t kMaxNoise = (int64_t)1 << 32;  // ceil(d/4)*p: noise group index fits 32 bits
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+bool finite(float x) { return isfinite(x) != 0; }
+
+dp_status check_shape(int64_t B, int64_t T, int64_t d, int64_t p) {
+  if (B < 1 || T < 1 || d < 1 || p < 1) return DP_ERR_SHAPE;
+  if (B >= kMaxDim || T >= kMaxDim || d + 1 >= kMaxDim || p >= kMaxDim) return DP_ERR_SHAPE;
+  if (B * T >= kMaxDim * 8) return DP_ERR_SHAPE;
+  const int64_t bt = B * T;
+  if (bt > kMaxElems / (d + 1) || bt > kMaxElems / p) return DP_ERR_SHAPE;
+  if ((d + 3) / 4 >= kMaxNoise / p) return DP_ERR_SHAPE;
+  return DP_OK;
+}
+
+dp_status check_layer(const void* A, const void* G, dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64_t p) {
+  if (!A || !G) return DP_ERR_NULL;
+  dp_status s = check_shape(B, T, d, p);
+  if (s != DP_OK) return s;
+  if (dtype != DP_F32 && dtype != DP_BF16) return DP_ERR_DTYPE;
+  if (!aligned(A, 16) || !aligned(G, 16)) return DP_ERR_ALIGN;
+  return DP_OK;
+}
+
+dp_status device_ready() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n < 1) return DP_ERR_NO_DEVICE;
+  return DP_OK;
+}
+
+int path_of(int64_t T, int64_t d, int64_t p, dp_mode mode, int32_t kappa) {
+  if (mode == DP_MODE_EXPLICIT) return DP_PATH_EXPLICIT;
+  if (T == 1) return DP_PATH_T1;
+  if (mode == DP_MODE_GHOST) return DP_PATH_GHOST;
+  // p*d < kappa*T^2 -> instantiate; compared in long double to stay exact for large sizes
+  const long double pd = (long double)p * (long double)d;
+  const long double t2 = (long double)kappa * (long double)T * (long double)T;
+  return pd < t2 ? DP_PATH_EXPLICIT : DP_PATH_GHOST;
+}
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t norm_ws_bytes(int path, int64_t B, int64_t T, int64_t d, int64_t p, int has_bias) {
+  if (path == DP_PATH_T1) return 0;
+  int64_t ntiles;
+  if (path == DP_PATH_GHOST) {
+    ntiles = dpk::ghost_ntiles(T);
+  } else {
+    const dpk::ExplicitPlan pl = dpk::explicit_plan(d, p, has_bias);
+    ntiles = (int64_t)pl.mt * pl.nt;
+  }
+  return round256((size_t)B * (size_t)ntiles * sizeof(float));
+}
+
+size_t contract_ws_bytes(dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64_t p, int has_bias) {
+  const dpk::ContractPlan pl = dpk::contract_plan(dtype, B, T, d, p, has_bias);
+  if (pl.ks == 1) return 0;  // one K split: the epilogue writes the output directly
+  return round256((size_t)pl.ks * (size_t)(d + (has_bias ? 1 : 0)) * (size_t)p * sizeof(float));
+}
+
+dp_status hip_status(hipError_t e) { return e == hipSuccess ? DP_OK : DP_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t dp_abi_version(void) { return DP_ABI_VERSION; }
+
+const char* dp_status_string(dp_status status) {
+  switch (status) {
+    case DP_OK: return "ok";
+    case DP_ERR_NULL: return "a required pointer is NULL";
+    case DP_ERR_SHAPE: return "a size is < 1 or too large";
+    case DP_ERR_DTYPE: return "unknown dtype";
+    case DP_ERR_VALUE: return "a scalar argument is out of range";
+    case DP_ERR_WORKSPACE: return "workspace too small";
+    case DP_ERR_HIP: return "HIP call or kernel launch failed";
+    case DP_ERR_NO_DEVICE: return "no usable GPU device";
+    case DP_ERR_ALIGN: return "pointer not aligned as required";
+    default: return "unknown status";
+  }
+}
+
+int32_t dp_choose_path(int64_t T, int64_t d, int64_t p, dp_mode mode, int32_t kappa) {
+  if (T < 1 || d < 1 || p < 1 || mode < DP_MODE_MIXED || mode > DP_MODE_EXPLICIT || kappa < 1) return -1;
+  return path_of(T, d, p, mode, kappa);
+}
+
+size_t dp_workspace_bytes(dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64_t p, dp_mode mode, int32_t kappa) {
+  if (check_shape(B, T, d, p) != DP_OK) return 0;
+  if (dtype != DP_F32 && dtype != DP_BF16) return 0;
+  if (mode < DP_MODE_MIXED || mode > DP_MODE_EXPLICIT || kappa < 1) return 0;
+  const int path = path_of(T, d, p, mode, kappa);
+  size_t w = 0;
+  for (int hb = 0; hb <= 1; ++hb) {
+    const size_t a = norm_ws_bytes(path, B, T, d, p, hb);
+    const size_t b = contract_ws_bytes(dtype, B, T, d, p, hb);
+    if (a > w) w = a;
+    if (b > w) w = b;
+  }
+  return w;
+}
+
+dp_status dp_ghost_norm(void* stream, const void* A, const void* G, dp_dtype dtype, int64_t B, int64_t T, int64_t d,
+                        int64_t p, int32_t has_bias, dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes,
+                        float* sqnorm, int32_t accumulate, int32_t* path_out) {
+  dp_status s = check_layer(A, G, dtype, B, T, d, p);
+  if (s != DP_OK) return s;
+  if (!sqnorm) return DP_ERR_NULL;
+  if (!aligned(sqnorm, 4)) return DP_ERR_ALIGN;
+  if (mode < DP_MODE_MIXED || mode > DP_MODE_EXPLICIT || kappa < 1) return DP_ERR_VALUE;
+  const int hb = has_bias ? 1 : 0;
+  const int path = path_of(T, d, p, mode, kappa);
+  const size_t need = norm_ws_bytes(path, B, T, d, p, hb);
+  if (need > 0) {
+    if (!workspace) return DP_ERR_NULL;
+    if (ws_bytes < need) return DP_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return DP_ERR_ALIGN;
+  }
+  if (path == DP_PATH_GHOST && (uint64_t)((B + 7) / 8 * 8) * (uint64_t)dpk::ghost_ntiles(T) >= (1ull << 32))
+    return DP_ERR_SHAPE;
+  s = device_ready();
+  if (s != DP_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int acc = accumulate ? 1 : 0;
+  if (path_out) *path_out = path;
+  if (path == DP_PATH_T1) return hip_status(dpk::launch_norm_t1(st, dtype, A, G, B, d, p, hb, acc, sqnorm));
+  float* partial = static_cast<float*>(workspace);
+  hipError_t e;
+  int64_t ntiles;
+  if (path == DP_PATH_GHOST) {
+    e = dpk::launch_ghost(st, dtype, A, G, B, T, d, p, hb, partial);
+    ntiles = dpk::ghost_ntiles(T);
+  } else {
+    e = dpk::launch_explicit(st, dtype, A, G, B, T, d, p, hb, partial);
+    const dpk::ExplicitPlan pl = dpk::explicit_plan(d, p, hb);
+    ntiles = (int64_t)pl.mt * pl.nt;
+  }
+  if (e != hipSuccess) return DP_ERR_HIP;
+  return hip_status(dpk::launch_finalize_norm(st, partial, B, ntiles, acc, sqnorm));
+}
+
+dp_status dp_clip_factors(void* stream, const float* sqnorm, int64_t B, float C, float* c, float* norm) {
+  if (!sqnorm || !c) return DP_ERR_NULL;
+  if (B < 1 || B >= kMaxDim) return DP_ERR_SHAPE;
+  if (!finite(C) || !(C > 0.0f)) return DP_ERR_VALUE;
+  if (!aligned(sqnorm, 4) || !aligned(c, 4) || (norm && !aligned(norm, 4))) return DP_ERR_ALIGN;
+  dp_status s = device_ready();
+  if (s != DP_OK) return s;
+  return hip_status(dpk::launch_clip_factors(static_cast<hipStream_t>(stream), sqnorm, B, C, c, norm));
+}
+
+dp_status dp_clipped_sum_noise(void* stream, const void* A, const void* G, dp_dtype dtype, int64_t B, int64_t T,
+                               int64_t d, int64_t p, const float* c, float C, float sigma, float denom, uint64_t seed,
+                               uint32_t layer_id, uint32_t step, void* workspace, size_t ws_bytes, float* out,
+                               float* bias_out) {
+  dp_status s = check_layer(A, G, dtype, B, T, d, p);
+  if (s != DP_OK) return s;
+  if (!c || !out) return DP_ERR_NULL;
+  if (!aligned(c, 4) || !aligned(out, 4) || (bias_out && !aligned(bias_out, 4))) return DP_ERR_ALIGN;
+  if (!finite(C) || !(C > 0.0f) || !finite(sigma) || sigma < 0.0f || !finite(denom) || !(denom > 0.0f))
+    return DP_ERR_VALUE;
+  const int hb = bias_out ? 1 : 0;
+  const dpk::ContractPlan pl = dpk::contract_plan(dtype, B, T, d, p, hb);
+  const size_t need = contract_ws_bytes(dtype, B, T, d, p, hb);
+  if (need > 0) {
+    if (!workspace) return DP_ERR_NULL;
+    if (ws_bytes < need) return DP_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return DP_ERR_ALIGN;
+  }
+  if ((int64_t)pl.mt * pl.nt * pl.ks >= ((int64_t)1 << 31)) return DP_ERR_SHAPE;
+  s = device_ready();
+  if (s != DP_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float sc = sigma * C;
+  return hip_status(dpk::launch_clipped_sum(st, dtype, A, G, c, B, T, d, p, pl, static_cast<float*>(workspace), sc,
+                                            denom, seed, layer_id, step, out, bias_out));
+}
+
+dp_status dp_adaptive_threshold(void* stream, const float* norm, int64_t B, float C_prev, float alpha, float beta,
+                                float sigma_l2, int32_t init, uint64_t seed, uint32_t layer_id, uint32_t step,
+                                float* C_next, float* C_l2_out) {
+  if (!norm || !C_next) return DP_ERR_NULL;
+  if (B < 1 || B >= kMaxDim) return DP_ERR_SHAPE;
+  if (!aligned(norm, 4) || !aligned(C_next, 4) || (C_l2_out && !aligned(C_l2_out, 4))) return DP_ERR_ALIGN;
+  if (!finite(alpha) || !(alpha > 0.0f) || !finite(beta) || !(beta > 0.0f) || !finite(sigma_l2) || sigma_l2 < 0.0f)
+    return DP_ERR_VALUE;
+  if (!init && (!finite(C_prev) || !(C_prev > 0.0f))) return DP_ERR_VALUE;
+  dp_status s = device_ready();
+  if (s != DP_OK) return s;
+  return hip_status(dpk::launch_adaptive_threshold(static_cast<hipStream_t>(stream), norm, B, C_prev, alpha, beta,
+                                                   sigma_l2, init ? 1 : 0, seed, layer_id, step, C_next, C_l2_out));
+}
+
+}  // extern "C"

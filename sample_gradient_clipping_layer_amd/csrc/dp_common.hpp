@@ -1,0 +1,125 @@
+// Shared device helpers for the clipping kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dpk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// Storage type of a bf16 element (bit pattern); fp32 is plain float.
+struct bf16s {
+  uint16_t u;
+};
+
+template <typename T>
+struct elem_traits;
+template <>
+struct elem_traits<float> {
+  static constexpr int bytes = 4;
+  static constexpr int per16 = 4;  // elements per 16-byte vector
+};
+template <>
+struct elem_traits<bf16s> {
+  static constexpr int bytes = 2;
+  static constexpr int per16 = 8;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16s x) { return __uint_as_float((uint32_t)x.u << 16); }
+
+// Raw bits of one element, widened to 32 bits (bf16 -> low 16 bits).
+__device__ __forceinline__ uint32_t raw_bits(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ uint32_t raw_bits(bf16s x) { return x.u; }
+
+// Sum over the 64 lanes of a wave in a fixed butterfly order. Every lane ends
+// with a value; lane 0's is used, and it is the same from run to run.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Sum over the block (NT threads) in a fixed order; valid in thread 0.
+// `red` is LDS scratch of NT/64 floats. Contains a barrier: every thread of
+// the block must call it.
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < NT / kWave; ++i) s += red[i];
+  }
+  return s;
+}
+
+// 16-byte load of elements [k, k+per16) of row `row` of an [nrows, K] matrix
+// (row-major), zero outside [0, nrows) x [0, K). `vec` says every row starts
+// 16-byte aligned (base aligned and K*bytes % 16 == 0), so a full vector
+// load is legal when the whole vector is inside the row.
+template <typename T>
+__device__ __forceinline__ uint4 load16_rowmajor(const T* __restrict__ X, int64_t nrows, int64_t K,
+                                                 int64_t row, int64_t k, bool vec) {
+  constexpr int P = elem_traits<T>::per16;
+  uint4 r = make_uint4(0u, 0u, 0u, 0u);
+  if (row < 0 || row >= nrows) return r;
+  const T* src = X + row * K;
+  if (vec && k + P <= K) {
+    r = *reinterpret_cast<const uint4*>(src + k);
+    return r;
+  }
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+    const int64_t kk = k + e;
+    uint32_t bits = 0u;
+    if (kk < K) bits = raw_bits(src[kk]);
+    if constexpr (P == 8) {
+      w[e >> 1] |= bits << (16 * (e & 1));
+    } else {
+      w[e] = bits;
+    }
+  }
+  r.x = w[0];
+  r.y = w[1];
+  r.z = w[2];
+  r.w = w[3];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D += A * B on one 32x32 output block, K = 16 (bf16 inputs).
+__device__ __forceinline__ f32x16 mfma32_bf16(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+// D += A * B on one 32x32 output block, K = 2 (fp32 inputs, one per lane).
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Position of accumulator element j of a 32x32 MFMA block held by `lane`:
+// column = lane % 32, row = 8*(j/4) + 4*(lane/32) + j%4.
+__device__ __forceinline__ int acc_row(int j, int lane) { return 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3); }
+__device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
+
+// Workgroup -> (group, item) map that keeps all items of one group on one XCD.
+// Workgroups are dispatched to the 8 XCDs round robin by their linear id, so
+// id % 8 is the XCD. Groups g with g % 8 == xcd are served by that XCD.
+__device__ __forceinline__ void xcd_group_map(int64_t bid, int64_t items, int64_t* group, int64_t* item) {
+  const int64_t xcd = bid & 7;
+  const int64_t local = bid >> 3;
+  *item = local % items;
+  *group = (local / items) * 8 + xcd;
+}
+
+}  // namespace dpk

@@ -1,0 +1,43 @@
+// Host-side launchers of the clipping kernels (internal to libdpclip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dpk {
+
+struct ContractPlan {
+  int bm, bn;               // output tile (64 or 128 each)
+  int mt, nt;               // tiles along d (+1 bias row) and p
+  int64_t ks;               // K splits (partial tiles summed by the reduce)
+  int64_t units_per_split;  // samples (bf16) or 16-row chunks (fp32) per split
+};
+struct ExplicitPlan {
+  int bm, bn, mt, nt;
+};
+
+ContractPlan contract_plan(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias);
+ExplicitPlan explicit_plan(int64_t d, int64_t p, int has_bias);
+int ghost_tile_size(int64_t T);
+int64_t ghost_ntiles(int64_t T);
+
+hipError_t launch_norm_t1(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t d, int64_t p,
+                          int has_bias, int accumulate, float* sqnorm);
+hipError_t launch_ghost(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
+                        int64_t p, int has_bias, float* partial);
+hipError_t launch_explicit(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
+                           int64_t p, int has_bias, float* partial);
+hipError_t launch_finalize_norm(hipStream_t st, const float* partial, int64_t B, int64_t ntiles, int accumulate,
+                                float* sqnorm);
+// Weighted contraction + noise + 1/denom: one kernel when pl.ks == 1,
+// else partial tiles in ws and a reduce kernel. bias_out != nullptr <=> bias row.
+hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const void* G, const float* c, int64_t B,
+                              int64_t Tn, int64_t d, int64_t p, const ContractPlan& pl, float* ws, float sc,
+                              float denom, uint64_t seed, uint32_t layer, uint32_t step, float* out,
+                              float* bias_out);
+hipError_t launch_clip_factors(hipStream_t st, const float* sqnorm, int64_t B, float C, float* c, float* norm);
+hipError_t launch_adaptive_threshold(hipStream_t st, const float* norm, int64_t B, float C_prev, float alpha,
+                                     float beta, float sigma_l2, int init, uint64_t seed, uint32_t layer,
+                                     uint32_t step, float* C_next, float* C_l2_out);
+
+}  // namespace dpk

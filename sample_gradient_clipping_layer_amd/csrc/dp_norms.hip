@@ -1,0 +1,322 @@
+// Per-example gradient norms of one layer (three paths) and their per-sample
+// reduction.
+//
+//  * closed form, T = 1: ||a_i (x) g_i||_F^2 = ||a_i||^2 ||g_i||^2 (FPC eq. (6));
+//    with a bias the input gains a constant-1 feature: (||a_i||^2 + 1) ||g_i||^2.
+//  * ghost: ||A_i^T G_i||_F^2 = <A_i A_i^T, G_i G_i^T> (SEDP eq. (2.7), Sec. 3.1)
+//    on LDS-staged Gram tiles computed by MFMA; the Grams never leave
+//    registers. With a bias, A_i A_i^T + 1 1^T.
+//  * explicit (per-sample instantiation, SEDP App. C.4) lives in dp_xty.hip.
+//
+// Reductions are fixed-order (no atomics), so results are bitwise
+// reproducible.
+#include "dp_common.hpp"
+#include "dp_launch.hpp"
+
+namespace dpk {
+
+// ---------------------------------------------------------------- T == 1
+template <typename T>
+__device__ __forceinline__ float row_sqsum(const T* __restrict__ row, int64_t n, int lane) {
+  constexpr int P = elem_traits<T>::per16;
+  float s0 = 0.f, s1 = 0.f;
+  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
+  int64_t nv = vec ? (n / P) : 0;
+  const uint4* rv = reinterpret_cast<const uint4*>(row);
+  for (int64_t q = lane; q < nv; q += kWave) {
+    const uint4 v = rv[q];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (P == 8) {
+        const float lo = __uint_as_float(w[e] << 16);
+        const float hi = __uint_as_float(w[e] & 0xFFFF0000u);
+        s0 += lo * lo;
+        s1 += hi * hi;
+      } else {
+        const float x = __uint_as_float(w[e]);
+        if (e & 1)
+          s1 += x * x;
+        else
+          s0 += x * x;
+      }
+    }
+  }
+  for (int64_t k = nv * P + lane; k < n; k += kWave) {
+    const float x = to_f32(row[k]);
+    s0 += x * x;
+  }
+  return s0 + s1;
+}
+
+// One wave per sample, four samples per workgroup.
+template <typename T>
+__global__ __launch_bounds__(256) void k_norm_t1(const T* __restrict__ A, const T* __restrict__ G, int64_t B,
+                                                 int64_t d, int64_t p, int has_bias, int accumulate,
+                                                 float* __restrict__ sqnorm) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= B) return;
+  float sa = wave_sum(row_sqsum(A + i * d, d, lane));
+  float sg = wave_sum(row_sqsum(G + i * p, p, lane));
+  if (lane == 0) {
+    const float v = (sa + (has_bias ? 1.0f : 0.0f)) * sg;
+    sqnorm[i] = accumulate ? sqnorm[i] + v : v;
+  }
+}
+
+// ---------------------------------------------------------------- ghost tiles
+// Workgroup = (sample i, Gram tile (sb, tb), sb <= tb) of TS x TS. Four waves
+// in 2 x 2, each a (TS/2)^2 sub-tile of 32x32 MFMA blocks. The K loop stages
+// 256-byte row chunks of the two row blocks (one if diagonal) into a
+// double-buffered LDS, with the next chunk's global loads in flight during
+// the MFMAs of this one: first the chunks of A_i (K = d, Gram of A), then
+// those of G_i (K = p, Gram of G). The epilogue forms sum (GA + bias) .* GG,
+// doubled off the diagonal.
+template <typename T, int TS>
+struct GhostCfg {
+  static constexpr int NT = 256;
+  static constexpr int P = elem_traits<T>::per16;
+  static constexpr int CB = TS == 64 ? 256 : 128;  // bytes per staged row chunk (8 vectors/thread either way)
+  static constexpr int V = CB / 16;                // 16-byte vectors per row chunk
+  static constexpr int KC = V * P;                 // elements per staged row chunk
+  static constexpr int ROWB = CB + 16;             // LDS row stride (bytes), conflict-free b128 reads
+  static constexpr int BUF = 2 * TS * ROWB;        // one buffer: both row blocks
+  static constexpr int WM = TS / 2;
+  static constexpr int NB = WM / 32;
+  static constexpr int PIECES = 2 * TS * V;        // 16-byte pieces of one chunk of both row blocks
+  static constexpr int PPT = PIECES / NT;
+  static_assert(PIECES % NT == 0, "tile/threads mismatch");
+  struct Regs {
+    uint4 v[PPT];
+  };
+};
+
+template <typename T, int TS>
+__device__ __forceinline__ void ghost_load(typename GhostCfg<T, TS>::Regs& regs, const T* __restrict__ Xi, int64_t Tn,
+                                           int64_t K, bool vec, int sb, int tb, int64_t chunk) {
+  using Cfg = GhostCfg<T, TS>;
+  const bool diag = (sb == tb);
+#pragma unroll
+  for (int r = 0; r < Cfg::PPT; ++r) {
+    const int q = threadIdx.x + r * Cfg::NT;
+    const int h = q / (TS * Cfg::V);
+    const int row = (q / Cfg::V) % TS;
+    const int c16 = q % Cfg::V;
+    if (diag && h == 1) {
+      regs.v[r] = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+      const int64_t grow = (int64_t)(h == 0 ? sb : tb) * TS + row;
+      regs.v[r] = load16_rowmajor(Xi, Tn, K, grow, chunk * Cfg::KC + c16 * Cfg::P, vec);
+    }
+  }
+}
+
+template <typename T, int TS>
+__device__ __forceinline__ void ghost_store(const typename GhostCfg<T, TS>::Regs& regs, unsigned char* buf, bool diag) {
+  using Cfg = GhostCfg<T, TS>;
+#pragma unroll
+  for (int r = 0; r < Cfg::PPT; ++r) {
+    const int q = threadIdx.x + r * Cfg::NT;
+    const int h = q / (TS * Cfg::V);
+    const int row = (q / Cfg::V) % TS;
+    const int c16 = q % Cfg::V;
+    if (!(diag && h == 1)) *reinterpret_cast<uint4*>(buf + (h * TS + row) * Cfg::ROWB + c16 * 16) = regs.v[r];
+  }
+}
+
+template <typename T, int TS>
+__device__ __forceinline__ void ghost_compute(const unsigned char* buf, bool diag,
+                                              f32x16 (&acc)[GhostCfg<T, TS>::NB][GhostCfg<T, TS>::NB]) {
+  using Cfg = GhostCfg<T, TS>;
+  constexpr int NB = Cfg::NB;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const unsigned char* sbase = buf;
+  const unsigned char* tbase = buf + (diag ? 0 : TS * Cfg::ROWB);
+  if constexpr (Cfg::P == 8) {
+#pragma unroll
+    for (int ks = 0; ks < Cfg::KC / 16; ++ks) {
+      uint4 a[NB], b[NB];
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi) {
+        const int row = wm * Cfg::WM + bi * 32 + (lane & 31);
+        a[bi] = *reinterpret_cast<const uint4*>(sbase + row * Cfg::ROWB + ks * 32 + (lane >> 5) * 16);
+      }
+#pragma unroll
+      for (int bj = 0; bj < NB; ++bj) {
+        const int row = wn * Cfg::WM + bj * 32 + (lane & 31);
+        b[bj] = *reinterpret_cast<const uint4*>(tbase + row * Cfg::ROWB + ks * 32 + (lane >> 5) * 16);
+      }
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj) acc[bi][bj] = mfma32_bf16(a[bi], b[bj], acc[bi][bj]);
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < Cfg::KC / 8; ++g) {
+      float4 a[NB], b[NB];
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi) {
+        const int row = wm * Cfg::WM + bi * 32 + (lane & 31);
+        a[bi] = *reinterpret_cast<const float4*>(sbase + row * Cfg::ROWB + g * 32 + (lane >> 5) * 16);
+      }
+#pragma unroll
+      for (int bj = 0; bj < NB; ++bj) {
+        const int row = wn * Cfg::WM + bj * 32 + (lane & 31);
+        b[bj] = *reinterpret_cast<const float4*>(tbase + row * Cfg::ROWB + g * 32 + (lane >> 5) * 16);
+      }
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj) {
+          acc[bi][bj] = mfma32_f32(a[bi].x, b[bj].x, acc[bi][bj]);
+          acc[bi][bj] = mfma32_f32(a[bi].y, b[bj].y, acc[bi][bj]);
+          acc[bi][bj] = mfma32_f32(a[bi].z, b[bj].z, acc[bi][bj]);
+          acc[bi][bj] = mfma32_f32(a[bi].w, b[bj].w, acc[bi][bj]);
+        }
+    }
+  }
+}
+
+template <typename T, int TS>
+__global__ __launch_bounds__(256) void k_ghost_tiles(const T* __restrict__ A, const T* __restrict__ G, int64_t B,
+                                                     int64_t Tn, int64_t d, int64_t p, int has_bias, int nb,
+                                                     int ntiles, int vecA, int vecG, float* __restrict__ partial) {
+  using Cfg = GhostCfg<T, TS>;
+  constexpr int NB = Cfg::NB;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  __shared__ float red[Cfg::NT / kWave];
+
+  int64_t i, tile;
+  xcd_group_map(blockIdx.x, ntiles, &i, &tile);
+  if (i >= B) return;
+  int sb = 0;
+  int rem = (int)tile;
+  while (rem >= nb - sb) {
+    rem -= nb - sb;
+    ++sb;
+  }
+  const int tb = sb + rem;
+  const bool diag = (sb == tb);
+
+  f32x16 acc_a[NB][NB], acc_g[NB][NB];
+#pragma unroll
+  for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        acc_a[bi][bj][j] = 0.f;
+        acc_g[bi][bj][j] = 0.f;
+      }
+
+  const T* Ai = A + i * Tn * d;
+  const T* Gi = G + i * Tn * p;
+  const int64_t nA = (d + Cfg::KC - 1) / Cfg::KC;
+  const int64_t nG = (p + Cfg::KC - 1) / Cfg::KC;
+  const int64_t n = nA + nG;
+  typename Cfg::Regs regs;
+  ghost_load<T, TS>(regs, Ai, Tn, d, vecA != 0, sb, tb, 0);
+  for (int64_t c = 0; c < n; ++c) {
+    unsigned char* buf = lds + (c & 1) * Cfg::BUF;
+    ghost_store<T, TS>(regs, buf, diag);
+    __syncthreads();
+    const int64_t cn = c + 1;
+    if (cn < nA)
+      ghost_load<T, TS>(regs, Ai, Tn, d, vecA != 0, sb, tb, cn);
+    else if (cn < n)
+      ghost_load<T, TS>(regs, Gi, Tn, p, vecG != 0, sb, tb, cn - nA);
+    if (c < nA)
+      ghost_compute<T, TS>(buf, diag, acc_a);
+    else
+      ghost_compute<T, TS>(buf, diag, acc_g);
+  }
+
+  const float one = has_bias ? 1.0f : 0.0f;
+  float s = 0.f;
+#pragma unroll
+  for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s += (acc_a[bi][bj][j] + one) * acc_g[bi][bj][j];
+  if (!diag) s *= 2.0f;
+  s = block_sum<Cfg::NT>(s, red);
+  if (threadIdx.x == 0) partial[i * ntiles + tile] = s;
+}
+
+// ---------------------------------------------------------------- finalize
+// sqnorm[i] (+)= sum over the sample's tile partials, in tile order.
+__global__ __launch_bounds__(256) void k_finalize_norm(const float* __restrict__ partial, int64_t B, int ntiles,
+                                                       int accumulate, float* __restrict__ sqnorm) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B) return;
+  float s = 0.f;
+  for (int t = 0; t < ntiles; ++t) s += partial[i * ntiles + t];
+  sqnorm[i] = accumulate ? sqnorm[i] + s : s;
+}
+
+// ---------------------------------------------------------------- launchers
+template <typename T>
+hipError_t launch_norm_t1_t(hipStream_t st, const void* A, const void* G, int64_t B, int64_t d, int64_t p,
+                            int has_bias, int accumulate, float* sqnorm) {
+  const dim3 grid((unsigned)((B + 3) / 4));
+  hipLaunchKernelGGL(k_norm_t1<T>, grid, dim3(256), 0, st, static_cast<const T*>(A), static_cast<const T*>(G), B, d,
+                     p, has_bias, accumulate, sqnorm);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_t1(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t d, int64_t p,
+                          int has_bias, int accumulate, float* sqnorm) {
+  if (dtype == 1) return launch_norm_t1_t<bf16s>(st, A, G, B, d, p, has_bias, accumulate, sqnorm);
+  return launch_norm_t1_t<float>(st, A, G, B, d, p, has_bias, accumulate, sqnorm);
+}
+
+int ghost_tile_size(int64_t T) { return T <= 384 ? 64 : 128; }
+
+int64_t ghost_ntiles(int64_t T) {
+  const int64_t ts = ghost_tile_size(T);
+  const int64_t nb = (T + ts - 1) / ts;
+  return nb * (nb + 1) / 2;
+}
+
+template <typename T, int TS>
+hipError_t launch_ghost_t(hipStream_t st, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d, int64_t p,
+                          int has_bias, float* partial) {
+  const int nb = (int)((Tn + TS - 1) / TS);
+  const int ntiles = nb * (nb + 1) / 2;
+  const int64_t groups8 = (B + 7) / 8;
+  const dim3 grid((unsigned)(groups8 * 8 * ntiles));
+  const int eb = elem_traits<T>::bytes;
+  const int vecA = ((reinterpret_cast<uintptr_t>(A) & 15) == 0) && ((d * eb) % 16 == 0);
+  const int vecG = ((reinterpret_cast<uintptr_t>(G) & 15) == 0) && ((p * eb) % 16 == 0);
+  const size_t lds_bytes = 2 * GhostCfg<T, TS>::BUF;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ghost_tiles<T, TS>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_ghost_tiles<T, TS>), grid, dim3(256), lds_bytes, st, static_cast<const T*>(A),
+                     static_cast<const T*>(G), B, Tn, d, p, has_bias, nb, ntiles, vecA, vecG, partial);
+  return hipGetLastError();
+}
+
+hipError_t launch_ghost(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
+                        int64_t p, int has_bias, float* partial) {
+  const int ts = ghost_tile_size(Tn);
+  if (dtype == 1) {
+    if (ts == 64) return launch_ghost_t<bf16s, 64>(st, A, G, B, Tn, d, p, has_bias, partial);
+    return launch_ghost_t<bf16s, 128>(st, A, G, B, Tn, d, p, has_bias, partial);
+  }
+  if (ts == 64) return launch_ghost_t<float, 64>(st, A, G, B, Tn, d, p, has_bias, partial);
+  return launch_ghost_t<float, 128>(st, A, G, B, Tn, d, p, has_bias, partial);
+}
+
+hipError_t launch_finalize_norm(hipStream_t st, const float* partial, int64_t B, int64_t ntiles, int accumulate,
+                                float* sqnorm) {
+  const dim3 grid((unsigned)((B + 255) / 256));
+  hipLaunchKernelGGL(k_finalize_norm, grid, dim3(256), 0, st, partial, B, (int)ntiles, accumulate, sqnorm);
+  return hipGetLastError();
+}
+
+}  // namespace dpk

@@ -1,0 +1,103 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the HIP path
+through the binding, and compare against the oracle with the stated bars.
+
+Tolerances (from the method's stated targets):
+  norms           |n_gpu - n_or| <= tau * n_or, tau = 1e-4 (fp32) / 1e-2 (bf16)
+  clip decisions  equal wherever |N_or - C| > 1e-3 * C; c within the norm tolerance
+  clipped sum     max|S_gpu - S_or| <= tau_S * max|S_or|, tau_S = 1e-3 (fp32) / 2e-2 (bf16)
+  noise           bit-exact against the oracle's fp32 replica (S exactly 0)
+  noised mean     |out_gpu - out_or| <= tau_S * max|S_or| / denom + 4 ulp
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import sample_gradient_clipping_layer_amd as dpc
+import workloads as W
+
+TAU_NORM = {"f32": 1e-4, "bf16": 1e-2}
+TAU_SUM = {"f32": 1e-3, "bf16": 2e-2}
+
+
+def dev():
+    return torch.device("cuda", 0)
+
+
+def upload(x: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev())
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev())
+
+
+def f32(x) -> torch.Tensor:
+    return torch.as_tensor(np.ascontiguousarray(x, dtype=np.float32)).to(dev())
+
+
+def gpu_global_step(layers_dev, has_bias, C, sigma, seed, step=0, denom=None, mode=dpc.MODE_MIXED, kappa=1,
+                    layer_ids=None):
+    """norms of all layers -> clip factors -> clipped noised mean per layer."""
+    B = layers_dev[0][0].shape[0]
+    denom = float(B) if denom is None else float(denom)
+    layer_ids = list(range(len(layers_dev))) if layer_ids is None else list(layer_ids)
+    sq = torch.full((B,), float("nan"), dtype=torch.float32, device=dev())
+    paths = []
+    for l, (A, G) in enumerate(layers_dev):
+        paths.append(dpc.dp_ghost_norm(A, G, sq, has_bias=has_bias, mode=mode, kappa=kappa, accumulate=l > 0))
+    c = torch.empty(B, dtype=torch.float32, device=dev())
+    norm = torch.empty(B, dtype=torch.float32, device=dev())
+    dpc.dp_clip_factors(sq, C, c, norm)
+    outs, bouts = [], []
+    for lid, (A, G) in zip(layer_ids, layers_dev):
+        d, p = A.shape[2], G.shape[2]
+        out = torch.empty(d, p, dtype=torch.float32, device=dev())
+        bout = torch.empty(p, dtype=torch.float32, device=dev()) if has_bias else None
+        dpc.dp_clipped_sum_noise(A, G, c, C, sigma, denom, seed, lid, step, out, bout)
+        outs.append(out)
+        bouts.append(bout)
+    torch.cuda.synchronize()
+    return dict(sq=sq.cpu().numpy(), norm=norm.cpu().numpy(), c=c.cpu().numpy(), paths=paths,
+                outs=[o.cpu().numpy() for o in outs],
+                bias_outs=[None if b is None else b.cpu().numpy() for b in bouts])
+
+
+def assert_norms(n_gpu, n_or, dtype, what="norm"):
+    n_gpu = np.asarray(n_gpu, dtype=np.float64)
+    err = np.abs(n_gpu - n_or)
+    bound = TAU_NORM[dtype] * np.abs(n_or)
+    bad = np.nonzero(~(err <= bound))[0]
+    assert bad.size == 0, f"{what}: {bad.size} outside tol, worst rel {np.max(err / np.maximum(np.abs(n_or), 1e-300)):.3e} at {bad[:5]}"
+
+
+def assert_clip(c_gpu, c_or, N_or, C, dtype):
+    c_gpu = np.asarray(c_gpu, dtype=np.float64)
+    away = np.abs(N_or - C) > 1e-3 * C
+    dec_gpu = c_gpu < 1.0
+    dec_or = c_or < 1.0
+    mism = np.nonzero(away & (dec_gpu != dec_or))[0]
+    assert mism.size == 0, f"clip decision mismatch at {mism[:10]}"
+    err = np.abs(c_gpu - c_or)
+    assert np.all(err <= TAU_NORM[dtype] * np.abs(c_or) + 1e-30), f"clip factor max rel err {np.max(err / c_or):.3e}"
+
+
+def assert_sum(S_gpu, S_or, dtype, what="sum"):
+    S_gpu = np.asarray(S_gpu, dtype=np.float64)
+    scale = np.max(np.abs(S_or))
+    err = np.max(np.abs(S_gpu - S_or))
+    assert err <= TAU_SUM[dtype] * scale, f"{what}: max err {err:.3e} vs bound {TAU_SUM[dtype] * scale:.3e}"
+
+
+def assert_noised(out_gpu, out_or, S_or, noise_or, dtype, denom, what="out", noise_rtol=0.0):
+    """noise_rtol: relative difference of the noise scale sigma*C between the
+    two sides (free-running adaptive bounds), 0 when both use the same C."""
+    out_gpu = np.asarray(out_gpu, dtype=np.float64)
+    atol = TAU_SUM[dtype] * np.max(np.abs(S_or)) / denom
+    ulp = (4 * 2.0 ** -23 + noise_rtol) * (np.abs(out_or) + np.abs(noise_or))
+    err = np.abs(out_gpu - out_or)
+    bad = np.nonzero(~(err <= atol + ulp))[0]
+    assert bad.size == 0, f"{what}: {bad.size} outside tol; max err {np.max(err):.3e}, atol {atol:.3e}"
+
+
+def layer_inputs(wl, l, step=0, B=None, shape=None):
+    A, G = W.make_layer(wl, l, step=step, B=B, shape=shape)
+    return (A, G), (W.as_f64(A, wl.dtype), W.as_f64(G, wl.dtype)), (upload(A, wl.dtype), upload(G, wl.dtype))

@@ -16,7 +16,15 @@ from oracle import noise as N
 import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _f64_default():
+    """fp64 autograd in these tests only (restored afterwards)."""
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(old)
 
 
 def _two_layer_net(rng, d, h, p):
@@ -364,3 +372,38 @@ def test_workload_inputs_shapes_and_recipe():
     b = W.f32_to_bf16_bits(x)
     np.testing.assert_array_equal(W.bf16_bits_to_f32(b),
                                   torch.tensor(x).to(torch.bfloat16).to(torch.float32).numpy())
+
+
+def test_entrywise_helpers_agree_with_whole_forms():
+    """The entry-wise clipped sum and the indexed noise lookup used by
+    full-size checks equal the corresponding entries of the whole forms."""
+    rng = np.random.default_rng(14)
+    A = rng.standard_normal((5, 3, 7))
+    G = rng.standard_normal((5, 3, 6))
+    c = rng.uniform(size=5)
+    S, _ = D.clipped_sum(A, G, c)
+    rows = rng.integers(0, 7, 20)
+    cols = rng.integers(0, 6, 20)
+    np.testing.assert_allclose(D.clipped_sum_entries(A, G, c, rows, cols), S[rows, cols], rtol=1e-13)
+    full = N.normals(42, 9, 4, 1, 3)
+    idx = rng.integers(0, 42, 30)
+    np.testing.assert_array_equal(N.normals_at(idx, 9, 4, 1, 3), full[idx])
+
+
+def test_weight_noise_layout():
+    """Weight noise element (m, n) is lane m % 4 of the Philox block at group
+    (m // 4) * p + n; rows past d in the last group are simply not used."""
+    d, p, seed, layer, step = 7, 5, 11, 2, 3
+    z = N.weight_noise(d, p, seed, layer, step)
+    assert z.shape == (d, p)
+    for m in range(d):
+        for n in range(p):
+            j = (m // 4) * p + n
+            x = N.philox4x32_10(tuple(np.array([v], dtype=np.uint64) for v in (j, 2 * layer, step, 0)),
+                                N.key_of(seed))
+            za, zb = N.box_muller_f32(x[0], x[1])
+            zc, zd = N.box_muller_f32(x[2], x[3])
+            assert z[m, n] == [za[0], zb[0], zc[0], zd[0]][m % 4]
+    rows = np.array([0, 3, 4, 6, 6])
+    cols = np.array([4, 0, 2, 1, 4])
+    np.testing.assert_array_equal(N.weight_noise_at(rows, cols, p, seed, layer, step), z[rows, cols])
