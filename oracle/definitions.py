@@ -146,13 +146,15 @@ def noised_mean(S: np.ndarray, z: np.ndarray, C: float, sigma: float, denom: flo
 
 def noised_mean_f32(S32: np.ndarray, z32: np.ndarray, C: float, sigma: float, denom: float) -> np.ndarray:
     """The same quantity evaluated as the fp32 operation sequence
-    out = ((S + (sigma*C)*z) / denom), every operation rounded to fp32. Used for
-    the bit-exact noise check, where S is exactly zero."""
+    out = (S + (sigma*C)*z) * (1/denom), every operation rounded to fp32 (the
+    reciprocal of denom rounded once; exact when denom is a power of two).
+    Used for the bit-exact noise check, where S is exactly zero."""
     f = np.float32
     sc = f(sigma) * f(C)
+    inv = f(1.0) / f(denom)
     n = (sc * np.asarray(z32, dtype=np.float32)).astype(np.float32)
     o = (np.asarray(S32, dtype=np.float32) + n).astype(np.float32)
-    return (o / f(denom)).astype(np.float32)
+    return (o * inv).astype(np.float32)
 
 
 def adaptive_clip_norm(norm: np.ndarray, C_l2: float) -> np.ndarray:

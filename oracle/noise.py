@@ -27,13 +27,20 @@ pairs (x0, x1) and (x2, x3):
   u1 = ((x >> 8) + 1) * 2^-24  in (0, 1]      (exact in fp32)
   v  = x' >> 8;  q = v >> 22 (quadrant);  f = (v & (2^22 - 1)) * 2^-22  (exact)
   r  = sqrt(-2 ln u1);  (z_a, z_b) = r * (cos 2 pi u2, sin 2 pi u2), u2 = v 2^-24
-All arithmetic is fp32 with every operation rounded (no fused multiply-add);
-sqrt and division are correctly rounded. ln and sin/cos are evaluated as below
-with the constants given as hex floats; the tails of the series beyond the
-kept terms are below 1e-9 relative, under the fp32 rounding of the result.
+All arithmetic is fp32 with every operation rounded (no fused multiply-add)
+and no division or square root: both are replaced by fixed Newton sequences
+from integer-bit initial guesses, so that the two implementations can follow
+the same operations exactly. ln and sin/cos are evaluated as below with the
+constants given as hex floats; the tails of the series beyond the kept terms
+are below 1e-9 relative, under the fp32 rounding of the result.
+  rcp(b), b in [1.7, 2.5]:  r = bits(0x7EF311C3 - bits(b)); 3 times
+          r = r * (2 - b*r).                       (max rel. error 1.5e-7)
+  rsqrt(t), t > 0:  y = bits(0x5F3759DF - (bits(t) >> 1)), h = 0.5*t; 3 times
+          y = y * (1.5 - h*(y*y)).                  (max rel. error 1.6e-7)
   ln u1:  u1 = m * 2^e with m in [2^-1/2, 2^1/2] (m halved and e raised when
-          m > SQRT2); s = (m - 1)/(m + 1); ln m = 2s * (1 + s^2/3 + ... + s^10/11)
-          by Horner in s^2; ln u1 = e*LN2 + ln m   (atanh series).
+          m > SQRT2); s = (m - 1) * rcp(m + 1); ln m = 2s * (1 + s^2/3 + ... +
+          s^10/11) by Horner in s^2; ln u1 = e*LN2 + ln m   (atanh series).
+  r = t * rsqrt(t) for t = -2 ln u1 > 0, and r = 0 for t = 0 (u1 = 1).
   sin/cos of (pi/2)*f: if f > 1/2 use g = 1 - f and swap sin and cos; phi = g*HALF_PI;
           sin phi = phi + phi*(phi^2*P_s(phi^2)), cos phi = 1 + phi^2*P_c(phi^2),
           Taylor polynomials to phi^9 and phi^10; then the quadrant q rotates
@@ -95,6 +102,34 @@ def philox4x32_10(ctr, key):
     return tuple(c.astype(np.uint32) for c in (c0, c1, c2, c3))
 
 
+RCP_MAGIC = np.uint32(0x7EF311C3)
+RSQRT_MAGIC = np.uint32(0x5F3759DF)
+
+
+def rcp_f32(b: np.ndarray) -> np.ndarray:
+    """Reciprocal of b in [1.7, 2.5] as the specified Newton sequence."""
+    b = np.asarray(b, dtype=np.float32)
+    r = (RCP_MAGIC - b.view(np.uint32)).view(np.float32)
+    for _ in range(3):
+        t = (b * r).astype(np.float32)
+        t = (_f(2.0) - t).astype(np.float32)
+        r = (r * t).astype(np.float32)
+    return r
+
+
+def rsqrt_f32(t: np.ndarray) -> np.ndarray:
+    """1/sqrt(t) for t > 0 as the specified Newton sequence."""
+    t = np.asarray(t, dtype=np.float32)
+    y = (RSQRT_MAGIC - (t.view(np.uint32) >> np.uint32(1))).view(np.float32)
+    h = (_f(0.5) * t).astype(np.float32)
+    for _ in range(3):
+        y2 = (y * y).astype(np.float32)
+        pr = (h * y2).astype(np.float32)
+        q = (_f(1.5) - pr).astype(np.float32)
+        y = (y * q).astype(np.float32)
+    return y
+
+
 def ln_f32(u: np.ndarray) -> np.ndarray:
     """Natural log of u in (0, 1] as the specified fp32 operation sequence."""
     u = np.asarray(u, dtype=np.float32)
@@ -104,7 +139,7 @@ def ln_f32(u: np.ndarray) -> np.ndarray:
     big = m > SQRT2
     m = np.where(big, (m * _f(0.5)).astype(np.float32), m)
     e = np.where(big, e + 1, e)
-    s = ((m - _f(1.0)).astype(np.float32) / (m + _f(1.0)).astype(np.float32)).astype(np.float32)
+    s = ((m - _f(1.0)).astype(np.float32) * rcp_f32((m + _f(1.0)).astype(np.float32))).astype(np.float32)
     s2 = (s * s).astype(np.float32)
     p = np.full_like(s2, K11)
     for k in (K9, K7, K5, K3, _f(1.0)):
@@ -141,7 +176,9 @@ def box_muller_f32(xa: np.ndarray, xb: np.ndarray):
     v = xb >> np.uint32(8)
     q = (v >> np.uint32(22)).astype(np.int32)
     frac = ((v & np.uint32(0x3FFFFF)).astype(np.float32) * TWO_M22).astype(np.float32)
-    r = np.sqrt((_f(-2.0) * ln_f32(u1)).astype(np.float32)).astype(np.float32)
+    t = (_f(-2.0) * ln_f32(u1)).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        r = np.where(t > _f(0.0), (t * rsqrt_f32(np.where(t > 0, t, _f(1.0)))).astype(np.float32), _f(0.0))
     s, c = sincos_quarter_f32(frac)
     # rotate (cos, sin) of the in-quadrant angle by q quarter turns
     cos_t = np.select([q == 0, q == 1, q == 2], [c, -s, -c], default=s).astype(np.float32)

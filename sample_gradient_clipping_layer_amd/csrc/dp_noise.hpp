@@ -13,10 +13,15 @@
 // Box-Muller on (x0, x1) and (x2, x3): u1 = ((x >> 8) + 1) * 2^-24,
 // v = x' >> 8, quadrant q = v >> 22, in-quadrant fraction f = (v mod 2^22) * 2^-22,
 // r = sqrt(-2 ln u1), (cos, sin)(2 pi u2) from quarter-turn polynomials.
-// Every operation is an IEEE fp32 operation rounded on its own: contraction is
-// off in these functions and division/sqrt use the correctly rounded forms.
-// ln: u1 = m 2^e, m in [2^-1/2, 2^1/2], s = (m-1)/(m+1),
+// Every operation is an IEEE fp32 add/sub/mul rounded on its own (contraction
+// is off in these functions); there is no division or square root: both are
+// fixed Newton sequences from integer-bit initial guesses, so that a CPU
+// replica can follow the same operations exactly.
+// rcp(b):   r = bits(0x7EF311C3 - bits(b)), 3 x  r = r * (2 - b*r)
+// rsqrt(t): y = bits(0x5F3759DF - (bits(t) >> 1)), h = t/2, 3 x  y = y * (1.5 - h*(y*y))
+// ln: u1 = m 2^e, m in [2^-1/2, 2^1/2], s = (m-1) * rcp(m+1),
 //     ln m = 2s * (1 + s^2/3 + s^4/5 + ... + s^10/11) (atanh series, Horner in s^2).
+// r = t * rsqrt(t) for t = -2 ln u1 > 0, else 0.
 // sin/cos of phi = g*pi/2, g = f or 1-f (then swapped), Taylor to phi^9 / phi^10.
 #pragma once
 
@@ -52,6 +57,34 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
 // hardware fp32 square root is not correctly rounded.
 __device__ __forceinline__ float sqrt_rn_f32(float x) { return (float)__dsqrt_rn((double)x); }
 
+// Reciprocal of b in [1.7, 2.5]: three Newton steps (relative error < 2e-7).
+__device__ __forceinline__ float rcp_spec(float b) {
+#pragma clang fp contract(off)
+  float r = __uint_as_float(0x7EF311C3u - __float_as_uint(b));
+#pragma unroll
+  for (int it = 0; it < 3; ++it) {
+    float t = b * r;
+    t = 2.0f - t;
+    r = r * t;
+  }
+  return r;
+}
+
+// 1/sqrt(t) for t > 0: three Newton steps (relative error < 2e-7).
+__device__ __forceinline__ float rsqrt_spec(float t) {
+#pragma clang fp contract(off)
+  float y = __uint_as_float(0x5F3759DFu - (__float_as_uint(t) >> 1));
+  const float h = 0.5f * t;
+#pragma unroll
+  for (int it = 0; it < 3; ++it) {
+    const float y2 = y * y;
+    const float pr = h * y2;
+    const float q = 1.5f - pr;
+    y = y * q;
+  }
+  return y;
+}
+
 __device__ __forceinline__ float ln_spec(float u) {
 #pragma clang fp contract(off)
   const float kLn2 = 0x1.62e430p-1f;
@@ -63,7 +96,7 @@ __device__ __forceinline__ float ln_spec(float u) {
     m = m * 0.5f;
     e = e + 1;
   }
-  const float s = __fdiv_rn(m - 1.0f, m + 1.0f);
+  const float s = (m - 1.0f) * rcp_spec(m + 1.0f);
   const float s2 = s * s;
   float p = 0x1.745d18p-4f;   // 1/11
   p = p * s2 + 0x1.c71c72p-4f;  // 1/9
@@ -103,7 +136,8 @@ __device__ __forceinline__ void box_muller_spec(uint32_t xa, uint32_t xb, float*
   const uint32_t v = xb >> 8;
   const uint32_t q = v >> 22;
   const float f = (float)(v & 0x3FFFFFu) * 0x1p-22f;
-  const float r = sqrt_rn_f32(-2.0f * ln_spec(u1));
+  const float t = -2.0f * ln_spec(u1);
+  const float r = t > 0.0f ? t * rsqrt_spec(t > 0.0f ? t : 1.0f) : 0.0f;
   float s, c;
   sincos_quarter_spec(f, &s, &c);
   // rotate (c, s) by q quarter turns without branches: odd q swaps the pair,
@@ -134,12 +168,13 @@ __device__ __forceinline__ f32x4 normals4(uint32_t j, uint32_t word1, uint32_t s
   return z;
 }
 
-// out = (S + (sigma*C) * z) / denom, each operation rounded to fp32.
-__device__ __forceinline__ float noised_mean_spec(float S, float sc, float z, float denom) {
+// out = (S + (sigma*C) * z) * inv_denom, each operation rounded to fp32;
+// inv_denom is 1/denom rounded once on the host (exact for powers of two).
+__device__ __forceinline__ float noised_mean_spec(float S, float sc, float z, float inv_denom) {
 #pragma clang fp contract(off)
   const float n = sc * z;
   const float o = S + n;
-  return __fdiv_rn(o, denom);
+  return o * inv_denom;
 }
 
 }  // namespace dpk

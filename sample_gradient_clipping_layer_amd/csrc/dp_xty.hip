@@ -36,52 +36,87 @@ struct XtyCfg;
 template <>
 struct XtyCfg<float> {
   static constexpr int KC = 32;  // rows per chunk (128 bytes per feature row)
+  static constexpr int RU = 4;   // rows per staging unit (4 x 4 floats, transposed)
 };
 template <>
 struct XtyCfg<bf16s> {
   static constexpr int KC = 64;
+  static constexpr int RU = 8;   // rows per staging unit (8 x 8 bf16, transposed)
 };
 constexpr int kRowB = 144;  // LDS bytes per feature row of a chunk (128 + 16 pad)
+
+// Where chunk rows come from: X rows at xp, Y rows at yp (row r of the chunk at
+// xp + r*Kx), rv of the KC rows valid; fp32 rows are scaled by c[(r0 + r) / Tn].
+template <typename T>
+struct ChunkSrc {
+  const T* xp;
+  const T* yp;
+  int rv;
+  int64_t r0;  // flat row index of chunk row 0 (for the clip factor)
+};
 
 template <typename T, int BM, int BN>
 struct Xty {
   static constexpr int NT = 256;
   static constexpr int P = elem_traits<T>::per16;
   static constexpr int KC = XtyCfg<T>::KC;
+  static constexpr int RU = XtyCfg<T>::RU;
   static constexpr int WMt = BM / 2, WNt = BN / 2;
   static constexpr int NBM = WMt / 32, NBN = WNt / 32;
-  static constexpr int UX = (KC / 4) * (BM / P);  // staging units (4 rows x 16 bytes) of X per chunk
-  static constexpr int UY = (KC / 4) * (BN / P);
+  static constexpr int UX = (KC / RU) * (BM / P);  // staging units (RU rows x 16 bytes) of X per chunk
+  static constexpr int UY = (KC / RU) * (BN / P);
   static constexpr int UT = UX + UY;
   static constexpr int UPT = (UT + NT - 1) / NT;  // units per thread
   static constexpr int BUF = (BM + BN) * kRowB;
   static constexpr int LDS_BYTES = 2 * BUF;
+  static_assert(KC / RU == 8, "eight row groups per chunk");
 
   typedef f32x16 AccT[NBM][NBN];
 
   struct Regs {
-    uint4 v[UPT][4];
-    float sc[UPT][4];
+    uint4 v[UPT][RU];
   };
 
-  // Global loads of one chunk: rows [row0, row0+KC) of X (features m0..) and
-  // Y (features n0..). Rows >= nrows and features past the end are zero; the
-  // virtual ones column of X is set on valid rows. fp32: Y rows carry c[row/Tn].
-  __device__ __forceinline__ static void load(Regs& R, const T* X, int64_t Kx, bool vecx, int64_t ones_col,
-                                              const T* Y, int64_t Ky, bool vecy, int64_t nrows, int64_t row0,
-                                              int64_t m0, int64_t n0, const float* c, int64_t Tn) {
+  // Unit u of an operand -> (row group rr, 16-byte column vector cc). The map
+  // makes every 16-lane pass of the transposed LDS stores hit 16 distinct
+  // 4-bank groups, and keeps global loads of one row contiguous across lanes.
+  __device__ __forceinline__ static void unit_rc(int u, int* rr, int* cc) {
+    if constexpr (P == 8) {
+      *rr = u & 7;
+      *cc = u >> 3;
+    } else {
+      *rr = (u & 3) + 4 * ((u >> 4) & 1);
+      *cc = ((u >> 2) & 3) + 4 * (u >> 5);
+    }
+  }
+
+  // Load one chunk into registers. x_full/y_full: the whole tile width is
+  // inside the matrix and rows are 16-byte aligned (no per-element checks).
+  __device__ __forceinline__ static void load(Regs& R, const ChunkSrc<T>& cs, int64_t Kx, int64_t Ky, int64_t m0,
+                                              int64_t n0, bool x_full, bool y_full, bool vecx, bool vecy,
+                                              int64_t ones_col) {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int unit = threadIdx.x + u * NT;
-      if (unit < UX) {
-        const int rq = unit / (BM / P), cu = unit % (BM / P);
-        const int64_t col0 = m0 + cu * P;
+      if (unit >= UT) continue;
+      const bool isx = unit < UX;
+      int rr, cc;
+      unit_rc(isx ? unit : unit - UX, &rr, &cc);
+      const T* base = isx ? cs.xp : cs.yp;
+      const int64_t K = isx ? Kx : Ky;
+      const int64_t col = (isx ? m0 : n0) + cc * P;
+      const bool full = (isx ? x_full : y_full) && cs.rv == KC;
+      if (full) {
+        const T* src = base + (int64_t)(rr * RU) * K + col;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t row = row0 + rq * 4 + r;
-          uint4 v = load16_rowmajor(X, nrows, Kx, row, col0, vecx);
-          if (ones_col >= col0 && ones_col < col0 + P && row < nrows) {
-            const int e = (int)(ones_col - col0);
+        for (int r = 0; r < RU; ++r) R.v[u][r] = *reinterpret_cast<const uint4*>(src + (int64_t)r * K);
+      } else {
+#pragma unroll
+        for (int r = 0; r < RU; ++r) {
+          const int row = rr * RU + r;
+          uint4 v = load16_rowmajor(base, (int64_t)cs.rv, K, (int64_t)row, col, isx ? vecx : vecy);
+          if (isx && ones_col >= col && ones_col < col + P && row < cs.rv) {
+            const int e = (int)(ones_col - col);
             uint32_t w[4] = {v.x, v.y, v.z, v.w};
             if constexpr (P == 8)
               w[e >> 1] |= 0x3F80u << (16 * (e & 1));
@@ -90,64 +125,56 @@ struct Xty {
             v = make_uint4(w[0], w[1], w[2], w[3]);
           }
           R.v[u][r] = v;
-          R.sc[u][r] = 1.0f;
-        }
-      } else if (unit < UT) {
-        const int uy = unit - UX;
-        const int rq = uy / (BN / P), cu = uy % (BN / P);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t row = row0 + rq * 4 + r;
-          R.v[u][r] = load16_rowmajor(Y, nrows, Ky, row, n0 + cu * P, vecy);
-          float s = 1.0f;
-          if constexpr (P == 4) {
-            if (c != nullptr) s = row < nrows ? c[row / Tn] : 0.0f;
-          }
-          R.sc[u][r] = s;
         }
       }
     }
   }
 
-  // Transposed stores of the loaded chunk into LDS rows [feature][k].
-  __device__ __forceinline__ static void store(const Regs& R, unsigned char* buf) {
+  // Transposed stores: feature f = cc*P + m gets the RU k-values of the unit
+  // as one 16-byte write at k offset rr*RU. fp32 G rows are scaled by c.
+  __device__ __forceinline__ static void store(const Regs& R, unsigned char* buf, const ChunkSrc<T>& cs,
+                                               const float* c, int64_t Tn) {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int unit = threadIdx.x + u * NT;
       if (unit >= UT) continue;
-      int rq, fbase;
-      if (unit < UX) {
-        rq = unit / (BM / P);
-        fbase = (unit % (BM / P)) * P;
-      } else {
-        const int uy = unit - UX;
-        rq = uy / (BN / P);
-        fbase = BM + (uy % (BN / P)) * P;
-      }
-      unsigned char* rows = buf + fbase * kRowB;
-      const int k0 = rq * 4;
+      const bool isx = unit < UX;
+      int rr, cc;
+      unit_rc(isx ? unit : unit - UX, &rr, &cc);
+      unsigned char* dst = buf + ((isx ? 0 : BM) + cc * P) * kRowB + rr * 16;
       if constexpr (P == 4) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          float4 o;
-          o.x = __uint_as_float(m == 0 ? R.v[u][0].x : m == 1 ? R.v[u][0].y : m == 2 ? R.v[u][0].z : R.v[u][0].w) * R.sc[u][0];
-          o.y = __uint_as_float(m == 0 ? R.v[u][1].x : m == 1 ? R.v[u][1].y : m == 2 ? R.v[u][1].z : R.v[u][1].w) * R.sc[u][1];
-          o.z = __uint_as_float(m == 0 ? R.v[u][2].x : m == 1 ? R.v[u][2].y : m == 2 ? R.v[u][2].z : R.v[u][2].w) * R.sc[u][2];
-          o.w = __uint_as_float(m == 0 ? R.v[u][3].x : m == 1 ? R.v[u][3].y : m == 2 ? R.v[u][3].z : R.v[u][3].w) * R.sc[u][3];
-          *reinterpret_cast<float4*>(rows + m * kRowB + k0 * 4) = o;
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const int sh = 16 * (m & 1);
-          uint32_t e[4];
+        float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if (!isx && c != nullptr) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint4& v = R.v[u][r];
-            const uint32_t w = (m >> 1) == 0 ? v.x : (m >> 1) == 1 ? v.y : (m >> 1) == 2 ? v.z : v.w;
-            e[r] = (w >> sh) & 0xFFFFu;
+            const int row = rr * 4 + r;
+            sc[r] = row < cs.rv ? c[(cs.r0 + row) / Tn] : 0.0f;
           }
-          *reinterpret_cast<uint2*>(rows + m * kRowB + k0 * 2) = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+        }
+        const uint4* v = R.v[u];
+        *reinterpret_cast<float4*>(dst + 0 * kRowB) = make_float4(__uint_as_float(v[0].x) * sc[0], __uint_as_float(v[1].x) * sc[1], __uint_as_float(v[2].x) * sc[2], __uint_as_float(v[3].x) * sc[3]);
+        *reinterpret_cast<float4*>(dst + 1 * kRowB) = make_float4(__uint_as_float(v[0].y) * sc[0], __uint_as_float(v[1].y) * sc[1], __uint_as_float(v[2].y) * sc[2], __uint_as_float(v[3].y) * sc[3]);
+        *reinterpret_cast<float4*>(dst + 2 * kRowB) = make_float4(__uint_as_float(v[0].z) * sc[0], __uint_as_float(v[1].z) * sc[1], __uint_as_float(v[2].z) * sc[2], __uint_as_float(v[3].z) * sc[3]);
+        *reinterpret_cast<float4*>(dst + 3 * kRowB) = make_float4(__uint_as_float(v[0].w) * sc[0], __uint_as_float(v[1].w) * sc[1], __uint_as_float(v[2].w) * sc[2], __uint_as_float(v[3].w) * sc[3]);
+      } else {
+        // 8 x 8 bf16 transpose: out[m] packs rows (2kp, 2kp+1) of column m
+        const uint4* v = R.v[u];
+#pragma unroll
+        for (int mp = 0; mp < 4; ++mp) {  // column pair (2mp, 2mp+1) lives in dword mp of every row
+          uint32_t w[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) w[r] = mp == 0 ? v[r].x : mp == 1 ? v[r].y : mp == 2 ? v[r].z : v[r].w;
+          uint4 even, odd;
+          even.x = (w[0] & 0xFFFFu) | (w[1] << 16);
+          even.y = (w[2] & 0xFFFFu) | (w[3] << 16);
+          even.z = (w[4] & 0xFFFFu) | (w[5] << 16);
+          even.w = (w[6] & 0xFFFFu) | (w[7] << 16);
+          odd.x = (w[0] >> 16) | (w[1] & 0xFFFF0000u);
+          odd.y = (w[2] >> 16) | (w[3] & 0xFFFF0000u);
+          odd.z = (w[4] >> 16) | (w[5] & 0xFFFF0000u);
+          odd.w = (w[6] >> 16) | (w[7] & 0xFFFF0000u);
+          *reinterpret_cast<uint4*>(dst + (2 * mp) * kRowB) = even;
+          *reinterpret_cast<uint4*>(dst + (2 * mp + 1) * kRowB) = odd;
         }
       }
     }
@@ -156,20 +183,16 @@ struct Xty {
   __device__ __forceinline__ static void compute(const unsigned char* buf, AccT& acc) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
-    const unsigned char* xb = buf;
-    const unsigned char* yb = buf + BM * kRowB;
+    const unsigned char* xb = buf + (wm * WMt + (lane & 31)) * kRowB + (lane >> 5) * 16;
+    const unsigned char* yb = buf + (BM + wn * WNt + (lane & 31)) * kRowB + (lane >> 5) * 16;
     if constexpr (P == 8) {
 #pragma unroll
       for (int ks = 0; ks < KC / 16; ++ks) {
         uint4 a[NBM], b[NBN];
 #pragma unroll
-        for (int bi = 0; bi < NBM; ++bi)
-          a[bi] = *reinterpret_cast<const uint4*>(xb + (wm * WMt + bi * 32 + (lane & 31)) * kRowB + ks * 32 +
-                                                  (lane >> 5) * 16);
+        for (int bi = 0; bi < NBM; ++bi) a[bi] = *reinterpret_cast<const uint4*>(xb + bi * 32 * kRowB + ks * 32);
 #pragma unroll
-        for (int bj = 0; bj < NBN; ++bj)
-          b[bj] = *reinterpret_cast<const uint4*>(yb + (wn * WNt + bj * 32 + (lane & 31)) * kRowB + ks * 32 +
-                                                  (lane >> 5) * 16);
+        for (int bj = 0; bj < NBN; ++bj) b[bj] = *reinterpret_cast<const uint4*>(yb + bj * 32 * kRowB + ks * 32);
 #pragma unroll
         for (int bi = 0; bi < NBM; ++bi)
 #pragma unroll
@@ -180,13 +203,9 @@ struct Xty {
       for (int g = 0; g < KC / 8; ++g) {
         float4 a[NBM], b[NBN];
 #pragma unroll
-        for (int bi = 0; bi < NBM; ++bi)
-          a[bi] = *reinterpret_cast<const float4*>(xb + (wm * WMt + bi * 32 + (lane & 31)) * kRowB + g * 32 +
-                                                   (lane >> 5) * 16);
+        for (int bi = 0; bi < NBM; ++bi) a[bi] = *reinterpret_cast<const float4*>(xb + bi * 32 * kRowB + g * 32);
 #pragma unroll
-        for (int bj = 0; bj < NBN; ++bj)
-          b[bj] = *reinterpret_cast<const float4*>(yb + (wn * WNt + bj * 32 + (lane & 31)) * kRowB + g * 32 +
-                                                   (lane >> 5) * 16);
+        for (int bj = 0; bj < NBN; ++bj) b[bj] = *reinterpret_cast<const float4*>(yb + bj * 32 * kRowB + g * 32);
 #pragma unroll
         for (int bi = 0; bi < NBM; ++bi)
 #pragma unroll
@@ -232,14 +251,28 @@ __global__ __launch_bounds__(256, 2) void k_explicit_tiles(const T* __restrict__
   typename E::AccT acc;
   E::zero(acc);
   typename E::Regs R;
+  const bool x_full = vecA && (m0 + BM <= d);
+  const bool y_full = vecG && (n0 + BN <= p);
   const int64_t nq = (Tn + E::KC - 1) / E::KC;
-  E::load(R, Xi, d, vecA != 0, ones_col, Yi, p, vecG != 0, Tn, 0, m0, n0, nullptr, Tn);
+  auto src = [&](int64_t q) {
+    ChunkSrc<T> cs;
+    cs.xp = Xi + q * E::KC * d;
+    cs.yp = Yi + q * E::KC * p;
+    const int64_t left = Tn - q * E::KC;
+    cs.rv = (int)(left < E::KC ? left : E::KC);
+    cs.r0 = 0;
+    return cs;
+  };
+  ChunkSrc<T> cs = src(0);
+  E::load(R, cs, d, p, m0, n0, x_full, y_full, vecA != 0, vecG != 0, ones_col);
   for (int64_t q = 0; q < nq; ++q) {
     unsigned char* buf = lds + (q & 1) * E::BUF;
-    E::store(R, buf);
+    E::store(R, buf, cs, nullptr, Tn);
     __syncthreads();
-    if (q + 1 < nq)
-      E::load(R, Xi, d, vecA != 0, ones_col, Yi, p, vecG != 0, Tn, (q + 1) * E::KC, m0, n0, nullptr, Tn);
+    if (q + 1 < nq) {
+      cs = src(q + 1);
+      E::load(R, cs, d, p, m0, n0, x_full, y_full, vecA != 0, vecG != 0, ones_col);
+    }
     E::compute(buf, acc);
   }
   float s = 0.f;
@@ -255,12 +288,12 @@ __global__ __launch_bounds__(256, 2) void k_explicit_tiles(const T* __restrict__
 
 // ---------------------------------------------------------------- contraction
 struct NoiseArgs {
-  float sc, denom;
+  float sc, inv_denom;  // sigma*C and the fp32 reciprocal of denom
   uint32_t k0, k1, layer, step;
 };
 
 // Workgroup = (output tile, K split). FUSED (one split): out and bias_out get
-// (S + sc*z)/denom directly. Otherwise ws[split][m][n] (m < d + has_bias).
+// (S + sc*z) * (1/denom) directly. Otherwise ws[split][m][n] (m < d + has_bias).
 template <typename T, int BM, int BN, bool FUSED>
 __global__ __launch_bounds__(256, 2) void k_contract_tiles(const T* __restrict__ A, const T* __restrict__ G,
                                                            const float* __restrict__ c, int64_t B, int64_t Tn,
@@ -281,42 +314,71 @@ __global__ __launch_bounds__(256, 2) void k_contract_tiles(const T* __restrict__
   typename E::AccT acc;
   E::zero(acc);
   typename E::Regs R;
+  const bool x_full = vecA && (m0 + BM <= d);
+  const bool y_full = vecG && (n0 + BN <= p);
   if constexpr (E::P == 4) {
     // flat K over all B*T rows in chunks of KC rows; G rows scaled by c[row / T]
     const int64_t nrows = B * Tn;
     const int64_t nunits = (nrows + E::KC - 1) / E::KC;
     const int64_t u0 = split * units_per_split;
     const int64_t u1 = u0 + units_per_split < nunits ? u0 + units_per_split : nunits;
-    if (u0 < u1) E::load(R, A, d, vecA != 0, ones_col, G, p, vecG != 0, nrows, u0 * E::KC, m0, n0, c, Tn);
+    auto src = [&](int64_t u) {
+      ChunkSrc<T> cs;
+      cs.r0 = u * E::KC;
+      cs.xp = A + cs.r0 * d;
+      cs.yp = G + cs.r0 * p;
+      const int64_t left = nrows - cs.r0;
+      cs.rv = (int)(left < E::KC ? left : E::KC);
+      return cs;
+    };
+    ChunkSrc<T> cs = src(u0);
+    if (u0 < u1) E::load(R, cs, d, p, m0, n0, x_full, y_full, vecA != 0, vecG != 0, ones_col);
     for (int64_t u = u0; u < u1; ++u) {
       unsigned char* buf = lds + ((u - u0) & 1) * E::BUF;
-      E::store(R, buf);
+      E::store(R, buf, cs, c, Tn);
       __syncthreads();
-      if (u + 1 < u1) E::load(R, A, d, vecA != 0, ones_col, G, p, vecG != 0, nrows, (u + 1) * E::KC, m0, n0, c, Tn);
+      if (u + 1 < u1) {
+        cs = src(u + 1);
+        E::load(R, cs, d, p, m0, n0, x_full, y_full, vecA != 0, vecG != 0, ones_col);
+      }
       E::compute(buf, acc);
     }
   } else {
     // per-sample exact accumulation: acc += c_i * (A_i^T G_i tile)
     const int64_t i0 = split * units_per_split;
     const int64_t i1 = i0 + units_per_split < B ? i0 + units_per_split : B;
-    const int64_t cps = (Tn + E::KC - 1) / E::KC;  // chunks per sample
-    const int64_t nq = (i1 > i0 ? i1 - i0 : 0) * cps;
+    const int cps = (int)((Tn + E::KC - 1) / E::KC);  // chunks per sample
     typename E::AccT tmp;
     E::zero(tmp);
-    if (nq > 0) E::load(R, A + i0 * Tn * d, d, vecA != 0, ones_col, G + i0 * Tn * p, p, vecG != 0, Tn, 0, m0, n0,
-                        nullptr, Tn);
-    for (int64_t q = 0; q < nq; ++q) {
+    auto src = [&](int64_t i, int ch) {
+      ChunkSrc<T> cs;
+      const int64_t row = i * Tn + (int64_t)ch * E::KC;
+      cs.xp = A + row * d;
+      cs.yp = G + row * p;
+      const int64_t left = Tn - (int64_t)ch * E::KC;
+      cs.rv = (int)(left < E::KC ? left : E::KC);
+      cs.r0 = row;
+      return cs;
+    };
+    int64_t i = i0;
+    int ch = 0;
+    ChunkSrc<T> cs = src(i, ch);
+    if (i0 < i1) E::load(R, cs, d, p, m0, n0, x_full, y_full, vecA != 0, vecG != 0, ones_col);
+    int64_t q = 0;
+    while (i < i1) {
       unsigned char* buf = lds + (q & 1) * E::BUF;
-      E::store(R, buf);
+      E::store(R, buf, cs, nullptr, Tn);
       __syncthreads();
-      if (q + 1 < nq) {
-        const int64_t in = i0 + (q + 1) / cps, chn = (q + 1) % cps;
-        E::load(R, A + in * Tn * d, d, vecA != 0, ones_col, G + in * Tn * p, p, vecG != 0, Tn, chn * E::KC, m0, n0,
-                nullptr, Tn);
+      const bool last = (ch == cps - 1);
+      const int64_t in = last ? i + 1 : i;
+      const int chn = last ? 0 : ch + 1;
+      if (in < i1) {
+        cs = src(in, chn);
+        E::load(R, cs, d, p, m0, n0, x_full, y_full, vecA != 0, vecG != 0, ones_col);
       }
       E::compute(buf, tmp);
-      if (q % cps == cps - 1) {
-        const float ci = c[i0 + q / cps];
+      if (last) {
+        const float ci = c[i];
 #pragma unroll
         for (int bi = 0; bi < E::NBM; ++bi)
 #pragma unroll
@@ -327,6 +389,9 @@ __global__ __launch_bounds__(256, 2) void k_contract_tiles(const T* __restrict__
               tmp[bi][bj][j] = 0.f;
             }
       }
+      i = in;
+      ch = chn;
+      ++q;
     }
   }
 
@@ -348,12 +413,12 @@ __global__ __launch_bounds__(256, 2) void k_contract_tiles(const T* __restrict__
             const f32x4 z = normals4((uint32_t)((mb >> 2) * p + n), 2u * na.layer, na.step, 0u, na.k0, na.k1);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (mb + r < d) out[(mb + r) * p + n] = noised_mean_spec(acc[bi][bj][4 * j4 + r], na.sc, z[r], na.denom);
+              if (mb + r < d) out[(mb + r) * p + n] = noised_mean_spec(acc[bi][bj][4 * j4 + r], na.sc, z[r], na.inv_denom);
           }
           if (has_bias && d >= mb && d < mb + 4) {
             const f32x4 zb = normals4((uint32_t)(n >> 2), 2u * na.layer + 1u, na.step, 0u, na.k0, na.k1);
             const int r = (int)(d - mb);
-            bias_out[n] = noised_mean_spec(acc[bi][bj][4 * j4 + r], na.sc, zb[(int)(n & 3)], na.denom);
+            bias_out[n] = noised_mean_spec(acc[bi][bj][4 * j4 + r], na.sc, zb[(int)(n & 3)], na.inv_denom);
           }
         }
   } else {
@@ -419,7 +484,7 @@ __global__ __launch_bounds__(256) void k_reduce_noise(const float* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t m = 4 * q + r;
-        if (m < d) s[r][k] = noised_mean_spec(s[r][k], na.sc, z[r], na.denom);
+        if (m < d) s[r][k] = noised_mean_spec(s[r][k], na.sc, z[r], na.inv_denom);
       }
     }
 #pragma unroll
@@ -443,7 +508,7 @@ __global__ __launch_bounds__(256) void k_reduce_noise(const float* __restrict__ 
       if (n >= p) continue;
       float s = 0.f;
       for (int64_t sp = 0; sp < ks; ++sp) s += ws[sp * split_stride + d * p + n];
-      bias_out[n] = noised_mean_spec(s, na.sc, z[k], na.denom);
+      bias_out[n] = noised_mean_spec(s, na.sc, z[k], na.inv_denom);
     }
   }
 }
@@ -551,7 +616,7 @@ hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const vo
   const int has_bias = bias_out != nullptr ? 1 : 0;
   NoiseArgs na;
   na.sc = sc;
-  na.denom = denom;
+  na.inv_denom = 1.0f / denom;
   na.k0 = (uint32_t)(seed & 0xFFFFFFFFu);
   na.k1 = (uint32_t)(seed >> 32);
   na.layer = layer;
