@@ -7,6 +7,10 @@
 namespace dpk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+// 16 bytes as a native vector (not HIP's uint4 wrapper class: whole-object
+// copies of the wrapper keep register arrays from being promoted out of
+// private memory).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -67,14 +71,14 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 // 16-byte aligned (base aligned and K*bytes % 16 == 0), so a full vector
 // load is legal when the whole vector is inside the row.
 template <typename T>
-__device__ __forceinline__ uint4 load16_rowmajor(const T* __restrict__ X, int64_t nrows, int64_t K,
+__device__ __forceinline__ u32x4 load16_rowmajor(const T* __restrict__ X, int64_t nrows, int64_t K,
                                                  int64_t row, int64_t k, bool vec) {
   constexpr int P = elem_traits<T>::per16;
-  uint4 r = make_uint4(0u, 0u, 0u, 0u);
+  u32x4 r = {0u, 0u, 0u, 0u};
   if (row < 0 || row >= nrows) return r;
   const T* src = X + row * K;
   if (vec && k + P <= K) {
-    r = *reinterpret_cast<const uint4*>(src + k);
+    r = *reinterpret_cast<const u32x4*>(src + k);
     return r;
   }
   uint32_t w[4] = {0u, 0u, 0u, 0u};
@@ -89,17 +93,17 @@ __device__ __forceinline__ uint4 load16_rowmajor(const T* __restrict__ X, int64_
       w[e] = bits;
     }
   }
-  r.x = w[0];
-  r.y = w[1];
-  r.z = w[2];
-  r.w = w[3];
+  r[0] = w[0];
+  r[1] = w[1];
+  r[2] = w[2];
+  r[3] = w[3];
   return r;
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // D += A * B on one 32x32 output block, K = 16 (bf16 inputs).
-__device__ __forceinline__ f32x16 mfma32_bf16(uint4 a, uint4 b, f32x16 c) {
+__device__ __forceinline__ f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 // D += A * B on one 32x32 output block, K = 2 (fp32 inputs, one per lane).

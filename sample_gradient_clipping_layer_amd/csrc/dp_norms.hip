@@ -22,10 +22,10 @@ __device__ __forceinline__ float row_sqsum(const T* __restrict__ row, int64_t n,
   float s0 = 0.f, s1 = 0.f;
   const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
   int64_t nv = vec ? (n / P) : 0;
-  const uint4* rv = reinterpret_cast<const uint4*>(row);
+  const u32x4* rv = reinterpret_cast<const u32x4*>(row);
   for (int64_t q = lane; q < nv; q += kWave) {
-    const uint4 v = rv[q];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const u32x4 v = rv[q];
+    const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if constexpr (P == 8) {
@@ -88,7 +88,7 @@ struct GhostCfg {
   static constexpr int PPT = PIECES / NT;
   static_assert(PIECES % NT == 0, "tile/threads mismatch");
   struct Regs {
-    uint4 v[PPT];
+    u32x4 v[PPT];
   };
 };
 
@@ -104,7 +104,7 @@ __device__ __forceinline__ void ghost_load(typename GhostCfg<T, TS>::Regs& regs,
     const int row = (q / Cfg::V) % TS;
     const int c16 = q % Cfg::V;
     if (diag && h == 1) {
-      regs.v[r] = make_uint4(0u, 0u, 0u, 0u);
+      regs.v[r] = u32x4{0u, 0u, 0u, 0u};
     } else {
       const int64_t grow = (int64_t)(h == 0 ? sb : tb) * TS + row;
       regs.v[r] = load16_rowmajor(Xi, Tn, K, grow, chunk * Cfg::KC + c16 * Cfg::P, vec);
@@ -121,7 +121,7 @@ __device__ __forceinline__ void ghost_store(const typename GhostCfg<T, TS>::Regs
     const int h = q / (TS * Cfg::V);
     const int row = (q / Cfg::V) % TS;
     const int c16 = q % Cfg::V;
-    if (!(diag && h == 1)) *reinterpret_cast<uint4*>(buf + (h * TS + row) * Cfg::ROWB + c16 * 16) = regs.v[r];
+    if (!(diag && h == 1)) *reinterpret_cast<u32x4*>(buf + (h * TS + row) * Cfg::ROWB + c16 * 16) = regs.v[r];
   }
 }
 
@@ -137,16 +137,16 @@ __device__ __forceinline__ void ghost_compute(const unsigned char* buf, bool dia
   if constexpr (Cfg::P == 8) {
 #pragma unroll
     for (int ks = 0; ks < Cfg::KC / 16; ++ks) {
-      uint4 a[NB], b[NB];
+      u32x4 a[NB], b[NB];
 #pragma unroll
       for (int bi = 0; bi < NB; ++bi) {
         const int row = wm * Cfg::WM + bi * 32 + (lane & 31);
-        a[bi] = *reinterpret_cast<const uint4*>(sbase + row * Cfg::ROWB + ks * 32 + (lane >> 5) * 16);
+        a[bi] = *reinterpret_cast<const u32x4*>(sbase + row * Cfg::ROWB + ks * 32 + (lane >> 5) * 16);
       }
 #pragma unroll
       for (int bj = 0; bj < NB; ++bj) {
         const int row = wn * Cfg::WM + bj * 32 + (lane & 31);
-        b[bj] = *reinterpret_cast<const uint4*>(tbase + row * Cfg::ROWB + ks * 32 + (lane >> 5) * 16);
+        b[bj] = *reinterpret_cast<const u32x4*>(tbase + row * Cfg::ROWB + ks * 32 + (lane >> 5) * 16);
       }
 #pragma unroll
       for (int bi = 0; bi < NB; ++bi)
@@ -179,6 +179,75 @@ __device__ __forceinline__ void ghost_compute(const unsigned char* buf, bool dia
     }
   }
 }
+
+// Unchecked pipeline for interior tiles: both row blocks inside the sample
+// and d, p multiples of the chunk. Chunk c < nA comes from A_i (Gram of A),
+// the rest from G_i. Two named register stages keep the loads of chunks c+1
+// and c+2 in flight (the last loads re-read the final chunk: a clamped index
+// keeps the body straight-line). Piece slot r of a thread belongs to row
+// block r / PPB (a compile-time constant), so diagonal tiles skip the second
+// block's slots without divergence.
+template <typename T, int TS, bool DIAG>
+struct GhostFull {
+  using Cfg = GhostCfg<T, TS>;
+  static constexpr int PPB = Cfg::PPT / 2;             // pieces per thread per row block
+  static constexpr int NPS = DIAG ? PPB : Cfg::PPT;    // piece slots in use (one block if diagonal)
+
+  // slot r of this thread: row block r / PPB, piece pb = tid + (r % PPB) * NT
+  __device__ __forceinline__ static void load(typename Cfg::Regs& R, const T* base, int64_t K, int64_t k0, int sb,
+                                              int tb) {
+#pragma unroll
+    for (int r = 0; r < NPS; ++r) {
+      const int pb = (int)threadIdx.x + (r % PPB) * Cfg::NT;
+      const int64_t row = (int64_t)((r / PPB) == 0 ? sb : tb) * TS + pb / Cfg::V;
+      R.v[r] = *reinterpret_cast<const u32x4*>(base + row * K + k0 + (pb % Cfg::V) * Cfg::P);
+    }
+  }
+  __device__ __forceinline__ static void store(const typename Cfg::Regs& R, unsigned char* buf) {
+#pragma unroll
+    for (int r = 0; r < NPS; ++r) {
+      const int pb = (int)threadIdx.x + (r % PPB) * Cfg::NT;
+      *reinterpret_cast<u32x4*>(buf + ((r / PPB) * TS + pb / Cfg::V) * Cfg::ROWB + (pb % Cfg::V) * 16) = R.v[r];
+    }
+  }
+  __device__ __forceinline__ static void load_chunk(typename Cfg::Regs& R, const T* Ai, const T* Gi, int64_t d,
+                                                    int64_t p, int64_t nA, int64_t c, int sb, int tb) {
+    const bool isA = c < nA;
+    load(R, isA ? Ai : Gi, isA ? d : p, (isA ? c : c - nA) * Cfg::KC, sb, tb);
+  }
+  __device__ __forceinline__ static void step(typename Cfg::Regs& R, unsigned char* buf, const T* Ai, const T* Gi,
+                                              int64_t d, int64_t p, int64_t nA, int64_t c, int64_t last, int sb,
+                                              int tb, f32x16 (&acc_a)[Cfg::NB][Cfg::NB],
+                                              f32x16 (&acc_g)[Cfg::NB][Cfg::NB]) {
+    store(R, buf);
+    __syncthreads();
+    load_chunk(R, Ai, Gi, d, p, nA, c + 2 <= last ? c + 2 : last, sb, tb);
+    if (c < nA)
+      ghost_compute<T, TS>(buf, DIAG, acc_a);
+    else
+      ghost_compute<T, TS>(buf, DIAG, acc_g);
+  }
+  // Unchecked pipeline for interior tiles: both row blocks inside the sample
+  // and d, p multiples of the chunk. Chunk c < nA comes from A_i (Gram of
+  // A), the rest from G_i. Two register stages keep the loads of chunks c+1
+  // and c+2 in flight (the last loads re-read the final chunk: a clamped
+  // index keeps the body straight-line).
+  __device__ __forceinline__ static void run(const T* Ai, const T* Gi, int64_t d, int64_t p, int sb, int tb,
+                                             unsigned char* lds, f32x16 (&acc_a)[Cfg::NB][Cfg::NB],
+                                             f32x16 (&acc_g)[Cfg::NB][Cfg::NB]) {
+    const int64_t nA = d / Cfg::KC, n = nA + p / Cfg::KC;
+    const int64_t last = n - 1;
+    typename Cfg::Regs R0, R1;
+    load_chunk(R0, Ai, Gi, d, p, nA, 0, sb, tb);
+    load_chunk(R1, Ai, Gi, d, p, nA, 1 <= last ? 1 : last, sb, tb);
+    int64_t c = 0;
+    for (; c + 1 <= last; c += 2) {
+      step(R0, lds, Ai, Gi, d, p, nA, c, last, sb, tb, acc_a, acc_g);
+      step(R1, lds + Cfg::BUF, Ai, Gi, d, p, nA, c + 1, last, sb, tb, acc_a, acc_g);
+    }
+    if (c == last) step(R0, lds, Ai, Gi, d, p, nA, c, last, sb, tb, acc_a, acc_g);
+  }
+};
 
 template <typename T, int TS>
 __global__ __launch_bounds__(256) void k_ghost_tiles(const T* __restrict__ A, const T* __restrict__ G, int64_t B,
@@ -214,6 +283,12 @@ __global__ __launch_bounds__(256) void k_ghost_tiles(const T* __restrict__ A, co
 
   const T* Ai = A + i * Tn * d;
   const T* Gi = G + i * Tn * p;
+  const bool full = vecA && vecG && (int64_t)(tb + 1) * TS <= Tn && d % Cfg::KC == 0 && p % Cfg::KC == 0;
+  if (full && sb == tb) {
+    GhostFull<T, TS, true>::run(Ai, Gi, d, p, sb, tb, lds, acc_a, acc_g);
+  } else if (full) {
+    GhostFull<T, TS, false>::run(Ai, Gi, d, p, sb, tb, lds, acc_a, acc_g);
+  } else {
   const int64_t nA = (d + Cfg::KC - 1) / Cfg::KC;
   const int64_t nG = (p + Cfg::KC - 1) / Cfg::KC;
   const int64_t n = nA + nG;
@@ -232,6 +307,7 @@ __global__ __launch_bounds__(256) void k_ghost_tiles(const T* __restrict__ A, co
       ghost_compute<T, TS>(buf, diag, acc_a);
     else
       ghost_compute<T, TS>(buf, diag, acc_g);
+  }
   }
 
   const float one = has_bias ? 1.0f : 0.0f;

@@ -74,7 +74,7 @@ struct Xty {
   typedef f32x16 AccT[NBM][NBN];
 
   struct Regs {
-    uint4 v[UPT][RU];
+    u32x4 v[UPT][RU];
   };
 
   // Unit u of an operand -> (row group rr, 16-byte column vector cc). The map
@@ -90,43 +90,71 @@ struct Xty {
     }
   }
 
-  // Load one chunk into registers. x_full/y_full: the whole tile width is
-  // inside the matrix and rows are 16-byte aligned (no per-element checks).
+  // Load one chunk into registers. FULL: every chunk row is valid, the whole
+  // tile width is inside both matrices and rows are 16-byte aligned, so the
+  // loads need no checks (and the compiled loop has no per-element fallback).
+  template <bool FULL>
   __device__ __forceinline__ static void load(Regs& R, const ChunkSrc<T>& cs, int64_t Kx, int64_t Ky, int64_t m0,
-                                              int64_t n0, bool x_full, bool y_full, bool vecx, bool vecy,
-                                              int64_t ones_col) {
+                                              int64_t n0, bool vecx, bool vecy, int64_t ones_col) {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int unit = threadIdx.x + u * NT;
-      if (unit >= UT) continue;
+      if (UT % NT != 0 && unit >= UT) continue;
       const bool isx = unit < UX;
       int rr, cc;
       unit_rc(isx ? unit : unit - UX, &rr, &cc);
       const T* base = isx ? cs.xp : cs.yp;
       const int64_t K = isx ? Kx : Ky;
       const int64_t col = (isx ? m0 : n0) + cc * P;
-      const bool full = (isx ? x_full : y_full) && cs.rv == KC;
-      if (full) {
+      if constexpr (FULL) {
         const T* src = base + (int64_t)(rr * RU) * K + col;
 #pragma unroll
-        for (int r = 0; r < RU; ++r) R.v[u][r] = *reinterpret_cast<const uint4*>(src + (int64_t)r * K);
+        for (int r = 0; r < RU; ++r) R.v[u][r] = *reinterpret_cast<const u32x4*>(src + (int64_t)r * K);
       } else {
 #pragma unroll
         for (int r = 0; r < RU; ++r) {
           const int row = rr * RU + r;
-          uint4 v = load16_rowmajor(base, (int64_t)cs.rv, K, (int64_t)row, col, isx ? vecx : vecy);
+          u32x4 v = load16_rowmajor(base, (int64_t)cs.rv, K, (int64_t)row, col, isx ? vecx : vecy);
           if (isx && ones_col >= col && ones_col < col + P && row < cs.rv) {
             const int e = (int)(ones_col - col);
-            uint32_t w[4] = {v.x, v.y, v.z, v.w};
             if constexpr (P == 8)
-              w[e >> 1] |= 0x3F80u << (16 * (e & 1));
+              v[e >> 1] |= 0x3F80u << (16 * (e & 1));
             else
-              w[e] = 0x3F800000u;
-            v = make_uint4(w[0], w[1], w[2], w[3]);
+              v[e] = 0x3F800000u;
           }
           R.v[u][r] = v;
         }
       }
+    }
+  }
+
+  // Per-thread byte-free element offsets of its staging units inside a chunk
+  // (row group rr, column vector cc), for the unchecked loads of kloop_full.
+  struct Offs {
+    int64_t off[UPT];
+    bool isx[UPT];
+  };
+  __device__ __forceinline__ static void full_offsets(Offs& O, int64_t Kx, int64_t Ky, int64_t m0, int64_t n0) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int unit = threadIdx.x + u * NT;
+      const bool isx = unit < UX;
+      int rr, cc;
+      unit_rc(isx ? unit : unit - UX, &rr, &cc);
+      O.isx[u] = isx;
+      O.off[u] = isx ? (int64_t)(rr * RU) * Kx + m0 + cc * P : (int64_t)(rr * RU) * Ky + n0 + cc * P;
+    }
+  }
+  // Unchecked loads of chunk q: rows [q*KC, q*KC + KC) of X = A and Y = G.
+  __device__ __forceinline__ static void load_full(Regs& R, const Offs& O, const T* A, const T* G, int64_t Kx,
+                                                   int64_t Ky, int64_t q) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      if (UT % NT != 0 && threadIdx.x + u * NT >= UT) continue;
+      const int64_t K = O.isx[u] ? Kx : Ky;
+      const T* src = (O.isx[u] ? A : G) + q * (int64_t)KC * K + O.off[u];
+#pragma unroll
+      for (int r = 0; r < RU; ++r) R.v[u][r] = *reinterpret_cast<const u32x4*>(src + (int64_t)r * K);
     }
   }
 
@@ -137,7 +165,7 @@ struct Xty {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int unit = threadIdx.x + u * NT;
-      if (unit >= UT) continue;
+      if (UT % NT != 0 && unit >= UT) continue;
       const bool isx = unit < UX;
       int rr, cc;
       unit_rc(isx ? unit : unit - UX, &rr, &cc);
@@ -151,35 +179,39 @@ struct Xty {
             sc[r] = row < cs.rv ? c[(cs.r0 + row) / Tn] : 0.0f;
           }
         }
-        const uint4* v = R.v[u];
+        const u32x4* v = R.v[u];
         *reinterpret_cast<float4*>(dst + 0 * kRowB) = make_float4(__uint_as_float(v[0].x) * sc[0], __uint_as_float(v[1].x) * sc[1], __uint_as_float(v[2].x) * sc[2], __uint_as_float(v[3].x) * sc[3]);
         *reinterpret_cast<float4*>(dst + 1 * kRowB) = make_float4(__uint_as_float(v[0].y) * sc[0], __uint_as_float(v[1].y) * sc[1], __uint_as_float(v[2].y) * sc[2], __uint_as_float(v[3].y) * sc[3]);
         *reinterpret_cast<float4*>(dst + 2 * kRowB) = make_float4(__uint_as_float(v[0].z) * sc[0], __uint_as_float(v[1].z) * sc[1], __uint_as_float(v[2].z) * sc[2], __uint_as_float(v[3].z) * sc[3]);
         *reinterpret_cast<float4*>(dst + 3 * kRowB) = make_float4(__uint_as_float(v[0].w) * sc[0], __uint_as_float(v[1].w) * sc[1], __uint_as_float(v[2].w) * sc[2], __uint_as_float(v[3].w) * sc[3]);
       } else {
         // 8 x 8 bf16 transpose: out[m] packs rows (2kp, 2kp+1) of column m
-        const uint4* v = R.v[u];
+        const u32x4* v = R.v[u];
 #pragma unroll
         for (int mp = 0; mp < 4; ++mp) {  // column pair (2mp, 2mp+1) lives in dword mp of every row
           uint32_t w[8];
 #pragma unroll
-          for (int r = 0; r < 8; ++r) w[r] = mp == 0 ? v[r].x : mp == 1 ? v[r].y : mp == 2 ? v[r].z : v[r].w;
-          uint4 even, odd;
-          even.x = (w[0] & 0xFFFFu) | (w[1] << 16);
-          even.y = (w[2] & 0xFFFFu) | (w[3] << 16);
-          even.z = (w[4] & 0xFFFFu) | (w[5] << 16);
-          even.w = (w[6] & 0xFFFFu) | (w[7] << 16);
-          odd.x = (w[0] >> 16) | (w[1] & 0xFFFF0000u);
-          odd.y = (w[2] >> 16) | (w[3] & 0xFFFF0000u);
-          odd.z = (w[4] >> 16) | (w[5] & 0xFFFF0000u);
-          odd.w = (w[6] >> 16) | (w[7] & 0xFFFF0000u);
-          *reinterpret_cast<uint4*>(dst + (2 * mp) * kRowB) = even;
-          *reinterpret_cast<uint4*>(dst + (2 * mp + 1) * kRowB) = odd;
+          for (int r = 0; r < 8; ++r) w[r] = v[r][mp];
+          // byte permutes: even = low halves of rows (2kp, 2kp+1), odd = high halves
+          u32x4 even, odd;
+          even[0] = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
+          even[1] = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
+          even[2] = __builtin_amdgcn_perm(w[5], w[4], 0x05040100u);
+          even[3] = __builtin_amdgcn_perm(w[7], w[6], 0x05040100u);
+          odd[0] = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
+          odd[1] = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
+          odd[2] = __builtin_amdgcn_perm(w[5], w[4], 0x07060302u);
+          odd[3] = __builtin_amdgcn_perm(w[7], w[6], 0x07060302u);
+          *reinterpret_cast<u32x4*>(dst + (2 * mp) * kRowB) = even;
+          *reinterpret_cast<u32x4*>(dst + (2 * mp + 1) * kRowB) = odd;
         }
       }
     }
   }
 
+  // acc += X^T Y of the chunk in buf. FRESH: acc is overwritten (the first
+  // MFMA of each block starts from zero instead of acc).
+  template <bool FRESH = false>
   __device__ __forceinline__ static void compute(const unsigned char* buf, AccT& acc) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
@@ -188,17 +220,25 @@ struct Xty {
     if constexpr (P == 8) {
 #pragma unroll
       for (int ks = 0; ks < KC / 16; ++ks) {
-        uint4 a[NBM], b[NBN];
+        u32x4 a[NBM], b[NBN];
 #pragma unroll
-        for (int bi = 0; bi < NBM; ++bi) a[bi] = *reinterpret_cast<const uint4*>(xb + bi * 32 * kRowB + ks * 32);
+        for (int bi = 0; bi < NBM; ++bi) a[bi] = *reinterpret_cast<const u32x4*>(xb + bi * 32 * kRowB + ks * 32);
 #pragma unroll
-        for (int bj = 0; bj < NBN; ++bj) b[bj] = *reinterpret_cast<const uint4*>(yb + bj * 32 * kRowB + ks * 32);
+        for (int bj = 0; bj < NBN; ++bj) b[bj] = *reinterpret_cast<const u32x4*>(yb + bj * 32 * kRowB + ks * 32);
 #pragma unroll
         for (int bi = 0; bi < NBM; ++bi)
 #pragma unroll
-          for (int bj = 0; bj < NBN; ++bj) acc[bi][bj] = mfma32_bf16(a[bi], b[bj], acc[bi][bj]);
+          for (int bj = 0; bj < NBN; ++bj) {
+            if (FRESH && ks == 0) {
+              const f32x16 zero = {};
+              acc[bi][bj] = mfma32_bf16(a[bi], b[bj], zero);
+            } else {
+              acc[bi][bj] = mfma32_bf16(a[bi], b[bj], acc[bi][bj]);
+            }
+          }
       }
     } else {
+      static_assert(!FRESH, "fp32 path accumulates directly");
 #pragma unroll
       for (int g = 0; g < KC / 8; ++g) {
         float4 a[NBM], b[NBN];
@@ -229,6 +269,171 @@ struct Xty {
   }
 };
 
+// ---------------------------------------------------------------- K loops
+// Software pipeline with prefetch distance 2: chunk q is stored from register
+// stage q&1 into LDS buffer q&1, then (after one barrier) the global loads of
+// chunk q+2 are issued into the freed register stage while the MFMAs of chunk
+// q run; the loads of chunk q+1 are in flight too. One barrier per chunk
+// suffices with two LDS buffers: a wave reaching the store of chunk q+1 has
+// passed the barrier of chunk q, so every wave has finished chunk q-1.
+//
+// Desc(q) returns the ChunkSrc of chunk q; Epi(q, acc-kind) is called after
+// the MFMAs of chunk q (per-sample scaling for bf16).
+template <typename T, int BM, int BN, bool FULL, bool PER_SAMPLE, typename Desc>
+__device__ __forceinline__ void kloop(typename Xty<T, BM, BN>::AccT& acc, unsigned char* lds, int64_t nq, Desc desc,
+                                      int cps, const float* cs_sample, int64_t d, int64_t p, int64_t m0, int64_t n0,
+                                      bool vecA, bool vecG, int64_t ones_col, const float* c_rows, int64_t Tn) {
+  using E = Xty<T, BM, BN>;
+  if (nq <= 0) return;
+  typename E::Regs R[2];
+  ChunkSrc<T> cs[2];
+  cs[0] = desc(0);
+  E::template load<FULL>(R[0], cs[0], d, p, m0, n0, vecA, vecG, ones_col);
+  if (nq > 1) {
+    cs[1] = desc(1);
+    E::template load<FULL>(R[1], cs[1], d, p, m0, n0, vecA, vecG, ones_col);
+  }
+  typename E::AccT tmp;
+  if constexpr (!PER_SAMPLE) (void)tmp;
+  for (int64_t q0 = 0; q0 < nq; q0 += 2) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int64_t q = q0 + st;
+      if (q < nq) {
+        unsigned char* buf = lds + st * E::BUF;
+        E::store(R[st], buf, cs[st], c_rows, Tn);
+        __syncthreads();
+        if (q + 2 < nq) {
+          cs[st] = desc(q + 2);
+          E::template load<FULL>(R[st], cs[st], d, p, m0, n0, vecA, vecG, ones_col);
+        }
+        if constexpr (PER_SAMPLE) {
+          const int ch = (int)(q % cps);
+          if (ch == 0)
+            E::template compute<true>(buf, tmp);
+          else
+            E::template compute<false>(buf, tmp);
+          if (ch == cps - 1) {
+            const float ci = cs_sample[q / cps];
+#pragma unroll
+            for (int bi = 0; bi < E::NBM; ++bi)
+#pragma unroll
+              for (int bj = 0; bj < E::NBN; ++bj)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) acc[bi][bj][j] += ci * tmp[bi][bj][j];
+          }
+        } else {
+          E::template compute<false>(buf, acc);
+        }
+      }
+    }
+  }
+}
+
+// Pipeline for the common case: every chunk is KC full rows of the flattened
+// [B*T] row space and the whole tile is inside both matrices, so chunk q is
+// simply rows [q*KC, q*KC + KC) and the loads need no checks. Two named
+// register stages keep the loads of chunks q+1 and q+2 in flight; the loads
+// of the last two iterations re-read the final chunk (clamped index) so the
+// loop body stays straight-line. PER_SAMPLE (bf16, T % KC == 0): chunks never
+// straddle samples; each sample's chunks go to tmp, then acc += c_i * tmp.
+// fp32: G rows are scaled by c[row / T] while staging.
+template <typename T, int BM, int BN, bool PER_SAMPLE>
+__device__ __forceinline__ void kloop_full(typename Xty<T, BM, BN>::AccT& acc, unsigned char* lds, const T* A,
+                                           const T* G, const float* c, int64_t q0, int64_t nq, int64_t Tn,
+                                           int64_t d, int64_t p, int64_t m0, int64_t n0) {
+  using E = Xty<T, BM, BN>;
+  if (nq <= 0) return;
+  typename E::Offs O;
+  E::full_offsets(O, d, p, m0, n0);
+  const int64_t qlast = q0 + nq - 1;
+  typename E::Regs R0, R1;
+  E::load_full(R0, O, A, G, d, p, q0);
+  E::load_full(R1, O, A, G, d, p, q0 + 1 <= qlast ? q0 + 1 : qlast);
+  typename E::AccT tmp;
+  const int cps = (int)(Tn / E::KC);             // chunks per sample (PER_SAMPLE)
+  int ch = PER_SAMPLE ? (int)(q0 % cps) : 0;     // chunk index inside its sample
+  int64_t sample = PER_SAMPLE ? q0 / cps : 0;
+  unsigned char* buf0 = lds;
+  unsigned char* buf1 = lds + E::BUF;
+
+  auto run = [&](typename E::Regs& R, unsigned char* buf, int64_t q) {
+    ChunkSrc<T> cs;
+    cs.rv = E::KC;
+    cs.r0 = q * E::KC;
+    E::store(R, buf, cs, PER_SAMPLE ? nullptr : c, Tn);
+    __syncthreads();
+    const int64_t qn = q + 2 <= qlast ? q + 2 : qlast;
+    E::load_full(R, O, A, G, d, p, qn);
+    if constexpr (PER_SAMPLE) {
+      if (ch == 0)
+        E::template compute<true>(buf, tmp);
+      else
+        E::template compute<false>(buf, tmp);
+      if (ch == cps - 1) {
+        const float ci = c[sample];
+#pragma unroll
+        for (int bi = 0; bi < E::NBM; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < E::NBN; ++bj)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[bi][bj][j] += ci * tmp[bi][bj][j];
+        ch = 0;
+        ++sample;
+      } else {
+        ++ch;
+      }
+    } else {
+      E::template compute<false>(buf, acc);
+    }
+  };
+
+  int64_t q = q0;
+  for (; q + 1 <= qlast; q += 2) {
+    run(R0, buf0, q);
+    run(R1, buf1, q + 1);
+  }
+  if (q == qlast) run(R0, buf0, q);
+}
+
+// Chunk q of a row range [q*KC, ...) of nrows rows starting at X/Y.
+template <typename T, int KC>
+struct RowDesc {
+  const T* X;
+  const T* Y;
+  int64_t nrows, d, p, q_base;
+  __device__ __forceinline__ ChunkSrc<T> operator()(int64_t q) const {
+    ChunkSrc<T> cs;
+    cs.r0 = (q + q_base) * KC;
+    cs.xp = X + cs.r0 * d;
+    cs.yp = Y + cs.r0 * p;
+    const int64_t left = nrows - cs.r0;
+    cs.rv = (int)(left < KC ? left : KC);
+    return cs;
+  }
+};
+
+// Chunk q of samples i0.. : sample i0 + q / cps, chunk q % cps of that sample.
+template <typename T, int KC>
+struct SampleDesc {
+  const T* A;
+  const T* G;
+  int64_t Tn, d, p, i0;
+  int cps;
+  __device__ __forceinline__ ChunkSrc<T> operator()(int64_t q) const {
+    ChunkSrc<T> cs;
+    const int64_t i = i0 + q / cps;
+    const int ch = (int)(q % cps);
+    const int64_t row = i * Tn + (int64_t)ch * KC;
+    cs.xp = A + row * d;
+    cs.yp = G + row * p;
+    const int64_t left = Tn - (int64_t)ch * KC;
+    cs.rv = (int)(left < KC ? left : KC);
+    cs.r0 = row;
+    return cs;
+  }
+};
+
 // ---------------------------------------------------------------- explicit
 template <typename T, int BM, int BN>
 __global__ __launch_bounds__(256, 2) void k_explicit_tiles(const T* __restrict__ A, const T* __restrict__ G,
@@ -244,37 +449,17 @@ __global__ __launch_bounds__(256, 2) void k_explicit_tiles(const T* __restrict__
   if (i >= B) return;
   const int64_t m0 = (tile / nt) * BM;
   const int64_t n0 = (tile % nt) * BN;
-  const T* Xi = A + i * Tn * d;
-  const T* Yi = G + i * Tn * p;
   const int64_t ones_col = has_bias ? d : -1;
-
+  const bool full = vecA && vecG && (m0 + BM <= d) && (n0 + BN <= p) && (Tn % E::KC == 0);
+  const int64_t nq = (Tn + E::KC - 1) / E::KC;
   typename E::AccT acc;
   E::zero(acc);
-  typename E::Regs R;
-  const bool x_full = vecA && (m0 + BM <= d);
-  const bool y_full = vecG && (n0 + BN <= p);
-  const int64_t nq = (Tn + E::KC - 1) / E::KC;
-  auto src = [&](int64_t q) {
-    ChunkSrc<T> cs;
-    cs.xp = Xi + q * E::KC * d;
-    cs.yp = Yi + q * E::KC * p;
-    const int64_t left = Tn - q * E::KC;
-    cs.rv = (int)(left < E::KC ? left : E::KC);
-    cs.r0 = 0;
-    return cs;
-  };
-  ChunkSrc<T> cs = src(0);
-  E::load(R, cs, d, p, m0, n0, x_full, y_full, vecA != 0, vecG != 0, ones_col);
-  for (int64_t q = 0; q < nq; ++q) {
-    unsigned char* buf = lds + (q & 1) * E::BUF;
-    E::store(R, buf, cs, nullptr, Tn);
-    __syncthreads();
-    if (q + 1 < nq) {
-      cs = src(q + 1);
-      E::load(R, cs, d, p, m0, n0, x_full, y_full, vecA != 0, vecG != 0, ones_col);
-    }
-    E::compute(buf, acc);
-  }
+  const RowDesc<T, E::KC> desc{A + i * Tn * d, G + i * Tn * p, Tn, d, p, 0};
+  if (full)
+    kloop_full<T, BM, BN, false>(acc, lds, A + i * Tn * d, G + i * Tn * p, nullptr, 0, nq, Tn, d, p, m0, n0);
+  else
+    kloop<T, BM, BN, false, false>(acc, lds, nq, desc, 1, nullptr, d, p, m0, n0, vecA != 0, vecG != 0, ones_col,
+                                   nullptr, Tn);
   float s = 0.f;
 #pragma unroll
   for (int bi = 0; bi < E::NBM; ++bi)
@@ -292,10 +477,18 @@ struct NoiseArgs {
   uint32_t k0, k1, layer, step;
 };
 
+// Workgroups per CU the register budget is sized for: the bf16 128x128 tile
+// carries a second accumulator set (per-sample exact scaling), so it runs one
+// workgroup per CU with the full register file; the others run two.
+template <typename T, int BM, int BN>
+struct ContractOcc {
+  static constexpr int value = (elem_traits<T>::per16 == 8 && BM == 128 && BN == 128) ? 1 : 2;
+};
+
 // Workgroup = (output tile, K split). FUSED (one split): out and bias_out get
 // (S + sc*z) * (1/denom) directly. Otherwise ws[split][m][n] (m < d + has_bias).
 template <typename T, int BM, int BN, bool FUSED>
-__global__ __launch_bounds__(256, 2) void k_contract_tiles(const T* __restrict__ A, const T* __restrict__ G,
+__global__ __launch_bounds__(256, (ContractOcc<T, BM, BN>::value)) void k_contract_tiles(const T* __restrict__ A, const T* __restrict__ G,
                                                            const float* __restrict__ c, int64_t B, int64_t Tn,
                                                            int64_t d, int64_t p, int has_bias, int mt, int nt,
                                                            int64_t units_per_split, int vecA, int vecG,
@@ -310,89 +503,34 @@ __global__ __launch_bounds__(256, 2) void k_contract_tiles(const T* __restrict__
   const int64_t n0 = (tile % nt) * BN;
   const int64_t ones_col = has_bias ? d : -1;
   const int64_t mrows = d + (has_bias ? 1 : 0);
+  const bool wide = vecA && vecG && (m0 + BM <= d) && (n0 + BN <= p);
 
   typename E::AccT acc;
   E::zero(acc);
-  typename E::Regs R;
-  const bool x_full = vecA && (m0 + BM <= d);
-  const bool y_full = vecG && (n0 + BN <= p);
   if constexpr (E::P == 4) {
     // flat K over all B*T rows in chunks of KC rows; G rows scaled by c[row / T]
     const int64_t nrows = B * Tn;
     const int64_t nunits = (nrows + E::KC - 1) / E::KC;
     const int64_t u0 = split * units_per_split;
     const int64_t u1 = u0 + units_per_split < nunits ? u0 + units_per_split : nunits;
-    auto src = [&](int64_t u) {
-      ChunkSrc<T> cs;
-      cs.r0 = u * E::KC;
-      cs.xp = A + cs.r0 * d;
-      cs.yp = G + cs.r0 * p;
-      const int64_t left = nrows - cs.r0;
-      cs.rv = (int)(left < E::KC ? left : E::KC);
-      return cs;
-    };
-    ChunkSrc<T> cs = src(u0);
-    if (u0 < u1) E::load(R, cs, d, p, m0, n0, x_full, y_full, vecA != 0, vecG != 0, ones_col);
-    for (int64_t u = u0; u < u1; ++u) {
-      unsigned char* buf = lds + ((u - u0) & 1) * E::BUF;
-      E::store(R, buf, cs, c, Tn);
-      __syncthreads();
-      if (u + 1 < u1) {
-        cs = src(u + 1);
-        E::load(R, cs, d, p, m0, n0, x_full, y_full, vecA != 0, vecG != 0, ones_col);
-      }
-      E::compute(buf, acc);
-    }
+    const RowDesc<T, E::KC> desc{A, G, nrows, d, p, u0};
+    const int64_t nq = u1 > u0 ? u1 - u0 : 0;
+    if (wide && (u1 < nunits || nrows % E::KC == 0))
+      kloop_full<T, BM, BN, false>(acc, lds, A, G, c, u0, nq, Tn, d, p, m0, n0);
+    else
+      kloop<T, BM, BN, false, false>(acc, lds, nq, desc, 1, nullptr, d, p, m0, n0, vecA != 0, vecG != 0, ones_col,
+                                     c, Tn);
   } else {
-    // per-sample exact accumulation: acc += c_i * (A_i^T G_i tile)
     const int64_t i0 = split * units_per_split;
     const int64_t i1 = i0 + units_per_split < B ? i0 + units_per_split : B;
-    const int cps = (int)((Tn + E::KC - 1) / E::KC);  // chunks per sample
-    typename E::AccT tmp;
-    E::zero(tmp);
-    auto src = [&](int64_t i, int ch) {
-      ChunkSrc<T> cs;
-      const int64_t row = i * Tn + (int64_t)ch * E::KC;
-      cs.xp = A + row * d;
-      cs.yp = G + row * p;
-      const int64_t left = Tn - (int64_t)ch * E::KC;
-      cs.rv = (int)(left < E::KC ? left : E::KC);
-      cs.r0 = row;
-      return cs;
-    };
-    int64_t i = i0;
-    int ch = 0;
-    ChunkSrc<T> cs = src(i, ch);
-    if (i0 < i1) E::load(R, cs, d, p, m0, n0, x_full, y_full, vecA != 0, vecG != 0, ones_col);
-    int64_t q = 0;
-    while (i < i1) {
-      unsigned char* buf = lds + (q & 1) * E::BUF;
-      E::store(R, buf, cs, nullptr, Tn);
-      __syncthreads();
-      const bool last = (ch == cps - 1);
-      const int64_t in = last ? i + 1 : i;
-      const int chn = last ? 0 : ch + 1;
-      if (in < i1) {
-        cs = src(in, chn);
-        E::load(R, cs, d, p, m0, n0, x_full, y_full, vecA != 0, vecG != 0, ones_col);
-      }
-      E::compute(buf, tmp);
-      if (last) {
-        const float ci = c[i];
-#pragma unroll
-        for (int bi = 0; bi < E::NBM; ++bi)
-#pragma unroll
-          for (int bj = 0; bj < E::NBN; ++bj)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              acc[bi][bj][j] += ci * tmp[bi][bj][j];
-              tmp[bi][bj][j] = 0.f;
-            }
-      }
-      i = in;
-      ch = chn;
-      ++q;
-    }
+    const int cps = (int)((Tn + E::KC - 1) / E::KC);
+    const SampleDesc<T, E::KC> desc{A, G, Tn, d, p, i0, cps};
+    const int64_t nq = i1 > i0 ? (i1 - i0) * cps : 0;
+    if (wide && Tn % E::KC == 0)
+      kloop_full<T, BM, BN, true>(acc, lds, A, G, c, i0 * cps, nq, Tn, d, p, m0, n0);
+    else
+      kloop<T, BM, BN, false, true>(acc, lds, nq, desc, cps, c + i0, d, p, m0, n0, vecA != 0, vecG != 0, ones_col,
+                                    nullptr, Tn);
   }
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -527,14 +665,36 @@ ContractPlan contract_plan(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t 
   pl.bn = pick_tile(p);
   pl.mt = (int)((mrows + pl.bm - 1) / pl.bm);
   pl.nt = (int)((p + pl.bn - 1) / pl.bn);
-  const int64_t kc = dtype == 1 ? XtyCfg<bf16s>::KC : XtyCfg<float>::KC;
-  const int64_t units = dtype == 1 ? B : (B * Tn + kc - 1) / kc;
+  const bool bf16 = dtype == 1;
+  const int64_t kc = bf16 ? XtyCfg<bf16s>::KC : XtyCfg<float>::KC;
+  // K units: whole samples (bf16, exact per-sample scaling) or KC-row chunks (fp32)
+  const int64_t units = bf16 ? B : (B * Tn + kc - 1) / kc;
+  const double rows_per_unit = bf16 ? (double)((Tn + kc - 1) / kc * kc) : (double)kc;
   const int64_t ntl = (int64_t)pl.mt * pl.nt;
-  // about two workgroups per CU (256 CUs); no split once the tiles alone fill most of the chip
-  int64_t ks = ntl >= 192 ? 1 : (512 + ntl - 1) / ntl;
-  if (ks > units) ks = units;
-  if (ks < 1) ks = 1;
-  pl.units_per_split = (units + ks - 1) / ks;
+  const int occ = (bf16 && pl.bm == 128 && pl.bn == 128) ? 1 : 2;
+  const int64_t slots = 256 * (int64_t)occ;  // 256 CUs
+  // cost model (seconds): MFMA rounds x per-split work on one CU, plus the
+  // split-K partial traffic (write + read of ks tiles) and a reduce launch
+  const double cu_rate = bf16 ? 4.0e12 : 0.27e12;  // sustained flop/s per CU at ~50% of peak
+  const double tile_unit_flops = 2.0 * pl.bm * pl.bn * rows_per_unit;
+  double best = 1e300;
+  int64_t best_ks = 1;
+  const int64_t ks_max = units < 1024 ? units : 1024;
+  for (int64_t ks = 1; ks <= ks_max; ++ks) {
+    const int64_t ups = (units + ks - 1) / ks;
+    const int64_t ks_eff = (units + ups - 1) / ups;
+    if (ks_eff != ks) continue;
+    const int64_t wgs = ntl * ks;
+    const double rounds = (double)((wgs + slots - 1) / slots);
+    const double t_mfma = rounds * (double)ups * tile_unit_flops / (cu_rate / occ);
+    const double t_red = ks > 1 ? (2.0 * ks + 1.0) * (double)mrows * (double)p * 4.0 / 5.0e12 + 4.0e-6 : 0.0;
+    const double t = t_mfma + t_red;
+    if (t < best * 0.999) {
+      best = t;
+      best_ks = ks;
+    }
+  }
+  pl.units_per_split = (units + best_ks - 1) / best_ks;
   pl.ks = (units + pl.units_per_split - 1) / pl.units_per_split;
   return pl;
 }
