@@ -30,6 +30,37 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 CACHE_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "sample_gradient_clipping_layer_amd", "csrc")
+
+
+def _csrc_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind, workload):
+    """HBM bytes per call of the dominant entry point, from the committed
+    FETCH_SIZE / WRITE_SIZE counter summary of this workload; None when there
+    is none or when the kernel sources changed after the counters were taken."""
+    name = {"sum": "clipped_sum", "norm": "ghost_norm"}[kind]
+    path = os.path.join(PROFILES, f"hbm_traffic_{name}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(("|", " ", "#")):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("csrc_sha256") != _csrc_sha256() or "traffic_bytes_per_call" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_call"])
 
 
 def _algorithmic(wl, T, d, p, kind):
@@ -147,6 +178,24 @@ def cpu_baseline(wl, budget_s=12.0):
                       f"materialised per-example gradients), {dt:.1f} s"}
 
 
+COPY_PROBE_BYTES = 256 << 20
+
+
+def copy_probe(reps=5):
+    """A plain copy of known size: reads and writes COPY_PROBE_BYTES per
+    launch. Profiling counters of this launch give the factor between a
+    counter's reading and the bytes that really moved."""
+    import torch
+    src = torch.full((COPY_PROBE_BYTES // 4,), 1.5, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    assert dst[-1].item() == 1.5
+    print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "launches": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,11 +204,16 @@ def main():
     ap.add_argument("--workload", default="gpt-block-t128", choices=W.WORKLOAD_ORDER)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="print per-call times to stderr")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 5 times (HBM counter calibration)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs the clipping path on a single MI355X "
               "(the multi-GPU design is described, not built). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if a.copy_probe:
+        copy_probe()
+        return
     wl = W.WORKLOADS[a.workload]
     wall, call_ms, shapes, n_sets = run_gpu(wl, a.steps, a.warmup)
     L = len(shapes)
@@ -174,6 +228,7 @@ def main():
         by_kind[kd] = by_kind.get(kd, 0.0) + mean_ms[j]
     dom = max(("norm", "sum"), key=lambda k: by_kind[k])
     flops = byts = t_ms = 0.0
+    ndom = 0
     for j, kd in enumerate(kinds):
         if kd != dom:
             continue
@@ -183,6 +238,7 @@ def main():
         flops += f
         byts += b
         t_ms += mean_ms[j]
+        ndom += 1
     if dom == "sum" or (wl.dtype == "bf16" and flops / byts > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3):
         peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
         achieved = flops / (t_ms * 1e-3) / 1e12
@@ -192,8 +248,12 @@ def main():
         achieved = byts / (t_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
-    roof["kernel"] = "dp_ghost_norm" if dom == "norm" else "dp_clipped_sum_noise"
-    roof["per_step_ms"] = round(t_ms, 4)
+    traffic = measured_traffic(dom, wl.name)
+    roof["traffic"] = None if traffic is None else round(traffic)
+    roof["algorithmic_bytes_per_call"] = round(byts / ndom)
+    roof["kernel"] = ("dp_ghost_norm: k_ghost_tiles + k_finalize_norm" if dom == "norm"
+                      else "dp_clipped_sum_noise: k_contract_tiles (+ k_reduce_noise when K is split)")
+    roof["avg_call_us"] = round(1e3 * t_ms / ndom, 2)
     if a.breakdown:
         names = [f"norm[{l}]" for l in range(L)] + ["clip"] + [f"sum[{l}]" for l in range(L)]
         for nm, m in zip(names, mean_ms):

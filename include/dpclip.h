@@ -113,8 +113,13 @@ dp_status dp_clip_factors(void* stream, const float* sqnorm, int64_t B, float C,
  * (re-weighted loss, Gaussian mechanism); SEDP eq. (2.1) and Sec. 3.2
  * (weighted gradient sum_i C_i g_i); DDP noisy aggregation.
  *
- *   out[m][n]   = (sum_b c[b] * sum_t A[b,t,m] G[b,t,n] + (sigma*C) * z_w[m][n]) / denom
- *   bias_out[n] = (sum_b c[b] * sum_t G[b,t,n]          + (sigma*C) * z_b[n])    / denom
+ *   out[m][n]   = (sum_b c[b] * sum_t A[b,t,m] G[b,t,n] + (sigma*C) * z_w[m][n]) * (1/denom)
+ *   bias_out[n] = (sum_b c[b] * sum_t G[b,t,n]          + (sigma*C) * z_b[n])    * (1/denom)
+ *
+ *  in fp32: the sum accumulates in fp32 (products of the input dtype),
+ *  sigma*C and 1/denom are each rounded to fp32 once, and the last two
+ *  operations are an fp32 add of fl(sigma*C)*z and a multiply by fl(1/denom)
+ *  (no division), so the noise term is reproducible bit for bit.
  *
  *  A, G, dtype, B, T, d, p  as in dp_ghost_norm.
  *  c        [B] fp32 device clip factors (any finite values).
