@@ -1,0 +1,388 @@
+// Weighted contraction S = A^T diag(c) G of a bf16 layer, direct-to-LDS engine.
+//
+// Computes the clipped sum of "Scaling up DP Deep Learning with Fast
+// Per-Example Gradient Clipping" (re-weighted loss) and "Scalable and
+// Efficient Training of Large CNNs with DP" eq. (2.1) / Sec. 3.2: the sum over
+// samples of c_i * A_i^T G_i as ONE contraction over K = B*T rows of the
+// flattened [B*T, d] and [B*T, p] views, plus the Gaussian noise and the mean
+// in the epilogue.
+//
+// Eligible layers: bf16, no bias row, T a multiple of 64 (a 64-row K chunk
+// never straddles two samples, so one clip factor covers a chunk), d and p
+// multiples of 8 (16-byte rows).
+//
+// gfx950 mapping:
+// - Operand chunks [64 k-rows x BM (or BN) features] go from HBM straight to
+//   LDS with 16-byte global_load_lds (no staging registers, no VALU), stored
+//   row-major [k][feature] with the 16-byte pieces of row r XOR-swizzled by
+//   4*(r % 4).
+// - MFMA 32x32x16 bf16 operands are read with ds_read_b64_tr_b16: within a
+//   16-lane group, the lane at (row k0+j, features f0+4a..f0+4a+3) supplies,
+//   and lane 4a+b receives feature f0+4a+b of rows k0..k0+3, i.e. the lane's
+//   half of an operand that holds 8 consecutive k of one feature. The swizzle
+//   puts the 4 rows x 64 bytes a half-wave reads on 64 distinct banks.
+// - The per-sample factor multiplies the operand with fewer 32-blocks per wave
+//   in fp32 and is rounded back to bf16 (RNE): the re-weighted operand c_i*G_i
+//   in the compute precision.
+// - STAGES LDS buffers: loads for chunk q+STAGES-1 are in flight while chunk q
+//   is computed; one barrier per chunk.
+// - Workgroups are mapped so that each XCD (blockIdx % 8) owns a contiguous
+//   range of (split, tile) work items, ordered with the shorter tile dimension
+//   fastest, so concurrently running workgroups of one XCD share operand tiles
+//   in its L2.
+#include "dp_common.hpp"
+#include "dp_launch.hpp"
+#include "dp_noise.hpp"
+
+namespace dpk {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_uchar;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int BM, int BN, int STAGES>
+struct DlCfg {
+  static constexpr int KC = 64;                 // K rows per chunk
+  static constexpr int RA = BM * 2, RG = BN * 2;  // LDS row bytes
+  static constexpr int A_BYTES = KC * RA, G_BYTES = KC * RG;
+  static constexpr int STAGE = A_BYTES + G_BYTES;
+  static constexpr int LDS = STAGES * STAGE;
+  static constexpr int WM = BM / 2, WN = BN / 2;  // 2 x 2 waves
+  static constexpr int NBM = WM / 32, NBN = WN / 32;
+  static constexpr int LA = A_BYTES / 4096;       // 1 KB loads per wave per chunk
+  static constexpr int LG = G_BYTES / 4096;
+  static constexpr int LPC = LA + LG;
+  static constexpr bool SCALE_G = NBN <= NBM;     // scale the operand with fewer blocks
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(LPC * (STAGES - 1) <= 63, "vmcnt range");
+};
+
+// s_waitcnt with vmcnt(n), expcnt and lgkmcnt left at their maxima (no wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8 bf16 values times s, rounded to bf16 (RNE).
+__device__ __forceinline__ u32x4 scale8(u32x4 v, float s) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(v[i] << 16) * s;
+    const float hi = __uint_as_float(v[i] & 0xFFFF0000u) * s;
+    r[i] = pack_bf16x2(lo, hi);
+  }
+  return r;
+}
+
+// One MFMA operand (8 consecutive k of one feature per lane) from a swizzled
+// stage: two transposing reads 4 rows apart.
+__device__ __forceinline__ u32x4 frag_tr(const unsigned char* base, int off, int four_rows) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off + four_rows));
+  u32x4 r;
+  r[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+  r[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+  r[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+  r[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+  return r;
+}
+
+struct DlArgs {
+  int64_t d, p;
+  int64_t cps;              // chunks per sample (T / 64)
+  int mt, nt;
+  int64_t ks;               // K splits
+  int64_t chunks_per_split;
+  int64_t nchunks;          // B * T / 64
+  int m_fast;               // work-item order: tile row index fastest
+  NoiseArgs na;
+};
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16*lane
+// (global_load_lds_dwordx4, base in M0). Written as asm so that the
+// compiler's wait insertion does not treat every later LDS read as aliasing
+// it: the pipeline orders these loads with explicit vmcnt waits + barriers.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_uchar*)p);
+}
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS reads
+// (lgkmcnt) but not for its global loads in flight (vmcnt), which the
+// pipeline waits for explicitly. The memory clobber keeps the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int BM, int BN, int STAGES, bool FUSED>
+__global__ __launch_bounds__(256, 1) void k_contract_dl(const bf16s* __restrict__ A, const bf16s* __restrict__ G,
+                                                       const float* __restrict__ c, float* __restrict__ ws,
+                                                       float* __restrict__ out, DlArgs a) {
+  using C = DlCfg<BM, BN, STAGES>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+
+  // ---- work item (XCD-contiguous)
+  const int64_t ntl = (int64_t)a.mt * a.nt;
+  const int64_t nitems = ntl * a.ks;
+  const int64_t per = (nitems + 7) / 8;
+  const int64_t w = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (w >= nitems) return;  // whole workgroup, before any barrier
+  const int64_t split = w / ntl;
+  const int64_t t = w - split * ntl;
+  const int tm = a.m_fast ? (int)(t % a.mt) : (int)(t / a.nt);
+  const int tn = a.m_fast ? (int)(t / a.mt) : (int)(t % a.nt);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t q0 = split * a.chunks_per_split;
+  const int64_t q1 = q0 + a.chunks_per_split < a.nchunks ? q0 + a.chunks_per_split : a.nchunks;
+  const int nq = (int)(q1 - q0);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // ---- per-lane global element offsets of this lane's 16-byte pieces within a chunk
+  int offA[C::LA], offG[C::LG];
+#pragma unroll
+  for (int i = 0; i < C::LA; ++i) {
+    const int byte = (wave + 4 * i) * 1024 + 16 * lane;
+    const int r = byte / C::RA, slot = (byte % C::RA) / 16;
+    int64_t col = m0 + 8 * (slot ^ (4 * (r & 3)));
+    if (col > a.d - 8) col = a.d - 8;  // columns past d only feed unwritten output rows
+    offA[i] = (int)(r * a.d + col);
+  }
+#pragma unroll
+  for (int i = 0; i < C::LG; ++i) {
+    const int byte = (wave + 4 * i) * 1024 + 16 * lane;
+    const int r = byte / C::RG, slot = (byte % C::RG) / 16;
+    int64_t col = n0 + 8 * (slot ^ (4 * (r & 3)));
+    if (col > a.p - 8) col = a.p - 8;
+    offG[i] = (int)(r * a.p + col);
+  }
+
+  auto issue = [&](int64_t q, int stage) {
+    const bf16s* ga = A + q * (int64_t)C::KC * a.d;
+    const bf16s* gg = G + q * (int64_t)C::KC * a.p;
+    const uint32_t sa = lds_addr(lds) + stage * C::STAGE + wave * 1024;
+    const uint32_t sg = sa + C::A_BYTES;
+#pragma unroll
+    for (int i = 0; i < C::LA; ++i) dma16(ga + offA[i], sa + 4096 * i);
+#pragma unroll
+    for (int i = 0; i < C::LG; ++i) dma16(gg + offG[i], sg + 4096 * i);
+  };
+
+  // ---- per-lane LDS read offsets (transposing reads)
+  const int s = lane & 15;
+  const int lo = 2 * ((lane >> 4) & 1) + ((s & 3) >> 1);
+  int rdA[C::NBM], rdG[C::NBN];
+#pragma unroll
+  for (int bi = 0; bi < C::NBM; ++bi) {
+    const int piece0 = (wm * C::WM + bi * 32) / 8;
+    rdA[bi] = (8 * (lane >> 5) + (s >> 2)) * C::RA + 16 * ((piece0 ^ (4 * (s >> 2))) + lo) + 8 * (s & 1);
+  }
+#pragma unroll
+  for (int bj = 0; bj < C::NBN; ++bj) {
+    const int piece0 = (wn * C::WN + bj * 32) / 8;
+    rdG[bj] = (8 * (lane >> 5) + (s >> 2)) * C::RG + 16 * ((piece0 ^ (4 * (s >> 2))) + lo) + 8 * (s & 1);
+  }
+
+  f32x16 acc[C::NBM][C::NBN];
+#pragma unroll
+  for (int bi = 0; bi < C::NBM; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < C::NBN; ++bj)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[bi][bj][j] = 0.f;
+
+  // ---- pipeline
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nq) issue(q0 + st, st);
+
+  int64_t sample = q0 / a.cps;       // sample of the chunk being computed
+  int64_t in_sample = q0 - sample * a.cps;
+  for (int it = 0; it < nq; ++it) {
+    if (it + STAGES - 2 < nq)
+      wait_vmcnt<C::LPC * (STAGES - 2)>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    if (it + STAGES - 1 < nq) issue(q0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
+
+    const float cq = c[sample];
+    if (++in_sample == a.cps) {
+      in_sample = 0;
+      ++sample;
+    }
+    const unsigned char* sa = lds + (it % STAGES) * C::STAGE;
+    const unsigned char* sg = sa + C::A_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < C::KC / 16; ++kk) {
+      u32x4 fa[C::NBM], fg[C::NBN];
+#pragma unroll
+      for (int bi = 0; bi < C::NBM; ++bi) fa[bi] = frag_tr(sa, rdA[bi] + kk * 16 * C::RA, 4 * C::RA);
+#pragma unroll
+      for (int bj = 0; bj < C::NBN; ++bj) fg[bj] = frag_tr(sg, rdG[bj] + kk * 16 * C::RG, 4 * C::RG);
+      if constexpr (C::SCALE_G) {
+#pragma unroll
+        for (int bj = 0; bj < C::NBN; ++bj) fg[bj] = scale8(fg[bj], cq);
+      } else {
+#pragma unroll
+        for (int bi = 0; bi < C::NBM; ++bi) fa[bi] = scale8(fa[bi], cq);
+      }
+#pragma unroll
+      for (int bi = 0; bi < C::NBM; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < C::NBN; ++bj) acc[bi][bj] = mfma32_bf16(fa[bi], fg[bj], acc[bi][bj]);
+    }
+  }
+
+  // ---- epilogue: the output tile goes through LDS ([BM][BN + 8] fp32; the
+  // stages are free once every wave passed the barrier), then each thread
+  // takes whole Philox blocks (4 rows of one column) or float4 row pieces,
+  // with consecutive threads on consecutive columns.
+  constexpr int TP = BN + 8;
+  static_assert(BM * TP * 4 <= C::LDS, "epilogue tile fits the stages");
+  float* tile = reinterpret_cast<float*>(lds);
+  lds_barrier();
+#pragma unroll
+  for (int bi = 0; bi < C::NBM; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < C::NBN; ++bj)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        tile[(wm * C::WM + bi * 32 + acc_row(j, lane)) * TP + wn * C::WN + bj * 32 + acc_col(lane)] = acc[bi][bj][j];
+  lds_barrier();
+  if constexpr (FUSED) {
+#pragma unroll 1
+    for (int b = threadIdx.x; b < (BM / 4) * BN; b += 256) {
+      const int rq = b / BN, nn = b % BN;
+      const int64_t m = m0 + 4 * rq, n = n0 + nn;
+      if (m >= a.d || n >= a.p) continue;
+      const f32x4 z = normals4((uint32_t)((m >> 2) * a.p + n), 2u * a.na.layer, a.na.step, 0u, a.na.k0, a.na.k1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (m + r < a.d)
+          out[(m + r) * a.p + n] = noised_mean_spec(tile[(4 * rq + r) * TP + nn], a.na.sc, z[r], a.na.inv_denom);
+    }
+  } else {
+    float* wsp = ws + split * a.d * a.p;
+#pragma unroll 1
+    for (int e = threadIdx.x; e < BM * (BN / 4); e += 256) {
+      const int row = e / (BN / 4), c4 = e % (BN / 4);
+      const int64_t m = m0 + row, n = n0 + 4 * c4;
+      if (m >= a.d || n >= a.p) continue;
+      const float4 v = *reinterpret_cast<const float4*>(tile + row * TP + 4 * c4);
+      // p % 8 == 0 and n % 4 == 0: the four columns are all in range and 16-byte aligned
+      *reinterpret_cast<float4*>(wsp + m * a.p + n) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- plan
+bool dl_eligible(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias) {
+  (void)B;
+  return dtype == 1 && !has_bias && Tn % 64 == 0 && d % 8 == 0 && p % 8 == 0 && 64 * (d > p ? d : p) < (1ll << 31);
+}
+
+// Tile and K split for the direct-load engine from a cost model: rounds of
+// one workgroup per CU (256 CUs) x the chunks each item runs at a per-CU
+// MFMA rate that grows with the tile (fewer LDS bytes per flop), plus the
+// write and re-read of split partials and a reduce launch.
+ContractPlan dl_plan(int64_t B, int64_t Tn, int64_t d, int64_t p) {
+  static const int tiles[2][2] = {{128, 128}, {256, 128}};
+  static const double eff[2] = {0.40, 0.55};
+  const double cu_peak = 2.5e15 / 256.0;
+  const int64_t nchunks = B * Tn / 64;
+  ContractPlan best{};
+  double best_t = 1e300;
+  for (int ti = 0; ti < 2; ++ti) {
+    const int bm = tiles[ti][0], bn = tiles[ti][1];
+    const int64_t mt = (d + bm - 1) / bm, nt = (p + bn - 1) / bn;
+    const double chunk_s = 2.0 * bm * bn * 64 / (cu_peak * eff[ti]);
+    const int64_t ks_max = nchunks < 512 ? nchunks : 512;
+    for (int64_t ks = 1; ks <= ks_max; ++ks) {
+      const int64_t cpsplit = (nchunks + ks - 1) / ks;
+      if ((nchunks + cpsplit - 1) / cpsplit != ks) continue;
+      const int64_t items = mt * nt * ks;
+      const double rounds = (double)((items + 255) / 256);
+      double t = rounds * (double)cpsplit * chunk_s + 3.0e-6;
+      if (ks > 1) t += (2.0 * ks + 1.0) * (double)d * (double)p * 4.0 / 5.0e12 + 4.0e-6;
+      if (t < best_t * 0.999) {
+        best_t = t;
+        best.bm = bm;
+        best.bn = bn;
+        best.mt = (int)mt;
+        best.nt = (int)nt;
+        best.ks = ks;
+        best.units_per_split = cpsplit;
+      }
+    }
+  }
+  best.engine = 1;
+  return best;
+}
+
+// ---------------------------------------------------------------- launch
+struct DlPtrs {
+  const bf16s* A;
+  const bf16s* G;
+  const float* c;
+  float* ws;
+  float* out;
+};
+
+template <int BM, int BN>
+static hipError_t launch_dl_t(hipStream_t st, const DlPtrs& P, const DlArgs& a, int64_t items) {
+  constexpr int S = 3;
+  using C = DlCfg<BM, BN, S>;
+  const int64_t per = (items + 7) / 8;
+  const dim3 grid((unsigned)(per * 8));
+  // more than 64 KB of dynamic LDS must be allowed per kernel (per call:
+  // cheap, and correct whichever device is current)
+  if (a.ks == 1) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_contract_dl<BM, BN, S, true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_contract_dl<BM, BN, S, true>), grid, dim3(256), C::LDS, st, P.A, P.G, P.c, P.ws, P.out, a);
+  } else {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_contract_dl<BM, BN, S, false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_contract_dl<BM, BN, S, false>), grid, dim3(256), C::LDS, st, P.A, P.G, P.c, P.ws, P.out, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_contract_dl(hipStream_t st, const void* A, const void* G, const float* c, int64_t B, int64_t Tn,
+                              int64_t d, int64_t p, const ContractPlan& pl, float* ws, const NoiseArgs& na,
+                              float* out) {
+  const DlPtrs P{static_cast<const bf16s*>(A), static_cast<const bf16s*>(G), c, ws, out};
+  DlArgs a;
+  a.d = d;
+  a.p = p;
+  a.cps = Tn / 64;
+  a.mt = pl.mt;
+  a.nt = pl.nt;
+  a.ks = pl.ks;
+  a.chunks_per_split = pl.units_per_split;
+  a.nchunks = B * Tn / 64;
+  a.m_fast = pl.mt <= pl.nt ? 1 : 0;
+  a.na = na;
+  const int64_t items = (int64_t)pl.mt * pl.nt * pl.ks;
+  if (pl.bm == 128 && pl.bn == 128) return launch_dl_t<128, 128>(st, P, a, items);
+  return launch_dl_t<256, 128>(st, P, a, items);
+}
+
+}  // namespace dpk

@@ -7,16 +7,28 @@
 namespace dpk {
 
 struct ContractPlan {
-  int bm, bn;               // output tile (64 or 128 each)
+  int bm, bn;               // output tile
   int mt, nt;               // tiles along d (+1 bias row) and p
   int64_t ks;               // K splits (partial tiles summed by the reduce)
-  int64_t units_per_split;  // samples (bf16) or 16-row chunks (fp32) per split
+  int64_t units_per_split;  // engine 0: samples (bf16) or KC-row chunks (fp32); engine 1: 64-row chunks
+  int engine;               // 0 register-staged engine (any shape), 1 direct-to-LDS bf16 engine
+};
+// Noise + mean applied in a contraction epilogue or reduce: out = (S + sc*z) * inv_denom.
+struct NoiseArgs {
+  float sc, inv_denom;  // sigma*C and the fp32 reciprocal of denom
+  uint32_t k0, k1, layer, step;
 };
 struct ExplicitPlan {
   int bm, bn, mt, nt;
 };
 
 ContractPlan contract_plan(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias);
+// direct-to-LDS bf16 engine: layers it takes, its plan, its launch (partials in ws when pl.ks > 1)
+bool dl_eligible(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias);
+ContractPlan dl_plan(int64_t B, int64_t Tn, int64_t d, int64_t p);
+hipError_t launch_contract_dl(hipStream_t st, const void* A, const void* G, const float* c, int64_t B, int64_t Tn,
+                              int64_t d, int64_t p, const ContractPlan& pl, float* ws, const NoiseArgs& na,
+                              float* out);
 ExplicitPlan explicit_plan(int64_t d, int64_t p, int has_bias);
 int ghost_tile_size(int64_t T);
 int64_t ghost_ntiles(int64_t T);

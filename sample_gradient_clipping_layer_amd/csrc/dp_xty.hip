@@ -472,11 +472,6 @@ __global__ __launch_bounds__(256, 2) void k_explicit_tiles(const T* __restrict__
 }
 
 // ---------------------------------------------------------------- contraction
-struct NoiseArgs {
-  float sc, inv_denom;  // sigma*C and the fp32 reciprocal of denom
-  uint32_t k0, k1, layer, step;
-};
-
 // Workgroups per CU the register budget is sized for: the bf16 128x128 tile
 // carries a second accumulator set (per-sample exact scaling), so it runs one
 // workgroup per CU with the full register file; the others run two.
@@ -659,7 +654,9 @@ static int pick_tile(int64_t n) {
 }
 
 ContractPlan contract_plan(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias) {
+  if (dl_eligible(dtype, B, Tn, d, p, has_bias)) return dl_plan(B, Tn, d, p);
   ContractPlan pl;
+  pl.engine = 0;
   const int64_t mrows = d + (has_bias ? 1 : 0);
   pl.bm = pick_tile(mrows);
   pl.bn = pick_tile(p);
@@ -781,8 +778,13 @@ hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const vo
   na.k1 = (uint32_t)(seed >> 32);
   na.layer = layer;
   na.step = step;
-  hipError_t e = dtype == 1 ? launch_contract_d<bf16s>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out)
-                            : launch_contract_d<float>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
+  hipError_t e;
+  if (pl.engine == 1)
+    e = launch_contract_dl(st, A, G, c, B, Tn, d, p, pl, ws, na, out);
+  else if (dtype == 1)
+    e = launch_contract_d<bf16s>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
+  else
+    e = launch_contract_d<float>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
   if (e != hipSuccess || pl.ks == 1) return e;
   const int vec = (p % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
   const int64_t threads = ((d + 3) / 4) * ((p + 3) / 4) + (has_bias ? (p + 3) / 4 : 0);

@@ -344,3 +344,51 @@ def test_deterministic_bitwise():
     np.testing.assert_array_equal(r1["sq"], r2["sq"])
     for a, b in zip(r1["outs"], r2["outs"]):
         np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ------------------------------------------------------------------ direct-to-LDS bf16 contraction engine
+# bf16 layers without bias whose T is a multiple of 64 and whose d, p are
+# multiples of 8 take this engine. The cases reach its plans: 128x128 and
+# 256x128 tiles, one K split (noise in the contraction's epilogue) and many
+# (partials + reduce kernel), splits that start inside a sample, ragged
+# last tiles and widths below one 16-byte piece per tile.
+DL_CASES = [
+    # B, T, d, p
+    (1, 64, 200, 328),      # 128x128, one split, ragged d and p
+    (64, 64, 8, 8),         # 128x128, 64 splits; every tile column past d/p
+    (6, 128, 264, 392),     # 128x128, splits on sample boundaries
+    (40, 128, 264, 136),    # 128x128, 3 chunks per split: splits start mid-sample
+    (32, 128, 776, 2312),   # 256x128, 3 splits, ragged
+    (4, 64, 2056, 4104),    # 256x128, one split, ragged
+]
+
+
+@pytest.mark.parametrize("B,T,d,p", DL_CASES)
+def test_dl_engine_clipped_sum(B, T, d, p):
+    rng = np.random.default_rng(B * 7919 + d)
+    A = W.f32_to_bf16_bits((rng.standard_normal((B, T, d)) / math.sqrt(d)).astype(np.float32))
+    G = W.f32_to_bf16_bits((rng.standard_normal((B, T, p)) / math.sqrt(p)).astype(np.float32))
+    c_np = rng.uniform(0.0, 1.0, B).astype(np.float32)
+    c_np[0] = 1.0
+    if B > 2:
+        c_np[2] = 0.0
+    out = torch.empty(d, p, dtype=torch.float32, device=dev())
+    dpc.dp_clipped_sum_noise(upload(A, "bf16"), upload(G, "bf16"), f32(c_np), 1.0, 0.0, 1.0, 0, 0, 0, out)
+    torch.cuda.synchronize()
+    S, _ = D.clipped_sum(W.as_f64(A, "bf16"), W.as_f64(G, "bf16"), c_np.astype(np.float64), False)
+    assert_sum(out.cpu().numpy(), S, "bf16")
+
+
+@pytest.mark.parametrize("B", [2, 512])   # one K split / 256 splits (reduce kernel)
+def test_dl_engine_noise_bit_exact(B):
+    T, d, p = 64, 24, 16
+    rng = np.random.default_rng(11)
+    A = W.f32_to_bf16_bits(rng.standard_normal((B, T, d)).astype(np.float32))
+    G = W.f32_to_bf16_bits(rng.standard_normal((B, T, p)).astype(np.float32))
+    c = torch.zeros(B, dtype=torch.float32, device=dev())
+    out = torch.empty(d, p, dtype=torch.float32, device=dev())
+    C, sigma, denom, seed, layer, step = 0.9, 1.7, 3.0, (7 << 32) | 5, 3, 12
+    dpc.dp_clipped_sum_noise(upload(A, "bf16"), upload(G, "bf16"), c, C, sigma, denom, seed, layer, step, out)
+    torch.cuda.synchronize()
+    zw = N.weight_noise(d, p, seed, layer, step)
+    np.testing.assert_array_equal(out.cpu().numpy(), D.noised_mean_f32(np.zeros((d, p)), zw, C, sigma, denom))
