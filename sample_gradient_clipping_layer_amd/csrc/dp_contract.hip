@@ -21,9 +21,9 @@
 //   and lane 4a+b receives feature f0+4a+b of rows k0..k0+3, i.e. the lane's
 //   half of an operand that holds 8 consecutive k of one feature. The swizzle
 //   puts the 4 rows x 64 bytes a half-wave reads on 64 distinct banks.
-// - The per-sample factor multiplies the operand with fewer 32-blocks per wave
-//   in fp32 and is rounded back to bf16 (RNE): the re-weighted operand c_i*G_i
-//   in the compute precision.
+// - Each sample's partial A_i^T G_i is accumulated unscaled in a second set of
+//   accumulators and folded in as acc += c_i * partial in fp32 at the sample's
+//   end: the clip factor is applied exactly.
 // - STAGES LDS buffers: loads for chunk q+STAGES-1 are in flight while chunk q
 //   is computed; one barrier per chunk.
 // - Workgroups are mapped so that each XCD (blockIdx % 8) owns a contiguous
@@ -34,27 +34,30 @@
 #include "dp_launch.hpp"
 #include "dp_noise.hpp"
 
+#include <type_traits>
+
 namespace dpk {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_uchar;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-template <int BM, int BN, int STAGES>
+template <int BM, int BN, int STAGES, int NW>
 struct DlCfg {
-  static constexpr int KC = 64;                 // K rows per chunk
+  static constexpr int KC = 64;                   // K rows per chunk
+  static constexpr int NT = 64 * NW;              // threads
   static constexpr int RA = BM * 2, RG = BN * 2;  // LDS row bytes
   static constexpr int A_BYTES = KC * RA, G_BYTES = KC * RG;
   static constexpr int STAGE = A_BYTES + G_BYTES;
   static constexpr int LDS = STAGES * STAGE;
-  static constexpr int WM = BM / 2, WN = BN / 2;  // 2 x 2 waves
+  static constexpr int WGM = NW / 2, WGN = 2;     // wave grid
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int NBM = WM / 32, NBN = WN / 32;
-  static constexpr int LA = A_BYTES / 4096;       // 1 KB loads per wave per chunk
-  static constexpr int LG = G_BYTES / 4096;
+  static constexpr int LA = A_BYTES / (1024 * NW);  // 1 KB loads per wave per chunk
+  static constexpr int LG = G_BYTES / (1024 * NW);
   static constexpr int LPC = LA + LG;
-  static constexpr bool SCALE_G = NBN <= NBM;     // scale the operand with fewer blocks
+  static_assert(LA * 1024 * NW == A_BYTES && LG * 1024 * NW == G_BYTES, "whole 1 KB loads per wave");
+  static_assert(NBM >= 1 && NBN >= 1 && WM % 32 == 0 && WN % 32 == 0, "32x32 blocks");
   static_assert(LDS <= 160 * 1024, "LDS budget");
   static_assert(LPC * (STAGES - 1) <= 63, "vmcnt range");
 };
@@ -66,28 +69,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const bf16x2 v = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// 8 bf16 values times s, rounded to bf16 (RNE).
-__device__ __forceinline__ u32x4 scale8(u32x4 v, float s) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = __uint_as_float(v[i] << 16) * s;
-    const float hi = __uint_as_float(v[i] & 0xFFFF0000u) * s;
-    r[i] = pack_bf16x2(lo, hi);
-  }
-  return r;
-}
-
 // One MFMA operand (8 consecutive k of one feature per lane) from a swizzled
-// stage: two transposing reads 4 rows apart.
-__device__ __forceinline__ u32x4 frag_tr(const unsigned char* base, int off, int four_rows) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off + four_rows));
+// stage: two transposing reads 4 rows apart. `addr` is an LDS byte address;
+// the constant offsets fold into the instructions' offset fields.
+__device__ __forceinline__ u32x4 frag_tr(uint32_t addr, int off, int four_rows) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(addr + off));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(addr + off + four_rows));
   u32x4 r;
   r[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
   r[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
@@ -126,11 +113,12 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
 // moving memory operations across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int BM, int BN, int STAGES, bool FUSED>
-__global__ __launch_bounds__(256, 1) void k_contract_dl(const bf16s* __restrict__ A, const bf16s* __restrict__ G,
-                                                       const float* __restrict__ c, float* __restrict__ ws,
-                                                       float* __restrict__ out, DlArgs a) {
-  using C = DlCfg<BM, BN, STAGES>;
+template <int BM, int BN, int STAGES, int NW, bool FUSED>
+__global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restrict__ A, const bf16s* __restrict__ G,
+                                                            const float* __restrict__ c, float* __restrict__ ws,
+                                                            float* __restrict__ out, DlArgs a) {
+  using C = DlCfg<BM, BN, STAGES, NW>;
+  static_assert(STAGES == 3, "pipeline written for three stages");
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
 
   // ---- work item (XCD-contiguous)
@@ -150,13 +138,13 @@ __global__ __launch_bounds__(256, 1) void k_contract_dl(const bf16s* __restrict_
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % C::WGM, wn = wave / C::WGM;
 
   // ---- per-lane global element offsets of this lane's 16-byte pieces within a chunk
   int offA[C::LA], offG[C::LG];
 #pragma unroll
   for (int i = 0; i < C::LA; ++i) {
-    const int byte = (wave + 4 * i) * 1024 + 16 * lane;
+    const int byte = (wave + NW * i) * 1024 + 16 * lane;
     const int r = byte / C::RA, slot = (byte % C::RA) / 16;
     int64_t col = m0 + 8 * (slot ^ (4 * (r & 3)));
     if (col > a.d - 8) col = a.d - 8;  // columns past d only feed unwritten output rows
@@ -164,7 +152,7 @@ __global__ __launch_bounds__(256, 1) void k_contract_dl(const bf16s* __restrict_
   }
 #pragma unroll
   for (int i = 0; i < C::LG; ++i) {
-    const int byte = (wave + 4 * i) * 1024 + 16 * lane;
+    const int byte = (wave + NW * i) * 1024 + 16 * lane;
     const int r = byte / C::RG, slot = (byte % C::RG) / 16;
     int64_t col = n0 + 8 * (slot ^ (4 * (r & 3)));
     if (col > a.p - 8) col = a.p - 8;
@@ -177,9 +165,9 @@ __global__ __launch_bounds__(256, 1) void k_contract_dl(const bf16s* __restrict_
     const uint32_t sa = lds_addr(lds) + stage * C::STAGE + wave * 1024;
     const uint32_t sg = sa + C::A_BYTES;
 #pragma unroll
-    for (int i = 0; i < C::LA; ++i) dma16(ga + offA[i], sa + 4096 * i);
+    for (int i = 0; i < C::LA; ++i) dma16(ga + offA[i], sa + 1024 * NW * i);
 #pragma unroll
-    for (int i = 0; i < C::LG; ++i) dma16(gg + offG[i], sg + 4096 * i);
+    for (int i = 0; i < C::LG; ++i) dma16(gg + offG[i], sg + 1024 * NW * i);
   };
 
   // ---- per-lane LDS read offsets (transposing reads)
@@ -194,10 +182,15 @@ __global__ __launch_bounds__(256, 1) void k_contract_dl(const bf16s* __restrict_
 #pragma unroll
   for (int bj = 0; bj < C::NBN; ++bj) {
     const int piece0 = (wn * C::WN + bj * 32) / 8;
-    rdG[bj] = (8 * (lane >> 5) + (s >> 2)) * C::RG + 16 * ((piece0 ^ (4 * (s >> 2))) + lo) + 8 * (s & 1);
+    rdG[bj] = C::A_BYTES + (8 * (lane >> 5) + (s >> 2)) * C::RG + 16 * ((piece0 ^ (4 * (s >> 2))) + lo) +
+              8 * (s & 1);
   }
 
-  f32x16 acc[C::NBM][C::NBN];
+  // acc: the clipped sum so far; tmp: the current sample's unscaled partial
+  // (restarted at each sample's first chunk, or at the split's first chunk),
+  // folded in as acc += c_i * tmp at the sample's (or the split's) last chunk,
+  // in fp32: the clip factor is applied exactly, not to bf16 operands.
+  f32x16 acc[C::NBM][C::NBN], tmp[C::NBM][C::NBN];
 #pragma unroll
   for (int bi = 0; bi < C::NBM; ++bi)
 #pragma unroll
@@ -205,46 +198,62 @@ __global__ __launch_bounds__(256, 1) void k_contract_dl(const bf16s* __restrict_
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[bi][bj][j] = 0.f;
 
-  // ---- pipeline
+  auto compute = [&](uint32_t sbase, auto fresh) {
+    uint32_t ra[C::NBM], rg[C::NBN];
 #pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st)
-    if (st < nq) issue(q0 + st, st);
-
-  int64_t sample = q0 / a.cps;       // sample of the chunk being computed
-  int64_t in_sample = q0 - sample * a.cps;
-  for (int it = 0; it < nq; ++it) {
-    if (it + STAGES - 2 < nq)
-      wait_vmcnt<C::LPC * (STAGES - 2)>();
-    else
-      wait_vmcnt<0>();
-    lds_barrier();
-    if (it + STAGES - 1 < nq) issue(q0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
-
-    const float cq = c[sample];
-    if (++in_sample == a.cps) {
-      in_sample = 0;
-      ++sample;
-    }
-    const unsigned char* sa = lds + (it % STAGES) * C::STAGE;
-    const unsigned char* sg = sa + C::A_BYTES;
+    for (int bi = 0; bi < C::NBM; ++bi) ra[bi] = sbase + rdA[bi];
+#pragma unroll
+    for (int bj = 0; bj < C::NBN; ++bj) rg[bj] = sbase + rdG[bj];
 #pragma unroll
     for (int kk = 0; kk < C::KC / 16; ++kk) {
       u32x4 fa[C::NBM], fg[C::NBN];
 #pragma unroll
-      for (int bi = 0; bi < C::NBM; ++bi) fa[bi] = frag_tr(sa, rdA[bi] + kk * 16 * C::RA, 4 * C::RA);
+      for (int bi = 0; bi < C::NBM; ++bi) fa[bi] = frag_tr(ra[bi], kk * 16 * C::RA, 4 * C::RA);
 #pragma unroll
-      for (int bj = 0; bj < C::NBN; ++bj) fg[bj] = frag_tr(sg, rdG[bj] + kk * 16 * C::RG, 4 * C::RG);
-      if constexpr (C::SCALE_G) {
-#pragma unroll
-        for (int bj = 0; bj < C::NBN; ++bj) fg[bj] = scale8(fg[bj], cq);
-      } else {
-#pragma unroll
-        for (int bi = 0; bi < C::NBM; ++bi) fa[bi] = scale8(fa[bi], cq);
-      }
+      for (int bj = 0; bj < C::NBN; ++bj) fg[bj] = frag_tr(rg[bj], kk * 16 * C::RG, 4 * C::RG);
 #pragma unroll
       for (int bi = 0; bi < C::NBM; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < C::NBN; ++bj) acc[bi][bj] = mfma32_bf16(fa[bi], fg[bj], acc[bi][bj]);
+        for (int bj = 0; bj < C::NBN; ++bj) {
+          if (decltype(fresh)::value && kk == 0)
+            tmp[bi][bj] = mfma32_bf16(fa[bi], fg[bj], f32x16{});
+          else
+            tmp[bi][bj] = mfma32_bf16(fa[bi], fg[bj], tmp[bi][bj]);
+        }
+    }
+  };
+
+  // ---- pipeline: chunk q in stage q % 3; loads for chunk it+2 go out once
+  // every wave is past chunk it-1 (the barrier), while chunk it is computed.
+  int64_t sample = q0 / a.cps;
+  int64_t in_sample = q0 - sample * a.cps;
+  if (nq > 0) issue(q0, 0);
+  if (nq > 1) issue(q0 + 1, 1);
+  for (int it = 0; it < nq; ++it) {
+    if (it + 1 < nq)
+      wait_vmcnt<C::LPC>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();  // chunk it landed for every wave; every wave is done with chunk it-1
+    if (it + 2 < nq) issue(q0 + it + 2, (it + 2) % 3);
+
+    const uint32_t sb = lds_addr(lds) + (uint32_t)((it % 3) * C::STAGE);
+    if (it == 0 || in_sample == 0)
+      compute(sb, std::true_type{});
+    else
+      compute(sb, std::false_type{});
+    if (++in_sample == a.cps || it + 1 == nq) {
+      const float ci = c[sample];
+#pragma unroll
+      for (int bi = 0; bi < C::NBM; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < C::NBN; ++bj)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) acc[bi][bj][j] = __builtin_fmaf(ci, tmp[bi][bj][j], acc[bi][bj][j]);
+      if (in_sample == a.cps) {
+        in_sample = 0;
+        ++sample;
+      }
     }
   }
 
@@ -266,7 +275,7 @@ __global__ __launch_bounds__(256, 1) void k_contract_dl(const bf16s* __restrict_
   lds_barrier();
   if constexpr (FUSED) {
 #pragma unroll 1
-    for (int b = threadIdx.x; b < (BM / 4) * BN; b += 256) {
+    for (int b = threadIdx.x; b < (BM / 4) * BN; b += C::NT) {
       const int rq = b / BN, nn = b % BN;
       const int64_t m = m0 + 4 * rq, n = n0 + nn;
       if (m >= a.d || n >= a.p) continue;
@@ -279,7 +288,7 @@ __global__ __launch_bounds__(256, 1) void k_contract_dl(const bf16s* __restrict_
   } else {
     float* wsp = ws + split * a.d * a.p;
 #pragma unroll 1
-    for (int e = threadIdx.x; e < BM * (BN / 4); e += 256) {
+    for (int e = threadIdx.x; e < BM * (BN / 4); e += C::NT) {
       const int row = e / (BN / 4), c4 = e % (BN / 4);
       const int64_t m = m0 + row, n = n0 + 4 * c4;
       if (m >= a.d || n >= a.p) continue;
@@ -343,24 +352,24 @@ struct DlPtrs {
   float* out;
 };
 
-template <int BM, int BN>
+template <int BM, int BN, int NW>
 static hipError_t launch_dl_t(hipStream_t st, const DlPtrs& P, const DlArgs& a, int64_t items) {
   constexpr int S = 3;
-  using C = DlCfg<BM, BN, S>;
+  using C = DlCfg<BM, BN, S, NW>;
   const int64_t per = (items + 7) / 8;
   const dim3 grid((unsigned)(per * 8));
   // more than 64 KB of dynamic LDS must be allowed per kernel (per call:
   // cheap, and correct whichever device is current)
   if (a.ks == 1) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_contract_dl<BM, BN, S, true>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_contract_dl<BM, BN, S, NW, true>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_contract_dl<BM, BN, S, true>), grid, dim3(256), C::LDS, st, P.A, P.G, P.c, P.ws, P.out, a);
+    hipLaunchKernelGGL((k_contract_dl<BM, BN, S, NW, true>), grid, dim3(C::NT), C::LDS, st, P.A, P.G, P.c, P.ws, P.out, a);
   } else {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_contract_dl<BM, BN, S, false>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_contract_dl<BM, BN, S, NW, false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_contract_dl<BM, BN, S, false>), grid, dim3(256), C::LDS, st, P.A, P.G, P.c, P.ws, P.out, a);
+    hipLaunchKernelGGL((k_contract_dl<BM, BN, S, NW, false>), grid, dim3(C::NT), C::LDS, st, P.A, P.G, P.c, P.ws, P.out, a);
   }
   return hipGetLastError();
 }
@@ -381,8 +390,8 @@ hipError_t launch_contract_dl(hipStream_t st, const void* A, const void* G, cons
   a.m_fast = pl.mt <= pl.nt ? 1 : 0;
   a.na = na;
   const int64_t items = (int64_t)pl.mt * pl.nt * pl.ks;
-  if (pl.bm == 128 && pl.bn == 128) return launch_dl_t<128, 128>(st, P, a, items);
-  return launch_dl_t<256, 128>(st, P, a, items);
+  if (pl.bm == 128 && pl.bn == 128) return launch_dl_t<128, 128, 8>(st, P, a, items);
+  return launch_dl_t<256, 128, 8>(st, P, a, items);
 }
 
 }  // namespace dpk
