@@ -11,9 +11,12 @@
  *    enqueued asynchronously on it; nothing is synchronised. The caller keeps
  *    every buffer alive until the stream has passed the call.
  *  - The caller owns every buffer, including the workspace. The library keeps
- *    no pointer after returning and has no global mutable state; calls are
- *    re-entrant. Identical inputs give bitwise-identical outputs (fixed-order
- *    reductions, no floating-point atomics).
+ *    no pointer after returning. Its only global state is an atomic call
+ *    counter that tags the arrival counters a call keeps in its workspace;
+ *    calls are re-entrant. A workspace serves one call at a time: calls that
+ *    may run concurrently (different streams) need distinct workspaces.
+ *    Identical inputs give bitwise-identical outputs (fixed-order reductions,
+ *    no floating-point atomics).
  *  - Every argument is validated before any HIP call. A failed validation
  *    returns its code and touches nothing. HIP launch failures return
  *    DP_ERR_HIP; no usable device returns DP_ERR_NO_DEVICE.
@@ -79,7 +82,11 @@ typedef int32_t dp_mode;
  *           closed form unless mode is EXPLICIT.
  *  workspace, ws_bytes  device scratch of at least dp_workspace_bytes(...)
  *           bytes (may be NULL when that is 0). Its contents on entry are
- *           ignored and on return undefined.
+ *           ignored and on return undefined: per-sample arrival counters kept
+ *           there carry a 48-bit per-call tag, so values left by earlier calls
+ *           (or arbitrary bytes) read as "no arrivals", except with
+ *           probability 2^-48 per counter. DP_ERR_SHAPE when a sample would
+ *           span more than 65535 tiles (explicit path with d*p beyond ~1e9).
  *  sqnorm   [B] fp32 device: overwritten (accumulate == 0) or incremented
  *           (accumulate != 0) by the layer's squared norms, so several layers
  *           can be summed in call order into one global norm.

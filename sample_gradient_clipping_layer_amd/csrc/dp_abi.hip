@@ -53,16 +53,23 @@ int path_of(int64_t T, int64_t d, int64_t p, dp_mode mode, int32_t kappa) {
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
+// a sample's tiles are counted in 16 bits of its arrival counter
+constexpr int64_t kMaxTilesPerSample = 65535;
+
+int64_t norm_ntiles(int path, int64_t T, int64_t d, int64_t p, int has_bias) {
+  if (path == DP_PATH_T1) return 1;
+  if (path == DP_PATH_GHOST) return dpk::ghost_ntiles(T);
+  const dpk::ExplicitPlan pl = dpk::explicit_plan(d, p, has_bias);
+  return (int64_t)pl.mt * pl.nt;
+}
+
+// tile partials [B][ntiles] fp32, then one arrival counter per sample
+size_t norm_partial_bytes(int64_t B, int64_t ntiles) { return round256((size_t)B * (size_t)ntiles * sizeof(float)); }
+
 size_t norm_ws_bytes(int path, int64_t B, int64_t T, int64_t d, int64_t p, int has_bias) {
-  if (path == DP_PATH_T1) return 0;
-  int64_t ntiles;
-  if (path == DP_PATH_GHOST) {
-    ntiles = dpk::ghost_ntiles(T);
-  } else {
-    const dpk::ExplicitPlan pl = dpk::explicit_plan(d, p, has_bias);
-    ntiles = (int64_t)pl.mt * pl.nt;
-  }
-  return round256((size_t)B * (size_t)ntiles * sizeof(float));
+  const int64_t ntiles = norm_ntiles(path, T, d, p, has_bias);
+  if (ntiles == 1) return 0;
+  return norm_partial_bytes(B, ntiles) + round256((size_t)B * sizeof(unsigned long long));
 }
 
 size_t contract_ws_bytes(dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64_t p, int has_bias) {
@@ -132,25 +139,25 @@ dp_status dp_ghost_norm(void* stream, const void* A, const void* G, dp_dtype dty
   }
   if (path == DP_PATH_GHOST && (uint64_t)((B + 7) / 8 * 8) * (uint64_t)dpk::ghost_ntiles(T) >= (1ull << 32))
     return DP_ERR_SHAPE;
+  if (norm_ntiles(path, T, d, p, hb) > kMaxTilesPerSample) return DP_ERR_SHAPE;
   s = device_ready();
   if (s != DP_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int acc = accumulate ? 1 : 0;
   if (path_out) *path_out = path;
   if (path == DP_PATH_T1) return hip_status(dpk::launch_norm_t1(st, dtype, A, G, B, d, p, hb, acc, sqnorm));
-  float* partial = static_cast<float*>(workspace);
-  hipError_t e;
-  int64_t ntiles;
-  if (path == DP_PATH_GHOST) {
-    e = dpk::launch_ghost(st, dtype, A, G, B, T, d, p, hb, partial);
-    ntiles = dpk::ghost_ntiles(T);
-  } else {
-    e = dpk::launch_explicit(st, dtype, A, G, B, T, d, p, hb, partial);
-    const dpk::ExplicitPlan pl = dpk::explicit_plan(d, p, hb);
-    ntiles = (int64_t)pl.mt * pl.nt;
-  }
-  if (e != hipSuccess) return DP_ERR_HIP;
-  return hip_status(dpk::launch_finalize_norm(st, partial, B, ntiles, acc, sqnorm));
+  const int64_t ntiles = norm_ntiles(path, T, d, p, hb);
+  dpk::NormSink sink;
+  sink.partial = static_cast<float*>(workspace);
+  sink.arrivals = ntiles > 1 ? reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(workspace) +
+                                                                      norm_partial_bytes(B, ntiles))
+                             : nullptr;
+  sink.sqnorm = sqnorm;
+  sink.ntiles = (int)ntiles;
+  sink.accumulate = acc;
+  sink.epoch = dpk::next_epoch();
+  if (path == DP_PATH_GHOST) return hip_status(dpk::launch_ghost(st, dtype, A, G, B, T, d, p, hb, sink));
+  return hip_status(dpk::launch_explicit(st, dtype, A, G, B, T, d, p, hb, sink));
 }
 
 dp_status dp_clip_factors(void* stream, const float* sqnorm, int64_t B, float C, float* c, float* norm) {

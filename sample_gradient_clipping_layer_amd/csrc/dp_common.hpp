@@ -126,4 +126,58 @@ __device__ __forceinline__ void xcd_group_map(int64_t bid, int64_t items, int64_
   *group = (local / items) * 8 + xcd;
 }
 
+// s_waitcnt with vmcnt(n), expcnt and lgkmcnt left at their maxima (no wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Arrival counter of a group of `total` workgroups: bits 63..16 hold the
+// call's epoch, bits 15..0 the arrivals of that call. A value left by an
+// earlier call (another epoch) counts as zero, so the counters need no
+// clearing between calls. Returns true for the last arrival. The CAS loop
+// retries only when another workgroup's update succeeded.
+__device__ __forceinline__ bool arrive_last(unsigned long long* ctr, uint64_t epoch, uint32_t total) {
+  unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    const unsigned long long nv = ((old >> 16) == epoch) ? old + 1ull : ((epoch << 16) | 1ull);
+    if (__hip_atomic_compare_exchange_strong(ctr, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return (uint32_t)(nv & 0xFFFFull) == total;
+  }
+}
+
+// Where a per-sample norm assembled from `ntiles` tile workgroups goes:
+// sqnorm[i] (+)= the sum of the tile partials in tile order.
+struct NormSink {
+  float* partial;                 // [B][ntiles] (unused when ntiles == 1)
+  unsigned long long* arrivals;   // [B] arrival counters (unused when ntiles == 1)
+  float* sqnorm;
+  int ntiles;
+  int accumulate;
+  uint64_t epoch;
+};
+
+// Called by ONE thread per tile workgroup with the tile's partial s. The
+// tiles of a sample run on different XCDs, whose L2 caches are not coherent
+// with each other: partials are stored and read with device-scope accesses,
+// which go through to the memory-side cache, and the store is complete
+// (vmcnt 0) before the arrival is counted. The last tile to arrive sums the
+// partials in tile order, so the result does not depend on arrival order.
+__device__ __forceinline__ void norm_sink_tile(const NormSink& k, int64_t i, int64_t tile, float s) {
+  if (k.ntiles == 1) {
+    const float tot = 0.f + s;
+    k.sqnorm[i] = k.accumulate ? k.sqnorm[i] + tot : tot;
+    return;
+  }
+  float* row = k.partial + i * k.ntiles;
+  __hip_atomic_store(row + tile, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_vmcnt<0>();
+  if (!arrive_last(k.arrivals + i, k.epoch, (uint32_t)k.ntiles)) return;
+  float tot = 0.f;
+  for (int t = 0; t < k.ntiles; ++t) tot += __hip_atomic_load(row + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  k.sqnorm[i] = k.accumulate ? k.sqnorm[i] + tot : tot;
+}
+
 }  // namespace dpk

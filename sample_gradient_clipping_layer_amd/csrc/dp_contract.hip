@@ -62,12 +62,6 @@ struct DlCfg {
   static_assert(LPC * (STAGES - 1) <= 63, "vmcnt range");
 };
 
-// s_waitcnt with vmcnt(n), expcnt and lgkmcnt left at their maxima (no wait).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // One MFMA operand (8 consecutive k of one feature per lane) from a swizzled
 // stage: two transposing reads 4 rows apart. `addr` is an LDS byte address;

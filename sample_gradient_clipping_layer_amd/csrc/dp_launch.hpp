@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dp_common.hpp"
+
 namespace dpk {
 
 struct ContractPlan {
@@ -35,12 +37,14 @@ int64_t ghost_ntiles(int64_t T);
 
 hipError_t launch_norm_t1(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t d, int64_t p,
                           int has_bias, int accumulate, float* sqnorm);
+// Norm kernels whose sample spans several tile workgroups finish each
+// sample in its last-arriving tile (NormSink in dp_common.hpp).
 hipError_t launch_ghost(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
-                        int64_t p, int has_bias, float* partial);
+                        int64_t p, int has_bias, const NormSink& sink);
 hipError_t launch_explicit(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
-                           int64_t p, int has_bias, float* partial);
-hipError_t launch_finalize_norm(hipStream_t st, const float* partial, int64_t B, int64_t ntiles, int accumulate,
-                                float* sqnorm);
+                           int64_t p, int has_bias, const NormSink& sink);
+// Tag of one call for its arrival counters: 48 bits, never 0, distinct per call in the process.
+uint64_t next_epoch();
 // Weighted contraction + noise + 1/denom: one kernel when pl.ks == 1,
 // else partial tiles in ws and a reduce kernel. bias_out != nullptr <=> bias row.
 hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const void* G, const float* c, int64_t B,

@@ -11,6 +11,8 @@
 // Reductions are fixed-order (no atomics), so results are bitwise
 // reproducible.
 #include "dp_common.hpp"
+
+#include <atomic>
 #include "dp_launch.hpp"
 
 namespace dpk {
@@ -252,7 +254,7 @@ struct GhostFull {
 template <typename T, int TS>
 __global__ __launch_bounds__(256) void k_ghost_tiles(const T* __restrict__ A, const T* __restrict__ G, int64_t B,
                                                      int64_t Tn, int64_t d, int64_t p, int has_bias, int nb,
-                                                     int ntiles, int vecA, int vecG, float* __restrict__ partial) {
+                                                     int ntiles, int vecA, int vecG, NormSink sink) {
   using Cfg = GhostCfg<T, TS>;
   constexpr int NB = Cfg::NB;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -320,18 +322,7 @@ __global__ __launch_bounds__(256) void k_ghost_tiles(const T* __restrict__ A, co
       for (int j = 0; j < 16; ++j) s += (acc_a[bi][bj][j] + one) * acc_g[bi][bj][j];
   if (!diag) s *= 2.0f;
   s = block_sum<Cfg::NT>(s, red);
-  if (threadIdx.x == 0) partial[i * ntiles + tile] = s;
-}
-
-// ---------------------------------------------------------------- finalize
-// sqnorm[i] (+)= sum over the sample's tile partials, in tile order.
-__global__ __launch_bounds__(256) void k_finalize_norm(const float* __restrict__ partial, int64_t B, int ntiles,
-                                                       int accumulate, float* __restrict__ sqnorm) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= B) return;
-  float s = 0.f;
-  for (int t = 0; t < ntiles; ++t) s += partial[i * ntiles + t];
-  sqnorm[i] = accumulate ? sqnorm[i] + s : s;
+  if (threadIdx.x == 0) norm_sink_tile(sink, i, tile, s);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -360,7 +351,7 @@ int64_t ghost_ntiles(int64_t T) {
 
 template <typename T, int TS>
 hipError_t launch_ghost_t(hipStream_t st, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d, int64_t p,
-                          int has_bias, float* partial) {
+                          int has_bias, const NormSink& sink) {
   const int nb = (int)((Tn + TS - 1) / TS);
   const int ntiles = nb * (nb + 1) / 2;
   const int64_t groups8 = (B + 7) / 8;
@@ -373,26 +364,29 @@ hipError_t launch_ghost_t(hipStream_t st, const void* A, const void* G, int64_t 
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_ghost_tiles<T, TS>), grid, dim3(256), lds_bytes, st, static_cast<const T*>(A),
-                     static_cast<const T*>(G), B, Tn, d, p, has_bias, nb, ntiles, vecA, vecG, partial);
+                     static_cast<const T*>(G), B, Tn, d, p, has_bias, nb, ntiles, vecA, vecG, sink);
   return hipGetLastError();
 }
 
 hipError_t launch_ghost(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
-                        int64_t p, int has_bias, float* partial) {
+                        int64_t p, int has_bias, const NormSink& sink) {
   const int ts = ghost_tile_size(Tn);
   if (dtype == 1) {
-    if (ts == 64) return launch_ghost_t<bf16s, 64>(st, A, G, B, Tn, d, p, has_bias, partial);
-    return launch_ghost_t<bf16s, 128>(st, A, G, B, Tn, d, p, has_bias, partial);
+    if (ts == 64) return launch_ghost_t<bf16s, 64>(st, A, G, B, Tn, d, p, has_bias, sink);
+    return launch_ghost_t<bf16s, 128>(st, A, G, B, Tn, d, p, has_bias, sink);
   }
-  if (ts == 64) return launch_ghost_t<float, 64>(st, A, G, B, Tn, d, p, has_bias, partial);
-  return launch_ghost_t<float, 128>(st, A, G, B, Tn, d, p, has_bias, partial);
+  if (ts == 64) return launch_ghost_t<float, 64>(st, A, G, B, Tn, d, p, has_bias, sink);
+  return launch_ghost_t<float, 128>(st, A, G, B, Tn, d, p, has_bias, sink);
 }
 
-hipError_t launch_finalize_norm(hipStream_t st, const float* partial, int64_t B, int64_t ntiles, int accumulate,
-                                float* sqnorm) {
-  const dim3 grid((unsigned)((B + 255) / 256));
-  hipLaunchKernelGGL(k_finalize_norm, grid, dim3(256), 0, st, partial, B, (int)ntiles, accumulate, sqnorm);
-  return hipGetLastError();
+static std::atomic<uint64_t> g_epoch{0};
+
+uint64_t next_epoch() {
+  uint64_t e;
+  do {
+    e = (g_epoch.fetch_add(1, std::memory_order_relaxed) + 1) & ((1ull << 48) - 1);
+  } while (e == 0);
+  return e;
 }
 
 }  // namespace dpk

@@ -438,8 +438,7 @@ struct SampleDesc {
 template <typename T, int BM, int BN>
 __global__ __launch_bounds__(256, 2) void k_explicit_tiles(const T* __restrict__ A, const T* __restrict__ G,
                                                            int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias,
-                                                           int mt, int nt, int vecA, int vecG,
-                                                           float* __restrict__ partial) {
+                                                           int mt, int nt, int vecA, int vecG, NormSink sink) {
   using E = Xty<T, BM, BN>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[E::LDS_BYTES];
   __shared__ float red[E::NT / kWave];
@@ -468,7 +467,7 @@ __global__ __launch_bounds__(256, 2) void k_explicit_tiles(const T* __restrict__
 #pragma unroll
       for (int j = 0; j < 16; ++j) s += acc[bi][bj][j] * acc[bi][bj][j];
   s = block_sum<E::NT>(s, red);
-  if (threadIdx.x == 0) partial[i * ntl + tile] = s;
+  if (threadIdx.x == 0) norm_sink_tile(sink, i, tile, s);
 }
 
 // ---------------------------------------------------------------- contraction
@@ -708,31 +707,31 @@ ExplicitPlan explicit_plan(int64_t d, int64_t p, int has_bias) {
 // ---------------------------------------------------------------- launchers
 template <typename T, int BM, int BN>
 static hipError_t launch_explicit_t(hipStream_t st, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
-                                    int64_t p, int has_bias, const ExplicitPlan& pl, float* partial) {
+                                    int64_t p, int has_bias, const ExplicitPlan& pl, const NormSink& sink) {
   const int eb = elem_traits<T>::bytes;
   const int vecA = ((reinterpret_cast<uintptr_t>(A) & 15) == 0) && ((d * eb) % 16 == 0);
   const int vecG = ((reinterpret_cast<uintptr_t>(G) & 15) == 0) && ((p * eb) % 16 == 0);
   const int64_t ntl = (int64_t)pl.mt * pl.nt;
   const dim3 grid((unsigned)((B + 7) / 8 * 8 * ntl));
   hipLaunchKernelGGL((k_explicit_tiles<T, BM, BN>), grid, dim3(256), 0, st, static_cast<const T*>(A),
-                     static_cast<const T*>(G), B, Tn, d, p, has_bias, pl.mt, pl.nt, vecA, vecG, partial);
+                     static_cast<const T*>(G), B, Tn, d, p, has_bias, pl.mt, pl.nt, vecA, vecG, sink);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_explicit_d(hipStream_t st, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
-                                    int64_t p, int has_bias, const ExplicitPlan& pl, float* partial) {
-  if (pl.bm == 64 && pl.bn == 64) return launch_explicit_t<T, 64, 64>(st, A, G, B, Tn, d, p, has_bias, pl, partial);
-  if (pl.bm == 64) return launch_explicit_t<T, 64, 128>(st, A, G, B, Tn, d, p, has_bias, pl, partial);
-  if (pl.bn == 64) return launch_explicit_t<T, 128, 64>(st, A, G, B, Tn, d, p, has_bias, pl, partial);
-  return launch_explicit_t<T, 128, 128>(st, A, G, B, Tn, d, p, has_bias, pl, partial);
+                                    int64_t p, int has_bias, const ExplicitPlan& pl, const NormSink& sink) {
+  if (pl.bm == 64 && pl.bn == 64) return launch_explicit_t<T, 64, 64>(st, A, G, B, Tn, d, p, has_bias, pl, sink);
+  if (pl.bm == 64) return launch_explicit_t<T, 64, 128>(st, A, G, B, Tn, d, p, has_bias, pl, sink);
+  if (pl.bn == 64) return launch_explicit_t<T, 128, 64>(st, A, G, B, Tn, d, p, has_bias, pl, sink);
+  return launch_explicit_t<T, 128, 128>(st, A, G, B, Tn, d, p, has_bias, pl, sink);
 }
 
 hipError_t launch_explicit(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
-                           int64_t p, int has_bias, float* partial) {
+                           int64_t p, int has_bias, const NormSink& sink) {
   const ExplicitPlan pl = explicit_plan(d, p, has_bias);
-  if (dtype == 1) return launch_explicit_d<bf16s>(st, A, G, B, Tn, d, p, has_bias, pl, partial);
-  return launch_explicit_d<float>(st, A, G, B, Tn, d, p, has_bias, pl, partial);
+  if (dtype == 1) return launch_explicit_d<bf16s>(st, A, G, B, Tn, d, p, has_bias, pl, sink);
+  return launch_explicit_d<float>(st, A, G, B, Tn, d, p, has_bias, pl, sink);
 }
 
 template <typename T, int BM, int BN>

@@ -65,10 +65,15 @@ def test_ghost_norm_validation(lib):
     assert _ghost(lib, A=FAKE_MIS)[0] == dpc.DP_ERR_ALIGN
     assert _ghost(lib, mode=3)[0] == dpc.DP_ERR_VALUE
     assert _ghost(lib, kappa=0)[0] == dpc.DP_ERR_VALUE
-    assert _ghost(lib, ws=None)[0] == dpc.DP_ERR_NULL
-    assert _ghost(lib, wsb=4)[0] == dpc.DP_ERR_WORKSPACE
-    st, path = _ghost(lib, wsb=4)
+    # T = 100 spans 3 Gram tiles per sample: partials + arrival counters in the workspace
+    assert _ghost(lib, ws=None, T=100, mode=dpc.MODE_GHOST)[0] == dpc.DP_ERR_NULL
+    assert _ghost(lib, wsb=4, T=100, mode=dpc.MODE_GHOST)[0] == dpc.DP_ERR_WORKSPACE
+    st, path = _ghost(lib, wsb=4, T=100, mode=dpc.MODE_GHOST)
     assert path == -7                                    # nothing written on failure
+    # a sample that is a single tile needs no workspace
+    assert lib.dp_workspace_bytes(0, 4, 3, 5, 6, 0, 1) == 0
+    # more than 65535 explicit tiles per sample is refused
+    assert _ghost(lib, T=1 << 16, d=1 << 15, p=1 << 15, B=1, mode=dpc.MODE_EXPLICIT, wsb=1 << 40)[0] == dpc.DP_ERR_SHAPE
 
 
 def test_clip_and_threshold_validation(lib):

@@ -392,3 +392,30 @@ def test_dl_engine_noise_bit_exact(B):
     torch.cuda.synchronize()
     zw = N.weight_noise(d, p, seed, layer, step)
     np.testing.assert_array_equal(out.cpu().numpy(), D.noised_mean_f32(np.zeros((d, p)), zw, C, sigma, denom))
+
+
+def test_dl_engine_workspace_reuse():
+    """Split-K tiles are finished by the last-arriving split, found through
+    per-tile counters in the workspace that carry a per-call tag. A workspace
+    full of arbitrary bytes, and one reused by earlier calls, must both give
+    the oracle's sums, bit-identically for identical inputs."""
+    B, T, d, p = 40, 128, 264, 136
+    rng = np.random.default_rng(5)
+    A = W.f32_to_bf16_bits((rng.standard_normal((B, T, d)) / math.sqrt(d)).astype(np.float32))
+    G = W.f32_to_bf16_bits((rng.standard_normal((B, T, p)) / math.sqrt(p)).astype(np.float32))
+    Ad, Gd = upload(A, "bf16"), upload(G, "bf16")
+    Ao, Go = W.as_f64(A, "bf16"), W.as_f64(G, "bf16")
+    nbytes = dpc.dp_workspace_bytes(dpc.DP_BF16, B, T, d, p)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=dev())
+    outs = []
+    for k in range(3):
+        c_np = (rng.uniform(0.0, 1.0, B) if k < 2 else c_first).astype(np.float32)
+        if k == 0:
+            c_first = c_np.copy()
+        out = torch.empty(d, p, dtype=torch.float32, device=dev())
+        dpc.dp_clipped_sum_noise(Ad, Gd, f32(c_np), 1.0, 0.0, 1.0, 0, 0, 0, out, workspace=ws)
+        torch.cuda.synchronize()
+        S, _ = D.clipped_sum(Ao, Go, c_np.astype(np.float64), False)
+        assert_sum(out.cpu().numpy(), S, "bf16", what=f"call {k}")
+        outs.append(out.cpu().numpy())
+    np.testing.assert_array_equal(outs[0], outs[2])
