@@ -22,8 +22,8 @@
 //   half of an operand that holds 8 consecutive k of one feature. The swizzle
 //   puts the 4 rows x 64 bytes a half-wave reads on 64 distinct banks.
 // - Each sample's partial A_i^T G_i is accumulated unscaled in a second set of
-//   accumulators and folded in as acc += c_i * partial in fp32 at the sample's
-//   end: the clip factor is applied exactly.
+//   accumulators and folded in as acc += c_i * partial in fp32: the clip
+//   factor is applied exactly.
 // - STAGES LDS buffers: loads for chunk q+STAGES-1 are in flight while chunk q
 //   is computed; one barrier per chunk.
 // - Workgroups are mapped so that each XCD (blockIdx % 8) owns a contiguous
@@ -92,8 +92,11 @@ struct DlArgs {
 // (global_load_lds_dwordx4, base in M0). Written as asm so that the
 // compiler's wait insertion does not treat every later LDS read as aliasing
 // it: the pipeline orders these loads with explicit vmcnt waits + barriers.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_base)
+// The global address is a wave-uniform 64-bit base plus this lane's 32-bit
+// byte offset (the instruction's SGPR-base form).
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t byte_off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(gbase),
+               "s"(lds_base)
                : "memory", "m0");
 }
 
@@ -134,15 +137,16 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave % C::WGM, wn = wave / C::WGM;
 
-  // ---- per-lane global element offsets of this lane's 16-byte pieces within a chunk
-  int offA[C::LA], offG[C::LG];
+  // ---- per-lane global byte offsets of this lane's 16-byte pieces within a chunk
+  // (< 64 * max(d, p) * 2 < 2^32)
+  uint32_t offA[C::LA], offG[C::LG];
 #pragma unroll
   for (int i = 0; i < C::LA; ++i) {
     const int byte = (wave + NW * i) * 1024 + 16 * lane;
     const int r = byte / C::RA, slot = (byte % C::RA) / 16;
     int64_t col = m0 + 8 * (slot ^ (4 * (r & 3)));
     if (col > a.d - 8) col = a.d - 8;  // columns past d only feed unwritten output rows
-    offA[i] = (int)(r * a.d + col);
+    offA[i] = (uint32_t)((r * a.d + col) * 2);
   }
 #pragma unroll
   for (int i = 0; i < C::LG; ++i) {
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
     const int r = byte / C::RG, slot = (byte % C::RG) / 16;
     int64_t col = n0 + 8 * (slot ^ (4 * (r & 3)));
     if (col > a.p - 8) col = a.p - 8;
-    offG[i] = (int)(r * a.p + col);
+    offG[i] = (uint32_t)((r * a.p + col) * 2);
   }
 
   auto issue = [&](int64_t q, int stage) {
@@ -159,9 +163,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
     const uint32_t sa = lds_addr(lds) + stage * C::STAGE + wave * 1024;
     const uint32_t sg = sa + C::A_BYTES;
 #pragma unroll
-    for (int i = 0; i < C::LA; ++i) dma16(ga + offA[i], sa + 1024 * NW * i);
+    for (int i = 0; i < C::LA; ++i) dma16(ga, offA[i], sa + 1024 * NW * i);
 #pragma unroll
-    for (int i = 0; i < C::LG; ++i) dma16(gg + offG[i], sg + 1024 * NW * i);
+    for (int i = 0; i < C::LG; ++i) dma16(gg, offG[i], sg + 1024 * NW * i);
   };
 
   // ---- per-lane LDS read offsets (transposing reads)
@@ -180,10 +184,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
               8 * (s & 1);
   }
 
-  // acc: the clipped sum so far; tmp: the current sample's unscaled partial
-  // (restarted at each sample's first chunk, or at the split's first chunk),
-  // folded in as acc += c_i * tmp at the sample's (or the split's) last chunk,
-  // in fp32: the clip factor is applied exactly, not to bf16 operands.
+  // acc: the clipped sum so far; tmp: the current sample segment's unscaled
+  // partial (a segment is the part of one sample inside this split), restarted
+  // by the segment's first MFMA and folded in as acc += c_i * tmp in fp32 at
+  // the segment's last chunk, so the clip factor is applied exactly.
   f32x16 acc[C::NBM][C::NBN], tmp[C::NBM][C::NBN];
 #pragma unroll
   for (int bi = 0; bi < C::NBM; ++bi)

@@ -645,6 +645,85 @@ __global__ __launch_bounds__(256) void k_reduce_noise(const float* __restrict__ 
   }
 }
 
+// Same result as k_reduce_noise (splits summed in split order per element)
+// for d % 4 == 0, p % 4 == 0 and 16-byte aligned out: every load is a float4
+// and each thread keeps 4 splits x 4 rows of loads in flight.
+__global__ __launch_bounds__(256) void k_reduce_noise_vec(const float* __restrict__ ws, int64_t ks, int64_t d,
+                                                          int64_t p, int has_bias, NoiseArgs na,
+                                                          float* __restrict__ out, float* __restrict__ bias_out) {
+  constexpr int U = 4;
+  const int64_t nq = d / 4, nc = p / 4;
+  const int64_t nw = nq * nc;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t split_stride = (d + (has_bias ? 1 : 0)) * p;
+  if (t < nw) {
+    const int64_t q = t / nc, cq = t % nc;
+    const float* base = ws + 4 * q * p + 4 * cq;
+    float4 s[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+    int64_t sp = 0;
+    for (; sp + U <= ks; sp += U) {
+      float4 v[U][4];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[u][r] = *reinterpret_cast<const float4*>(base + (sp + u) * split_stride + r * p);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s[r].x += v[u][r].x;
+          s[r].y += v[u][r].y;
+          s[r].z += v[u][r].z;
+          s[r].w += v[u][r].w;
+        }
+    }
+    for (; sp < ks; ++sp) {
+      float4 v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = *reinterpret_cast<const float4*>(base + sp * split_stride + r * p);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[r].x += v[r].x;
+        s[r].y += v[r].y;
+        s[r].z += v[r].z;
+        s[r].w += v[r].w;
+      }
+    }
+    float o[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t n = 4 * cq + k;
+      const f32x4 z = normals4((uint32_t)(q * p + n), 2u * na.layer, na.step, 0u, na.k0, na.k1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sv = k == 0 ? s[r].x : k == 1 ? s[r].y : k == 2 ? s[r].z : s[r].w;
+        o[r][k] = noised_mean_spec(sv, na.sc, z[r], na.inv_denom);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      *reinterpret_cast<float4*>(out + (4 * q + r) * p + 4 * cq) = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
+  } else if (has_bias && t < nw + nc) {
+    const int64_t cq = t - nw;
+    const float* base = ws + d * p + 4 * cq;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t sp = 0; sp < ks; ++sp) {
+      const float4 v = *reinterpret_cast<const float4*>(base + sp * split_stride);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    const f32x4 z = normals4((uint32_t)cq, 2u * na.layer + 1u, na.step, 0u, na.k0, na.k1);
+    bias_out[4 * cq + 0] = noised_mean_spec(s.x, na.sc, z[0], na.inv_denom);
+    bias_out[4 * cq + 1] = noised_mean_spec(s.y, na.sc, z[1], na.inv_denom);
+    bias_out[4 * cq + 2] = noised_mean_spec(s.z, na.sc, z[2], na.inv_denom);
+    bias_out[4 * cq + 3] = noised_mean_spec(s.w, na.sc, z[3], na.inv_denom);
+  }
+}
+
 // ---------------------------------------------------------------- plans
 static int pick_tile(int64_t n) {
   // 64 or 128, whichever pads n less (ties -> 128)
@@ -786,6 +865,12 @@ hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const vo
     e = launch_contract_d<float>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
   if (e != hipSuccess || pl.ks == 1) return e;
   const int vec = (p % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
+  if (vec && d % 4 == 0) {
+    const int64_t threads = (d / 4) * (p / 4) + (has_bias ? p / 4 : 0);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    hipLaunchKernelGGL(k_reduce_noise_vec, grid, dim3(256), 0, st, ws, pl.ks, d, p, has_bias, na, out, bias_out);
+    return hipGetLastError();
+  }
   const int64_t threads = ((d + 3) / 4) * ((p + 3) / 4) + (has_bias ? (p + 3) / 4 : 0);
   const dim3 grid((unsigned)((threads + 255) / 256));
   hipLaunchKernelGGL(k_reduce_noise, grid, dim3(256), 0, st, ws, pl.ks, d, p, has_bias, vec, na, out, bias_out);
