@@ -56,7 +56,7 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 // a sample's tiles are counted in 16 bits of its arrival counter
 constexpr int64_t kMaxTilesPerSample = 65535;
 
-int64_t norm_ntiles(int path, int64_t T, int64_t d, int64_t p, int has_bias) {
+int64_t norm_ntiles(int dtype, int path, int64_t T, int64_t d, int64_t p, int has_bias) {
   if (path == DP_PATH_T1) return 1;
   if (path == DP_PATH_GHOST) return dpk::ghost_ntiles(T);
   const dpk::ExplicitPlan pl = dpk::explicit_plan(d, p, has_bias);
@@ -66,8 +66,8 @@ int64_t norm_ntiles(int path, int64_t T, int64_t d, int64_t p, int has_bias) {
 // tile partials [B][ntiles] fp32, then one arrival counter per sample
 size_t norm_partial_bytes(int64_t B, int64_t ntiles) { return round256((size_t)B * (size_t)ntiles * sizeof(float)); }
 
-size_t norm_ws_bytes(int path, int64_t B, int64_t T, int64_t d, int64_t p, int has_bias) {
-  const int64_t ntiles = norm_ntiles(path, T, d, p, has_bias);
+size_t norm_ws_bytes(int dtype, int path, int64_t B, int64_t T, int64_t d, int64_t p, int has_bias) {
+  const int64_t ntiles = norm_ntiles(dtype, path, T, d, p, has_bias);
   if (ntiles == 1) return 0;
   return norm_partial_bytes(B, ntiles) + round256((size_t)B * sizeof(unsigned long long));
 }
@@ -113,7 +113,7 @@ size_t dp_workspace_bytes(dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64
   const int path = path_of(T, d, p, mode, kappa);
   size_t w = 0;
   for (int hb = 0; hb <= 1; ++hb) {
-    const size_t a = norm_ws_bytes(path, B, T, d, p, hb);
+    const size_t a = norm_ws_bytes(dtype, path, B, T, d, p, hb);
     const size_t b = contract_ws_bytes(dtype, B, T, d, p, hb);
     if (a > w) w = a;
     if (b > w) w = b;
@@ -131,22 +131,22 @@ dp_status dp_ghost_norm(void* stream, const void* A, const void* G, dp_dtype dty
   if (mode < DP_MODE_MIXED || mode > DP_MODE_EXPLICIT || kappa < 1) return DP_ERR_VALUE;
   const int hb = has_bias ? 1 : 0;
   const int path = path_of(T, d, p, mode, kappa);
-  const size_t need = norm_ws_bytes(path, B, T, d, p, hb);
+  const size_t need = norm_ws_bytes(dtype, path, B, T, d, p, hb);
   if (need > 0) {
     if (!workspace) return DP_ERR_NULL;
     if (ws_bytes < need) return DP_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return DP_ERR_ALIGN;
   }
-  if (path == DP_PATH_GHOST && (uint64_t)((B + 7) / 8 * 8) * (uint64_t)dpk::ghost_ntiles(T) >= (1ull << 32))
+  if (path == DP_PATH_GHOST && (uint64_t)((B + 7) / 8 * 8) * (uint64_t)norm_ntiles(dtype, path, T, d, p, hb) >= (1ull << 32))
     return DP_ERR_SHAPE;
-  if (norm_ntiles(path, T, d, p, hb) > kMaxTilesPerSample) return DP_ERR_SHAPE;
+  if (norm_ntiles(dtype, path, T, d, p, hb) > kMaxTilesPerSample) return DP_ERR_SHAPE;
   s = device_ready();
   if (s != DP_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int acc = accumulate ? 1 : 0;
   if (path_out) *path_out = path;
   if (path == DP_PATH_T1) return hip_status(dpk::launch_norm_t1(st, dtype, A, G, B, d, p, hb, acc, sqnorm));
-  const int64_t ntiles = norm_ntiles(path, T, d, p, hb);
+  const int64_t ntiles = norm_ntiles(dtype, path, T, d, p, hb);
   dpk::NormSink sink;
   sink.partial = static_cast<float*>(workspace);
   sink.arrivals = ntiles > 1 ? reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(workspace) +

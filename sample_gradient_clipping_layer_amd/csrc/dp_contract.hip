@@ -32,15 +32,13 @@
 //   in its L2.
 #include "dp_common.hpp"
 #include "dp_launch.hpp"
+#include "dp_lds.hpp"
 #include "dp_noise.hpp"
 
 #include <type_traits>
 
 namespace dpk {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) unsigned char lds_uchar;
 
 template <int BM, int BN, int STAGES, int NW>
 struct DlCfg {
@@ -88,27 +86,7 @@ struct DlArgs {
   NoiseArgs na;
 };
 
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16*lane
-// (global_load_lds_dwordx4, base in M0). Written as asm so that the
-// compiler's wait insertion does not treat every later LDS read as aliasing
-// it: the pipeline orders these loads with explicit vmcnt waits + barriers.
-// The global address is a wave-uniform 64-bit base plus this lane's 32-bit
-// byte offset (the instruction's SGPR-base form).
-__device__ __forceinline__ void dma16(const void* gbase, uint32_t byte_off, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(gbase),
-               "s"(lds_base)
-               : "memory", "m0");
-}
 
-__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
-  return (uint32_t)reinterpret_cast<uintptr_t>((const lds_uchar*)p);
-}
-
-// Workgroup barrier that orders LDS only: waits for this wave's LDS reads
-// (lgkmcnt) but not for its global loads in flight (vmcnt), which the
-// pipeline waits for explicitly. The memory clobber keeps the compiler from
-// moving memory operations across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int BM, int BN, int STAGES, int NW, bool FUSED>
 __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restrict__ A, const bf16s* __restrict__ G,

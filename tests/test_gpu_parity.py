@@ -419,3 +419,38 @@ def test_dl_engine_workspace_reuse():
         assert_sum(out.cpu().numpy(), S, "bf16", what=f"call {k}")
         outs.append(out.cpu().numpy())
     np.testing.assert_array_equal(outs[0], outs[2])
+
+
+# ------------------------------------------------------------------ ghost path shapes
+# bf16 ghost norms over 64-row tiles (T <= 384) and 128-row tiles (T > 384):
+# one tile with most rows past T, 3 and 10 tiles with ragged T, 15 tiles,
+# 36 tiles, bias on and off, accumulation into sqnorm.
+GHOST_CASES = [
+    # B, T, d, p, has_bias
+    (3, 5, 128, 256, True),      # 1 tile of 64
+    (4, 100, 256, 128, False),   # 3 tiles, ragged
+    (5, 128, 384, 128, False),   # 3 tiles: the gpt-block T
+    (9, 64, 128, 128, True),     # 1 tile
+    (3, 200, 128, 256, True),    # 10 tiles, ragged
+    (2, 300, 256, 128, False),   # 15 tiles, ragged
+    (2, 385, 64, 192, True),     # 128-row tiles: 10, ragged
+    (1, 1000, 128, 64, False),   # 128-row tiles: 36
+]
+
+
+@pytest.mark.parametrize("B,T,d,p,hb", GHOST_CASES)
+def test_ghost_norms_shapes(B, T, d, p, hb):
+    rng = np.random.default_rng(B * 131 + T)
+    A = W.f32_to_bf16_bits((rng.standard_normal((B, T, d)) / math.sqrt(d)).astype(np.float32))
+    G = W.f32_to_bf16_bits((rng.standard_normal((B, T, p)) / math.sqrt(p)).astype(np.float32))
+    Ad, Gd = upload(A, "bf16"), upload(G, "bf16")
+    sq = torch.full((B,), 2.0, dtype=torch.float32, device=dev())
+    path = dpc.dp_ghost_norm(Ad, Gd, sq, has_bias=hb, mode=dpc.MODE_GHOST, accumulate=True)
+    assert path == dpc.PATH_GHOST
+    torch.cuda.synchronize()
+    sq_or = D.layer_sqnorms(W.as_f64(A, "bf16"), W.as_f64(G, "bf16"), hb)
+    assert_norms(sq.cpu().numpy() - 2.0, sq_or, "bf16", what="accumulated sqnorm")
+    sq2 = torch.empty(B, dtype=torch.float32, device=dev())
+    dpc.dp_ghost_norm(Ad, Gd, sq2, has_bias=hb, mode=dpc.MODE_GHOST)
+    torch.cuda.synchronize()
+    assert_norms(sq2.cpu().numpy(), sq_or, "bf16")
