@@ -81,7 +81,21 @@ def _algorithmic(wl, T, d, p, kind):
     return flops, inp + 4 * (d + hb) * p + 4 * B
 
 
+DEVICE_GEN_BYTES = 8 << 30
+
+
 def run_gpu(wl, steps, warmup):
+    """Times `steps` whole steps of the workload after `warmup` untimed ones.
+
+    Global clipping (one norm per example over all layers): every layer's
+    norms accumulate into one buffer, then one clip-factor call, then every
+    layer's clipped noised sum. Per-layer adaptive clipping: per layer, its
+    norms, its clip factors under its current bound C_t[l], its clipped noised
+    sum with noise scale sigma * C_t[l], and the update of its bound from this
+    step's norms; the new bounds are read back to the host once per step
+    (they are host arguments of the next step's calls), inside the timed
+    region. Returns wall seconds, per-call event times [steps, calls], the
+    kinds and layers of the calls, and the number of rotated input sets."""
     import torch
     import sample_gradient_clipping_layer_amd as dpc
 
@@ -89,8 +103,10 @@ def run_gpu(wl, steps, warmup):
     torch.cuda.set_device(dev)
     shapes = W.layer_list(wl)
     B = wl.B
-    set_bytes = sum(B * T * (d + p) * (2 if wl.dtype == "bf16" else 4) for (T, d, p) in shapes)
+    eb = 2 if wl.dtype == "bf16" else 4
+    set_bytes = sum(B * T * (d + p) * eb for (T, d, p) in shapes)
     n_sets = max(1, min(4, math.ceil(2 * CACHE_BYTES / set_bytes) + 1)) if set_bytes < 4 * CACHE_BYTES else 1
+    on_device = set_bytes > DEVICE_GEN_BYTES
 
     def up(x):
         if wl.dtype == "bf16":
@@ -101,45 +117,80 @@ def run_gpu(wl, steps, warmup):
     for s in range(n_sets):
         layers = []
         for l in range(len(shapes)):
-            A, G = W.make_layer(wl, l, step=s)
-            layers.append((up(A), up(G)))
+            if on_device:
+                layers.append(W.make_layer_device(wl, l, dev, step=s))
+            else:
+                A, G = W.make_layer(wl, l, step=s)
+                layers.append((up(A), up(G)))
+                del A, G
         sets.append(layers)
+    torch.cuda.synchronize()
     dt = dpc.DP_BF16 if wl.dtype == "bf16" else dpc.DP_F32
-    ws = []
-    for (T, d, p) in shapes:
-        nbytes = dpc.dp_workspace_bytes(dt, B, T, d, p)
-        ws.append(torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev))
-    sq = torch.empty(B, dtype=torch.float32, device=dev)
-    c = torch.empty(B, dtype=torch.float32, device=dev)
+    # one workspace per distinct shape (calls on one stream run one at a time)
+    ws_by_shape = {}
+    for sh in set(shapes):
+        nbytes = dpc.dp_workspace_bytes(dt, B, *sh)
+        ws_by_shape[sh] = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    ws = [ws_by_shape[sh] for sh in shapes]
     outs = [torch.empty(d, p, dtype=torch.float32, device=dev) for (T, d, p) in shapes]
     bouts = [torch.empty(p, dtype=torch.float32, device=dev) if wl.has_bias else None for (T, d, p) in shapes]
     stream = torch.cuda.current_stream()
+    L = len(shapes)
 
-    # per-call event pairs (calls: norm per layer, clip, sum per layer)
-    ncalls = 2 * len(shapes) + 1
+    if wl.per_layer:
+        sq = [torch.empty(B, dtype=torch.float32, device=dev) for _ in range(L)]
+        c = [torch.empty(B, dtype=torch.float32, device=dev) for _ in range(L)]
+        nrm = [torch.empty(B, dtype=torch.float32, device=dev) for _ in range(L)]
+        C_next = torch.empty(L, dtype=torch.float32, device=dev)
+        # initial bounds: one adaptive-threshold init call per layer on the first input set
+        for l, (A, G) in enumerate(sets[0]):
+            dpc.dp_ghost_norm(A, G, sq[l], has_bias=wl.has_bias, workspace=ws[l])
+            dpc.dp_clip_factors(sq[l], 3.0e38, c[l], nrm[l])
+            dpc.dp_adaptive_threshold(nrm[l], 1.0, wl.alpha, wl.beta, wl.sigma_l2, True, wl.seed, l, 0,
+                                      C_next[l:l + 1])
+        C_t = [float(v) for v in C_next.tolist()]
+        kinds = [(kd, l) for l in range(L) for kd in ("norm", "clip", "sum", "thr")]
+    else:
+        sq = torch.empty(B, dtype=torch.float32, device=dev)
+        c = torch.empty(B, dtype=torch.float32, device=dev)
+        kinds = [("norm", l) for l in range(L)] + [("clip", -1)] + [("sum", l) for l in range(L)]
+
+    ncalls = len(kinds)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ncalls)]
           for _ in range(steps)]
 
     def step(k, timed):
+        nonlocal C_t
         layers = sets[k % n_sets]
         e = ev[k] if timed else None
         j = 0
-        for l, (A, G) in enumerate(layers):
+
+        def call(fn, *args, **kw):
+            nonlocal j
             if e: e[j][0].record(stream)
-            dpc.dp_ghost_norm(A, G, sq, has_bias=wl.has_bias, accumulate=l > 0, workspace=ws[l])
-            if e: e[j][1].record(stream)
-            j += 1
-        if e: e[j][0].record(stream)
-        dpc.dp_clip_factors(sq, wl.C, c)
-        if e: e[j][1].record(stream)
-        j += 1
-        for l, (A, G) in enumerate(layers):
-            if e: e[j][0].record(stream)
-            dpc.dp_clipped_sum_noise(A, G, c, wl.C, wl.sigma, float(B), wl.seed, l, k, outs[l], bouts[l],
-                                     workspace=ws[l])
+            fn(*args, **kw)
             if e: e[j][1].record(stream)
             j += 1
 
+        if wl.per_layer:
+            for l, (A, G) in enumerate(layers):
+                call(dpc.dp_ghost_norm, A, G, sq[l], has_bias=wl.has_bias, workspace=ws[l])
+                call(dpc.dp_clip_factors, sq[l], C_t[l], c[l], nrm[l])
+                call(dpc.dp_clipped_sum_noise, A, G, c[l], C_t[l], wl.sigma, float(B), wl.seed, l, k, outs[l],
+                     bouts[l], workspace=ws[l])
+                call(dpc.dp_adaptive_threshold, nrm[l], C_t[l], wl.alpha, wl.beta, wl.sigma_l2, False, wl.seed,
+                     l, k + 1, C_next[l:l + 1])
+            C_t = [float(v) for v in C_next.tolist()]
+            return
+        for l, (A, G) in enumerate(layers):
+            call(dpc.dp_ghost_norm, A, G, sq, has_bias=wl.has_bias, accumulate=l > 0, workspace=ws[l])
+        call(dpc.dp_clip_factors, sq, wl.C, c)
+        for l, (A, G) in enumerate(layers):
+            call(dpc.dp_clipped_sum_noise, A, G, c, wl.C, wl.sigma, float(B), wl.seed, l, k, outs[l], bouts[l],
+                 workspace=ws[l])
+
+    if not wl.per_layer:
+        C_t = None
     for k in range(warmup):
         step(k, False)
     torch.cuda.synchronize()
@@ -151,31 +202,78 @@ def run_gpu(wl, steps, warmup):
     call_ms = np.array([[a.elapsed_time(b) for (a, b) in ev[k]] for k in range(steps)])  # [steps, ncalls]
     for o in outs:
         assert torch.isfinite(o).all().item(), "non-finite output"
-    return wall, call_ms, shapes, n_sets
+    if wl.per_layer:
+        assert all(math.isfinite(v) and v > 0 for v in C_t), f"adaptive bounds {C_t}"
+    return wall, call_ms, shapes, kinds, n_sets, on_device
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The fp64 oracle as it stands, on the same workload: whole steps (all
-    layers: norms, clip factors, clipped sum, noise) on the host cores."""
+def cpu_baseline(wl, budget_s=12.0, step_s=3.0, max_step_s=25.0):
+    """The fp64 oracle as it stands, timed on the host cores on a bounded
+    sample of the same workload: whole steps (norms, clip factors, clipped
+    sums, noise; with per-layer clipping also the bound updates) over all
+    layers, or over the first decoder block when the set repeats blocks, on
+    the first b examples. b is calibrated so that one step takes about
+    `step_s` seconds and the per-example work is at least three times the
+    step's fixed cost (its noise draw), within `max_step_s` per step. The
+    oracle's cost is linear in the examples and, for a repeated block, in the
+    blocks, so the rate is scaled to the whole set; the fixed cost is amortised
+    over b examples, not the full batch, which makes the reported rate an
+    underestimate when b is smaller than the batch."""
     from threadpoolctl import threadpool_info
     from oracle import drivers
 
-    layers = []
-    for l in range(wl.n_layers):
-        A, G = W.make_layer(wl, l, step=0)
-        layers.append((W.as_f64(A, wl.dtype), W.as_f64(G, wl.dtype)))
+    nl = len(wl.layers) if wl.blocks > 1 else wl.n_layers
+    scale = nl / wl.n_layers
+
+    def sample(b):
+        layers = []
+        for l in range(nl):
+            A, G = W.make_layer(wl, l, step=0, B=b)
+            layers.append((W.as_f64(A, wl.dtype), W.as_f64(G, wl.dtype)))
+        return layers
+
+    def one_step(layers, n):
+        if wl.per_layer:
+            drivers.adaptive_step(layers, [wl.C] * len(layers), wl.sigma, wl.alpha, wl.beta, wl.sigma_l2,
+                                  wl.seed, step=n, has_bias=wl.has_bias, denom=float(wl.B))
+        else:
+            drivers.global_clip_step(layers, wl.C, wl.sigma, wl.seed, step=n, has_bias=wl.has_bias,
+                                     denom=float(wl.B))
+
+    def timed(b):
+        layers = sample(b)
+        t0 = time.perf_counter()
+        one_step(layers, 0)
+        return layers, time.perf_counter() - t0
+
+    # two calibration steps give the per-example and the fixed (noise) cost of a step
+    b0 = min(wl.B, 2)
+    layers, t0 = timed(b0)
+    b = b0
+    if b0 < wl.B:
+        b1 = min(wl.B, 4 * b0)
+        layers, t1 = timed(b1)
+        slope = max((t1 - t0) / (b1 - b0), 1e-9)
+        fixed = max(t0 - slope * b0, 0.0)
+        # enough examples for one step of about step_s, and for the per-example work to be
+        # at least three times the fixed cost, within max_step_s per step
+        want = max((step_s - fixed) / slope, 3.0 * fixed / slope)
+        b = int(min(wl.B, max(b1, min(want, (max_step_s - fixed) / slope))))
+        layers = sample(b) if b != b1 else layers
     n = 0
     t0 = time.perf_counter()
     while True:
-        drivers.global_clip_step(layers, wl.C, wl.sigma, wl.seed, step=n, has_bias=wl.has_bias)
+        one_step(layers, n)
         n += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    return {"value": wl.B * n / dt, "unit": "examples/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} whole step(s) of {wl.name} (B={wl.B}, all {wl.n_layers} layers, fp64 numpy, "
-                      f"materialised per-example gradients), {dt:.1f} s"}
+    what = f"first {nl} of {wl.n_layers} layers" if nl < wl.n_layers else f"all {nl} layers"
+    return {"value": b * n / dt * scale, "unit": "examples/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} whole step(s) of {wl.name} on {b} of {wl.B} examples, {what} "
+                      f"(fp64 numpy, materialised per-example gradients), {dt:.1f} s"
+                      + (f"; rate scaled by {nl}/{wl.n_layers} layers" if nl < wl.n_layers else "")}
 
 
 COPY_PROBE_BYTES = 256 << 20
@@ -215,31 +313,30 @@ def main():
         copy_probe()
         return
     wl = W.WORKLOADS[a.workload]
-    wall, call_ms, shapes, n_sets = run_gpu(wl, a.steps, a.warmup)
+    wall, call_ms, shapes, kinds, n_sets, on_device = run_gpu(wl, a.steps, a.warmup)
     L = len(shapes)
     ms_per_step = 1e3 * wall / a.steps
     value = wl.B * a.steps / wall
 
-    # dominant call by total event time
+    # dominant entry point by total event time: the norm calls or the clipped-sum calls
     mean_ms = call_ms.mean(axis=0)
-    kinds = ["norm"] * L + ["clip"] + ["sum"] * L
     by_kind = {}
-    for j, kd in enumerate(kinds):
+    for j, (kd, l) in enumerate(kinds):
         by_kind[kd] = by_kind.get(kd, 0.0) + mean_ms[j]
     dom = max(("norm", "sum"), key=lambda k: by_kind[k])
     flops = byts = t_ms = 0.0
     ndom = 0
-    for j, kd in enumerate(kinds):
+    for j, (kd, l) in enumerate(kinds):
         if kd != dom:
             continue
-        l = j if kd == "norm" else j - L - 1
         T, d, p = shapes[l]
         f, b = _algorithmic(wl, T, d, p, kd)
         flops += f
         byts += b
         t_ms += mean_ms[j]
         ndom += 1
-    if dom == "sum" or (wl.dtype == "bf16" and flops / byts > PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3):
+    if dom == "sum" or (flops / byts > (PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS)
+                        / PEAK_HBM_GBS * 1e3):
         peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
         achieved = flops / (t_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
@@ -251,20 +348,26 @@ def main():
     traffic = measured_traffic(dom, wl.name)
     roof["traffic"] = None if traffic is None else round(traffic)
     roof["algorithmic_bytes_per_call"] = round(byts / ndom)
-    roof["kernel"] = ("dp_ghost_norm: k_ghost_tiles + k_finalize_norm" if dom == "norm"
-                      else "dp_clipped_sum_noise: k_contract_tiles (+ k_reduce_noise when K is split)")
+    roof["kernel"] = ("dp_ghost_norm: k_ghost_tiles / k_explicit_tiles / k_norm_t1" if dom == "norm"
+                      else "dp_clipped_sum_noise: k_contract_dl or k_contract_tiles (+ k_reduce_noise[_vec] "
+                           "when K is split)")
     roof["avg_call_us"] = round(1e3 * t_ms / ndom, 2)
     if a.breakdown:
-        names = [f"norm[{l}]" for l in range(L)] + ["clip"] + [f"sum[{l}]" for l in range(L)]
-        for nm, m in zip(names, mean_ms):
+        for (kd, l), m in zip(kinds, mean_ms):
+            nm = kd if l < 0 else f"{kd}[{l}]"
             print(f"{nm:10s} {m * 1e3:9.2f} us", file=sys.stderr)
+        for kd, m in by_kind.items():
+            print(f"total {kd:5s} {m * 1e3:9.2f} us", file=sys.stderr)
+    cfg = {"workload": wl.name, "global_batch": wl.B, "seq_len": shapes[0][0],
+           "layers": [list(s) for s in shapes] if L <= 8 else f"{wl.blocks} x {[list(s) for s in wl.layers]}",
+           "parallelism": "single-gpu", "input_sets_rotated": n_sets,
+           "clipping": "per-layer adaptive" if wl.per_layer else "global"}
+    if on_device:
+        cfg["inputs"] = "drawn on the device (torch generator), distinct for every layer"
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "examples/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
-        "config": {"workload": wl.name, "global_batch": wl.B, "seq_len": shapes[0][0],
-                   "layers": [list(s) for s in shapes] if L <= 8 else f"{L} layers",
-                   "parallelism": "single-gpu", "input_sets_rotated": n_sets},
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic", "config": cfg,
         "roofline": roof,
         "events_ms_per_step": round(float(call_ms.sum(axis=1).mean()), 4),
     }

@@ -189,3 +189,37 @@ def make_vector(n: int, lo: float, hi: float, tag: int, base: int = BASE_SEED) -
 
 def layer_list(wl: Workload) -> List[Tuple[int, int, int]]:
     return [wl.layer_shape(l) for l in range(wl.n_layers)]
+
+
+def device_seed(wl_id: int, layer: int, step: int, tensor: int, base: int = BASE_SEED) -> int:
+    """64-bit seed of torch's device generator for one (workload, layer, step, tensor)."""
+    m = (1 << 64) - 1
+    h = base & m
+    for v in (wl_id, layer, step + 1, tensor):
+        h = (h + (v & 0xFFFFFFFF) + 0x9E3779B97F4A7C15) & m   # splitmix64 step per field
+        h = ((h ^ (h >> 30)) * 0xBF58476D1CE4E5B9) & m
+        h = ((h ^ (h >> 27)) * 0x94D049BB133111EB) & m
+        h ^= h >> 31
+    return h >> 1
+
+
+def make_layer_device(wl: Workload, layer: int, device, step: int = 0):
+    """Inputs (A, G) of a transformer layer drawn on the device with torch's
+    generator: the same distributions as ``make_layer`` (N(0, 1)/sqrt(d) and
+    N(0, 1)/sqrt(p) in fp32, rounded to bf16 to nearest even), not the same
+    values. For layer sets too large to draw on the host in reasonable time
+    (the GPT-2-large stack: 48 GB per pass)."""
+    import torch
+    if wl.dtype != "bf16" or wl.conv:
+        raise ValueError("device generation covers the bf16 transformer workloads only")
+    B = wl.B
+    T, d, p = wl.layer_shape(layer)
+    out = []
+    for tensor, (width, scale) in enumerate(((d, 1.0 / math.sqrt(d)), (p, 1.0 / math.sqrt(p)))):
+        g = torch.Generator(device=device)
+        g.manual_seed(device_seed(wl.wl_id, layer, step, tensor))
+        x = torch.randn((B, T, width), generator=g, device=device, dtype=torch.float32)
+        x.mul_(scale)
+        out.append(x.to(torch.bfloat16))
+        del x
+    return out[0], out[1]
