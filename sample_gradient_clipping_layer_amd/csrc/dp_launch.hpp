@@ -12,8 +12,8 @@ struct ContractPlan {
   int bm, bn;               // output tile
   int mt, nt;               // tiles along d (+1 bias row) and p
   int64_t ks;               // K splits (partial tiles summed by the reduce)
-  int64_t units_per_split;  // engine 0: samples (bf16) or KC-row chunks (fp32); engine 1: 64-row chunks
-  int engine;               // 0 register-staged engine (any shape), 1 direct-to-LDS bf16 engine
+  int64_t units_per_split;  // engine 0: samples (bf16) or KC-row chunks (fp32); 1: 64-row, 2: 32-row chunks
+  int engine;               // 0 register-staged (any shape), 1 direct-to-LDS bf16, 2 direct-to-LDS fp32
 };
 // Noise + mean applied in a contraction epilogue or reduce: out = (S + sc*z) * inv_denom.
 struct NoiseArgs {
@@ -31,6 +31,12 @@ ContractPlan dl_plan(int64_t B, int64_t Tn, int64_t d, int64_t p);
 hipError_t launch_contract_dl(hipStream_t st, const void* A, const void* G, const float* c, int64_t B, int64_t Tn,
                               int64_t d, int64_t p, const ContractPlan& pl, float* ws, const NoiseArgs& na,
                               float* out);
+// direct-to-LDS fp32 engine (bias row accumulated on the side, partials [ks][d + bias][p] in ws)
+bool dl32_eligible(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias);
+ContractPlan dl32_plan(int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias);
+hipError_t launch_contract_dl32(hipStream_t st, const void* A, const void* G, const float* c, int64_t B, int64_t Tn,
+                                int64_t d, int64_t p, const ContractPlan& pl, float* ws, const NoiseArgs& na,
+                                float* out, float* bias_out);
 ExplicitPlan explicit_plan(int64_t d, int64_t p, int has_bias);
 int ghost_tile_size(int64_t T);
 int64_t ghost_ntiles(int64_t T);

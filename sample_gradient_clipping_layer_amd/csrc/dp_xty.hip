@@ -75,7 +75,16 @@ struct Xty {
 
   struct Regs {
     u32x4 v[UPT][RU];
+    float sc[UPT][RU];  // fp32: clip factor of each staged G row (loaded with the rows)
   };
+
+  // Index of the sample that flat row `row` belongs to (T rows per sample).
+  __device__ __forceinline__ static int64_t sample_of(int64_t row, int64_t Tn) {
+    if (Tn == 1) return row;
+    if ((uint64_t)row <= 0xFFFFFFFFull && (uint64_t)Tn <= 0xFFFFFFFFull)
+      return (int64_t)((uint32_t)row / (uint32_t)Tn);
+    return row / Tn;
+  }
 
   // Unit u of an operand -> (row group rr, 16-byte column vector cc). The map
   // makes every 16-lane pass of the transposed LDS stores hit 16 distinct
@@ -95,7 +104,8 @@ struct Xty {
   // loads need no checks (and the compiled loop has no per-element fallback).
   template <bool FULL>
   __device__ __forceinline__ static void load(Regs& R, const ChunkSrc<T>& cs, int64_t Kx, int64_t Ky, int64_t m0,
-                                              int64_t n0, bool vecx, bool vecy, int64_t ones_col) {
+                                              int64_t n0, bool vecx, bool vecy, int64_t ones_col,
+                                              const float* c = nullptr, int64_t Tn = 1) {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int unit = threadIdx.x + u * NT;
@@ -103,6 +113,15 @@ struct Xty {
       const bool isx = unit < UX;
       int rr, cc;
       unit_rc(isx ? unit : unit - UX, &rr, &cc);
+      if constexpr (P == 4) {
+        if (!isx && c != nullptr) {
+#pragma unroll
+          for (int r = 0; r < RU; ++r) {
+            const int row = rr * RU + r;
+            R.sc[u][r] = row < cs.rv ? c[sample_of(cs.r0 + row, Tn)] : 0.0f;
+          }
+        }
+      }
       const T* base = isx ? cs.xp : cs.yp;
       const int64_t K = isx ? Kx : Ky;
       const int64_t col = (isx ? m0 : n0) + cc * P;
@@ -133,6 +152,7 @@ struct Xty {
   struct Offs {
     int64_t off[UPT];
     bool isx[UPT];
+    int row[UPT];  // first chunk row of the unit
   };
   __device__ __forceinline__ static void full_offsets(Offs& O, int64_t Kx, int64_t Ky, int64_t m0, int64_t n0) {
 #pragma unroll
@@ -142,15 +162,23 @@ struct Xty {
       int rr, cc;
       unit_rc(isx ? unit : unit - UX, &rr, &cc);
       O.isx[u] = isx;
+      O.row[u] = rr * RU;
       O.off[u] = isx ? (int64_t)(rr * RU) * Kx + m0 + cc * P : (int64_t)(rr * RU) * Ky + n0 + cc * P;
     }
   }
   // Unchecked loads of chunk q: rows [q*KC, q*KC + KC) of X = A and Y = G.
   __device__ __forceinline__ static void load_full(Regs& R, const Offs& O, const T* A, const T* G, int64_t Kx,
-                                                   int64_t Ky, int64_t q) {
+                                                   int64_t Ky, int64_t q, const float* c = nullptr,
+                                                   int64_t Tn = 1) {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       if (UT % NT != 0 && threadIdx.x + u * NT >= UT) continue;
+      if constexpr (P == 4) {
+        if (!O.isx[u] && c != nullptr) {
+#pragma unroll
+          for (int r = 0; r < RU; ++r) R.sc[u][r] = c[sample_of(q * (int64_t)KC + O.row[u] + r, Tn)];
+        }
+      }
       const int64_t K = O.isx[u] ? Kx : Ky;
       const T* src = (O.isx[u] ? A : G) + q * (int64_t)KC * K + O.off[u];
 #pragma unroll
@@ -159,9 +187,9 @@ struct Xty {
   }
 
   // Transposed stores: feature f = cc*P + m gets the RU k-values of the unit
-  // as one 16-byte write at k offset rr*RU. fp32 G rows are scaled by c.
-  __device__ __forceinline__ static void store(const Regs& R, unsigned char* buf, const ChunkSrc<T>& cs,
-                                               const float* c, int64_t Tn) {
+  // as one 16-byte write at k offset rr*RU. fp32 G rows are scaled by c (the
+  // factors were loaded with the rows; `scaled` says whether they were).
+  __device__ __forceinline__ static void store(const Regs& R, unsigned char* buf, bool scaled) {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int unit = threadIdx.x + u * NT;
@@ -172,12 +200,9 @@ struct Xty {
       unsigned char* dst = buf + ((isx ? 0 : BM) + cc * P) * kRowB + rr * 16;
       if constexpr (P == 4) {
         float sc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-        if (!isx && c != nullptr) {
+        if (!isx && scaled) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = rr * 4 + r;
-            sc[r] = row < cs.rv ? c[(cs.r0 + row) / Tn] : 0.0f;
-          }
+          for (int r = 0; r < 4; ++r) sc[r] = R.sc[u][r];
         }
         const u32x4* v = R.v[u];
         *reinterpret_cast<float4*>(dst + 0 * kRowB) = make_float4(__uint_as_float(v[0].x) * sc[0], __uint_as_float(v[1].x) * sc[1], __uint_as_float(v[2].x) * sc[2], __uint_as_float(v[3].x) * sc[3]);
@@ -288,10 +313,10 @@ __device__ __forceinline__ void kloop(typename Xty<T, BM, BN>::AccT& acc, unsign
   typename E::Regs R[2];
   ChunkSrc<T> cs[2];
   cs[0] = desc(0);
-  E::template load<FULL>(R[0], cs[0], d, p, m0, n0, vecA, vecG, ones_col);
+  E::template load<FULL>(R[0], cs[0], d, p, m0, n0, vecA, vecG, ones_col, c_rows, Tn);
   if (nq > 1) {
     cs[1] = desc(1);
-    E::template load<FULL>(R[1], cs[1], d, p, m0, n0, vecA, vecG, ones_col);
+    E::template load<FULL>(R[1], cs[1], d, p, m0, n0, vecA, vecG, ones_col, c_rows, Tn);
   }
   typename E::AccT tmp;
   if constexpr (!PER_SAMPLE) (void)tmp;
@@ -301,11 +326,11 @@ __device__ __forceinline__ void kloop(typename Xty<T, BM, BN>::AccT& acc, unsign
       const int64_t q = q0 + st;
       if (q < nq) {
         unsigned char* buf = lds + st * E::BUF;
-        E::store(R[st], buf, cs[st], c_rows, Tn);
+        E::store(R[st], buf, c_rows != nullptr);
         __syncthreads();
         if (q + 2 < nq) {
           cs[st] = desc(q + 2);
-          E::template load<FULL>(R[st], cs[st], d, p, m0, n0, vecA, vecG, ones_col);
+          E::template load<FULL>(R[st], cs[st], d, p, m0, n0, vecA, vecG, ones_col, c_rows, Tn);
         }
         if constexpr (PER_SAMPLE) {
           const int ch = (int)(q % cps);
@@ -348,8 +373,9 @@ __device__ __forceinline__ void kloop_full(typename Xty<T, BM, BN>::AccT& acc, u
   E::full_offsets(O, d, p, m0, n0);
   const int64_t qlast = q0 + nq - 1;
   typename E::Regs R0, R1;
-  E::load_full(R0, O, A, G, d, p, q0);
-  E::load_full(R1, O, A, G, d, p, q0 + 1 <= qlast ? q0 + 1 : qlast);
+  const float* c_rows = PER_SAMPLE ? nullptr : c;  // fp32: G rows scaled while staging
+  E::load_full(R0, O, A, G, d, p, q0, c_rows, Tn);
+  E::load_full(R1, O, A, G, d, p, q0 + 1 <= qlast ? q0 + 1 : qlast, c_rows, Tn);
   typename E::AccT tmp;
   const int cps = (int)(Tn / E::KC);             // chunks per sample (PER_SAMPLE)
   int ch = PER_SAMPLE ? (int)(q0 % cps) : 0;     // chunk index inside its sample
@@ -358,13 +384,10 @@ __device__ __forceinline__ void kloop_full(typename Xty<T, BM, BN>::AccT& acc, u
   unsigned char* buf1 = lds + E::BUF;
 
   auto run = [&](typename E::Regs& R, unsigned char* buf, int64_t q) {
-    ChunkSrc<T> cs;
-    cs.rv = E::KC;
-    cs.r0 = q * E::KC;
-    E::store(R, buf, cs, PER_SAMPLE ? nullptr : c, Tn);
+    E::store(R, buf, c_rows != nullptr);
     __syncthreads();
     const int64_t qn = q + 2 <= qlast ? q + 2 : qlast;
-    E::load_full(R, O, A, G, d, p, qn);
+    E::load_full(R, O, A, G, d, p, qn, c_rows, Tn);
     if constexpr (PER_SAMPLE) {
       if (ch == 0)
         E::template compute<true>(buf, tmp);
@@ -733,6 +756,7 @@ static int pick_tile(int64_t n) {
 
 ContractPlan contract_plan(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias) {
   if (dl_eligible(dtype, B, Tn, d, p, has_bias)) return dl_plan(B, Tn, d, p);
+  if (dl32_eligible(dtype, B, Tn, d, p, has_bias)) return dl32_plan(B, Tn, d, p, has_bias);
   ContractPlan pl;
   pl.engine = 0;
   const int64_t mrows = d + (has_bias ? 1 : 0);
@@ -859,6 +883,8 @@ hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const vo
   hipError_t e;
   if (pl.engine == 1)
     e = launch_contract_dl(st, A, G, c, B, Tn, d, p, pl, ws, na, out);
+  else if (pl.engine == 2)
+    e = launch_contract_dl32(st, A, G, c, B, Tn, d, p, pl, ws, na, out, bias_out);
   else if (dtype == 1)
     e = launch_contract_d<bf16s>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
   else

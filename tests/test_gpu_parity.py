@@ -421,6 +421,58 @@ def test_dl_engine_workspace_reuse():
     np.testing.assert_array_equal(outs[0], outs[2])
 
 
+# ------------------------------------------------------------------ fp32 direct-to-LDS engine
+# fp32 layers with d, p >= 128, multiples of 4, and B*T a multiple of 32 go to
+# the direct-to-LDS fp32 engine (32-row chunks, 256x128 tiles, bias summed on
+# the side in the tiles that hold output row 0).
+DL32_CASES = [
+    # B, T, d, p, has_bias
+    (256, 1, 128, 128, True),     # T = 1: one sample per chunk row; 8 chunks -> K splits + reduce
+    (64, 16, 260, 132, True),     # two samples per chunk; ragged d (2 m-tiles) and p (clamped columns)
+    (8, 48, 384, 256, False),     # chunks straddle samples (48 rows per sample)
+    (2048, 1, 512, 640, True),    # 64 chunks, bias with several n-tiles
+    (4, 1024, 1152, 128, False),  # one sample per chunk, long K per sample
+    (32, 1, 4096, 1000, True),    # one chunk: one split, fused epilogue; 16 m-tiles, ragged last n-tile
+]
+
+
+@pytest.mark.parametrize("B,T,d,p,hb", DL32_CASES)
+def test_dl32_engine_clipped_sum(B, T, d, p, hb):
+    rng = np.random.default_rng(B * 104729 + d * 31 + p)
+    A = rng.standard_normal((B, T, d)).astype(np.float32)
+    G = rng.standard_normal((B, T, p)).astype(np.float32)
+    c_np = rng.uniform(0.0, 1.0, B).astype(np.float32)
+    c_np[0] = 1.0
+    if B > 2:
+        c_np[2] = 0.0
+    out = torch.empty(d, p, dtype=torch.float32, device=dev())
+    bout = torch.empty(p, dtype=torch.float32, device=dev()) if hb else None
+    dpc.dp_clipped_sum_noise(upload(A, "f32"), upload(G, "f32"), f32(c_np), 1.0, 0.0, 1.0, 0, 0, 0, out, bout)
+    torch.cuda.synchronize()
+    S, Sb = D.clipped_sum(A.astype(np.float64), G.astype(np.float64), c_np.astype(np.float64), bool(hb))
+    assert_sum(out.cpu().numpy(), S, "f32")
+    if hb:
+        assert_sum(bout.cpu().numpy(), Sb, "f32", what="bias sum")
+
+
+@pytest.mark.parametrize("B", [32, 8192])   # one chunk (fused epilogue) / 256 chunks (K splits + reduce)
+def test_dl32_engine_noise_bit_exact(B):
+    T, d, p = 1, 128, 132
+    rng = np.random.default_rng(13)
+    A = rng.standard_normal((B, T, d)).astype(np.float32)
+    G = rng.standard_normal((B, T, p)).astype(np.float32)
+    c = torch.zeros(B, dtype=torch.float32, device=dev())
+    out = torch.empty(d, p, dtype=torch.float32, device=dev())
+    bout = torch.empty(p, dtype=torch.float32, device=dev())
+    C, sigma, denom, seed, layer, step = 1.3, 0.725, 7.0, (3 << 32) | 9, 2, 4
+    dpc.dp_clipped_sum_noise(upload(A, "f32"), upload(G, "f32"), c, C, sigma, denom, seed, layer, step, out, bout)
+    torch.cuda.synchronize()
+    zw = N.weight_noise(d, p, seed, layer, step)
+    np.testing.assert_array_equal(out.cpu().numpy(), D.noised_mean_f32(np.zeros((d, p)), zw, C, sigma, denom))
+    zb = N.normals(p, seed, layer, 1, step)
+    np.testing.assert_array_equal(bout.cpu().numpy(), D.noised_mean_f32(np.zeros(p), zb, C, sigma, denom))
+
+
 # ------------------------------------------------------------------ ghost path shapes
 # bf16 ghost norms over 64-row tiles (T <= 384) and 128-row tiles (T > 384):
 # one tile with most rows past T, 3 and 10 tiles with ragged T, 15 tiles,
