@@ -747,6 +747,100 @@ __global__ __launch_bounds__(256) void k_reduce_noise_vec(const float* __restric
   }
 }
 
+// Many splits, small output. A workgroup takes a block of 4 weight rows x 16
+// columns: thread (lane sl = t / 16, element e = t % 16 = row r x column
+// quad) sums the float4 partials of splits sl, sl + 16, ... in split order;
+// the 16 lane sums are then added in lane order through LDS and each of 16
+// threads takes one column (4 rows = one Philox block) and writes the noised
+// mean. Blocks past the weight rows do the bias row, 64 columns each.
+// Requires p % 4 == 0 and 16-byte aligned ws (float4 partial rows).
+__global__ __launch_bounds__(256) void k_reduce_noise_wide(const float* __restrict__ ws, int64_t ks, int64_t d,
+                                                           int64_t p, int has_bias, NoiseArgs na,
+                                                           float* __restrict__ out, float* __restrict__ bias_out) {
+  __shared__ float4 part[16][16];
+  const int64_t split_stride = (d + (has_bias ? 1 : 0)) * p;
+  const int64_t nq = (d + 3) / 4, nc16 = (p + 15) / 16;
+  const int64_t nwb = nq * nc16;
+  const int t = threadIdx.x, sl = t >> 4, e = t & 15;
+  const bool bias_blk = (int64_t)blockIdx.x >= nwb;
+  int64_t m, cq;  // row and column quad this thread sums
+  bool valid;
+  if (!bias_blk) {
+    const int64_t q = blockIdx.x / nc16, c16 = blockIdx.x % nc16;
+    m = 4 * q + (e >> 2);
+    cq = 4 * c16 + (e & 3);
+    valid = m < d && 4 * cq < p;
+  } else {
+    m = d;
+    cq = 16 * ((int64_t)blockIdx.x - nwb) + e;
+    valid = 4 * cq < p;
+  }
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (valid) {
+    const float* base = ws + m * p + 4 * cq;
+    int64_t sp = sl;
+    for (; sp + 48 < ks; sp += 64) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(base + (sp + 16 * u) * split_stride);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s.x += v[u].x;
+        s.y += v[u].y;
+        s.z += v[u].z;
+        s.w += v[u].w;
+      }
+    }
+    for (; sp < ks; sp += 16) {
+      const float4 v = *reinterpret_cast<const float4*>(base + sp * split_stride);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+  }
+  part[sl][e] = s;
+  __syncthreads();
+  if (t >= 16) return;
+  if (!bias_blk) {
+    // thread t: column 4 * (4 * c16 + t / 4) + t % 4 of rows 4q .. 4q+3
+    const int64_t q = blockIdx.x / nc16, c16 = blockIdx.x % nc16;
+    const int qi = t >> 2, comp = t & 3;
+    const int64_t n = 4 * (4 * c16 + qi) + comp;
+    if (n >= p) return;
+    float r4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float acc = 0.f;
+      for (int l = 0; l < 16; ++l) {
+        const float4 v = part[l][4 * r + qi];
+        acc += comp == 0 ? v.x : comp == 1 ? v.y : comp == 2 ? v.z : v.w;
+      }
+      r4[r] = acc;
+    }
+    const f32x4 z = normals4((uint32_t)(q * p + n), 2u * na.layer, na.step, 0u, na.k0, na.k1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * q + r < d) out[(4 * q + r) * p + n] = noised_mean_spec(r4[r], na.sc, z[r], na.inv_denom);
+  } else {
+    const int64_t cqb = 16 * ((int64_t)blockIdx.x - nwb) + t;
+    if (4 * cqb >= p) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int l = 0; l < 16; ++l) {
+      const float4 v = part[l][t];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const f32x4 z = normals4((uint32_t)cqb, 2u * na.layer + 1u, na.step, 0u, na.k0, na.k1);
+    bias_out[4 * cqb + 0] = noised_mean_spec(acc.x, na.sc, z[0], na.inv_denom);
+    bias_out[4 * cqb + 1] = noised_mean_spec(acc.y, na.sc, z[1], na.inv_denom);
+    bias_out[4 * cqb + 2] = noised_mean_spec(acc.z, na.sc, z[2], na.inv_denom);
+    bias_out[4 * cqb + 3] = noised_mean_spec(acc.w, na.sc, z[3], na.inv_denom);
+  }
+}
+
 // ---------------------------------------------------------------- plans
 static int pick_tile(int64_t n) {
   // 64 or 128, whichever pads n less (ties -> 128)
@@ -890,6 +984,14 @@ hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const vo
   else
     e = launch_contract_d<float>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
   if (e != hipSuccess || pl.ks == 1) return e;
+  const int64_t std_threads = ((d + 3) / 4) * ((p + 3) / 4);
+  if (p % 4 == 0 && pl.ks >= 64 && std_threads < 32768) {
+    // many splits, few outputs: split lanes in parallel
+    const int64_t blocks = ((d + 3) / 4) * ((p + 15) / 16) + (has_bias ? (p + 63) / 64 : 0);
+    hipLaunchKernelGGL(k_reduce_noise_wide, dim3((unsigned)blocks), dim3(256), 0, st, ws, pl.ks, d, p, has_bias, na,
+                       out, bias_out);
+    return hipGetLastError();
+  }
   const int vec = (p % 4 == 0) && ((reinterpret_cast<uintptr_t>(out) & 15) == 0);
   if (vec && d % 4 == 0) {
     const int64_t threads = (d / 4) * (p / 4) + (has_bias ? p / 4 : 0);

@@ -473,6 +473,58 @@ def test_dl32_engine_noise_bit_exact(B):
     np.testing.assert_array_equal(bout.cpu().numpy(), D.noised_mean_f32(np.zeros(p), zb, C, sigma, denom))
 
 
+# ------------------------------------------------------------------ many K splits, small outputs
+# Narrow layers split K into >= 64 parts; the reduce then runs split lanes in
+# parallel (16 lanes per 4 x 16 output block, summed in lane order).
+WIDE_REDUCE_CASES = [
+    # dtype, B, T, d, p, has_bias
+    ("f32", 64, 1024, 27, 64, True),   # the unfolded 3-channel 3x3 conv layer shape
+    ("f32", 4096, 4, 29, 36, False),   # partial last row group, partial last 16-column block
+    ("bf16", 2048, 2, 13, 12, True),
+]
+
+
+def _wide_case(dtype, B, T, d, p, seed):
+    rng = np.random.default_rng(seed)
+    A = rng.standard_normal((B, T, d)).astype(np.float32)
+    G = rng.standard_normal((B, T, p)).astype(np.float32)
+    if dtype == "bf16":
+        A, G = W.f32_to_bf16_bits(A), W.f32_to_bf16_bits(G)
+    nbytes = dpc.dp_workspace_bytes(dpc.DP_BF16 if dtype == "bf16" else dpc.DP_F32, B, T, d, p)
+    assert nbytes >= 64 * (d + 1) * p * 4, "expected at least 64 K splits"
+    return A, G, rng
+
+
+@pytest.mark.parametrize("dtype,B,T,d,p,hb", WIDE_REDUCE_CASES)
+def test_wide_reduce_clipped_sum(dtype, B, T, d, p, hb):
+    A, G, rng = _wide_case(dtype, B, T, d, p, B + d)
+    c_np = rng.uniform(0.0, 1.0, B).astype(np.float32)
+    out = torch.empty(d, p, dtype=torch.float32, device=dev())
+    bout = torch.empty(p, dtype=torch.float32, device=dev()) if hb else None
+    dpc.dp_clipped_sum_noise(upload(A, dtype), upload(G, dtype), f32(c_np), 1.0, 0.0, 1.0, 0, 0, 0, out, bout)
+    torch.cuda.synchronize()
+    S, Sb = D.clipped_sum(W.as_f64(A, dtype), W.as_f64(G, dtype), c_np.astype(np.float64), hb)
+    assert_sum(out.cpu().numpy(), S, dtype)
+    if hb:
+        assert_sum(bout.cpu().numpy(), Sb, dtype, what="bias sum")
+
+
+@pytest.mark.parametrize("dtype,B,T,d,p,hb", WIDE_REDUCE_CASES)
+def test_wide_reduce_noise_bit_exact(dtype, B, T, d, p, hb):
+    A, G, _ = _wide_case(dtype, B, T, d, p, 17)
+    c = torch.zeros(B, dtype=torch.float32, device=dev())
+    out = torch.empty(d, p, dtype=torch.float32, device=dev())
+    bout = torch.empty(p, dtype=torch.float32, device=dev()) if hb else None
+    C, sigma, denom, seed, layer, step = 0.8, 1.1, 5.0, (9 << 32) | 2, 6, 3
+    dpc.dp_clipped_sum_noise(upload(A, dtype), upload(G, dtype), c, C, sigma, denom, seed, layer, step, out, bout)
+    torch.cuda.synchronize()
+    zw = N.weight_noise(d, p, seed, layer, step)
+    np.testing.assert_array_equal(out.cpu().numpy(), D.noised_mean_f32(np.zeros((d, p)), zw, C, sigma, denom))
+    if hb:
+        zb = N.normals(p, seed, layer, 1, step)
+        np.testing.assert_array_equal(bout.cpu().numpy(), D.noised_mean_f32(np.zeros(p), zb, C, sigma, denom))
+
+
 # ------------------------------------------------------------------ ghost path shapes
 # bf16 ghost norms over 64-row tiles (T <= 384) and 128-row tiles (T > 384):
 # one tile with most rows past T, 3 and 10 tiles with ragged T, 15 tiles,
