@@ -58,7 +58,7 @@ constexpr int64_t kMaxTilesPerSample = 65535;
 
 int64_t norm_ntiles(int dtype, int path, int64_t T, int64_t d, int64_t p, int has_bias) {
   if (path == DP_PATH_T1) return 1;
-  if (path == DP_PATH_GHOST) return dpk::ghost_ntiles(T);
+  if (path == DP_PATH_GHOST) return dpk::ghost_ntiles(dtype, T, d, p);
   const dpk::ExplicitPlan pl = dpk::explicit_plan(d, p, has_bias);
   return (int64_t)pl.mt * pl.nt;
 }

@@ -1,0 +1,261 @@
+// Ghost norm of a bf16 layer with long sequences, direct-to-LDS engine.
+//
+// The per-example squared norm of "Scalable and Efficient Training of Large
+// CNNs with DP", eq. (2.7) / Sec. 3.1 (ghost clipping):
+// n_i^2 = <A_i A_i^T, G_i G_i^T>_F, plus the bias term through
+// A_i A_i^T + 1 1^T, without forming A_i^T G_i. Both Grams are symmetric, so
+// only entries s <= t are computed; entries s < t count twice.
+//
+// Eligible layers: bf16, T >= 512, d and p multiples of 64.
+//
+// Work item = (sample i, Gram tile (r, c)): rows s in [256 r, 256 r + 256) x
+// columns t in [128 c, 128 c + 128), c >= 2r (every entry with s <= t lies in
+// such a tile). A T x T Gram has sum over r of (ceil(T/128) - 2r) tiles.
+// When the column block lies inside the row block (c = 2r or 2r + 1) its
+// rows are read from the row block's stage instead of being loaded again.
+//
+// gfx950 mapping:
+// - Features are streamed in chunks of 64: a chunk holds the tile's rows
+//   (256 + 128, or 256) x 128 bytes and goes from HBM straight to LDS with
+//   16-byte global_load_lds; the 16-byte pieces of row R are XOR-swizzled by
+//   (R / 2) % 8, so that the 16 rows a ds_read_b128 serves per pass land on
+//   64 distinct banks. The chunks of A_i come first (Gram of A), then those
+//   of G_i (Gram of G).
+// - A Gram product only needs row-major operands: an MFMA 32x32x16 operand
+//   is 8 consecutive features of one row, one ds_read_b128 (no transposes).
+// - 8 waves in a 4 x 2 grid of 64 x 64 sub-tiles; each lane holds both
+//   Grams' 64-entry accumulators until the epilogue forms
+//   sum_{s,t} w(s,t) (GA + bias) GG with w = 2 (s < t), 1 (s = t), 0 (s > t
+//   or past T).
+// - Three LDS stages, one barrier per chunk; the sample's last-arriving tile
+//   sums the tiles' parts in tile order (NormSink).
+// - Work items are XCD-grouped by sample: the tiles of one sample run on one
+//   XCD and share its rows in that XCD's L2.
+#include "dp_common.hpp"
+#include "dp_launch.hpp"
+#include "dp_lds.hpp"
+
+namespace dpk {
+
+namespace gw {
+constexpr int BM = 256, BN = 128;  // Gram tile rows x columns
+constexpr int KC = 64;             // features per chunk
+constexpr int ROWB = KC * 2;       // LDS bytes per row and chunk
+constexpr int NW = 8, NT = 64 * NW;
+constexpr int STAGES = 3;
+constexpr int STAGE_MAX = (BM + BN) * ROWB;  // 48 KB
+constexpr int LDS = STAGES * STAGE_MAX;
+constexpr int WGM = 4, WGN = 2;              // wave grid
+constexpr int WM = BM / WGM, WN = BN / WGN;  // 64 x 64
+static_assert(WM == 64 && WN == 64, "two 32-blocks per operand and wave");
+static_assert(LDS <= 160 * 1024, "LDS budget");
+
+// TIN: the column block's rows are inside the row block (not loaded twice).
+template <bool TIN>
+struct Cfg {
+  static constexpr int ROWS = TIN ? BM : BM + BN;
+  static constexpr int STAGE = ROWS * ROWB;
+  static constexpr int LPC = STAGE / (1024 * NW);  // 1 KB loads per wave per chunk
+  static_assert(LPC * 1024 * NW == STAGE, "whole 1 KB loads per wave");
+};
+}  // namespace gw
+
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
+struct GwArgs {
+  int64_t B, Tn, d, p;
+  int has_bias;
+  int nbc;     // column blocks: ceil(T / 128)
+  int ntiles;  // tiles per sample
+};
+
+// Row block r and column block c of tile `tile` (r-major, c from 2r).
+__device__ __forceinline__ void gw_tile_rc(int tile, int nbc, int* r, int* c) {
+  int rr = 0, rem = tile;
+  while (rem >= nbc - 2 * rr) {
+    rem -= nbc - 2 * rr;
+    ++rr;
+  }
+  *r = rr;
+  *c = 2 * rr + rem;
+}
+
+template <bool TIN>
+__device__ __forceinline__ float gw_item(const bf16s* __restrict__ Ai, const bf16s* __restrict__ Gi, const GwArgs& a,
+                                         int r, int c, unsigned char* lds) {
+  using C = gw::Cfg<TIN>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % gw::WGM, wn = wave / gw::WGM;
+  const int64_t row0 = (int64_t)r * gw::BM;       // first Gram row of the tile
+  const int64_t col0 = (int64_t)c * gw::BN;       // first Gram column of the tile
+  const int toff = TIN ? (int)(col0 - row0) : gw::BM;  // stage row of the column block's first row
+  const int64_t nA = a.d / gw::KC, nG = a.p / gw::KC, n = nA + nG;
+
+  // ---- this lane's 16-byte pieces: load i of the wave covers stage rows
+  // R = 8 (wave + 8 i) + lane / 8, slot lane % 8, which holds logical piece
+  // slot ^ ((R / 2) % 8) -- the same piece for every i. grow[i] is the Gram
+  // row (clamped: rows past T hold finite values and get weight 0).
+  const uint32_t piece16 = (uint32_t)(((lane & 7) ^ ((4 * wave + (lane >> 4)) & 7)) * 16);
+  uint32_t grow[C::LPC];
+#pragma unroll
+  for (int i = 0; i < C::LPC; ++i) {
+    const int R = 8 * (wave + gw::NW * i) + (lane >> 3);
+    int64_t g = R < gw::BM ? row0 + R : col0 + (R - gw::BM);
+    if (g > a.Tn - 1) g = a.Tn - 1;
+    grow[i] = (uint32_t)g;
+  }
+  const uint32_t rowbA = (uint32_t)(a.d * 2), rowbG = (uint32_t)(a.p * 2);  // row bytes
+  auto issue = [&](int64_t q, int stage) {
+    const uint32_t sl = lds_addr(lds) + stage * gw::STAGE_MAX + wave * 1024;
+    const bool inA = q < nA;
+    const bf16s* g = inA ? Ai + q * gw::KC : Gi + (q - nA) * gw::KC;
+    const uint32_t rowb = inA ? rowbA : rowbG;
+#pragma unroll
+    for (int i = 0; i < C::LPC; ++i) dma16(g, grow[i] * rowb + piece16, sl + 1024 * gw::NW * i);
+  };
+
+  // ---- per-lane LDS read offsets: row j = lane % 32 of a 32-row block,
+  // logical piece 2 kk + lane / 32 for k-step kk (16 features); the swizzle
+  // term depends on j only (block starts are multiples of 16 rows)
+  const int j = lane & 31, h = lane >> 5;
+  uint32_t rd[gw::KC / 16];
+#pragma unroll
+  for (int kk = 0; kk < gw::KC / 16; ++kk) rd[kk] = j * gw::ROWB + (((2 * kk + h) ^ ((j >> 1) & 7)) * 16);
+  const int ra0 = wm * gw::WM, rg0 = toff + wn * gw::WN;  // stage rows of the wave's operand blocks
+
+  f32x16 accA[2][2], accG[2][2];
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        accA[bi][bj][e] = 0.f;
+        accG[bi][bj][e] = 0.f;
+      }
+
+  // all operand reads of a chunk are issued before its MFMAs
+  auto compute = [&](uint32_t sb, f32x16 (&acc)[2][2]) {
+    u32x4 fa[gw::KC / 16][2], fb[gw::KC / 16][2];
+#pragma unroll
+    for (int kk = 0; kk < gw::KC / 16; ++kk)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        fa[kk][b] = *(const lds_u32x4*)(uintptr_t)(sb + rd[kk] + (ra0 + 32 * b) * gw::ROWB);
+        fb[kk][b] = *(const lds_u32x4*)(uintptr_t)(sb + rd[kk] + (rg0 + 32 * b) * gw::ROWB);
+      }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+#pragma unroll
+    for (int kk = 0; kk < gw::KC / 16; ++kk)
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mfma32_bf16(fa[kk][bi], fb[kk][bj], acc[bi][bj]);
+  };
+
+  // ---- pipeline: chunk q in stage q % 3; loads for chunk q+2 go out once
+  // every wave is past chunk q-1 (the barrier), while chunk q is computed.
+  // Two loops (A chunks, then G chunks) so that each body updates one
+  // accumulator set.
+  auto step = [&](int64_t q) -> uint32_t {
+    if (q + 1 < n)
+      wait_vmcnt<C::LPC>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    if (q + 2 < n) issue(q + 2, (int)((q + 2) % 3));
+    return lds_addr(lds) + (uint32_t)((q % 3) * gw::STAGE_MAX);
+  };
+  issue(0, 0);
+  if (n > 1) issue(1, 1);
+  for (int64_t q = 0; q < nA; ++q) compute(step(q), accA);
+  for (int64_t q = nA; q < n; ++q) compute(step(q), accG);
+
+  // ---- epilogue: weighted Frobenius product of the tile
+  const float one = a.has_bias ? 1.0f : 0.0f;
+  const bool above = row0 + gw::BM <= col0 && col0 + gw::BN <= a.Tn;  // every entry s < t < T
+  float s = 0.f;
+  if (above) {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += (accA[bi][bj][e] + one) * accG[bi][bj][e];
+    s *= 2.0f;
+  } else {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int64_t srow = row0 + ra0 + 32 * bi + acc_row(e, lane);
+          const int64_t tcol = col0 + wn * gw::WN + 32 * bj + acc_col(lane);
+          const float w = (srow >= a.Tn || tcol >= a.Tn || srow > tcol) ? 0.0f : (srow == tcol ? 1.0f : 2.0f);
+          s += w * ((accA[bi][bj][e] + one) * accG[bi][bj][e]);
+        }
+  }
+  return s;
+}
+
+__global__ __launch_bounds__(gw::NT, 1) void k_ghost_wide(const bf16s* __restrict__ A, const bf16s* __restrict__ G,
+                                                          GwArgs a, NormSink sink) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+  __shared__ float red[gw::NW];
+  int64_t i, tile;
+  xcd_group_map(blockIdx.x, a.ntiles, &i, &tile);
+  if (i >= a.B) return;  // whole workgroup, before any barrier
+  int r, c;
+  gw_tile_rc((int)tile, a.nbc, &r, &c);
+  // the sample's bases are wave-uniform; readfirstlane lets them live in SGPRs
+  // (the direct-to-LDS loads take a scalar base)
+  const bf16s* Ai = uniform_ptr(A + i * a.Tn * a.d);
+  const bf16s* Gi = uniform_ptr(G + i * a.Tn * a.p);
+  const bool tin = c < 2 * r + 2;  // column block inside the row block
+  float s = tin ? gw_item<true>(Ai, Gi, a, r, c, lds) : gw_item<false>(Ai, Gi, a, r, c, lds);
+  s = block_sum<gw::NT>(s, red);
+  if (threadIdx.x == 0) norm_sink_tile(sink, i, tile, s);
+}
+
+bool ghost_wide_eligible(int dtype, int64_t Tn, int64_t d, int64_t p) {
+  // per-sample byte offsets are 32-bit: T * max(d, p) * 2 < 2^32
+  return dtype == 1 && Tn >= 512 && d % gw::KC == 0 && p % gw::KC == 0 &&
+         Tn * (d > p ? d : p) * 2 < (1ll << 32) - 4096;
+}
+
+int64_t ghost_wide_ntiles(int64_t Tn) {
+  const int64_t nbc = (Tn + gw::BN - 1) / gw::BN;
+  int64_t n = 0;
+  for (int64_t r = 0; 2 * r < nbc; ++r) n += nbc - 2 * r;
+  return n;
+}
+
+hipError_t launch_ghost_wide(hipStream_t st, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
+                             int64_t p, int has_bias, const NormSink& sink) {
+  GwArgs a;
+  a.B = B;
+  a.Tn = Tn;
+  a.d = d;
+  a.p = p;
+  a.has_bias = has_bias;
+  a.nbc = (int)((Tn + gw::BN - 1) / gw::BN);
+  a.ntiles = (int)ghost_wide_ntiles(Tn);
+  const int64_t groups8 = (B + 7) / 8;
+  const dim3 grid((unsigned)(groups8 * 8 * a.ntiles));
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ghost_wide),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, gw::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_ghost_wide, grid, dim3(gw::NT), gw::LDS, st, static_cast<const bf16s*>(A),
+                     static_cast<const bf16s*>(G), a, sink);
+  return hipGetLastError();
+}
+
+}  // namespace dpk

@@ -39,7 +39,13 @@ hipError_t launch_contract_dl32(hipStream_t st, const void* A, const void* G, co
                                 float* out, float* bias_out);
 ExplicitPlan explicit_plan(int64_t d, int64_t p, int has_bias);
 int ghost_tile_size(int64_t T);
-int64_t ghost_ntiles(int64_t T);
+// Gram tiles per sample of the ghost kernel that dp_ghost_norm runs for this layer
+int64_t ghost_ntiles(int dtype, int64_t T, int64_t d, int64_t p);
+// bf16 long-sequence ghost engine (256 x 128 Gram tiles, direct-to-LDS)
+bool ghost_wide_eligible(int dtype, int64_t Tn, int64_t d, int64_t p);
+int64_t ghost_wide_ntiles(int64_t Tn);
+hipError_t launch_ghost_wide(hipStream_t st, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
+                             int64_t p, int has_bias, const NormSink& sink);
 
 hipError_t launch_norm_t1(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t d, int64_t p,
                           int has_bias, int accumulate, float* sqnorm);

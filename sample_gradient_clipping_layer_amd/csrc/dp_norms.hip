@@ -343,7 +343,8 @@ hipError_t launch_norm_t1(hipStream_t st, int dtype, const void* A, const void* 
 
 int ghost_tile_size(int64_t T) { return T <= 384 ? 64 : 128; }
 
-int64_t ghost_ntiles(int64_t T) {
+int64_t ghost_ntiles(int dtype, int64_t T, int64_t d, int64_t p) {
+  if (ghost_wide_eligible(dtype, T, d, p)) return ghost_wide_ntiles(T);
   const int64_t ts = ghost_tile_size(T);
   const int64_t nb = (T + ts - 1) / ts;
   return nb * (nb + 1) / 2;
@@ -370,6 +371,7 @@ hipError_t launch_ghost_t(hipStream_t st, const void* A, const void* G, int64_t 
 
 hipError_t launch_ghost(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
                         int64_t p, int has_bias, const NormSink& sink) {
+  if (ghost_wide_eligible(dtype, Tn, d, p)) return launch_ghost_wide(st, A, G, B, Tn, d, p, has_bias, sink);
   const int ts = ghost_tile_size(Tn);
   if (dtype == 1) {
     if (ts == 64) return launch_ghost_t<bf16s, 64>(st, A, G, B, Tn, d, p, has_bias, sink);

@@ -526,9 +526,10 @@ def test_wide_reduce_noise_bit_exact(dtype, B, T, d, p, hb):
 
 
 # ------------------------------------------------------------------ ghost path shapes
-# bf16 ghost norms over 64-row tiles (T <= 384) and 128-row tiles (T > 384):
-# one tile with most rows past T, 3 and 10 tiles with ragged T, 15 tiles,
-# 36 tiles, bias on and off, accumulation into sqnorm.
+# bf16 ghost norms over 64-row tiles (T <= 384), 128-row tiles (T > 384) and
+# 256 x 128 tiles (T >= 512 with d and p multiples of 64): one tile with most
+# rows past T, ragged T, up to 36 tiles per sample, bias on and off,
+# accumulation into sqnorm.
 GHOST_CASES = [
     # B, T, d, p, has_bias
     (3, 5, 128, 256, True),      # 1 tile of 64
@@ -538,7 +539,12 @@ GHOST_CASES = [
     (3, 200, 128, 256, True),    # 10 tiles, ragged
     (2, 300, 256, 128, False),   # 15 tiles, ragged
     (2, 385, 64, 192, True),     # 128-row tiles: 10, ragged
-    (1, 1000, 128, 64, False),   # 128-row tiles: 36
+    (1, 1000, 128, 64, False),   # 256 x 128 tiles (T >= 512, d and p multiples of 64): 28, ragged
+    (2, 512, 64, 128, True),     # 256 x 128 tiles: 6
+    (3, 600, 128, 192, False),   # 9 tiles, last row block 88 rows
+    (1, 1100, 192, 64, True),    # 25 tiles, ragged
+    (4, 1024, 64, 64, False),    # 20 tiles
+    (9, 520, 64, 64, True),      # 9 tiles; samples on two XCD rounds
 ]
 
 
