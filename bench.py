@@ -82,6 +82,7 @@ def _algorithmic(wl, T, d, p, kind):
 
 
 DEVICE_GEN_BYTES = 8 << 30
+BREAKDOWN_STEPS = 50
 
 
 def run_gpu(wl, steps, warmup):
@@ -94,8 +95,13 @@ def run_gpu(wl, steps, warmup):
     sum with noise scale sigma * C_t[l], and the update of its bound from this
     step's norms; the new bounds are read back to the host once per step
     (they are host arguments of the next step's calls), inside the timed
-    region. Returns wall seconds, per-call event times [steps, calls], the
-    kinds and layers of the calls, and the number of rotated input sets."""
+    region. The throughput steps run with nothing else on the stream; then
+    up to BREAKDOWN_STEPS more steps run with a HIP event pair around every
+    call, for the per-call durations. Returns the wall seconds and the GPU
+    milliseconds (events on the stream) of the throughput steps, per-call
+    event times [breakdown steps, calls], the kinds and layers of the calls,
+    the number of rotated input sets and whether inputs were drawn on the
+    device."""
     import torch
     import sample_gradient_clipping_layer_amd as dpc
 
@@ -156,13 +162,13 @@ def run_gpu(wl, steps, warmup):
         kinds = [("norm", l) for l in range(L)] + [("clip", -1)] + [("sum", l) for l in range(L)]
 
     ncalls = len(kinds)
+    bsteps = min(steps, BREAKDOWN_STEPS)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ncalls)]
-          for _ in range(steps)]
+          for _ in range(bsteps)]
 
-    def step(k, timed):
+    def step(k, e=None):
         nonlocal C_t
         layers = sets[k % n_sets]
-        e = ev[k] if timed else None
         j = 0
 
         def call(fn, *args, **kw):
@@ -192,19 +198,29 @@ def run_gpu(wl, steps, warmup):
     if not wl.per_layer:
         C_t = None
     for k in range(warmup):
-        step(k, False)
+        step(k)
+    # throughput: `steps` steps with nothing else on the stream
     torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    g0.record(stream)
     for k in range(steps):
-        step(k, True)
+        step(warmup + k)
+    g1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    call_ms = np.array([[a.elapsed_time(b) for (a, b) in ev[k]] for k in range(steps)])  # [steps, ncalls]
+    gpu_ms = g0.elapsed_time(g1)
+    # per-call durations: further steps with an event pair around every call
+    # (the markers cost a little GPU time, so these steps are timed apart)
+    for k in range(bsteps):
+        step(warmup + steps + k, ev[k])
+    torch.cuda.synchronize()
+    call_ms = np.array([[a.elapsed_time(b) for (a, b) in ev[k]] for k in range(bsteps)])  # [bsteps, ncalls]
     for o in outs:
         assert torch.isfinite(o).all().item(), "non-finite output"
     if wl.per_layer:
         assert all(math.isfinite(v) and v > 0 for v in C_t), f"adaptive bounds {C_t}"
-    return wall, call_ms, shapes, kinds, n_sets, on_device
+    return wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device
 
 
 def cpu_baseline(wl, budget_s=12.0, step_s=3.0, max_step_s=25.0):
@@ -313,7 +329,7 @@ def main():
         copy_probe()
         return
     wl = W.WORKLOADS[a.workload]
-    wall, call_ms, shapes, kinds, n_sets, on_device = run_gpu(wl, a.steps, a.warmup)
+    wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device = run_gpu(wl, a.steps, a.warmup)
     L = len(shapes)
     ms_per_step = 1e3 * wall / a.steps
     value = wl.B * a.steps / wall
@@ -369,7 +385,9 @@ def main():
         "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic", "config": cfg,
         "roofline": roof,
-        "events_ms_per_step": round(float(call_ms.sum(axis=1).mean()), 4),
+        "gpu_ms_per_step": round(gpu_ms / a.steps, 4),
+        "calls_ms_per_step": round(float(call_ms.sum(axis=1).mean()), 4),
+        "breakdown_steps": int(call_ms.shape[0]),
     }
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)

@@ -40,9 +40,20 @@
 namespace dpk {
 
 
+// K rows per chunk and LDS stages of the pipeline
+#ifndef DL_KC
+#define DL_KC 64
+#endif
+#ifndef DL_STAGES
+#define DL_STAGES 3
+#endif
+constexpr int kDlKC = DL_KC;
+constexpr int kDlStages = DL_STAGES;
+static_assert(kDlKC % 16 == 0 && kDlStages >= 3, "chunk of whole MFMA k-steps; at least 3 stages");
+
 template <int BM, int BN, int STAGES, int NW>
 struct DlCfg {
-  static constexpr int KC = 64;                   // K rows per chunk
+  static constexpr int KC = kDlKC;                // K rows per chunk
   static constexpr int NT = 64 * NW;              // threads
   static constexpr int RA = BM * 2, RG = BN * 2;  // LDS row bytes
   static constexpr int A_BYTES = KC * RA, G_BYTES = KC * RG;
@@ -57,7 +68,7 @@ struct DlCfg {
   static_assert(LA * 1024 * NW == A_BYTES && LG * 1024 * NW == G_BYTES, "whole 1 KB loads per wave");
   static_assert(NBM >= 1 && NBN >= 1 && WM % 32 == 0 && WN % 32 == 0, "32x32 blocks");
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  static_assert(LPC * (STAGES - 1) <= 63, "vmcnt range");
+  static_assert(LPC * (STAGES - 2) <= 63, "vmcnt range");
 };
 
 
@@ -75,13 +86,19 @@ __device__ __forceinline__ u32x4 frag_tr(uint32_t addr, int off, int four_rows) 
   return r;
 }
 
+// k-steps whose operand reads are grouped ahead of their MFMAs
+#ifndef DL_READ_GROUP
+#define DL_READ_GROUP 1
+#endif
+constexpr int kDlReadGroup = DL_READ_GROUP;
+
 struct DlArgs {
   int64_t d, p;
-  int64_t cps;              // chunks per sample (T / 64)
+  int64_t cps;              // chunks per sample (T / KC)
   int mt, nt;
   int64_t ks;               // K splits
   int64_t chunks_per_split;
-  int64_t nchunks;          // B * T / 64
+  int64_t nchunks;          // B * T / KC
   int m_fast;               // work-item order: tile row index fastest
   NoiseArgs na;
 };
@@ -93,7 +110,6 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
                                                             const float* __restrict__ c, float* __restrict__ ws,
                                                             float* __restrict__ out, DlArgs a) {
   using C = DlCfg<BM, BN, STAGES, NW>;
-  static_assert(STAGES == 3, "pipeline written for three stages");
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
 
   // ---- work item (XCD-contiguous)
@@ -116,7 +132,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
   const int wm = wave % C::WGM, wn = wave / C::WGM;
 
   // ---- per-lane global byte offsets of this lane's 16-byte pieces within a chunk
-  // (< 64 * max(d, p) * 2 < 2^32)
+  // (< KC * max(d, p) * 2 < 2^32)
   uint32_t offA[C::LA], offG[C::LG];
 #pragma unroll
   for (int i = 0; i < C::LA; ++i) {
@@ -180,40 +196,49 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
     for (int bi = 0; bi < C::NBM; ++bi) ra[bi] = sbase + rdA[bi];
 #pragma unroll
     for (int bj = 0; bj < C::NBN; ++bj) rg[bj] = sbase + rdG[bj];
+    // operand reads of KG k-steps are issued together, ahead of their MFMAs
+    constexpr int KG = kDlReadGroup;
 #pragma unroll
-    for (int kk = 0; kk < C::KC / 16; ++kk) {
-      u32x4 fa[C::NBM], fg[C::NBN];
+    for (int k0 = 0; k0 < C::KC / 16; k0 += KG) {
+      u32x4 fa[KG][C::NBM], fg[KG][C::NBN];
 #pragma unroll
-      for (int bi = 0; bi < C::NBM; ++bi) fa[bi] = frag_tr(ra[bi], kk * 16 * C::RA, 4 * C::RA);
+      for (int kk = 0; kk < KG; ++kk) {
 #pragma unroll
-      for (int bj = 0; bj < C::NBN; ++bj) fg[bj] = frag_tr(rg[bj], kk * 16 * C::RG, 4 * C::RG);
+        for (int bi = 0; bi < C::NBM; ++bi) fa[kk][bi] = frag_tr(ra[bi], (k0 + kk) * 16 * C::RA, 4 * C::RA);
 #pragma unroll
-      for (int bi = 0; bi < C::NBM; ++bi)
+        for (int bj = 0; bj < C::NBN; ++bj) fg[kk][bj] = frag_tr(rg[bj], (k0 + kk) * 16 * C::RG, 4 * C::RG);
+      }
+      if constexpr (KG > 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int bj = 0; bj < C::NBN; ++bj) {
-          if (decltype(fresh)::value && kk == 0)
-            tmp[bi][bj] = mfma32_bf16(fa[bi], fg[bj], f32x16{});
-          else
-            tmp[bi][bj] = mfma32_bf16(fa[bi], fg[bj], tmp[bi][bj]);
-        }
+      for (int kk = 0; kk < KG; ++kk)
+#pragma unroll
+        for (int bi = 0; bi < C::NBM; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < C::NBN; ++bj) {
+            if (decltype(fresh)::value && k0 + kk == 0)
+              tmp[bi][bj] = mfma32_bf16(fa[kk][bi], fg[kk][bj], f32x16{});
+            else
+              tmp[bi][bj] = mfma32_bf16(fa[kk][bi], fg[kk][bj], tmp[bi][bj]);
+          }
     }
   };
 
-  // ---- pipeline: chunk q in stage q % 3; loads for chunk it+2 go out once
-  // every wave is past chunk it-1 (the barrier), while chunk it is computed.
+  // ---- pipeline: chunk q in stage q % STAGES; loads for chunk it+STAGES-1
+  // go out once every wave is past chunk it-1 (the barrier), while chunk it
+  // is computed.
   int64_t sample = q0 / a.cps;
   int64_t in_sample = q0 - sample * a.cps;
-  if (nq > 0) issue(q0, 0);
-  if (nq > 1) issue(q0 + 1, 1);
+#pragma unroll
+  for (int c = 0; c < STAGES - 1; ++c)
+    if (c < nq) issue(q0 + c, c);
   for (int it = 0; it < nq; ++it) {
-    if (it + 1 < nq)
-      wait_vmcnt<C::LPC>();
-    else
-      wait_vmcnt<0>();
+    // chunks it+1 .. it+STAGES-2 (those issued) may still be in flight
+    const int later = nq - 1 - it < STAGES - 2 ? nq - 1 - it : STAGES - 2;
+    wait_chunks<C::LPC, STAGES - 2>(later);
     lds_barrier();  // chunk it landed for every wave; every wave is done with chunk it-1
-    if (it + 2 < nq) issue(q0 + it + 2, (it + 2) % 3);
+    if (it + STAGES - 1 < nq) issue(q0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
 
-    const uint32_t sb = lds_addr(lds) + (uint32_t)((it % 3) * C::STAGE);
+    const uint32_t sb = lds_addr(lds) + (uint32_t)((it % STAGES) * C::STAGE);
     if (it == 0 || in_sample == 0)
       compute(sb, std::true_type{});
     else
@@ -278,7 +303,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
 // ---------------------------------------------------------------- plan
 bool dl_eligible(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias) {
   (void)B;
-  return dtype == 1 && !has_bias && Tn % 64 == 0 && d % 8 == 0 && p % 8 == 0 && 64 * (d > p ? d : p) < (1ll << 31);
+  return dtype == 1 && !has_bias && Tn % kDlKC == 0 && d % 8 == 0 && p % 8 == 0 &&
+         kDlKC * (d > p ? d : p) < (1ll << 31);
 }
 
 // Tile and K split for the direct-load engine from a cost model: rounds of
@@ -289,13 +315,13 @@ ContractPlan dl_plan(int64_t B, int64_t Tn, int64_t d, int64_t p) {
   static const int tiles[2][2] = {{128, 128}, {256, 128}};
   static const double eff[2] = {0.40, 0.55};
   const double cu_peak = 2.5e15 / 256.0;
-  const int64_t nchunks = B * Tn / 64;
+  const int64_t nchunks = B * Tn / kDlKC;
   ContractPlan best{};
   double best_t = 1e300;
   for (int ti = 0; ti < 2; ++ti) {
     const int bm = tiles[ti][0], bn = tiles[ti][1];
     const int64_t mt = (d + bm - 1) / bm, nt = (p + bn - 1) / bn;
-    const double chunk_s = 2.0 * bm * bn * 64 / (cu_peak * eff[ti]);
+    const double chunk_s = 2.0 * bm * bn * kDlKC / (cu_peak * eff[ti]);
     const int64_t ks_max = nchunks < 512 ? nchunks : 512;
     for (int64_t ks = 1; ks <= ks_max; ++ks) {
       const int64_t cpsplit = (nchunks + ks - 1) / ks;
@@ -330,7 +356,7 @@ struct DlPtrs {
 
 template <int BM, int BN, int NW>
 static hipError_t launch_dl_t(hipStream_t st, const DlPtrs& P, const DlArgs& a, int64_t items) {
-  constexpr int S = 3;
+  constexpr int S = kDlStages;
   using C = DlCfg<BM, BN, S, NW>;
   const int64_t per = (items + 7) / 8;
   const dim3 grid((unsigned)(per * 8));
@@ -357,12 +383,12 @@ hipError_t launch_contract_dl(hipStream_t st, const void* A, const void* G, cons
   DlArgs a;
   a.d = d;
   a.p = p;
-  a.cps = Tn / 64;
+  a.cps = Tn / kDlKC;
   a.mt = pl.mt;
   a.nt = pl.nt;
   a.ks = pl.ks;
   a.chunks_per_split = pl.units_per_split;
-  a.nchunks = B * Tn / 64;
+  a.nchunks = B * Tn / kDlKC;
   a.m_fast = pl.mt <= pl.nt ? 1 : 0;
   a.na = na;
   const int64_t items = (int64_t)pl.mt * pl.nt * pl.ks;
