@@ -473,6 +473,39 @@ def test_dl32_engine_noise_bit_exact(B):
     np.testing.assert_array_equal(bout.cpu().numpy(), D.noised_mean_f32(np.zeros(p), zb, C, sigma, denom))
 
 
+# ------------------------------------------------------------------ single-tile ghost samples
+# Samples of at most one or two Gram tiles with wide and narrow feature
+# counts on either side, bias on and off, accumulation into sqnorm.
+SPLIT_CASES = [
+    # dtype, B, T, d, p, has_bias
+    ("bf16", 5, 128, 1024, 192, True),   # d >> p, bias
+    ("bf16", 7, 128, 128, 640, True),    # p >> d, bias
+    ("bf16", 3, 100, 256, 384, False),   # rows past T
+    ("bf16", 20, 128, 64, 64, True),     # 20 samples over 3 XCD groups
+    ("f32", 6, 64, 320, 64, True),
+    ("f32", 4, 128, 96, 224, True),
+]
+
+
+@pytest.mark.parametrize("dtype,B,T,d,p,hb", SPLIT_CASES)
+def test_ghost_single_tile_samples(dtype, B, T, d, p, hb):
+    rng = np.random.default_rng(B * 977 + d + p)
+    A = (rng.standard_normal((B, T, d)) / math.sqrt(d)).astype(np.float32)
+    G = (rng.standard_normal((B, T, p)) / math.sqrt(p)).astype(np.float32)
+    if dtype == "bf16":
+        A, G = W.f32_to_bf16_bits(A), W.f32_to_bf16_bits(G)
+    Ad, Gd = upload(A, dtype), upload(G, dtype)
+    sq = torch.full((B,), 3.0, dtype=torch.float32, device=dev())
+    assert dpc.dp_ghost_norm(Ad, Gd, sq, has_bias=hb, mode=dpc.MODE_GHOST, accumulate=True) == dpc.PATH_GHOST
+    torch.cuda.synchronize()
+    sq_or = D.layer_sqnorms(W.as_f64(A, dtype), W.as_f64(G, dtype), hb)
+    assert_norms(sq.cpu().numpy() - 3.0, sq_or, dtype, what="accumulated sqnorm")
+    sq2 = torch.empty(B, dtype=torch.float32, device=dev())
+    dpc.dp_ghost_norm(Ad, Gd, sq2, has_bias=hb, mode=dpc.MODE_GHOST)
+    torch.cuda.synchronize()
+    assert_norms(sq2.cpu().numpy(), sq_or, dtype)
+
+
 # ------------------------------------------------------------------ many K splits, small outputs
 # Narrow layers split K into >= 64 parts; the reduce then runs split lanes in
 # parallel (16 lanes per 4 x 16 output block, summed in lane order).
