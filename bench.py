@@ -85,7 +85,7 @@ DEVICE_GEN_BYTES = 8 << 30
 BREAKDOWN_STEPS = 50
 
 
-def run_gpu(wl, steps, warmup):
+def run_gpu(wl, steps, warmup, nstreams=1):
     """Times `steps` whole steps of the workload after `warmup` untimed ones.
 
     Global clipping (one norm per example over all layers): every layer's
@@ -141,6 +141,11 @@ def run_gpu(wl, steps, warmup):
     outs = [torch.empty(d, p, dtype=torch.float32, device=dev) for (T, d, p) in shapes]
     bouts = [torch.empty(p, dtype=torch.float32, device=dev) if wl.has_bias else None for (T, d, p) in shapes]
     stream = torch.cuda.current_stream()
+    # with nstreams > 1 (global clipping, throughput steps) the clipped sums of the layers
+    # go round-robin to side streams once the clip factors are ready; each layer keeps
+    # its own stream, output and workspace, and the next step's clip factors wait for them
+    side = [torch.cuda.Stream(device=dev) for _ in range(nstreams)] if nstreams > 1 and not wl.per_layer else []
+    ws_sum = ([torch.empty_like(w) for w in ws] if side else ws)
     L = len(shapes)
 
     if wl.per_layer:
@@ -166,10 +171,13 @@ def run_gpu(wl, steps, warmup):
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ncalls)]
           for _ in range(bsteps)]
 
+    sum_done = [None] * len(shapes)
+
     def step(k, e=None):
         nonlocal C_t
         layers = sets[k % n_sets]
         j = 0
+        use_side = bool(side) and e is None
 
         def call(fn, *args, **kw):
             nonlocal j
@@ -190,10 +198,32 @@ def run_gpu(wl, steps, warmup):
             return
         for l, (A, G) in enumerate(layers):
             call(dpc.dp_ghost_norm, A, G, sq, has_bias=wl.has_bias, accumulate=l > 0, workspace=ws[l])
-        call(dpc.dp_clip_factors, sq, wl.C, c)
+        if not use_side:
+            join()
+            call(dpc.dp_clip_factors, sq, wl.C, c)
+            for l, (A, G) in enumerate(layers):
+                call(dpc.dp_clipped_sum_noise, A, G, c, wl.C, wl.sigma, float(B), wl.seed, l, k, outs[l], bouts[l],
+                     workspace=ws[l])
+            return
+        join()  # the previous step's sums still read c
+        dpc.dp_clip_factors(sq, wl.C, c)
+        ready = torch.cuda.Event()
+        ready.record(stream)
         for l, (A, G) in enumerate(layers):
-            call(dpc.dp_clipped_sum_noise, A, G, c, wl.C, wl.sigma, float(B), wl.seed, l, k, outs[l], bouts[l],
-                 workspace=ws[l])
+            s_l = side[l % len(side)]
+            s_l.wait_event(ready)
+            with torch.cuda.stream(s_l):
+                dpc.dp_clipped_sum_noise(A, G, c, wl.C, wl.sigma, float(B), wl.seed, l, k, outs[l], bouts[l],
+                                         workspace=ws_sum[l])
+                done = torch.cuda.Event()
+                done.record(s_l)
+            sum_done[l] = done
+
+    def join():
+        for l, ev_l in enumerate(sum_done):
+            if ev_l is not None:
+                stream.wait_event(ev_l)
+                sum_done[l] = None
 
     if not wl.per_layer:
         C_t = None
@@ -206,6 +236,7 @@ def run_gpu(wl, steps, warmup):
     g0.record(stream)
     for k in range(steps):
         step(warmup + k)
+    join()
     g1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -318,6 +349,9 @@ def main():
     ap.add_argument("--workload", default="gpt-block-t128", choices=W.WORKLOAD_ORDER)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="print per-call times to stderr")
+    ap.add_argument("--streams", type=int, default=None,
+                    help="side streams for the layers' clipped sums in the throughput steps (global clipping); "
+                         "default 3 for layer sets of at most 8 layers, else 1")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (HBM counter calibration)")
     a = ap.parse_args()
@@ -329,7 +363,8 @@ def main():
         copy_probe()
         return
     wl = W.WORKLOADS[a.workload]
-    wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device = run_gpu(wl, a.steps, a.warmup)
+    nstreams = a.streams if a.streams is not None else (3 if wl.n_layers <= 8 and not wl.per_layer else 1)
+    wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device = run_gpu(wl, a.steps, a.warmup, nstreams)
     L = len(shapes)
     ms_per_step = 1e3 * wall / a.steps
     value = wl.B * a.steps / wall
@@ -377,7 +412,8 @@ def main():
     cfg = {"workload": wl.name, "global_batch": wl.B, "seq_len": shapes[0][0],
            "layers": [list(s) for s in shapes] if L <= 8 else f"{wl.blocks} x {[list(s) for s in wl.layers]}",
            "parallelism": "single-gpu", "input_sets_rotated": n_sets,
-           "clipping": "per-layer adaptive" if wl.per_layer else "global"}
+           "clipping": "per-layer adaptive" if wl.per_layer else "global",
+           "sum_streams": nstreams if not wl.per_layer else 1}
     if on_device:
         cfg["inputs"] = "drawn on the device (torch generator), distinct for every layer"
     line = {

@@ -558,6 +558,38 @@ def test_wide_reduce_noise_bit_exact(dtype, B, T, d, p, hb):
         np.testing.assert_array_equal(bout.cpu().numpy(), D.noised_mean_f32(np.zeros(p), zb, C, sigma, denom))
 
 
+# ------------------------------------------------------------------ concurrent calls
+def test_concurrent_streams_bitwise():
+    """Clipped sums of several layers issued on separate HIP streams at once
+    (each with its own workspace) equal the same calls issued one after
+    another, bit for bit."""
+    wl = W.WORKLOADS["gpt-block-t128"]
+    B = 16
+    shapes = [(128, 256, 512), (128, 384, 256), (64, 512, 384)]
+    layers = []
+    for l, sh in enumerate(shapes):
+        A, G = W.make_layer(wl, l, B=B, shape=sh)
+        layers.append((upload(A, "bf16"), upload(G, "bf16")))
+    c = f32(W.make_vector(B, 0.1, 1.0, tag=5))
+
+    def run(concurrent):
+        outs = [torch.empty(sh[1], sh[2], dtype=torch.float32, device=dev()) for sh in shapes]
+        wss = [torch.empty(max(256, dpc.dp_workspace_bytes(dpc.DP_BF16, B, *sh)), dtype=torch.uint8, device=dev())
+               for sh in shapes]
+        streams = [torch.cuda.Stream() for _ in shapes] if concurrent else [torch.cuda.current_stream()] * 3
+        torch.cuda.synchronize()
+        for l, (A, G) in enumerate(layers):
+            with torch.cuda.stream(streams[l]):
+                dpc.dp_clipped_sum_noise(A, G, c, 1.0, 1.0, float(B), 3, l, 7, outs[l], workspace=wss[l])
+        torch.cuda.synchronize()
+        return [o.cpu().numpy() for o in outs]
+
+    serial = run(False)
+    for _ in range(3):
+        for a_, b_ in zip(run(True), serial):
+            np.testing.assert_array_equal(a_, b_)
+
+
 # ------------------------------------------------------------------ ghost path shapes
 # bf16 ghost norms over 64-row tiles (T <= 384), 128-row tiles (T > 384) and
 # 256 x 128 tiles (T >= 512 with d and p multiples of 64): one tile with most
