@@ -473,15 +473,17 @@ def test_dl32_engine_noise_bit_exact(B):
     np.testing.assert_array_equal(bout.cpu().numpy(), D.noised_mean_f32(np.zeros(p), zb, C, sigma, denom))
 
 
-# ------------------------------------------------------------------ single-tile ghost samples
-# Samples of at most one or two Gram tiles with wide and narrow feature
-# counts on either side, bias on and off, accumulation into sqnorm.
+# ------------------------------------------------------------------ one- and two-block ghost samples
+# Samples of one or two Gram row blocks with wide and narrow feature counts on
+# either side, bias on and off, accumulation into sqnorm.
 SPLIT_CASES = [
     # dtype, B, T, d, p, has_bias
     ("bf16", 5, 128, 1024, 192, True),   # d >> p, bias
     ("bf16", 7, 128, 128, 640, True),    # p >> d, bias
     ("bf16", 3, 100, 256, 384, False),   # rows past T
     ("bf16", 20, 128, 64, 64, True),     # 20 samples over 3 XCD groups
+    ("bf16", 4, 128, 1024, 256, True),   # two row blocks, d >> p, bias
+    ("f32", 3, 128, 320, 64, True),      # the same in fp32
     ("f32", 6, 64, 320, 64, True),
     ("f32", 4, 128, 96, 224, True),
 ]
