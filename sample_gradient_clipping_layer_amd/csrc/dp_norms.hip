@@ -77,7 +77,11 @@ __global__ __launch_bounds__(256) void k_norm_t1(const T* __restrict__ A, const 
 // doubled off the diagonal.
 template <typename T, int TS>
 struct GhostCfg {
-  static constexpr int NT = 256;
+  // 64-row tiles: 8 waves, two groups of 4 taking alternate MFMA k-steps of
+  // every chunk (two waves per SIMD; the groups' partial Grams are added
+  // before the Frobenius product); 128-row tiles: 4 waves
+  static constexpr int NT = TS == 64 ? 512 : 256;
+  static constexpr int KW = NT / 256;              // wave groups sharing a chunk's k-steps
   static constexpr int P = elem_traits<T>::per16;
   static constexpr int CB = TS == 64 ? 256 : 128;  // bytes per staged row chunk (8 vectors/thread either way)
   static constexpr int V = CB / 16;                // 16-byte vectors per row chunk
@@ -133,12 +137,14 @@ __device__ __forceinline__ void ghost_compute(const unsigned char* buf, bool dia
   using Cfg = GhostCfg<T, TS>;
   constexpr int NB = Cfg::NB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wq = wave & 3, kg = wave >> 2;  // sub-tile, and share of the chunk's k-steps
+  const int wm = wq & 1, wn = wq >> 1;
   const unsigned char* sbase = buf;
   const unsigned char* tbase = buf + (diag ? 0 : TS * Cfg::ROWB);
   if constexpr (Cfg::P == 8) {
 #pragma unroll
-    for (int ks = 0; ks < Cfg::KC / 16; ++ks) {
+    for (int kj = 0; kj < Cfg::KC / 16 / Cfg::KW; ++kj) {
+      const int ks = kj * Cfg::KW + kg;
       u32x4 a[NB], b[NB];
 #pragma unroll
       for (int bi = 0; bi < NB; ++bi) {
@@ -157,7 +163,8 @@ __device__ __forceinline__ void ghost_compute(const unsigned char* buf, bool dia
     }
   } else {
 #pragma unroll
-    for (int g = 0; g < Cfg::KC / 8; ++g) {
+    for (int gj = 0; gj < Cfg::KC / 8 / Cfg::KW; ++gj) {
+      const int g = gj * Cfg::KW + kg;
       float4 a[NB], b[NB];
 #pragma unroll
       for (int bi = 0; bi < NB; ++bi) {
@@ -252,7 +259,7 @@ struct GhostFull {
 };
 
 template <typename T, int TS>
-__global__ __launch_bounds__(256) void k_ghost_tiles(const T* __restrict__ A, const T* __restrict__ G, int64_t B,
+__global__ __launch_bounds__((GhostCfg<T, TS>::NT)) void k_ghost_tiles(const T* __restrict__ A, const T* __restrict__ G, int64_t B,
                                                      int64_t Tn, int64_t d, int64_t p, int has_bias, int nb,
                                                      int ntiles, int vecA, int vecG, NormSink sink) {
   using Cfg = GhostCfg<T, TS>;
@@ -312,14 +319,55 @@ __global__ __launch_bounds__(256) void k_ghost_tiles(const T* __restrict__ A, co
   }
   }
 
+  bool owner = true;  // this wave holds complete Gram entries
+  if constexpr (Cfg::KW > 1) {
+    static_assert(Cfg::KW == 2, "two wave groups");
+    // group 1's partial Grams are added into group 0's through LDS, entry-major
+    // ([entry][sub-tile][lane]: consecutive lanes, consecutive words)
+    constexpr int PER = 2 * NB * NB * 16;
+    static_assert(PER * 4 * 64 * 4 <= 2 * Cfg::BUF, "exchange fits the staging buffers");
+    float* xch = reinterpret_cast<float*>(lds);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int slot = (wave & 3) * 64 + lane;
+    __syncthreads();  // every wave is done with the staging buffers
+    if (wave >= 4) {
+      int e = 0;
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            xch[(e++) * 256 + slot] = acc_a[bi][bj][j];
+            xch[(e++) * 256 + slot] = acc_g[bi][bj][j];
+          }
+    }
+    __syncthreads();
+    owner = wave < 4;
+    if (owner) {
+      int e = 0;
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            acc_a[bi][bj][j] += xch[(e++) * 256 + slot];
+            acc_g[bi][bj][j] += xch[(e++) * 256 + slot];
+          }
+    }
+  }
+
   const float one = has_bias ? 1.0f : 0.0f;
   float s = 0.f;
+  if (owner) {
 #pragma unroll
-  for (int bi = 0; bi < NB; ++bi)
+    for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < NB; ++bj)
+      for (int bj = 0; bj < NB; ++bj)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) s += (acc_a[bi][bj][j] + one) * acc_g[bi][bj][j];
+        for (int j = 0; j < 16; ++j) s += (acc_a[bi][bj][j] + one) * acc_g[bi][bj][j];
+  }
   if (!diag) s *= 2.0f;
   s = block_sum<Cfg::NT>(s, red);
   if (threadIdx.x == 0) norm_sink_tile(sink, i, tile, s);
@@ -364,7 +412,7 @@ hipError_t launch_ghost_t(hipStream_t st, const void* A, const void* G, int64_t 
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ghost_tiles<T, TS>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_ghost_tiles<T, TS>), grid, dim3(256), lds_bytes, st, static_cast<const T*>(A),
+  hipLaunchKernelGGL((k_ghost_tiles<T, TS>), grid, dim3(GhostCfg<T, TS>::NT), lds_bytes, st, static_cast<const T*>(A),
                      static_cast<const T*>(G), B, Tn, d, p, has_bias, nb, ntiles, vecA, vecG, sink);
   return hipGetLastError();
 }
