@@ -75,13 +75,19 @@ __global__ __launch_bounds__(256) void k_norm_t1(const T* __restrict__ A, const 
 // the MFMAs of this one: first the chunks of A_i (K = d, Gram of A), then
 // those of G_i (K = p, Gram of G). The epilogue forms sum (GA + bias) .* GG,
 // doubled off the diagonal.
+#ifndef GHOST64_GROUPS
+#define GHOST64_GROUPS 2
+#endif
+constexpr int kGhost64Groups = GHOST64_GROUPS;
+
 template <typename T, int TS>
 struct GhostCfg {
-  // 64-row tiles: 8 waves, two groups of 4 taking alternate MFMA k-steps of
-  // every chunk (two waves per SIMD; the groups' partial Grams are added
-  // before the Frobenius product); 128-row tiles: 4 waves
-  static constexpr int NT = TS == 64 ? 512 : 256;
-  static constexpr int KW = NT / 256;              // wave groups sharing a chunk's k-steps
+  // 64-row tiles: KW groups of 4 waves taking interleaved MFMA k-steps of
+  // every chunk (more waves per SIMD to hide LDS latency; the groups'
+  // partial Grams are added before the Frobenius product); 128-row tiles: 4
+  // waves
+  static constexpr int KW = TS == 64 ? kGhost64Groups : 1;  // wave groups sharing a chunk's k-steps
+  static constexpr int NT = 256 * KW;
   static constexpr int P = elem_traits<T>::per16;
   static constexpr int CB = TS == 64 ? 256 : 128;  // bytes per staged row chunk (8 vectors/thread either way)
   static constexpr int V = CB / 16;                // 16-byte vectors per row chunk
@@ -138,6 +144,7 @@ __device__ __forceinline__ void ghost_compute(const unsigned char* buf, bool dia
   constexpr int NB = Cfg::NB;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wq = wave & 3, kg = wave >> 2;  // sub-tile, and share of the chunk's k-steps
+  static_assert(Cfg::KC / 16 % Cfg::KW == 0 && Cfg::KC / 8 % Cfg::KW == 0, "k-steps split evenly");
   const int wm = wq & 1, wn = wq >> 1;
   const unsigned char* sbase = buf;
   const unsigned char* tbase = buf + (diag ? 0 : TS * Cfg::ROWB);
@@ -321,41 +328,47 @@ __global__ __launch_bounds__((GhostCfg<T, TS>::NT)) void k_ghost_tiles(const T* 
 
   bool owner = true;  // this wave holds complete Gram entries
   if constexpr (Cfg::KW > 1) {
-    static_assert(Cfg::KW == 2, "two wave groups");
-    // group 1's partial Grams are added into group 0's through LDS, entry-major
-    // ([entry][sub-tile][lane]: consecutive lanes, consecutive words)
+    // the groups' partial Grams are added pairwise through LDS (groups
+    // [h, 2h) into [0, h), h = KW/2 .. 1), entry-major ([entry][sub-tile][lane]:
+    // consecutive lanes, consecutive words)
     constexpr int PER = 2 * NB * NB * 16;
-    static_assert(PER * 4 * 64 * 4 <= 2 * Cfg::BUF, "exchange fits the staging buffers");
+    constexpr int REGION = PER * 256;  // floats of one group
+    static_assert((Cfg::KW / 2) * REGION * 4 <= 2 * Cfg::BUF, "exchange fits the staging buffers");
     float* xch = reinterpret_cast<float*>(lds);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int slot = (wave & 3) * 64 + lane;
-    __syncthreads();  // every wave is done with the staging buffers
-    if (wave >= 4) {
-      int e = 0;
+    const int grp = wave >> 2, slot = (wave & 3) * 64 + lane;
 #pragma unroll
-      for (int bi = 0; bi < NB; ++bi)
+    for (int h = Cfg::KW / 2; h >= 1; h /= 2) {
+      __syncthreads();  // every wave is done with the staging buffers / the previous round
+      if (grp >= h && grp < 2 * h) {
+        float* dst = xch + (grp - h) * REGION;
+        int e = 0;
 #pragma unroll
-        for (int bj = 0; bj < NB; ++bj)
+        for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            xch[(e++) * 256 + slot] = acc_a[bi][bj][j];
-            xch[(e++) * 256 + slot] = acc_g[bi][bj][j];
-          }
+          for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              dst[(e++) * 256 + slot] = acc_a[bi][bj][j];
+              dst[(e++) * 256 + slot] = acc_g[bi][bj][j];
+            }
+      }
+      __syncthreads();
+      if (grp < h) {
+        const float* src = xch + grp * REGION;
+        int e = 0;
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              acc_a[bi][bj][j] += src[(e++) * 256 + slot];
+              acc_g[bi][bj][j] += src[(e++) * 256 + slot];
+            }
+      }
     }
-    __syncthreads();
-    owner = wave < 4;
-    if (owner) {
-      int e = 0;
-#pragma unroll
-      for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < NB; ++bj)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            acc_a[bi][bj][j] += xch[(e++) * 256 + slot];
-            acc_g[bi][bj][j] += xch[(e++) * 256 + slot];
-          }
-    }
+    owner = grp == 0;
   }
 
   const float one = has_bias ? 1.0f : 0.0f;
