@@ -74,7 +74,7 @@ size_t norm_ws_bytes(int dtype, int path, int64_t B, int64_t T, int64_t d, int64
 
 size_t contract_ws_bytes(dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64_t p, int has_bias) {
   const dpk::ContractPlan pl = dpk::contract_plan(dtype, B, T, d, p, has_bias);
-  if (pl.ks == 1) return 0;  // one K split: the epilogue writes the output directly
+  if (pl.ks == 1 && !pl.partials) return 0;  // one K split: the epilogue writes the output directly
   return round256((size_t)pl.ks * (size_t)(d + (has_bias ? 1 : 0)) * (size_t)p * sizeof(float));
 }
 

@@ -51,9 +51,9 @@ constexpr int kDlKC = DL_KC;
 constexpr int kDlStages = DL_STAGES;
 static_assert(kDlKC % 16 == 0 && kDlStages >= 3, "chunk of whole MFMA k-steps; at least 3 stages");
 
-template <int BM, int BN, int STAGES, int NW>
+template <int BM, int BN, int STAGES, int NW, int KC_ = kDlKC>
 struct DlCfg {
-  static constexpr int KC = kDlKC;                // K rows per chunk
+  static constexpr int KC = KC_;                  // K rows per chunk
   static constexpr int NT = 64 * NW;              // threads
   static constexpr int RA = BM * 2, RG = BN * 2;  // LDS row bytes
   static constexpr int A_BYTES = KC * RA, G_BYTES = KC * RG;
@@ -105,11 +105,19 @@ struct DlArgs {
 
 
 
-template <int BM, int BN, int STAGES, int NW, bool FUSED>
+// RATIO (one accumulator set, for wave tiles too large for two): acc holds
+// the clipped sum so far divided by the current sample's clip factor; at the
+// first chunk of a sample with c_i != 0 it is rescaled by c_prev / c_i, and
+// at the end multiplied by the last c. One fp32 rounding per sample instead
+// of the exact fold; samples with c_i = 0 contribute exactly nothing and are
+// skipped; a NaN factor still propagates. The partial tile is written to the
+// workspace straight from registers (FUSED is not used).
+template <int BM, int BN, int STAGES, int NW, bool FUSED, int KCK = kDlKC, bool RATIO = false>
 __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restrict__ A, const bf16s* __restrict__ G,
                                                             const float* __restrict__ c, float* __restrict__ ws,
                                                             float* __restrict__ out, DlArgs a) {
-  using C = DlCfg<BM, BN, STAGES, NW>;
+  using C = DlCfg<BM, BN, STAGES, NW, KCK>;
+  static_assert(!(RATIO && FUSED), "the single-accumulator variant writes partials");
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
 
   // ---- work item (XCD-contiguous)
@@ -182,7 +190,14 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
   // partial (a segment is the part of one sample inside this split), restarted
   // by the segment's first MFMA and folded in as acc += c_i * tmp in fp32 at
   // the segment's last chunk, so the clip factor is applied exactly.
-  f32x16 acc[C::NBM][C::NBN], tmp[C::NBM][C::NBN];
+  f32x16 acc[C::NBM][C::NBN];
+  f32x16 tmp_[RATIO ? 1 : C::NBM][RATIO ? 1 : C::NBN];
+  auto& tmp = [&]() -> auto& {
+    if constexpr (RATIO)
+      return acc;
+    else
+      return tmp_;
+  }();
 #pragma unroll
   for (int bi = 0; bi < C::NBM; ++bi)
 #pragma unroll
@@ -228,6 +243,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
   // is computed.
   int64_t sample = q0 / a.cps;
   int64_t in_sample = q0 - sample * a.cps;
+  float cur = 0.0f, prev = 0.0f;  // RATIO: current and last nonzero clip factor
+  bool have_prev = false;
 #pragma unroll
   for (int c = 0; c < STAGES - 1; ++c)
     if (c < nq) issue(q0 + c, c);
@@ -239,10 +256,35 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
     if (it + STAGES - 1 < nq) issue(q0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
 
     const uint32_t sb = lds_addr(lds) + (uint32_t)((it % STAGES) * C::STAGE);
-    if (it == 0 || in_sample == 0)
-      compute(sb, std::true_type{});
-    else
-      compute(sb, std::false_type{});
+    if constexpr (RATIO) {
+      if (it == 0 || in_sample == 0) {
+        cur = c[sample];
+        if (cur != 0.0f) {  // a NaN factor is not 0: it propagates
+          if (have_prev) {
+            const float r = prev / cur;
+#pragma unroll
+            for (int bi = 0; bi < C::NBM; ++bi)
+#pragma unroll
+              for (int bj = 0; bj < C::NBN; ++bj)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) acc[bi][bj][j] *= r;
+          }
+          prev = cur;
+          have_prev = true;
+        }
+      }
+      if (cur != 0.0f) compute(sb, std::false_type{});
+      if (++in_sample == a.cps) {
+        in_sample = 0;
+        ++sample;
+      }
+      continue;
+    } else {
+      if (it == 0 || in_sample == 0)
+        compute(sb, std::true_type{});
+      else
+        compute(sb, std::false_type{});
+    }
     if (++in_sample == a.cps || it + 1 == nq) {
       const float ci = c[sample];
 #pragma unroll
@@ -258,6 +300,23 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
     }
   }
 
+  if constexpr (RATIO) {
+    // ---- epilogue: undo the last sample's division and write the partial
+    // tile [m][n] (m < d, n < p) straight from the accumulators
+    const float last = have_prev ? prev : 0.0f;
+    float* wsp = ws + split * a.d * a.p;
+#pragma unroll
+    for (int bi = 0; bi < C::NBM; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < C::NBN; ++bj)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int64_t m = m0 + wm * C::WM + bi * 32 + acc_row(j, lane);
+          const int64_t n = n0 + wn * C::WN + bj * 32 + acc_col(lane);
+          if (m < a.d && n < a.p) wsp[m * a.p + n] = have_prev ? acc[bi][bj][j] * last : 0.0f;
+        }
+    return;
+  } else {
   // ---- epilogue: the output tile goes through LDS ([BM][BN + 8] fp32; the
   // stages are free once every wave passed the barrier), then each thread
   // takes whole Philox blocks (4 rows of one column) or float4 row pieces,
@@ -298,6 +357,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
       *reinterpret_cast<float4*>(wsp + m * a.p + n) = v;
     }
   }
+  }
 }
 
 // ---------------------------------------------------------------- plan
@@ -311,25 +371,38 @@ bool dl_eligible(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has
 // one workgroup per CU (256 CUs) x the chunks each item runs at a per-CU
 // MFMA rate that grows with the tile (fewer LDS bytes per flop), plus the
 // write and re-read of split partials and a reduce launch.
+// The 256 x 256 tile (64 x 128 wave tiles, single accumulator set) streams
+// 32-row chunks through four stages and always writes partials.
+constexpr int kDlWideKC = 32, kDlWideStages = 4;
+
+// Tile and K split from a cost model fitted to MI355X measurements of this
+// engine: rounds of one workgroup per CU (256 CUs) x (the item's chunks at a
+// sustained fraction of the bf16 MFMA peak + a fixed cost per item: fill and
+// the partial tile's write), plus the write and re-read of split partials by
+// the reduce kernel and its launch.
 ContractPlan dl_plan(int64_t B, int64_t Tn, int64_t d, int64_t p) {
-  static const int tiles[2][2] = {{128, 128}, {256, 128}};
-  static const double eff[2] = {0.40, 0.55};
+  static const int tiles[3][2] = {{128, 128}, {256, 128}, {256, 256}};
+  static const double eff[3] = {0.30, 0.35, 0.47};        // of the bf16 peak, in the K loop
+  static const double fixed_s[3] = {6e-6, 8e-6, 13.5e-6};  // per item
+  static const int kcs[3] = {kDlKC, kDlKC, kDlWideKC};
   const double cu_peak = 2.5e15 / 256.0;
-  const int64_t nchunks = B * Tn / kDlKC;
   ContractPlan best{};
   double best_t = 1e300;
-  for (int ti = 0; ti < 2; ++ti) {
+  for (int ti = 0; ti < 3; ++ti) {
     const int bm = tiles[ti][0], bn = tiles[ti][1];
+    const bool wide = bn == 256;
+    if (Tn % kcs[ti] != 0) continue;
+    const int64_t nchunks = B * Tn / kcs[ti];
     const int64_t mt = (d + bm - 1) / bm, nt = (p + bn - 1) / bn;
-    const double chunk_s = 2.0 * bm * bn * kDlKC / (cu_peak * eff[ti]);
+    const double chunk_s = 2.0 * bm * bn * kcs[ti] / (cu_peak * eff[ti]);
     const int64_t ks_max = nchunks < 512 ? nchunks : 512;
     for (int64_t ks = 1; ks <= ks_max; ++ks) {
       const int64_t cpsplit = (nchunks + ks - 1) / ks;
       if ((nchunks + cpsplit - 1) / cpsplit != ks) continue;
       const int64_t items = mt * nt * ks;
       const double rounds = (double)((items + 255) / 256);
-      double t = rounds * (double)cpsplit * chunk_s + 3.0e-6;
-      if (ks > 1) t += (2.0 * ks + 1.0) * (double)d * (double)p * 4.0 / 5.0e12 + 4.0e-6;
+      double t = rounds * ((double)cpsplit * chunk_s + fixed_s[ti]);
+      if (ks > 1 || wide) t += (2.0 * ks + 1.0) * (double)d * (double)p * 4.0 / 8.0e12 + 4.0e-6;
       if (t < best_t * 0.999) {
         best_t = t;
         best.bm = bm;
@@ -338,6 +411,7 @@ ContractPlan dl_plan(int64_t B, int64_t Tn, int64_t d, int64_t p) {
         best.nt = (int)nt;
         best.ks = ks;
         best.units_per_split = cpsplit;
+        best.partials = wide ? 1 : 0;
       }
     }
   }
@@ -380,18 +454,32 @@ hipError_t launch_contract_dl(hipStream_t st, const void* A, const void* G, cons
                               int64_t d, int64_t p, const ContractPlan& pl, float* ws, const NoiseArgs& na,
                               float* out) {
   const DlPtrs P{static_cast<const bf16s*>(A), static_cast<const bf16s*>(G), c, ws, out};
+  const bool wide = pl.bn == 256;
+  const int kc = wide ? kDlWideKC : kDlKC;
   DlArgs a;
   a.d = d;
   a.p = p;
-  a.cps = Tn / kDlKC;
+  a.cps = Tn / kc;
   a.mt = pl.mt;
   a.nt = pl.nt;
   a.ks = pl.ks;
   a.chunks_per_split = pl.units_per_split;
-  a.nchunks = B * Tn / kDlKC;
+  a.nchunks = B * Tn / kc;
   a.m_fast = pl.mt <= pl.nt ? 1 : 0;
   a.na = na;
   const int64_t items = (int64_t)pl.mt * pl.nt * pl.ks;
+  if (wide) {
+    constexpr int S = kDlWideStages, KCW = kDlWideKC;
+    using C = DlCfg<256, 256, S, 8, KCW>;
+    const int64_t per = (items + 7) / 8;
+    const dim3 grid((unsigned)(per * 8));
+    auto kern = &k_contract_dl<256, 256, S, 8, false, KCW, true>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::LDS, st, P.A, P.G, P.c, P.ws, P.out, a);
+    return hipGetLastError();
+  }
   if (pl.bm == 128 && pl.bn == 128) return launch_dl_t<128, 128, 8>(st, P, a, items);
   return launch_dl_t<256, 128, 8>(st, P, a, items);
 }

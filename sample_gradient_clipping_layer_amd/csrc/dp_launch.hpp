@@ -14,6 +14,7 @@ struct ContractPlan {
   int64_t ks;               // K splits (partial tiles summed by the reduce)
   int64_t units_per_split;  // engine 0: samples (bf16) or KC-row chunks (fp32); 1: 64-row, 2: 32-row chunks
   int engine;               // 0 register-staged (any shape), 1 direct-to-LDS bf16, 2 direct-to-LDS fp32
+  int partials = 0;         // the contraction writes partials (and a reduce adds the noise) even with one split
 };
 // Noise + mean applied in a contraction epilogue or reduce: out = (S + sc*z) * inv_denom.
 struct NoiseArgs {

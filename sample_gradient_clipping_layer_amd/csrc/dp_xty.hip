@@ -983,7 +983,7 @@ hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const vo
     e = launch_contract_d<bf16s>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
   else
     e = launch_contract_d<float>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
-  if (e != hipSuccess || pl.ks == 1) return e;
+  if (e != hipSuccess || (pl.ks == 1 && !pl.partials)) return e;
   const int64_t std_threads = ((d + 3) / 4) * ((p + 3) / 4);
   if (p % 4 == 0 && pl.ks >= 64 && std_threads < 32768) {
     // many splits, few outputs: split lanes in parallel

@@ -421,6 +421,54 @@ def test_dl_engine_workspace_reuse():
     np.testing.assert_array_equal(outs[0], outs[2])
 
 
+# ------------------------------------------------------------------ bf16 256 x 256 tiles
+# Large bf16 layers (here the 768 -> 3072 block linear) take 256 x 256 tiles
+# with one accumulator set: the running sum is kept divided by the current
+# sample's clip factor and rescaled at each sample; zero factors are skipped
+# and a NaN factor propagates.
+def _clip_pattern(kind, B, rng):
+    if kind == "zeros-and-range":
+        c = rng.uniform(0.0, 1.0, B)
+        c[:3] = 0.0
+        c[B // 2] = 0.0
+        c[-1] = 0.0
+        c[5] = 1e-4
+        c[6] = 1.0
+        c[9] = 3e-3
+        return c.astype(np.float32)
+    if kind == "all-zero":
+        return np.zeros(B, dtype=np.float32)
+    c = rng.uniform(0.2, 1.0, B).astype(np.float32)
+    c[7] = np.nan
+    return c
+
+
+@pytest.mark.parametrize("kind", ["zeros-and-range", "all-zero", "nan"])
+def test_wide_tile_clip_patterns(kind):
+    wl = W.WORKLOADS["gpt-block-t128"]
+    l = 2  # 768 -> 3072
+    A, G = W.make_layer(wl, l)
+    B, T, d = A.shape
+    p = G.shape[2]
+    rng = np.random.default_rng(23)
+    c_np = _clip_pattern(kind, B, rng)
+    out = torch.empty(d, p, dtype=torch.float32, device=dev())
+    sigma = 1.0 if kind == "all-zero" else 0.0
+    C, denom, seed, step = 0.7, 3.0, 11, 2
+    dpc.dp_clipped_sum_noise(upload(A, "bf16"), upload(G, "bf16"), f32(c_np), C, sigma, denom, seed, l, step, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    if kind == "all-zero":
+        zw = N.weight_noise(d, p, seed, l, step)
+        np.testing.assert_array_equal(got, D.noised_mean_f32(np.zeros((d, p)), zw, C, sigma, denom))
+        return
+    if kind == "nan":
+        assert np.isnan(got).all()
+        return
+    S, _ = D.clipped_sum(W.as_f64(A, "bf16"), W.as_f64(G, "bf16"), c_np.astype(np.float64), False)
+    assert_sum(got * denom, S, "bf16")
+
+
 # ------------------------------------------------------------------ fp32 direct-to-LDS engine
 # fp32 layers with d, p >= 128, multiples of 4, and B*T a multiple of 32 go to
 # the direct-to-LDS fp32 engine (32-row chunks, 256x128 tiles, bias summed on
