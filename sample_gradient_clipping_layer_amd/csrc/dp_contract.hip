@@ -399,6 +399,10 @@ ContractPlan dl_plan(int64_t B, int64_t Tn, int64_t d, int64_t p) {
     for (int64_t ks = 1; ks <= ks_max; ++ks) {
       const int64_t cpsplit = (nchunks + ks - 1) / ks;
       if ((nchunks + cpsplit - 1) / cpsplit != ks) continue;
+      // the wide tile pays off with long K ranges per item; on short ones its
+      // larger partial tiles cost more than the model sees once other
+      // layers' calls run beside it
+      if (wide && cpsplit < 64) continue;
       const int64_t items = mt * nt * ks;
       const double rounds = (double)((items + 255) / 256);
       double t = rounds * ((double)cpsplit * chunk_s + fixed_s[ti]);

@@ -422,10 +422,11 @@ def test_dl_engine_workspace_reuse():
 
 
 # ------------------------------------------------------------------ bf16 256 x 256 tiles
-# Large bf16 layers (here the 768 -> 3072 block linear) take 256 x 256 tiles
-# with one accumulator set: the running sum is kept divided by the current
-# sample's clip factor and rescaled at each sample; zero factors are skipped
-# and a NaN factor propagates.
+# Large bf16 layers with long K per work item (here the GPT-2-large qkv
+# linear) take 256 x 256 tiles with one accumulator set: the running sum is
+# kept divided by the current sample's clip factor and rescaled at each
+# sample; zero factors are skipped and a NaN factor propagates. Sampled
+# entries are compared with the oracle's definition.
 def _clip_pattern(kind, B, rng):
     if kind == "zeros-and-range":
         c = rng.uniform(0.0, 1.0, B)
@@ -443,30 +444,38 @@ def _clip_pattern(kind, B, rng):
     return c
 
 
+@pytest.fixture(scope="module")
+def gpt2large_qkv():
+    wl = W.WORKLOADS["gpt2large-t1024"]
+    return layer_inputs(wl, 0)
+
+
 @pytest.mark.parametrize("kind", ["zeros-and-range", "all-zero", "nan"])
-def test_wide_tile_clip_patterns(kind):
-    wl = W.WORKLOADS["gpt-block-t128"]
-    l = 2  # 768 -> 3072
-    A, G = W.make_layer(wl, l)
+def test_wide_tile_clip_patterns(kind, gpt2large_qkv):
+    (A_raw, G_raw), (Ao, Go), (A, G) = gpt2large_qkv
     B, T, d = A.shape
     p = G.shape[2]
+    assert dpc.dp_workspace_bytes(dpc.DP_BF16, B, T, d, p) > 0
     rng = np.random.default_rng(23)
     c_np = _clip_pattern(kind, B, rng)
     out = torch.empty(d, p, dtype=torch.float32, device=dev())
     sigma = 1.0 if kind == "all-zero" else 0.0
-    C, denom, seed, step = 0.7, 3.0, 11, 2
-    dpc.dp_clipped_sum_noise(upload(A, "bf16"), upload(G, "bf16"), f32(c_np), C, sigma, denom, seed, l, step, out)
+    C, denom, seed, l, step = 0.7, 3.0, 11, 0, 2
+    dpc.dp_clipped_sum_noise(A, G, f32(c_np), C, sigma, denom, seed, l, step, out)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
+    rows = rng.integers(0, d, 96)
+    cols = rng.integers(0, p, 96)
     if kind == "all-zero":
-        zw = N.weight_noise(d, p, seed, l, step)
-        np.testing.assert_array_equal(got, D.noised_mean_f32(np.zeros((d, p)), zw, C, sigma, denom))
+        z = N.weight_noise_at(rows, cols, p, seed, l, step)
+        np.testing.assert_array_equal(got[rows, cols],
+                                      D.noised_mean_f32(np.zeros(rows.shape[0]), z, C, sigma, denom))
         return
     if kind == "nan":
         assert np.isnan(got).all()
         return
-    S, _ = D.clipped_sum(W.as_f64(A, "bf16"), W.as_f64(G, "bf16"), c_np.astype(np.float64), False)
-    assert_sum(got * denom, S, "bf16")
+    S_or = D.clipped_sum_entries(Ao, Go, c_np.astype(np.float64), rows, cols)
+    assert_noised(got[rows, cols], S_or / denom, S_or, np.zeros(rows.shape[0]), "bf16", denom)
 
 
 # ------------------------------------------------------------------ fp32 direct-to-LDS engine
