@@ -1,7 +1,8 @@
 """Benchmark of the DP-SGD per-sample clipping hot path on one MI355X.
 
 A step is one pass of the whole path over one batch of a layer set: the
-per-example norms of every layer (dp_ghost_norm), the clip factors
+per-example norms of every layer (global clipping: their sum, from one
+dp_ghost_norm_layers call; per-layer clipping: dp_ghost_norm), the clip factors
 (dp_clip_factors) and the clipped, noised mean gradient of every layer
 (dp_clipped_sum_noise). Inputs are seeded synthetic tensors already resident
 in HBM; several copies are rotated so that consecutive steps do not hit the
@@ -85,7 +86,7 @@ DEVICE_GEN_BYTES = 8 << 30
 BREAKDOWN_STEPS = 50
 
 
-def run_gpu(wl, steps, warmup, nstreams=1):
+def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False):
     """Times `steps` whole steps of the workload after `warmup` untimed ones.
 
     Global clipping (one norm per example over all layers): every layer's
@@ -164,7 +165,12 @@ def run_gpu(wl, steps, warmup, nstreams=1):
     else:
         sq = torch.empty(B, dtype=torch.float32, device=dev)
         c = torch.empty(B, dtype=torch.float32, device=dev)
-        kinds = [("norm", l) for l in range(L)] + [("clip", -1)] + [("sum", l) for l in range(L)]
+        # the global norm: one multi-layer call (layers sharing a kernel share a launch),
+        # or one call per layer with accumulate
+        norm_kinds = [("norm", l) for l in range(L)] if per_layer_norms else [("norm", -1)]
+        kinds = norm_kinds + [("clip", -1)] + [("sum", l) for l in range(L)]
+        ws_norm = torch.empty(max(256, dpc.dp_layers_workspace_bytes(sets[0], has_bias=wl.has_bias)),
+                              dtype=torch.uint8, device=dev)
 
     ncalls = len(kinds)
     bsteps = min(steps, BREAKDOWN_STEPS)
@@ -196,8 +202,11 @@ def run_gpu(wl, steps, warmup, nstreams=1):
                      l, k + 1, C_next[l:l + 1])
             C_t = [float(v) for v in C_next.tolist()]
             return
-        for l, (A, G) in enumerate(layers):
-            call(dpc.dp_ghost_norm, A, G, sq, has_bias=wl.has_bias, accumulate=l > 0, workspace=ws[l])
+        if per_layer_norms:
+            for l, (A, G) in enumerate(layers):
+                call(dpc.dp_ghost_norm, A, G, sq, has_bias=wl.has_bias, accumulate=l > 0, workspace=ws[l])
+        else:
+            call(dpc.dp_ghost_norm_layers, layers, sq, has_bias=wl.has_bias, workspace=ws_norm)
         if not use_side:
             join()
             call(dpc.dp_clip_factors, sq, wl.C, c)
@@ -349,6 +358,8 @@ def main():
     ap.add_argument("--workload", default="gpt-block-t128", choices=W.WORKLOAD_ORDER)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="print per-call times to stderr")
+    ap.add_argument("--per-layer-norms", action="store_true",
+                    help="global clipping: one dp_ghost_norm call per layer instead of one multi-layer call")
     ap.add_argument("--streams", type=int, default=None,
                     help="side streams for the layers' clipped sums in the throughput steps (global clipping); "
                          "default 3 for layer sets of at most 8 layers, else 1")
@@ -364,7 +375,8 @@ def main():
         return
     wl = W.WORKLOADS[a.workload]
     nstreams = a.streams if a.streams is not None else (3 if wl.n_layers <= 8 and not wl.per_layer else 1)
-    wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device = run_gpu(wl, a.steps, a.warmup, nstreams)
+    wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device = run_gpu(wl, a.steps, a.warmup, nstreams,
+                                                                      a.per_layer_norms)
     L = len(shapes)
     ms_per_step = 1e3 * wall / a.steps
     value = wl.B * a.steps / wall
@@ -380,10 +392,11 @@ def main():
     for j, (kd, l) in enumerate(kinds):
         if kd != dom:
             continue
-        T, d, p = shapes[l]
-        f, b = _algorithmic(wl, T, d, p, kd)
-        flops += f
-        byts += b
+        for ll in (range(L) if l < 0 else (l,)):  # l < 0: one call over all layers
+            T, d, p = shapes[ll]
+            f, b = _algorithmic(wl, T, d, p, kd)
+            flops += f
+            byts += b
         t_ms += mean_ms[j]
         ndom += 1
     if dom == "sum" or (flops / byts > (PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS)
@@ -399,7 +412,8 @@ def main():
     traffic = measured_traffic(dom, wl.name)
     roof["traffic"] = None if traffic is None else round(traffic)
     roof["algorithmic_bytes_per_call"] = round(byts / ndom)
-    roof["kernel"] = ("dp_ghost_norm: k_ghost_tiles / k_explicit_tiles / k_norm_t1" if dom == "norm"
+    roof["kernel"] = ("dp_ghost_norm[_layers]: k_ghost_tiles / k_ghost_wide / k_explicit_tiles / k_norm_t1"
+                      if dom == "norm"
                       else "dp_clipped_sum_noise: k_contract_dl or k_contract_tiles (+ k_reduce_noise[_vec] "
                            "when K is split)")
     roof["avg_call_us"] = round(1e3 * t_ms / ndom, 2)

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DP_ABI_VERSION 1
+#define DP_ABI_VERSION 2
 
 typedef int32_t dp_status;
 #define DP_OK 0
@@ -96,6 +96,48 @@ dp_status dp_ghost_norm(void* stream, const void* A, const void* G, dp_dtype dty
                         int64_t B, int64_t T, int64_t d, int64_t p, int32_t has_bias,
                         dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes,
                         float* sqnorm, int32_t accumulate, int32_t* path_out);
+
+/* One layer of a dp_ghost_norm_layers call. */
+typedef struct dp_layer {
+  const void* A;     /* [B, T, d] layer inputs, as in dp_ghost_norm */
+  const void* G;     /* [B, T, p] output gradients */
+  int64_t T, d, p;
+  int32_t has_bias;
+  int32_t reserved;  /* must be 0 */
+} dp_layer;
+
+/*
+ * Per-example squared gradient norm over several layers,
+ * N_i^2 = sum_l n_{i,l}^2: the norm of the whole per-sample gradient that
+ * the clip factor of SEDP eq. (2.1) (and FPC's clip_c) is taken of, with each
+ * layer's n_{i,l}^2 as in dp_ghost_norm.
+ *
+ * The result is bitwise the one of dp_ghost_norm called on layers[0],
+ * layers[1], ... in that order (one stream, one workspace), the first call
+ * with `accumulate` and the others with accumulate = 1. Runs of up to 8
+ * consecutive layers that take the tiled ghost kernel with one tile size
+ * share a launch, whose Gram tiles fill the GPU together (a small layer
+ * alone leaves most compute units idle); the last tile of a sample to finish
+ * adds the layers in order. Other layers (closed form, explicit, the
+ * long-sequence bf16 ghost engine) run one launch each.
+ *
+ *  layers, n_layers  host array, 1 <= n_layers <= 4096; each layer as in
+ *           dp_ghost_norm (A, G non-NULL and 16-byte aligned, shape limits),
+ *           reserved == 0.
+ *  dtype, B, mode, kappa  shared by all layers, as in dp_ghost_norm.
+ *  workspace, ws_bytes  at least dp_layers_workspace_bytes(...) bytes (may be
+ *           NULL when that is 0); contents as in dp_ghost_norm.
+ *  sqnorm, accumulate   as in dp_ghost_norm.
+ *  paths_out host int[n_layers] (may be NULL): DP_PATH_* of each layer.
+ */
+dp_status dp_ghost_norm_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype,
+                               int64_t B, dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes,
+                               float* sqnorm, int32_t accumulate, int32_t* paths_out);
+
+/* Workspace bytes dp_ghost_norm_layers needs for these layers. Returns 0 for
+ * invalid arguments (and when no workspace is needed). */
+size_t dp_layers_workspace_bytes(const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B,
+                                 dp_mode mode, int32_t kappa);
 
 /*
  * Norms and clip factors from squared norms.

@@ -9,6 +9,9 @@ The functions mirror the C ABI in ``include/dpclip.h``:
 
     dp_ghost_norm(A, G, sqnorm, has_bias=False, mode=MODE_MIXED, kappa=1,
                   accumulate=False, workspace=None) -> path
+    dp_ghost_norm_layers(layers, sqnorm, has_bias=False, mode=MODE_MIXED, kappa=1,
+                         accumulate=False, workspace=None) -> [path, ...]
+    dp_layers_workspace_bytes(layers, has_bias=False, mode=MODE_MIXED, kappa=1) -> int
     dp_clip_factors(sqnorm, C, c, norm=None)
     dp_clipped_sum_noise(A, G, c, C, sigma, denom, seed, layer_id, step, out,
                          bias_out=None, workspace=None)
@@ -34,10 +37,16 @@ DP_F32, DP_BF16 = 0, 1
 MODE_MIXED, MODE_GHOST, MODE_EXPLICIT = 0, 1, 2
 PATH_GHOST, PATH_EXPLICIT, PATH_T1 = 1, 2, 3
 
-EXPORTS = ("dp_ghost_norm", "dp_clip_factors", "dp_clipped_sum_noise", "dp_adaptive_threshold",
+EXPORTS = ("dp_ghost_norm", "dp_ghost_norm_layers", "dp_layers_workspace_bytes", "dp_clip_factors", "dp_clipped_sum_noise", "dp_adaptive_threshold",
            "dp_workspace_bytes", "dp_choose_path", "dp_status_string", "dp_abi_version")
 
 _lib = None
+
+
+class DpLayer(ctypes.Structure):
+    """struct dp_layer of the C ABI."""
+    _fields_ = [("A", ctypes.c_void_p), ("G", ctypes.c_void_p), ("T", ctypes.c_int64), ("d", ctypes.c_int64),
+                ("p", ctypes.c_int64), ("has_bias", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class DpError(RuntimeError):
@@ -52,6 +61,12 @@ def _declare(lib):
     lib.dp_ghost_norm.argtypes = [vp, vp, vp, c_i32, c_i64, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32,
                                   vp, ctypes.c_size_t, fp, c_i32, ctypes.POINTER(c_i32)]
     lib.dp_ghost_norm.restype = c_i32
+    lp = ctypes.POINTER(DpLayer)
+    lib.dp_ghost_norm_layers.argtypes = [vp, lp, c_i32, c_i32, c_i64, c_i32, c_i32, vp, ctypes.c_size_t, fp, c_i32,
+                                         ctypes.POINTER(c_i32)]
+    lib.dp_ghost_norm_layers.restype = c_i32
+    lib.dp_layers_workspace_bytes.argtypes = [lp, c_i32, c_i32, c_i64, c_i32, c_i32]
+    lib.dp_layers_workspace_bytes.restype = ctypes.c_size_t
     lib.dp_clip_factors.argtypes = [vp, fp, c_i64, f, fp, fp]
     lib.dp_clip_factors.restype = c_i32
     lib.dp_clipped_sum_noise.argtypes = [vp, vp, vp, c_i32, c_i64, c_i64, c_i64, c_i64, fp, f, f, f,
@@ -159,6 +174,49 @@ def dp_ghost_norm(A, G, sqnorm, has_bias: bool = False, mode: int = MODE_MIXED, 
                                                 int(mode), int(kappa), _ptr(ws), nbytes, _ptr(sqnorm),
                                                 int(bool(accumulate)), ctypes.byref(path)))
     return path.value
+
+
+def _layer_table(layers, has_bias):
+    """(dtype, B, ctypes array of DpLayer) for a list of (A, G) pairs;
+    has_bias is one flag for all layers or one per layer."""
+    if len(layers) < 1:
+        raise ValueError("at least one layer")
+    flags = list(has_bias) if isinstance(has_bias, (list, tuple)) else [has_bias] * len(layers)
+    if len(flags) != len(layers):
+        raise ValueError("one has_bias flag per layer")
+    arr = (DpLayer * len(layers))()
+    dt0 = B0 = None
+    for k, ((A, G), hb) in enumerate(zip(layers, flags)):
+        dt, B, T, d, p = _layer(A, G)
+        if dt0 is None:
+            dt0, B0 = dt, B
+        elif dt != dt0 or B != B0:
+            raise ValueError("all layers must share one dtype and batch size")
+        arr[k] = DpLayer(A.data_ptr(), G.data_ptr(), T, d, p, int(bool(hb)), 0)
+    return dt0, B0, arr
+
+
+def dp_layers_workspace_bytes(layers, has_bias=False, mode: int = MODE_MIXED, kappa: int = 1) -> int:
+    dt, B, arr = _layer_table(layers, has_bias)
+    return int(lib().dp_layers_workspace_bytes(arr, len(layers), dt, B, int(mode), int(kappa)))
+
+
+def dp_ghost_norm_layers(layers, sqnorm, has_bias=False, mode: int = MODE_MIXED, kappa: int = 1,
+                         accumulate: bool = False, workspace=None):
+    """Squared norms summed over `layers` (a list of (A, G) pairs) into sqnorm."""
+    import torch
+    dt, B, arr = _layer_table(layers, has_bias)
+    _f32_vec(sqnorm, "sqnorm")
+    if sqnorm.numel() != B:
+        raise ValueError("sqnorm must have B elements")
+    if workspace is None:
+        need = int(lib().dp_layers_workspace_bytes(arr, len(layers), dt, B, int(mode), int(kappa)))
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=sqnorm.device)
+    paths = (ctypes.c_int32 * len(layers))()
+    _check("dp_ghost_norm_layers", lib().dp_ghost_norm_layers(
+        _stream(), arr, len(layers), dt, B, int(mode), int(kappa), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(sqnorm), int(bool(accumulate)), paths))
+    return list(paths)
 
 
 def dp_clip_factors(sqnorm, C: float, c, norm=None):

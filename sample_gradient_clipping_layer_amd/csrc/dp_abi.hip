@@ -4,6 +4,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "../../include/dpclip.h"
 #include "dp_launch.hpp"
 
@@ -80,6 +83,93 @@ size_t contract_ws_bytes(dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64_
 
 dp_status hip_status(hipError_t e) { return e == hipSuccess ? DP_OK : DP_ERR_HIP; }
 
+// Launches the norm kernels of one layer whose arguments are validated.
+hipError_t launch_layer_norm(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t T, int64_t d,
+                             int64_t p, int hb, int path, void* workspace, float* sqnorm, int acc) {
+  if (path == DP_PATH_T1) return dpk::launch_norm_t1(st, dtype, A, G, B, d, p, hb, acc, sqnorm);
+  const int64_t ntiles = norm_ntiles(dtype, path, T, d, p, hb);
+  const dpk::NormSink sink = dpk::make_norm_sink(
+      static_cast<float*>(workspace),
+      ntiles > 1 ? reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(workspace) +
+                                                         norm_partial_bytes(B, ntiles))
+                 : nullptr,
+      sqnorm, (int)ntiles, acc, dpk::next_epoch());
+  if (path == DP_PATH_GHOST) return dpk::launch_ghost(st, dtype, A, G, B, T, d, p, hb, sink);
+  return dpk::launch_explicit(st, dtype, A, G, B, T, d, p, hb, sink);
+}
+
+// Per-layer limits of dp_ghost_norm: tiles per sample (16-bit arrival count)
+// and the ghost grid (32-bit workgroup ids).
+bool layer_fits(int dtype, int path, int64_t B, int64_t T, int64_t d, int64_t p, int hb) {
+  const int64_t nt = norm_ntiles(dtype, path, T, d, p, hb);
+  if (path == DP_PATH_GHOST && (uint64_t)((B + 7) / 8 * 8) * (uint64_t)nt >= (1ull << 32)) return false;
+  return nt <= kMaxTilesPerSample;
+}
+
+// Consecutive layers of a multi-layer norm call that share one launch.
+struct NormRun {
+  int first, count;
+  bool grouped;       // the tiled ghost kernel, one launch for all of them
+  int64_t ntiles;     // tiles per sample over the run
+};
+
+constexpr int32_t kMaxNormLayers = 4096;
+
+dp_status check_norm_layers(const dp_layer* layers, int32_t n, dp_dtype dtype, int64_t B, dp_mode mode,
+                            int32_t kappa) {
+  if (!layers) return DP_ERR_NULL;
+  if (n < 1 || n > kMaxNormLayers) return DP_ERR_SHAPE;
+  if (mode < DP_MODE_MIXED || mode > DP_MODE_EXPLICIT || kappa < 1) return DP_ERR_VALUE;
+  for (int32_t l = 0; l < n; ++l) {
+    const dp_layer& x = layers[l];
+    const dp_status s = check_layer(x.A, x.G, dtype, B, x.T, x.d, x.p);
+    if (s != DP_OK) return s;
+    if (x.reserved != 0) return DP_ERR_VALUE;
+    const int path = path_of(x.T, x.d, x.p, mode, kappa);
+    if (!layer_fits(dtype, path, B, x.T, x.d, x.p, x.has_bias ? 1 : 0)) return DP_ERR_SHAPE;
+  }
+  return DP_OK;
+}
+
+// Runs in layer order: a run of the tiled ghost kernel grows while the next
+// layer takes that kernel with the same tile size and the run stays within
+// one launch's limits (kNormGroupMax layers, the sample's tile count, the
+// grid); every other layer is a run of its own.
+int plan_norm_runs(const dp_layer* layers, int32_t n, dp_dtype dtype, int64_t B, dp_mode mode, int32_t kappa,
+                   NormRun* runs) {
+  int nr = 0;
+  for (int32_t l = 0; l < n; ++l) {
+    const dp_layer& x = layers[l];
+    const int hb = x.has_bias ? 1 : 0;
+    const int path = path_of(x.T, x.d, x.p, mode, kappa);
+    const int64_t nt = norm_ntiles(dtype, path, x.T, x.d, x.p, hb);
+    const bool groupable = path == DP_PATH_GHOST && dpk::ghost_groupable(dtype, x.T, x.d, x.p);
+    if (groupable && nr > 0) {
+      NormRun& r = runs[nr - 1];
+      const dp_layer& f = layers[r.first];
+      if (r.grouped && r.count < dpk::kNormGroupMax &&
+          dpk::ghost_group_key(dtype, f.T) == dpk::ghost_group_key(dtype, x.T) &&
+          r.ntiles + nt <= kMaxTilesPerSample &&
+          (uint64_t)((B + 7) / 8 * 8) * (uint64_t)(r.ntiles + nt) < (1ull << 32)) {
+        r.count += 1;
+        r.ntiles += nt;
+        continue;
+      }
+    }
+    runs[nr++] = NormRun{(int)l, 1, groupable, nt};
+  }
+  return nr;
+}
+
+size_t run_ws_bytes(const NormRun& r, const dp_layer* layers, int dtype, int64_t B, dp_mode mode, int32_t kappa) {
+  if (r.grouped) {
+    if (r.ntiles == 1) return 0;
+    return norm_partial_bytes(B, r.ntiles) + round256((size_t)B * sizeof(unsigned long long));
+  }
+  const dp_layer& x = layers[r.first];
+  return norm_ws_bytes(dtype, path_of(x.T, x.d, x.p, mode, kappa), B, x.T, x.d, x.p, x.has_bias ? 1 : 0);
+}
+
 }  // namespace
 
 extern "C" {
@@ -137,27 +227,74 @@ dp_status dp_ghost_norm(void* stream, const void* A, const void* G, dp_dtype dty
     if (ws_bytes < need) return DP_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return DP_ERR_ALIGN;
   }
-  if (path == DP_PATH_GHOST && (uint64_t)((B + 7) / 8 * 8) * (uint64_t)norm_ntiles(dtype, path, T, d, p, hb) >= (1ull << 32))
-    return DP_ERR_SHAPE;
-  if (norm_ntiles(dtype, path, T, d, p, hb) > kMaxTilesPerSample) return DP_ERR_SHAPE;
+  if (!layer_fits(dtype, path, B, T, d, p, hb)) return DP_ERR_SHAPE;
+  s = device_ready();
+  if (s != DP_OK) return s;
+  if (path_out) *path_out = path;
+  return hip_status(launch_layer_norm(static_cast<hipStream_t>(stream), dtype, A, G, B, T, d, p, hb, path, workspace,
+                                      sqnorm, accumulate ? 1 : 0));
+}
+
+size_t dp_layers_workspace_bytes(const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B, dp_mode mode,
+                                 int32_t kappa) {
+  if (check_norm_layers(layers, n_layers, dtype, B, mode, kappa) != DP_OK) return 0;
+  std::vector<NormRun> runs((size_t)n_layers);
+  const int nr = plan_norm_runs(layers, n_layers, dtype, B, mode, kappa, runs.data());
+  size_t w = 0;
+  for (int r = 0; r < nr; ++r) w = std::max(w, run_ws_bytes(runs[r], layers, dtype, B, mode, kappa));
+  return w;
+}
+
+dp_status dp_ghost_norm_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B,
+                               dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes, float* sqnorm,
+                               int32_t accumulate, int32_t* paths_out) {
+  dp_status s = check_norm_layers(layers, n_layers, dtype, B, mode, kappa);
+  if (s != DP_OK) return s;
+  if (!sqnorm) return DP_ERR_NULL;
+  if (!aligned(sqnorm, 4)) return DP_ERR_ALIGN;
+  std::vector<NormRun> runs((size_t)n_layers);
+  const int nr = plan_norm_runs(layers, n_layers, dtype, B, mode, kappa, runs.data());
+  size_t need = 0;
+  for (int r = 0; r < nr; ++r) need = std::max(need, run_ws_bytes(runs[r], layers, dtype, B, mode, kappa));
+  if (need > 0) {
+    if (!workspace) return DP_ERR_NULL;
+    if (ws_bytes < need) return DP_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return DP_ERR_ALIGN;
+  }
   s = device_ready();
   if (s != DP_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int acc = accumulate ? 1 : 0;
-  if (path_out) *path_out = path;
-  if (path == DP_PATH_T1) return hip_status(dpk::launch_norm_t1(st, dtype, A, G, B, d, p, hb, acc, sqnorm));
-  const int64_t ntiles = norm_ntiles(dtype, path, T, d, p, hb);
-  dpk::NormSink sink;
-  sink.partial = static_cast<float*>(workspace);
-  sink.arrivals = ntiles > 1 ? reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(workspace) +
-                                                                      norm_partial_bytes(B, ntiles))
-                             : nullptr;
-  sink.sqnorm = sqnorm;
-  sink.ntiles = (int)ntiles;
-  sink.accumulate = acc;
-  sink.epoch = dpk::next_epoch();
-  if (path == DP_PATH_GHOST) return hip_status(dpk::launch_ghost(st, dtype, A, G, B, T, d, p, hb, sink));
-  return hip_status(dpk::launch_explicit(st, dtype, A, G, B, T, d, p, hb, sink));
+  for (int32_t l = 0; l < n_layers; ++l)
+    if (paths_out) paths_out[l] = path_of(layers[l].T, layers[l].d, layers[l].p, mode, kappa);
+  for (int r = 0; r < nr; ++r) {
+    const NormRun& run = runs[r];
+    const int acc = (run.first == 0 && !accumulate) ? 0 : 1;
+    hipError_t e;
+    if (run.grouped) {
+      dpk::GhostLayerDesc desc[dpk::kNormGroupMax];
+      dpk::NormSink sink = dpk::make_norm_sink(
+          static_cast<float*>(workspace),
+          run.ntiles > 1 ? reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(workspace) +
+                                                                 norm_partial_bytes(B, run.ntiles))
+                         : nullptr,
+          sqnorm, (int)run.ntiles, acc, dpk::next_epoch());
+      sink.nlayers = run.count;
+      sink.lt[0] = 0;
+      for (int k = 0; k < run.count; ++k) {
+        const dp_layer& x = layers[run.first + k];
+        desc[k] = dpk::GhostLayerDesc{x.A, x.G, x.T, x.d, x.p, x.has_bias ? 1 : 0};
+        sink.lt[k + 1] = sink.lt[k] + (int)norm_ntiles(dtype, DP_PATH_GHOST, x.T, x.d, x.p, desc[k].has_bias);
+      }
+      e = dpk::launch_ghost_group(st, dtype, desc, run.count, B, sink);
+    } else {
+      const dp_layer& x = layers[run.first];
+      const int hb = x.has_bias ? 1 : 0;
+      e = launch_layer_norm(st, dtype, x.A, x.G, B, x.T, x.d, x.p, hb, path_of(x.T, x.d, x.p, mode, kappa),
+                            workspace, sqnorm, acc);
+    }
+    if (e != hipSuccess) return DP_ERR_HIP;
+  }
+  return DP_OK;
 }
 
 dp_status dp_clip_factors(void* stream, const float* sqnorm, int64_t B, float C, float* c, float* norm) {

@@ -148,8 +148,16 @@ __device__ __forceinline__ bool arrive_last(unsigned long long* ctr, uint64_t ep
   }
 }
 
-// Where a per-sample norm assembled from `ntiles` tile workgroups goes:
-// sqnorm[i] (+)= the sum of the tile partials in tile order.
+// Layers one grouped norm launch can take.
+constexpr int kNormGroupMax = 8;
+
+// Where a per-sample norm assembled from `ntiles` tile workgroups goes. The
+// tiles may belong to several layers (a grouped launch): layer l owns tiles
+// [lt[l], lt[l+1]) of each sample, lt[0] = 0, lt[nlayers] = ntiles. Each
+// layer's value is the sum of its tile partials in tile order; sqnorm[i]
+// then takes the layers in order, as calls with accumulate = 1 after the
+// first would: sqnorm[i] = ((start + n_0) + n_1) + ..., start = sqnorm[i]
+// when accumulating, else the first layer's value stands alone.
 struct NormSink {
   float* partial;                 // [B][ntiles] (unused when ntiles == 1)
   unsigned long long* arrivals;   // [B] arrival counters (unused when ntiles == 1)
@@ -157,7 +165,25 @@ struct NormSink {
   int ntiles;
   int accumulate;
   uint64_t epoch;
+  int nlayers;
+  int lt[kNormGroupMax + 1];
 };
+
+// A sink for one layer of `ntiles` tiles per sample.
+inline NormSink make_norm_sink(float* partial, unsigned long long* arrivals, float* sqnorm, int ntiles,
+                               int accumulate, uint64_t epoch) {
+  NormSink k{};
+  k.partial = partial;
+  k.arrivals = arrivals;
+  k.sqnorm = sqnorm;
+  k.ntiles = ntiles;
+  k.accumulate = accumulate;
+  k.epoch = epoch;
+  k.nlayers = 1;
+  k.lt[0] = 0;
+  k.lt[1] = ntiles;
+  return k;
+}
 
 // Called by ONE thread per tile workgroup with the tile's partial s. The
 // tiles of a sample run on different XCDs, whose L2 caches are not coherent
@@ -175,9 +201,14 @@ __device__ __forceinline__ void norm_sink_tile(const NormSink& k, int64_t i, int
   __hip_atomic_store(row + tile, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   wait_vmcnt<0>();
   if (!arrive_last(k.arrivals + i, k.epoch, (uint32_t)k.ntiles)) return;
-  float tot = 0.f;
-  for (int t = 0; t < k.ntiles; ++t) tot += __hip_atomic_load(row + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  k.sqnorm[i] = k.accumulate ? k.sqnorm[i] + tot : tot;
+  float v = k.accumulate ? k.sqnorm[i] : 0.f;
+  for (int l = 0; l < k.nlayers; ++l) {
+    float tot = 0.f;
+    for (int t = k.lt[l]; t < k.lt[l + 1]; ++t)
+      tot += __hip_atomic_load(row + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    v = (l == 0 && !k.accumulate) ? tot : v + tot;
+  }
+  k.sqnorm[i] = v;
 }
 
 }  // namespace dpk

@@ -50,6 +50,23 @@ hipError_t launch_ghost_wide(hipStream_t st, const void* A, const void* G, int64
 
 hipError_t launch_norm_t1(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t d, int64_t p,
                           int has_bias, int accumulate, float* sqnorm);
+// One layer handed to a grouped ghost launch.
+struct GhostLayerDesc {
+  const void* A;
+  const void* G;
+  int64_t Tn, d, p;
+  int has_bias;
+};
+// Layers that the tiled ghost kernel takes (the long-sequence bf16 engine
+// runs one layer per launch); layers of one launch share ghost_group_key.
+bool ghost_groupable(int dtype, int64_t Tn, int64_t d, int64_t p);
+int ghost_group_key(int dtype, int64_t Tn);
+// Workgroups of a grouped launch (the caller keeps it below 2^32).
+int64_t ghost_group_grid(int64_t B, const GhostLayerDesc* layers, int n);
+// Up to kNormGroupMax groupable layers with one key in one launch; the sink
+// spans the tiles of all of them (lt[] in the order of `layers`).
+hipError_t launch_ghost_group(hipStream_t st, int dtype, const GhostLayerDesc* layers, int n, int64_t B,
+                              const NormSink& sink);
 // Norm kernels whose sample spans several tile workgroups finish each
 // sample in its last-arriving tile (NormSink in dp_common.hpp).
 hipError_t launch_ghost(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,

@@ -265,17 +265,44 @@ struct GhostFull {
   }
 };
 
+// One layer of a ghost launch: its operands and sizes, the first workgroup
+// of its range in the grid (a multiple of 8, so that a workgroup's id mod 8
+// is still its XCD within the range) and its first tile in the sink.
+template <typename T>
+struct GhostLayer {
+  const T* A;
+  const T* G;
+  int64_t Tn, d, p;
+  int64_t wg_begin;
+  int nb, ntiles, tile_base, vecA, vecG, has_bias;
+};
+// The layers of one launch, ordered by wg_begin.
+template <typename T>
+struct GhostGroup {
+  GhostLayer<T> L[kNormGroupMax];
+  int n;
+};
+
 template <typename T, int TS>
-__global__ __launch_bounds__((GhostCfg<T, TS>::NT)) void k_ghost_tiles(const T* __restrict__ A, const T* __restrict__ G, int64_t B,
-                                                     int64_t Tn, int64_t d, int64_t p, int has_bias, int nb,
-                                                     int ntiles, int vecA, int vecG, NormSink sink) {
+__global__ __launch_bounds__((GhostCfg<T, TS>::NT)) void k_ghost_tiles(GhostGroup<T> grp, int64_t B, NormSink sink) {
   using Cfg = GhostCfg<T, TS>;
   constexpr int NB = Cfg::NB;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   __shared__ float red[Cfg::NT / kWave];
 
+  // the layer whose workgroup range holds this workgroup (a uniform choice
+  // among compile-time entries: no indexing into the argument block)
+  GhostLayer<T> L = grp.L[0];
+#pragma unroll
+  for (int k = 1; k < kNormGroupMax; ++k)
+    if (k < grp.n && (int64_t)blockIdx.x >= grp.L[k].wg_begin) L = grp.L[k];
+  const T* __restrict__ A = L.A;
+  const T* __restrict__ G = L.G;
+  const int64_t Tn = L.Tn, d = L.d, p = L.p;
+  const int nb = L.nb, vecA = L.vecA, vecG = L.vecG, has_bias = L.has_bias;
+
   int64_t i, tile;
-  xcd_group_map(blockIdx.x, ntiles, &i, &tile);
+  xcd_group_map((int64_t)blockIdx.x - L.wg_begin, L.ntiles, &i, &tile);
   if (i >= B) return;
   int sb = 0;
   int rem = (int)tile;
@@ -383,7 +410,7 @@ __global__ __launch_bounds__((GhostCfg<T, TS>::NT)) void k_ghost_tiles(const T* 
   }
   if (!diag) s *= 2.0f;
   s = block_sum<Cfg::NT>(s, red);
-  if (threadIdx.x == 0) norm_sink_tile(sink, i, tile, s);
+  if (threadIdx.x == 0) norm_sink_tile(sink, i, L.tile_base + tile, s);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -411,43 +438,116 @@ int64_t ghost_ntiles(int dtype, int64_t T, int64_t d, int64_t p) {
   return nb * (nb + 1) / 2;
 }
 
-template <typename T, int TS>
-hipError_t launch_ghost_t(hipStream_t st, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d, int64_t p,
-                          int has_bias, const NormSink& sink) {
-  const int nb = (int)((Tn + TS - 1) / TS);
-  const int ntiles = nb * (nb + 1) / 2;
-  const int64_t groups8 = (B + 7) / 8;
-  const dim3 grid((unsigned)(groups8 * 8 * ntiles));
+template <typename T>
+static GhostLayer<T> ghost_layer(const GhostLayerDesc& x, int ts) {
   const int eb = elem_traits<T>::bytes;
-  const int vecA = ((reinterpret_cast<uintptr_t>(A) & 15) == 0) && ((d * eb) % 16 == 0);
-  const int vecG = ((reinterpret_cast<uintptr_t>(G) & 15) == 0) && ((p * eb) % 16 == 0);
+  GhostLayer<T> L{};
+  L.A = static_cast<const T*>(x.A);
+  L.G = static_cast<const T*>(x.G);
+  L.Tn = x.Tn;
+  L.d = x.d;
+  L.p = x.p;
+  L.nb = (int)((x.Tn + ts - 1) / ts);
+  L.ntiles = L.nb * (L.nb + 1) / 2;
+  L.vecA = ((reinterpret_cast<uintptr_t>(x.A) & 15) == 0) && ((x.d * eb) % 16 == 0);
+  L.vecG = ((reinterpret_cast<uintptr_t>(x.G) & 15) == 0) && ((x.p * eb) % 16 == 0);
+  L.has_bias = x.has_bias;
+  return L;
+}
+
+// Layers are laid out in the grid by decreasing work per tile (the largest
+// tiles start first and the short ones fill the tail); tile_base follows the
+// caller's order, which is the order of the sink's fold.
+template <typename T, int TS>
+hipError_t launch_ghost_t(hipStream_t st, const GhostLayerDesc* layers, int n, int64_t B, const NormSink& sink) {
+  GhostGroup<T> grp{};
+  int order[kNormGroupMax];
+  int base = 0;
+  for (int l = 0; l < n; ++l) {
+    grp.L[l] = ghost_layer<T>(layers[l], TS);
+    grp.L[l].tile_base = base;
+    base += grp.L[l].ntiles;
+    order[l] = l;
+  }
+  for (int a = 1; a < n; ++a)  // stable insertion sort by d + p, largest first
+    for (int b = a; b > 0 && layers[order[b]].d + layers[order[b]].p > layers[order[b - 1]].d + layers[order[b - 1]].p;
+         --b) {
+      const int t = order[b];
+      order[b] = order[b - 1];
+      order[b - 1] = t;
+    }
+  GhostGroup<T> sorted{};
+  const int64_t groups8 = (B + 7) / 8;
+  int64_t wg = 0;
+  for (int k = 0; k < n; ++k) {
+    sorted.L[k] = grp.L[order[k]];
+    sorted.L[k].wg_begin = wg;
+    wg += groups8 * 8 * sorted.L[k].ntiles;
+  }
+  sorted.n = n;
   const size_t lds_bytes = 2 * GhostCfg<T, TS>::BUF;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ghost_tiles<T, TS>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_ghost_tiles<T, TS>), grid, dim3(GhostCfg<T, TS>::NT), lds_bytes, st, static_cast<const T*>(A),
-                     static_cast<const T*>(G), B, Tn, d, p, has_bias, nb, ntiles, vecA, vecG, sink);
+  hipLaunchKernelGGL((k_ghost_tiles<T, TS>), dim3((unsigned)wg), dim3(GhostCfg<T, TS>::NT), lds_bytes, st, sorted, B,
+                     sink);
   return hipGetLastError();
+}
+
+bool ghost_groupable(int dtype, int64_t Tn, int64_t d, int64_t p) { return !ghost_wide_eligible(dtype, Tn, d, p); }
+
+int ghost_group_key(int dtype, int64_t Tn) { return 2 * ghost_tile_size(Tn) + (dtype == 1 ? 1 : 0); }
+
+int64_t ghost_group_grid(int64_t B, const GhostLayerDesc* layers, int n) {
+  int64_t wg = 0;
+  for (int l = 0; l < n; ++l) {
+    const int64_t ts = ghost_tile_size(layers[l].Tn);
+    const int64_t nb = (layers[l].Tn + ts - 1) / ts;
+    wg += (B + 7) / 8 * 8 * (nb * (nb + 1) / 2);
+  }
+  return wg;
+}
+
+hipError_t launch_ghost_group(hipStream_t st, int dtype, const GhostLayerDesc* layers, int n, int64_t B,
+                              const NormSink& sink) {
+  const int ts = ghost_tile_size(layers[0].Tn);
+  if (dtype == 1) {
+    if (ts == 64) return launch_ghost_t<bf16s, 64>(st, layers, n, B, sink);
+    return launch_ghost_t<bf16s, 128>(st, layers, n, B, sink);
+  }
+  if (ts == 64) return launch_ghost_t<float, 64>(st, layers, n, B, sink);
+  return launch_ghost_t<float, 128>(st, layers, n, B, sink);
 }
 
 hipError_t launch_ghost(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
                         int64_t p, int has_bias, const NormSink& sink) {
   if (ghost_wide_eligible(dtype, Tn, d, p)) return launch_ghost_wide(st, A, G, B, Tn, d, p, has_bias, sink);
-  const int ts = ghost_tile_size(Tn);
-  if (dtype == 1) {
-    if (ts == 64) return launch_ghost_t<bf16s, 64>(st, A, G, B, Tn, d, p, has_bias, sink);
-    return launch_ghost_t<bf16s, 128>(st, A, G, B, Tn, d, p, has_bias, sink);
-  }
-  if (ts == 64) return launch_ghost_t<float, 64>(st, A, G, B, Tn, d, p, has_bias, sink);
-  return launch_ghost_t<float, 128>(st, A, G, B, Tn, d, p, has_bias, sink);
+  const GhostLayerDesc x{A, G, Tn, d, p, has_bias};
+  return launch_ghost_group(st, dtype, &x, 1, B, sink);
 }
 
 static std::atomic<uint64_t> g_epoch{0};
 
+// The call counter through a bijection of 48-bit words (xor-shifts and odd
+// multipliers modulo 2^48), so that epochs differ from call to call but look
+// like no small integer or float pattern: an arrival counter's word may hold
+// data a kernel left there (the workspace is shared with tile partials), and
+// such a word passes for the current epoch only if its top 48 bits match.
+static uint64_t mix48(uint64_t x) {
+  constexpr uint64_t M = (1ull << 48) - 1;
+  x &= M;
+  x ^= x >> 24;
+  x = (x * 0x9E3779B97F4Bull) & M;
+  x ^= x >> 21;
+  x = (x * 0xD6E8FEB86659ull) & M;
+  x ^= x >> 24;
+  return x;
+}
+
 uint64_t next_epoch() {
   uint64_t e;
   do {
-    e = (g_epoch.fetch_add(1, std::memory_order_relaxed) + 1) & ((1ull << 48) - 1);
+    e = mix48(g_epoch.fetch_add(1, std::memory_order_relaxed) + 1);
   } while (e == 0);
   return e;
 }

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(dpc.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.dp_abi_version() == 1
+    assert lib.dp_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -159,3 +159,77 @@ def test_binding_fails_loudly_without_gpu_tensors():
     A = torch.zeros(2, 1, 3)
     with pytest.raises(ValueError):
         dpc.dp_ghost_norm(A, A, torch.zeros(2))
+
+
+def _layers(specs, A=FAKE, G=FAKE, reserved=0):
+    arr = (dpc.DpLayer * max(1, len(specs)))()
+    for k, (T, d, p, hb) in enumerate(specs):
+        arr[k] = dpc.DpLayer(A, G, T, d, p, hb, reserved)
+    return arr
+
+
+GPT_BLOCK = [(128, 768, 2304, 0), (128, 768, 768, 0), (128, 768, 3072, 0), (128, 3072, 768, 0)]
+
+
+def test_ghost_norm_layers_validation(lib):
+    """The multi-layer norm call validates every layer before any HIP call
+    and writes nothing on failure."""
+    fn = lib.dp_ghost_norm_layers
+
+    def call(arr, n=None, dt=1, B=64, mode=0, kappa=1, ws=FAKE, wsb=1 << 30, sq=FAKE):
+        paths = (ctypes.c_int32 * 16)(*([-7] * 16))
+        st = fn(None, arr, len(GPT_BLOCK) if n is None else n, dt, B, mode, kappa, ws, wsb, sq, 0, paths)
+        return st, list(paths)
+
+    ok = _layers(GPT_BLOCK)
+    assert call(None)[0] == dpc.DP_ERR_NULL
+    assert call(ok, n=0)[0] == dpc.DP_ERR_SHAPE
+    assert call(ok, n=4097)[0] == dpc.DP_ERR_SHAPE
+    assert call(ok, sq=None)[0] == dpc.DP_ERR_NULL
+    assert call(ok, B=0)[0] == dpc.DP_ERR_SHAPE
+    assert call(ok, dt=3)[0] == dpc.DP_ERR_DTYPE
+    assert call(ok, mode=5)[0] == dpc.DP_ERR_VALUE
+    assert call(ok, kappa=0)[0] == dpc.DP_ERR_VALUE
+    assert call(_layers(GPT_BLOCK, reserved=1))[0] == dpc.DP_ERR_VALUE
+    assert call(_layers(GPT_BLOCK, A=FAKE_MIS))[0] == dpc.DP_ERR_ALIGN
+    assert call(_layers(GPT_BLOCK, G=None))[0] == dpc.DP_ERR_NULL
+    bad = _layers(GPT_BLOCK[:3] + [(128, 0, 768, 0)])  # the last layer's d
+    assert call(bad)[0] == dpc.DP_ERR_SHAPE
+    assert call(ok, ws=None)[0] == dpc.DP_ERR_NULL
+    st, paths = call(ok, wsb=1024)
+    assert st == dpc.DP_ERR_WORKSPACE and paths[:4] == [-7] * 4
+    # an explicit layer beyond the per-sample tile limit fails the whole call
+    huge = _layers(GPT_BLOCK[:1] + [(1 << 16, 1 << 15, 1 << 15, 0)])
+    assert call(huge, n=2, B=1, mode=dpc.MODE_EXPLICIT)[0] == dpc.DP_ERR_SHAPE
+    import torch
+    if not torch.cuda.is_available():
+        assert call(ok)[0] == dpc.DP_ERR_NO_DEVICE
+
+
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
+def test_layers_workspace_follows_the_runs(lib):
+    """Consecutive ghost layers of one tile size share a launch (at most 8)
+    whose partials span all their tiles; other layers need their own."""
+    ws = lib.dp_layers_workspace_bytes
+    B = 64
+    # four T = 128 layers: one launch, 3 Gram tiles per layer and sample
+    assert ws(_layers(GPT_BLOCK), 4, 1, B, 0, 1) == _r256(B * 12 * 4) + _r256(B * 8)
+    # nine layers: runs of 8 and 1
+    nine = _layers([GPT_BLOCK[0]] * 9)
+    assert ws(nine, 9, 1, B, 0, 1) == _r256(B * 24 * 4) + _r256(B * 8)
+    # a T = 1 layer in between splits the run; it needs no workspace
+    mixed = _layers([GPT_BLOCK[0], (1, 64, 32, 0), GPT_BLOCK[1]])
+    assert ws(mixed, 3, 1, B, 0, 1) == _r256(B * 3 * 4) + _r256(B * 8)
+    # one single-tile ghost layer: nothing
+    assert ws(_layers([(64, 32, 48, 0)]), 1, 0, 5, dpc.MODE_GHOST, 1) == 0
+    # two single-tile ghost layers share a launch: two tiles per sample
+    two = _layers([(64, 32, 48, 0), (40, 16, 16, 1)])
+    assert ws(two, 2, 0, 5, dpc.MODE_GHOST, 1) == _r256(5 * 2 * 4) + _r256(5 * 8)
+    # the long-sequence bf16 engine runs alone: its own tile count
+    long_ = _layers([(1024, 1280, 3840, 0)])
+    assert ws(long_, 1, 1, 32, 0, 1) > 0
+    assert ws(None, 1, 1, B, 0, 1) == 0
+    assert ws(_layers(GPT_BLOCK), 0, 1, B, 0, 1) == 0

@@ -1,0 +1,138 @@
+"""Multi-layer norm call (dp_ghost_norm_layers) on the GPU.
+
+The call must give, bit for bit, what per-layer dp_ghost_norm calls with
+accumulate give (same fold order: each layer's tile partials in tile order,
+then the layers in call order), whether its layers share one launch or not;
+and the sum over layers must match the oracle's within the norm tolerance.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import sample_gradient_clipping_layer_amd as dpc
+import workloads as W
+from oracle import definitions as D
+
+from gpu_util import assert_norms, dev, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, specs, dtype, seed):
+    """specs: (T, d, p) per layer; seeded normal inputs scaled like the workloads."""
+    rng = np.random.default_rng(seed)
+    host, devs = [], []
+    for (T, d, p) in specs:
+        A = (rng.standard_normal((B, T, d)) / np.sqrt(d)).astype(np.float32)
+        G = (rng.standard_normal((B, T, p)) / np.sqrt(p)).astype(np.float32)
+        if dtype == "bf16":
+            A, G = W.f32_to_bf16_bits(A), W.f32_to_bf16_bits(G)
+        host.append((W.as_f64(A, dtype), W.as_f64(G, dtype)))
+        devs.append((upload(A, dtype), upload(G, dtype)))
+    return host, devs
+
+
+def _sequential(devs, flags, mode, start=None):
+    B = devs[0][0].shape[0]
+    sq = start.clone() if start is not None else torch.full((B,), float("nan"), dtype=torch.float32, device=dev())
+    paths = []
+    for l, ((A, G), hb) in enumerate(zip(devs, flags)):
+        paths.append(dpc.dp_ghost_norm(A, G, sq, has_bias=hb, mode=mode, accumulate=(l > 0 or start is not None)))
+    torch.cuda.synchronize()
+    return sq.cpu().numpy(), paths
+
+
+def _grouped(devs, flags, mode, start=None):
+    B = devs[0][0].shape[0]
+    sq = start.clone() if start is not None else torch.full((B,), float("nan"), dtype=torch.float32, device=dev())
+    paths = dpc.dp_ghost_norm_layers(devs, sq, has_bias=flags, mode=mode, accumulate=start is not None)
+    torch.cuda.synchronize()
+    return sq.cpu().numpy(), paths
+
+
+def _oracle(host, flags, start=None):
+    tot = np.zeros(host[0][0].shape[0]) if start is None else np.asarray(start, dtype=np.float64)
+    for (A, G), hb in zip(host, flags):
+        tot = tot + D.layer_sqnorms(A, G, hb)
+    return tot
+
+
+GPT_BLOCK = [(128, 768, 2304), (128, 768, 768), (128, 768, 3072), (128, 3072, 768)]
+
+CASES = {
+    # name: (B, specs, dtype, has_bias flags, mode)
+    "gpt-block": (64, GPT_BLOCK, "bf16", [False] * 4, dpc.MODE_MIXED),
+    "ragged-bias-f32": (13, [(100, 96, 80), (128, 64, 200), (37, 72, 72), (64, 128, 64)], "f32",
+                        [True, False, True, True], dpc.MODE_GHOST),
+    "mixed-paths": (9, [(1, 64, 32), (96, 128, 128), (200, 16, 24), (96, 200, 64), (600, 64, 96), (80, 64, 128)],
+                    "bf16", [False, True, False, True, False, True], dpc.MODE_MIXED),
+    "ten-layers": (11, [(128, 64 + 8 * k, 128) for k in range(10)], "bf16", [k % 2 == 0 for k in range(10)],
+                   dpc.MODE_GHOST),
+    "wide-engine-inside": (3, [(128, 128, 128), (512, 128, 192), (128, 64, 128)], "bf16", [False, False, True],
+                           dpc.MODE_GHOST),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layers_match_sequential_and_oracle(name):
+    B, specs, dtype, flags, mode = CASES[name]
+    host, devs = _inputs(B, specs, dtype, seed=len(name))
+    seq, p_seq = _sequential(devs, flags, mode)
+    grp, p_grp = _grouped(devs, flags, mode)
+    assert p_grp == p_seq
+    np.testing.assert_array_equal(grp.view(np.uint32), seq.view(np.uint32))
+    assert_norms(np.sqrt(grp), np.sqrt(_oracle(host, flags)), dtype)
+
+
+def test_layers_accumulate_onto_existing_values():
+    B, specs, dtype, flags, mode = CASES["ragged-bias-f32"]
+    host, devs = _inputs(B, specs, dtype, seed=5)
+    start_np = np.linspace(0.5, 3.0, B).astype(np.float32)
+    start = torch.from_numpy(start_np).to(dev())
+    seq, _ = _sequential(devs, flags, mode, start=start)
+    grp, _ = _grouped(devs, flags, mode, start=start)
+    np.testing.assert_array_equal(grp.view(np.uint32), seq.view(np.uint32))
+    assert_norms(np.sqrt(grp), np.sqrt(_oracle(host, flags, start_np)), dtype)
+
+
+def test_layers_zero_and_nan_samples():
+    """A sample whose inputs are all zero has norm 0; a NaN in one layer of
+    one sample makes only that sample's norm NaN."""
+    B, specs, dtype, flags, mode = CASES["gpt-block"]
+    B = 16
+    rng = np.random.default_rng(9)
+    devs = []
+    for k, (T, d, p) in enumerate(specs):
+        A = (rng.standard_normal((B, T, d)) / np.sqrt(d)).astype(np.float32)
+        G = (rng.standard_normal((B, T, p)) / np.sqrt(p)).astype(np.float32)
+        A[3] = 0.0
+        G[3] = 0.0
+        if k == 2:
+            G[7, 5, 11] = np.nan
+        devs.append((upload(W.f32_to_bf16_bits(A), "bf16"), upload(W.f32_to_bf16_bits(G), "bf16")))
+    grp, _ = _grouped(devs, flags, mode)
+    seq, _ = _sequential(devs, flags, mode)
+    np.testing.assert_array_equal(grp.view(np.uint32), seq.view(np.uint32))
+    assert grp[3] == 0.0
+    assert np.isnan(grp[7])
+    assert np.isfinite(np.delete(grp, 7)).all()
+
+
+def test_layers_repeated_calls_share_a_workspace():
+    """Calls of different layer lists on one workspace (arrival counters of
+    other shapes, partials left in it) give the same results as fresh ones."""
+    B = 12
+    lists = [CASES["ten-layers"][1][:5], GPT_BLOCK[:2], [(100, 96, 80), (37, 72, 72)]]
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev())
+    ws.fill_(0x3F)  # float-like bytes
+    for rep in range(2):
+        for k, specs in enumerate(lists):
+            _, devs = _inputs(B, specs, "bf16", seed=100 + k)
+            flags = [False] * len(specs)
+            sq = torch.empty(B, dtype=torch.float32, device=dev())
+            dpc.dp_ghost_norm_layers(devs, sq, has_bias=flags, mode=dpc.MODE_GHOST, workspace=ws)
+            torch.cuda.synchronize()
+            ref, _ = _sequential(devs, flags, dpc.MODE_GHOST)
+            np.testing.assert_array_equal(sq.cpu().numpy().view(np.uint32), ref.view(np.uint32))
