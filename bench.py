@@ -4,7 +4,8 @@ A step is one pass of the whole path over one batch of a layer set: the
 per-example norms of every layer (global clipping: their sum, from one
 dp_ghost_norm_layers call; per-layer clipping: dp_ghost_norm), the clip factors
 (dp_clip_factors) and the clipped, noised mean gradient of every layer
-(dp_clipped_sum_noise). Inputs are seeded synthetic tensors already resident
+(global clipping: one dp_clipped_sum_noise_layers call; per-layer clipping:
+dp_clipped_sum_noise). Inputs are seeded synthetic tensors already resident
 in HBM; several copies are rotated so that consecutive steps do not hit the
 256 MB Infinity Cache. Prints one JSON line.
 
@@ -86,7 +87,7 @@ DEVICE_GEN_BYTES = 8 << 30
 BREAKDOWN_STEPS = 50
 
 
-def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False):
+def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums=False):
     """Times `steps` whole steps of the workload after `warmup` untimed ones.
 
     Global clipping (one norm per example over all layers): every layer's
@@ -167,10 +168,13 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False):
         c = torch.empty(B, dtype=torch.float32, device=dev)
         # the global norm: one multi-layer call (layers sharing a kernel share a launch),
         # or one call per layer with accumulate
+        per_layer_norms = per_layer_norms or L == 1  # one layer: the plain call costs less host time
         norm_kinds = [("norm", l) for l in range(L)] if per_layer_norms else [("norm", -1)]
-        kinds = norm_kinds + [("clip", -1)] + [("sum", l) for l in range(L)]
-        ws_norm = torch.empty(max(256, dpc.dp_layers_workspace_bytes(sets[0], has_bias=wl.has_bias)),
-                              dtype=torch.uint8, device=dev)
+        sum_kinds = [("sum", l) for l in range(L)] if per_layer_sums else [("sum", -1)]
+        kinds = norm_kinds + [("clip", -1)] + sum_kinds
+        # one workspace for the multi-layer calls (they run one after another on the stream)
+        ws_layers = torch.empty(max(256, dpc.dp_layers_workspace_bytes(sets[0], has_bias=wl.has_bias)),
+                                dtype=torch.uint8, device=dev)
 
     ncalls = len(kinds)
     bsteps = min(steps, BREAKDOWN_STEPS)
@@ -178,6 +182,9 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False):
           for _ in range(bsteps)]
 
     sum_done = [None] * len(shapes)
+    # events are recorded again every step (created once: creating them costs host time)
+    ready = torch.cuda.Event()
+    done_ev = [torch.cuda.Event() for _ in shapes]
 
     def step(k, e=None):
         nonlocal C_t
@@ -206,7 +213,12 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False):
             for l, (A, G) in enumerate(layers):
                 call(dpc.dp_ghost_norm, A, G, sq, has_bias=wl.has_bias, accumulate=l > 0, workspace=ws[l])
         else:
-            call(dpc.dp_ghost_norm_layers, layers, sq, has_bias=wl.has_bias, workspace=ws_norm)
+            call(dpc.dp_ghost_norm_layers, layers, sq, has_bias=wl.has_bias, workspace=ws_layers)
+        if not per_layer_sums:
+            call(dpc.dp_clip_factors, sq, wl.C, c)
+            call(dpc.dp_clipped_sum_noise_layers, layers, c, wl.C, wl.sigma, float(B), wl.seed, k, outs,
+                 bias_outs=bouts if wl.has_bias else None, has_bias=wl.has_bias, workspace=ws_layers)
+            return
         if not use_side:
             join()
             call(dpc.dp_clip_factors, sq, wl.C, c)
@@ -216,17 +228,14 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False):
             return
         join()  # the previous step's sums still read c
         dpc.dp_clip_factors(sq, wl.C, c)
-        ready = torch.cuda.Event()
         ready.record(stream)
         for l, (A, G) in enumerate(layers):
             s_l = side[l % len(side)]
             s_l.wait_event(ready)
-            with torch.cuda.stream(s_l):
-                dpc.dp_clipped_sum_noise(A, G, c, wl.C, wl.sigma, float(B), wl.seed, l, k, outs[l], bouts[l],
-                                         workspace=ws_sum[l])
-                done = torch.cuda.Event()
-                done.record(s_l)
-            sum_done[l] = done
+            dpc.dp_clipped_sum_noise(A, G, c, wl.C, wl.sigma, float(B), wl.seed, l, k, outs[l], bouts[l],
+                                     workspace=ws_sum[l], stream=s_l)
+            done_ev[l].record(s_l)
+            sum_done[l] = done_ev[l]
 
     def join():
         for l, ev_l in enumerate(sum_done):
@@ -360,6 +369,9 @@ def main():
     ap.add_argument("--breakdown", action="store_true", help="print per-call times to stderr")
     ap.add_argument("--per-layer-norms", action="store_true",
                     help="global clipping: one dp_ghost_norm call per layer instead of one multi-layer call")
+    ap.add_argument("--per-layer-sums", action="store_true",
+                    help="global clipping: one dp_clipped_sum_noise call per layer (on --streams side streams) "
+                         "instead of one multi-layer call")
     ap.add_argument("--streams", type=int, default=None,
                     help="side streams for the layers' clipped sums in the throughput steps (global clipping); "
                          "default 3 for layer sets of at most 8 layers, else 1")
@@ -374,9 +386,19 @@ def main():
         copy_probe()
         return
     wl = W.WORKLOADS[a.workload]
-    nstreams = a.streams if a.streams is not None else (3 if wl.n_layers <= 8 and not wl.per_layer else 1)
+    # the multi-layer clipped-sum call shares launches among bf16 layers without bias whose T is a
+    # multiple of 64 and d, p multiples of 8; a set with none of those runs per-layer calls on side
+    # streams instead (the library runs them one after another within one call)
+    shapes0 = [wl.layer_shape(l) for l in range(wl.n_layers)]
+    groupable = (wl.dtype == "bf16" and not wl.has_bias and
+                 sum(1 for (T, d, p) in shapes0 if T % 64 == 0 and d % 8 == 0 and p % 8 == 0) >= 2)
+    per_layer_sums = a.per_layer_sums or not groupable
+    if per_layer_sums and not wl.per_layer:
+        nstreams = a.streams if a.streams is not None else (3 if wl.n_layers <= 8 else 1)
+    else:
+        nstreams = 1
     wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device = run_gpu(wl, a.steps, a.warmup, nstreams,
-                                                                      a.per_layer_norms)
+                                                                      a.per_layer_norms, per_layer_sums)
     L = len(shapes)
     ms_per_step = 1e3 * wall / a.steps
     value = wl.B * a.steps / wall
@@ -414,8 +436,8 @@ def main():
     roof["algorithmic_bytes_per_call"] = round(byts / ndom)
     roof["kernel"] = ("dp_ghost_norm[_layers]: k_ghost_tiles / k_ghost_wide / k_explicit_tiles / k_norm_t1"
                       if dom == "norm"
-                      else "dp_clipped_sum_noise: k_contract_dl or k_contract_tiles (+ k_reduce_noise[_vec] "
-                           "when K is split)")
+                      else "dp_clipped_sum_noise[_layers]: k_contract_dl (split tiles finished in-kernel), "
+                           "k_contract_dl32 / k_contract_tiles (+ k_reduce_noise[_vec|_wide] when K is split)")
     roof["avg_call_us"] = round(1e3 * t_ms / ndom, 2)
     if a.breakdown:
         for (kd, l), m in zip(kinds, mean_ms):
@@ -427,7 +449,9 @@ def main():
            "layers": [list(s) for s in shapes] if L <= 8 else f"{wl.blocks} x {[list(s) for s in wl.layers]}",
            "parallelism": "single-gpu", "input_sets_rotated": n_sets,
            "clipping": "per-layer adaptive" if wl.per_layer else "global",
-           "sum_streams": nstreams if not wl.per_layer else 1}
+           "norm_call": "per-layer" if (wl.per_layer or a.per_layer_norms or L == 1) else "multi-layer",
+           "sum_call": ("per-layer" if (wl.per_layer or per_layer_sums) else "multi-layer"),
+           "sum_streams": nstreams}
     if on_device:
         cfg["inputs"] = "drawn on the device (torch generator), distinct for every layer"
     line = {

@@ -134,8 +134,9 @@ dp_status dp_ghost_norm_layers(void* stream, const dp_layer* layers, int32_t n_l
                                int64_t B, dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes,
                                float* sqnorm, int32_t accumulate, int32_t* paths_out);
 
-/* Workspace bytes dp_ghost_norm_layers needs for these layers. Returns 0 for
- * invalid arguments (and when no workspace is needed). */
+/* Workspace bytes that dp_ghost_norm_layers (with this mode and kappa) and
+ * dp_clipped_sum_noise_layers need for these layers (the larger of the two).
+ * Returns 0 for invalid arguments (and when no workspace is needed). */
 size_t dp_layers_workspace_bytes(const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B,
                                  dp_mode mode, int32_t kappa);
 
@@ -191,6 +192,37 @@ dp_status dp_clipped_sum_noise(void* stream, const void* A, const void* G, dp_dt
                                uint64_t seed, uint32_t layer_id, uint32_t step,
                                void* workspace, size_t ws_bytes,
                                float* out, float* bias_out);
+
+/*
+ * Clipped, noised mean gradients of several layers under one set of clip
+ * factors (flat clipping: one c for every layer), each layer's output as
+ * dp_clipped_sum_noise defines it, with noise stream layer_ids[l] (or l when
+ * layer_ids is NULL).
+ *
+ * Layers that the bf16 direct-to-LDS engine takes (bf16, no bias, T a
+ * multiple of 64, d and p multiples of 8) share kernel launches of up to 8
+ * layers: one tile shape and a K split per layer chosen for the set, so that
+ * the work items of all of them fill the GPU together; a split output tile
+ * is finished by the last of its splits inside the same launch. Other layers
+ * run one dp_clipped_sum_noise-like launch each. Results are deterministic
+ * for a given set of layer shapes; the K split of a layer may differ from the
+ * one a single-layer call picks, which changes the fp32 rounding of the sum
+ * (the noise term is the same bit for bit).
+ *
+ *  layers, n_layers  as in dp_ghost_norm_layers.
+ *  dtype, B          shared by all layers.
+ *  c, C, sigma, denom, seed, step  as in dp_clipped_sum_noise (c: [B]).
+ *  layer_ids         host uint32[n_layers] or NULL.
+ *  workspace, ws_bytes  at least dp_layers_workspace_bytes(...) bytes.
+ *  outs              host array of n_layers device pointers, outs[l] [d_l, p_l] fp32.
+ *  bias_outs         host array of n_layers device pointers or NULL: entry l
+ *                    ([p_l] fp32) is required when layers[l].has_bias and
+ *                    ignored otherwise; NULL when no layer has a bias.
+ */
+dp_status dp_clipped_sum_noise_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype,
+                                      int64_t B, const float* c, float C, float sigma, float denom, uint64_t seed,
+                                      const uint32_t* layer_ids, uint32_t step, void* workspace, size_t ws_bytes,
+                                      float* const* outs, float* const* bias_outs);
 
 /*
  * One update of the adaptive per-layer clipping bound of TTP:

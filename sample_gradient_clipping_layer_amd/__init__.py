@@ -12,6 +12,8 @@ The functions mirror the C ABI in ``include/dpclip.h``:
     dp_ghost_norm_layers(layers, sqnorm, has_bias=False, mode=MODE_MIXED, kappa=1,
                          accumulate=False, workspace=None) -> [path, ...]
     dp_layers_workspace_bytes(layers, has_bias=False, mode=MODE_MIXED, kappa=1) -> int
+    dp_clipped_sum_noise_layers(layers, c, C, sigma, denom, seed, step, outs,
+                                bias_outs=None, has_bias=False, layer_ids=None, workspace=None)
     dp_clip_factors(sqnorm, C, c, norm=None)
     dp_clipped_sum_noise(A, G, c, C, sigma, denom, seed, layer_id, step, out,
                          bias_out=None, workspace=None)
@@ -21,7 +23,8 @@ The functions mirror the C ABI in ``include/dpclip.h``:
     dp_choose_path(T, d, p, mode=MODE_MIXED, kappa=1) -> int
 
 A and G are contiguous [B, T, d] / [B, T, p] tensors (float32 or bfloat16) on
-the current GPU; norm, factor and output vectors are float32.
+the current GPU; norm, factor and output vectors are float32. Every call also
+takes ``stream=`` (a torch stream; default: torch's current stream).
 """
 from __future__ import annotations
 
@@ -37,7 +40,8 @@ DP_F32, DP_BF16 = 0, 1
 MODE_MIXED, MODE_GHOST, MODE_EXPLICIT = 0, 1, 2
 PATH_GHOST, PATH_EXPLICIT, PATH_T1 = 1, 2, 3
 
-EXPORTS = ("dp_ghost_norm", "dp_ghost_norm_layers", "dp_layers_workspace_bytes", "dp_clip_factors", "dp_clipped_sum_noise", "dp_adaptive_threshold",
+EXPORTS = ("dp_ghost_norm", "dp_ghost_norm_layers", "dp_layers_workspace_bytes", "dp_clipped_sum_noise_layers",
+           "dp_clip_factors", "dp_clipped_sum_noise", "dp_adaptive_threshold",
            "dp_workspace_bytes", "dp_choose_path", "dp_status_string", "dp_abi_version")
 
 _lib = None
@@ -65,6 +69,10 @@ def _declare(lib):
     lib.dp_ghost_norm_layers.argtypes = [vp, lp, c_i32, c_i32, c_i64, c_i32, c_i32, vp, ctypes.c_size_t, fp, c_i32,
                                          ctypes.POINTER(c_i32)]
     lib.dp_ghost_norm_layers.restype = c_i32
+    lib.dp_clipped_sum_noise_layers.argtypes = [vp, lp, c_i32, c_i32, c_i64, fp, f, f, f, c_u64,
+                                                ctypes.POINTER(c_u32), c_u32, vp, ctypes.c_size_t,
+                                                ctypes.POINTER(vp), ctypes.POINTER(vp)]
+    lib.dp_clipped_sum_noise_layers.restype = c_i32
     lib.dp_layers_workspace_bytes.argtypes = [lp, c_i32, c_i32, c_i64, c_i32, c_i32]
     lib.dp_layers_workspace_bytes.restype = ctypes.c_size_t
     lib.dp_clip_factors.argtypes = [vp, fp, c_i64, f, fp, fp]
@@ -101,9 +109,11 @@ def _check(fn: str, status: int):
         raise DpError(fn, status, lib().dp_status_string(status).decode())
 
 
-def _stream():
+def _stream(stream=None):
+    """HIP stream handle: the given torch stream, else torch's current one."""
     import torch
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    st = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(st.cuda_stream)
 
 
 def _ptr(t):
@@ -163,14 +173,14 @@ def _workspace(workspace, dt, B, T, d, p, mode, kappa, device):
 
 
 def dp_ghost_norm(A, G, sqnorm, has_bias: bool = False, mode: int = MODE_MIXED, kappa: int = 1,
-                  accumulate: bool = False, workspace=None) -> int:
+                  accumulate: bool = False, workspace=None, stream=None) -> int:
     dt, B, T, d, p = _layer(A, G)
     _f32_vec(sqnorm, "sqnorm")
     if sqnorm.numel() != B:
         raise ValueError("sqnorm must have B elements")
     ws, nbytes = _workspace(workspace, dt, B, T, d, p, mode, kappa, A.device)
     path = ctypes.c_int32(0)
-    _check("dp_ghost_norm", lib().dp_ghost_norm(_stream(), _ptr(A), _ptr(G), dt, B, T, d, p, int(bool(has_bias)),
+    _check("dp_ghost_norm", lib().dp_ghost_norm(_stream(stream), _ptr(A), _ptr(G), dt, B, T, d, p, int(bool(has_bias)),
                                                 int(mode), int(kappa), _ptr(ws), nbytes, _ptr(sqnorm),
                                                 int(bool(accumulate)), ctypes.byref(path)))
     return path.value
@@ -202,7 +212,7 @@ def dp_layers_workspace_bytes(layers, has_bias=False, mode: int = MODE_MIXED, ka
 
 
 def dp_ghost_norm_layers(layers, sqnorm, has_bias=False, mode: int = MODE_MIXED, kappa: int = 1,
-                         accumulate: bool = False, workspace=None):
+                         accumulate: bool = False, workspace=None, stream=None):
     """Squared norms summed over `layers` (a list of (A, G) pairs) into sqnorm."""
     import torch
     dt, B, arr = _layer_table(layers, has_bias)
@@ -214,12 +224,42 @@ def dp_ghost_norm_layers(layers, sqnorm, has_bias=False, mode: int = MODE_MIXED,
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=sqnorm.device)
     paths = (ctypes.c_int32 * len(layers))()
     _check("dp_ghost_norm_layers", lib().dp_ghost_norm_layers(
-        _stream(), arr, len(layers), dt, B, int(mode), int(kappa), _ptr(workspace),
+        _stream(stream), arr, len(layers), dt, B, int(mode), int(kappa), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(sqnorm), int(bool(accumulate)), paths))
     return list(paths)
 
 
-def dp_clip_factors(sqnorm, C: float, c, norm=None):
+def dp_clipped_sum_noise_layers(layers, c, C: float, sigma: float, denom: float, seed: int, step: int, outs,
+                                bias_outs=None, has_bias=False, layer_ids=None, workspace=None, stream=None):
+    """Clipped noised means of `layers` (a list of (A, G) pairs) under one c
+    into outs[l] ([d_l, p_l]); bias_outs[l] for the layers with a bias."""
+    import torch
+    dt, B, arr = _layer_table(layers, has_bias)
+    n = len(layers)
+    _f32_vec(c, "c")
+    if c.numel() != B or len(outs) != n:
+        raise ValueError("c must have B elements and outs one tensor per layer")
+    for k, o in enumerate(outs):
+        _f32_vec(o, "outs[k]")
+        if o.numel() != arr[k].d * arr[k].p:
+            raise ValueError(f"outs[{k}] must have d*p elements")
+    bptr = None
+    if bias_outs is not None:
+        if len(bias_outs) != n:
+            raise ValueError("one bias output (or None) per layer")
+        bptr = (ctypes.c_void_p * n)(*[None if b is None else b.data_ptr() for b in bias_outs])
+    ids = None if layer_ids is None else (ctypes.c_uint32 * n)(*[int(v) & 0xFFFFFFFF for v in layer_ids])
+    if workspace is None:
+        need = int(lib().dp_layers_workspace_bytes(arr, n, dt, B, MODE_MIXED, 1))
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=c.device)
+    optr = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    _check("dp_clipped_sum_noise_layers", lib().dp_clipped_sum_noise_layers(
+        _stream(stream), arr, n, dt, B, _ptr(c), float(C), float(sigma), float(denom),
+        int(seed) & 0xFFFFFFFFFFFFFFFF, ids, int(step) & 0xFFFFFFFF, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), optr, bptr))
+
+
+def dp_clip_factors(sqnorm, C: float, c, norm=None, stream=None):
     _f32_vec(sqnorm, "sqnorm")
     _f32_vec(c, "c")
     if norm is not None:
@@ -227,11 +267,11 @@ def dp_clip_factors(sqnorm, C: float, c, norm=None):
     B = sqnorm.numel()
     if c.numel() != B or (norm is not None and norm.numel() != B):
         raise ValueError("sqnorm, c and norm must have the same length")
-    _check("dp_clip_factors", lib().dp_clip_factors(_stream(), _ptr(sqnorm), B, float(C), _ptr(c), _ptr(norm)))
+    _check("dp_clip_factors", lib().dp_clip_factors(_stream(stream), _ptr(sqnorm), B, float(C), _ptr(c), _ptr(norm)))
 
 
 def dp_clipped_sum_noise(A, G, c, C: float, sigma: float, denom: float, seed: int, layer_id: int, step: int,
-                         out, bias_out=None, workspace=None):
+                         out, bias_out=None, workspace=None, stream=None):
     dt, B, T, d, p = _layer(A, G)
     _f32_vec(c, "c")
     _f32_vec(out, "out")
@@ -243,18 +283,18 @@ def dp_clipped_sum_noise(A, G, c, C: float, sigma: float, denom: float, seed: in
             raise ValueError("bias_out must have p elements")
     ws, nbytes = _workspace(workspace, dt, B, T, d, p, MODE_MIXED, 1, A.device)
     _check("dp_clipped_sum_noise", lib().dp_clipped_sum_noise(
-        _stream(), _ptr(A), _ptr(G), dt, B, T, d, p, _ptr(c), float(C), float(sigma), float(denom),
+        _stream(stream), _ptr(A), _ptr(G), dt, B, T, d, p, _ptr(c), float(C), float(sigma), float(denom),
         int(seed) & 0xFFFFFFFFFFFFFFFF, int(layer_id) & 0xFFFFFFFF, int(step) & 0xFFFFFFFF, _ptr(ws), nbytes,
         _ptr(out), _ptr(bias_out)))
 
 
 def dp_adaptive_threshold(norm, C_prev: float, alpha: float, beta: float, sigma_l2: float, init: bool, seed: int,
-                          layer_id: int, step: int, C_next, C_l2_out=None):
+                          layer_id: int, step: int, C_next, C_l2_out=None, stream=None):
     _f32_vec(norm, "norm")
     _f32_vec(C_next, "C_next")
     if C_l2_out is not None:
         _f32_vec(C_l2_out, "C_l2_out")
     _check("dp_adaptive_threshold", lib().dp_adaptive_threshold(
-        _stream(), _ptr(norm), norm.numel(), float(C_prev), float(alpha), float(beta), float(sigma_l2),
+        _stream(stream), _ptr(norm), norm.numel(), float(C_prev), float(alpha), float(beta), float(sigma_l2),
         int(bool(init)), int(seed) & 0xFFFFFFFFFFFFFFFF, int(layer_id) & 0xFFFFFFFF, int(step) & 0xFFFFFFFF,
         _ptr(C_next), _ptr(C_l2_out)))

@@ -75,10 +75,14 @@ size_t norm_ws_bytes(int dtype, int path, int64_t B, int64_t T, int64_t d, int64
   return norm_partial_bytes(B, ntiles) + round256((size_t)B * sizeof(unsigned long long));
 }
 
-size_t contract_ws_bytes(dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64_t p, int has_bias) {
-  const dpk::ContractPlan pl = dpk::contract_plan(dtype, B, T, d, p, has_bias);
+size_t contract_ws_for(const dpk::ContractPlan& pl, int64_t d, int64_t p, int has_bias) {
+  if (pl.engine == 1) return dpk::dl_layer_ws_bytes(dpk::dl_single_plan(pl), 0, d, p);
   if (pl.ks == 1 && !pl.partials) return 0;  // one K split: the epilogue writes the output directly
   return round256((size_t)pl.ks * (size_t)(d + (has_bias ? 1 : 0)) * (size_t)p * sizeof(float));
+}
+
+size_t contract_ws_bytes(dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64_t p, int has_bias) {
+  return contract_ws_for(dpk::contract_plan(dtype, B, T, d, p, has_bias), d, p, has_bias);
 }
 
 dp_status hip_status(hipError_t e) { return e == hipSuccess ? DP_OK : DP_ERR_HIP; }
@@ -115,16 +119,26 @@ struct NormRun {
 
 constexpr int32_t kMaxNormLayers = 4096;
 
-dp_status check_norm_layers(const dp_layer* layers, int32_t n, dp_dtype dtype, int64_t B, dp_mode mode,
-                            int32_t kappa) {
+// The layer list itself: count, pointers, shapes, dtype, reserved fields.
+dp_status check_layer_list(const dp_layer* layers, int32_t n, dp_dtype dtype, int64_t B) {
   if (!layers) return DP_ERR_NULL;
   if (n < 1 || n > kMaxNormLayers) return DP_ERR_SHAPE;
-  if (mode < DP_MODE_MIXED || mode > DP_MODE_EXPLICIT || kappa < 1) return DP_ERR_VALUE;
   for (int32_t l = 0; l < n; ++l) {
     const dp_layer& x = layers[l];
     const dp_status s = check_layer(x.A, x.G, dtype, B, x.T, x.d, x.p);
     if (s != DP_OK) return s;
     if (x.reserved != 0) return DP_ERR_VALUE;
+  }
+  return DP_OK;
+}
+
+dp_status check_norm_layers(const dp_layer* layers, int32_t n, dp_dtype dtype, int64_t B, dp_mode mode,
+                            int32_t kappa) {
+  const dp_status s = check_layer_list(layers, n, dtype, B);
+  if (s != DP_OK) return s;
+  if (mode < DP_MODE_MIXED || mode > DP_MODE_EXPLICIT || kappa < 1) return DP_ERR_VALUE;
+  for (int32_t l = 0; l < n; ++l) {
+    const dp_layer& x = layers[l];
     const int path = path_of(x.T, x.d, x.p, mode, kappa);
     if (!layer_fits(dtype, path, B, x.T, x.d, x.p, x.has_bias ? 1 : 0)) return DP_ERR_SHAPE;
   }
@@ -168,6 +182,76 @@ size_t run_ws_bytes(const NormRun& r, const dp_layer* layers, int dtype, int64_t
   }
   const dp_layer& x = layers[r.first];
   return norm_ws_bytes(dtype, path_of(x.T, x.d, x.p, mode, kappa), B, x.T, x.d, x.p, x.has_bias ? 1 : 0);
+}
+
+// ---- multi-layer clipped sums
+// Layers the direct-to-LDS bf16 engine takes go, in the caller's order, in
+// launches of up to kDlGroupMax layers (each layer's workspace region after
+// the previous one's); the others, and an eligible layer left alone, get
+// single-layer launches. Launches follow one
+// another on the stream, so every launch starts again at the workspace base.
+struct SumLaunch {
+  int first[dpk::kDlGroupMax];
+  int count;
+  bool grouped;
+};
+
+std::vector<SumLaunch> plan_sum_launches(const dp_layer* layers, int32_t n, dp_dtype dtype, int64_t B) {
+  std::vector<SumLaunch> out;
+  SumLaunch cur{};
+  for (int32_t l = 0; l < n; ++l) {
+    const dp_layer& x = layers[l];
+    const int hb = x.has_bias ? 1 : 0;
+    if (dpk::dl_eligible(dtype, B, x.T, x.d, x.p, hb)) {  // the engine contract_plan picks first
+      cur.grouped = true;
+      cur.first[cur.count++] = (int)l;
+      if (cur.count == dpk::kDlGroupMax) {
+        out.push_back(cur);
+        cur = SumLaunch{};
+      }
+    } else {
+      SumLaunch one{};
+      one.first[0] = (int)l;
+      one.count = 1;
+      one.grouped = false;
+      out.push_back(one);
+    }
+  }
+  if (cur.count > 0) out.push_back(cur);
+  // one eligible layer alone: the single-layer path (its split tiles go to the reduce kernel)
+  for (SumLaunch& g : out)
+    if (g.count == 1) g.grouped = false;
+  return out;
+}
+
+dpk::DlGroupPlan group_plan_of(const SumLaunch& g, const dp_layer* layers, int64_t B) {
+  int64_t Bv[dpk::kDlGroupMax], Tv[dpk::kDlGroupMax], dv[dpk::kDlGroupMax], pv[dpk::kDlGroupMax];
+  for (int k = 0; k < g.count; ++k) {
+    const dp_layer& x = layers[g.first[k]];
+    Bv[k] = B;
+    Tv[k] = x.T;
+    dv[k] = x.d;
+    pv[k] = x.p;
+  }
+  return dpk::dl_group_plan(Bv, Tv, dv, pv, g.count, g.count > 1);
+}
+
+size_t sum_launch_ws_bytes(const SumLaunch& g, const dp_layer* layers, dp_dtype dtype, int64_t B) {
+  if (!g.grouped) {
+    const dp_layer& x = layers[g.first[0]];
+    return contract_ws_bytes(dtype, B, x.T, x.d, x.p, x.has_bias ? 1 : 0);
+  }
+  const dpk::DlGroupPlan pl = group_plan_of(g, layers, B);
+  size_t w = 0;
+  for (int k = 0; k < g.count; ++k) w += dpk::dl_layer_ws_bytes(pl, k, layers[g.first[k]].d, layers[g.first[k]].p);
+  return w;
+}
+
+size_t sum_layers_ws_bytes(const dp_layer* layers, int32_t n, dp_dtype dtype, int64_t B) {
+  size_t w = 0;
+  for (const SumLaunch& g : plan_sum_launches(layers, n, dtype, B))
+    w = std::max(w, sum_launch_ws_bytes(g, layers, dtype, B));
+  return w;
 }
 
 }  // namespace
@@ -240,7 +324,7 @@ size_t dp_layers_workspace_bytes(const dp_layer* layers, int32_t n_layers, dp_dt
   if (check_norm_layers(layers, n_layers, dtype, B, mode, kappa) != DP_OK) return 0;
   std::vector<NormRun> runs((size_t)n_layers);
   const int nr = plan_norm_runs(layers, n_layers, dtype, B, mode, kappa, runs.data());
-  size_t w = 0;
+  size_t w = sum_layers_ws_bytes(layers, n_layers, dtype, B);
   for (int r = 0; r < nr; ++r) w = std::max(w, run_ws_bytes(runs[r], layers, dtype, B, mode, kappa));
   return w;
 }
@@ -297,6 +381,85 @@ dp_status dp_ghost_norm_layers(void* stream, const dp_layer* layers, int32_t n_l
   return DP_OK;
 }
 
+dp_status dp_clipped_sum_noise_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype,
+                                      int64_t B, const float* c, float C, float sigma, float denom, uint64_t seed,
+                                      const uint32_t* layer_ids, uint32_t step, void* workspace, size_t ws_bytes,
+                                      float* const* outs, float* const* bias_outs) {
+  dp_status s = check_layer_list(layers, n_layers, dtype, B);
+  if (s != DP_OK) return s;
+  if (!c || !outs) return DP_ERR_NULL;
+  if (!aligned(c, 4)) return DP_ERR_ALIGN;
+  if (!finite(C) || !(C > 0.0f) || !finite(sigma) || sigma < 0.0f || !finite(denom) || !(denom > 0.0f))
+    return DP_ERR_VALUE;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const dp_layer& x = layers[l];
+    if (!outs[l]) return DP_ERR_NULL;
+    if (!aligned(outs[l], 4)) return DP_ERR_ALIGN;
+    if (x.has_bias) {
+      if (!bias_outs || !bias_outs[l]) return DP_ERR_NULL;
+      if (!aligned(bias_outs[l], 4)) return DP_ERR_ALIGN;
+    }
+  }
+  // plans of every launch, made once (the grouped launches check their own grid size)
+  const std::vector<SumLaunch> launches = plan_sum_launches(layers, n_layers, dtype, B);
+  std::vector<dpk::DlGroupPlan> gplans(launches.size());
+  std::vector<dpk::ContractPlan> splans(launches.size());
+  size_t need = 0;
+  for (size_t k = 0; k < launches.size(); ++k) {
+    const SumLaunch& g = launches[k];
+    const dp_layer& x0 = layers[g.first[0]];
+    if (g.grouped) {
+      gplans[k] = group_plan_of(g, layers, B);
+      size_t w = 0;
+      for (int j = 0; j < g.count; ++j)
+        w += dpk::dl_layer_ws_bytes(gplans[k], j, layers[g.first[j]].d, layers[g.first[j]].p);
+      need = std::max(need, w);
+    } else {
+      const int hb = x0.has_bias ? 1 : 0;
+      splans[k] = dpk::contract_plan(dtype, B, x0.T, x0.d, x0.p, hb);
+      if ((int64_t)splans[k].mt * splans[k].nt * splans[k].ks >= ((int64_t)1 << 31)) return DP_ERR_SHAPE;
+      need = std::max(need, contract_ws_for(splans[k], x0.d, x0.p, hb));
+    }
+  }
+  if (need > 0) {
+    if (!workspace) return DP_ERR_NULL;
+    if (ws_bytes < need) return DP_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return DP_ERR_ALIGN;
+  }
+  s = device_ready();
+  if (s != DP_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float sc = sigma * C;
+  auto lid = [&](int l) { return layer_ids ? layer_ids[l] : (uint32_t)l; };
+  for (size_t k = 0; k < launches.size(); ++k) {
+    const SumLaunch& g = launches[k];
+    hipError_t e;
+    if (g.grouped) {
+      const dpk::DlGroupPlan& pl = gplans[k];
+      dpk::DlLaunchLayer ll[dpk::kDlGroupMax];
+      size_t off = 0;
+      for (int k = 0; k < g.count; ++k) {
+        const int l = g.first[k];
+        const dp_layer& x = layers[l];
+        const size_t wb = dpk::dl_layer_ws_bytes(pl, k, x.d, x.p);
+        float* wsl = wb ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + off) : nullptr;
+        off += wb;
+        ll[k] = dpk::DlLaunchLayer{x.A, x.G, B, x.T, x.d, x.p, wsl, outs[l],
+                                   dpk::make_noise_args(sc, denom, seed, lid(l), step)};
+      }
+      e = dpk::launch_contract_dl_group(st, ll, g.count, c, pl, dpk::next_epoch());
+    } else {
+      const int l = g.first[0];
+      const dp_layer& x = layers[l];
+      const int hb = x.has_bias ? 1 : 0;
+      e = dpk::launch_clipped_sum(st, dtype, x.A, x.G, c, B, x.T, x.d, x.p, splans[k], static_cast<float*>(workspace), sc,
+                                  denom, seed, lid(l), step, outs[l], hb ? bias_outs[l] : nullptr);
+    }
+    if (e != hipSuccess) return DP_ERR_HIP;
+  }
+  return DP_OK;
+}
+
 dp_status dp_clip_factors(void* stream, const float* sqnorm, int64_t B, float C, float* c, float* norm) {
   if (!sqnorm || !c) return DP_ERR_NULL;
   if (B < 1 || B >= kMaxDim) return DP_ERR_SHAPE;
@@ -319,7 +482,7 @@ dp_status dp_clipped_sum_noise(void* stream, const void* A, const void* G, dp_dt
     return DP_ERR_VALUE;
   const int hb = bias_out ? 1 : 0;
   const dpk::ContractPlan pl = dpk::contract_plan(dtype, B, T, d, p, hb);
-  const size_t need = contract_ws_bytes(dtype, B, T, d, p, hb);
+  const size_t need = contract_ws_for(pl, d, p, hb);
   if (need > 0) {
     if (!workspace) return DP_ERR_NULL;
     if (ws_bytes < need) return DP_ERR_WORKSPACE;

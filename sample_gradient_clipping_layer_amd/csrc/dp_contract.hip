@@ -92,18 +92,87 @@ __device__ __forceinline__ u32x4 frag_tr(uint32_t addr, int off, int four_rows) 
 #endif
 constexpr int kDlReadGroup = DL_READ_GROUP;
 
-struct DlArgs {
+// One layer of a contraction launch.
+struct DlLayer {
+  const bf16s* A;
+  const bf16s* G;
+  float* ws;                  // partial tiles [ks][d][p] (when ks > 1 or the tile always writes partials)
+  unsigned long long* ctr;    // [mt * nt] arrival counters of each output tile's K splits
+  float* out;
   int64_t d, p;
-  int64_t cps;              // chunks per sample (T / KC)
-  int mt, nt;
-  int64_t ks;               // K splits
+  int64_t cps;                // chunks per sample (T / KC)
+  int64_t ks;                 // K splits
   int64_t chunks_per_split;
-  int64_t nchunks;          // B * T / KC
-  int m_fast;               // work-item order: tile row index fastest
+  int64_t nchunks;            // B * T / KC
+  int64_t per;                // work items per XCD: ceil(mt * nt * ks / 8)
+  int mt, nt;
+  int m_fast;                 // work-item order: tile row index fastest
   NoiseArgs na;
 };
+// The layers of one launch, in dispatch order, and the call's tag for the
+// arrival counters of the in-kernel fix-up.
+struct DlGroup {
+  DlLayer L[kDlGroupMax];
+  int n;
+  int fixup;       // split tiles finished in-kernel; else left in ws for the reduce kernel
+  uint64_t epoch;
+};
 
-
+// K-split fix-up of output tile `tile` (rows m0.., columns n0..): called by
+// every thread of each split's workgroup after its partial tile went to
+// ws[split] with plain stores. The barrier orders them before thread 0's
+// device-scope release fence (the XCDs' L2 caches are not coherent with each
+// other: the fence writes this L2's dirty lines back) and the arrival count;
+// the last split to arrive takes an acquire fence, then adds the ks partials
+// in split order (0 + P_0 + P_1 + ...), the noise and 1/denom, and writes the
+// output. Which split arrives last does not change the result. Rows are
+// taken in groups of 4 (one Philox block per column), columns in pairs.
+template <int BM, int BN, int NT>
+__device__ __forceinline__ void dl_fixup(const DlLayer& L, uint64_t epoch, int64_t tile, int64_t m0, int64_t n0,
+                                         unsigned* flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const bool last = arrive_last(L.ctr + tile, epoch, (uint32_t)L.ks);
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *flag = last ? 1u : 0u;
+  }
+  __syncthreads();
+  if (*flag == 0u) return;
+  const int64_t sstride = L.d * L.p;
+  constexpr int KU = 4;  // splits whose loads are issued together
+#pragma unroll 1
+  for (int u = threadIdx.x; u < (BM / 4) * (BN / 2); u += NT) {
+    const int64_t m = m0 + 4 * (u / (BN / 2)), n = n0 + 2 * (u % (BN / 2));
+    if (m >= L.d || n >= L.p) continue;  // d % 8 == 0, p % 8 == 0: all 4 rows and both columns exist
+    const float* base = L.ws + m * L.p + n;
+    float sx[4] = {0.f, 0.f, 0.f, 0.f}, sy[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int64_t s0 = 0; s0 < L.ks; s0 += KU) {
+      float2 v[KU][4];
+#pragma unroll
+      for (int j = 0; j < KU; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (s0 + j < L.ks) v[j][r] = *reinterpret_cast<const float2*>(base + (s0 + j) * sstride + r * L.p);
+#pragma unroll
+      for (int j = 0; j < KU; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (s0 + j < L.ks) {
+            sx[r] += v[j][r].x;
+            sy[r] += v[j][r].y;
+          }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const f32x4 z = normals4((uint32_t)((m >> 2) * L.p + n + cc), 2u * L.na.layer, L.na.step, 0u, L.na.k0, L.na.k1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        L.out[(m + r) * L.p + n + cc] = noised_mean_spec(cc ? sy[r] : sx[r], L.na.sc, z[r], L.na.inv_denom);
+    }
+  }
+}
 
 // RATIO (one accumulator set, for wave tiles too large for two): acc holds
 // the clipped sum so far divided by the current sample's clip factor; at the
@@ -111,28 +180,48 @@ struct DlArgs {
 // at the end multiplied by the last c. One fp32 rounding per sample instead
 // of the exact fold; samples with c_i = 0 contribute exactly nothing and are
 // skipped; a NaN factor still propagates. The partial tile is written to the
-// workspace straight from registers (FUSED is not used).
-template <int BM, int BN, int STAGES, int NW, bool FUSED, int KCK = kDlKC, bool RATIO = false>
-__global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restrict__ A, const bf16s* __restrict__ G,
-                                                            const float* __restrict__ c, float* __restrict__ ws,
-                                                            float* __restrict__ out, DlArgs a) {
+// workspace straight from registers.
+//
+// Work items: XCD x (blockIdx % 8) takes items [x * per_l, (x+1) * per_l) of
+// every layer l in turn, so that each XCD holds a share of every layer and
+// its concurrently running workgroups share operand tiles in its L2.
+template <int BM, int BN, int STAGES, int NW, int KCK = kDlKC, bool RATIO = false>
+__global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const float* __restrict__ c, DlGroup g) {
   using C = DlCfg<BM, BN, STAGES, NW, KCK>;
-  static_assert(!(RATIO && FUSED), "the single-accumulator variant writes partials");
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+  __shared__ unsigned fix_flag;
 
-  // ---- work item (XCD-contiguous)
-  const int64_t ntl = (int64_t)a.mt * a.nt;
-  const int64_t nitems = ntl * a.ks;
-  const int64_t per = (nitems + 7) / 8;
-  const int64_t w = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (w >= nitems) return;  // whole workgroup, before any barrier
+  // ---- layer and work item
+  const int64_t xcd = blockIdx.x & 7;
+  const int64_t local = blockIdx.x >> 3;
+  int li = -1;
+  int64_t first = 0, acc_per = 0;
+#pragma unroll
+  for (int k = 0; k < kDlGroupMax; ++k)
+    if (k < g.n && li < 0) {
+      if (local < acc_per + g.L[k].per) {
+        li = k;
+        first = acc_per;
+      }
+      acc_per += g.L[k].per;
+    }
+  if (li < 0) return;  // whole workgroup, before any barrier
+  DlLayer L = g.L[0];
+#pragma unroll
+  for (int k = 1; k < kDlGroupMax; ++k)
+    if (k == li) L = g.L[k];
+  const bf16s* __restrict__ A = L.A;
+  const bf16s* __restrict__ G = L.G;
+  const int64_t ntl = (int64_t)L.mt * L.nt;
+  const int64_t w = xcd * L.per + (local - first);
+  if (w >= ntl * L.ks) return;
   const int64_t split = w / ntl;
   const int64_t t = w - split * ntl;
-  const int tm = a.m_fast ? (int)(t % a.mt) : (int)(t / a.nt);
-  const int tn = a.m_fast ? (int)(t / a.mt) : (int)(t % a.nt);
+  const int tm = L.m_fast ? (int)(t % L.mt) : (int)(t / L.nt);
+  const int tn = L.m_fast ? (int)(t / L.mt) : (int)(t % L.nt);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const int64_t q0 = split * a.chunks_per_split;
-  const int64_t q1 = q0 + a.chunks_per_split < a.nchunks ? q0 + a.chunks_per_split : a.nchunks;
+  const int64_t q0 = split * L.chunks_per_split;
+  const int64_t q1 = q0 + L.chunks_per_split < L.nchunks ? q0 + L.chunks_per_split : L.nchunks;
   const int nq = (int)(q1 - q0);
 
   const int lane = threadIdx.x & 63;
@@ -147,21 +236,21 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
     const int byte = (wave + NW * i) * 1024 + 16 * lane;
     const int r = byte / C::RA, slot = (byte % C::RA) / 16;
     int64_t col = m0 + 8 * (slot ^ (4 * (r & 3)));
-    if (col > a.d - 8) col = a.d - 8;  // columns past d only feed unwritten output rows
-    offA[i] = (uint32_t)((r * a.d + col) * 2);
+    if (col > L.d - 8) col = L.d - 8;  // columns past d only feed unwritten output rows
+    offA[i] = (uint32_t)((r * L.d + col) * 2);
   }
 #pragma unroll
   for (int i = 0; i < C::LG; ++i) {
     const int byte = (wave + NW * i) * 1024 + 16 * lane;
     const int r = byte / C::RG, slot = (byte % C::RG) / 16;
     int64_t col = n0 + 8 * (slot ^ (4 * (r & 3)));
-    if (col > a.p - 8) col = a.p - 8;
-    offG[i] = (uint32_t)((r * a.p + col) * 2);
+    if (col > L.p - 8) col = L.p - 8;
+    offG[i] = (uint32_t)((r * L.p + col) * 2);
   }
 
   auto issue = [&](int64_t q, int stage) {
-    const bf16s* ga = A + q * (int64_t)C::KC * a.d;
-    const bf16s* gg = G + q * (int64_t)C::KC * a.p;
+    const bf16s* ga = A + q * (int64_t)C::KC * L.d;
+    const bf16s* gg = G + q * (int64_t)C::KC * L.p;
     const uint32_t sa = lds_addr(lds) + stage * C::STAGE + wave * 1024;
     const uint32_t sg = sa + C::A_BYTES;
 #pragma unroll
@@ -241,8 +330,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
   // ---- pipeline: chunk q in stage q % STAGES; loads for chunk it+STAGES-1
   // go out once every wave is past chunk it-1 (the barrier), while chunk it
   // is computed.
-  int64_t sample = q0 / a.cps;
-  int64_t in_sample = q0 - sample * a.cps;
+  int64_t sample = q0 / L.cps;
+  int64_t in_sample = q0 - sample * L.cps;
   float cur = 0.0f, prev = 0.0f;  // RATIO: current and last nonzero clip factor
   bool have_prev = false;
 #pragma unroll
@@ -274,7 +363,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
         }
       }
       if (cur != 0.0f) compute(sb, std::false_type{});
-      if (++in_sample == a.cps) {
+      if (++in_sample == L.cps) {
         in_sample = 0;
         ++sample;
       }
@@ -285,7 +374,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
       else
         compute(sb, std::false_type{});
     }
-    if (++in_sample == a.cps || it + 1 == nq) {
+    if (++in_sample == L.cps || it + 1 == nq) {
       const float ci = c[sample];
 #pragma unroll
       for (int bi = 0; bi < C::NBM; ++bi)
@@ -293,7 +382,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
         for (int bj = 0; bj < C::NBN; ++bj)
 #pragma unroll
           for (int j = 0; j < 16; ++j) acc[bi][bj][j] = __builtin_fmaf(ci, tmp[bi][bj][j], acc[bi][bj][j]);
-      if (in_sample == a.cps) {
+      if (in_sample == L.cps) {
         in_sample = 0;
         ++sample;
       }
@@ -301,10 +390,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
   }
 
   if constexpr (RATIO) {
-    // ---- epilogue: undo the last sample's division and write the partial
-    // tile [m][n] (m < d, n < p) straight from the accumulators
+    // ---- epilogue: undo the last sample's division, write the partial tile
+    // [m][n] (m < d, n < p) straight from the accumulators, then the fix-up
     const float last = have_prev ? prev : 0.0f;
-    float* wsp = ws + split * a.d * a.p;
+    float* wsp = L.ws + split * L.d * L.p;
 #pragma unroll
     for (int bi = 0; bi < C::NBM; ++bi)
 #pragma unroll
@@ -313,14 +402,17 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
         for (int j = 0; j < 16; ++j) {
           const int64_t m = m0 + wm * C::WM + bi * 32 + acc_row(j, lane);
           const int64_t n = n0 + wn * C::WN + bj * 32 + acc_col(lane);
-          if (m < a.d && n < a.p) wsp[m * a.p + n] = have_prev ? acc[bi][bj][j] * last : 0.0f;
+          if (m < L.d && n < L.p) wsp[m * L.p + n] = have_prev ? acc[bi][bj][j] * last : 0.0f;
         }
+    if (g.fixup) dl_fixup<BM, BN, C::NT>(L, g.epoch, t, m0, n0, &fix_flag);
     return;
   } else {
   // ---- epilogue: the output tile goes through LDS ([BM][BN + 8] fp32; the
-  // stages are free once every wave passed the barrier), then each thread
-  // takes whole Philox blocks (4 rows of one column) or float4 row pieces,
-  // with consecutive threads on consecutive columns.
+  // stages are free once every wave passed the barrier). With one K split the
+  // noise and the mean are applied here: each thread takes whole Philox
+  // blocks (4 rows of one column), consecutive threads on consecutive
+  // columns. Otherwise the partial tile goes to ws[split] (16-byte pieces
+  // of consecutive columns) and the fix-up follows.
   constexpr int TP = BN + 8;
   static_assert(BM * TP * 4 <= C::LDS, "epilogue tile fits the stages");
   float* tile = reinterpret_cast<float*>(lds);
@@ -333,30 +425,30 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const bf16s* __restr
       for (int j = 0; j < 16; ++j)
         tile[(wm * C::WM + bi * 32 + acc_row(j, lane)) * TP + wn * C::WN + bj * 32 + acc_col(lane)] = acc[bi][bj][j];
   lds_barrier();
-  if constexpr (FUSED) {
+  if (L.ks == 1) {
 #pragma unroll 1
     for (int b = threadIdx.x; b < (BM / 4) * BN; b += C::NT) {
       const int rq = b / BN, nn = b % BN;
       const int64_t m = m0 + 4 * rq, n = n0 + nn;
-      if (m >= a.d || n >= a.p) continue;
-      const f32x4 z = normals4((uint32_t)((m >> 2) * a.p + n), 2u * a.na.layer, a.na.step, 0u, a.na.k0, a.na.k1);
+      if (m >= L.d || n >= L.p) continue;
+      const f32x4 z = normals4((uint32_t)((m >> 2) * L.p + n), 2u * L.na.layer, L.na.step, 0u, L.na.k0, L.na.k1);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (m + r < a.d)
-          out[(m + r) * a.p + n] = noised_mean_spec(tile[(4 * rq + r) * TP + nn], a.na.sc, z[r], a.na.inv_denom);
+        if (m + r < L.d)
+          L.out[(m + r) * L.p + n] = noised_mean_spec(tile[(4 * rq + r) * TP + nn], L.na.sc, z[r], L.na.inv_denom);
     }
-  } else {
-    float* wsp = ws + split * a.d * a.p;
-#pragma unroll 1
-    for (int e = threadIdx.x; e < BM * (BN / 4); e += C::NT) {
-      const int row = e / (BN / 4), c4 = e % (BN / 4);
-      const int64_t m = m0 + row, n = n0 + 4 * c4;
-      if (m >= a.d || n >= a.p) continue;
-      const float4 v = *reinterpret_cast<const float4*>(tile + row * TP + 4 * c4);
-      // p % 8 == 0 and n % 4 == 0: the four columns are all in range and 16-byte aligned
-      *reinterpret_cast<float4*>(wsp + m * a.p + n) = v;
-    }
+    return;
   }
+  float* wsp = L.ws + split * L.d * L.p;
+#pragma unroll 1
+  for (int e = threadIdx.x; e < BM * (BN / 4); e += C::NT) {
+    const int row = e / (BN / 4), c4 = e % (BN / 4);
+    const int64_t m = m0 + row, n = n0 + 4 * c4;
+    if (m >= L.d || n >= L.p) continue;
+    // p % 8 == 0 and n % 4 == 0: the four columns are all in range and 16-byte aligned
+    *reinterpret_cast<float4*>(wsp + m * L.p + n) = *reinterpret_cast<const float4*>(tile + row * TP + 4 * c4);
+  }
+  if (g.fixup) dl_fixup<BM, BN, C::NT>(L, g.epoch, t, m0, n0, &fix_flag);
   }
 }
 
@@ -367,125 +459,233 @@ bool dl_eligible(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has
          kDlKC * (d > p ? d : p) < (1ll << 31);
 }
 
-// Tile and K split for the direct-load engine from a cost model: rounds of
-// one workgroup per CU (256 CUs) x the chunks each item runs at a per-CU
-// MFMA rate that grows with the tile (fewer LDS bytes per flop), plus the
-// write and re-read of split partials and a reduce launch.
 // The 256 x 256 tile (64 x 128 wave tiles, single accumulator set) streams
 // 32-row chunks through four stages and always writes partials.
 constexpr int kDlWideKC = 32, kDlWideStages = 4;
 
-// Tile and K split from a cost model fitted to MI355X measurements of this
-// engine: rounds of one workgroup per CU (256 CUs) x (the item's chunks at a
-// sustained fraction of the bf16 MFMA peak + a fixed cost per item: fill and
-// the partial tile's write), plus the write and re-read of split partials by
-// the reduce kernel and its launch.
-ContractPlan dl_plan(int64_t B, int64_t Tn, int64_t d, int64_t p) {
-  static const int tiles[3][2] = {{128, 128}, {256, 128}, {256, 256}};
-  static const double eff[3] = {0.30, 0.35, 0.47};        // of the bf16 peak, in the K loop
-  static const double fixed_s[3] = {6e-6, 8e-6, 13.5e-6};  // per item
-  static const int kcs[3] = {kDlKC, kDlKC, kDlWideKC};
-  const double cu_peak = 2.5e15 / 256.0;
-  ContractPlan best{};
+namespace {
+constexpr int kTiles = 3;
+const int kTileBM[kTiles] = {128, 256, 256}, kTileBN[kTiles] = {128, 128, 256};
+const int kTileKC[kTiles] = {kDlKC, kDlKC, kDlWideKC};
+// Cost model fitted to MI355X measurements of this engine: a work item runs
+// its chunks at a sustained fraction of the bf16 MFMA peak of one CU, plus a
+// fixed cost (pipeline fill, epilogue); one workgroup per CU (LDS). A split
+// tile's partials are written by every split and read back by the last one
+// (the fix-up) at the bandwidth one CU achieves.
+const double kTileEff[kTiles] = {0.30, 0.35, 0.47};
+const double kTileFixed[kTiles] = {6e-6, 8e-6, 13.5e-6};
+constexpr double kCuPeak = 2.5e15 / 256.0;
+constexpr double kFixupBytesPerS = 1.0e11;
+constexpr double kFixupFixed = 1.0e-6;
+constexpr int kCusPerXcd = 32;
+
+struct LayerChoice {
+  int64_t ks, cps, mt, nt, per;
+  double item_s, reduce_s;
+};
+
+// Split of one layer into items of about `target` chunks; false when the
+// tile cannot take it.
+bool choose_split(int ti, int64_t B, int64_t Tn, int64_t d, int64_t p, int64_t target, bool fixup,
+                  LayerChoice* o) {
+  const int kc = kTileKC[ti];
+  if (Tn % kc != 0) return false;
+  const int64_t nchunks = B * Tn / kc;
+  int64_t ks = (nchunks + target - 1) / target;
+  if (ks < 1) ks = 1;
+  if (ks > 512) ks = 512;
+  const int64_t cps = (nchunks + ks - 1) / ks;
+  ks = (nchunks + cps - 1) / cps;
+  if (kTileBN[ti] == 256 && cps < 64) return false;  // the wide tile needs long K ranges per item
+  o->ks = ks;
+  o->cps = cps;
+  o->mt = (d + kTileBM[ti] - 1) / kTileBM[ti];
+  o->nt = (p + kTileBN[ti] - 1) / kTileBN[ti];
+  o->per = (o->mt * o->nt * ks + 7) / 8;
+  const double chunk_s = 2.0 * kTileBM[ti] * kTileBN[ti] * kc / (kCuPeak * kTileEff[ti]);
+  const bool partials = ks > 1 || kTileBN[ti] == 256;
+  const double fix_s =
+      partials && fixup ? (double)ks * kTileBM[ti] * kTileBN[ti] * 4.0 / kFixupBytesPerS + kFixupFixed : 0.0;
+  o->item_s = (double)cps * chunk_s + kTileFixed[ti] + fix_s / (double)ks;  // the fix-up, spread over the splits
+  // without the fix-up: the reduce kernel writes the output after reading every partial
+  o->reduce_s = partials && !fixup ? (2.0 * ks + 1.0) * (double)d * (double)p * 4.0 / 8.0e12 + 4.0e-6 : 0.0;
+  return true;
+}
+
+// Makespan of one XCD's share (the first XCD holds the most): its 32 CUs
+// take the items in dispatch order, each as soon as one is free. A layer's
+// items are alike: whole rounds go to every CU, the rest to the least loaded
+// (the loads stay sorted: two sorted runs merged).
+double xcd_makespan(const LayerChoice* ch, const int* order, int n) {
+  double cu[kCusPerXcd] = {}, nx[kCusPerXcd];  // ascending
+  for (int k = 0; k < n; ++k) {
+    const LayerChoice& x = ch[order[k]];
+    const int64_t full = x.per / kCusPerXcd;
+    const int rem = (int)(x.per % kCusPerXcd);
+    const double add = (double)full * x.item_s;
+    int i = rem, j = 0, o = 0;  // run 1: cu[rem..] + add; run 2: cu[..rem) + add + item
+    while (o < kCusPerXcd) {
+      const bool take1 = j >= rem || (i < kCusPerXcd && cu[i] <= cu[j] + x.item_s);
+      nx[o++] = take1 ? cu[i++] + add : cu[j++] + add + x.item_s;
+    }
+    for (int u = 0; u < kCusPerXcd; ++u) cu[u] = nx[u];
+  }
+  return cu[kCusPerXcd - 1];
+}
+}  // namespace
+
+// Tile (shared by the launch) and per-layer K splits: over the three tiles
+// and a range of target item lengths, the smallest simulated makespan.
+// Layers go in dispatch order by decreasing item time.
+DlGroupPlan dl_group_plan(const int64_t* B, const int64_t* Tn, const int64_t* d, const int64_t* p, int n,
+                          bool fixup) {
+  static const int64_t targets[] = {4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256, 384, 512, 768, 1024,
+                                    1536, 2048, 4096, 8192, 1ll << 40};
+  DlGroupPlan best{};
+  best.n = 0;
   double best_t = 1e300;
-  for (int ti = 0; ti < 3; ++ti) {
-    const int bm = tiles[ti][0], bn = tiles[ti][1];
-    const bool wide = bn == 256;
-    if (Tn % kcs[ti] != 0) continue;
-    const int64_t nchunks = B * Tn / kcs[ti];
-    const int64_t mt = (d + bm - 1) / bm, nt = (p + bn - 1) / bn;
-    const double chunk_s = 2.0 * bm * bn * kcs[ti] / (cu_peak * eff[ti]);
-    const int64_t ks_max = nchunks < 512 ? nchunks : 512;
-    for (int64_t ks = 1; ks <= ks_max; ++ks) {
-      const int64_t cpsplit = (nchunks + ks - 1) / ks;
-      if ((nchunks + cpsplit - 1) / cpsplit != ks) continue;
-      // the wide tile pays off with long K ranges per item; on short ones its
-      // larger partial tiles cost more than the model sees once other
-      // layers' calls run beside it
-      if (wide && cpsplit < 64) continue;
-      const int64_t items = mt * nt * ks;
-      const double rounds = (double)((items + 255) / 256);
-      double t = rounds * ((double)cpsplit * chunk_s + fixed_s[ti]);
-      if (ks > 1 || wide) t += (2.0 * ks + 1.0) * (double)d * (double)p * 4.0 / 8.0e12 + 4.0e-6;
+  for (int ti = 0; ti < kTiles; ++ti) {
+    int64_t prev_ks[kDlGroupMax] = {};
+    for (int64_t target : targets) {
+      LayerChoice ch[kDlGroupMax];
+      bool ok = true;
+      for (int l = 0; l < n && ok; ++l) ok = choose_split(ti, B[l], Tn[l], d[l], p[l], target, fixup, &ch[l]);
+      if (!ok) continue;
+      bool same = true;  // the splits of the previous target: nothing new
+      for (int l = 0; l < n; ++l) {
+        same = same && ch[l].ks == prev_ks[l];
+        prev_ks[l] = ch[l].ks;
+      }
+      if (same) continue;
+      int order[kDlGroupMax];
+      for (int l = 0; l < n; ++l) order[l] = l;
+      for (int a = 1; a < n; ++a)  // stable, by decreasing item time
+        for (int b = a; b > 0 && ch[order[b]].item_s > ch[order[b - 1]].item_s; --b) {
+          const int tmp = order[b];
+          order[b] = order[b - 1];
+          order[b - 1] = tmp;
+        }
+      double t = xcd_makespan(ch, order, n);
+      for (int l = 0; l < n; ++l) t += ch[l].reduce_s;
       if (t < best_t * 0.999) {
         best_t = t;
-        best.bm = bm;
-        best.bn = bn;
-        best.mt = (int)mt;
-        best.nt = (int)nt;
-        best.ks = ks;
-        best.units_per_split = cpsplit;
-        best.partials = wide ? 1 : 0;
+        best.n = n;
+        best.bm = kTileBM[ti];
+        best.bn = kTileBN[ti];
+        best.kc = kTileKC[ti];
+        best.seconds = t;
+        best.fixup = fixup ? 1 : 0;
+        for (int l = 0; l < n; ++l) {
+          best.ks[l] = ch[l].ks;
+          best.cps[l] = ch[l].cps;
+          best.mt[l] = (int)ch[l].mt;
+          best.nt[l] = (int)ch[l].nt;
+          best.order[l] = order[l];
+        }
       }
     }
   }
-  best.engine = 1;
   return best;
 }
 
-// ---------------------------------------------------------------- launch
-struct DlPtrs {
-  const bf16s* A;
-  const bf16s* G;
-  const float* c;
-  float* ws;
-  float* out;
-};
+// One layer alone fills the GPU with a single round of items at best: the
+// last split of a tile would finish it alone at the end, so its partials go
+// to the reduce kernel instead.
+ContractPlan dl_plan(int64_t B, int64_t Tn, int64_t d, int64_t p) {
+  const DlGroupPlan g = dl_group_plan(&B, &Tn, &d, &p, 1, false);
+  ContractPlan pl{};
+  pl.bm = g.bm;
+  pl.bn = g.bn;
+  pl.mt = g.mt[0];
+  pl.nt = g.nt[0];
+  pl.ks = g.ks[0];
+  pl.units_per_split = g.cps[0];
+  pl.partials = (g.ks[0] > 1 || g.bn == 256) ? 1 : 0;
+  pl.engine = 1;
+  return pl;
+}
 
-template <int BM, int BN, int NW>
-static hipError_t launch_dl_t(hipStream_t st, const DlPtrs& P, const DlArgs& a, int64_t items) {
-  constexpr int S = kDlStages;
-  using C = DlCfg<BM, BN, S, NW>;
-  const int64_t per = (items + 7) / 8;
-  const dim3 grid((unsigned)(per * 8));
+DlGroupPlan dl_single_plan(const ContractPlan& pl) {
+  DlGroupPlan g{};
+  g.n = 1;
+  g.bm = pl.bm;
+  g.bn = pl.bn;
+  g.kc = pl.bn == 256 ? kDlWideKC : kDlKC;
+  g.ks[0] = pl.ks;
+  g.cps[0] = pl.units_per_split;
+  g.mt[0] = pl.mt;
+  g.nt[0] = pl.nt;
+  g.order[0] = 0;
+  g.fixup = 0;
+  return g;
+}
+
+size_t dl_layer_ws_bytes(const DlGroupPlan& g, int l, int64_t d, int64_t p) {
+  if (g.ks[l] == 1 && g.bn != 256) return 0;
+  const size_t part = (size_t)g.ks[l] * (size_t)d * (size_t)p * sizeof(float);
+  const size_t ctr = g.fixup ? (size_t)g.mt[l] * (size_t)g.nt[l] * sizeof(unsigned long long) : 0;
+  return (part + 255) / 256 * 256 + (ctr + 255) / 256 * 256;
+}
+
+// ---------------------------------------------------------------- launch
+template <int BM, int BN, int S, int KC, bool RATIO>
+static hipError_t launch_dl_t(hipStream_t st, const float* c, const DlGroup& grp, int64_t wgs) {
+  using C = DlCfg<BM, BN, S, 8, KC>;
+  auto kern = &k_contract_dl<BM, BN, S, 8, KC, RATIO>;
   // more than 64 KB of dynamic LDS must be allowed per kernel (per call:
   // cheap, and correct whichever device is current)
-  if (a.ks == 1) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_contract_dl<BM, BN, S, NW, true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_contract_dl<BM, BN, S, NW, true>), grid, dim3(C::NT), C::LDS, st, P.A, P.G, P.c, P.ws, P.out, a);
-  } else {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_contract_dl<BM, BN, S, NW, false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_contract_dl<BM, BN, S, NW, false>), grid, dim3(C::NT), C::LDS, st, P.A, P.G, P.c, P.ws, P.out, a);
-  }
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     C::LDS);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(C::NT), C::LDS, st, c, grp);
   return hipGetLastError();
+}
+
+hipError_t launch_contract_dl_group(hipStream_t st, const DlLaunchLayer* layers, int n, const float* c,
+                                    const DlGroupPlan& g, uint64_t epoch) {
+  DlGroup grp{};
+  grp.n = n;
+  grp.fixup = g.fixup;
+  grp.epoch = epoch;
+  int64_t per_sum = 0;
+  for (int k = 0; k < n; ++k) {
+    const int l = g.order[k];
+    const DlLaunchLayer& x = layers[l];
+    DlLayer& L = grp.L[k];
+    L.A = static_cast<const bf16s*>(x.A);
+    L.G = static_cast<const bf16s*>(x.G);
+    L.out = x.out;
+    L.d = x.d;
+    L.p = x.p;
+    L.cps = x.Tn / g.kc;
+    L.ks = g.ks[l];
+    L.chunks_per_split = g.cps[l];
+    L.nchunks = x.B * x.Tn / g.kc;
+    L.mt = g.mt[l];
+    L.nt = g.nt[l];
+    L.per = ((int64_t)L.mt * L.nt * L.ks + 7) / 8;
+    L.m_fast = L.mt <= L.nt ? 1 : 0;
+    L.na = x.na;
+    L.ws = x.ws;
+    const size_t part = (size_t)L.ks * (size_t)L.d * (size_t)L.p * sizeof(float);
+    L.ctr = x.ws && g.fixup ? reinterpret_cast<unsigned long long*>(reinterpret_cast<unsigned char*>(x.ws) +
+                                                                    (part + 255) / 256 * 256)
+                            : nullptr;
+    per_sum += L.per;
+  }
+  const int64_t wgs = 8 * per_sum;
+  if (wgs >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (g.bn == 256) return launch_dl_t<256, 256, kDlWideStages, kDlWideKC, true>(st, c, grp, wgs);
+  if (g.bm == 256) return launch_dl_t<256, 128, kDlStages, kDlKC, false>(st, c, grp, wgs);
+  return launch_dl_t<128, 128, kDlStages, kDlKC, false>(st, c, grp, wgs);
 }
 
 hipError_t launch_contract_dl(hipStream_t st, const void* A, const void* G, const float* c, int64_t B, int64_t Tn,
                               int64_t d, int64_t p, const ContractPlan& pl, float* ws, const NoiseArgs& na,
                               float* out) {
-  const DlPtrs P{static_cast<const bf16s*>(A), static_cast<const bf16s*>(G), c, ws, out};
-  const bool wide = pl.bn == 256;
-  const int kc = wide ? kDlWideKC : kDlKC;
-  DlArgs a;
-  a.d = d;
-  a.p = p;
-  a.cps = Tn / kc;
-  a.mt = pl.mt;
-  a.nt = pl.nt;
-  a.ks = pl.ks;
-  a.chunks_per_split = pl.units_per_split;
-  a.nchunks = B * Tn / kc;
-  a.m_fast = pl.mt <= pl.nt ? 1 : 0;
-  a.na = na;
-  const int64_t items = (int64_t)pl.mt * pl.nt * pl.ks;
-  if (wide) {
-    constexpr int S = kDlWideStages, KCW = kDlWideKC;
-    using C = DlCfg<256, 256, S, 8, KCW>;
-    const int64_t per = (items + 7) / 8;
-    const dim3 grid((unsigned)(per * 8));
-    auto kern = &k_contract_dl<256, 256, S, 8, false, KCW, true>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, grid, dim3(C::NT), C::LDS, st, P.A, P.G, P.c, P.ws, P.out, a);
-    return hipGetLastError();
-  }
-  if (pl.bm == 128 && pl.bn == 128) return launch_dl_t<128, 128, 8>(st, P, a, items);
-  return launch_dl_t<256, 128, 8>(st, P, a, items);
+  const DlGroupPlan g = dl_single_plan(pl);
+  const DlLaunchLayer x{A, G, B, Tn, d, p, ws, out, na};
+  return launch_contract_dl_group(st, &x, 1, c, g, next_epoch());
 }
 
 }  // namespace dpk

@@ -14,13 +14,24 @@ struct ContractPlan {
   int64_t ks;               // K splits (partial tiles summed by the reduce)
   int64_t units_per_split;  // engine 0: samples (bf16) or KC-row chunks (fp32); 1: 64-row, 2: 32-row chunks
   int engine;               // 0 register-staged (any shape), 1 direct-to-LDS bf16, 2 direct-to-LDS fp32
-  int partials = 0;         // the contraction writes partials (and a reduce adds the noise) even with one split
+  int partials = 0;         // the contraction writes partials even with one split
 };
 // Noise + mean applied in a contraction epilogue or reduce: out = (S + sc*z) * inv_denom.
 struct NoiseArgs {
   float sc, inv_denom;  // sigma*C and the fp32 reciprocal of denom
   uint32_t k0, k1, layer, step;
 };
+// out = (S + fl(sigma*C) * z) * fl(1/denom); noise key (seed lo32, seed hi32).
+inline NoiseArgs make_noise_args(float sc, float denom, uint64_t seed, uint32_t layer, uint32_t step) {
+  NoiseArgs na;
+  na.sc = sc;
+  na.inv_denom = 1.0f / denom;
+  na.k0 = (uint32_t)(seed & 0xFFFFFFFFu);
+  na.k1 = (uint32_t)(seed >> 32);
+  na.layer = layer;
+  na.step = step;
+  return na;
+}
 struct ExplicitPlan {
   int bm, bn, mt, nt;
 };
@@ -32,6 +43,36 @@ ContractPlan dl_plan(int64_t B, int64_t Tn, int64_t d, int64_t p);
 hipError_t launch_contract_dl(hipStream_t st, const void* A, const void* G, const float* c, int64_t B, int64_t Tn,
                               int64_t d, int64_t p, const ContractPlan& pl, float* ws, const NoiseArgs& na,
                               float* out);
+// Launches of the direct-to-LDS bf16 engine: up to kDlGroupMax eligible
+// layers in one kernel launch, one tile shape for all of them, K splits per
+// layer. In a multi-layer launch split tiles are finished inside the kernel
+// by their last split; a single-layer launch leaves them to the reduce kernel.
+constexpr int kDlGroupMax = 8;
+struct DlLaunchLayer {
+  const void* A;
+  const void* G;
+  int64_t B, Tn, d, p;
+  float* ws;  // this layer's workspace region (dl_layer_ws_bytes), or nullptr when that is 0
+  float* out;
+  NoiseArgs na;
+};
+struct DlGroupPlan {
+  int n;
+  int bm, bn, kc;                 // tile and K rows per chunk
+  int64_t ks[kDlGroupMax];        // per layer (caller's order)
+  int64_t cps[kDlGroupMax];       // chunks per split
+  int mt[kDlGroupMax], nt[kDlGroupMax];
+  int order[kDlGroupMax];         // dispatch order (layer indices)
+  int fixup;                      // split tiles finished in-kernel (else by the reduce kernel)
+  double seconds;                 // modelled time
+};
+DlGroupPlan dl_group_plan(const int64_t* B, const int64_t* Tn, const int64_t* d, const int64_t* p, int n,
+                          bool fixup);
+size_t dl_layer_ws_bytes(const DlGroupPlan& g, int l, int64_t d, int64_t p);
+// The one-layer group plan of a single-layer engine-1 plan.
+DlGroupPlan dl_single_plan(const ContractPlan& pl);
+hipError_t launch_contract_dl_group(hipStream_t st, const DlLaunchLayer* layers, int n, const float* c,
+                                    const DlGroupPlan& g, uint64_t epoch);
 // direct-to-LDS fp32 engine (bias row accumulated on the side, partials [ks][d + bias][p] in ws)
 bool dl32_eligible(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias);
 ContractPlan dl32_plan(int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias);
@@ -75,8 +116,8 @@ hipError_t launch_explicit(hipStream_t st, int dtype, const void* A, const void*
                            int64_t p, int has_bias, const NormSink& sink);
 // Tag of one call for its arrival counters: 48 bits, never 0, distinct per call in the process.
 uint64_t next_epoch();
-// Weighted contraction + noise + 1/denom: one kernel when pl.ks == 1,
-// else partial tiles in ws and a reduce kernel. bias_out != nullptr <=> bias row.
+// Weighted contraction + noise + 1/denom: one kernel when pl.ks == 1, else
+// partial tiles in ws and a reduce kernel. bias_out != nullptr <=> bias row.
 hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const void* G, const float* c, int64_t B,
                               int64_t Tn, int64_t d, int64_t p, const ContractPlan& pl, float* ws, float sc,
                               float denom, uint64_t seed, uint32_t layer, uint32_t step, float* out,

@@ -967,13 +967,7 @@ hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const vo
                               float denom, uint64_t seed, uint32_t layer, uint32_t step, float* out,
                               float* bias_out) {
   const int has_bias = bias_out != nullptr ? 1 : 0;
-  NoiseArgs na;
-  na.sc = sc;
-  na.inv_denom = 1.0f / denom;
-  na.k0 = (uint32_t)(seed & 0xFFFFFFFFu);
-  na.k1 = (uint32_t)(seed >> 32);
-  na.layer = layer;
-  na.step = step;
+  const NoiseArgs na = make_noise_args(sc, denom, seed, layer, step);
   hipError_t e;
   if (pl.engine == 1)
     e = launch_contract_dl(st, A, G, c, B, Tn, d, p, pl, ws, na, out);

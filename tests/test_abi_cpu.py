@@ -210,26 +210,74 @@ def _r256(x):
     return (x + 255) // 256 * 256
 
 
+def _norm_need_ok(lib, arr, n, dt, B, mode, need):
+    """dp_ghost_norm_layers accepts a workspace of `need` bytes and refuses one
+    byte less (validation only: with no GPU the valid call reports no device)."""
+    paths = (ctypes.c_int32 * n)()
+    fn = lib.dp_ghost_norm_layers
+    if need > 0:
+        assert fn(None, arr, n, dt, B, mode, 1, FAKE, need - 1, FAKE, 0, paths) == dpc.DP_ERR_WORKSPACE
+    st = fn(None, arr, n, dt, B, mode, 1, FAKE if need else None, need, FAKE, 0, paths)
+    assert st in (dpc.DP_OK, dpc.DP_ERR_NO_DEVICE), st
+    assert lib.dp_layers_workspace_bytes(arr, n, dt, B, mode, 1) >= need
+
+
 def test_layers_workspace_follows_the_runs(lib):
     """Consecutive ghost layers of one tile size share a launch (at most 8)
     whose partials span all their tiles; other layers need their own."""
-    ws = lib.dp_layers_workspace_bytes
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("checks the no-device validation path")
     B = 64
     # four T = 128 layers: one launch, 3 Gram tiles per layer and sample
-    assert ws(_layers(GPT_BLOCK), 4, 1, B, 0, 1) == _r256(B * 12 * 4) + _r256(B * 8)
+    _norm_need_ok(lib, _layers(GPT_BLOCK), 4, 1, B, 0, _r256(B * 12 * 4) + _r256(B * 8))
     # nine layers: runs of 8 and 1
-    nine = _layers([GPT_BLOCK[0]] * 9)
-    assert ws(nine, 9, 1, B, 0, 1) == _r256(B * 24 * 4) + _r256(B * 8)
+    _norm_need_ok(lib, _layers([GPT_BLOCK[0]] * 9), 9, 1, B, 0, _r256(B * 24 * 4) + _r256(B * 8))
     # a T = 1 layer in between splits the run; it needs no workspace
     mixed = _layers([GPT_BLOCK[0], (1, 64, 32, 0), GPT_BLOCK[1]])
-    assert ws(mixed, 3, 1, B, 0, 1) == _r256(B * 3 * 4) + _r256(B * 8)
+    _norm_need_ok(lib, mixed, 3, 1, B, 0, _r256(B * 3 * 4) + _r256(B * 8))
     # one single-tile ghost layer: nothing
-    assert ws(_layers([(64, 32, 48, 0)]), 1, 0, 5, dpc.MODE_GHOST, 1) == 0
+    _norm_need_ok(lib, _layers([(64, 32, 48, 0)]), 1, 0, 5, dpc.MODE_GHOST, 0)
     # two single-tile ghost layers share a launch: two tiles per sample
     two = _layers([(64, 32, 48, 0), (40, 16, 16, 1)])
-    assert ws(two, 2, 0, 5, dpc.MODE_GHOST, 1) == _r256(5 * 2 * 4) + _r256(5 * 8)
-    # the long-sequence bf16 engine runs alone: its own tile count
-    long_ = _layers([(1024, 1280, 3840, 0)])
-    assert ws(long_, 1, 1, 32, 0, 1) > 0
-    assert ws(None, 1, 1, B, 0, 1) == 0
-    assert ws(_layers(GPT_BLOCK), 0, 1, B, 0, 1) == 0
+    _norm_need_ok(lib, two, 2, 0, 5, dpc.MODE_GHOST, _r256(5 * 2 * 4) + _r256(5 * 8))
+    # the long-sequence bf16 engine runs alone, with its own tile count
+    assert lib.dp_layers_workspace_bytes(_layers([(1024, 1280, 3840, 0)]), 1, 1, 32, 0, 1) > 0
+    assert lib.dp_layers_workspace_bytes(None, 1, 1, B, 0, 1) == 0
+    assert lib.dp_layers_workspace_bytes(_layers(GPT_BLOCK), 0, 1, B, 0, 1) == 0
+
+
+def test_clipped_sum_layers_validation(lib):
+    """The multi-layer clipped-sum call validates everything before any HIP
+    call; its workspace need is covered by dp_layers_workspace_bytes."""
+    fn = lib.dp_clipped_sum_noise_layers
+    n = len(GPT_BLOCK)
+    outs = (ctypes.c_void_p * n)(*([FAKE] * n))
+
+    def call(arr=None, n_=n, dt=1, B=64, c=FAKE, C=1.0, sigma=1.0, denom=64.0, ws=FAKE, wsb=1 << 34, o=outs,
+             b=None):
+        arr = _layers(GPT_BLOCK) if arr is None else arr
+        return fn(None, arr, n_, dt, B, c, C, sigma, denom, 0, None, 0, ws, wsb, o, b)
+
+    assert fn(None, None, n, 1, 64, FAKE, 1.0, 1.0, 64.0, 0, None, 0, FAKE, 1 << 34, outs, None) == dpc.DP_ERR_NULL
+    assert call(n_=0) == dpc.DP_ERR_SHAPE
+    assert call(c=None) == dpc.DP_ERR_NULL
+    assert call(o=None) == dpc.DP_ERR_NULL
+    assert call(o=(ctypes.c_void_p * n)(FAKE, None, FAKE, FAKE)) == dpc.DP_ERR_NULL
+    assert call(o=(ctypes.c_void_p * n)(FAKE, FAKE + 2, FAKE, FAKE)) == dpc.DP_ERR_ALIGN
+    assert call(C=0.0) == dpc.DP_ERR_VALUE
+    assert call(sigma=-1.0) == dpc.DP_ERR_VALUE
+    assert call(denom=float("nan")) == dpc.DP_ERR_VALUE
+    assert call(dt=4) == dpc.DP_ERR_DTYPE
+    assert call(arr=_layers(GPT_BLOCK, reserved=2)) == dpc.DP_ERR_VALUE
+    # a layer with a bias needs its bias output
+    biased = _layers(GPT_BLOCK[:3] + [(128, 3072, 768, 1)])
+    assert call(arr=biased) == dpc.DP_ERR_NULL
+    assert call(arr=biased, b=(ctypes.c_void_p * n)(None, None, None, None)) == dpc.DP_ERR_NULL
+    need = lib.dp_layers_workspace_bytes(_layers(GPT_BLOCK), n, 1, 64, 0, 1)
+    assert need > 0
+    assert call(ws=None) == dpc.DP_ERR_NULL
+    assert call(wsb=need // 2) == dpc.DP_ERR_WORKSPACE
+    import torch
+    if not torch.cuda.is_available():
+        assert call(wsb=need) == dpc.DP_ERR_NO_DEVICE

@@ -1,9 +1,12 @@
-"""Multi-layer norm call (dp_ghost_norm_layers) on the GPU.
+"""Multi-layer calls (dp_ghost_norm_layers, dp_clipped_sum_noise_layers) on the GPU.
 
-The call must give, bit for bit, what per-layer dp_ghost_norm calls with
+The norm call must give, bit for bit, what per-layer dp_ghost_norm calls with
 accumulate give (same fold order: each layer's tile partials in tile order,
 then the layers in call order), whether its layers share one launch or not;
 and the sum over layers must match the oracle's within the norm tolerance.
+The clipped-sum call must match the oracle per layer within the sum
+tolerance (its K splits may differ from a single-layer call's) and give the
+noise bit for bit.
 """
 from __future__ import annotations
 
@@ -136,3 +139,96 @@ def test_layers_repeated_calls_share_a_workspace():
             torch.cuda.synchronize()
             ref, _ = _sequential(devs, flags, dpc.MODE_GHOST)
             np.testing.assert_array_equal(sq.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+# ---------------------------------------------------------------- clipped sums of several layers
+from oracle import noise as N  # noqa: E402
+
+from gpu_util import assert_noised, f32  # noqa: E402
+
+
+def _sum_layers(devs, c_np, C, sigma, denom, seed, step, flags=None, layer_ids=None, workspace=None):
+    B = devs[0][0].shape[0]
+    flags = [False] * len(devs) if flags is None else flags
+    outs = [torch.empty(A.shape[2], G.shape[2], dtype=torch.float32, device=dev()) for (A, G) in devs]
+    bouts = [torch.empty(G.shape[2], dtype=torch.float32, device=dev()) if hb else None
+             for (A, G), hb in zip(devs, flags)]
+    dpc.dp_clipped_sum_noise_layers(devs, f32(c_np), C, sigma, denom, seed, step, outs,
+                                    bias_outs=bouts if any(flags) else None, has_bias=flags,
+                                    layer_ids=layer_ids, workspace=workspace)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in outs], [None if b is None else b.cpu().numpy() for b in bouts]
+
+
+def test_sum_layers_gpt_block_full_size():
+    """The four layers of a GPT block at full size (B = 64, T = 128) in one
+    call: sampled entries of every layer's clipped sum against the oracle,
+    and the noise, at c = 0, bit for bit over every entry."""
+    B, specs, dtype, _, _ = CASES["gpt-block"]
+    host, devs = _inputs(B, specs, dtype, seed=21)
+    rng = np.random.default_rng(4)
+    c_np = rng.uniform(0.0, 1.0, B).astype(np.float32)
+    c_np[[0, 17, 40]] = 0.0
+    c_np[5] = 1.0
+    C, denom, seed, step = 0.8, float(B), 12345, 3
+    outs, _ = _sum_layers(devs, c_np, C, 0.0, denom, seed, step)
+    for l, ((Ao, Go), out) in enumerate(zip(host, outs)):
+        d, p = out.shape
+        rows, cols = rng.integers(0, d, 128), rng.integers(0, p, 128)
+        S_or = D.clipped_sum_entries(Ao, Go, c_np.astype(np.float64), rows, cols)
+        assert_noised(out[rows, cols], S_or / denom, S_or, np.zeros(rows.size), dtype, denom, what=f"layer {l}")
+    zeros = np.zeros(B, dtype=np.float32)
+    outs, _ = _sum_layers(devs, zeros, C, 1.3, denom, seed, step, layer_ids=[7, 8, 9, 10])
+    for l, out in enumerate(outs):
+        d, p = out.shape
+        zw = N.weight_noise(d, p, seed, 7 + l, step)
+        np.testing.assert_array_equal(out, D.noised_mean_f32(np.zeros((d, p)), zw, C, 1.3, denom))
+
+
+SUM_CASES = {
+    # name: (B, specs, flags)
+    "mixed-engines": (6, [(128, 64, 96), (100, 40, 24), (64, 128, 64), (128, 96, 32), (192, 136, 200)],
+                      [False, False, False, True, False]),
+    "ten-layers": (5, [(64, 64 + 8 * k, 128 - 8 * k) for k in range(10)], [False] * 10),
+    # launches of 8 and 1: the last eligible layer takes the single-layer path
+    "nine-layers": (4, [(128, 64 + 16 * k, 64) for k in range(9)], [False] * 9),
+    "one-eligible": (7, [(100, 40, 24), (128, 136, 64)], [False, False]),
+}
+
+
+@pytest.mark.parametrize("name", list(SUM_CASES))
+def test_sum_layers_against_oracle_and_single_calls(name):
+    """Every layer of a mixed list (grouped engine, other engines, a bias)
+    against the oracle's full clipped noised mean, and against the
+    single-layer call within the same tolerance."""
+    B, specs, flags = SUM_CASES[name]
+    host, devs = _inputs(B, specs, "bf16", seed=33 + len(name))
+    c_np = np.linspace(0.05, 1.0, B).astype(np.float32)
+    c_np[1] = 0.0
+    C, sigma, denom, seed, step = 1.1, 0.0, 2.0 * B, 99, 6
+    outs, bouts = _sum_layers(devs, c_np, C, sigma, denom, seed, step, flags=flags)
+    for l, ((Ao, Go), (A, G), hb) in enumerate(zip(host, devs, flags)):
+        S_or, Sb = D.clipped_sum(Ao, Go, c_np.astype(np.float64), has_bias=hb)
+        assert_noised(outs[l], S_or / denom, S_or, np.zeros_like(S_or), "bf16", denom, what=f"layer {l}")
+        if hb:
+            assert_noised(bouts[l], Sb / denom, Sb, np.zeros_like(Sb), "bf16", denom, what=f"bias {l}")
+        one = torch.empty(A.shape[2], G.shape[2], dtype=torch.float32, device=dev())
+        bone = torch.empty(G.shape[2], dtype=torch.float32, device=dev()) if hb else None
+        dpc.dp_clipped_sum_noise(A, G, f32(c_np), C, sigma, denom, seed, l, step, one, bone)
+        torch.cuda.synchronize()
+        assert_noised(outs[l], one.cpu().numpy(), S_or, np.zeros_like(S_or), "bf16", denom, what=f"single {l}")
+
+
+def test_sum_layers_repeatable_bitwise():
+    """Two calls with the same inputs give the same bits, also when the
+    workspace holds another call's partials and counters in between."""
+    B, specs, _ = SUM_CASES["ten-layers"]
+    _, devs = _inputs(B, specs, "bf16", seed=8)
+    c_np = np.linspace(0.1, 0.9, B).astype(np.float32)
+    ws = torch.empty(dpc.dp_layers_workspace_bytes(devs) + 256, dtype=torch.uint8, device=dev())
+    a, _ = _sum_layers(devs, c_np, 1.0, 0.5, float(B), 5, 1, workspace=ws)
+    _, other = _inputs(B, specs[:3], "bf16", seed=9)
+    _sum_layers(other, c_np, 1.0, 0.5, float(B), 5, 1, workspace=ws)
+    b, _ = _sum_layers(devs, c_np, 1.0, 0.5, float(B), 5, 1, workspace=ws)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x.view(np.uint32), y.view(np.uint32))
