@@ -463,6 +463,15 @@ bool dl_eligible(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has
 // 32-row chunks through four stages and always writes partials.
 constexpr int kDlWideKC = 32, kDlWideStages = 4;
 
+// tiles the planner may choose (bit i: kTileBM/kTileBN[i])
+#ifndef DL_TILE_MASK
+#define DL_TILE_MASK 7
+#endif
+// bytes per second one CU reads back split partials at in the fix-up
+#ifndef DL_FIXUP_BW
+#define DL_FIXUP_BW 1.0e11
+#endif
+
 namespace {
 constexpr int kTiles = 3;
 const int kTileBM[kTiles] = {128, 256, 256}, kTileBN[kTiles] = {128, 128, 256};
@@ -475,7 +484,7 @@ const int kTileKC[kTiles] = {kDlKC, kDlKC, kDlWideKC};
 const double kTileEff[kTiles] = {0.30, 0.35, 0.47};
 const double kTileFixed[kTiles] = {6e-6, 8e-6, 13.5e-6};
 constexpr double kCuPeak = 2.5e15 / 256.0;
-constexpr double kFixupBytesPerS = 1.0e11;
+constexpr double kFixupBytesPerS = DL_FIXUP_BW;
 constexpr double kFixupFixed = 1.0e-6;
 constexpr int kCusPerXcd = 32;
 
@@ -545,6 +554,7 @@ DlGroupPlan dl_group_plan(const int64_t* B, const int64_t* Tn, const int64_t* d,
   best.n = 0;
   double best_t = 1e300;
   for (int ti = 0; ti < kTiles; ++ti) {
+    if (!((DL_TILE_MASK >> ti) & 1)) continue;
     int64_t prev_ks[kDlGroupMax] = {};
     for (int64_t target : targets) {
       LayerChoice ch[kDlGroupMax];
