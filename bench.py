@@ -87,7 +87,7 @@ DEVICE_GEN_BYTES = 8 << 30
 BREAKDOWN_STEPS = 50
 
 
-def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums=False):
+def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums=False, virtual_steps=1):
     """Times `steps` whole steps of the workload after `warmup` untimed ones.
 
     Global clipping (one norm per example over all layers): every layer's
@@ -175,6 +175,17 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
         # one workspace for the multi-layer calls (they run one after another on the stream)
         ws_layers = torch.empty(max(256, dpc.dp_layers_workspace_bytes(sets[0], has_bias=wl.has_bias)),
                                 dtype=torch.uint8, device=dev)
+        if virtual_steps > 1:
+            # a logical batch of `virtual_steps` physical batches: per physical batch the norms, the
+            # clip factors and each layer's clipped sum added to its accumulator; once per logical
+            # batch each layer's noise and mean
+            kinds = (norm_kinds + [("clip", -1)] + [("sum", l) for l in range(L)]) * virtual_steps + \
+                [("noise", l) for l in range(L)]
+            accs = [torch.empty(d, p, dtype=torch.float32, device=dev) for (T, d, p) in shapes]
+            baccs = [torch.empty(p, dtype=torch.float32, device=dev) if wl.has_bias else None
+                     for (T, d, p) in shapes]
+            ws_acc = [torch.empty(max(256, dpc.lib().dp_accumulate_workspace_bytes(
+                dt, B, T, d, p, int(wl.has_bias))), dtype=torch.uint8, device=dev) for (T, d, p) in shapes]
 
     ncalls = len(kinds)
     bsteps = min(steps, BREAKDOWN_STEPS)
@@ -208,6 +219,22 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
                 call(dpc.dp_adaptive_threshold, nrm[l], C_t[l], wl.alpha, wl.beta, wl.sigma_l2, False, wl.seed,
                      l, k + 1, C_next[l:l + 1])
             C_t = [float(v) for v in C_next.tolist()]
+            return
+        if virtual_steps > 1:
+            for v in range(virtual_steps):
+                layers = sets[(k * virtual_steps + v) % n_sets]
+                if per_layer_norms:
+                    for l, (A, G) in enumerate(layers):
+                        call(dpc.dp_ghost_norm, A, G, sq, has_bias=wl.has_bias, accumulate=l > 0, workspace=ws[l])
+                else:
+                    call(dpc.dp_ghost_norm_layers, layers, sq, has_bias=wl.has_bias, workspace=ws_layers)
+                call(dpc.dp_clip_factors, sq, wl.C, c)
+                for l, (A, G) in enumerate(layers):
+                    call(dpc.dp_clipped_sum_accumulate, A, G, c, accs[l], bias_acc=baccs[l], accumulate=v > 0,
+                         workspace=ws_acc[l])
+            for l in range(L):
+                call(dpc.dp_noise_mean, accs[l], wl.C, wl.sigma, float(B * virtual_steps), wl.seed, l, k, outs[l],
+                     bias_acc=baccs[l], bias_out=bouts[l])
             return
         if per_layer_norms:
             for l, (A, G) in enumerate(layers):
@@ -369,6 +396,9 @@ def main():
     ap.add_argument("--breakdown", action="store_true", help="print per-call times to stderr")
     ap.add_argument("--per-layer-norms", action="store_true",
                     help="global clipping: one dp_ghost_norm call per layer instead of one multi-layer call")
+    ap.add_argument("--virtual-steps", type=int, default=1,
+                    help="global clipping: each step is a logical batch of this many physical batches "
+                         "(gradient accumulation; noise and mean once per logical batch)")
     ap.add_argument("--per-layer-sums", action="store_true",
                     help="global clipping: one dp_clipped_sum_noise call per layer (on --streams side streams) "
                          "instead of one multi-layer call")
@@ -397,11 +427,17 @@ def main():
         nstreams = a.streams if a.streams is not None else (3 if wl.n_layers <= 8 else 1)
     else:
         nstreams = 1
+    if a.virtual_steps > 1 and wl.per_layer:
+        print("--virtual-steps applies to global clipping workloads", file=sys.stderr)
+        sys.exit(2)
+    if a.virtual_steps > 1:
+        per_layer_sums, nstreams = True, 1
     wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device = run_gpu(wl, a.steps, a.warmup, nstreams,
-                                                                      a.per_layer_norms, per_layer_sums)
+                                                                      a.per_layer_norms, per_layer_sums,
+                                                                      a.virtual_steps)
     L = len(shapes)
     ms_per_step = 1e3 * wall / a.steps
-    value = wl.B * a.steps / wall
+    value = wl.B * a.virtual_steps * a.steps / wall
 
     # dominant entry point by total event time: the norm calls or the clipped-sum calls
     mean_ms = call_ms.mean(axis=0)
@@ -452,6 +488,9 @@ def main():
            "norm_call": "per-layer" if (wl.per_layer or a.per_layer_norms or L == 1) else "multi-layer",
            "sum_call": ("per-layer" if (wl.per_layer or per_layer_sums) else "multi-layer"),
            "sum_streams": nstreams}
+    if a.virtual_steps > 1:
+        cfg["virtual_steps"] = a.virtual_steps
+        cfg["logical_batch"] = wl.B * a.virtual_steps
     if on_device:
         cfg["inputs"] = "drawn on the device (torch generator), distinct for every layer"
     line = {

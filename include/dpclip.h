@@ -225,6 +225,40 @@ dp_status dp_clipped_sum_noise_layers(void* stream, const dp_layer* layers, int3
                                       float* const* outs, float* const* bias_outs);
 
 /*
+ * Virtual step (gradient accumulation): a logical batch fed to the GPU as
+ * several physical batches, each back-propagated before one update (SEDP,
+ * Performance section: physical vs logical batch size; App. E, the virtual
+ * step). Each physical batch's samples are clipped with their own factors;
+ * the clipped sums add up over the logical batch and the noise and the mean
+ * are applied once, by dp_noise_mean.
+ *
+ * dp_clipped_sum_accumulate: acc[d][p] = (accumulate ? acc : 0) + sum_b c[b] A_b^T G_b
+ * (and bias_acc[p] with sum_b c[b] sum_t G_b[t] when bias_acc != NULL), in
+ * fp32: the physical batch's clipped sum as dp_clipped_sum_noise forms it,
+ * then one fp32 add per element. A, G, dtype, B, T, d, p, c as in
+ * dp_clipped_sum_noise; workspace of at least
+ * dp_accumulate_workspace_bytes(dtype, B, T, d, p, bias_acc != NULL) bytes
+ * (with accumulate == 0, dp_workspace_bytes(...) suffice).
+ */
+size_t dp_accumulate_workspace_bytes(dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64_t p, int32_t has_bias);
+dp_status dp_clipped_sum_accumulate(void* stream, const void* A, const void* G, dp_dtype dtype,
+                                    int64_t B, int64_t T, int64_t d, int64_t p, const float* c,
+                                    void* workspace, size_t ws_bytes, float* acc, float* bias_acc,
+                                    int32_t accumulate);
+
+/*
+ * dp_noise_mean: out[m][n] = (acc[m][n] + (sigma*C) * z_w[m][n]) * (1/denom),
+ * bias_out[n] likewise with z_b[n], the noise of dp_clipped_sum_noise
+ * (same seed, layer_id, step -> same z, bit for bit; same fp32 operation
+ * order). denom is the logical batch size for the plain mean. out may be acc
+ * and bias_out may be bias_acc (each element is read before it is written).
+ * bias_acc and bias_out are both NULL or both set.
+ */
+dp_status dp_noise_mean(void* stream, const float* acc, const float* bias_acc, int64_t d, int64_t p, float C,
+                        float sigma, float denom, uint64_t seed, uint32_t layer_id, uint32_t step,
+                        float* out, float* bias_out);
+
+/*
  * One update of the adaptive per-layer clipping bound of TTP:
  *
  *   C_l2   = init ? mean_b(norm[b]) : beta * C_prev

@@ -89,3 +89,25 @@ def adaptive_step(layers, C_t, sigma, alpha, beta, sigma_l2, seed, step, has_bia
         res["C_l2"].append(cl2)
         res["C_next"].append(cn)
     return res
+
+
+def virtual_step(batches, cs, C, sigma, seed, layer_id=0, step=0, has_bias=False):
+    """One layer's update over a logical batch fed as several physical batches
+    ([SEDP] Performance section: the physical batch is what is fed to the GPU
+    at one time, the logical batch what one update covers, with one
+    back-propagation per physical batch before the update; App. E, the virtual
+    step). Each physical batch's samples carry their own clip factors cs[k];
+    the clipped sums of the physical batches add up and the noise and the mean
+    over the logical batch (denom = its size) are applied once."""
+    acc = bacc = None
+    n = 0
+    for (A, G), c in zip(batches, cs):
+        S, Sb = D.clipped_sum(A, G, c, has_bias)
+        acc = S if acc is None else acc + S
+        if has_bias:
+            bacc = Sb if bacc is None else bacc + Sb
+        n += A.shape[0]
+    d, p = acc.shape
+    out = D.noised_mean(acc, N.weight_noise(d, p, seed, layer_id, step), C, sigma, n)
+    bout = D.noised_mean(bacc, N.normals(p, seed, layer_id, 1, step), C, sigma, n) if has_bias else None
+    return dict(sum=acc, bias_sum=bacc, out=out, bias_out=bout, denom=float(n))

@@ -14,6 +14,8 @@ The functions mirror the C ABI in ``include/dpclip.h``:
     dp_layers_workspace_bytes(layers, has_bias=False, mode=MODE_MIXED, kappa=1) -> int
     dp_clipped_sum_noise_layers(layers, c, C, sigma, denom, seed, step, outs,
                                 bias_outs=None, has_bias=False, layer_ids=None, workspace=None)
+    dp_clipped_sum_accumulate(A, G, c, acc, bias_acc=None, accumulate=False, workspace=None)
+    dp_noise_mean(acc, C, sigma, denom, seed, layer_id, step, out, bias_acc=None, bias_out=None)
     dp_clip_factors(sqnorm, C, c, norm=None)
     dp_clipped_sum_noise(A, G, c, C, sigma, denom, seed, layer_id, step, out,
                          bias_out=None, workspace=None)
@@ -41,7 +43,7 @@ MODE_MIXED, MODE_GHOST, MODE_EXPLICIT = 0, 1, 2
 PATH_GHOST, PATH_EXPLICIT, PATH_T1 = 1, 2, 3
 
 EXPORTS = ("dp_ghost_norm", "dp_ghost_norm_layers", "dp_layers_workspace_bytes", "dp_clipped_sum_noise_layers",
-           "dp_clip_factors", "dp_clipped_sum_noise", "dp_adaptive_threshold",
+           "dp_clip_factors", "dp_clipped_sum_accumulate", "dp_noise_mean", "dp_accumulate_workspace_bytes", "dp_clipped_sum_noise", "dp_adaptive_threshold",
            "dp_workspace_bytes", "dp_choose_path", "dp_status_string", "dp_abi_version")
 
 _lib = None
@@ -73,6 +75,13 @@ def _declare(lib):
                                                 ctypes.POINTER(c_u32), c_u32, vp, ctypes.c_size_t,
                                                 ctypes.POINTER(vp), ctypes.POINTER(vp)]
     lib.dp_clipped_sum_noise_layers.restype = c_i32
+    lib.dp_clipped_sum_accumulate.argtypes = [vp, vp, vp, c_i32, c_i64, c_i64, c_i64, c_i64, fp, vp, ctypes.c_size_t,
+                                              fp, fp, c_i32]
+    lib.dp_clipped_sum_accumulate.restype = c_i32
+    lib.dp_noise_mean.argtypes = [vp, fp, fp, c_i64, c_i64, f, f, f, c_u64, c_u32, c_u32, fp, fp]
+    lib.dp_noise_mean.restype = c_i32
+    lib.dp_accumulate_workspace_bytes.argtypes = [c_i32, c_i64, c_i64, c_i64, c_i64, c_i32]
+    lib.dp_accumulate_workspace_bytes.restype = ctypes.c_size_t
     lib.dp_layers_workspace_bytes.argtypes = [lp, c_i32, c_i32, c_i64, c_i32, c_i32]
     lib.dp_layers_workspace_bytes.restype = ctypes.c_size_t
     lib.dp_clip_factors.argtypes = [vp, fp, c_i64, f, fp, fp]
@@ -257,6 +266,47 @@ def dp_clipped_sum_noise_layers(layers, c, C: float, sigma: float, denom: float,
         _stream(stream), arr, n, dt, B, _ptr(c), float(C), float(sigma), float(denom),
         int(seed) & 0xFFFFFFFFFFFFFFFF, ids, int(step) & 0xFFFFFFFF, _ptr(workspace),
         workspace.numel() * workspace.element_size(), optr, bptr))
+
+
+def dp_clipped_sum_accumulate(A, G, c, acc, bias_acc=None, accumulate: bool = False, workspace=None, stream=None):
+    """acc (+)= the clipped sum of one physical batch (no noise, no mean)."""
+    import torch
+    dt, B, T, d, p = _layer(A, G)
+    _f32_vec(c, "c")
+    _f32_vec(acc, "acc")
+    if c.numel() != B or acc.numel() != d * p:
+        raise ValueError("c must have B elements and acc d*p")
+    if bias_acc is not None:
+        _f32_vec(bias_acc, "bias_acc")
+        if bias_acc.numel() != p:
+            raise ValueError("bias_acc must have p elements")
+    if workspace is None:
+        need = int(lib().dp_accumulate_workspace_bytes(dt, B, T, d, p, int(bias_acc is not None)))
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=A.device)
+    _check("dp_clipped_sum_accumulate", lib().dp_clipped_sum_accumulate(
+        _stream(stream), _ptr(A), _ptr(G), dt, B, T, d, p, _ptr(c), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(acc), _ptr(bias_acc), int(bool(accumulate))))
+
+
+def dp_noise_mean(acc, C: float, sigma: float, denom: float, seed: int, layer_id: int, step: int, out,
+                  bias_acc=None, bias_out=None, stream=None):
+    """out = (acc + sigma*C*z) / denom, the noise of dp_clipped_sum_noise; acc is [d, p]."""
+    _f32_vec(acc, "acc")
+    _f32_vec(out, "out")
+    if acc.dim() != 2 or out.shape != acc.shape:
+        raise ValueError("acc and out must be [d, p]")
+    d, p = int(acc.shape[0]), int(acc.shape[1])
+    if (bias_acc is None) != (bias_out is None):
+        raise ValueError("bias_acc and bias_out go together")
+    if bias_acc is not None:
+        _f32_vec(bias_acc, "bias_acc")
+        _f32_vec(bias_out, "bias_out")
+        if bias_acc.numel() != p or bias_out.numel() != p:
+            raise ValueError("bias vectors must have p elements")
+    _check("dp_noise_mean", lib().dp_noise_mean(
+        _stream(stream), _ptr(acc), _ptr(bias_acc), d, p, float(C), float(sigma), float(denom),
+        int(seed) & 0xFFFFFFFFFFFFFFFF, int(layer_id) & 0xFFFFFFFF, int(step) & 0xFFFFFFFF, _ptr(out),
+        _ptr(bias_out)))
 
 
 def dp_clip_factors(sqnorm, C: float, c, norm=None, stream=None):

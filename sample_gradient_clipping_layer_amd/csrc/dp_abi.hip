@@ -497,6 +497,63 @@ dp_status dp_clipped_sum_noise(void* stream, const void* A, const void* G, dp_dt
                                             denom, seed, layer_id, step, out, bias_out));
 }
 
+size_t dp_accumulate_workspace_bytes(dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64_t p, int32_t has_bias) {
+  if (check_shape(B, T, d, p) != DP_OK) return 0;
+  if (dtype != DP_F32 && dtype != DP_BF16) return 0;
+  const int hb = has_bias ? 1 : 0;
+  return round256(contract_ws_bytes(dtype, B, T, d, p, hb)) + round256((size_t)(d + hb) * (size_t)p * sizeof(float));
+}
+
+dp_status dp_clipped_sum_accumulate(void* stream, const void* A, const void* G, dp_dtype dtype, int64_t B, int64_t T,
+                                    int64_t d, int64_t p, const float* c, void* workspace, size_t ws_bytes,
+                                    float* acc, float* bias_acc, int32_t accumulate) {
+  dp_status s = check_layer(A, G, dtype, B, T, d, p);
+  if (s != DP_OK) return s;
+  if (!c || !acc) return DP_ERR_NULL;
+  if (!aligned(c, 4) || !aligned(acc, 4) || (bias_acc && !aligned(bias_acc, 4))) return DP_ERR_ALIGN;
+  const int hb = bias_acc ? 1 : 0;
+  const dpk::ContractPlan pl = dpk::contract_plan(dtype, B, T, d, p, hb);
+  if ((int64_t)pl.mt * pl.nt * pl.ks >= ((int64_t)1 << 31)) return DP_ERR_SHAPE;
+  const size_t cws = round256(contract_ws_for(pl, d, p, hb));
+  const size_t need = accumulate ? cws + round256((size_t)(d + hb) * (size_t)p * sizeof(float)) : cws;
+  if (need > 0) {
+    if (!workspace) return DP_ERR_NULL;
+    if (ws_bytes < need) return DP_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return DP_ERR_ALIGN;
+  }
+  s = device_ready();
+  if (s != DP_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* ws = static_cast<float*>(workspace);
+  // the physical batch's clipped sum, exactly: (S + 0*z) * 1 = S
+  if (!accumulate)
+    return hip_status(dpk::launch_clipped_sum(st, dtype, A, G, c, B, T, d, p, pl, ws, 0.0f, 1.0f, 0, 0, 0, acc,
+                                              bias_acc));
+  float* sum = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + cws);
+  float* bias_sum = hb ? sum + d * p : nullptr;
+  hipError_t e = dpk::launch_clipped_sum(st, dtype, A, G, c, B, T, d, p, pl, ws, 0.0f, 1.0f, 0, 0, 0, sum, bias_sum);
+  if (e == hipSuccess) e = dpk::launch_accumulate(st, acc, sum, d * p);
+  if (e == hipSuccess && hb) e = dpk::launch_accumulate(st, bias_acc, bias_sum, p);
+  return hip_status(e);
+}
+
+dp_status dp_noise_mean(void* stream, const float* acc, const float* bias_acc, int64_t d, int64_t p, float C,
+                        float sigma, float denom, uint64_t seed, uint32_t layer_id, uint32_t step, float* out,
+                        float* bias_out) {
+  if (!acc || !out) return DP_ERR_NULL;
+  if ((bias_acc != nullptr) != (bias_out != nullptr)) return DP_ERR_NULL;
+  if (check_shape(1, 1, d, p) != DP_OK) return DP_ERR_SHAPE;
+  if (!aligned(acc, 4) || !aligned(out, 4) || (bias_acc && (!aligned(bias_acc, 4) || !aligned(bias_out, 4))))
+    return DP_ERR_ALIGN;
+  if (!finite(C) || !(C > 0.0f) || !finite(sigma) || sigma < 0.0f || !finite(denom) || !(denom > 0.0f))
+    return DP_ERR_VALUE;
+  dp_status s = device_ready();
+  if (s != DP_OK) return s;
+  return hip_status(dpk::launch_noise_mean(static_cast<hipStream_t>(stream), acc, bias_acc, d, p,
+                                           dpk::make_noise_args(sigma * C, denom, seed, layer_id, step), out,
+                                           bias_out));
+}
+
 dp_status dp_adaptive_threshold(void* stream, const float* norm, int64_t B, float C_prev, float alpha, float beta,
                                 float sigma_l2, int32_t init, uint64_t seed, uint32_t layer_id, uint32_t step,
                                 float* C_next, float* C_l2_out) {

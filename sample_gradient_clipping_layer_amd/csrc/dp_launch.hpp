@@ -123,6 +123,10 @@ hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const vo
                               float denom, uint64_t seed, uint32_t layer, uint32_t step, float* out,
                               float* bias_out);
 hipError_t launch_clip_factors(hipStream_t st, const float* sqnorm, int64_t B, float C, float* c, float* norm);
+// Virtual step: acc += s (n floats); out = (acc + sc z) * inv_denom with the clipped sums' noise counters.
+hipError_t launch_accumulate(hipStream_t st, float* acc, const float* s, int64_t n);
+hipError_t launch_noise_mean(hipStream_t st, const float* acc, const float* bias_acc, int64_t d, int64_t p,
+                             const NoiseArgs& na, float* out, float* bias_out);
 hipError_t launch_adaptive_threshold(hipStream_t st, const float* norm, int64_t B, float C_prev, float alpha,
                                      float beta, float sigma_l2, int init, uint64_t seed, uint32_t layer,
                                      uint32_t step, float* C_next, float* C_l2_out);

@@ -61,6 +61,77 @@ __global__ __launch_bounds__(1024) void k_adaptive_threshold(const float* __rest
   }
 }
 
+// Virtual step ("Scalable and Efficient Training of Large CNNs with DP",
+// Performance section: several physical batches back-propagated before one
+// update; App. E, the virtual step): the clipped sums of the physical batches
+// add up in fp32, acc[i] = acc[i] + s[i], in batch order.
+__global__ __launch_bounds__(256) void k_accumulate(float* __restrict__ acc, const float* __restrict__ s, int64_t n,
+                                                    int vec) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (vec) {
+    if (4 * t + 3 < n) {
+      float4 a = reinterpret_cast<float4*>(acc)[t];
+      const float4 b = reinterpret_cast<const float4*>(s)[t];
+      a.x = a.x + b.x;
+      a.y = a.y + b.y;
+      a.z = a.z + b.z;
+      a.w = a.w + b.w;
+      reinterpret_cast<float4*>(acc)[t] = a;
+    } else {
+      for (int64_t i = 4 * t; i < n; ++i) acc[i] = acc[i] + s[i];
+    }
+  } else if (t < n) {
+    acc[t] = acc[t] + s[t];
+  }
+}
+
+// The noise and the mean of a logical batch, once: out = (acc + fl(sigma*C) z)
+// * fl(1/denom), z from the same counters as the clipped-sum kernels (weight
+// element (m, n): lane m % 4 of group (m/4)*p + n, word 2*layer; bias element
+// n: lane n % 4 of group n/4, word 2*layer + 1). One thread per Philox block
+// (4 rows of one column); reads its block before writing it, so out may be acc.
+__global__ __launch_bounds__(256) void k_noise_mean(const float* acc, const float* bias_acc, int64_t d, int64_t p,
+                                                    NoiseArgs na, float* out, float* bias_out) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nw = ((d + 3) / 4) * p;
+  if (t < nw) {
+    const int64_t q = t / p, n = t % p;
+    const f32x4 z = normals4((uint32_t)t, 2u * na.layer, na.step, 0u, na.k0, na.k1);
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * q + r < d) v[r] = acc[(4 * q + r) * p + n];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * q + r < d) out[(4 * q + r) * p + n] = noised_mean_spec(v[r], na.sc, z[r], na.inv_denom);
+  } else if (bias_acc && t < nw + (p + 3) / 4) {
+    const int64_t g = t - nw;
+    const f32x4 z = normals4((uint32_t)g, 2u * na.layer + 1u, na.step, 0u, na.k0, na.k1);
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * g + r < p) v[r] = bias_acc[4 * g + r];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * g + r < p) bias_out[4 * g + r] = noised_mean_spec(v[r], na.sc, z[r], na.inv_denom);
+  }
+}
+
+hipError_t launch_accumulate(hipStream_t st, float* acc, const float* s, int64_t n) {
+  const int vec = ((reinterpret_cast<uintptr_t>(acc) | reinterpret_cast<uintptr_t>(s)) & 15) == 0;
+  const int64_t threads = vec ? (n + 3) / 4 : n;
+  hipLaunchKernelGGL(k_accumulate, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, acc, s, n, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_noise_mean(hipStream_t st, const float* acc, const float* bias_acc, int64_t d, int64_t p,
+                             const NoiseArgs& na, float* out, float* bias_out) {
+  const int64_t threads = ((d + 3) / 4) * p + (bias_acc ? (p + 3) / 4 : 0);
+  hipLaunchKernelGGL(k_noise_mean, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, acc, bias_acc, d, p, na,
+                     out, bias_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_clip_factors(hipStream_t st, const float* sqnorm, int64_t B, float C, float* c, float* norm) {
   const dim3 grid((unsigned)((B + 255) / 256));
   hipLaunchKernelGGL(k_clip_factors, grid, dim3(256), 0, st, sqnorm, B, C, c, norm);

@@ -281,3 +281,45 @@ def test_clipped_sum_layers_validation(lib):
     import torch
     if not torch.cuda.is_available():
         assert call(wsb=need) == dpc.DP_ERR_NO_DEVICE
+
+
+def test_virtual_step_validation(lib):
+    """dp_clipped_sum_accumulate and dp_noise_mean validate before any HIP
+    call; accumulating needs room for the batch's sum in the workspace."""
+    acc_fn = lib.dp_clipped_sum_accumulate
+
+    def acc_call(A=FAKE, dt=1, B=4, T=64, d=128, p=64, c=FAKE, ws=FAKE, wsb=1 << 30, acc=FAKE, bacc=None, accum=1):
+        return acc_fn(None, A, FAKE, dt, B, T, d, p, c, ws, wsb, acc, bacc, accum)
+
+    assert acc_call(A=None) == dpc.DP_ERR_NULL
+    assert acc_call(c=None) == dpc.DP_ERR_NULL
+    assert acc_call(acc=None) == dpc.DP_ERR_NULL
+    assert acc_call(acc=FAKE + 2) == dpc.DP_ERR_ALIGN
+    assert acc_call(d=0) == dpc.DP_ERR_SHAPE
+    assert acc_call(dt=7) == dpc.DP_ERR_DTYPE
+    need = lib.dp_accumulate_workspace_bytes(1, 4, 64, 128, 64, 0)
+    plain = lib.dp_workspace_bytes(1, 4, 64, 128, 64, 0, 1)
+    assert need >= plain + 128 * 64 * 4
+    assert acc_call(wsb=need - 1) == dpc.DP_ERR_WORKSPACE
+    assert acc_call(ws=None) == dpc.DP_ERR_NULL
+    assert lib.dp_accumulate_workspace_bytes(1, 0, 64, 128, 64, 0) == 0
+    nm = lib.dp_noise_mean
+    f = ctypes.c_float
+
+    def nm_call(acc=FAKE, bacc=None, d=8, p=4, C=1.0, sigma=1.0, denom=4.0, out=FAKE, bout=None):
+        return nm(None, acc, bacc, d, p, f(C), f(sigma), f(denom), 0, 0, 0, out, bout)
+
+    assert nm_call(acc=None) == dpc.DP_ERR_NULL
+    assert nm_call(out=None) == dpc.DP_ERR_NULL
+    assert nm_call(bacc=FAKE) == dpc.DP_ERR_NULL          # bias in without bias out
+    assert nm_call(bout=FAKE) == dpc.DP_ERR_NULL
+    assert nm_call(d=0) == dpc.DP_ERR_SHAPE
+    assert nm_call(d=1 << 20, p=1 << 15) == dpc.DP_ERR_SHAPE  # noise counters beyond 32 bits
+    assert nm_call(C=0.0) == dpc.DP_ERR_VALUE
+    assert nm_call(sigma=-1.0) == dpc.DP_ERR_VALUE
+    assert nm_call(denom=0.0) == dpc.DP_ERR_VALUE
+    assert nm_call(out=FAKE + 1) == dpc.DP_ERR_ALIGN
+    import torch
+    if not torch.cuda.is_available():
+        assert nm_call() == dpc.DP_ERR_NO_DEVICE
+        assert acc_call(wsb=need) == dpc.DP_ERR_NO_DEVICE

@@ -213,6 +213,41 @@ def test_global_step_without_noise_or_clipping_is_mean_gradient():
     assert np.all(r["c"] == 1.0)
 
 
+def test_virtual_step_is_accumulated_reweighted_backprop():
+    """[SEDP] gradient accumulation: back-propagating each physical batch's
+    re-weighted loss sum_i c_i L_i into the same .grad before one update gives
+    the logical batch's clipped sum; divided by the logical batch size it is
+    the virtual step's update (sigma = 0). Catches a batch dropped or counted
+    twice, factors applied to the wrong batch, or the mean taken per physical
+    batch instead of over the logical one."""
+    rng = np.random.default_rng(17)
+    T, d, h, p = 3, 5, 4, 3
+    W1, b1, W2, b2 = _two_layer_net(rng, d, h, p)
+    Wg = [w.detach().clone().requires_grad_(True) for w in (W1, b1, W2, b2)]
+    batches, cs = [], []
+    for B in (3, 2, 4):
+        x = torch.tensor(rng.standard_normal((B, T, d)))
+        y = torch.tensor(rng.standard_normal((B, T, p)))
+        c = rng.uniform(0.1, 1.0, B)
+        losses, s1, _, _ = _per_example_losses(x, y, *Wg)
+        s1.retain_grad()
+        (torch.tensor(c) * losses).sum().backward()  # accumulates into Wg[k].grad
+        # layer-1 output gradients of the unweighted per-example losses
+        l2, s1u, _, _ = _per_example_losses(x, y, W1, b1, W2, b2)
+        s1u.retain_grad()
+        l2.sum().backward()
+        batches.append((x.numpy(), s1u.grad.numpy()))
+        cs.append(c)
+    r = drivers.virtual_step(batches, cs, C=1.0, sigma=0.0, seed=3, has_bias=True)
+    assert r["denom"] == 9.0
+    np.testing.assert_allclose(r["out"], Wg[0].grad.numpy().T / 9.0, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(r["bias_out"], Wg[1].grad.numpy() / 9.0, rtol=1e-11, atol=1e-13)
+    # the noise is drawn once, from the logical step's counters
+    rn = drivers.virtual_step(batches, cs, C=1.5, sigma=0.5, seed=3, layer_id=2, step=4, has_bias=True)
+    z = N.weight_noise(d, h, 3, 2, 4).astype(np.float64)
+    np.testing.assert_allclose(rn["out"] - r["out"], 1.5 * 0.5 * z / 9.0, rtol=1e-12, atol=1e-15)
+
+
 # ---------------------------------------------------------------- P6: noise
 def _kat_rows():
     rows = []
