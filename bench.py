@@ -65,7 +65,11 @@ def measured_traffic(kind, workload):
     return float(fields["traffic_bytes_per_call"])
 
 
-def _algorithmic(wl, T, d, p, kind):
+# norm path rules: the C ABI's DP_MODE_MIXED (space, kappa = 1) and DP_MODE_TIME
+MODES = {"space": 0, "time": 3}
+
+
+def _algorithmic(wl, T, d, p, kind, mode=0):
     """Algorithmic flops and bytes of one call on one layer (no re-reads, no
     intermediate buffers). ghost: unique Gram entries B*T(T+1)(d+p) + 2BT^2;
     explicit: 2BTdp + 2Bdp; T = 1: 2B(d+p); contraction: 2BTdp."""
@@ -76,7 +80,8 @@ def _algorithmic(wl, T, d, p, kind):
     if kind == "norm":
         if T == 1:
             return 2.0 * B * (d + p), inp + 4 * B
-        if p * d < T * T:
+        import sample_gradient_clipping_layer_amd as dpc
+        if dpc.dp_choose_path(T, d, p, mode) == dpc.PATH_EXPLICIT:
             return 2.0 * B * T * d * p + 2.0 * B * d * p, inp + 4 * B
         return float(B) * T * (T + 1) * (d + p) + 2.0 * B * T * T, inp + 4 * B
     flops = 2.0 * B * T * (d + hb) * p
@@ -87,7 +92,8 @@ DEVICE_GEN_BYTES = 8 << 30
 BREAKDOWN_STEPS = 50
 
 
-def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums=False, virtual_steps=1):
+def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums=False, virtual_steps=1,
+            mode=0):
     """Times `steps` whole steps of the workload after `warmup` untimed ones.
 
     Global clipping (one norm per example over all layers): every layer's
@@ -137,7 +143,7 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
     # one workspace per distinct shape (calls on one stream run one at a time)
     ws_by_shape = {}
     for sh in set(shapes):
-        nbytes = dpc.dp_workspace_bytes(dt, B, *sh)
+        nbytes = dpc.dp_workspace_bytes(dt, B, *sh, mode=mode)
         ws_by_shape[sh] = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     ws = [ws_by_shape[sh] for sh in shapes]
     outs = [torch.empty(d, p, dtype=torch.float32, device=dev) for (T, d, p) in shapes]
@@ -157,7 +163,7 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
         C_next = torch.empty(L, dtype=torch.float32, device=dev)
         # initial bounds: one adaptive-threshold init call per layer on the first input set
         for l, (A, G) in enumerate(sets[0]):
-            dpc.dp_ghost_norm(A, G, sq[l], has_bias=wl.has_bias, workspace=ws[l])
+            dpc.dp_ghost_norm(A, G, sq[l], has_bias=wl.has_bias, mode=mode, workspace=ws[l])
             dpc.dp_clip_factors(sq[l], 3.0e38, c[l], nrm[l])
             dpc.dp_adaptive_threshold(nrm[l], 1.0, wl.alpha, wl.beta, wl.sigma_l2, True, wl.seed, l, 0,
                                       C_next[l:l + 1])
@@ -173,7 +179,7 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
         sum_kinds = [("sum", l) for l in range(L)] if per_layer_sums else [("sum", -1)]
         kinds = norm_kinds + [("clip", -1)] + sum_kinds
         # one workspace for the multi-layer calls (they run one after another on the stream)
-        ws_layers = torch.empty(max(256, dpc.dp_layers_workspace_bytes(sets[0], has_bias=wl.has_bias)),
+        ws_layers = torch.empty(max(256, dpc.dp_layers_workspace_bytes(sets[0], has_bias=wl.has_bias, mode=mode)),
                                 dtype=torch.uint8, device=dev)
         if virtual_steps > 1:
             # a logical batch of `virtual_steps` physical batches: per physical batch the norms, the
@@ -212,7 +218,7 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
 
         if wl.per_layer:
             for l, (A, G) in enumerate(layers):
-                call(dpc.dp_ghost_norm, A, G, sq[l], has_bias=wl.has_bias, workspace=ws[l])
+                call(dpc.dp_ghost_norm, A, G, sq[l], has_bias=wl.has_bias, mode=mode, workspace=ws[l])
                 call(dpc.dp_clip_factors, sq[l], C_t[l], c[l], nrm[l])
                 call(dpc.dp_clipped_sum_noise, A, G, c[l], C_t[l], wl.sigma, float(B), wl.seed, l, k, outs[l],
                      bouts[l], workspace=ws[l])
@@ -225,9 +231,9 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
                 layers = sets[(k * virtual_steps + v) % n_sets]
                 if per_layer_norms:
                     for l, (A, G) in enumerate(layers):
-                        call(dpc.dp_ghost_norm, A, G, sq, has_bias=wl.has_bias, accumulate=l > 0, workspace=ws[l])
+                        call(dpc.dp_ghost_norm, A, G, sq, has_bias=wl.has_bias, mode=mode, accumulate=l > 0, workspace=ws[l])
                 else:
-                    call(dpc.dp_ghost_norm_layers, layers, sq, has_bias=wl.has_bias, workspace=ws_layers)
+                    call(dpc.dp_ghost_norm_layers, layers, sq, has_bias=wl.has_bias, mode=mode, workspace=ws_layers)
                 call(dpc.dp_clip_factors, sq, wl.C, c)
                 for l, (A, G) in enumerate(layers):
                     call(dpc.dp_clipped_sum_accumulate, A, G, c, accs[l], bias_acc=baccs[l], accumulate=v > 0,
@@ -238,9 +244,9 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
             return
         if per_layer_norms:
             for l, (A, G) in enumerate(layers):
-                call(dpc.dp_ghost_norm, A, G, sq, has_bias=wl.has_bias, accumulate=l > 0, workspace=ws[l])
+                call(dpc.dp_ghost_norm, A, G, sq, has_bias=wl.has_bias, mode=mode, accumulate=l > 0, workspace=ws[l])
         else:
-            call(dpc.dp_ghost_norm_layers, layers, sq, has_bias=wl.has_bias, workspace=ws_layers)
+            call(dpc.dp_ghost_norm_layers, layers, sq, has_bias=wl.has_bias, mode=mode, workspace=ws_layers)
         if not per_layer_sums:
             call(dpc.dp_clip_factors, sq, wl.C, c)
             call(dpc.dp_clipped_sum_noise_layers, layers, c, wl.C, wl.sigma, float(B), wl.seed, k, outs,
@@ -396,6 +402,9 @@ def main():
     ap.add_argument("--breakdown", action="store_true", help="print per-call times to stderr")
     ap.add_argument("--per-layer-norms", action="store_true",
                     help="global clipping: one dp_ghost_norm call per layer instead of one multi-layer call")
+    ap.add_argument("--path-rule", choices=("space", "time"), default="space",
+                    help="norm path per layer: the space rule p*d < T^2 (default) or the time rule "
+                         "(DP_MODE_TIME: the smaller per-sample matrix-core work)")
     ap.add_argument("--virtual-steps", type=int, default=1,
                     help="global clipping: each step is a logical batch of this many physical batches "
                          "(gradient accumulation; noise and mean once per logical batch)")
@@ -434,7 +443,7 @@ def main():
         per_layer_sums, nstreams = True, 1
     wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device = run_gpu(wl, a.steps, a.warmup, nstreams,
                                                                       a.per_layer_norms, per_layer_sums,
-                                                                      a.virtual_steps)
+                                                                      a.virtual_steps, MODES[a.path_rule])
     L = len(shapes)
     ms_per_step = 1e3 * wall / a.steps
     value = wl.B * a.virtual_steps * a.steps / wall
@@ -452,7 +461,7 @@ def main():
             continue
         for ll in (range(L) if l < 0 else (l,)):  # l < 0: one call over all layers
             T, d, p = shapes[ll]
-            f, b = _algorithmic(wl, T, d, p, kd)
+            f, b = _algorithmic(wl, T, d, p, kd, MODES[a.path_rule])
             flops += f
             byts += b
         t_ms += mean_ms[j]
@@ -487,7 +496,7 @@ def main():
            "clipping": "per-layer adaptive" if wl.per_layer else "global",
            "norm_call": "per-layer" if (wl.per_layer or a.per_layer_norms or L == 1) else "multi-layer",
            "sum_call": ("per-layer" if (wl.per_layer or per_layer_sums) else "multi-layer"),
-           "sum_streams": nstreams}
+           "sum_streams": nstreams, "path_rule": a.path_rule}
     if a.virtual_steps > 1:
         cfg["virtual_steps"] = a.virtual_steps
         cfg["logical_batch"] = wl.B * a.virtual_steps

@@ -60,6 +60,9 @@ typedef int32_t dp_mode;
 #define DP_MODE_MIXED 0    /* layerwise decision (SEDP Sec. 4, rule (4.1)) */
 #define DP_MODE_GHOST 1    /* always the ghost norm (SEDP 'ghost' mode, App. E) */
 #define DP_MODE_EXPLICIT 2 /* always per-sample instantiation */
+#define DP_MODE_TIME 3     /* layerwise decision by matrix-core work per sample: explicit when
+                              2*T*d*p + 2*d*p < T*(T+1)*(d+p) + 2*T*T (SEDP App. C costs, the
+                              ghost Grams' unique entries), else ghost; kappa is not used */
 
 #define DP_PATH_GHOST 1    /* <A_i A_i^T, G_i G_i^T> on per-sample Gram tiles */
 #define DP_PATH_EXPLICIT 2 /* ||A_i^T G_i||_F^2 from per-sample gradient tiles */
@@ -78,8 +81,9 @@ typedef int32_t dp_mode;
  *  G        [B, T, p] output gradients dL/ds_i (for a conv: F^-1, spatial flattened).
  *  dtype    DP_F32 or DP_BF16 (both tensors); accumulation is fp32.
  *  mode     DP_MODE_*; kappa >= 1: MIXED takes the explicit path when
- *           p*d < kappa*T*T, else ghost (tie -> ghost); T == 1 takes the
- *           closed form unless mode is EXPLICIT.
+ *           p*d < kappa*T*T, else ghost (tie -> ghost); TIME compares the
+ *           per-sample work of both paths; T == 1 takes the closed form
+ *           unless mode is EXPLICIT.
  *  workspace, ws_bytes  device scratch of at least dp_workspace_bytes(...)
  *           bytes (may be NULL when that is 0). Its contents on entry are
  *           ignored and on return undefined: per-sample arrival counters kept

@@ -39,6 +39,7 @@ PATH_T1 = 3
 MODE_MIXED = 0
 MODE_GHOST = 1
 MODE_EXPLICIT = 2
+MODE_TIME = 3
 
 
 def per_example_weight_grad(A_i: np.ndarray, G_i: np.ndarray) -> np.ndarray:
@@ -92,6 +93,13 @@ def choose_path(T: int, d: int, p: int, mode: int = MODE_MIXED, kappa: int = 1) 
     reproduces the 2T^2-vs-pD comparison; a tie goes to ghost. T = 1 uses the
     closed form of the ghost norm (a 1x1 Gram). mode GHOST/EXPLICIT forces
     the path ([SEDP] Appendix E: 'ghost' and 'ghost-mixed' modes).
+
+    mode TIME decides by time instead of space: per sample, the matrix-core
+    work of instantiation, 2Tdp + 2dp ([SEDP] Appendix C: the per-sample
+    gradient product and its squared norm), against that of the ghost norm
+    with its Grams' unique entries, T(T+1)(d+p) + 2T^2 (both Grams' s <= t
+    entries, then the Frobenius product); explicit when strictly smaller,
+    a tie goes to ghost.
     """
     if mode == MODE_EXPLICIT:
         return PATH_EXPLICIT
@@ -99,6 +107,10 @@ def choose_path(T: int, d: int, p: int, mode: int = MODE_MIXED, kappa: int = 1) 
         return PATH_T1
     if mode == MODE_GHOST:
         return PATH_GHOST
+    if mode == MODE_TIME:
+        explicit = 2 * T * d * p + 2 * d * p
+        ghost = T * (T + 1) * (d + p) + 2 * T * T
+        return PATH_EXPLICIT if explicit < ghost else PATH_GHOST
     return PATH_EXPLICIT if p * d < kappa * T * T else PATH_GHOST
 
 

@@ -39,7 +39,7 @@ DP_OK = 0
 DP_ERR_NULL, DP_ERR_SHAPE, DP_ERR_DTYPE, DP_ERR_VALUE = 1, 2, 3, 4
 DP_ERR_WORKSPACE, DP_ERR_HIP, DP_ERR_NO_DEVICE, DP_ERR_ALIGN = 5, 6, 7, 8
 DP_F32, DP_BF16 = 0, 1
-MODE_MIXED, MODE_GHOST, MODE_EXPLICIT = 0, 1, 2
+MODE_MIXED, MODE_GHOST, MODE_EXPLICIT, MODE_TIME = 0, 1, 2, 3
 PATH_GHOST, PATH_EXPLICIT, PATH_T1 = 1, 2, 3
 
 EXPORTS = ("dp_ghost_norm", "dp_ghost_norm_layers", "dp_layers_workspace_bytes", "dp_clipped_sum_noise_layers",

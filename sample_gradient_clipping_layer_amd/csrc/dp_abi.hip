@@ -48,6 +48,13 @@ int path_of(int64_t T, int64_t d, int64_t p, dp_mode mode, int32_t kappa) {
   if (mode == DP_MODE_EXPLICIT) return DP_PATH_EXPLICIT;
   if (T == 1) return DP_PATH_T1;
   if (mode == DP_MODE_GHOST) return DP_PATH_GHOST;
+  if (mode == DP_MODE_TIME) {
+    // per-sample matrix-core work: instantiation 2Tdp + 2dp, ghost T(T+1)(d+p) + 2T^2 (long double: exact here)
+    const long double Tl = (long double)T, dl = (long double)d, pl = (long double)p;
+    const long double expl = 2.0L * Tl * dl * pl + 2.0L * dl * pl;
+    const long double ghost = Tl * (Tl + 1.0L) * (dl + pl) + 2.0L * Tl * Tl;
+    return expl < ghost ? DP_PATH_EXPLICIT : DP_PATH_GHOST;
+  }
   // p*d < kappa*T^2 -> instantiate; compared in long double to stay exact for large sizes
   const long double pd = (long double)p * (long double)d;
   const long double t2 = (long double)kappa * (long double)T * (long double)T;
@@ -136,7 +143,7 @@ dp_status check_norm_layers(const dp_layer* layers, int32_t n, dp_dtype dtype, i
                             int32_t kappa) {
   const dp_status s = check_layer_list(layers, n, dtype, B);
   if (s != DP_OK) return s;
-  if (mode < DP_MODE_MIXED || mode > DP_MODE_EXPLICIT || kappa < 1) return DP_ERR_VALUE;
+  if (mode < DP_MODE_MIXED || mode > DP_MODE_TIME || kappa < 1) return DP_ERR_VALUE;
   for (int32_t l = 0; l < n; ++l) {
     const dp_layer& x = layers[l];
     const int path = path_of(x.T, x.d, x.p, mode, kappa);
@@ -276,14 +283,14 @@ const char* dp_status_string(dp_status status) {
 }
 
 int32_t dp_choose_path(int64_t T, int64_t d, int64_t p, dp_mode mode, int32_t kappa) {
-  if (T < 1 || d < 1 || p < 1 || mode < DP_MODE_MIXED || mode > DP_MODE_EXPLICIT || kappa < 1) return -1;
+  if (T < 1 || d < 1 || p < 1 || mode < DP_MODE_MIXED || mode > DP_MODE_TIME || kappa < 1) return -1;
   return path_of(T, d, p, mode, kappa);
 }
 
 size_t dp_workspace_bytes(dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64_t p, dp_mode mode, int32_t kappa) {
   if (check_shape(B, T, d, p) != DP_OK) return 0;
   if (dtype != DP_F32 && dtype != DP_BF16) return 0;
-  if (mode < DP_MODE_MIXED || mode > DP_MODE_EXPLICIT || kappa < 1) return 0;
+  if (mode < DP_MODE_MIXED || mode > DP_MODE_TIME || kappa < 1) return 0;
   const int path = path_of(T, d, p, mode, kappa);
   size_t w = 0;
   for (int hb = 0; hb <= 1; ++hb) {
@@ -302,7 +309,7 @@ dp_status dp_ghost_norm(void* stream, const void* A, const void* G, dp_dtype dty
   if (s != DP_OK) return s;
   if (!sqnorm) return DP_ERR_NULL;
   if (!aligned(sqnorm, 4)) return DP_ERR_ALIGN;
-  if (mode < DP_MODE_MIXED || mode > DP_MODE_EXPLICIT || kappa < 1) return DP_ERR_VALUE;
+  if (mode < DP_MODE_MIXED || mode > DP_MODE_TIME || kappa < 1) return DP_ERR_VALUE;
   const int hb = has_bias ? 1 : 0;
   const int path = path_of(T, d, p, mode, kappa);
   const size_t need = norm_ws_bytes(dtype, path, B, T, d, p, hb);

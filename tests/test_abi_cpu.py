@@ -63,7 +63,7 @@ def test_ghost_norm_validation(lib):
     assert _ghost(lib, B=1 << 30, T=1 << 12, d=1 << 12)[0] == dpc.DP_ERR_SHAPE   # element count overflow
     assert _ghost(lib, dt=2)[0] == dpc.DP_ERR_DTYPE
     assert _ghost(lib, A=FAKE_MIS)[0] == dpc.DP_ERR_ALIGN
-    assert _ghost(lib, mode=3)[0] == dpc.DP_ERR_VALUE
+    assert _ghost(lib, mode=4)[0] == dpc.DP_ERR_VALUE
     assert _ghost(lib, kappa=0)[0] == dpc.DP_ERR_VALUE
     # T = 100 spans 3 Gram tiles per sample: partials + arrival counters in the workspace
     assert _ghost(lib, ws=None, T=100, mode=dpc.MODE_GHOST)[0] == dpc.DP_ERR_NULL
@@ -129,6 +129,15 @@ def test_workspace_and_path_helpers(lib):
     assert lib.dp_choose_path(4, 2, 8, 0, 1) == dpc.PATH_GHOST
     assert lib.dp_choose_path(1, 2, 8, 2, 1) == dpc.PATH_EXPLICIT
     assert lib.dp_choose_path(0, 2, 8, 0, 1) == -1
+    assert lib.dp_choose_path(4, 2, 8, 4, 1) == -1
+    # the time rule: explicit on the conv layers whose per-sample product is the smaller work
+    conv = [(1024, 27, 64), (1024, 576, 64), (256, 576, 128), (256, 1152, 128), (64, 1152, 256),
+            (64, 2304, 256), (16, 2304, 512), (16, 4608, 512)]
+    assert [lib.dp_choose_path(T, d, p, dpc.MODE_TIME, 1) for (T, d, p) in conv] == \
+        [dpc.PATH_EXPLICIT] * 4 + [dpc.PATH_GHOST] * 4
+    for (T, d, p) in [(128, 768, 2304), (128, 768, 768), (1024, 1280, 1280), (1024, 5120, 1280)]:
+        assert lib.dp_choose_path(T, d, p, dpc.MODE_TIME, 1) == dpc.PATH_GHOST
+    assert lib.dp_choose_path(1, 64, 32, dpc.MODE_TIME, 1) == dpc.PATH_T1
 
 
 def test_path_rule_agrees_with_oracle(lib):
@@ -139,7 +148,7 @@ def test_path_rule_agrees_with_oracle(lib):
     for name in W.WORKLOAD_ORDER:
         wl = W.WORKLOADS[name]
         for (T, d, p) in wl.layers:
-            for mode in (0, 1, 2):
+            for mode in (0, 1, 2, 3):
                 for kappa in (1, 2):
                     assert lib.dp_choose_path(T, d, p, mode, kappa) == D.choose_path(T, d, p, mode, kappa)
 

@@ -232,3 +232,23 @@ def test_sum_layers_repeatable_bitwise():
     b, _ = _sum_layers(devs, c_np, 1.0, 0.5, float(B), 5, 1, workspace=ws)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+def test_time_rule_on_conv_layers():
+    """The time rule (DP_MODE_TIME) on the conv layer set (B = 5): the paths
+    the oracle's rule picks (explicit on the four early layers), and the norm
+    summed over layers against the oracle's."""
+    wl = W.WORKLOADS["resnet18-conv-t1024"]
+    host, devs = [], []
+    for l in range(wl.n_layers):
+        A, G = W.make_layer(wl, l, B=5)
+        host.append((W.as_f64(A, wl.dtype), W.as_f64(G, wl.dtype)))
+        devs.append((upload(A, wl.dtype), upload(G, wl.dtype)))
+    flags = [False] * wl.n_layers
+    grp, paths = _grouped(devs, flags, dpc.MODE_TIME)
+    want = [D.choose_path(*wl.layer_shape(l), D.MODE_TIME) for l in range(wl.n_layers)]
+    assert paths == want
+    assert paths[:4] == [dpc.PATH_EXPLICIT] * 4 and paths[4:] == [dpc.PATH_GHOST] * 4
+    seq, _ = _sequential(devs, flags, dpc.MODE_TIME)
+    np.testing.assert_array_equal(grp.view(np.uint32), seq.view(np.uint32))
+    assert_norms(np.sqrt(grp), np.sqrt(_oracle(host, flags)), wl.dtype)

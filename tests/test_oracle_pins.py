@@ -374,6 +374,29 @@ def test_adaptive_chain_driver():
 
 
 # ---------------------------------------------------------------- P8: path rule
+def test_time_rule_counts_the_work_of_each_path():
+    """The time rule's per-sample work figures, counted by brute force: the
+    instantiated product A_i^T G_i (d*p entries of T multiply-adds) and its
+    squared norm (d*p multiply-adds); the ghost Grams' unique entries (s <= t,
+    d multiply-adds for A's and p for G's) and the Frobenius product over all
+    T^2 entries ([SEDP] Appendix C). Catches a dropped term or a factor of 2."""
+    def explicit_flops(T, d, p):
+        macs = sum(T for _ in range(d) for _ in range(p)) + d * p
+        return 2 * macs
+
+    def ghost_flops(T, d, p):
+        macs = sum(d + p for s_ in range(T) for t_ in range(s_, T)) + T * T
+        return 2 * macs
+
+    for (T, d, p) in [(2, 3, 5), (7, 4, 4), (16, 3, 9), (9, 40, 2), (30, 5, 6)]:
+        e, g = explicit_flops(T, d, p), ghost_flops(T, d, p)
+        want = D.PATH_EXPLICIT if e < g else D.PATH_GHOST
+        assert D.choose_path(T, d, p, D.MODE_TIME) == want, (T, d, p, e, g)
+    # both outcomes occur among these shapes
+    assert {D.choose_path(T, d, p, D.MODE_TIME) for (T, d, p) in [(2, 3, 5), (30, 5, 6)]} == \
+        {D.PATH_EXPLICIT, D.PATH_GHOST}
+
+
 def test_path_rule_matches_the_pages_layer_pattern():
     """[SEDP] Sec. 4.2: in ResNets the early layers (large H*W, few channels)
     favour instantiation and the late layers (small H*W, many channels) the
