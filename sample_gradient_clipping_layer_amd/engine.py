@@ -1,0 +1,148 @@
+"""Privacy engine front end: per-sample clipping and Gaussian noise for the
+Linear and Conv2d layers of a torch model, through the C ABI.
+
+"Scalable and Efficient Training of Large CNNs with DP", App. E (the privacy
+engine with its 'ghost' and 'ghost-mixed' modes) and Sec. 3 (ghost norm, then
+the weighted gradient instead of per-sample gradients): hooks keep each
+layer's input a and output gradient dL/ds during one ordinary forward and
+backward pass of the summed per-sample loss; step() then runs the library's
+path over all layers -- the per-sample norm over every layer, the clip
+factors, and each layer's clipped noised mean -- and writes the results into
+the parameters' .grad. A convolution's input is unfolded first (U(a) of the
+same page, Sec. 2.2: D = C_in * kH * kW features per output position), in
+torch, on the GPU.
+
+Only argument marshalling and layout changes happen here; every step of the
+clipping path runs in libdpclip.
+"""
+from __future__ import annotations
+
+import torch
+import torch.nn.functional as F
+
+from . import (MODE_EXPLICIT, MODE_GHOST, MODE_MIXED, MODE_TIME, dp_clip_factors, dp_clipped_sum_noise_layers,
+               dp_ghost_norm_layers, dp_layers_workspace_bytes)
+
+MODES = {"ghost-mixed": MODE_MIXED, "ghost": MODE_GHOST, "explicit": MODE_EXPLICIT, "time": MODE_TIME}
+
+
+class _Layer:
+    def __init__(self, module: torch.nn.Module):
+        self.module = module
+        self.a = None   # the module's input of the last forward pass
+        self.g = None   # dL/d(output) of the last backward pass
+
+
+class PrivacyEngine:
+    """Flat (global) per-sample clipping at bound C with noise multiplier
+    sigma for every nn.Linear and nn.Conv2d (groups = 1) with trainable
+    parameters in `model`.
+
+    Usage, per step:
+        out = model(x)                       # hooks keep the layer inputs
+        per_sample_loss(out, y).sum().backward()   # hooks keep dL/ds
+        engine.step(step_index)              # .grad = (sum_i c_i g_i + N(0, s^2 C^2 I)) / B
+
+    The backward pass must be of the SUM of the per-sample losses, so that the
+    kept output gradients are the per-sample ones. A module may run once per
+    forward pass. Any other trainable parameter makes the constructor fail:
+    its per-sample gradient would go unclipped.
+    """
+
+    def __init__(self, model: torch.nn.Module, C: float, sigma: float, seed: int = 0, mode: str = "ghost-mixed",
+                 kappa: int = 1):
+        if mode not in MODES:
+            raise ValueError(f"mode must be one of {sorted(MODES)}")
+        self.C, self.sigma, self.seed = float(C), float(sigma), int(seed)
+        self.mode, self.kappa = MODES[mode], int(kappa)
+        self.layers: list[_Layer] = []
+        covered = set()
+        for m in model.modules():
+            if isinstance(m, (torch.nn.Linear, torch.nn.Conv2d)) and any(p.requires_grad for p in m.parameters()):
+                if isinstance(m, torch.nn.Conv2d) and m.groups != 1:
+                    raise ValueError("Conv2d with groups != 1 is not supported")
+                if isinstance(m, torch.nn.Conv2d) and m.padding_mode != "zeros":
+                    raise ValueError("Conv2d padding must be zeros")
+                if not m.weight.requires_grad:
+                    raise ValueError("a layer with a trainable bias needs a trainable weight (one norm covers both)")
+                self.layers.append(_Layer(m))
+                covered.update(id(p) for p in m.parameters())
+        others = [n for n, p in model.named_parameters() if p.requires_grad and id(p) not in covered]
+        if others:
+            raise ValueError(f"trainable parameters outside Linear/Conv2d layers: {others}")
+        if not self.layers:
+            raise ValueError("no Linear or Conv2d layer with trainable parameters")
+        self._handles = []
+        for L in self.layers:
+            self._handles.append(L.module.register_forward_hook(self._forward_hook(L)))
+            self._handles.append(L.module.register_full_backward_hook(self._backward_hook(L)))
+        self.last_norms = None  # per-sample norms of the last step
+
+    @staticmethod
+    def _forward_hook(L):
+        def hook(module, inputs, output):
+            if L.a is not None and L.g is None:
+                raise RuntimeError("a module ran twice in one forward pass")
+            L.a = inputs[0].detach()
+            L.g = None
+        return hook
+
+    @staticmethod
+    def _backward_hook(L):
+        def hook(module, grad_input, grad_output):
+            L.g = grad_output[0].detach()
+        return hook
+
+    def detach(self):
+        """Remove the hooks."""
+        for h in self._handles:
+            h.remove()
+        self._handles = []
+
+    def _operands(self, L):
+        """(A [B, T, d], G [B, T, p]) of one layer, contiguous, in the activation dtype."""
+        m, a, g = L.module, L.a, L.g
+        if a is None or g is None:
+            raise RuntimeError("step() needs one forward and one backward pass of every layer first")
+        B = a.shape[0]
+        if isinstance(m, torch.nn.Linear):
+            A = a.reshape(B, -1, a.shape[-1])
+            G = g.reshape(B, -1, g.shape[-1])
+        else:
+            U = F.unfold(a, m.kernel_size, dilation=m.dilation, padding=m.padding, stride=m.stride)  # [B, D, L]
+            A = U.transpose(1, 2)
+            G = g.reshape(B, g.shape[1], -1).transpose(1, 2)
+        dt = a.dtype if a.dtype in (torch.float32, torch.bfloat16) else torch.float32
+        return A.to(dt).contiguous(), G.to(dt).contiguous()
+
+    def step(self, step: int, denom: float | None = None):
+        """Clipped noised mean gradients into .grad; returns the per-sample norms."""
+        ops = [self._operands(L) for L in self.layers]
+        B = ops[0][0].shape[0]
+        dev = ops[0][0].device
+        dtypes = {A.dtype for A, _ in ops}
+        if len(dtypes) != 1:
+            raise RuntimeError("all layers must share one activation dtype")
+        has_bias = [L.module.bias is not None and L.module.bias.requires_grad for L in self.layers]
+        ws = torch.empty(max(256, dp_layers_workspace_bytes(ops, has_bias=has_bias, mode=self.mode,
+                                                            kappa=self.kappa)), dtype=torch.uint8, device=dev)
+        sq = torch.empty(B, dtype=torch.float32, device=dev)
+        dp_ghost_norm_layers(ops, sq, has_bias=has_bias, mode=self.mode, kappa=self.kappa, workspace=ws)
+        c = torch.empty(B, dtype=torch.float32, device=dev)
+        norms = torch.empty(B, dtype=torch.float32, device=dev)
+        dp_clip_factors(sq, self.C, c, norms)
+        outs = [torch.empty(A.shape[2], G.shape[2], dtype=torch.float32, device=dev) for A, G in ops]
+        bouts = [torch.empty(G.shape[2], dtype=torch.float32, device=dev) if hb else None
+                 for (A, G), hb in zip(ops, has_bias)]
+        dp_clipped_sum_noise_layers(ops, c, self.C, self.sigma, float(B) if denom is None else float(denom),
+                                    self.seed, step, outs, bias_outs=bouts if any(has_bias) else None,
+                                    has_bias=has_bias, workspace=ws)
+        for L, out, bout in zip(self.layers, outs, bouts):
+            w = L.module.weight
+            if w.requires_grad:
+                w.grad = out.t().reshape(w.shape).to(w.dtype).contiguous()  # [p, d] (conv: [C_out, C_in, kH, kW])
+            if bout is not None:
+                L.module.bias.grad = bout.to(L.module.bias.dtype)
+            L.a = L.g = None
+        self.last_norms = norms
+        return norms
