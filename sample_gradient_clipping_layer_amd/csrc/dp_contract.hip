@@ -21,15 +21,21 @@
 //   and lane 4a+b receives feature f0+4a+b of rows k0..k0+3, i.e. the lane's
 //   half of an operand that holds 8 consecutive k of one feature. The swizzle
 //   puts the 4 rows x 64 bytes a half-wave reads on 64 distinct banks.
-// - Each sample's partial A_i^T G_i is accumulated unscaled in a second set of
-//   accumulators and folded in as acc += c_i * partial in fp32: the clip
-//   factor is applied exactly.
+// - 128x128 and 256x128 tiles: each sample's partial A_i^T G_i is accumulated
+//   unscaled in a second set of accumulators and folded in as
+//   acc += c_i * partial in fp32 (the clip factor applied exactly). 256x256
+//   tiles keep one set and rescale it by c_prev / c_i at each sample (one
+//   more fp32 rounding per sample; see RATIO below).
 // - STAGES LDS buffers: loads for chunk q+STAGES-1 are in flight while chunk q
 //   is computed; one barrier per chunk.
-// - Workgroups are mapped so that each XCD (blockIdx % 8) owns a contiguous
-//   range of (split, tile) work items, ordered with the shorter tile dimension
-//   fastest, so concurrently running workgroups of one XCD share operand tiles
-//   in its L2.
+// - One launch takes up to kDlGroupMax layers (one tile shape, a K split per
+//   layer). Each XCD (blockIdx % 8) owns a contiguous range of every layer's
+//   (split, tile) work items, ordered with the shorter tile dimension fastest,
+//   so concurrently running workgroups of one XCD share operand tiles in its
+//   L2.
+// - A split output tile is finished either by the reduce kernel (single-layer
+//   launches) or, in multi-layer launches, by its last split inside the kernel
+//   (dl_fixup).
 #include "dp_common.hpp"
 #include "dp_launch.hpp"
 #include "dp_lds.hpp"
