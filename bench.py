@@ -185,8 +185,10 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
             # a logical batch of `virtual_steps` physical batches: per physical batch the norms, the
             # clip factors and each layer's clipped sum added to its accumulator; once per logical
             # batch each layer's noise and mean
-            kinds = (norm_kinds + [("clip", -1)] + [("sum", l) for l in range(L)]) * virtual_steps + \
-                [("noise", l) for l in range(L)]
+            acc_kinds = [("sum", l) for l in range(L)] if per_layer_sums else [("sum", -1)]
+            kinds = (norm_kinds + [("clip", -1)] + acc_kinds) * virtual_steps + [("noise", l) for l in range(L)]
+            ws_acc_layers = torch.empty(max(256, dpc.lib().dp_layers_accumulate_workspace_bytes(
+                dpc._layer_table(sets[0], wl.has_bias)[2], L, dt, B)), dtype=torch.uint8, device=dev)
             accs = [torch.empty(d, p, dtype=torch.float32, device=dev) for (T, d, p) in shapes]
             baccs = [torch.empty(p, dtype=torch.float32, device=dev) if wl.has_bias else None
                      for (T, d, p) in shapes]
@@ -235,9 +237,14 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
                 else:
                     call(dpc.dp_ghost_norm_layers, layers, sq, has_bias=wl.has_bias, mode=mode, workspace=ws_layers)
                 call(dpc.dp_clip_factors, sq, wl.C, c)
-                for l, (A, G) in enumerate(layers):
-                    call(dpc.dp_clipped_sum_accumulate, A, G, c, accs[l], bias_acc=baccs[l], accumulate=v > 0,
-                         workspace=ws_acc[l])
+                if per_layer_sums:
+                    for l, (A, G) in enumerate(layers):
+                        call(dpc.dp_clipped_sum_accumulate, A, G, c, accs[l], bias_acc=baccs[l], accumulate=v > 0,
+                             workspace=ws_acc[l])
+                else:
+                    call(dpc.dp_clipped_sum_accumulate_layers, layers, c, accs,
+                         bias_accs=baccs if wl.has_bias else None, has_bias=wl.has_bias, accumulate=v > 0,
+                         workspace=ws_acc_layers)
             for l in range(L):
                 call(dpc.dp_noise_mean, accs[l], wl.C, wl.sigma, float(B * virtual_steps), wl.seed, l, k, outs[l],
                      bias_acc=baccs[l], bias_out=bouts[l])
@@ -440,7 +447,7 @@ def main():
         print("--virtual-steps applies to global clipping workloads", file=sys.stderr)
         sys.exit(2)
     if a.virtual_steps > 1:
-        per_layer_sums, nstreams = True, 1
+        nstreams = 1
     wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device = run_gpu(wl, a.steps, a.warmup, nstreams,
                                                                       a.per_layer_norms, per_layer_sums,
                                                                       a.virtual_steps, MODES[a.path_rule])

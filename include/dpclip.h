@@ -251,6 +251,20 @@ dp_status dp_clipped_sum_accumulate(void* stream, const void* A, const void* G, 
                                     int32_t accumulate);
 
 /*
+ * dp_clipped_sum_accumulate_layers: the same for several layers under one c
+ * (flat clipping): accs[l] (+)= the clipped sum of layer l over this physical
+ * batch, formed as dp_clipped_sum_noise_layers forms it (shared launches,
+ * then one fp32 add per element). layers, n_layers, dtype, B, c as in
+ * dp_clipped_sum_noise_layers; accs / bias_accs like its outs / bias_outs.
+ * Workspace: dp_layers_accumulate_workspace_bytes(...) bytes (with
+ * accumulate == 0, dp_layers_workspace_bytes(...) suffice).
+ */
+size_t dp_layers_accumulate_workspace_bytes(const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B);
+dp_status dp_clipped_sum_accumulate_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype,
+                                           int64_t B, const float* c, void* workspace, size_t ws_bytes,
+                                           float* const* accs, float* const* bias_accs, int32_t accumulate);
+
+/*
  * dp_noise_mean: out[m][n] = (acc[m][n] + (sigma*C) * z_w[m][n]) * (1/denom),
  * bias_out[n] likewise with z_b[n], the noise of dp_clipped_sum_noise
  * (same seed, layer_id, step -> same z, bit for bit; same fp32 operation

@@ -15,6 +15,8 @@ The functions mirror the C ABI in ``include/dpclip.h``:
     dp_clipped_sum_noise_layers(layers, c, C, sigma, denom, seed, step, outs,
                                 bias_outs=None, has_bias=False, layer_ids=None, workspace=None)
     dp_clipped_sum_accumulate(A, G, c, acc, bias_acc=None, accumulate=False, workspace=None)
+    dp_clipped_sum_accumulate_layers(layers, c, accs, bias_accs=None, has_bias=False, accumulate=False,
+                                     workspace=None)
     dp_noise_mean(acc, C, sigma, denom, seed, layer_id, step, out, bias_acc=None, bias_out=None)
     dp_clip_factors(sqnorm, C, c, norm=None)
     dp_clipped_sum_noise(A, G, c, C, sigma, denom, seed, layer_id, step, out,
@@ -43,7 +45,8 @@ MODE_MIXED, MODE_GHOST, MODE_EXPLICIT, MODE_TIME = 0, 1, 2, 3
 PATH_GHOST, PATH_EXPLICIT, PATH_T1 = 1, 2, 3
 
 EXPORTS = ("dp_ghost_norm", "dp_ghost_norm_layers", "dp_layers_workspace_bytes", "dp_clipped_sum_noise_layers",
-           "dp_clip_factors", "dp_clipped_sum_accumulate", "dp_noise_mean", "dp_accumulate_workspace_bytes", "dp_clipped_sum_noise", "dp_adaptive_threshold",
+           "dp_clip_factors", "dp_clipped_sum_accumulate", "dp_noise_mean", "dp_accumulate_workspace_bytes",
+           "dp_clipped_sum_accumulate_layers", "dp_layers_accumulate_workspace_bytes", "dp_clipped_sum_noise", "dp_adaptive_threshold",
            "dp_workspace_bytes", "dp_choose_path", "dp_status_string", "dp_abi_version")
 
 _lib = None
@@ -78,6 +81,11 @@ def _declare(lib):
     lib.dp_clipped_sum_accumulate.argtypes = [vp, vp, vp, c_i32, c_i64, c_i64, c_i64, c_i64, fp, vp, ctypes.c_size_t,
                                               fp, fp, c_i32]
     lib.dp_clipped_sum_accumulate.restype = c_i32
+    lib.dp_clipped_sum_accumulate_layers.argtypes = [vp, lp, c_i32, c_i32, c_i64, fp, vp, ctypes.c_size_t,
+                                                     ctypes.POINTER(vp), ctypes.POINTER(vp), c_i32]
+    lib.dp_clipped_sum_accumulate_layers.restype = c_i32
+    lib.dp_layers_accumulate_workspace_bytes.argtypes = [lp, c_i32, c_i32, c_i64]
+    lib.dp_layers_accumulate_workspace_bytes.restype = ctypes.c_size_t
     lib.dp_noise_mean.argtypes = [vp, fp, fp, c_i64, c_i64, f, f, f, c_u64, c_u32, c_u32, fp, fp]
     lib.dp_noise_mean.restype = c_i32
     lib.dp_accumulate_workspace_bytes.argtypes = [c_i32, c_i64, c_i64, c_i64, c_i64, c_i32]
@@ -286,6 +294,33 @@ def dp_clipped_sum_accumulate(A, G, c, acc, bias_acc=None, accumulate: bool = Fa
     _check("dp_clipped_sum_accumulate", lib().dp_clipped_sum_accumulate(
         _stream(stream), _ptr(A), _ptr(G), dt, B, T, d, p, _ptr(c), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(acc), _ptr(bias_acc), int(bool(accumulate))))
+
+
+def dp_clipped_sum_accumulate_layers(layers, c, accs, bias_accs=None, has_bias=False, accumulate: bool = False,
+                                     workspace=None, stream=None):
+    """accs[l] (+)= the clipped sum of layer l over one physical batch (no noise, no mean)."""
+    import torch
+    dt, B, arr = _layer_table(layers, has_bias)
+    n = len(layers)
+    _f32_vec(c, "c")
+    if c.numel() != B or len(accs) != n:
+        raise ValueError("c must have B elements and accs one tensor per layer")
+    for k, a in enumerate(accs):
+        _f32_vec(a, "accs[k]")
+        if a.numel() != arr[k].d * arr[k].p:
+            raise ValueError(f"accs[{k}] must have d*p elements")
+    bptr = None
+    if bias_accs is not None:
+        if len(bias_accs) != n:
+            raise ValueError("one bias accumulator (or None) per layer")
+        bptr = (ctypes.c_void_p * n)(*[None if b is None else b.data_ptr() for b in bias_accs])
+    if workspace is None:
+        need = int(lib().dp_layers_accumulate_workspace_bytes(arr, n, dt, B))
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=c.device)
+    aptr = (ctypes.c_void_p * n)(*[a.data_ptr() for a in accs])
+    _check("dp_clipped_sum_accumulate_layers", lib().dp_clipped_sum_accumulate_layers(
+        _stream(stream), arr, n, dt, B, _ptr(c), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        aptr, bptr, int(bool(accumulate))))
 
 
 def dp_noise_mean(acc, C: float, sigma: float, denom: float, seed: int, layer_id: int, step: int, out,

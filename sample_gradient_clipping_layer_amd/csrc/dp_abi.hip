@@ -504,6 +504,56 @@ dp_status dp_clipped_sum_noise(void* stream, const void* A, const void* G, dp_dt
                                             denom, seed, layer_id, step, out, bias_out));
 }
 
+size_t dp_layers_accumulate_workspace_bytes(const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B) {
+  if (check_layer_list(layers, n_layers, dtype, B) != DP_OK) return 0;
+  size_t w = round256(sum_layers_ws_bytes(layers, n_layers, dtype, B));
+  for (int32_t l = 0; l < n_layers; ++l)
+    w += round256((size_t)(layers[l].d + (layers[l].has_bias ? 1 : 0)) * (size_t)layers[l].p * sizeof(float));
+  return w;
+}
+
+dp_status dp_clipped_sum_accumulate_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype,
+                                           int64_t B, const float* c, void* workspace, size_t ws_bytes,
+                                           float* const* accs, float* const* bias_accs, int32_t accumulate) {
+  dp_status s = check_layer_list(layers, n_layers, dtype, B);
+  if (s != DP_OK) return s;
+  if (!c || !accs) return DP_ERR_NULL;
+  const size_t sum_ws = round256(sum_layers_ws_bytes(layers, n_layers, dtype, B));
+  // the physical batch's clipped sums, exactly: (S + 0*z) * 1 = S
+  if (!accumulate)
+    return dp_clipped_sum_noise_layers(stream, layers, n_layers, dtype, B, c, 1.0f, 0.0f, 1.0f, 0, nullptr, 0,
+                                       workspace, ws_bytes, accs, bias_accs);
+  for (int32_t l = 0; l < n_layers; ++l) {
+    if (!accs[l]) return DP_ERR_NULL;
+    if (!aligned(accs[l], 4)) return DP_ERR_ALIGN;
+    if (layers[l].has_bias && (!bias_accs || !bias_accs[l])) return DP_ERR_NULL;
+    if (layers[l].has_bias && !aligned(bias_accs[l], 4)) return DP_ERR_ALIGN;
+  }
+  const size_t need = dp_layers_accumulate_workspace_bytes(layers, n_layers, dtype, B);
+  if (!workspace) return DP_ERR_NULL;
+  if (ws_bytes < need) return DP_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return DP_ERR_ALIGN;
+  // per layer: its sum (and bias sum) after the clipped sums' own workspace
+  std::vector<float*> sums((size_t)n_layers), bsums((size_t)n_layers, nullptr);
+  size_t off = sum_ws;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    float* base = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + off);
+    sums[l] = base;
+    if (layers[l].has_bias) bsums[l] = base + layers[l].d * layers[l].p;
+    off += round256((size_t)(layers[l].d + (layers[l].has_bias ? 1 : 0)) * (size_t)layers[l].p * sizeof(float));
+  }
+  s = dp_clipped_sum_noise_layers(stream, layers, n_layers, dtype, B, c, 1.0f, 0.0f, 1.0f, 0, nullptr, 0, workspace,
+                                  sum_ws, sums.data(), bsums.data());
+  if (s != DP_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int32_t l = 0; l < n_layers; ++l) {
+    hipError_t e = dpk::launch_accumulate(st, accs[l], sums[l], layers[l].d * layers[l].p);
+    if (e == hipSuccess && layers[l].has_bias) e = dpk::launch_accumulate(st, bias_accs[l], bsums[l], layers[l].p);
+    if (e != hipSuccess) return DP_ERR_HIP;
+  }
+  return DP_OK;
+}
+
 size_t dp_accumulate_workspace_bytes(dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64_t p, int32_t has_bias) {
   if (check_shape(B, T, d, p) != DP_OK) return 0;
   if (dtype != DP_F32 && dtype != DP_BF16) return 0;

@@ -355,3 +355,22 @@ def test_engine_refuses_unclipped_parameters():
                       C=1.0, sigma=1.0)
     assert len(e.layers) == 2
     e.detach()
+
+
+def test_accumulate_layers_validation(lib):
+    fn = lib.dp_clipped_sum_accumulate_layers
+    n = len(GPT_BLOCK)
+    accs = (ctypes.c_void_p * n)(*([FAKE] * n))
+    need = lib.dp_layers_accumulate_workspace_bytes(_layers(GPT_BLOCK), n, 1, 64)
+    assert need >= sum(d * p * 4 for (_, d, p, _) in GPT_BLOCK)
+    assert fn(None, None, n, 1, 64, FAKE, FAKE, need, accs, None, 1) == dpc.DP_ERR_NULL
+    assert fn(None, _layers(GPT_BLOCK), n, 1, 64, None, FAKE, need, accs, None, 1) == dpc.DP_ERR_NULL
+    assert fn(None, _layers(GPT_BLOCK), n, 1, 64, FAKE, FAKE, need, None, None, 1) == dpc.DP_ERR_NULL
+    assert fn(None, _layers(GPT_BLOCK), n, 1, 64, FAKE, FAKE, need - 1, accs, None, 1) == dpc.DP_ERR_WORKSPACE
+    assert fn(None, _layers(GPT_BLOCK), n, 1, 64, FAKE, None, need, accs, None, 1) == dpc.DP_ERR_NULL
+    bad = (ctypes.c_void_p * n)(FAKE, FAKE, None, FAKE)
+    assert fn(None, _layers(GPT_BLOCK), n, 1, 64, FAKE, FAKE, need, bad, None, 1) == dpc.DP_ERR_NULL
+    assert lib.dp_layers_accumulate_workspace_bytes(None, n, 1, 64) == 0
+    import torch
+    if not torch.cuda.is_available():
+        assert fn(None, _layers(GPT_BLOCK), n, 1, 64, FAKE, FAKE, need, accs, None, 1) == dpc.DP_ERR_NO_DEVICE

@@ -109,3 +109,51 @@ def test_noise_mean_in_place():
     np.testing.assert_array_equal(bacc.cpu().numpy(), bref.cpu().numpy())
     zw = N.weight_noise(d, p, 1, 0, 2)
     np.testing.assert_array_equal(ref.cpu().numpy(), D.noised_mean_f32(acc_np, zw, 1.0, 0.5, 3.0))
+
+
+def test_virtual_step_multi_layer():
+    """Several layers per physical batch (dp_clipped_sum_accumulate_layers,
+    bf16 layers sharing launches and one with a bias on another engine)
+    against the oracle's virtual step per layer; the first batch alone is
+    bit for bit the multi-layer clipped sum at sigma = 0, denom = 1."""
+    specs = [(64, 128, 192), (64, 96, 64), (128, 64, 136), (20, 40, 24)]
+    flags = [False, False, False, True]
+    sizes = (4, 6, 3)
+    rng = np.random.default_rng(12)
+    host = [[] for _ in specs]
+    devs = []
+    for B in sizes:
+        batch = []
+        for l, (T, d, p) in enumerate(specs):
+            A = W.f32_to_bf16_bits((rng.standard_normal((B, T, d)) / np.sqrt(d)).astype(np.float32))
+            G = W.f32_to_bf16_bits((rng.standard_normal((B, T, p)) / np.sqrt(p)).astype(np.float32))
+            host[l].append((W.as_f64(A, "bf16"), W.as_f64(G, "bf16")))
+            batch.append((upload(A, "bf16"), upload(G, "bf16")))
+        devs.append(batch)
+    cs = [rng.uniform(0.0, 1.0, B).astype(np.float32) for B in sizes]
+    accs = [torch.full((d, p), float("nan"), dtype=torch.float32, device=dev()) for (T, d, p) in specs]
+    baccs = [torch.full((p,), float("nan"), dtype=torch.float32, device=dev()) if hb else None
+             for (T, d, p), hb in zip(specs, flags)]
+    for k, batch in enumerate(devs):
+        dpc.dp_clipped_sum_accumulate_layers(batch, f32(cs[k]), accs, bias_accs=baccs, has_bias=flags,
+                                             accumulate=k > 0)
+        if k == 0:
+            torch.cuda.synchronize()
+            first = [a.cpu().numpy().copy() for a in accs]
+            outs = [torch.empty_like(a) for a in accs]
+            bouts = [torch.empty_like(b) if b is not None else None for b in baccs]
+            dpc.dp_clipped_sum_noise_layers(batch, f32(cs[0]), 1.0, 0.0, 1.0, 0, 0, outs, bias_outs=bouts,
+                                            has_bias=flags)
+            torch.cuda.synchronize()
+            for x, y in zip(first, outs):
+                np.testing.assert_array_equal(x.view(np.uint32), y.cpu().numpy().view(np.uint32))
+    n = float(sum(sizes))
+    for l, ((T, d, p), hb) in enumerate(zip(specs, flags)):
+        out = torch.empty(d, p, dtype=torch.float32, device=dev())
+        bout = torch.empty(p, dtype=torch.float32, device=dev()) if hb else None
+        dpc.dp_noise_mean(accs[l], 1.0, 0.0, n, 3, l, 1, out, bias_acc=baccs[l], bias_out=bout)
+        torch.cuda.synchronize()
+        r = drivers.virtual_step(host[l], [c.astype(np.float64) for c in cs], 1.0, 0.0, 3, l, 1, has_bias=hb)
+        assert_noised(out.cpu().numpy(), r["out"], r["sum"], np.zeros((d, p)), "bf16", n, what=f"layer {l}")
+        if hb:
+            assert_noised(bout.cpu().numpy(), r["bias_out"], r["bias_sum"], np.zeros(p), "bf16", n, what="bias")
