@@ -177,7 +177,9 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
         per_layer_norms = per_layer_norms or L == 1  # one layer: the plain call costs less host time
         norm_kinds = [("norm", l) for l in range(L)] if per_layer_norms else [("norm", -1)]
         sum_kinds = [("sum", l) for l in range(L)] if per_layer_sums else [("sum", -1)]
-        kinds = norm_kinds + [("clip", -1)] + sum_kinds
+        # the clip factors come out of the norm call when both calls are multi-layer
+        clip_kinds = [] if not (per_layer_norms or per_layer_sums) else [("clip", -1)]
+        kinds = norm_kinds + clip_kinds + sum_kinds
         # one workspace for the multi-layer calls (they run one after another on the stream)
         ws_layers = torch.empty(max(256, dpc.dp_layers_workspace_bytes(sets[0], has_bias=wl.has_bias, mode=mode)),
                                 dtype=torch.uint8, device=dev)
@@ -252,10 +254,14 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
         if per_layer_norms:
             for l, (A, G) in enumerate(layers):
                 call(dpc.dp_ghost_norm, A, G, sq, has_bias=wl.has_bias, mode=mode, accumulate=l > 0, workspace=ws[l])
-        else:
+        elif per_layer_sums:
             call(dpc.dp_ghost_norm_layers, layers, sq, has_bias=wl.has_bias, mode=mode, workspace=ws_layers)
+        else:  # the clip factors come out of the norm kernels
+            call(dpc.dp_ghost_norm_clip_layers, layers, sq, wl.C, c, has_bias=wl.has_bias, mode=mode,
+                 workspace=ws_layers)
         if not per_layer_sums:
-            call(dpc.dp_clip_factors, sq, wl.C, c)
+            if per_layer_norms:
+                call(dpc.dp_clip_factors, sq, wl.C, c)
             call(dpc.dp_clipped_sum_noise_layers, layers, c, wl.C, wl.sigma, float(B), wl.seed, k, outs,
                  bias_outs=bouts if wl.has_bias else None, has_bias=wl.has_bias, workspace=ws_layers)
             return

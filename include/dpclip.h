@@ -138,6 +138,18 @@ dp_status dp_ghost_norm_layers(void* stream, const dp_layer* layers, int32_t n_l
                                int64_t B, dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes,
                                float* sqnorm, int32_t accumulate, int32_t* paths_out);
 
+/*
+ * dp_ghost_norm_layers, and the clip factors of its result in the same pass:
+ * c[b] and norm[b] (norm may be NULL) exactly as dp_clip_factors(sqnorm, B,
+ * C, c, norm) would give them after the call (same fp32 operations), formed
+ * by the kernel that finishes each sample's squared norm (by the clip kernel
+ * after it when the last layer takes the T = 1 closed form). C finite, > 0.
+ */
+dp_status dp_ghost_norm_clip_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype,
+                                    int64_t B, dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes,
+                                    float* sqnorm, int32_t accumulate, float C, float* c, float* norm,
+                                    int32_t* paths_out);
+
 /* Workspace bytes that dp_ghost_norm_layers (with this mode and kappa) and
  * dp_clipped_sum_noise_layers need for these layers (the larger of the two).
  * Returns 0 for invalid arguments (and when no workspace is needed). */

@@ -11,6 +11,8 @@ The functions mirror the C ABI in ``include/dpclip.h``:
                   accumulate=False, workspace=None) -> path
     dp_ghost_norm_layers(layers, sqnorm, has_bias=False, mode=MODE_MIXED, kappa=1,
                          accumulate=False, workspace=None) -> [path, ...]
+    dp_ghost_norm_clip_layers(layers, sqnorm, C, c, norm=None, has_bias=False, mode=MODE_MIXED, kappa=1,
+                              accumulate=False, workspace=None) -> [path, ...]
     dp_layers_workspace_bytes(layers, has_bias=False, mode=MODE_MIXED, kappa=1) -> int
     dp_clipped_sum_noise_layers(layers, c, C, sigma, denom, seed, step, outs,
                                 bias_outs=None, has_bias=False, layer_ids=None, workspace=None)
@@ -44,7 +46,7 @@ DP_F32, DP_BF16 = 0, 1
 MODE_MIXED, MODE_GHOST, MODE_EXPLICIT, MODE_TIME = 0, 1, 2, 3
 PATH_GHOST, PATH_EXPLICIT, PATH_T1 = 1, 2, 3
 
-EXPORTS = ("dp_ghost_norm", "dp_ghost_norm_layers", "dp_layers_workspace_bytes", "dp_clipped_sum_noise_layers",
+EXPORTS = ("dp_ghost_norm", "dp_ghost_norm_layers", "dp_ghost_norm_clip_layers", "dp_layers_workspace_bytes", "dp_clipped_sum_noise_layers",
            "dp_clip_factors", "dp_clipped_sum_accumulate", "dp_noise_mean", "dp_accumulate_workspace_bytes",
            "dp_clipped_sum_accumulate_layers", "dp_layers_accumulate_workspace_bytes", "dp_clipped_sum_noise", "dp_adaptive_threshold",
            "dp_workspace_bytes", "dp_choose_path", "dp_status_string", "dp_abi_version")
@@ -74,6 +76,9 @@ def _declare(lib):
     lib.dp_ghost_norm_layers.argtypes = [vp, lp, c_i32, c_i32, c_i64, c_i32, c_i32, vp, ctypes.c_size_t, fp, c_i32,
                                          ctypes.POINTER(c_i32)]
     lib.dp_ghost_norm_layers.restype = c_i32
+    lib.dp_ghost_norm_clip_layers.argtypes = [vp, lp, c_i32, c_i32, c_i64, c_i32, c_i32, vp, ctypes.c_size_t, fp,
+                                              c_i32, f, fp, fp, ctypes.POINTER(c_i32)]
+    lib.dp_ghost_norm_clip_layers.restype = c_i32
     lib.dp_clipped_sum_noise_layers.argtypes = [vp, lp, c_i32, c_i32, c_i64, fp, f, f, f, c_u64,
                                                 ctypes.POINTER(c_u32), c_u32, vp, ctypes.c_size_t,
                                                 ctypes.POINTER(vp), ctypes.POINTER(vp)]
@@ -243,6 +248,26 @@ def dp_ghost_norm_layers(layers, sqnorm, has_bias=False, mode: int = MODE_MIXED,
     _check("dp_ghost_norm_layers", lib().dp_ghost_norm_layers(
         _stream(stream), arr, len(layers), dt, B, int(mode), int(kappa), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(sqnorm), int(bool(accumulate)), paths))
+    return list(paths)
+
+
+def dp_ghost_norm_clip_layers(layers, sqnorm, C: float, c, norm=None, has_bias=False, mode: int = MODE_MIXED,
+                              kappa: int = 1, accumulate: bool = False, workspace=None, stream=None):
+    """dp_ghost_norm_layers plus the clip factors (and norms) of the result, in the same pass."""
+    import torch
+    dt, B, arr = _layer_table(layers, has_bias)
+    for t, nm in ((sqnorm, "sqnorm"), (c, "c")) + (((norm, "norm"),) if norm is not None else ()):
+        _f32_vec(t, nm)
+        if t.numel() != B:
+            raise ValueError(f"{nm} must have B elements")
+    if workspace is None:
+        need = int(lib().dp_layers_workspace_bytes(arr, len(layers), dt, B, int(mode), int(kappa)))
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=sqnorm.device)
+    paths = (ctypes.c_int32 * len(layers))()
+    _check("dp_ghost_norm_clip_layers", lib().dp_ghost_norm_clip_layers(
+        _stream(stream), arr, len(layers), dt, B, int(mode), int(kappa), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(sqnorm), int(bool(accumulate)), float(C), _ptr(c),
+        _ptr(norm), paths))
     return list(paths)
 
 

@@ -94,17 +94,36 @@ size_t contract_ws_bytes(dp_dtype dtype, int64_t B, int64_t T, int64_t d, int64_
 
 dp_status hip_status(hipError_t e) { return e == hipSuccess ? DP_OK : DP_ERR_HIP; }
 
-// Launches the norm kernels of one layer whose arguments are validated.
+// Clip factors (and norms) to form from the final squared norms of a call.
+struct ClipOut {
+  float C;
+  float* c;
+  float* norm;  // may be null
+};
+
+// Launches the norm kernels of one layer whose arguments are validated; with
+// `clip`, also the clip factors of the resulting squared norms (in the
+// kernel's per-sample sink, or by the clip kernel after the closed form).
 hipError_t launch_layer_norm(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t T, int64_t d,
-                             int64_t p, int hb, int path, void* workspace, float* sqnorm, int acc) {
-  if (path == DP_PATH_T1) return dpk::launch_norm_t1(st, dtype, A, G, B, d, p, hb, acc, sqnorm);
+                             int64_t p, int hb, int path, void* workspace, float* sqnorm, int acc,
+                             const ClipOut* clip = nullptr) {
+  if (path == DP_PATH_T1) {
+    hipError_t e = dpk::launch_norm_t1(st, dtype, A, G, B, d, p, hb, acc, sqnorm);
+    if (e == hipSuccess && clip) e = dpk::launch_clip_factors(st, sqnorm, B, clip->C, clip->c, clip->norm);
+    return e;
+  }
   const int64_t ntiles = norm_ntiles(dtype, path, T, d, p, hb);
-  const dpk::NormSink sink = dpk::make_norm_sink(
+  dpk::NormSink sink = dpk::make_norm_sink(
       static_cast<float*>(workspace),
       ntiles > 1 ? reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(workspace) +
                                                          norm_partial_bytes(B, ntiles))
                  : nullptr,
       sqnorm, (int)ntiles, acc, dpk::next_epoch());
+  if (clip) {
+    sink.clip_c = clip->c;
+    sink.clip_norm = clip->norm;
+    sink.C = clip->C;
+  }
   if (path == DP_PATH_GHOST) return dpk::launch_ghost(st, dtype, A, G, B, T, d, p, hb, sink);
   return dpk::launch_explicit(st, dtype, A, G, B, T, d, p, hb, sink);
 }
@@ -336,9 +355,9 @@ size_t dp_layers_workspace_bytes(const dp_layer* layers, int32_t n_layers, dp_dt
   return w;
 }
 
-dp_status dp_ghost_norm_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B,
-                               dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes, float* sqnorm,
-                               int32_t accumulate, int32_t* paths_out) {
+static dp_status norm_layers_impl(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B,
+                                  dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes, float* sqnorm,
+                                  int32_t accumulate, int32_t* paths_out, const ClipOut* clip) {
   dp_status s = check_norm_layers(layers, n_layers, dtype, B, mode, kappa);
   if (s != DP_OK) return s;
   if (!sqnorm) return DP_ERR_NULL;
@@ -370,6 +389,11 @@ dp_status dp_ghost_norm_layers(void* stream, const dp_layer* layers, int32_t n_l
                          : nullptr,
           sqnorm, (int)run.ntiles, acc, dpk::next_epoch());
       sink.nlayers = run.count;
+      if (clip && r == nr - 1) {  // the last run's sink holds each sample's final value
+        sink.clip_c = clip->c;
+        sink.clip_norm = clip->norm;
+        sink.C = clip->C;
+      }
       sink.lt[0] = 0;
       for (int k = 0; k < run.count; ++k) {
         const dp_layer& x = layers[run.first + k];
@@ -381,11 +405,29 @@ dp_status dp_ghost_norm_layers(void* stream, const dp_layer* layers, int32_t n_l
       const dp_layer& x = layers[run.first];
       const int hb = x.has_bias ? 1 : 0;
       e = launch_layer_norm(st, dtype, x.A, x.G, B, x.T, x.d, x.p, hb, path_of(x.T, x.d, x.p, mode, kappa),
-                            workspace, sqnorm, acc);
+                            workspace, sqnorm, acc, r == nr - 1 ? clip : nullptr);
     }
     if (e != hipSuccess) return DP_ERR_HIP;
   }
   return DP_OK;
+}
+
+dp_status dp_ghost_norm_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B,
+                               dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes, float* sqnorm,
+                               int32_t accumulate, int32_t* paths_out) {
+  return norm_layers_impl(stream, layers, n_layers, dtype, B, mode, kappa, workspace, ws_bytes, sqnorm, accumulate,
+                          paths_out, nullptr);
+}
+
+dp_status dp_ghost_norm_clip_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B,
+                                    dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes, float* sqnorm,
+                                    int32_t accumulate, float C, float* c, float* norm, int32_t* paths_out) {
+  if (!c) return DP_ERR_NULL;
+  if (!aligned(c, 4) || (norm && !aligned(norm, 4))) return DP_ERR_ALIGN;
+  if (!finite(C) || !(C > 0.0f)) return DP_ERR_VALUE;
+  const ClipOut clip{C, c, norm};
+  return norm_layers_impl(stream, layers, n_layers, dtype, B, mode, kappa, workspace, ws_bytes, sqnorm, accumulate,
+                          paths_out, &clip);
 }
 
 dp_status dp_clipped_sum_noise_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype,

@@ -148,6 +148,25 @@ __device__ __forceinline__ bool arrive_last(unsigned long long* ctr, uint64_t ep
   }
 }
 
+// Correctly rounded fp32 square root (through the double-precision one).
+__device__ __forceinline__ float sqrt_rn_f32(float x) { return (float)__dsqrt_rn((double)x); }
+
+// Clip factor of one sample from its squared norm: norm = sqrt(sq) with
+// negative round-off clamped to 0 (NaN kept); c = C / norm when norm > C,
+// else 1 (NaN norm -> NaN; infinite norm -> 0). FPC clip_c; SEDP App. C,
+// C_i = min(R/||g_i||, 1).
+__device__ __forceinline__ void clip_factor_of(float sq, float C, float* c, float* norm) {
+  const float s = sq < 0.0f ? 0.0f : sq;
+  const float n = sqrt_rn_f32(s);
+  float ci;
+  if (n > C)
+    ci = __fdiv_rn(C, n);
+  else
+    ci = (n == n) ? 1.0f : n;
+  *c = ci;
+  if (norm) *norm = n;
+}
+
 // Layers one grouped norm launch can take.
 constexpr int kNormGroupMax = 8;
 
@@ -167,6 +186,9 @@ struct NormSink {
   uint64_t epoch;
   int nlayers;
   int lt[kNormGroupMax + 1];
+  float* clip_c;                  // when set: clip factors (and clip_norm, when set) of the final sqnorm
+  float* clip_norm;
+  float C;
 };
 
 // A sink for one layer of `ntiles` tiles per sample.
@@ -194,7 +216,9 @@ inline NormSink make_norm_sink(float* partial, unsigned long long* arrivals, flo
 __device__ __forceinline__ void norm_sink_tile(const NormSink& k, int64_t i, int64_t tile, float s) {
   if (k.ntiles == 1) {
     const float tot = 0.f + s;
-    k.sqnorm[i] = k.accumulate ? k.sqnorm[i] + tot : tot;
+    const float v = k.accumulate ? k.sqnorm[i] + tot : tot;
+    k.sqnorm[i] = v;
+    if (k.clip_c) clip_factor_of(v, k.C, k.clip_c + i, k.clip_norm ? k.clip_norm + i : nullptr);
     return;
   }
   float* row = k.partial + i * k.ntiles;
@@ -209,6 +233,7 @@ __device__ __forceinline__ void norm_sink_tile(const NormSink& k, int64_t i, int
     v = (l == 0 && !k.accumulate) ? tot : v + tot;
   }
   k.sqnorm[i] = v;
+  if (k.clip_c) clip_factor_of(v, k.C, k.clip_c + i, k.clip_norm ? k.clip_norm + i : nullptr);
 }
 
 }  // namespace dpk

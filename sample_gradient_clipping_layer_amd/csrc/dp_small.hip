@@ -12,16 +12,7 @@ __global__ __launch_bounds__(256) void k_clip_factors(const float* __restrict__ 
                                                       float* __restrict__ c, float* __restrict__ norm) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= B) return;
-  float s = sqnorm[i];
-  s = s < 0.0f ? 0.0f : s;
-  const float n = sqrt_rn_f32(s);
-  float ci;
-  if (n > C)
-    ci = __fdiv_rn(C, n);
-  else
-    ci = (n == n) ? 1.0f : n;
-  c[i] = ci;
-  if (norm) norm[i] = n;
+  clip_factor_of(sqnorm[i], C, c + i, norm ? norm + i : nullptr);
 }
 
 // TTP adaptive clipping, one layer: one workgroup of 1024 threads.

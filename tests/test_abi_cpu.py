@@ -374,3 +374,24 @@ def test_accumulate_layers_validation(lib):
     import torch
     if not torch.cuda.is_available():
         assert fn(None, _layers(GPT_BLOCK), n, 1, 64, FAKE, FAKE, need, accs, None, 1) == dpc.DP_ERR_NO_DEVICE
+
+
+def test_norm_clip_layers_validation(lib):
+    fn = lib.dp_ghost_norm_clip_layers
+    f = ctypes.c_float
+    n = len(GPT_BLOCK)
+    paths = (ctypes.c_int32 * n)()
+
+    def call(C=1.0, c=FAKE, norm=None, sq=FAKE, wsb=1 << 30):
+        return fn(None, _layers(GPT_BLOCK), n, 1, 64, 0, 1, FAKE, wsb, sq, 0, f(C), c, norm, paths)
+
+    assert call(c=None) == dpc.DP_ERR_NULL
+    assert call(c=FAKE + 2) == dpc.DP_ERR_ALIGN
+    assert call(norm=FAKE + 1) == dpc.DP_ERR_ALIGN
+    for C in (0.0, -1.0, float("inf"), float("nan")):
+        assert call(C=C) == dpc.DP_ERR_VALUE
+    assert call(sq=None) == dpc.DP_ERR_NULL
+    assert call(wsb=16) == dpc.DP_ERR_WORKSPACE
+    import torch
+    if not torch.cuda.is_available():
+        assert call() == dpc.DP_ERR_NO_DEVICE

@@ -252,3 +252,49 @@ def test_time_rule_on_conv_layers():
     seq, _ = _sequential(devs, flags, dpc.MODE_TIME)
     np.testing.assert_array_equal(grp.view(np.uint32), seq.view(np.uint32))
     assert_norms(np.sqrt(grp), np.sqrt(_oracle(host, flags)), wl.dtype)
+
+
+FUSED_CLIP_CASES = ["gpt-block", "ragged-bias-f32", "mixed-paths", "ten-layers", "wide-engine-inside"]
+
+
+@pytest.mark.parametrize("name", FUSED_CLIP_CASES)
+def test_norm_clip_layers_equal_separate_clip(name):
+    """Clip factors formed in the norm kernels' sinks (dp_ghost_norm_clip_layers)
+    equal dp_clip_factors applied after dp_ghost_norm_layers, bit for bit,
+    whatever path the last layer takes; so do the squared norms."""
+    B, specs, dtype, flags, mode = CASES[name]
+    host, devs = _inputs(B, specs, dtype, seed=40 + len(name))
+    sq_ref, _ = _grouped(devs, flags, mode)
+    sq_ref_t = torch.from_numpy(sq_ref).to(dev())
+    norms = np.sqrt(_oracle(host, flags))
+    for C in (float(np.median(norms)), 1e-3, 1e9):
+        c_ref = torch.empty(B, dtype=torch.float32, device=dev())
+        n_ref = torch.empty(B, dtype=torch.float32, device=dev())
+        dpc.dp_clip_factors(sq_ref_t, C, c_ref, n_ref)
+        sq = torch.full((B,), float("nan"), dtype=torch.float32, device=dev())
+        c = torch.full((B,), float("nan"), dtype=torch.float32, device=dev())
+        n = torch.full((B,), float("nan"), dtype=torch.float32, device=dev())
+        dpc.dp_ghost_norm_clip_layers(devs, sq, C, c, n, has_bias=flags, mode=mode)
+        torch.cuda.synchronize()
+        for got, want in ((sq, sq_ref_t), (c, c_ref), (n, n_ref)):
+            np.testing.assert_array_equal(got.cpu().numpy().view(np.uint32), want.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("last", [dpc.PATH_T1, dpc.PATH_EXPLICIT])
+def test_norm_clip_layers_last_layer_path(last):
+    """A last layer with T = 1 has no per-sample sink: its call is followed
+    by the clip kernel; an explicit last layer forms the factors in its own
+    sink. Either way the factors are the same bits."""
+    B = 7
+    specs = [(96, 128, 128), (1, 64, 32) if last == dpc.PATH_T1 else (200, 16, 24)]
+    _, devs = _inputs(B, specs, "bf16", seed=77)
+    flags = [False, True]
+    sq_ref, paths = _grouped(devs, flags, dpc.MODE_MIXED)
+    assert paths[-1] == last
+    c_ref = torch.empty(B, dtype=torch.float32, device=dev())
+    dpc.dp_clip_factors(torch.from_numpy(sq_ref).to(dev()), 0.5, c_ref)
+    sq = torch.empty(B, dtype=torch.float32, device=dev())
+    c = torch.empty(B, dtype=torch.float32, device=dev())
+    dpc.dp_ghost_norm_clip_layers(devs, sq, 0.5, c, has_bias=flags)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(c.cpu().numpy().view(np.uint32), c_ref.cpu().numpy().view(np.uint32))
