@@ -446,7 +446,7 @@ def main():
                  sum(1 for (T, d, p) in shapes0 if T % 64 == 0 and d % 8 == 0 and p % 8 == 0) >= 2)
     per_layer_sums = a.per_layer_sums or not groupable
     if per_layer_sums and not wl.per_layer:
-        nstreams = a.streams if a.streams is not None else (3 if wl.n_layers <= 8 else 1)
+        nstreams = a.streams if a.streams is not None else (3 if 2 <= wl.n_layers <= 8 else 1)
     else:
         nstreams = 1
     if a.virtual_steps > 1 and wl.per_layer:
