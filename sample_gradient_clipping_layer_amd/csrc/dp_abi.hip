@@ -139,7 +139,7 @@ bool layer_fits(int dtype, int path, int64_t B, int64_t T, int64_t d, int64_t p,
 // Consecutive layers of a multi-layer norm call that share one launch.
 struct NormRun {
   int first, count;
-  bool grouped;       // the tiled ghost kernel, one launch for all of them
+  bool grouped;       // ghost layers of one kernel, one launch for all of them
   int64_t ntiles;     // tiles per sample over the run
 };
 
@@ -171,10 +171,11 @@ dp_status check_norm_layers(const dp_layer* layers, int32_t n, dp_dtype dtype, i
   return DP_OK;
 }
 
-// Runs in layer order: a run of the tiled ghost kernel grows while the next
-// layer takes that kernel with the same tile size and the run stays within
-// one launch's limits (kNormGroupMax layers, the sample's tile count, the
-// grid); every other layer is a run of its own.
+// Runs in layer order: a run of ghost layers grows while the next layer takes
+// the same ghost kernel (the tiled one with the same tile size, or the
+// long-sequence bf16 engine) and the run stays within one launch's limits
+// (kNormGroupMax layers, the sample's tile count, the grid); every other
+// layer is a run of its own.
 int plan_norm_runs(const dp_layer* layers, int32_t n, dp_dtype dtype, int64_t B, dp_mode mode, int32_t kappa,
                    NormRun* runs) {
   int nr = 0;
@@ -183,12 +184,12 @@ int plan_norm_runs(const dp_layer* layers, int32_t n, dp_dtype dtype, int64_t B,
     const int hb = x.has_bias ? 1 : 0;
     const int path = path_of(x.T, x.d, x.p, mode, kappa);
     const int64_t nt = norm_ntiles(dtype, path, x.T, x.d, x.p, hb);
-    const bool groupable = path == DP_PATH_GHOST && dpk::ghost_groupable(dtype, x.T, x.d, x.p);
+    const bool groupable = path == DP_PATH_GHOST;
     if (groupable && nr > 0) {
       NormRun& r = runs[nr - 1];
       const dp_layer& f = layers[r.first];
       if (r.grouped && r.count < dpk::kNormGroupMax &&
-          dpk::ghost_group_key(dtype, f.T) == dpk::ghost_group_key(dtype, x.T) &&
+          dpk::ghost_group_key(dtype, f.T, f.d, f.p) == dpk::ghost_group_key(dtype, x.T, x.d, x.p) &&
           r.ntiles + nt <= kMaxTilesPerSample &&
           (uint64_t)((B + 7) / 8 * 8) * (uint64_t)(r.ntiles + nt) < (1ull << 32)) {
         r.count += 1;

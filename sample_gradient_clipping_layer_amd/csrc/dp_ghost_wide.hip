@@ -206,23 +206,41 @@ __device__ __forceinline__ float gw_item(const bf16s* __restrict__ Ai, const bf1
   return s;
 }
 
-__global__ __launch_bounds__(gw::NT, 1) void k_ghost_wide(const bf16s* __restrict__ A, const bf16s* __restrict__ G,
-                                                          GwArgs a, NormSink sink) {
+// One layer of a wide-ghost launch (workgroup range a multiple of 8, first tile in the sink).
+struct GwLayer {
+  const bf16s* A;
+  const bf16s* G;
+  GwArgs a;
+  int64_t wg_begin;
+  int tile_base;
+};
+struct GwGroup {
+  GwLayer L[kNormGroupMax];
+  int n;
+};
+
+__global__ __launch_bounds__(gw::NT, 1) void k_ghost_wide(GwGroup g, NormSink sink) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
   __shared__ float red[gw::NW];
+  // the layer whose workgroup range holds this workgroup (uniform choice among compile-time entries)
+  GwLayer L = g.L[0];
+#pragma unroll
+  for (int k = 1; k < kNormGroupMax; ++k)
+    if (k < g.n && (int64_t)blockIdx.x >= g.L[k].wg_begin) L = g.L[k];
+  const GwArgs& a = L.a;
   int64_t i, tile;
-  xcd_group_map(blockIdx.x, a.ntiles, &i, &tile);
+  xcd_group_map((int64_t)blockIdx.x - L.wg_begin, a.ntiles, &i, &tile);
   if (i >= a.B) return;  // whole workgroup, before any barrier
   int r, c;
   gw_tile_rc((int)tile, a.nbc, &r, &c);
   // the sample's bases are wave-uniform; readfirstlane lets them live in SGPRs
   // (the direct-to-LDS loads take a scalar base)
-  const bf16s* Ai = uniform_ptr(A + i * a.Tn * a.d);
-  const bf16s* Gi = uniform_ptr(G + i * a.Tn * a.p);
+  const bf16s* Ai = uniform_ptr(L.A + i * a.Tn * a.d);
+  const bf16s* Gi = uniform_ptr(L.G + i * a.Tn * a.p);
   const bool tin = c < 2 * r + 2;  // column block inside the row block
   float s = tin ? gw_item<true>(Ai, Gi, a, r, c, lds) : gw_item<false>(Ai, Gi, a, r, c, lds);
   s = block_sum<gw::NT>(s, red);
-  if (threadIdx.x == 0) norm_sink_tile(sink, i, tile, s);
+  if (threadIdx.x == 0) norm_sink_tile(sink, i, L.tile_base + tile, s);
 }
 
 bool ghost_wide_eligible(int dtype, int64_t Tn, int64_t d, int64_t p) {
@@ -238,24 +256,56 @@ int64_t ghost_wide_ntiles(int64_t Tn) {
   return n;
 }
 
-hipError_t launch_ghost_wide(hipStream_t st, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
-                             int64_t p, int has_bias, const NormSink& sink) {
-  GwArgs a;
-  a.B = B;
-  a.Tn = Tn;
-  a.d = d;
-  a.p = p;
-  a.has_bias = has_bias;
-  a.nbc = (int)((Tn + gw::BN - 1) / gw::BN);
-  a.ntiles = (int)ghost_wide_ntiles(Tn);
+// Layers laid out in the grid by decreasing d + p (largest tiles first);
+// tile_base follows the caller's order, the order of the sink's fold.
+hipError_t launch_ghost_wide_group(hipStream_t st, const GhostLayerDesc* layers, int n, int64_t B,
+                                   const NormSink& sink) {
+  GwGroup g{};
+  int order[kNormGroupMax];
+  int base[kNormGroupMax];
+  int tb = 0;
+  for (int l = 0; l < n; ++l) {
+    order[l] = l;
+    base[l] = tb;
+    tb += (int)ghost_wide_ntiles(layers[l].Tn);
+  }
+  for (int x = 1; x < n; ++x)  // stable insertion sort by d + p, largest first
+    for (int y = x; y > 0 && layers[order[y]].d + layers[order[y]].p > layers[order[y - 1]].d + layers[order[y - 1]].p;
+         --y) {
+      const int t = order[y];
+      order[y] = order[y - 1];
+      order[y - 1] = t;
+    }
   const int64_t groups8 = (B + 7) / 8;
-  const dim3 grid((unsigned)(groups8 * 8 * a.ntiles));
+  int64_t wg = 0;
+  for (int k = 0; k < n; ++k) {
+    const GhostLayerDesc& x = layers[order[k]];
+    GwLayer& L = g.L[k];
+    L.A = static_cast<const bf16s*>(x.A);
+    L.G = static_cast<const bf16s*>(x.G);
+    L.a.B = B;
+    L.a.Tn = x.Tn;
+    L.a.d = x.d;
+    L.a.p = x.p;
+    L.a.has_bias = x.has_bias;
+    L.a.nbc = (int)((x.Tn + gw::BN - 1) / gw::BN);
+    L.a.ntiles = (int)ghost_wide_ntiles(x.Tn);
+    L.wg_begin = wg;
+    L.tile_base = base[order[k]];
+    wg += groups8 * 8 * L.a.ntiles;
+  }
+  g.n = n;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ghost_wide),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, gw::LDS);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_ghost_wide, grid, dim3(gw::NT), gw::LDS, st, static_cast<const bf16s*>(A),
-                     static_cast<const bf16s*>(G), a, sink);
+  hipLaunchKernelGGL(k_ghost_wide, dim3((unsigned)wg), dim3(gw::NT), gw::LDS, st, g, sink);
   return hipGetLastError();
+}
+
+hipError_t launch_ghost_wide(hipStream_t st, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
+                             int64_t p, int has_bias, const NormSink& sink) {
+  const GhostLayerDesc x{A, G, Tn, d, p, has_bias};
+  return launch_ghost_wide_group(st, &x, 1, B, sink);
 }
 
 }  // namespace dpk

@@ -98,16 +98,16 @@ struct GhostLayerDesc {
   int64_t Tn, d, p;
   int has_bias;
 };
-// Layers that the tiled ghost kernel takes (the long-sequence bf16 engine
-// runs one layer per launch); layers of one launch share ghost_group_key.
-bool ghost_groupable(int dtype, int64_t Tn, int64_t d, int64_t p);
-int ghost_group_key(int dtype, int64_t Tn);
-// Workgroups of a grouped launch (the caller keeps it below 2^32).
-int64_t ghost_group_grid(int64_t B, const GhostLayerDesc* layers, int n);
-// Up to kNormGroupMax groupable layers with one key in one launch; the sink
-// spans the tiles of all of them (lt[] in the order of `layers`).
+// Layers of one ghost launch share ghost_group_key: the tiled kernel's tile
+// size and dtype, or the long-sequence bf16 engine.
+int ghost_group_key(int dtype, int64_t Tn, int64_t d, int64_t p);
+// Up to kNormGroupMax groupable layers with one key in one launch (the tiled
+// kernel, or the long-sequence bf16 engine); the sink spans the tiles of all
+// of them (lt[] in the order of `layers`).
 hipError_t launch_ghost_group(hipStream_t st, int dtype, const GhostLayerDesc* layers, int n, int64_t B,
                               const NormSink& sink);
+hipError_t launch_ghost_wide_group(hipStream_t st, const GhostLayerDesc* layers, int n, int64_t B,
+                                   const NormSink& sink);
 // Norm kernels whose sample spans several tile workgroups finish each
 // sample in its last-arriving tile (NormSink in dp_common.hpp).
 hipError_t launch_ghost(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,

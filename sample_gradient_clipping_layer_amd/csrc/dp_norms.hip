@@ -494,22 +494,15 @@ hipError_t launch_ghost_t(hipStream_t st, const GhostLayerDesc* layers, int n, i
   return hipGetLastError();
 }
 
-bool ghost_groupable(int dtype, int64_t Tn, int64_t d, int64_t p) { return !ghost_wide_eligible(dtype, Tn, d, p); }
-
-int ghost_group_key(int dtype, int64_t Tn) { return 2 * ghost_tile_size(Tn) + (dtype == 1 ? 1 : 0); }
-
-int64_t ghost_group_grid(int64_t B, const GhostLayerDesc* layers, int n) {
-  int64_t wg = 0;
-  for (int l = 0; l < n; ++l) {
-    const int64_t ts = ghost_tile_size(layers[l].Tn);
-    const int64_t nb = (layers[l].Tn + ts - 1) / ts;
-    wg += (B + 7) / 8 * 8 * (nb * (nb + 1) / 2);
-  }
-  return wg;
+int ghost_group_key(int dtype, int64_t Tn, int64_t d, int64_t p) {
+  if (ghost_wide_eligible(dtype, Tn, d, p)) return 1;
+  return 2 * ghost_tile_size(Tn) + (dtype == 1 ? 1 : 0);
 }
 
 hipError_t launch_ghost_group(hipStream_t st, int dtype, const GhostLayerDesc* layers, int n, int64_t B,
                               const NormSink& sink) {
+  if (ghost_wide_eligible(dtype, layers[0].Tn, layers[0].d, layers[0].p))
+    return launch_ghost_wide_group(st, layers, n, B, sink);
   const int ts = ghost_tile_size(layers[0].Tn);
   if (dtype == 1) {
     if (ts == 64) return launch_ghost_t<bf16s, 64>(st, layers, n, B, sink);

@@ -75,6 +75,9 @@ CASES = {
                    dpc.MODE_GHOST),
     "wide-engine-inside": (3, [(128, 128, 128), (512, 128, 192), (128, 64, 128)], "bf16", [False, False, True],
                            dpc.MODE_GHOST),
+    # consecutive long-sequence layers share one launch of that engine
+    "wide-group": (3, [(512, 128, 192), (576, 64, 128), (1024, 128, 64), (512, 192, 64)], "bf16",
+                   [False, True, False, True], dpc.MODE_GHOST),
 }
 
 
@@ -254,7 +257,7 @@ def test_time_rule_on_conv_layers():
     assert_norms(np.sqrt(grp), np.sqrt(_oracle(host, flags)), wl.dtype)
 
 
-FUSED_CLIP_CASES = ["gpt-block", "ragged-bias-f32", "mixed-paths", "ten-layers", "wide-engine-inside"]
+FUSED_CLIP_CASES = ["gpt-block", "ragged-bias-f32", "mixed-paths", "ten-layers", "wide-engine-inside", "wide-group"]
 
 
 @pytest.mark.parametrize("name", FUSED_CLIP_CASES)
