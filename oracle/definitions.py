@@ -210,3 +210,33 @@ def clipped_sum_entries(A: np.ndarray, G: np.ndarray, c: np.ndarray, rows, cols)
                       axis=1)  # per-example gradient entry [B]
         out[k] = float(np.dot(c, g_mn))
     return out
+
+
+def unfold2d(a: np.ndarray, kernel, stride=(1, 1), padding=(0, 0), dilation=(1, 1)) -> np.ndarray:
+    """U(a): the unfolded input of a 2-D convolution, [B, T, d] in fp64 from the
+    folded input a [B, C_in, H, W].
+
+    [SEDP] Sec. 2.2 (convolution as a linear layer on U(a_i), eqs. (2.5)-(2.6));
+    [FPC] Algorithm 3 (the im2col matrix). Row t = ho*W_out + wo is the receptive
+    field of output position (ho, wo); its column f = (ci*kH + i)*kW + j holds
+    the input at channel ci, row ho*s_h - p_h + i*dl_h, column
+    wo*s_w - p_w + j*dl_w, and 0 where that lies in the zero padding. Written as
+    loops over the kernel offsets: each offset (i, j) fills one column per
+    channel with a strided slice of the zero-padded input.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    B, Cin, H, W = a.shape
+    (kh, kw), (sh, sw), (ph, pw), (dh, dw) = kernel, stride, padding, dilation
+    Ho = (H + 2 * ph - dh * (kh - 1) - 1) // sh + 1
+    Wo = (W + 2 * pw - dw * (kw - 1) - 1) // sw + 1
+    if Ho < 1 or Wo < 1:
+        raise ValueError("the kernel does not fit the padded input")
+    padded = np.zeros((B, Cin, H + 2 * ph, W + 2 * pw), dtype=np.float64)
+    padded[:, :, ph:ph + H, pw:pw + W] = a
+    U = np.zeros((B, Ho, Wo, Cin, kh, kw), dtype=np.float64)
+    for i in range(kh):
+        for j in range(kw):
+            y0, x0 = i * dh, j * dw  # padded coordinates of output (0, 0)'s tap (i, j)
+            U[:, :, :, :, i, j] = padded[:, :, y0:y0 + sh * (Ho - 1) + 1:sh,
+                                         x0:x0 + sw * (Wo - 1) + 1:sw].transpose(0, 2, 3, 1)
+    return U.reshape(B, Ho * Wo, Cin * kh * kw)

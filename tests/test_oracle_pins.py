@@ -93,6 +93,58 @@ def test_conv_per_example_grad_via_unfold(cin, H, cout, stride):
         np.testing.assert_allclose(g, gW.reshape(cout, -1).T.numpy(), rtol=1e-10, atol=1e-10)
 
 
+CONV_GEOMETRIES = [  # (C_in, H, W, kernel, stride, padding, dilation)
+    (3, 7, 9, (3, 3), (1, 1), (1, 1), (1, 1)),
+    (2, 8, 8, (3, 3), (2, 2), (1, 1), (1, 1)),
+    (4, 6, 5, (5, 3), (2, 1), (2, 0), (1, 2)),
+    (3, 4, 4, (1, 1), (2, 2), (0, 0), (1, 1)),
+    (2, 9, 7, (2, 4), (3, 2), (0, 3), (2, 1)),
+]
+
+
+@pytest.mark.parametrize("cin,H,Wd,k,s,pad,dil", CONV_GEOMETRIES)
+def test_unfold2d_gives_conv_weight_grad(cin, H, Wd, k, s, pad, dil):
+    """[SEDP] Sec. 2.2, eqs. (2.5)-(2.6); [FPC] Algorithm 3: the oracle's
+    unfolding U(a_i) times F^-1(dL/ds_i) is the per-example conv weight
+    gradient, here from a batch-1 conv2d backward with stride, padding,
+    dilation and a rectangular kernel. A wrong column order, tap offset or
+    padding fill fails it."""
+    rng = np.random.default_rng(7)
+    B, cout = 2, 3
+    x = rng.standard_normal((B, cin, H, Wd))
+    Wt = torch.tensor(rng.standard_normal((cout, cin) + k), requires_grad=True)
+    U = D.unfold2d(x, k, s, pad, dil)
+    for i in range(B):
+        out = F.conv2d(torch.tensor(x[i:i + 1]), Wt, stride=s, padding=pad, dilation=dil)
+        assert U.shape[1] == out.shape[2] * out.shape[3]
+        R = torch.tensor(rng.standard_normal(out.shape))
+        (gW,) = torch.autograd.grad((out * R).sum(), [Wt])
+        Gi = R[0].reshape(cout, -1).T.numpy()
+        np.testing.assert_allclose(D.per_example_weight_grad(U[i], Gi), gW.reshape(cout, -1).T.numpy(),
+                                   rtol=1e-10, atol=1e-10)
+
+
+@pytest.mark.parametrize("cin,H,Wd,k,s,pad,dil", CONV_GEOMETRIES)
+def test_unfold2d_matches_torch_unfold(cin, H, Wd, k, s, pad, dil):
+    """The unfolding is torch's im2col (F.unfold) laid out [B, T, d]; a
+    library routine of the same definition ([FPC] Algorithm 3)."""
+    x = np.random.default_rng(8).standard_normal((2, cin, H, Wd))
+    ref = F.unfold(torch.tensor(x), k, dilation=dil, padding=pad, stride=s).transpose(1, 2).numpy()
+    np.testing.assert_array_equal(D.unfold2d(x, k, s, pad, dil), ref)
+
+
+def test_unfold2d_closed_forms():
+    """A 1x1 kernel at stride 1 is the channel-last view of the input; with a
+    kernel as large as the padded input there is one row, the flattened padded
+    input. Checks the row count and the zero fill of the padding."""
+    x = np.random.default_rng(9).standard_normal((2, 3, 4, 5))
+    np.testing.assert_array_equal(D.unfold2d(x, (1, 1)), x.reshape(2, 3, 20).transpose(0, 2, 1))
+    U = D.unfold2d(x, (6, 7), padding=(1, 1))
+    padded = np.pad(x, ((0, 0), (0, 0), (1, 1), (1, 1)))
+    assert U.shape == (2, 1, 3 * 6 * 7)
+    np.testing.assert_array_equal(U[:, 0, :], padded.reshape(2, -1))
+
+
 # ---------------------------------------------------------------- P2/P3: identities
 @pytest.mark.parametrize("B,T,d,p", [(3, 1, 7, 5), (2, 17, 9, 4), (4, 33, 3, 40), (1, 5, 64, 2)])
 @pytest.mark.parametrize("has_bias", [False, True])
