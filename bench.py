@@ -69,14 +69,16 @@ def measured_traffic(kind, workload):
 MODES = {"space": 0, "time": 3}
 
 
-def _algorithmic(wl, T, d, p, kind, mode=0):
+def _algorithmic(wl, T, d, p, kind, mode=0, a_elems=None):
     """Algorithmic flops and bytes of one call on one layer (no re-reads, no
     intermediate buffers). ghost: unique Gram entries B*T(T+1)(d+p) + 2BT^2;
-    explicit: 2BTdp + 2Bdp; T = 1: 2B(d+p); contraction: 2BTdp."""
+    explicit: 2BTdp + 2Bdp; T = 1: 2B(d+p); contraction: 2BTdp. a_elems: the
+    elements of one sample's layer input when the call reads a folded conv
+    input (C_in*H*W) instead of the unfolded T*d."""
     B = wl.B
     eb = 2 if wl.dtype == "bf16" else 4
     hb = 1 if wl.has_bias else 0
-    inp = B * T * (d + p) * eb
+    inp = B * (T * d if a_elems is None else a_elems) * eb + B * T * p * eb
     if kind == "norm":
         if T == 1:
             return 2.0 * B * (d + p), inp + 4 * B
@@ -93,7 +95,7 @@ BREAKDOWN_STEPS = 50
 
 
 def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums=False, virtual_steps=1,
-            mode=0):
+            mode=0, implicit_conv=False):
     """Times `steps` whole steps of the workload after `warmup` untimed ones.
 
     Global clipping (one norm per example over all layers): every layer's
@@ -109,7 +111,9 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
     milliseconds (events on the stream) of the throughput steps, per-call
     event times [breakdown steps, calls], the kinds and layers of the calls,
     the number of rotated input sets and whether inputs were drawn on the
-    device."""
+    device. implicit_conv (conv workloads): the layers are given by their
+    folded inputs, one dp_conv_norm per layer into the global norm, the clip
+    factors, one dp_conv_clipped_sum_noise per layer."""
     import torch
     import sample_gradient_clipping_layer_amd as dpc
 
@@ -127,11 +131,21 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
             return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(x).to(dev)
 
+    geos = None
+    if implicit_conv:
+        geos = [dpc.conv_geometry(cin, h, w, 3, st, 1) for (cin, h, w, st) in wl.conv]
+        set_bytes = sum(B * (g.C_in * g.H * g.W + T * p) * eb for g, (T, d, p) in zip(geos, shapes))
+        n_sets = max(1, min(4, math.ceil(2 * CACHE_BYTES / set_bytes) + 1))
+        on_device = False
     sets = []
     for s in range(n_sets):
         layers = []
         for l in range(len(shapes)):
-            if on_device:
+            if implicit_conv:
+                fm, G = W.make_folded(wl, l, step=s)
+                layers.append((up(fm), up(G)))
+                del fm, G
+            elif on_device:
                 layers.append(W.make_layer_device(wl, l, dev, step=s))
             else:
                 A, G = W.make_layer(wl, l, step=s)
@@ -155,6 +169,9 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
     side = [torch.cuda.Stream(device=dev) for _ in range(nstreams)] if nstreams > 1 and not wl.per_layer else []
     ws_sum = ([torch.empty_like(w) for w in ws] if side else ws)
     L = len(shapes)
+    if implicit_conv:
+        ws = [torch.empty(max(256, dpc.dp_conv_workspace_bytes(g, dt, B, p, wl.has_bias, mode)), dtype=torch.uint8,
+                          device=dev) for g, (T, d, p) in zip(geos, shapes)]
 
     if wl.per_layer:
         sq = [torch.empty(B, dtype=torch.float32, device=dev) for _ in range(L)]
@@ -180,9 +197,12 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
         # the clip factors come out of the norm call when both calls are multi-layer
         clip_kinds = [] if not (per_layer_norms or per_layer_sums) else [("clip", -1)]
         kinds = norm_kinds + clip_kinds + sum_kinds
+        if implicit_conv:
+            kinds = [("norm", l) for l in range(L)] + [("clip", -1)] + [("sum", l) for l in range(L)]
         # one workspace for the multi-layer calls (they run one after another on the stream)
-        ws_layers = torch.empty(max(256, dpc.dp_layers_workspace_bytes(sets[0], has_bias=wl.has_bias, mode=mode)),
-                                dtype=torch.uint8, device=dev)
+        ws_layers = None if implicit_conv else torch.empty(
+            max(256, dpc.dp_layers_workspace_bytes(sets[0], has_bias=wl.has_bias, mode=mode)), dtype=torch.uint8,
+            device=dev)
         if virtual_steps > 1:
             # a logical batch of `virtual_steps` physical batches: per physical batch the norms, the
             # clip factors and each layer's clipped sum added to its accumulator; once per logical
@@ -229,6 +249,15 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
                 call(dpc.dp_adaptive_threshold, nrm[l], C_t[l], wl.alpha, wl.beta, wl.sigma_l2, False, wl.seed,
                      l, k + 1, C_next[l:l + 1])
             C_t = [float(v) for v in C_next.tolist()]
+            return
+        if implicit_conv:
+            for l, (a, G) in enumerate(layers):
+                call(dpc.dp_conv_norm, a, G, geos[l], sq, has_bias=wl.has_bias, mode=mode, accumulate=l > 0,
+                     workspace=ws[l])
+            call(dpc.dp_clip_factors, sq, wl.C, c)
+            for l, (a, G) in enumerate(layers):
+                call(dpc.dp_conv_clipped_sum_noise, a, G, geos[l], c, wl.C, wl.sigma, float(B), wl.seed, l, k,
+                     outs[l], bouts[l], workspace=ws[l])
             return
         if virtual_steps > 1:
             for v in range(virtual_steps):
@@ -315,7 +344,7 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
         assert torch.isfinite(o).all().item(), "non-finite output"
     if wl.per_layer:
         assert all(math.isfinite(v) and v > 0 for v in C_t), f"adaptive bounds {C_t}"
-    return wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device
+    return wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device, geos
 
 
 def cpu_baseline(wl, budget_s=12.0, step_s=3.0, max_step_s=25.0):
@@ -427,6 +456,8 @@ def main():
     ap.add_argument("--streams", type=int, default=None,
                     help="side streams for the layers' clipped sums in the throughput steps (global clipping); "
                          "default 3 for layer sets of at most 8 layers, else 1")
+    ap.add_argument("--implicit-conv", action="store_true",
+                    help="conv workloads: pass each layer's folded input (dp_conv_* calls) instead of its unfolding")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (HBM counter calibration)")
     a = ap.parse_args()
@@ -454,9 +485,14 @@ def main():
         sys.exit(2)
     if a.virtual_steps > 1:
         nstreams = 1
-    wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device = run_gpu(wl, a.steps, a.warmup, nstreams,
-                                                                      a.per_layer_norms, per_layer_sums,
-                                                                      a.virtual_steps, MODES[a.path_rule])
+    if a.implicit_conv:
+        if not wl.conv or a.virtual_steps > 1 or a.per_layer_norms or a.per_layer_sums:
+            print("--implicit-conv applies to conv workloads, alone", file=sys.stderr)
+            sys.exit(2)
+        nstreams, per_layer_sums = 1, True
+    wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device, geos = run_gpu(
+        wl, a.steps, a.warmup, nstreams, a.per_layer_norms, per_layer_sums, a.virtual_steps, MODES[a.path_rule],
+        a.implicit_conv)
     L = len(shapes)
     ms_per_step = 1e3 * wall / a.steps
     value = wl.B * a.virtual_steps * a.steps / wall
@@ -474,7 +510,8 @@ def main():
             continue
         for ll in (range(L) if l < 0 else (l,)):  # l < 0: one call over all layers
             T, d, p = shapes[ll]
-            f, b = _algorithmic(wl, T, d, p, kd, MODES[a.path_rule])
+            a_el = None if geos is None else geos[ll].C_in * geos[ll].H * geos[ll].W
+            f, b = _algorithmic(wl, T, d, p, kd, MODES[a.path_rule], a_el)
             flops += f
             byts += b
         t_ms += mean_ms[j]
@@ -489,13 +526,16 @@ def main():
         achieved = byts / (t_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
-    traffic = measured_traffic(dom, wl.name)
+    traffic = measured_traffic(dom, wl.name + ("-implicit-conv" if a.implicit_conv else ""))
     roof["traffic"] = None if traffic is None else round(traffic)
     roof["algorithmic_bytes_per_call"] = round(byts / ndom)
     roof["kernel"] = ("dp_ghost_norm[_layers]: k_ghost_tiles / k_ghost_wide / k_explicit_tiles / k_norm_t1"
                       if dom == "norm"
                       else "dp_clipped_sum_noise[_layers]: k_contract_dl (split tiles finished in-kernel), "
                            "k_contract_dl32 / k_contract_tiles (+ k_reduce_noise[_vec|_wide] when K is split)")
+    if a.implicit_conv:
+        roof["kernel"] = ("dp_conv_norm: k_ghost_tiles / k_explicit_tiles on folded inputs" if dom == "norm" else
+                          "dp_conv_clipped_sum_noise: k_contract_tiles on folded inputs (+ k_reduce_noise[_vec|_wide])")
     roof["avg_call_us"] = round(1e3 * t_ms / ndom, 2)
     if a.breakdown:
         for (kd, l), m in zip(kinds, mean_ms):
@@ -510,6 +550,9 @@ def main():
            "norm_call": "per-layer" if (wl.per_layer or a.per_layer_norms or L == 1) else "multi-layer",
            "sum_call": ("per-layer" if (wl.per_layer or per_layer_sums) else "multi-layer"),
            "sum_streams": nstreams, "path_rule": a.path_rule}
+    if a.implicit_conv:
+        cfg["conv_input"] = "folded [B, C_in, H, W]; unfolded rows formed in the kernels"
+        cfg["norm_call"] = cfg["sum_call"] = "per-layer (dp_conv_*)"
     if a.virtual_steps > 1:
         cfg["virtual_steps"] = a.virtual_steps
         cfg["logical_batch"] = wl.B * a.virtual_steps

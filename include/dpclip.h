@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DP_ABI_VERSION 2
+#define DP_ABI_VERSION 3
 
 typedef int32_t dp_status;
 #define DP_OK 0
@@ -307,6 +307,69 @@ dp_status dp_adaptive_threshold(void* stream, const float* norm, int64_t B, floa
                                 float alpha, float beta, float sigma_l2, int32_t init,
                                 uint64_t seed, uint32_t layer_id, uint32_t step,
                                 float* C_next, float* C_l2_out);
+
+/*
+ * Convolution layers from their folded input (implicit unfolding).
+ *
+ * SEDP Sec. 2.2 writes a 2-D convolution as a product with the unfolded
+ * input U(a_i): one row per output position (T = H_out*W_out rows), one
+ * column per (input channel, kernel row, kernel column), so d = C_in*kH*kW.
+ * The entry points below take the folded input a [B, C_in, H, W] instead of
+ * U(a) [B, T, d] and form U(a)'s rows on chip, element by element:
+ *
+ *   U(a)[b][t = ho*W_out + wo][f = (ci*kH + i)*kW + j]
+ *       = a[b][ci][ho*stride_h - pad_h + i*dil_h][wo*stride_w - pad_w + j*dil_w]
+ *         (0 where that position lies in the zero padding),
+ *   H_out = (H + 2*pad_h - dil_h*(kH-1) - 1) / stride_h + 1, likewise W_out,
+ *
+ * which is torch's unfold (and conv2d, groups = 1) layout. The unfolded input
+ * is never written to memory: a conv layer reads a, not kH*kW/(stride_h*stride_w)
+ * times as much. Results are those of dp_ghost_norm / dp_clipped_sum_noise on
+ * U(a) up to fp32 summation order.
+ */
+typedef struct dp_conv2d {
+  int64_t C_in, H, W;          /* folded input geometry */
+  int64_t kh, kw;              /* kernel size, >= 1 */
+  int64_t stride_h, stride_w;  /* >= 1 */
+  int64_t pad_h, pad_w;        /* zero padding, >= 0 */
+  int64_t dil_h, dil_w;        /* dilation, >= 1 */
+} dp_conv2d;
+
+/*
+ * dp_conv_norm: dp_ghost_norm of the layer (U(a), G).
+ *
+ *  a        [B, C_in, H, W] folded input, dtype as G, 4-byte aligned (fp32)
+ *           or 2-byte aligned (bf16); C_in*H*W < 2^31.
+ *  G        [B, T, p] output gradients (T = H_out*W_out, spatial positions
+ *           row-major), 16-byte aligned.
+ *  conv     host geometry; H_out, W_out >= 1; every size below 2^31.
+ *  dtype, B, p, has_bias, mode, kappa, sqnorm, accumulate  as in dp_ghost_norm,
+ *           with T and d of U(a). The path rule is dp_ghost_norm's; a T = 1
+ *           layer takes the ghost path (the closed form reads U(a) rows).
+ *  workspace, ws_bytes  at least dp_conv_workspace_bytes(...) bytes.
+ *  path_out host int (may be NULL): DP_PATH_* taken.
+ */
+dp_status dp_conv_norm(void* stream, const void* a, const void* G, const dp_conv2d* conv, dp_dtype dtype,
+                       int64_t B, int64_t p, int32_t has_bias, dp_mode mode, int32_t kappa,
+                       void* workspace, size_t ws_bytes, float* sqnorm, int32_t accumulate, int32_t* path_out);
+
+/*
+ * dp_conv_clipped_sum_noise: dp_clipped_sum_noise of the layer (U(a), G):
+ * out [d, p] fp32 with d = C_in*kH*kW in U(a)'s column order (torch's
+ * weight.grad [p, C_in, kH, kW] transposed), bias_out [p] or NULL; c, C,
+ * sigma, denom, seed, layer_id, step and the noise as in dp_clipped_sum_noise.
+ * a, G, conv, dtype, B, p as in dp_conv_norm.
+ */
+dp_status dp_conv_clipped_sum_noise(void* stream, const void* a, const void* G, const dp_conv2d* conv,
+                                    dp_dtype dtype, int64_t B, int64_t p, const float* c, float C, float sigma,
+                                    float denom, uint64_t seed, uint32_t layer_id, uint32_t step,
+                                    void* workspace, size_t ws_bytes, float* out, float* bias_out);
+
+/* Workspace bytes that dp_conv_norm (with this mode and kappa) and
+ * dp_conv_clipped_sum_noise need for this layer (the larger of the two).
+ * Returns 0 for invalid arguments. */
+size_t dp_conv_workspace_bytes(const dp_conv2d* conv, dp_dtype dtype, int64_t B, int64_t p, int32_t has_bias,
+                               dp_mode mode, int32_t kappa);
 
 /* Workspace bytes that dp_ghost_norm and dp_clipped_sum_noise need for this
  * layer shape (the larger of the two). Returns 0 for invalid arguments. */

@@ -27,6 +27,15 @@ The functions mirror the C ABI in ``include/dpclip.h``:
                           layer_id, step, C_next, C_l2_out=None)
     dp_workspace_bytes(dtype, B, T, d, p, mode=MODE_MIXED, kappa=1) -> int
     dp_choose_path(T, d, p, mode=MODE_MIXED, kappa=1) -> int
+    dp_conv_norm(a, G, conv, sqnorm, has_bias=False, mode=MODE_MIXED, kappa=1,
+                 accumulate=False, workspace=None) -> path
+    dp_conv_clipped_sum_noise(a, G, conv, c, C, sigma, denom, seed, layer_id, step, out,
+                              bias_out=None, workspace=None)
+    dp_conv_workspace_bytes(conv, dtype, B, p, has_bias=False, mode=MODE_MIXED, kappa=1) -> int
+
+The dp_conv_* calls take a convolution layer's folded input a [B, C_in, H, W]
+and its geometry (``conv_geometry(C_in, H, W, kernel_size, stride, padding,
+dilation)``); the unfolded rows are formed inside the kernels.
 
 A and G are contiguous [B, T, d] / [B, T, p] tensors (float32 or bfloat16) on
 the current GPU; norm, factor and output vectors are float32. Every call also
@@ -49,7 +58,8 @@ PATH_GHOST, PATH_EXPLICIT, PATH_T1 = 1, 2, 3
 EXPORTS = ("dp_ghost_norm", "dp_ghost_norm_layers", "dp_ghost_norm_clip_layers", "dp_layers_workspace_bytes", "dp_clipped_sum_noise_layers",
            "dp_clip_factors", "dp_clipped_sum_accumulate", "dp_noise_mean", "dp_accumulate_workspace_bytes",
            "dp_clipped_sum_accumulate_layers", "dp_layers_accumulate_workspace_bytes", "dp_clipped_sum_noise", "dp_adaptive_threshold",
-           "dp_workspace_bytes", "dp_choose_path", "dp_status_string", "dp_abi_version")
+           "dp_workspace_bytes", "dp_choose_path", "dp_status_string", "dp_abi_version",
+           "dp_conv_norm", "dp_conv_clipped_sum_noise", "dp_conv_workspace_bytes")
 
 _lib = None
 
@@ -58,6 +68,26 @@ class DpLayer(ctypes.Structure):
     """struct dp_layer of the C ABI."""
     _fields_ = [("A", ctypes.c_void_p), ("G", ctypes.c_void_p), ("T", ctypes.c_int64), ("d", ctypes.c_int64),
                 ("p", ctypes.c_int64), ("has_bias", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class DpConv2d(ctypes.Structure):
+    """struct dp_conv2d of the C ABI."""
+    _fields_ = [(n, ctypes.c_int64) for n in ("C_in", "H", "W", "kh", "kw", "stride_h", "stride_w", "pad_h", "pad_w",
+                                              "dil_h", "dil_w")]
+
+
+def conv_geometry(C_in, H, W, kernel_size, stride=1, padding=0, dilation=1) -> DpConv2d:
+    """DpConv2d from torch-style Conv2d arguments (ints or pairs)."""
+    pair = lambda v: (int(v), int(v)) if isinstance(v, int) else (int(v[0]), int(v[1]))
+    (kh, kw), (sh, sw), (ph, pw), (dh, dw) = pair(kernel_size), pair(stride), pair(padding), pair(dilation)
+    return DpConv2d(int(C_in), int(H), int(W), kh, kw, sh, sw, ph, pw, dh, dw)
+
+
+def conv_out_shape(g: DpConv2d):
+    """(T, d) of the unfolded input U(a): T = H_out*W_out rows, d = C_in*kh*kw columns."""
+    Ho = (g.H + 2 * g.pad_h - g.dil_h * (g.kh - 1) - 1) // g.stride_h + 1
+    Wo = (g.W + 2 * g.pad_w - g.dil_w * (g.kw - 1) - 1) // g.stride_w + 1
+    return Ho * Wo, g.C_in * g.kh * g.kw
 
 
 class DpError(RuntimeError):
@@ -110,6 +140,15 @@ def _declare(lib):
     lib.dp_choose_path.restype = c_i32
     lib.dp_status_string.argtypes = [c_i32]
     lib.dp_status_string.restype = ctypes.c_char_p
+    cp = ctypes.POINTER(DpConv2d)
+    lib.dp_conv_norm.argtypes = [vp, vp, vp, cp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32, vp, ctypes.c_size_t, fp,
+                                 c_i32, ctypes.POINTER(c_i32)]
+    lib.dp_conv_norm.restype = c_i32
+    lib.dp_conv_clipped_sum_noise.argtypes = [vp, vp, vp, cp, c_i32, c_i64, c_i64, fp, f, f, f, c_u64, c_u32, c_u32,
+                                              vp, ctypes.c_size_t, fp, fp]
+    lib.dp_conv_clipped_sum_noise.restype = c_i32
+    lib.dp_conv_workspace_bytes.argtypes = [cp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32]
+    lib.dp_conv_workspace_bytes.restype = ctypes.c_size_t
     lib.dp_abi_version.argtypes = []
     lib.dp_abi_version.restype = c_i32
     return lib
@@ -408,3 +447,68 @@ def dp_adaptive_threshold(norm, C_prev: float, alpha: float, beta: float, sigma_
         _stream(stream), _ptr(norm), norm.numel(), float(C_prev), float(alpha), float(beta), float(sigma_l2),
         int(bool(init)), int(seed) & 0xFFFFFFFFFFFFFFFF, int(layer_id) & 0xFFFFFFFF, int(step) & 0xFFFFFFFF,
         _ptr(C_next), _ptr(C_l2_out)))
+
+
+def _conv_layer(a, G, conv: DpConv2d):
+    """(dtype, B, T, d, p) of a conv layer given by its folded input a [B, C_in, H, W]."""
+    if a.dim() != 4 or G.dim() != 3 or a.shape[0] != G.shape[0]:
+        raise ValueError(f"a [B,C_in,H,W] and G [B,T,p] expected, got {tuple(a.shape)} and {tuple(G.shape)}")
+    if tuple(a.shape[1:]) != (conv.C_in, conv.H, conv.W):
+        raise ValueError("a's shape does not match the geometry")
+    T, d = conv_out_shape(conv)
+    if G.shape[1] != T:
+        raise ValueError(f"G must have T = H_out*W_out = {T} rows per sample")
+    if a.dtype != G.dtype:
+        raise TypeError("a and G must share one dtype")
+    if not (a.is_contiguous() and G.is_contiguous() and a.is_cuda and G.is_cuda):
+        raise ValueError("a and G must be contiguous GPU tensors")
+    return _dtype_code(a), int(a.shape[0]), T, d, int(G.shape[2])
+
+
+def dp_conv_workspace_bytes(conv: DpConv2d, dtype: int, B: int, p: int, has_bias: bool = False,
+                            mode: int = MODE_MIXED, kappa: int = 1) -> int:
+    return int(lib().dp_conv_workspace_bytes(ctypes.byref(conv), dtype, B, p, int(bool(has_bias)), int(mode),
+                                             int(kappa)))
+
+
+def _conv_ws(workspace, conv, dt, B, p, has_bias, mode, kappa, device):
+    import torch
+    if workspace is None:
+        need = dp_conv_workspace_bytes(conv, dt, B, p, has_bias, mode, kappa)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def dp_conv_norm(a, G, conv: DpConv2d, sqnorm, has_bias: bool = False, mode: int = MODE_MIXED, kappa: int = 1,
+                 accumulate: bool = False, workspace=None, stream=None) -> int:
+    """Per-sample squared norms of a conv layer from its folded input a
+    [B, C_in, H, W] and G [B, T, p] into sqnorm; returns the path taken."""
+    dt, B, T, d, p = _conv_layer(a, G, conv)
+    _f32_vec(sqnorm, "sqnorm")
+    if sqnorm.numel() != B:
+        raise ValueError("sqnorm must have B elements")
+    ws, nbytes = _conv_ws(workspace, conv, dt, B, p, has_bias, mode, kappa, a.device)
+    path = ctypes.c_int32(0)
+    _check("dp_conv_norm", lib().dp_conv_norm(_stream(stream), _ptr(a), _ptr(G), ctypes.byref(conv), dt, B, p,
+                                              int(bool(has_bias)), int(mode), int(kappa), _ptr(ws), nbytes,
+                                              _ptr(sqnorm), int(bool(accumulate)), ctypes.byref(path)))
+    return path.value
+
+
+def dp_conv_clipped_sum_noise(a, G, conv: DpConv2d, c, C: float, sigma: float, denom: float, seed: int,
+                              layer_id: int, step: int, out, bias_out=None, workspace=None, stream=None):
+    """Clipped noised mean of a conv layer from its folded input into out ([d, p])."""
+    dt, B, T, d, p = _conv_layer(a, G, conv)
+    _f32_vec(c, "c")
+    _f32_vec(out, "out")
+    if c.numel() != B or out.numel() != d * p:
+        raise ValueError("c must have B elements and out d*p")
+    if bias_out is not None:
+        _f32_vec(bias_out, "bias_out")
+        if bias_out.numel() != p:
+            raise ValueError("bias_out must have p elements")
+    ws, nbytes = _conv_ws(workspace, conv, dt, B, p, bias_out is not None, MODE_MIXED, 1, a.device)
+    _check("dp_conv_clipped_sum_noise", lib().dp_conv_clipped_sum_noise(
+        _stream(stream), _ptr(a), _ptr(G), ctypes.byref(conv), dt, B, p, _ptr(c), float(C), float(sigma),
+        float(denom), int(seed) & 0xFFFFFFFFFFFFFFFF, int(layer_id) & 0xFFFFFFFF, int(step) & 0xFFFFFFFF, _ptr(ws),
+        nbytes, _ptr(out), _ptr(bias_out)))

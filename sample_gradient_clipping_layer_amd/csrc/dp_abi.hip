@@ -281,6 +281,67 @@ size_t sum_layers_ws_bytes(const dp_layer* layers, int32_t n, dp_dtype dtype, in
   return w;
 }
 
+// ---- convolution layers given by their folded input
+constexpr int64_t kMaxConv = (int64_t)1 << 31;
+
+// Geometry, shapes and limits of a folded-input convolution layer: every size
+// >= 1 (padding >= 0) and below 2^31, one sample's folded input and the
+// window offsets within 32-bit indexing, and the unfolded shape (T, d) within
+// dp_ghost_norm's limits.
+dp_status check_conv(const void* a, const void* G, const dp_conv2d* cv, dp_dtype dtype, int64_t B, int64_t p,
+                     dpk::ConvGeo* geo) {
+  if (!a || !G || !cv) return DP_ERR_NULL;
+  if (dtype != DP_F32 && dtype != DP_BF16) return DP_ERR_DTYPE;
+  const int64_t v[] = {cv->C_in, cv->H, cv->W, cv->kh, cv->kw, cv->stride_h, cv->stride_w, cv->dil_h, cv->dil_w};
+  for (int64_t x : v)
+    if (x < 1 || x >= kMaxConv) return DP_ERR_SHAPE;
+  if (cv->pad_h < 0 || cv->pad_w < 0 || cv->pad_h >= kMaxConv || cv->pad_w >= kMaxConv) return DP_ERR_SHAPE;
+  if (cv->C_in * cv->H >= kMaxConv || cv->C_in * cv->H * cv->W >= kMaxConv) return DP_ERR_SHAPE;
+  if (cv->kh * cv->kw >= kMaxConv || cv->C_in * cv->kh * cv->kw >= kMaxConv) return DP_ERR_SHAPE;
+  const int64_t span_h = cv->dil_h * (cv->kh - 1) + 1, span_w = cv->dil_w * (cv->kw - 1) + 1;
+  const int64_t ext_h = cv->H + 2 * cv->pad_h, ext_w = cv->W + 2 * cv->pad_w;
+  if (span_h > ext_h || span_w > ext_w || ext_h >= kMaxConv || ext_w >= kMaxConv) return DP_ERR_SHAPE;
+  const int64_t Ho = (ext_h - span_h) / cv->stride_h + 1, Wo = (ext_w - span_w) / cv->stride_w + 1;
+  // window positions ho*stride - pad + i*dil, and Ho*Wo, within int32
+  if ((Ho - 1) * cv->stride_h + span_h >= kMaxConv || (Wo - 1) * cv->stride_w + span_w >= kMaxConv) return DP_ERR_SHAPE;
+  if (Ho * Wo >= kMaxConv) return DP_ERR_SHAPE;
+  const int64_t T = Ho * Wo, d = cv->C_in * cv->kh * cv->kw;
+  dp_status s = check_shape(B, T, d, p);
+  if (s != DP_OK) return s;
+  const uintptr_t eb = dtype == DP_BF16 ? 2 : 4;
+  if (!aligned(a, eb) || !aligned(G, 16)) return DP_ERR_ALIGN;
+  if (geo) {
+    *geo = dpk::ConvGeo{a, (int32_t)cv->C_in, (int32_t)cv->H, (int32_t)cv->W, (int32_t)cv->kh, (int32_t)cv->kw,
+                        (int32_t)cv->stride_h, (int32_t)cv->stride_w, (int32_t)cv->pad_h, (int32_t)cv->pad_w,
+                        (int32_t)cv->dil_h, (int32_t)cv->dil_w, (int32_t)Wo, (int32_t)T, (int32_t)d};
+  }
+  return DP_OK;
+}
+
+// The path of a folded-input conv layer: dp_ghost_norm's rule, with the
+// ghost kernel for T = 1 (the closed form reads unfolded rows).
+int conv_path(int64_t T, int64_t d, int64_t p, dp_mode mode, int32_t kappa) {
+  const int path = path_of(T, d, p, mode, kappa);
+  return path == DP_PATH_T1 ? DP_PATH_GHOST : path;
+}
+
+int64_t conv_norm_ntiles(int path, int64_t T, int64_t d, int64_t p, int has_bias) {
+  if (path == DP_PATH_GHOST) return dpk::ghost_tiled_ntiles(T);
+  const dpk::ExplicitPlan pl = dpk::explicit_plan(d, p, has_bias);
+  return (int64_t)pl.mt * pl.nt;
+}
+
+size_t conv_norm_ws_bytes(int path, int64_t B, int64_t T, int64_t d, int64_t p, int has_bias) {
+  const int64_t nt = conv_norm_ntiles(path, T, d, p, has_bias);
+  if (nt == 1) return 0;
+  return norm_partial_bytes(B, nt) + round256((size_t)B * sizeof(unsigned long long));
+}
+
+size_t conv_sum_ws_bytes(const dpk::ContractPlan& pl, int64_t d, int64_t p, int has_bias) {
+  if (pl.ks == 1) return 0;
+  return round256((size_t)pl.ks * (size_t)(d + (has_bias ? 1 : 0)) * (size_t)p * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -545,6 +606,78 @@ dp_status dp_clipped_sum_noise(void* stream, const void* A, const void* G, dp_dt
   const float sc = sigma * C;
   return hip_status(dpk::launch_clipped_sum(st, dtype, A, G, c, B, T, d, p, pl, static_cast<float*>(workspace), sc,
                                             denom, seed, layer_id, step, out, bias_out));
+}
+
+size_t dp_conv_workspace_bytes(const dp_conv2d* conv, dp_dtype dtype, int64_t B, int64_t p, int32_t has_bias,
+                               dp_mode mode, int32_t kappa) {
+  alignas(16) static const float probe[4] = {};  // stands in for the data pointers: only the shapes are checked
+  dpk::ConvGeo g;
+  if (!conv || check_conv(probe, probe, conv, dtype, B, p, &g) != DP_OK) return 0;
+  if (mode < DP_MODE_MIXED || mode > DP_MODE_TIME || kappa < 1) return 0;
+  const int hb = has_bias ? 1 : 0;
+  const size_t a = conv_norm_ws_bytes(conv_path(g.T, g.d, p, mode, kappa), B, g.T, g.d, p, hb);
+  const size_t b = conv_sum_ws_bytes(dpk::tiles_plan(dtype, B, g.T, g.d, p, hb), g.d, p, hb);
+  return std::max(a, b);
+}
+
+dp_status dp_conv_norm(void* stream, const void* a, const void* G, const dp_conv2d* conv, dp_dtype dtype, int64_t B,
+                       int64_t p, int32_t has_bias, dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes,
+                       float* sqnorm, int32_t accumulate, int32_t* path_out) {
+  dpk::ConvGeo g;
+  dp_status s = check_conv(a, G, conv, dtype, B, p, &g);
+  if (s != DP_OK) return s;
+  if (!sqnorm) return DP_ERR_NULL;
+  if (!aligned(sqnorm, 4)) return DP_ERR_ALIGN;
+  if (mode < DP_MODE_MIXED || mode > DP_MODE_TIME || kappa < 1) return DP_ERR_VALUE;
+  const int hb = has_bias ? 1 : 0;
+  const int path = conv_path(g.T, g.d, p, mode, kappa);
+  const int64_t nt = conv_norm_ntiles(path, g.T, g.d, p, hb);
+  if (nt > kMaxTilesPerSample) return DP_ERR_SHAPE;
+  if (path == DP_PATH_GHOST && (uint64_t)((B + 7) / 8 * 8) * (uint64_t)nt >= (1ull << 32)) return DP_ERR_SHAPE;
+  const size_t need = conv_norm_ws_bytes(path, B, g.T, g.d, p, hb);
+  if (need > 0) {
+    if (!workspace) return DP_ERR_NULL;
+    if (ws_bytes < need) return DP_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return DP_ERR_ALIGN;
+  }
+  s = device_ready();
+  if (s != DP_OK) return s;
+  if (path_out) *path_out = path;
+  const dpk::NormSink sink = dpk::make_norm_sink(
+      static_cast<float*>(workspace),
+      nt > 1 ? reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(workspace) + norm_partial_bytes(B, nt))
+             : nullptr,
+      sqnorm, (int)nt, accumulate ? 1 : 0, dpk::next_epoch());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (path == DP_PATH_GHOST) return hip_status(dpk::launch_ghost_conv(st, dtype, g, G, B, p, hb, sink));
+  return hip_status(dpk::launch_explicit_conv(st, dtype, g, G, B, p, hb, sink));
+}
+
+dp_status dp_conv_clipped_sum_noise(void* stream, const void* a, const void* G, const dp_conv2d* conv, dp_dtype dtype,
+                                    int64_t B, int64_t p, const float* c, float C, float sigma, float denom,
+                                    uint64_t seed, uint32_t layer_id, uint32_t step, void* workspace, size_t ws_bytes,
+                                    float* out, float* bias_out) {
+  dpk::ConvGeo g;
+  dp_status s = check_conv(a, G, conv, dtype, B, p, &g);
+  if (s != DP_OK) return s;
+  if (!c || !out) return DP_ERR_NULL;
+  if (!aligned(c, 4) || !aligned(out, 4) || (bias_out && !aligned(bias_out, 4))) return DP_ERR_ALIGN;
+  if (!finite(C) || !(C > 0.0f) || !finite(sigma) || sigma < 0.0f || !finite(denom) || !(denom > 0.0f))
+    return DP_ERR_VALUE;
+  const int hb = bias_out ? 1 : 0;
+  const dpk::ContractPlan pl = dpk::tiles_plan(dtype, B, g.T, g.d, p, hb);
+  const size_t need = conv_sum_ws_bytes(pl, g.d, p, hb);
+  if (need > 0) {
+    if (!workspace) return DP_ERR_NULL;
+    if (ws_bytes < need) return DP_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return DP_ERR_ALIGN;
+  }
+  if ((int64_t)pl.mt * pl.nt * pl.ks >= ((int64_t)1 << 31)) return DP_ERR_SHAPE;
+  s = device_ready();
+  if (s != DP_OK) return s;
+  return hip_status(dpk::launch_clipped_sum_conv(static_cast<hipStream_t>(stream), dtype, g, G, c, B, p, pl,
+                                                 static_cast<float*>(workspace), sigma * C, denom, seed, layer_id,
+                                                 step, out, bias_out));
 }
 
 size_t dp_layers_accumulate_workspace_bytes(const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B) {

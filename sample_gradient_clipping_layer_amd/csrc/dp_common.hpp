@@ -100,6 +100,69 @@ __device__ __forceinline__ u32x4 load16_rowmajor(const T* __restrict__ X, int64_
   return r;
 }
 
+// A 2-D convolution layer given by its folded input a [B, Cin, H, W]: row t of
+// sample b's unfolded input U(a) (t = ho*Wo + wo) holds, in column
+// f = (ci*KH + i)*KW + j, a[b][ci][ho*sh - ph + i*dh][wo*sw - pw + j*dw], or 0
+// in the zero padding ("Scalable and Efficient Training of Large CNNs with
+// DP", Sec. 2.2, the unfolding U). T = Ho*Wo rows, d = Cin*KH*KW columns.
+// Every size and per-sample offset fits 32 bits (checked by the host).
+struct ConvGeo {
+  const void* a;
+  int32_t Cin, H, W, KH, KW, sh, sw, ph, pw, dh, dw, Wo, T, d;
+};
+
+// Column f0 of U(a) as (channel, kernel row, kernel column).
+struct ConvCol {
+  int ci, i, j;
+};
+__device__ __forceinline__ ConvCol conv_col(const ConvGeo& g, int64_t f0) {
+  const uint32_t f = (uint32_t)f0, khw = (uint32_t)(g.KH * g.KW);
+  const uint32_t ci = f / khw, r = f - ci * khw;
+  const uint32_t i = r / (uint32_t)g.KW;
+  return ConvCol{(int)ci, (int)i, (int)(r - i * (uint32_t)g.KW)};
+}
+
+// Elements [f0, f0 + per16) of row t of sample b's U(a) as one 16-byte
+// vector (c0 = conv_col(g, f0)): zero in the padding, past column d, and
+// everywhere when !row_ok; column ones_col (if >= 0) reads 1.
+template <typename T>
+__device__ __forceinline__ u32x4 conv_row16(const ConvGeo& g, int64_t b, int t, ConvCol c0, int64_t f0, bool row_ok,
+                                            int64_t ones_col) {
+  constexpr int P = elem_traits<T>::per16;
+  constexpr uint32_t one_bits = P == 8 ? 0x3F80u : 0x3F800000u;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (row_ok) {
+    const int ho = (int)((uint32_t)t / (uint32_t)g.Wo);
+    const int wo = t - ho * g.Wo;
+    const int y0 = ho * g.sh - g.ph, x0 = wo * g.sw - g.pw;
+    const T* __restrict__ ab = static_cast<const T*>(g.a) + b * (int64_t)g.Cin * g.H * g.W;
+    int ci = c0.ci, i = c0.i, j = c0.j;
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      const int64_t f = f0 + e;
+      uint32_t bits = 0u;
+      if (f < g.d) {
+        const int y = y0 + i * g.dh, x = x0 + j * g.dw;
+        if ((unsigned)y < (unsigned)g.H && (unsigned)x < (unsigned)g.W) bits = raw_bits(ab[(ci * g.H + y) * g.W + x]);
+      } else if (f == ones_col) {
+        bits = one_bits;
+      }
+      if constexpr (P == 8)
+        w[e >> 1] |= bits << (16 * (e & 1));
+      else
+        w[e] = bits;
+      if (++j == g.KW) {
+        j = 0;
+        if (++i == g.KH) {
+          i = 0;
+          ++ci;
+        }
+      }
+    }
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // D += A * B on one 32x32 output block, K = 16 (bf16 inputs).

@@ -83,6 +83,9 @@ ExplicitPlan explicit_plan(int64_t d, int64_t p, int has_bias);
 int ghost_tile_size(int64_t T);
 // Gram tiles per sample of the ghost kernel that dp_ghost_norm runs for this layer
 int64_t ghost_ntiles(int dtype, int64_t T, int64_t d, int64_t p);
+// Gram tiles per sample of the tiled ghost kernel (the kernel convolution
+// layers given by their folded input take, whatever the shape).
+int64_t ghost_tiled_ntiles(int64_t T);
 // bf16 long-sequence ghost engine (256 x 128 Gram tiles, direct-to-LDS)
 bool ghost_wide_eligible(int dtype, int64_t Tn, int64_t d, int64_t p);
 int64_t ghost_wide_ntiles(int64_t Tn);
@@ -118,6 +121,17 @@ hipError_t launch_explicit(hipStream_t st, int dtype, const void* A, const void*
 uint64_t next_epoch();
 // Weighted contraction + noise + 1/denom: one kernel when pl.ks == 1, else
 // partial tiles in ws and a reduce kernel. bias_out != nullptr <=> bias row.
+// Convolution layers given by their folded input (ConvGeo): the unfolded
+// rows are formed on chip by the tiled ghost, explicit and register-staged
+// contraction kernels; G is [B, geo.T, p]. The contraction plan is tiles_plan.
+ContractPlan tiles_plan(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias);
+hipError_t launch_ghost_conv(hipStream_t st, int dtype, const ConvGeo& geo, const void* G, int64_t B, int64_t p,
+                             int has_bias, const NormSink& sink);
+hipError_t launch_explicit_conv(hipStream_t st, int dtype, const ConvGeo& geo, const void* G, int64_t B, int64_t p,
+                                int has_bias, const NormSink& sink);
+hipError_t launch_clipped_sum_conv(hipStream_t st, int dtype, const ConvGeo& geo, const void* G, const float* c,
+                                   int64_t B, int64_t p, const ContractPlan& pl, float* ws, float sc, float denom,
+                                   uint64_t seed, uint32_t layer, uint32_t step, float* out, float* bias_out);
 hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const void* G, const float* c, int64_t B,
                               int64_t Tn, int64_t d, int64_t p, const ContractPlan& pl, float* ws, float sc,
                               float denom, uint64_t seed, uint32_t layer, uint32_t step, float* out,

@@ -124,6 +124,29 @@ __device__ __forceinline__ void ghost_load(typename GhostCfg<T, TS>::Regs& regs,
   }
 }
 
+// ghost_load of a chunk of A_i = U(a_i), the unfolded input of convolution
+// `g`, formed from sample i of its folded input.
+template <typename T, int TS>
+__device__ __forceinline__ void ghost_load_conv(typename GhostCfg<T, TS>::Regs& regs, const ConvGeo& g, int64_t i,
+                                                int sb, int tb, int64_t chunk) {
+  using Cfg = GhostCfg<T, TS>;
+  const bool diag = (sb == tb);
+#pragma unroll
+  for (int r = 0; r < Cfg::PPT; ++r) {
+    const int q = threadIdx.x + r * Cfg::NT;
+    const int h = q / (TS * Cfg::V);
+    const int row = (q / Cfg::V) % TS;
+    const int c16 = q % Cfg::V;
+    if (diag && h == 1) {
+      regs.v[r] = u32x4{0u, 0u, 0u, 0u};
+    } else {
+      const int grow = (h == 0 ? sb : tb) * TS + row;
+      const int64_t col = chunk * Cfg::KC + c16 * Cfg::P;
+      regs.v[r] = conv_row16<T>(g, i, grow, conv_col(g, col), col, grow < g.T, -1);
+    }
+  }
+}
+
 template <typename T, int TS>
 __device__ __forceinline__ void ghost_store(const typename GhostCfg<T, TS>::Regs& regs, unsigned char* buf, bool diag) {
   using Cfg = GhostCfg<T, TS>;
@@ -281,9 +304,10 @@ template <typename T>
 struct GhostGroup {
   GhostLayer<T> L[kNormGroupMax];
   int n;
+  ConvGeo conv;  // IM2COL launches (one layer): A_i is formed from conv's folded input
 };
 
-template <typename T, int TS>
+template <typename T, int TS, bool IM2COL>
 __global__ __launch_bounds__((GhostCfg<T, TS>::NT)) void k_ghost_tiles(GhostGroup<T> grp, int64_t B, NormSink sink) {
   using Cfg = GhostCfg<T, TS>;
   constexpr int NB = Cfg::NB;
@@ -324,9 +348,10 @@ __global__ __launch_bounds__((GhostCfg<T, TS>::NT)) void k_ghost_tiles(GhostGrou
         acc_g[bi][bj][j] = 0.f;
       }
 
-  const T* Ai = A + i * Tn * d;
+  const T* Ai = IM2COL ? A : A + i * Tn * d;
   const T* Gi = G + i * Tn * p;
-  const bool full = vecA && vecG && (int64_t)(tb + 1) * TS <= Tn && d % Cfg::KC == 0 && p % Cfg::KC == 0;
+  const bool full =
+      !IM2COL && vecA && vecG && (int64_t)(tb + 1) * TS <= Tn && d % Cfg::KC == 0 && p % Cfg::KC == 0;
   if (full && sb == tb) {
     GhostFull<T, TS, true>::run(Ai, Gi, d, p, sb, tb, lds, acc_a, acc_g);
   } else if (full) {
@@ -336,15 +361,21 @@ __global__ __launch_bounds__((GhostCfg<T, TS>::NT)) void k_ghost_tiles(GhostGrou
   const int64_t nG = (p + Cfg::KC - 1) / Cfg::KC;
   const int64_t n = nA + nG;
   typename Cfg::Regs regs;
-  ghost_load<T, TS>(regs, Ai, Tn, d, vecA != 0, sb, tb, 0);
+  if constexpr (IM2COL)
+    ghost_load_conv<T, TS>(regs, grp.conv, i, sb, tb, 0);
+  else
+    ghost_load<T, TS>(regs, Ai, Tn, d, vecA != 0, sb, tb, 0);
   for (int64_t c = 0; c < n; ++c) {
     unsigned char* buf = lds + (c & 1) * Cfg::BUF;
     ghost_store<T, TS>(regs, buf, diag);
     __syncthreads();
     const int64_t cn = c + 1;
-    if (cn < nA)
-      ghost_load<T, TS>(regs, Ai, Tn, d, vecA != 0, sb, tb, cn);
-    else if (cn < n)
+    if (cn < nA) {
+      if constexpr (IM2COL)
+        ghost_load_conv<T, TS>(regs, grp.conv, i, sb, tb, cn);
+      else
+        ghost_load<T, TS>(regs, Ai, Tn, d, vecA != 0, sb, tb, cn);
+    } else if (cn < n)
       ghost_load<T, TS>(regs, Gi, Tn, p, vecG != 0, sb, tb, cn - nA);
     if (c < nA)
       ghost_compute<T, TS>(buf, diag, acc_a);
@@ -431,11 +462,15 @@ hipError_t launch_norm_t1(hipStream_t st, int dtype, const void* A, const void* 
 
 int ghost_tile_size(int64_t T) { return T <= 384 ? 64 : 128; }
 
-int64_t ghost_ntiles(int dtype, int64_t T, int64_t d, int64_t p) {
-  if (ghost_wide_eligible(dtype, T, d, p)) return ghost_wide_ntiles(T);
+int64_t ghost_tiled_ntiles(int64_t T) {
   const int64_t ts = ghost_tile_size(T);
   const int64_t nb = (T + ts - 1) / ts;
   return nb * (nb + 1) / 2;
+}
+
+int64_t ghost_ntiles(int dtype, int64_t T, int64_t d, int64_t p) {
+  if (ghost_wide_eligible(dtype, T, d, p)) return ghost_wide_ntiles(T);
+  return ghost_tiled_ntiles(T);
 }
 
 template <typename T>
@@ -459,7 +494,8 @@ static GhostLayer<T> ghost_layer(const GhostLayerDesc& x, int ts) {
 // tiles start first and the short ones fill the tail); tile_base follows the
 // caller's order, which is the order of the sink's fold.
 template <typename T, int TS>
-hipError_t launch_ghost_t(hipStream_t st, const GhostLayerDesc* layers, int n, int64_t B, const NormSink& sink) {
+hipError_t launch_ghost_t(hipStream_t st, const GhostLayerDesc* layers, int n, int64_t B, const NormSink& sink,
+                          const ConvGeo* conv = nullptr) {
   GhostGroup<T> grp{};
   int order[kNormGroupMax];
   int base = 0;
@@ -486,11 +522,20 @@ hipError_t launch_ghost_t(hipStream_t st, const GhostLayerDesc* layers, int n, i
   }
   sorted.n = n;
   const size_t lds_bytes = 2 * GhostCfg<T, TS>::BUF;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ghost_tiles<T, TS>),
+  if (conv) {
+    sorted.conv = *conv;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ghost_tiles<T, TS, true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_ghost_tiles<T, TS, true>), dim3((unsigned)wg), dim3(GhostCfg<T, TS>::NT), lds_bytes, st,
+                       sorted, B, sink);
+    return hipGetLastError();
+  }
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ghost_tiles<T, TS, false>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_ghost_tiles<T, TS>), dim3((unsigned)wg), dim3(GhostCfg<T, TS>::NT), lds_bytes, st, sorted, B,
-                     sink);
+  hipLaunchKernelGGL((k_ghost_tiles<T, TS, false>), dim3((unsigned)wg), dim3(GhostCfg<T, TS>::NT), lds_bytes, st,
+                     sorted, B, sink);
   return hipGetLastError();
 }
 
@@ -517,6 +562,18 @@ hipError_t launch_ghost(hipStream_t st, int dtype, const void* A, const void* G,
   if (ghost_wide_eligible(dtype, Tn, d, p)) return launch_ghost_wide(st, A, G, B, Tn, d, p, has_bias, sink);
   const GhostLayerDesc x{A, G, Tn, d, p, has_bias};
   return launch_ghost_group(st, dtype, &x, 1, B, sink);
+}
+
+hipError_t launch_ghost_conv(hipStream_t st, int dtype, const ConvGeo& geo, const void* G, int64_t B, int64_t p,
+                             int has_bias, const NormSink& sink) {
+  const GhostLayerDesc x{geo.a, G, geo.T, geo.d, p, has_bias};
+  const int ts = ghost_tile_size(geo.T);
+  if (dtype == 1) {
+    if (ts == 64) return launch_ghost_t<bf16s, 64>(st, &x, 1, B, sink, &geo);
+    return launch_ghost_t<bf16s, 128>(st, &x, 1, B, sink, &geo);
+  }
+  if (ts == 64) return launch_ghost_t<float, 64>(st, &x, 1, B, sink, &geo);
+  return launch_ghost_t<float, 128>(st, &x, 1, B, sink, &geo);
 }
 
 static std::atomic<uint64_t> g_epoch{0};

@@ -52,7 +52,8 @@ struct ChunkSrc {
   const T* xp;
   const T* yp;
   int rv;
-  int64_t r0;  // flat row index of chunk row 0 (for the clip factor)
+  int64_t r0;    // flat row index of chunk row 0 (for the clip factor)
+  int64_t xrow;  // row of the unfolded input (b*T + t) of chunk row 0, for X = U(a) formed from a folded input
 };
 
 template <typename T, int BM, int BN>
@@ -102,10 +103,13 @@ struct Xty {
   // Load one chunk into registers. FULL: every chunk row is valid, the whole
   // tile width is inside both matrices and rows are 16-byte aligned, so the
   // loads need no checks (and the compiled loop has no per-element fallback).
-  template <bool FULL>
+  // IM2COL: X is the unfolded input of the convolution `geo`, its rows formed
+  // element by element from the folded input.
+  template <bool FULL, bool IM2COL = false>
   __device__ __forceinline__ static void load(Regs& R, const ChunkSrc<T>& cs, int64_t Kx, int64_t Ky, int64_t m0,
                                               int64_t n0, bool vecx, bool vecy, int64_t ones_col,
-                                              const float* c = nullptr, int64_t Tn = 1) {
+                                              const float* c = nullptr, int64_t Tn = 1,
+                                              const ConvGeo* geo = nullptr) {
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const int unit = threadIdx.x + u * NT;
@@ -125,6 +129,20 @@ struct Xty {
       const T* base = isx ? cs.xp : cs.yp;
       const int64_t K = isx ? Kx : Ky;
       const int64_t col = (isx ? m0 : n0) + cc * P;
+      if constexpr (IM2COL) {
+        static_assert(!FULL, "unfolded rows are formed with checks");
+        if (isx) {
+          const ConvCol c0 = conv_col(*geo, col);
+#pragma unroll
+          for (int r = 0; r < RU; ++r) {
+            const int row = rr * RU + r;
+            const int64_t flat = cs.xrow + row;
+            const int64_t b = sample_of(flat, geo->T);
+            R.v[u][r] = conv_row16<T>(*geo, b, (int)(flat - b * geo->T), c0, col, row < cs.rv, ones_col);
+          }
+          continue;
+        }
+      }
       if constexpr (FULL) {
         const T* src = base + (int64_t)(rr * RU) * K + col;
 #pragma unroll
@@ -304,19 +322,20 @@ struct Xty {
 //
 // Desc(q) returns the ChunkSrc of chunk q; Epi(q, acc-kind) is called after
 // the MFMAs of chunk q (per-sample scaling for bf16).
-template <typename T, int BM, int BN, bool FULL, bool PER_SAMPLE, typename Desc>
+template <typename T, int BM, int BN, bool FULL, bool PER_SAMPLE, bool IM2COL, typename Desc>
 __device__ __forceinline__ void kloop(typename Xty<T, BM, BN>::AccT& acc, unsigned char* lds, int64_t nq, Desc desc,
                                       int cps, const float* cs_sample, int64_t d, int64_t p, int64_t m0, int64_t n0,
-                                      bool vecA, bool vecG, int64_t ones_col, const float* c_rows, int64_t Tn) {
+                                      bool vecA, bool vecG, int64_t ones_col, const float* c_rows, int64_t Tn,
+                                      const ConvGeo* geo = nullptr) {
   using E = Xty<T, BM, BN>;
   if (nq <= 0) return;
   typename E::Regs R[2];
   ChunkSrc<T> cs[2];
   cs[0] = desc(0);
-  E::template load<FULL>(R[0], cs[0], d, p, m0, n0, vecA, vecG, ones_col, c_rows, Tn);
+  E::template load<FULL, IM2COL>(R[0], cs[0], d, p, m0, n0, vecA, vecG, ones_col, c_rows, Tn, geo);
   if (nq > 1) {
     cs[1] = desc(1);
-    E::template load<FULL>(R[1], cs[1], d, p, m0, n0, vecA, vecG, ones_col, c_rows, Tn);
+    E::template load<FULL, IM2COL>(R[1], cs[1], d, p, m0, n0, vecA, vecG, ones_col, c_rows, Tn, geo);
   }
   typename E::AccT tmp;
   if constexpr (!PER_SAMPLE) (void)tmp;
@@ -330,7 +349,7 @@ __device__ __forceinline__ void kloop(typename Xty<T, BM, BN>::AccT& acc, unsign
         __syncthreads();
         if (q + 2 < nq) {
           cs[st] = desc(q + 2);
-          E::template load<FULL>(R[st], cs[st], d, p, m0, n0, vecA, vecG, ones_col, c_rows, Tn);
+          E::template load<FULL, IM2COL>(R[st], cs[st], d, p, m0, n0, vecA, vecG, ones_col, c_rows, Tn, geo);
         }
         if constexpr (PER_SAMPLE) {
           const int ch = (int)(q % cps);
@@ -425,11 +444,13 @@ struct RowDesc {
   const T* X;
   const T* Y;
   int64_t nrows, d, p, q_base;
+  int64_t xrow_base;  // unfolded-input row of row 0 of X
   __device__ __forceinline__ ChunkSrc<T> operator()(int64_t q) const {
     ChunkSrc<T> cs;
     cs.r0 = (q + q_base) * KC;
     cs.xp = X + cs.r0 * d;
     cs.yp = Y + cs.r0 * p;
+    cs.xrow = xrow_base + cs.r0;
     const int64_t left = nrows - cs.r0;
     cs.rv = (int)(left < KC ? left : KC);
     return cs;
@@ -453,15 +474,19 @@ struct SampleDesc {
     const int64_t left = Tn - (int64_t)ch * KC;
     cs.rv = (int)(left < KC ? left : KC);
     cs.r0 = row;
+    cs.xrow = row;
     return cs;
   }
 };
 
 // ---------------------------------------------------------------- explicit
-template <typename T, int BM, int BN>
+// IM2COL: A is unused and the rows of the unfolded input of `geo` are formed
+// from its folded input.
+template <typename T, int BM, int BN, bool IM2COL>
 __global__ __launch_bounds__(256, 2) void k_explicit_tiles(const T* __restrict__ A, const T* __restrict__ G,
                                                            int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias,
-                                                           int mt, int nt, int vecA, int vecG, NormSink sink) {
+                                                           int mt, int nt, int vecA, int vecG, NormSink sink,
+                                                           ConvGeo geo) {
   using E = Xty<T, BM, BN>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[E::LDS_BYTES];
   __shared__ float red[E::NT / kWave];
@@ -472,16 +497,16 @@ __global__ __launch_bounds__(256, 2) void k_explicit_tiles(const T* __restrict__
   const int64_t m0 = (tile / nt) * BM;
   const int64_t n0 = (tile % nt) * BN;
   const int64_t ones_col = has_bias ? d : -1;
-  const bool full = vecA && vecG && (m0 + BM <= d) && (n0 + BN <= p) && (Tn % E::KC == 0);
+  const bool full = !IM2COL && vecA && vecG && (m0 + BM <= d) && (n0 + BN <= p) && (Tn % E::KC == 0);
   const int64_t nq = (Tn + E::KC - 1) / E::KC;
   typename E::AccT acc;
   E::zero(acc);
-  const RowDesc<T, E::KC> desc{A + i * Tn * d, G + i * Tn * p, Tn, d, p, 0};
+  const RowDesc<T, E::KC> desc{IM2COL ? A : A + i * Tn * d, G + i * Tn * p, Tn, d, p, 0, i * Tn};
   if (full)
     kloop_full<T, BM, BN, false>(acc, lds, A + i * Tn * d, G + i * Tn * p, nullptr, 0, nq, Tn, d, p, m0, n0);
   else
-    kloop<T, BM, BN, false, false>(acc, lds, nq, desc, 1, nullptr, d, p, m0, n0, vecA != 0, vecG != 0, ones_col,
-                                   nullptr, Tn);
+    kloop<T, BM, BN, false, false, IM2COL>(acc, lds, nq, desc, 1, nullptr, d, p, m0, n0, vecA != 0, vecG != 0,
+                                           ones_col, nullptr, Tn, &geo);
   float s = 0.f;
 #pragma unroll
   for (int bi = 0; bi < E::NBM; ++bi)
@@ -504,13 +529,15 @@ struct ContractOcc {
 
 // Workgroup = (output tile, K split). FUSED (one split): out and bias_out get
 // (S + sc*z) * (1/denom) directly. Otherwise ws[split][m][n] (m < d + has_bias).
-template <typename T, int BM, int BN, bool FUSED>
+// IM2COL: A is the folded input of `geo`, whose unfolded rows are formed on chip.
+template <typename T, int BM, int BN, bool FUSED, bool IM2COL>
 __global__ __launch_bounds__(256, (ContractOcc<T, BM, BN>::value)) void k_contract_tiles(const T* __restrict__ A, const T* __restrict__ G,
                                                            const float* __restrict__ c, int64_t B, int64_t Tn,
                                                            int64_t d, int64_t p, int has_bias, int mt, int nt,
                                                            int64_t units_per_split, int vecA, int vecG,
                                                            float* __restrict__ ws, NoiseArgs na,
-                                                           float* __restrict__ out, float* __restrict__ bias_out) {
+                                                           float* __restrict__ out, float* __restrict__ bias_out,
+                                                           ConvGeo geo) {
   using E = Xty<T, BM, BN>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[E::LDS_BYTES];
   const int ntl = mt * nt;
@@ -520,7 +547,7 @@ __global__ __launch_bounds__(256, (ContractOcc<T, BM, BN>::value)) void k_contra
   const int64_t n0 = (tile % nt) * BN;
   const int64_t ones_col = has_bias ? d : -1;
   const int64_t mrows = d + (has_bias ? 1 : 0);
-  const bool wide = vecA && vecG && (m0 + BM <= d) && (n0 + BN <= p);
+  const bool wide = !IM2COL && vecA && vecG && (m0 + BM <= d) && (n0 + BN <= p);
 
   typename E::AccT acc;
   E::zero(acc);
@@ -530,13 +557,13 @@ __global__ __launch_bounds__(256, (ContractOcc<T, BM, BN>::value)) void k_contra
     const int64_t nunits = (nrows + E::KC - 1) / E::KC;
     const int64_t u0 = split * units_per_split;
     const int64_t u1 = u0 + units_per_split < nunits ? u0 + units_per_split : nunits;
-    const RowDesc<T, E::KC> desc{A, G, nrows, d, p, u0};
+    const RowDesc<T, E::KC> desc{A, G, nrows, d, p, u0, 0};
     const int64_t nq = u1 > u0 ? u1 - u0 : 0;
     if (wide && (u1 < nunits || nrows % E::KC == 0))
       kloop_full<T, BM, BN, false>(acc, lds, A, G, c, u0, nq, Tn, d, p, m0, n0);
     else
-      kloop<T, BM, BN, false, false>(acc, lds, nq, desc, 1, nullptr, d, p, m0, n0, vecA != 0, vecG != 0, ones_col,
-                                     c, Tn);
+      kloop<T, BM, BN, false, false, IM2COL>(acc, lds, nq, desc, 1, nullptr, d, p, m0, n0, vecA != 0, vecG != 0,
+                                             ones_col, c, Tn, &geo);
   } else {
     const int64_t i0 = split * units_per_split;
     const int64_t i1 = i0 + units_per_split < B ? i0 + units_per_split : B;
@@ -546,8 +573,8 @@ __global__ __launch_bounds__(256, (ContractOcc<T, BM, BN>::value)) void k_contra
     if (wide && Tn % E::KC == 0)
       kloop_full<T, BM, BN, true>(acc, lds, A, G, c, i0 * cps, nq, Tn, d, p, m0, n0);
     else
-      kloop<T, BM, BN, false, true>(acc, lds, nq, desc, cps, c + i0, d, p, m0, n0, vecA != 0, vecG != 0, ones_col,
-                                    nullptr, Tn);
+      kloop<T, BM, BN, false, true, IM2COL>(acc, lds, nq, desc, cps, c + i0, d, p, m0, n0, vecA != 0, vecG != 0,
+                                            ones_col, nullptr, Tn, &geo);
   }
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -851,6 +878,10 @@ static int pick_tile(int64_t n) {
 ContractPlan contract_plan(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias) {
   if (dl_eligible(dtype, B, Tn, d, p, has_bias)) return dl_plan(B, Tn, d, p);
   if (dl32_eligible(dtype, B, Tn, d, p, has_bias)) return dl32_plan(B, Tn, d, p, has_bias);
+  return tiles_plan(dtype, B, Tn, d, p, has_bias);
+}
+
+ContractPlan tiles_plan(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias) {
   ContractPlan pl;
   pl.engine = 0;
   const int64_t mrows = d + (has_bias ? 1 : 0);
@@ -902,82 +933,100 @@ ExplicitPlan explicit_plan(int64_t d, int64_t p, int has_bias) {
 }
 
 // ---------------------------------------------------------------- launchers
+// geo != nullptr: a convolution layer, A is its folded input (the IM2COL
+// kernels); otherwise A is [B, T, d].
 template <typename T, int BM, int BN>
 static hipError_t launch_explicit_t(hipStream_t st, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
-                                    int64_t p, int has_bias, const ExplicitPlan& pl, const NormSink& sink) {
+                                    int64_t p, int has_bias, const ExplicitPlan& pl, const NormSink& sink,
+                                    const ConvGeo* geo) {
   const int eb = elem_traits<T>::bytes;
   const int vecA = ((reinterpret_cast<uintptr_t>(A) & 15) == 0) && ((d * eb) % 16 == 0);
   const int vecG = ((reinterpret_cast<uintptr_t>(G) & 15) == 0) && ((p * eb) % 16 == 0);
   const int64_t ntl = (int64_t)pl.mt * pl.nt;
   const dim3 grid((unsigned)((B + 7) / 8 * 8 * ntl));
-  hipLaunchKernelGGL((k_explicit_tiles<T, BM, BN>), grid, dim3(256), 0, st, static_cast<const T*>(A),
-                     static_cast<const T*>(G), B, Tn, d, p, has_bias, pl.mt, pl.nt, vecA, vecG, sink);
+  if (geo)
+    hipLaunchKernelGGL((k_explicit_tiles<T, BM, BN, true>), grid, dim3(256), 0, st, static_cast<const T*>(A),
+                       static_cast<const T*>(G), B, Tn, d, p, has_bias, pl.mt, pl.nt, 0, vecG, sink, *geo);
+  else
+    hipLaunchKernelGGL((k_explicit_tiles<T, BM, BN, false>), grid, dim3(256), 0, st, static_cast<const T*>(A),
+                       static_cast<const T*>(G), B, Tn, d, p, has_bias, pl.mt, pl.nt, vecA, vecG, sink, ConvGeo{});
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_explicit_d(hipStream_t st, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
-                                    int64_t p, int has_bias, const ExplicitPlan& pl, const NormSink& sink) {
-  if (pl.bm == 64 && pl.bn == 64) return launch_explicit_t<T, 64, 64>(st, A, G, B, Tn, d, p, has_bias, pl, sink);
-  if (pl.bm == 64) return launch_explicit_t<T, 64, 128>(st, A, G, B, Tn, d, p, has_bias, pl, sink);
-  if (pl.bn == 64) return launch_explicit_t<T, 128, 64>(st, A, G, B, Tn, d, p, has_bias, pl, sink);
-  return launch_explicit_t<T, 128, 128>(st, A, G, B, Tn, d, p, has_bias, pl, sink);
+                                    int64_t p, int has_bias, const ExplicitPlan& pl, const NormSink& sink,
+                                    const ConvGeo* geo) {
+  if (pl.bm == 64 && pl.bn == 64) return launch_explicit_t<T, 64, 64>(st, A, G, B, Tn, d, p, has_bias, pl, sink, geo);
+  if (pl.bm == 64) return launch_explicit_t<T, 64, 128>(st, A, G, B, Tn, d, p, has_bias, pl, sink, geo);
+  if (pl.bn == 64) return launch_explicit_t<T, 128, 64>(st, A, G, B, Tn, d, p, has_bias, pl, sink, geo);
+  return launch_explicit_t<T, 128, 128>(st, A, G, B, Tn, d, p, has_bias, pl, sink, geo);
 }
 
 hipError_t launch_explicit(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
                            int64_t p, int has_bias, const NormSink& sink) {
   const ExplicitPlan pl = explicit_plan(d, p, has_bias);
-  if (dtype == 1) return launch_explicit_d<bf16s>(st, A, G, B, Tn, d, p, has_bias, pl, sink);
-  return launch_explicit_d<float>(st, A, G, B, Tn, d, p, has_bias, pl, sink);
+  if (dtype == 1) return launch_explicit_d<bf16s>(st, A, G, B, Tn, d, p, has_bias, pl, sink, nullptr);
+  return launch_explicit_d<float>(st, A, G, B, Tn, d, p, has_bias, pl, sink, nullptr);
+}
+
+hipError_t launch_explicit_conv(hipStream_t st, int dtype, const ConvGeo& geo, const void* G, int64_t B, int64_t p,
+                                int has_bias, const NormSink& sink) {
+  const ExplicitPlan pl = explicit_plan(geo.d, p, has_bias);
+  if (dtype == 1) return launch_explicit_d<bf16s>(st, geo.a, G, B, geo.T, geo.d, p, has_bias, pl, sink, &geo);
+  return launch_explicit_d<float>(st, geo.a, G, B, geo.T, geo.d, p, has_bias, pl, sink, &geo);
+}
+
+template <typename T, int BM, int BN, bool FUSED>
+static void launch_contract_k(hipStream_t st, dim3 grid, const void* A, const void* G, const float* c, int64_t B,
+                              int64_t Tn, int64_t d, int64_t p, int has_bias, const ContractPlan& pl, int vecA,
+                              int vecG, float* ws, const NoiseArgs& na, float* out, float* bias_out,
+                              const ConvGeo* geo) {
+  if (geo)
+    hipLaunchKernelGGL((k_contract_tiles<T, BM, BN, FUSED, true>), grid, dim3(256), 0, st, static_cast<const T*>(A),
+                       static_cast<const T*>(G), c, B, Tn, d, p, has_bias, pl.mt, pl.nt, pl.units_per_split, 0,
+                       vecG, ws, na, out, bias_out, *geo);
+  else
+    hipLaunchKernelGGL((k_contract_tiles<T, BM, BN, FUSED, false>), grid, dim3(256), 0, st, static_cast<const T*>(A),
+                       static_cast<const T*>(G), c, B, Tn, d, p, has_bias, pl.mt, pl.nt, pl.units_per_split, vecA,
+                       vecG, ws, na, out, bias_out, ConvGeo{});
 }
 
 template <typename T, int BM, int BN>
 static hipError_t launch_contract_t(hipStream_t st, const void* A, const void* G, const float* c, int64_t B,
                                     int64_t Tn, int64_t d, int64_t p, int has_bias, const ContractPlan& pl,
-                                    float* ws, const NoiseArgs& na, float* out, float* bias_out) {
+                                    float* ws, const NoiseArgs& na, float* out, float* bias_out,
+                                    const ConvGeo* geo) {
   const int eb = elem_traits<T>::bytes;
   const int vecA = ((reinterpret_cast<uintptr_t>(A) & 15) == 0) && ((d * eb) % 16 == 0);
   const int vecG = ((reinterpret_cast<uintptr_t>(G) & 15) == 0) && ((p * eb) % 16 == 0);
   const dim3 grid((unsigned)((int64_t)pl.mt * pl.nt * pl.ks));
-  if (pl.ks == 1) {
-    hipLaunchKernelGGL((k_contract_tiles<T, BM, BN, true>), grid, dim3(256), 0, st, static_cast<const T*>(A),
-                       static_cast<const T*>(G), c, B, Tn, d, p, has_bias, pl.mt, pl.nt, pl.units_per_split, vecA,
-                       vecG, ws, na, out, bias_out);
-  } else {
-    hipLaunchKernelGGL((k_contract_tiles<T, BM, BN, false>), grid, dim3(256), 0, st, static_cast<const T*>(A),
-                       static_cast<const T*>(G), c, B, Tn, d, p, has_bias, pl.mt, pl.nt, pl.units_per_split, vecA,
-                       vecG, ws, na, out, bias_out);
-  }
+  if (pl.ks == 1)
+    launch_contract_k<T, BM, BN, true>(st, grid, A, G, c, B, Tn, d, p, has_bias, pl, vecA, vecG, ws, na, out,
+                                       bias_out, geo);
+  else
+    launch_contract_k<T, BM, BN, false>(st, grid, A, G, c, B, Tn, d, p, has_bias, pl, vecA, vecG, ws, na, out,
+                                        bias_out, geo);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_contract_d(hipStream_t st, const void* A, const void* G, const float* c, int64_t B,
                                     int64_t Tn, int64_t d, int64_t p, int has_bias, const ContractPlan& pl,
-                                    float* ws, const NoiseArgs& na, float* out, float* bias_out) {
+                                    float* ws, const NoiseArgs& na, float* out, float* bias_out,
+                                    const ConvGeo* geo = nullptr) {
   if (pl.bm == 64 && pl.bn == 64)
-    return launch_contract_t<T, 64, 64>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
-  if (pl.bm == 64) return launch_contract_t<T, 64, 128>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
-  if (pl.bn == 64) return launch_contract_t<T, 128, 64>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
-  return launch_contract_t<T, 128, 128>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
+    return launch_contract_t<T, 64, 64>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out, geo);
+  if (pl.bm == 64)
+    return launch_contract_t<T, 64, 128>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out, geo);
+  if (pl.bn == 64)
+    return launch_contract_t<T, 128, 64>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out, geo);
+  return launch_contract_t<T, 128, 128>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out, geo);
 }
 
-hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const void* G, const float* c, int64_t B,
-                              int64_t Tn, int64_t d, int64_t p, const ContractPlan& pl, float* ws, float sc,
-                              float denom, uint64_t seed, uint32_t layer, uint32_t step, float* out,
-                              float* bias_out) {
-  const int has_bias = bias_out != nullptr ? 1 : 0;
-  const NoiseArgs na = make_noise_args(sc, denom, seed, layer, step);
-  hipError_t e;
-  if (pl.engine == 1)
-    e = launch_contract_dl(st, A, G, c, B, Tn, d, p, pl, ws, na, out);
-  else if (pl.engine == 2)
-    e = launch_contract_dl32(st, A, G, c, B, Tn, d, p, pl, ws, na, out, bias_out);
-  else if (dtype == 1)
-    e = launch_contract_d<bf16s>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
-  else
-    e = launch_contract_d<float>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
-  if (e != hipSuccess || (pl.ks == 1 && !pl.partials)) return e;
+// Split partials in ws -> out (and bias_out) with the noise and the mean.
+static hipError_t launch_reduce_noise(hipStream_t st, const ContractPlan& pl, float* ws, int64_t d, int64_t p,
+                                      int has_bias, const NoiseArgs& na, float* out, float* bias_out) {
   const int64_t std_threads = ((d + 3) / 4) * ((p + 3) / 4);
   if (p % 4 == 0 && pl.ks >= 64 && std_threads < 32768) {
     // many splits, few outputs: split lanes in parallel
@@ -997,6 +1046,39 @@ hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const vo
   const dim3 grid((unsigned)((threads + 255) / 256));
   hipLaunchKernelGGL(k_reduce_noise, grid, dim3(256), 0, st, ws, pl.ks, d, p, has_bias, vec, na, out, bias_out);
   return hipGetLastError();
+}
+
+hipError_t launch_clipped_sum_conv(hipStream_t st, int dtype, const ConvGeo& geo, const void* G, const float* c,
+                                   int64_t B, int64_t p, const ContractPlan& pl, float* ws, float sc, float denom,
+                                   uint64_t seed, uint32_t layer, uint32_t step, float* out, float* bias_out) {
+  const int has_bias = bias_out != nullptr ? 1 : 0;
+  const NoiseArgs na = make_noise_args(sc, denom, seed, layer, step);
+  hipError_t e;
+  if (dtype == 1)
+    e = launch_contract_d<bf16s>(st, geo.a, G, c, B, geo.T, geo.d, p, has_bias, pl, ws, na, out, bias_out, &geo);
+  else
+    e = launch_contract_d<float>(st, geo.a, G, c, B, geo.T, geo.d, p, has_bias, pl, ws, na, out, bias_out, &geo);
+  if (e != hipSuccess || pl.ks == 1) return e;
+  return launch_reduce_noise(st, pl, ws, geo.d, p, has_bias, na, out, bias_out);
+}
+
+hipError_t launch_clipped_sum(hipStream_t st, int dtype, const void* A, const void* G, const float* c, int64_t B,
+                              int64_t Tn, int64_t d, int64_t p, const ContractPlan& pl, float* ws, float sc,
+                              float denom, uint64_t seed, uint32_t layer, uint32_t step, float* out,
+                              float* bias_out) {
+  const int has_bias = bias_out != nullptr ? 1 : 0;
+  const NoiseArgs na = make_noise_args(sc, denom, seed, layer, step);
+  hipError_t e;
+  if (pl.engine == 1)
+    e = launch_contract_dl(st, A, G, c, B, Tn, d, p, pl, ws, na, out);
+  else if (pl.engine == 2)
+    e = launch_contract_dl32(st, A, G, c, B, Tn, d, p, pl, ws, na, out, bias_out);
+  else if (dtype == 1)
+    e = launch_contract_d<bf16s>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
+  else
+    e = launch_contract_d<float>(st, A, G, c, B, Tn, d, p, has_bias, pl, ws, na, out, bias_out);
+  if (e != hipSuccess || (pl.ks == 1 && !pl.partials)) return e;
+  return launch_reduce_noise(st, pl, ws, d, p, has_bias, na, out, bias_out);
 }
 
 }  // namespace dpk

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(dpc.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.dp_abi_version() == 2
+    assert lib.dp_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -395,3 +395,72 @@ def test_norm_clip_layers_validation(lib):
     import torch
     if not torch.cuda.is_available():
         assert call() == dpc.DP_ERR_NO_DEVICE
+
+
+def _conv(lib, a=FAKE, G=FAKE, geo=None, dt=0, B=4, p=6, hb=0, mode=0, kappa=1, ws=FAKE, wsb=1 << 20, sq=FAKE):
+    geo = dpc.conv_geometry(3, 8, 8, 3, 1, 1) if geo is None else geo
+    path = ctypes.c_int32(-7)
+    st = lib.dp_conv_norm(None, a, G, ctypes.byref(geo) if geo is not False else None, dt, B, p, hb, mode, kappa,
+                          ws, wsb, sq, 0, ctypes.byref(path))
+    return st, path.value
+
+
+def _conv_sum(lib, a=FAKE, G=FAKE, geo=None, dt=0, B=4, p=6, c=FAKE, C=1.0, sigma=1.0, denom=4.0, ws=FAKE,
+              wsb=1 << 20, out=FAKE, bout=None):
+    geo = dpc.conv_geometry(3, 8, 8, 3, 1, 1) if geo is None else geo
+    return lib.dp_conv_clipped_sum_noise(None, a, G, ctypes.byref(geo), dt, B, p, c, C, sigma, denom, 0, 0, 0, ws,
+                                         wsb, out, bout)
+
+
+def test_conv_validation(lib):
+    """Folded-input conv calls: geometry, pointers, alignment and scalars are
+    checked before any device work; a failed call writes nothing."""
+    g = dpc.conv_geometry
+    assert _conv(lib, geo=False)[0] == dpc.DP_ERR_NULL
+    assert _conv(lib, a=None)[0] == dpc.DP_ERR_NULL
+    assert _conv(lib, sq=None)[0] == dpc.DP_ERR_NULL
+    assert _conv(lib, geo=g(3, 8, 8, 3, 0, 1))[0] == dpc.DP_ERR_SHAPE          # stride 0
+    assert _conv(lib, geo=g(3, 8, 8, 3, 1, -1))[0] == dpc.DP_ERR_SHAPE         # negative padding
+    assert _conv(lib, geo=g(3, 8, 8, 3, 1, 1, 0))[0] == dpc.DP_ERR_SHAPE       # dilation 0
+    assert _conv(lib, geo=g(3, 4, 4, 7, 1, 1))[0] == dpc.DP_ERR_SHAPE          # kernel beyond the padded input
+    assert _conv(lib, geo=g(3, 4, 4, (3, 3), 1, 0, (2, 1)))[0] == dpc.DP_ERR_SHAPE  # dilated span 5 > 4
+    assert _conv(lib, geo=g(1 << 12, 1 << 10, 1 << 10, 1))[0] == dpc.DP_ERR_SHAPE  # C_in*H*W >= 2^31
+    assert _conv(lib, geo=g(0, 8, 8, 3, 1, 1))[0] == dpc.DP_ERR_SHAPE
+    assert _conv(lib, B=0)[0] == dpc.DP_ERR_SHAPE
+    assert _conv(lib, dt=2)[0] == dpc.DP_ERR_DTYPE
+    assert _conv(lib, a=FAKE + 2)[0] == dpc.DP_ERR_ALIGN                        # fp32 input needs 4 bytes
+    assert _conv(lib, G=FAKE_MIS)[0] == dpc.DP_ERR_ALIGN
+    assert _conv(lib, mode=4)[0] == dpc.DP_ERR_VALUE
+    st, path = _conv(lib, ws=None, mode=dpc.MODE_GHOST)                         # T = 64: 1 tile, no workspace
+    assert st in (dpc.DP_OK, dpc.DP_ERR_NO_DEVICE)
+    big = g(3, 32, 32, 3, 1, 1)                                                 # T = 1024: partials + counters
+    assert _conv(lib, geo=big, ws=None, mode=dpc.MODE_GHOST)[0] == dpc.DP_ERR_NULL
+    st, path = _conv(lib, geo=big, wsb=4, mode=dpc.MODE_GHOST)
+    assert st == dpc.DP_ERR_WORKSPACE and path == -7
+    assert _conv_sum(lib, c=None) == dpc.DP_ERR_NULL
+    assert _conv_sum(lib, out=None) == dpc.DP_ERR_NULL
+    assert _conv_sum(lib, C=0.0) == dpc.DP_ERR_VALUE
+    assert _conv_sum(lib, sigma=-1.0) == dpc.DP_ERR_VALUE
+    assert _conv_sum(lib, denom=float("nan")) == dpc.DP_ERR_VALUE
+    assert _conv_sum(lib, bout=FAKE + 2) == dpc.DP_ERR_ALIGN
+    assert _conv_sum(lib, a=FAKE + 2, dt=1) != dpc.DP_ERR_ALIGN                 # bf16 input: 2-byte alignment
+
+
+def test_conv_workspace_and_geometry(lib):
+    """dp_conv_workspace_bytes covers the path the norm call takes (tiles of the
+    tiled ghost kernel or the explicit tiles) and the contraction's splits; the
+    binding's output shape is the oracle unfolding's."""
+    import numpy as np
+    from oracle.definitions import unfold2d
+    for args in [(3, 32, 32, 3, 1, 1), (64, 16, 16, 3, 2, 1), (16, 9, 11, (5, 3), (2, 1), (2, 0), (1, 2)),
+                 (5, 6, 6, 6, 1, 0)]:
+        geo = dpc.conv_geometry(*args)
+        x = np.zeros((1, geo.C_in, geo.H, geo.W))
+        U = unfold2d(x, (geo.kh, geo.kw), (geo.stride_h, geo.stride_w), (geo.pad_h, geo.pad_w),
+                     (geo.dil_h, geo.dil_w))
+        assert dpc.conv_out_shape(geo) == U.shape[1:]
+    big = dpc.conv_geometry(3, 32, 32, 3, 1, 1)
+    w = dpc.dp_conv_workspace_bytes(big, dpc.DP_F32, 256, 64, False, dpc.MODE_GHOST)
+    assert w >= 256 * 36 * 4                  # T = 1024: 8 x 8 blocks of 128 rows, 36 Gram tiles per sample
+    assert dpc.dp_conv_workspace_bytes(dpc.conv_geometry(3, 4, 4, 7), dpc.DP_F32, 4, 6) == 0   # invalid
+    assert dpc.dp_conv_workspace_bytes(big, dpc.DP_F32, 4, 6, mode=7) == 0

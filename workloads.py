@@ -180,6 +180,19 @@ def make_layer(wl: Workload, layer: int, step: int = 0, B: int | None = None,
     return np.ascontiguousarray(A), np.ascontiguousarray(G)
 
 
+def make_folded(wl: Workload, layer: int, step: int = 0, B: int | None = None, base: int = BASE_SEED):
+    """The folded input fmap [B, C_in, H, W] and output gradients G [B, T, p]
+    of one convolution layer of a workload with conv geometry: the same seeded
+    values make_layer unfolds (make_layer's A is unfold3x3(fmap, stride))."""
+    B = wl.B if B is None else B
+    T, d, p = wl.layer_shape(layer)
+    cin, hin, win, stride = wl.conv[layer]
+    fmap = _normal(rng_for(wl.wl_id, layer, step, 0, base), (B, cin, hin, win))
+    u = rng_for(wl.wl_id, layer, step, 2, base).uniform(-2.0, 0.0)
+    G = (_normal(rng_for(wl.wl_id, layer, step, 1, base), (B, T, p)) * np.float32(10.0 ** u)).astype(np.float32)
+    return np.ascontiguousarray(fmap), G
+
+
 def make_vector(n: int, lo: float, hi: float, tag: int, base: int = BASE_SEED) -> np.ndarray:
     """Seeded fp32 vector in [lo, hi): free inputs of an entry point (clip factors,
     norm vectors) for tests that exercise one entry point on its own."""
