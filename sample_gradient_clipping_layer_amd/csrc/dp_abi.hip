@@ -313,7 +313,9 @@ dp_status check_conv(const void* a, const void* G, const dp_conv2d* cv, dp_dtype
   if (geo) {
     *geo = dpk::ConvGeo{a, (int32_t)cv->C_in, (int32_t)cv->H, (int32_t)cv->W, (int32_t)cv->kh, (int32_t)cv->kw,
                         (int32_t)cv->stride_h, (int32_t)cv->stride_w, (int32_t)cv->pad_h, (int32_t)cv->pad_w,
-                        (int32_t)cv->dil_h, (int32_t)cv->dil_w, (int32_t)Wo, (int32_t)T, (int32_t)d};
+                        (int32_t)cv->dil_h, (int32_t)cv->dil_w, (int32_t)Ho, (int32_t)Wo, (int32_t)T, (int32_t)d,
+                        dpk::make_fastdiv((uint32_t)(cv->kh * cv->kw)), dpk::make_fastdiv((uint32_t)cv->kw),
+                        dpk::make_fastdiv((uint32_t)Wo), dpk::make_fastdiv((uint32_t)T)};
   }
   return DP_OK;
 }

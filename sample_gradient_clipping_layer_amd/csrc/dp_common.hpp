@@ -100,6 +100,25 @@ __device__ __forceinline__ u32x4 load16_rowmajor(const T* __restrict__ X, int64_
   return r;
 }
 
+// Unsigned 32-bit division by a divisor fixed for a launch, as a multiply
+// and a shift (Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", 1994): with s = ceil(log2 d) and
+// m = floor(2^32 (2^s - d) / d) + 1, n / d = (hi32(n * m) + n) >> s for every
+// 32-bit n (the sum is formed in 64 bits).
+struct FastDiv {
+  uint32_t m;
+  int32_t s;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  int s = 0;
+  while ((uint64_t{1} << s) < d) ++s;
+  const uint64_t num = (uint64_t{1} << 32) * ((uint64_t{1} << s) - d);
+  return FastDiv{(uint32_t)(num / d + 1), s};
+}
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)__umulhi(n, f.m) + n) >> f.s);
+}
+
 // A 2-D convolution layer given by its folded input a [B, Cin, H, W]: row t of
 // sample b's unfolded input U(a) (t = ho*Wo + wo) holds, in column
 // f = (ci*KH + i)*KW + j, a[b][ci][ho*sh - ph + i*dh][wo*sw - pw + j*dw], or 0
@@ -108,7 +127,8 @@ __device__ __forceinline__ u32x4 load16_rowmajor(const T* __restrict__ X, int64_
 // Every size and per-sample offset fits 32 bits (checked by the host).
 struct ConvGeo {
   const void* a;
-  int32_t Cin, H, W, KH, KW, sh, sw, ph, pw, dh, dw, Wo, T, d;
+  int32_t Cin, H, W, KH, KW, sh, sw, ph, pw, dh, dw, Ho, Wo, T, d;
+  FastDiv by_khw, by_kw, by_wo, by_t;  // division by KH*KW, KW, Wo and T
 };
 
 // Column f0 of U(a) as (channel, kernel row, kernel column).
@@ -116,26 +136,53 @@ struct ConvCol {
   int ci, i, j;
 };
 __device__ __forceinline__ ConvCol conv_col(const ConvGeo& g, int64_t f0) {
-  const uint32_t f = (uint32_t)f0, khw = (uint32_t)(g.KH * g.KW);
-  const uint32_t ci = f / khw, r = f - ci * khw;
-  const uint32_t i = r / (uint32_t)g.KW;
+  const uint32_t f = (uint32_t)f0;
+  const uint32_t ci = fast_div(f, g.by_khw), r = f - ci * (uint32_t)(g.KH * g.KW);
+  const uint32_t i = fast_div(r, g.by_kw);
   return ConvCol{(int)ci, (int)i, (int)(r - i * (uint32_t)g.KW)};
 }
 
-// Elements [f0, f0 + per16) of row t of sample b's U(a) as one 16-byte
-// vector (c0 = conv_col(g, f0)): zero in the padding, past column d, and
-// everywhere when !row_ok; column ones_col (if >= 0) reads 1.
+// A row of U(a) as (sample, output row, output column); next() steps to the
+// following flat row b*T + t.
+struct ConvRow {
+  int64_t b;
+  int ho, wo;
+  __device__ __forceinline__ void next(const ConvGeo& g) {
+    if (++wo == g.Wo) {
+      wo = 0;
+      if (++ho == g.Ho) {
+        ho = 0;
+        ++b;
+      }
+    }
+  }
+};
+__device__ __forceinline__ ConvRow conv_row_at(const ConvGeo& g, int64_t b, int t) {
+  const int ho = (int)fast_div((uint32_t)t, g.by_wo);
+  return ConvRow{b, ho, t - ho * g.Wo};
+}
+// Row `flat` = b*T + t of the unfolded input of the whole batch.
+__device__ __forceinline__ ConvRow conv_row_flat(const ConvGeo& g, int64_t flat) {
+  int64_t b;
+  if ((uint64_t)flat <= 0xFFFFFFFFull)
+    b = fast_div((uint32_t)flat, g.by_t);
+  else
+    b = flat / g.T;
+  return conv_row_at(g, b, (int)(flat - b * g.T));
+}
+
+// Elements [f0, f0 + per16) of row `rw` of U(a) as one 16-byte vector
+// (c0 = conv_col(g, f0)): zero in the padding, past column d, and everywhere
+// when !row_ok; column ones_col (if >= 0) reads 1.
 template <typename T>
-__device__ __forceinline__ u32x4 conv_row16(const ConvGeo& g, int64_t b, int t, ConvCol c0, int64_t f0, bool row_ok,
+__device__ __forceinline__ u32x4 conv_row16(const ConvGeo& g, const ConvRow& rw, ConvCol c0, int64_t f0, bool row_ok,
                                             int64_t ones_col) {
   constexpr int P = elem_traits<T>::per16;
   constexpr uint32_t one_bits = P == 8 ? 0x3F80u : 0x3F800000u;
   uint32_t w[4] = {0u, 0u, 0u, 0u};
   if (row_ok) {
-    const int ho = (int)((uint32_t)t / (uint32_t)g.Wo);
-    const int wo = t - ho * g.Wo;
-    const int y0 = ho * g.sh - g.ph, x0 = wo * g.sw - g.pw;
-    const T* __restrict__ ab = static_cast<const T*>(g.a) + b * (int64_t)g.Cin * g.H * g.W;
+    const int y0 = rw.ho * g.sh - g.ph, x0 = rw.wo * g.sw - g.pw;
+    const T* __restrict__ ab = static_cast<const T*>(g.a) + rw.b * (int64_t)g.Cin * g.H * g.W;
     int ci = c0.ci, i = c0.i, j = c0.j;
 #pragma unroll
     for (int e = 0; e < P; ++e) {

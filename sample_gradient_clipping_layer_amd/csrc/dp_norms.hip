@@ -130,19 +130,22 @@ template <typename T, int TS>
 __device__ __forceinline__ void ghost_load_conv(typename GhostCfg<T, TS>::Regs& regs, const ConvGeo& g, int64_t i,
                                                 int sb, int tb, int64_t chunk) {
   using Cfg = GhostCfg<T, TS>;
+  static_assert(Cfg::NT % Cfg::V == 0, "a thread keeps one column vector");
   const bool diag = (sb == tb);
+  // every piece of this thread covers the same columns
+  const int64_t col = chunk * Cfg::KC + (threadIdx.x % Cfg::V) * Cfg::P;
+  const ConvCol c0 = conv_col(g, col);
 #pragma unroll
   for (int r = 0; r < Cfg::PPT; ++r) {
     const int q = threadIdx.x + r * Cfg::NT;
     const int h = q / (TS * Cfg::V);
     const int row = (q / Cfg::V) % TS;
-    const int c16 = q % Cfg::V;
     if (diag && h == 1) {
       regs.v[r] = u32x4{0u, 0u, 0u, 0u};
     } else {
       const int grow = (h == 0 ? sb : tb) * TS + row;
-      const int64_t col = chunk * Cfg::KC + c16 * Cfg::P;
-      regs.v[r] = conv_row16<T>(g, i, grow, conv_col(g, col), col, grow < g.T, -1);
+      const bool ok = grow < g.T;
+      regs.v[r] = conv_row16<T>(g, conv_row_at(g, i, ok ? grow : 0), c0, col, ok, -1);
     }
   }
 }

@@ -132,13 +132,13 @@ struct Xty {
       if constexpr (IM2COL) {
         static_assert(!FULL, "unfolded rows are formed with checks");
         if (isx) {
+          // the unit's RU consecutive rows: one division for the first, then steps
           const ConvCol c0 = conv_col(*geo, col);
+          ConvRow rw = conv_row_flat(*geo, cs.xrow + rr * RU);
 #pragma unroll
           for (int r = 0; r < RU; ++r) {
-            const int row = rr * RU + r;
-            const int64_t flat = cs.xrow + row;
-            const int64_t b = sample_of(flat, geo->T);
-            R.v[u][r] = conv_row16<T>(*geo, b, (int)(flat - b * geo->T), c0, col, row < cs.rv, ones_col);
+            R.v[u][r] = conv_row16<T>(*geo, rw, c0, col, rr * RU + r < cs.rv, ones_col);
+            rw.next(*geo);
           }
           continue;
         }
