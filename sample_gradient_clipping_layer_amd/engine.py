@@ -10,7 +10,8 @@ path over all layers -- the per-sample norm over every layer, the clip
 factors, and each layer's clipped noised mean -- and writes the results into
 the parameters' .grad. A convolution's input is unfolded first (U(a) of the
 same page, Sec. 2.2: D = C_in * kH * kW features per output position), in
-torch, on the GPU.
+torch, on the GPU; with conv_input="folded" the library takes the folded
+input instead and forms U(a)'s rows inside its kernels (dp_conv_* calls).
 
 Only argument marshalling and layout changes happen here; every step of the
 clipping path runs in libdpclip.
@@ -20,7 +21,8 @@ from __future__ import annotations
 import torch
 import torch.nn.functional as F
 
-from . import (MODE_EXPLICIT, MODE_GHOST, MODE_MIXED, MODE_TIME, dp_clip_factors, dp_clipped_sum_noise_layers,
+from . import (DP_BF16, DP_F32, MODE_EXPLICIT, MODE_GHOST, MODE_MIXED, MODE_TIME, conv_geometry, dp_clip_factors,
+               dp_clipped_sum_noise_layers, dp_conv_clipped_sum_noise, dp_conv_norm, dp_conv_workspace_bytes,
                dp_ghost_norm_layers, dp_layers_workspace_bytes)
 
 MODES = {"ghost-mixed": MODE_MIXED, "ghost": MODE_GHOST, "explicit": MODE_EXPLICIT, "time": MODE_TIME}
@@ -50,9 +52,12 @@ class PrivacyEngine:
     """
 
     def __init__(self, model: torch.nn.Module, C: float, sigma: float, seed: int = 0, mode: str = "ghost-mixed",
-                 kappa: int = 1):
+                 kappa: int = 1, conv_input: str = "unfolded"):
         if mode not in MODES:
             raise ValueError(f"mode must be one of {sorted(MODES)}")
+        if conv_input not in ("unfolded", "folded"):
+            raise ValueError("conv_input must be 'unfolded' or 'folded'")
+        self.folded = conv_input == "folded"
         self.C, self.sigma, self.seed = float(C), float(sigma), int(seed)
         self.mode, self.kappa = MODES[mode], int(kappa)
         self.layers: list[_Layer] = []
@@ -63,6 +68,8 @@ class PrivacyEngine:
                     raise ValueError("Conv2d with groups != 1 is not supported")
                 if isinstance(m, torch.nn.Conv2d) and m.padding_mode != "zeros":
                     raise ValueError("Conv2d padding must be zeros")
+                if isinstance(m, torch.nn.Conv2d) and isinstance(m.padding, str) and m.padding != "valid":
+                    raise ValueError("Conv2d padding must be numeric or 'valid'")
                 if not m.weight.requires_grad:
                     raise ValueError("a layer with a trainable bias needs a trainable weight (one norm covers both)")
                 self.layers.append(_Layer(m))
@@ -99,44 +106,81 @@ class PrivacyEngine:
             h.remove()
         self._handles = []
 
+    @staticmethod
+    def _padding(m):
+        return 0 if isinstance(m.padding, str) else m.padding  # 'valid' is no padding
+
+    def _is_folded(self, L):
+        return self.folded and isinstance(L.module, torch.nn.Conv2d)
+
     def _operands(self, L):
-        """(A [B, T, d], G [B, T, p]) of one layer, contiguous, in the activation dtype."""
+        """(A [B, T, d], G [B, T, p]) of one layer, contiguous, in the activation dtype;
+        for a conv layer taken folded, (a [B, C_in, H, W], G [B, T, p], geometry)."""
         m, a, g = L.module, L.a, L.g
         if a is None or g is None:
             raise RuntimeError("step() needs one forward and one backward pass of every layer first")
         B = a.shape[0]
+        dt = a.dtype if a.dtype in (torch.float32, torch.bfloat16) else torch.float32
         if isinstance(m, torch.nn.Linear):
             A = a.reshape(B, -1, a.shape[-1])
             G = g.reshape(B, -1, g.shape[-1])
+        elif self._is_folded(L):
+            geo = conv_geometry(a.shape[1], a.shape[2], a.shape[3], m.kernel_size, m.stride, self._padding(m),
+                                m.dilation)
+            G = g.reshape(B, g.shape[1], -1).transpose(1, 2)
+            return a.to(dt).contiguous(), G.to(dt).contiguous(), geo
         else:
-            U = F.unfold(a, m.kernel_size, dilation=m.dilation, padding=m.padding, stride=m.stride)  # [B, D, L]
+            U = F.unfold(a, m.kernel_size, dilation=m.dilation, padding=self._padding(m), stride=m.stride)  # [B, D, L]
             A = U.transpose(1, 2)
             G = g.reshape(B, g.shape[1], -1).transpose(1, 2)
-        dt = a.dtype if a.dtype in (torch.float32, torch.bfloat16) else torch.float32
         return A.to(dt).contiguous(), G.to(dt).contiguous()
 
     def step(self, step: int, denom: float | None = None):
-        """Clipped noised mean gradients into .grad; returns the per-sample norms."""
+        """Clipped noised mean gradients into .grad; returns the per-sample norms.
+
+        The noise stream of a layer is its index in the engine's layer list
+        (the model's module order), whichever call serves it."""
         ops = [self._operands(L) for L in self.layers]
         B = ops[0][0].shape[0]
         dev = ops[0][0].device
-        dtypes = {A.dtype for A, _ in ops}
+        dtypes = {op[0].dtype for op in ops}
         if len(dtypes) != 1:
             raise RuntimeError("all layers must share one activation dtype")
+        dt = DP_BF16 if ops[0][0].dtype == torch.bfloat16 else DP_F32
+        denom = float(B) if denom is None else float(denom)
         has_bias = [L.module.bias is not None and L.module.bias.requires_grad for L in self.layers]
-        ws = torch.empty(max(256, dp_layers_workspace_bytes(ops, has_bias=has_bias, mode=self.mode,
-                                                            kappa=self.kappa)), dtype=torch.uint8, device=dev)
+        dense = [k for k, op in enumerate(ops) if len(op) == 2]   # [B, T, d] operands: multi-layer calls
+        folded = [k for k, op in enumerate(ops) if len(op) == 3]  # folded conv inputs: dp_conv_* calls
         sq = torch.empty(B, dtype=torch.float32, device=dev)
-        dp_ghost_norm_layers(ops, sq, has_bias=has_bias, mode=self.mode, kappa=self.kappa, workspace=ws)
+        ws = None
+        if dense:
+            dops, dhb = [ops[k] for k in dense], [has_bias[k] for k in dense]
+            ws = torch.empty(max(256, dp_layers_workspace_bytes(dops, has_bias=dhb, mode=self.mode,
+                                                                kappa=self.kappa)), dtype=torch.uint8, device=dev)
+            dp_ghost_norm_layers(dops, sq, has_bias=dhb, mode=self.mode, kappa=self.kappa, workspace=ws)
+        wsc = {}
+        for k in folded:
+            a, G, geo = ops[k]
+            wsc[k] = torch.empty(max(256, dp_conv_workspace_bytes(geo, dt, B, G.shape[2], has_bias[k], self.mode,
+                                                                  self.kappa)), dtype=torch.uint8, device=dev)
+            dp_conv_norm(a, G, geo, sq, has_bias=has_bias[k], mode=self.mode, kappa=self.kappa,
+                         accumulate=bool(dense) or k != folded[0], workspace=wsc[k])
         c = torch.empty(B, dtype=torch.float32, device=dev)
         norms = torch.empty(B, dtype=torch.float32, device=dev)
         dp_clip_factors(sq, self.C, c, norms)
-        outs = [torch.empty(A.shape[2], G.shape[2], dtype=torch.float32, device=dev) for A, G in ops]
-        bouts = [torch.empty(G.shape[2], dtype=torch.float32, device=dev) if hb else None
-                 for (A, G), hb in zip(ops, has_bias)]
-        dp_clipped_sum_noise_layers(ops, c, self.C, self.sigma, float(B) if denom is None else float(denom),
-                                    self.seed, step, outs, bias_outs=bouts if any(has_bias) else None,
-                                    has_bias=has_bias, workspace=ws)
+        d_of = [op[2].C_in * op[2].kh * op[2].kw if len(op) == 3 else op[0].shape[2] for op in ops]
+        outs = [torch.empty(d_of[k], op[1].shape[2], dtype=torch.float32, device=dev) for k, op in enumerate(ops)]
+        bouts = [torch.empty(op[1].shape[2], dtype=torch.float32, device=dev) if hb else None
+                 for op, hb in zip(ops, has_bias)]
+        if dense:
+            dp_clipped_sum_noise_layers([ops[k] for k in dense], c, self.C, self.sigma, denom, self.seed, step,
+                                        [outs[k] for k in dense],
+                                        bias_outs=[bouts[k] for k in dense] if any(dhb) else None, has_bias=dhb,
+                                        layer_ids=dense, workspace=ws)
+        for k in folded:
+            a, G, geo = ops[k]
+            dp_conv_clipped_sum_noise(a, G, geo, c, self.C, self.sigma, denom, self.seed, k, step, outs[k],
+                                      bias_out=bouts[k], workspace=wsc[k])
         for L, out, bout in zip(self.layers, outs, bouts):
             w = L.module.weight
             if w.requires_grad:

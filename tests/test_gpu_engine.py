@@ -54,7 +54,7 @@ def _reference(model, x, y, C, scale_grad_of=None):
     return dict(zip(names, mean)), norms
 
 
-@pytest.mark.parametrize("kind", ["mlp-sequence", "conv"])
+@pytest.mark.parametrize("kind", ["mlp-sequence", "conv", "conv-folded"])
 def test_engine_matches_per_example_backprop(kind):
     dev = torch.device("cuda", 0)
     g = torch.Generator().manual_seed(5)
@@ -70,7 +70,8 @@ def test_engine_matches_per_example_backprop(kind):
         C = 4.0
     ref, norms = _reference(model, x, y, C)
     model = model.to(dev)
-    engine = PrivacyEngine(model, C=C, sigma=0.0, seed=9)
+    engine = PrivacyEngine(model, C=C, sigma=0.0, seed=9,
+                           conv_input="folded" if kind == "conv-folded" else "unfolded")
     _per_sample_loss(model(x.to(dev)), y.to(dev)).sum().backward()
     n_gpu = engine.step(0)
     np.testing.assert_allclose(n_gpu.cpu().numpy(), norms.numpy(), rtol=1e-4)
@@ -104,3 +105,21 @@ def test_engine_noise_matches_the_stream():
         zb = N.normals(p, 21, l, 1, 7).astype(np.float64)
         np.testing.assert_allclose(grads[1][wn] - grads[0][wn], 2.0 * zw / 4.0, rtol=1e-5, atol=1e-6)
         np.testing.assert_allclose(grads[1][bn] - grads[0][bn], 2.0 * zb / 4.0, rtol=1e-5, atol=1e-6)
+
+
+def test_engine_folded_conv_noise_matches_unfolded():
+    """Folded and unfolded conv inputs give the same noise (each layer's
+    stream is its index in the engine) and the same clipped means."""
+    dev = torch.device("cuda", 0)
+    g = torch.Generator().manual_seed(8)
+    x, y = torch.randn(6, 3, 8, 8, generator=g), torch.randn(6, 3, generator=g)
+    grads = {}
+    for conv_input in ("unfolded", "folded"):
+        model = _ConvNet(4).to(dev)
+        engine = PrivacyEngine(model, C=3.0, sigma=1.5, seed=33, conv_input=conv_input)
+        _per_sample_loss(model(x.to(dev)), y.to(dev)).sum().backward()
+        engine.step(5)
+        grads[conv_input] = {n: p.grad.detach().cpu().double().numpy() for n, p in model.named_parameters()}
+        engine.detach()
+    for n, want in grads["unfolded"].items():
+        np.testing.assert_allclose(grads["folded"][n], want, rtol=1e-4, atol=1e-5 * np.abs(want).max(), err_msg=n)
