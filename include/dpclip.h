@@ -339,7 +339,7 @@ typedef struct dp_conv2d {
  * dp_conv_norm: dp_ghost_norm of the layer (U(a), G).
  *
  *  a        [B, C_in, H, W] folded input, dtype as G, 4-byte aligned (fp32)
- *           or 2-byte aligned (bf16); C_in*H*W < 2^31.
+ *           or 2-byte aligned (bf16); (C_in+2)*(H+2*pad_h)*(W+2*pad_w) < 2^31.
  *  G        [B, T, p] output gradients (T = H_out*W_out, spatial positions
  *           row-major), 16-byte aligned.
  *  conv     host geometry; H_out, W_out >= 1; every size below 2^31.

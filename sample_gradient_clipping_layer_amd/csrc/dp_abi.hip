@@ -301,6 +301,8 @@ dp_status check_conv(const void* a, const void* G, const dp_conv2d* cv, dp_dtype
   const int64_t span_h = cv->dil_h * (cv->kh - 1) + 1, span_w = cv->dil_w * (cv->kw - 1) + 1;
   const int64_t ext_h = cv->H + 2 * cv->pad_h, ext_w = cv->W + 2 * cv->pad_w;
   if (span_h > ext_h || span_w > ext_w || ext_h >= kMaxConv || ext_w >= kMaxConv) return DP_ERR_SHAPE;
+  // 32-bit offsets in the kernels: column offsets, window origins and their sums
+  if ((cv->C_in + 2) * ext_h >= kMaxConv || (cv->C_in + 2) * ext_h * ext_w >= kMaxConv) return DP_ERR_SHAPE;
   const int64_t Ho = (ext_h - span_h) / cv->stride_h + 1, Wo = (ext_w - span_w) / cv->stride_w + 1;
   // window positions ho*stride - pad + i*dil, and Ho*Wo, within int32
   if ((Ho - 1) * cv->stride_h + span_h >= kMaxConv || (Wo - 1) * cv->stride_w + span_w >= kMaxConv) return DP_ERR_SHAPE;

@@ -124,7 +124,9 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
 // f = (ci*KH + i)*KW + j, a[b][ci][ho*sh - ph + i*dh][wo*sw - pw + j*dw], or 0
 // in the zero padding ("Scalable and Efficient Training of Large CNNs with
 // DP", Sec. 2.2, the unfolding U). T = Ho*Wo rows, d = Cin*KH*KW columns.
-// Every size and per-sample offset fits 32 bits (checked by the host).
+// Every size and per-sample offset fits 32 bits: the host checks
+// (Cin + 2) * (H + 2ph) * (W + 2pw) < 2^31, which bounds the column offsets,
+// the window origins y0*W + x0 and their sums.
 struct ConvGeo {
   const void* a;
   int32_t Cin, H, W, KH, KW, sh, sw, ph, pw, dh, dw, Ho, Wo, T, d;
@@ -171,14 +173,75 @@ __device__ __forceinline__ ConvRow conv_row_flat(const ConvGeo& g, int64_t flat)
   return conv_row_at(g, b, (int)(flat - b * g.T));
 }
 
-// Elements [f0, f0 + per16) of row `rw` of U(a) as one 16-byte vector
-// (c0 = conv_col(g, f0)): zero in the padding, past column d, and everywhere
-// when !row_ok; column ones_col (if >= 0) reads 1.
+// The per16 columns [f0, f0 + per16) of U(a), each as its offset in a
+// sample's folded input from the window origin, (ci*H + i*dh)*W + j*dw, and its
+// tap displacement (i*dh, j*dw); `in` says the column is one of U(a)'s d
+// columns, `one` that it is the ones column of the bias.
+template <int P>
+struct ConvCols {
+  int off[P], dy[P], dx[P];
+  bool in[P], one[P];
+};
+template <int P>
+__device__ __forceinline__ ConvCols<P> conv_cols(const ConvGeo& g, int64_t f0, int64_t ones_col) {
+  ConvCols<P> k;
+  const ConvCol c = conv_col(g, f0);
+  int ci = c.ci, i = c.i, j = c.j;
+#pragma unroll
+  for (int e = 0; e < P; ++e) {
+    const int64_t f = f0 + e;
+    k.in[e] = f < g.d;
+    k.one[e] = f == ones_col;
+    k.dy[e] = i * g.dh;
+    k.dx[e] = j * g.dw;
+    k.off[e] = k.in[e] ? (ci * g.H + k.dy[e]) * g.W + k.dx[e] : 0;
+    if (++j == g.KW) {
+      j = 0;
+      if (++i == g.KH) {
+        i = 0;
+        ++ci;
+      }
+    }
+  }
+  return k;
+}
+
+// Columns `k` of row `rw` of U(a) as one 16-byte vector: zero in the padding,
+// past column d and everywhere when !row_ok; the ones column reads 1. An
+// element is read only where its input position (y, x) lies inside the H x W
+// input, where its offset equals ((ci*H + y)*W + x).
 template <typename T>
-__device__ __forceinline__ u32x4 conv_row16(const ConvGeo& g, const ConvRow& rw, ConvCol c0, int64_t f0, bool row_ok,
-                                            int64_t ones_col) {
+__device__ __forceinline__ u32x4 conv_row16(const ConvGeo& g, const ConvRow& rw,
+                                            const ConvCols<elem_traits<T>::per16>& k, bool row_ok) {
   constexpr int P = elem_traits<T>::per16;
   constexpr uint32_t one_bits = P == 8 ? 0x3F80u : 0x3F800000u;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (row_ok) {
+    const int y0 = rw.ho * g.sh - g.ph, x0 = rw.wo * g.sw - g.pw;
+    const int org = y0 * g.W + x0;
+    const T* __restrict__ ab = static_cast<const T*>(g.a) + rw.b * (int64_t)g.Cin * g.H * g.W;
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      uint32_t bits = k.one[e] ? one_bits : 0u;
+      if (k.in[e] && (unsigned)(y0 + k.dy[e]) < (unsigned)g.H && (unsigned)(x0 + k.dx[e]) < (unsigned)g.W)
+        bits = raw_bits(ab[k.off[e] + org]);
+      if constexpr (P == 8)
+        w[e >> 1] |= bits << (16 * (e & 1));
+      else
+        w[e] = bits;
+    }
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// conv_row16 for columns given by their first one (c0 = conv_col(g, f0)),
+// stepping the kernel offsets element by element: fewer registers than a
+// ConvCols set, which suits kernels that gather several rows per thread with
+// little reuse of the column set (the tiled ghost kernel).
+template <typename T>
+__device__ __forceinline__ u32x4 conv_row16_walk(const ConvGeo& g, const ConvRow& rw, ConvCol c0, int64_t f0,
+                                                 bool row_ok) {
+  constexpr int P = elem_traits<T>::per16;
   uint32_t w[4] = {0u, 0u, 0u, 0u};
   if (row_ok) {
     const int y0 = rw.ho * g.sh - g.ph, x0 = rw.wo * g.sw - g.pw;
@@ -186,13 +249,10 @@ __device__ __forceinline__ u32x4 conv_row16(const ConvGeo& g, const ConvRow& rw,
     int ci = c0.ci, i = c0.i, j = c0.j;
 #pragma unroll
     for (int e = 0; e < P; ++e) {
-      const int64_t f = f0 + e;
       uint32_t bits = 0u;
-      if (f < g.d) {
+      if (f0 + e < g.d) {
         const int y = y0 + i * g.dh, x = x0 + j * g.dw;
         if ((unsigned)y < (unsigned)g.H && (unsigned)x < (unsigned)g.W) bits = raw_bits(ab[(ci * g.H + y) * g.W + x]);
-      } else if (f == ones_col) {
-        bits = one_bits;
       }
       if constexpr (P == 8)
         w[e >> 1] |= bits << (16 * (e & 1));

@@ -145,7 +145,7 @@ __device__ __forceinline__ void ghost_load_conv(typename GhostCfg<T, TS>::Regs& 
     } else {
       const int grow = (h == 0 ? sb : tb) * TS + row;
       const bool ok = grow < g.T;
-      regs.v[r] = conv_row16<T>(g, conv_row_at(g, i, ok ? grow : 0), c0, col, ok, -1);
+      regs.v[r] = conv_row16_walk<T>(g, conv_row_at(g, i, ok ? grow : 0), c0, col, ok);
     }
   }
 }

@@ -133,11 +133,11 @@ struct Xty {
         static_assert(!FULL, "unfolded rows are formed with checks");
         if (isx) {
           // the unit's RU consecutive rows: one division for the first, then steps
-          const ConvCol c0 = conv_col(*geo, col);
+          const ConvCols<P> kc = conv_cols<P>(*geo, col, ones_col);
           ConvRow rw = conv_row_flat(*geo, cs.xrow + rr * RU);
 #pragma unroll
           for (int r = 0; r < RU; ++r) {
-            R.v[u][r] = conv_row16<T>(*geo, rw, c0, col, rr * RU + r < cs.rv, ones_col);
+            R.v[u][r] = conv_row16<T>(*geo, rw, kc, rr * RU + r < cs.rv);
             rw.next(*geo);
           }
           continue;

@@ -49,6 +49,12 @@ class PrivacyEngine:
     kept output gradients are the per-sample ones. A module may run once per
     forward pass. Any other trainable parameter makes the constructor fail:
     its per-sample gradient would go unclipped.
+
+    mode: the per-layer path rule ('ghost-mixed', 'ghost', 'explicit',
+    'time'). conv_input: 'unfolded' (torch unfolds each Conv2d input; the
+    layers share the multi-layer calls) or 'folded' (the library takes the
+    folded input and forms the unfolded rows in its kernels, one call per
+    Conv2d layer).
     """
 
     def __init__(self, model: torch.nn.Module, C: float, sigma: float, seed: int = 0, mode: str = "ghost-mixed",

@@ -351,6 +351,11 @@ def test_engine_refuses_unclipped_parameters():
         PrivacyEngine(torch.nn.Conv2d(4, 4, 3, groups=2), C=1.0, sigma=1.0)
     with pytest.raises(ValueError):
         PrivacyEngine(torch.nn.Linear(4, 4), C=1.0, sigma=1.0, mode="fast")
+    with pytest.raises(ValueError):
+        PrivacyEngine(torch.nn.Conv2d(3, 4, 3, padding="same"), C=1.0, sigma=1.0)
+    with pytest.raises(ValueError):
+        PrivacyEngine(torch.nn.Linear(4, 4), C=1.0, sigma=1.0, conv_input="im2col")
+    assert PrivacyEngine(torch.nn.Conv2d(3, 4, 3, padding="valid"), C=1.0, sigma=1.0, conv_input="folded").folded
     e = PrivacyEngine(torch.nn.Sequential(torch.nn.Conv2d(3, 4, 3), torch.nn.Flatten(), torch.nn.Linear(4, 2)),
                       C=1.0, sigma=1.0)
     assert len(e.layers) == 2
