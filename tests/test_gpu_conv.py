@@ -37,6 +37,7 @@ GEOMS = {  # B, C_in, H, W, kernel, stride, padding, dilation, p
     "valid-3x3": (2, 7, 13, 13, (3, 3), (1, 1), (0, 0), (1, 1), 130),    # T = 121, p ragged
     "late-3x3": (3, 20, 4, 4, (3, 3), (1, 1), (1, 1), (1, 1), 96),       # T = 16
     "t1": (4, 5, 6, 6, (6, 6), (1, 1), (0, 0), (1, 1), 24),              # one output position
+    "mid-3x3": (16, 128, 16, 16, (3, 3), (1, 1), (1, 1), (1, 1), 128),   # T = 256, d = 1152: 4 row blocks
 }
 
 
@@ -62,7 +63,7 @@ def _expected_path(T, d, p, mode):
 
 @pytest.mark.parametrize("name", sorted(GEOMS))
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("mode", [dpc.MODE_GHOST, dpc.MODE_EXPLICIT, dpc.MODE_MIXED])
+@pytest.mark.parametrize("mode", [dpc.MODE_GHOST, dpc.MODE_EXPLICIT, dpc.MODE_MIXED, dpc.MODE_TIME])
 def test_conv_norms(name, dtype, mode):
     geo, (U, Go), (a, G) = _case(name, dtype)
     B, T, d = U.shape
