@@ -63,6 +63,11 @@ int path_of(int64_t T, int64_t d, int64_t p, dp_mode mode, int32_t kappa) {
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
+// A dispatch's work-items (workgroups x threads) are counted in 32 bits; the
+// kernels run at most 512 threads per workgroup.
+constexpr uint64_t kMaxWorkgroups = (1ull << 32) / 512;
+bool grid_fits(uint64_t workgroups) { return workgroups < kMaxWorkgroups; }
+
 // a sample's tiles are counted in 16 bits of its arrival counter
 constexpr int64_t kMaxTilesPerSample = 65535;
 
@@ -132,7 +137,7 @@ hipError_t launch_layer_norm(hipStream_t st, int dtype, const void* A, const voi
 // and the ghost grid (32-bit workgroup ids).
 bool layer_fits(int dtype, int path, int64_t B, int64_t T, int64_t d, int64_t p, int hb) {
   const int64_t nt = norm_ntiles(dtype, path, T, d, p, hb);
-  if (path == DP_PATH_GHOST && (uint64_t)((B + 7) / 8 * 8) * (uint64_t)nt >= (1ull << 32)) return false;
+  if (!grid_fits((uint64_t)((B + 7) / 8 * 8) * (uint64_t)nt)) return false;  // ghost / explicit grids
   return nt <= kMaxTilesPerSample;
 }
 
@@ -191,7 +196,7 @@ int plan_norm_runs(const dp_layer* layers, int32_t n, dp_dtype dtype, int64_t B,
       if (r.grouped && r.count < dpk::kNormGroupMax &&
           dpk::ghost_group_key(dtype, f.T, f.d, f.p) == dpk::ghost_group_key(dtype, x.T, x.d, x.p) &&
           r.ntiles + nt <= kMaxTilesPerSample &&
-          (uint64_t)((B + 7) / 8 * 8) * (uint64_t)(r.ntiles + nt) < (1ull << 32)) {
+          grid_fits((uint64_t)((B + 7) / 8 * 8) * (uint64_t)(r.ntiles + nt))) {
         r.count += 1;
         r.ntiles += nt;
         continue;
@@ -532,7 +537,7 @@ dp_status dp_clipped_sum_noise_layers(void* stream, const dp_layer* layers, int3
     } else {
       const int hb = x0.has_bias ? 1 : 0;
       splans[k] = dpk::contract_plan(dtype, B, x0.T, x0.d, x0.p, hb);
-      if ((int64_t)splans[k].mt * splans[k].nt * splans[k].ks >= ((int64_t)1 << 31)) return DP_ERR_SHAPE;
+      if (!grid_fits((uint64_t)splans[k].mt * splans[k].nt * splans[k].ks)) return DP_ERR_SHAPE;
       need = std::max(need, contract_ws_for(splans[k], x0.d, x0.p, hb));
     }
   }
@@ -603,7 +608,7 @@ dp_status dp_clipped_sum_noise(void* stream, const void* A, const void* G, dp_dt
     if (ws_bytes < need) return DP_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return DP_ERR_ALIGN;
   }
-  if ((int64_t)pl.mt * pl.nt * pl.ks >= ((int64_t)1 << 31)) return DP_ERR_SHAPE;
+  if (!grid_fits((uint64_t)pl.mt * pl.nt * pl.ks)) return DP_ERR_SHAPE;
   s = device_ready();
   if (s != DP_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -637,7 +642,7 @@ dp_status dp_conv_norm(void* stream, const void* a, const void* G, const dp_conv
   const int path = conv_path(g.T, g.d, p, mode, kappa);
   const int64_t nt = conv_norm_ntiles(path, g.T, g.d, p, hb);
   if (nt > kMaxTilesPerSample) return DP_ERR_SHAPE;
-  if (path == DP_PATH_GHOST && (uint64_t)((B + 7) / 8 * 8) * (uint64_t)nt >= (1ull << 32)) return DP_ERR_SHAPE;
+  if (!grid_fits((uint64_t)((B + 7) / 8 * 8) * (uint64_t)nt)) return DP_ERR_SHAPE;
   const size_t need = conv_norm_ws_bytes(path, B, g.T, g.d, p, hb);
   if (need > 0) {
     if (!workspace) return DP_ERR_NULL;
@@ -676,7 +681,7 @@ dp_status dp_conv_clipped_sum_noise(void* stream, const void* a, const void* G, 
     if (ws_bytes < need) return DP_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return DP_ERR_ALIGN;
   }
-  if ((int64_t)pl.mt * pl.nt * pl.ks >= ((int64_t)1 << 31)) return DP_ERR_SHAPE;
+  if (!grid_fits((uint64_t)pl.mt * pl.nt * pl.ks)) return DP_ERR_SHAPE;
   s = device_ready();
   if (s != DP_OK) return s;
   return hip_status(dpk::launch_clipped_sum_conv(static_cast<hipStream_t>(stream), dtype, g, G, c, B, p, pl,
@@ -750,7 +755,7 @@ dp_status dp_clipped_sum_accumulate(void* stream, const void* A, const void* G, 
   if (!aligned(c, 4) || !aligned(acc, 4) || (bias_acc && !aligned(bias_acc, 4))) return DP_ERR_ALIGN;
   const int hb = bias_acc ? 1 : 0;
   const dpk::ContractPlan pl = dpk::contract_plan(dtype, B, T, d, p, hb);
-  if ((int64_t)pl.mt * pl.nt * pl.ks >= ((int64_t)1 << 31)) return DP_ERR_SHAPE;
+  if (!grid_fits((uint64_t)pl.mt * pl.nt * pl.ks)) return DP_ERR_SHAPE;
   const size_t cws = round256(contract_ws_for(pl, d, p, hb));
   const size_t need = accumulate ? cws + round256((size_t)(d + hb) * (size_t)p * sizeof(float)) : cws;
   if (need > 0) {

@@ -690,7 +690,7 @@ hipError_t launch_contract_dl_group(hipStream_t st, const DlLaunchLayer* layers,
     per_sum += L.per;
   }
   const int64_t wgs = 8 * per_sum;
-  if (wgs >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (wgs * 512 >= ((int64_t)1 << 32)) return hipErrorInvalidValue;  // work-items counted in 32 bits
   if (g.bn == 256) return launch_dl_t<256, 256, kDlWideStages, kDlWideKC, true>(st, c, grp, wgs);
   if (g.bm == 256) return launch_dl_t<256, 128, kDlStages, kDlKC, false>(st, c, grp, wgs);
   return launch_dl_t<128, 128, kDlStages, kDlKC, false>(st, c, grp, wgs);
