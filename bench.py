@@ -462,8 +462,8 @@ def main():
                     help="only run a plain 256 MiB device-to-device copy 5 times (HBM counter calibration)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the clipping path on a single MI355X "
-              "(the multi-GPU design is described, not built). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library runs the clipping path on a single MI355X "
+              "and has no multi-GPU path. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if a.copy_probe:
         copy_probe()
