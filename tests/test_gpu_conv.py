@@ -133,13 +133,14 @@ def test_conv_workspace_reuse_and_errors():
         dpc.dp_conv_norm(a, G, bad, sq)
 
 
-@pytest.mark.parametrize("l", [1, 7])
-def test_resnet_full_size_layer(l):
-    """ResNet-18 conv layers at the benchmark's size (B = 256): layer 1
-    (64 channels at 32x32, T = 1024, explicit path) and layer 7 (512 channels
-    at 4x4, T = 16, ghost path), from the folded input. Norms of sampled
-    examples and sampled entries of the clipped noised sum against the oracle
-    on U(a), formed per sample."""
+@pytest.mark.parametrize("mode", [dpc.MODE_MIXED, dpc.MODE_TIME])
+@pytest.mark.parametrize("l", range(8))
+def test_resnet_full_size_layer(l, mode):
+    """Every ResNet-18 conv layer of the benchmark at its size (B = 256) from
+    the folded input, under the space and the time path rules (from 3
+    channels at 32x32, T = 1024, to 512 channels at 4x4, T = 16; explicit and
+    ghost paths). Norms of sampled examples and sampled entries of the
+    clipped noised sum against the oracle on U(a), formed per sample."""
     wl = W.WORKLOADS["resnet18-conv-t1024"]
     fmap, Gn = W.make_folded(wl, l)
     cin, hin, win, stride = wl.conv[l]
@@ -149,8 +150,8 @@ def test_resnet_full_size_layer(l):
     p = Gn.shape[2]
     a, G = upload(fmap, "f32"), upload(Gn, "f32")
     sq = torch.empty(B, dtype=torch.float32, device=dev())
-    path = dpc.dp_conv_norm(a, G, geo, sq)
-    assert path == D.choose_path(T, d, p)
+    path = dpc.dp_conv_norm(a, G, geo, sq, mode=mode)
+    assert path == D.choose_path(T, d, p, mode)
     c_np = W.make_vector(B, 0.05, 1.0, tag=12)
     out = torch.empty(d, p, dtype=torch.float32, device=dev())
     dpc.dp_conv_clipped_sum_noise(a, G, geo, f32(c_np), wl.C, wl.sigma, float(B), wl.seed, l, 0, out)
