@@ -38,6 +38,8 @@ GEOMS = {  # B, C_in, H, W, kernel, stride, padding, dilation, p
     "late-3x3": (3, 20, 4, 4, (3, 3), (1, 1), (1, 1), (1, 1), 96),       # T = 16
     "t1": (4, 5, 6, 6, (6, 6), (1, 1), (0, 0), (1, 1), 24),              # one output position
     "mid-3x3": (16, 128, 16, 16, (3, 3), (1, 1), (1, 1), (1, 1), 128),   # T = 256, d = 1152: 4 row blocks
+    "b1-dil2": (1, 1, 5, 5, (3, 3), (1, 1), (2, 2), (2, 2), 3),          # one sample, one channel, d = 9
+    "wide-stride": (2, 3, 10, 17, (2, 5), (3, 4), (1, 2), (1, 1), 20),   # strides larger than the kernel rows
 }
 
 
