@@ -33,6 +33,18 @@ class _ConvNet(torch.nn.Module):
         return self.fc(torch.relu(self.conv2(torch.relu(self.conv(x)))).flatten(1))
 
 
+class _DilatedNet(torch.nn.Module):
+    """A rectangular, dilated, strided convolution with a bias, then a linear layer."""
+    def __init__(self, seed):
+        super().__init__()
+        torch.manual_seed(seed)
+        self.conv = torch.nn.Conv2d(3, 5, (3, 2), stride=(1, 2), padding=(2, 1), dilation=2)
+        self.fc = torch.nn.Linear(5 * 6 * 4, 2)
+
+    def forward(self, x):
+        return self.fc(torch.tanh(self.conv(x)).flatten(1))
+
+
 def _per_sample_loss(out, y):
     return ((out - y) ** 2).reshape(out.shape[0], -1).sum(dim=1)
 
@@ -54,7 +66,7 @@ def _reference(model, x, y, C, scale_grad_of=None):
     return dict(zip(names, mean)), norms
 
 
-@pytest.mark.parametrize("kind", ["mlp-sequence", "conv", "conv-folded"])
+@pytest.mark.parametrize("kind", ["mlp-sequence", "conv", "conv-folded", "dilated", "dilated-folded-time"])
 def test_engine_matches_per_example_backprop(kind):
     dev = torch.device("cuda", 0)
     g = torch.Generator().manual_seed(5)
@@ -63,15 +75,20 @@ def test_engine_matches_per_example_backprop(kind):
         x = torch.randn(6, 3, 12, generator=g)   # 6 samples of 3 positions
         y = torch.randn(6, 3, 5, generator=g)
         C = 20.0
-    else:
+    elif kind.startswith("conv"):
         model = _ConvNet(2)
         x = torch.randn(5, 3, 8, 8, generator=g)
         y = torch.randn(5, 3, generator=g)
         C = 4.0
+    else:
+        model = _DilatedNet(3)
+        x = torch.randn(6, 3, 6, 8, generator=g)   # -> 5 channels at 6 x 4
+        y = torch.randn(6, 2, generator=g)
+        C = 2.0
     ref, norms = _reference(model, x, y, C)
     model = model.to(dev)
-    engine = PrivacyEngine(model, C=C, sigma=0.0, seed=9,
-                           conv_input="folded" if kind == "conv-folded" else "unfolded")
+    engine = PrivacyEngine(model, C=C, sigma=0.0, seed=9, mode="time" if kind.endswith("time") else "ghost-mixed",
+                           conv_input="folded" if "folded" in kind else "unfolded")
     _per_sample_loss(model(x.to(dev)), y.to(dev)).sum().backward()
     n_gpu = engine.step(0)
     np.testing.assert_allclose(n_gpu.cpu().numpy(), norms.numpy(), rtol=1e-4)
