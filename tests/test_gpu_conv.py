@@ -170,3 +170,30 @@ def test_resnet_full_size_layer(l, mode):
     z = N.weight_noise_at(rows, cols, p, wl.seed, l, 0)
     assert_noised(out.cpu().numpy()[rows, cols], D.noised_mean(S_or, z, wl.C, wl.sigma, B), S_or,
                   wl.sigma * wl.C * z / B, "f32", B)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_conv_folded_input_at_an_element_offset(dtype):
+    """The folded input needs element alignment only: the same values starting
+    one element into a buffer (4- or 2-byte aligned, not 16) give the same
+    norms and sums bit for bit as the aligned copy."""
+    geo, (U, Go), (a, G) = _case("rect-dil", dtype)
+    B = U.shape[0]
+    d, p = U.shape[2], Go.shape[2]
+    buf = torch.empty(a.numel() + 1, dtype=a.dtype, device=dev())
+    a_off = buf[1:].view(a.shape)
+    a_off.copy_(a)
+    assert a_off.data_ptr() % 16 != 0
+    c = f32(W.make_vector(B, 0.05, 1.0, tag=14))
+    res = []
+    for x in (a, a_off):
+        sq = torch.empty(B, dtype=torch.float32, device=dev())
+        out = torch.empty(d, p, dtype=torch.float32, device=dev())
+        bout = torch.empty(p, dtype=torch.float32, device=dev())
+        dpc.dp_conv_norm(x, G, geo, sq, has_bias=True, mode=dpc.MODE_GHOST)
+        dpc.dp_conv_clipped_sum_noise(x, G, geo, c, 1.0, 0.5, float(B), 3, 1, 0, out, bias_out=bout)
+        torch.cuda.synchronize()
+        res.append((sq.cpu().numpy(), out.cpu().numpy(), bout.cpu().numpy()))
+    for r0, r1 in zip(res[0], res[1]):
+        np.testing.assert_array_equal(r0.view(np.uint32), r1.view(np.uint32))
+    assert_norms(res[0][0], D.layer_sqnorms(U, Go, has_bias=True), dtype)
