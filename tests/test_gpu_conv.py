@@ -197,3 +197,26 @@ def test_conv_folded_input_at_an_element_offset(dtype):
     for r0, r1 in zip(res[0], res[1]):
         np.testing.assert_array_equal(r0.view(np.uint32), r1.view(np.uint32))
     assert_norms(res[0][0], D.layer_sqnorms(U, Go, has_bias=True), dtype)
+
+
+def test_conv_calls_deterministic_and_on_a_given_stream():
+    """Repeated calls give the same bits; a call on a side stream (stream=)
+    gives the bits of the call on the current stream."""
+    geo, (U, Go), (a, G) = _case("mid-3x3", "bf16")
+    B, d, p = U.shape[0], U.shape[2], Go.shape[2]
+    c = f32(W.make_vector(B, 0.05, 1.0, tag=15))
+    side = torch.cuda.Stream(device=dev())
+
+    def run(stream):
+        sq = torch.empty(B, dtype=torch.float32, device=dev())
+        out = torch.empty(d, p, dtype=torch.float32, device=dev())
+        dpc.dp_conv_norm(a, G, geo, sq, mode=dpc.MODE_MIXED, stream=stream)
+        dpc.dp_conv_clipped_sum_noise(a, G, geo, c, 1.0, 1.0, float(B), 5, 2, 9, out, stream=stream)
+        torch.cuda.synchronize()
+        return sq.cpu().numpy().view(np.uint32), out.cpu().numpy().view(np.uint32)
+
+    torch.cuda.synchronize()  # inputs are ready before the side stream reads them
+    r0, r1, r2 = run(None), run(None), run(side)
+    for x, y, z in zip(r0, r1, r2):
+        np.testing.assert_array_equal(x, y)
+        np.testing.assert_array_equal(x, z)
