@@ -625,7 +625,7 @@ size_t dp_conv_workspace_bytes(const dp_conv2d* conv, dp_dtype dtype, int64_t B,
   if (mode < DP_MODE_MIXED || mode > DP_MODE_TIME || kappa < 1) return 0;
   const int hb = has_bias ? 1 : 0;
   const size_t a = conv_norm_ws_bytes(conv_path(g.T, g.d, p, mode, kappa), B, g.T, g.d, p, hb);
-  const size_t b = conv_sum_ws_bytes(dpk::tiles_plan(dtype, B, g.T, g.d, p, hb), g.d, p, hb);
+  const size_t b = conv_sum_ws_bytes(dpk::tiles_plan(dtype, B, g.T, g.d, p, hb, true), g.d, p, hb);
   return std::max(a, b);
 }
 
@@ -674,7 +674,7 @@ dp_status dp_conv_clipped_sum_noise(void* stream, const void* a, const void* G, 
   if (!finite(C) || !(C > 0.0f) || !finite(sigma) || sigma < 0.0f || !finite(denom) || !(denom > 0.0f))
     return DP_ERR_VALUE;
   const int hb = bias_out ? 1 : 0;
-  const dpk::ContractPlan pl = dpk::tiles_plan(dtype, B, g.T, g.d, p, hb);
+  const dpk::ContractPlan pl = dpk::tiles_plan(dtype, B, g.T, g.d, p, hb, true);
   const size_t need = conv_sum_ws_bytes(pl, g.d, p, hb);
   if (need > 0) {
     if (!workspace) return DP_ERR_NULL;

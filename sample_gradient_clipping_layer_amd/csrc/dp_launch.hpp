@@ -124,7 +124,8 @@ uint64_t next_epoch();
 // Convolution layers given by their folded input (ConvGeo): the unfolded
 // rows are formed on chip by the tiled ghost, explicit and register-staged
 // contraction kernels; G is [B, geo.T, p]. The contraction plan is tiles_plan.
-ContractPlan tiles_plan(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias);
+// `folded`: the plan of a folded-input convolution.
+ContractPlan tiles_plan(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias, bool folded);
 hipError_t launch_ghost_conv(hipStream_t st, int dtype, const ConvGeo& geo, const void* G, int64_t B, int64_t p,
                              int has_bias, const NormSink& sink);
 hipError_t launch_explicit_conv(hipStream_t st, int dtype, const ConvGeo& geo, const void* G, int64_t B, int64_t p,
