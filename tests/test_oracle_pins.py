@@ -529,3 +529,92 @@ def test_newton_reciprocal_and_rsqrt():
     assert np.max(np.abs(y * np.sqrt(t.astype(np.float64)) - 1.0)) < 2e-7
     z0, z1 = N.box_muller_f32(np.array([0xFFFFFFFF], dtype=np.uint32), np.array([5], dtype=np.uint32))
     assert z0[0] == 0.0 and z1[0] == 0.0   # u1 = 1 gives r = 0
+
+
+def _stream_positions(values, stream):
+    """Position in `stream` of every entry of `values`, found by value (no
+    index formula): a dict from fp32 bit pattern to the list of positions
+    where it occurs. Returns (positions, ambiguous) where ambiguous counts
+    the values that occur more than once in the stream."""
+    where = {}
+    for k, b in enumerate(stream.view(np.uint32).tolist()):
+        where.setdefault(b, []).append(k)
+    pos, amb = [], 0
+    for b in values.reshape(-1).view(np.uint32).tolist():
+        ks = where.get(b)
+        assert ks is not None, "a noise value that the stream does not hold"
+        amb += len(ks) > 1
+        pos.append(ks[0])
+    return np.array(pos, dtype=np.int64), amb
+
+
+@pytest.mark.parametrize("d,p", [(7, 5), (8, 1), (1, 9), (13, 3), (64, 32), (5, 17)])
+def test_weight_noise_draws_distinct_normals_of_its_stream(d, p):
+    """[FPC] Gaussian mechanism and [SEDP] eq. (2.1): the noise added to the
+    [d, p] clipped sum is N(0, sigma^2 C^2 I), every coordinate its own
+    independent normal. Located by value in the flat weight stream
+    (which = 0) of the first ceil(d/4)*p blocks: every entry of
+    weight_noise(d, p) is there, no two entries share one position (a map
+    that reused a normal fails), and the entries touch exactly those
+    ceil(d/4)*p blocks (a map that skipped or overran blocks fails). The bias
+    noise of [p] is the first p normals of the which = 1 stream, in order, and
+    shares no value with the weight noise."""
+    seed, layer, step = 0xABCDEF12345, 3, 9
+    nq = -(-d // 4)
+    z = N.weight_noise(d, p, seed, layer, step)
+    assert z.shape == (d, p) and z.dtype == np.float32
+    stream = N.normals(4 * nq * p + 64, seed, layer, 0, step)
+    pos, amb = _stream_positions(z, stream)
+    assert amb == 0
+    assert len(set(pos.tolist())) == d * p                       # injective
+    assert pos.max() < 4 * nq * p                                # nothing past the blocks it needs
+    assert set((pos // 4).tolist()) == set(range(nq * p))        # every needed block used
+    zb = N.normals(p, seed, layer, 1, step)
+    bstream = N.normals(p + 8, seed, layer, 1, step)
+    bpos, bamb = _stream_positions(zb, bstream)
+    assert bamb == 0 and bpos.tolist() == list(range(p))
+    assert not (set(zb.view(np.uint32).tolist()) & set(z.reshape(-1).view(np.uint32).tolist()))
+
+
+def test_weight_noise_array_has_the_gaussian_law():
+    """The [d, p] weight-noise array (and the [p] bias noise) as a sample of
+    N(0, I): mean, variance and KS distance of all entries, and lag-1
+    correlations along rows, along columns and across the 4-row groups that
+    share a Philox block, each within 5/sqrt(n). Sizes are ragged (d % 4 != 0)
+    so the partial last group is included. A layout that repeated or
+    correlated normals within the array would fail the lag tests; one that
+    biased the lanes would fail the moments."""
+    from scipy.special import ndtr
+    d, p = 2051, 997
+    z = N.weight_noise(d, p, 77, 5, 2).astype(np.float64)
+    n = z.size
+    assert abs(z.mean()) <= 5 / math.sqrt(n)
+    assert abs(z.var() - 1.0) <= 5 * math.sqrt(2 / n)
+    zs = np.sort(z.reshape(-1))
+    cdf = ndtr(zs)
+    ks = max(np.max(np.arange(1, n + 1) / n - cdf), np.max(cdf - np.arange(0, n) / n))
+    assert ks < 2.7 / math.sqrt(n)
+
+    def lag_corr(x, y):
+        x = x.reshape(-1) - x.mean()
+        y = y.reshape(-1) - y.mean()
+        return float(np.dot(x, y) / math.sqrt(np.dot(x, x) * np.dot(y, y))), x.size
+
+    for a, b in [(z[:, :-1], z[:, 1:]),          # along rows (neighbouring columns)
+                 (z[:-1, :], z[1:, :]),          # along columns (neighbouring rows)
+                 (z[0:-4:4, :], z[3::4, :][: (d - 1) // 4]),   # first and last lane of a block
+                 (z[:-4, :], z[4:, :])]:         # the same lane of consecutive blocks
+        r, m = lag_corr(a, b)
+        assert abs(r) <= 5 / math.sqrt(m), r
+    # per-lane moments: no lane of the 4-row groups is biased
+    for lane in range(4):
+        zl = z[lane::4, :]
+        assert abs(zl.mean()) <= 5 / math.sqrt(zl.size)
+        assert abs(zl.var() - 1.0) <= 5 * math.sqrt(2 / zl.size)
+    zb = N.normals(200_003, 77, 5, 1, 2).astype(np.float64)
+    assert abs(zb.mean()) <= 5 / math.sqrt(zb.size)
+    assert abs(zb.var() - 1.0) <= 5 * math.sqrt(2 / zb.size)
+    r, m = lag_corr(zb[:-1], zb[1:])
+    assert abs(r) <= 5 / math.sqrt(m)
+    r, m = lag_corr(zb[:100_000], z.reshape(-1)[:100_000])   # bias vs weight stream
+    assert abs(r) <= 5 / math.sqrt(m)
