@@ -125,6 +125,10 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
     set_bytes = sum(B * T * (d + p) * eb for (T, d, p) in shapes)
     n_sets = max(1, min(4, math.ceil(2 * CACHE_BYTES / set_bytes) + 1)) if set_bytes < 4 * CACHE_BYTES else 1
     on_device = set_bytes > DEVICE_GEN_BYTES
+    if wl.per_layer and wl.steps > 1:
+        # the adaptive schedule draws fresh inputs every step: one set per step of the
+        # schedule, drawn on the device (4.8 GB each for the B = 65536 MLP)
+        n_sets, on_device = wl.steps, True
 
     def up(x):
         if wl.dtype == "bf16":
@@ -178,12 +182,16 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
         c = [torch.empty(B, dtype=torch.float32, device=dev) for _ in range(L)]
         nrm = [torch.empty(B, dtype=torch.float32, device=dev) for _ in range(L)]
         C_next = torch.empty(L, dtype=torch.float32, device=dev)
-        # initial bounds: one adaptive-threshold init call per layer on the first input set
-        for l, (A, G) in enumerate(sets[0]):
+        # initial bounds: one adaptive-threshold init call per layer on an initialisation batch of
+        # random-noise inputs (step -1 of the generator), apart from the training sets: the first
+        # bound then depends on no training data
+        for l in range(L):
+            A, G = W.make_layer_device(wl, l, dev, step=-1)
             dpc.dp_ghost_norm(A, G, sq[l], has_bias=wl.has_bias, mode=mode, workspace=ws[l])
             dpc.dp_clip_factors(sq[l], 3.0e38, c[l], nrm[l])
             dpc.dp_adaptive_threshold(nrm[l], 1.0, wl.alpha, wl.beta, wl.sigma_l2, True, wl.seed, l, 0,
                                       C_next[l:l + 1])
+            del A, G
         C_t = [float(v) for v in C_next.tolist()]
         kinds = [(kd, l) for l in range(L) for kd in ("norm", "clip", "sum", "thr")]
     else:
@@ -409,8 +417,11 @@ def cpu_baseline(wl, budget_s=12.0, step_s=3.0, max_step_s=25.0):
             break
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    host_cores = len(os.sched_getaffinity(0))
     what = f"first {nl} of {wl.n_layers} layers" if nl < wl.n_layers else f"all {nl} layers"
-    return {"value": b * n / dt * scale, "unit": "examples/s", "cores": int(threads), "kind": "oracle",
+    # cores: the threads the oracle actually ran on (its BLAS pool; the rest of it is one Python thread)
+    return {"value": b * n / dt * scale, "unit": "examples/s", "cores": int(min(threads, host_cores)),
+            "host_cores": int(host_cores), "blas_threads": int(threads), "kind": "oracle",
             "sample": f"{n} whole step(s) of {wl.name} on {b} of {wl.B} examples, {what} "
                       f"(fp64 numpy, materialised per-example gradients), {dt:.1f} s"
                       + (f"; rate scaled by {nl}/{wl.n_layers} layers" if nl < wl.n_layers else "")}
@@ -439,7 +450,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gpt-block-t128", choices=W.WORKLOAD_ORDER)
+    # default: the largest configuration that fits one GPU (GPT-2-large-shaped decoder stack)
+    ap.add_argument("--workload", default="gpt2large-t1024", choices=W.WORKLOAD_ORDER)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="print per-call times to stderr")
     ap.add_argument("--per-layer-norms", action="store_true",
@@ -558,6 +570,11 @@ def main():
         cfg["logical_batch"] = wl.B * a.virtual_steps
     if on_device:
         cfg["inputs"] = "drawn on the device (torch generator), distinct for every layer"
+    if wl.per_layer and wl.steps > 1:
+        cfg["inputs"] = (f"drawn on the device (torch generator): fresh A and G for each of the {wl.steps} "
+                         f"steps of the adaptive schedule (step k uses set k mod {n_sets}); the initial bounds "
+                         f"from a separate random-noise batch")
+        cfg["schedule_steps"] = wl.steps
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "examples/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",

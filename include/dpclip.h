@@ -20,6 +20,11 @@
  *  - Every argument is validated before any HIP call. A failed validation
  *    returns its code and touches nothing. HIP launch failures return
  *    DP_ERR_HIP; no usable device returns DP_ERR_NO_DEVICE.
+ *  - Calls may be captured into a HIP graph and replayed: they enqueue kernel
+ *    launches only (no memset, copy or allocation), and each arrival counter
+ *    is returned to zero arrivals by the last arrival of its launch, so a
+ *    replay with the captured tag counts from zero again. Buffers captured by
+ *    pointer keep their addresses across replays, as graphs require.
  *
  * Page keys used in the comments:
  *  FPC  "Scaling up Differentially Private Deep Learning with Fast Per-Example
@@ -299,6 +304,11 @@ dp_status dp_noise_mean(void* stream, const float* acc, const float* bias_acc, i
  * lane 0. By convention `step` is the index t of the bound C_t being produced.
  *
  *  norm     [B] fp32 device per-example norms of the layer (previous step).
+ *           With init != 0, C_l2 is their plain mean with no noise added, so
+ *           they must come from a data-independent batch: TTP initialises
+ *           C_l2,0 from one iteration on random noise. Norms of private
+ *           training data there would make C_l2 and the noise scale
+ *           sigma_l2 * C_l2 depend on that data without protection.
  *  C_prev   previous bound (host); must be finite and > 0 unless init != 0.
  *  alpha, beta > 0, sigma_l2 >= 0, finite.
  *  C_next   fp32 device scalar out; C_l2_out fp32 device scalar out (may be NULL).

@@ -225,12 +225,53 @@ def dp_status_string(status: int) -> str:
     return lib().dp_status_string(status).decode()
 
 
-def _workspace(workspace, dt, B, T, d, p, mode, kappa, device):
+def _scratch(nbytes: int, device, stream=None):
+    """A workspace of at least nbytes (>= 256) that the binding allocates for
+    one call. torch's caching allocator ties a block to the stream current at
+    allocation; when the call runs on another stream, record_stream keeps the
+    block from being handed out again before that stream has passed the call
+    (the library keeps every buffer in use until then)."""
     import torch
-    need = dp_workspace_bytes(dt, B, T, d, p, mode, kappa)
+    ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        ws.record_stream(stream)
+    return ws
+
+
+def _ws_bytes(workspace) -> int:
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return workspace.numel() * workspace.element_size()
+
+
+def _workspace(workspace, dt, B, T, d, p, mode, kappa, device, stream=None):
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
-    return workspace, workspace.numel() * workspace.element_size()
+        workspace = _scratch(dp_workspace_bytes(dt, B, T, d, p, mode, kappa), device, stream)
+    return workspace, _ws_bytes(workspace)
+
+
+def _bias_ptrs(vecs, arr, n, name):
+    """ctypes array of the per-layer bias vectors (None where a layer has no
+    bias). Entry l must be a contiguous float32 GPU vector of p_l elements
+    when layer l has a bias; entries of layers without one are ignored."""
+    if vecs is None:
+        if any(arr[k].has_bias for k in range(n)):
+            raise ValueError(f"{name} is required when a layer has a bias")
+        return None
+    if len(vecs) != n:
+        raise ValueError(f"one {name} entry (or None) per layer")
+    ptrs = []
+    for k, b in enumerate(vecs):
+        if not arr[k].has_bias:
+            ptrs.append(None)
+            continue
+        if b is None:
+            raise ValueError(f"{name}[{k}] is required: layer {k} has a bias")
+        _f32_vec(b, f"{name}[{k}]")
+        if b.numel() != arr[k].p:
+            raise ValueError(f"{name}[{k}] must have p = {arr[k].p} elements")
+        ptrs.append(b.data_ptr())
+    return (ctypes.c_void_p * n)(*ptrs)
 
 
 def dp_ghost_norm(A, G, sqnorm, has_bias: bool = False, mode: int = MODE_MIXED, kappa: int = 1,
@@ -239,7 +280,7 @@ def dp_ghost_norm(A, G, sqnorm, has_bias: bool = False, mode: int = MODE_MIXED, 
     _f32_vec(sqnorm, "sqnorm")
     if sqnorm.numel() != B:
         raise ValueError("sqnorm must have B elements")
-    ws, nbytes = _workspace(workspace, dt, B, T, d, p, mode, kappa, A.device)
+    ws, nbytes = _workspace(workspace, dt, B, T, d, p, mode, kappa, A.device, stream)
     path = ctypes.c_int32(0)
     _check("dp_ghost_norm", lib().dp_ghost_norm(_stream(stream), _ptr(A), _ptr(G), dt, B, T, d, p, int(bool(has_bias)),
                                                 int(mode), int(kappa), _ptr(ws), nbytes, _ptr(sqnorm),
@@ -275,37 +316,35 @@ def dp_layers_workspace_bytes(layers, has_bias=False, mode: int = MODE_MIXED, ka
 def dp_ghost_norm_layers(layers, sqnorm, has_bias=False, mode: int = MODE_MIXED, kappa: int = 1,
                          accumulate: bool = False, workspace=None, stream=None):
     """Squared norms summed over `layers` (a list of (A, G) pairs) into sqnorm."""
-    import torch
     dt, B, arr = _layer_table(layers, has_bias)
     _f32_vec(sqnorm, "sqnorm")
     if sqnorm.numel() != B:
         raise ValueError("sqnorm must have B elements")
     if workspace is None:
-        need = int(lib().dp_layers_workspace_bytes(arr, len(layers), dt, B, int(mode), int(kappa)))
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=sqnorm.device)
+        workspace = _scratch(lib().dp_layers_workspace_bytes(arr, len(layers), dt, B, int(mode), int(kappa)),
+                             sqnorm.device, stream)
     paths = (ctypes.c_int32 * len(layers))()
     _check("dp_ghost_norm_layers", lib().dp_ghost_norm_layers(
         _stream(stream), arr, len(layers), dt, B, int(mode), int(kappa), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _ptr(sqnorm), int(bool(accumulate)), paths))
+        _ws_bytes(workspace), _ptr(sqnorm), int(bool(accumulate)), paths))
     return list(paths)
 
 
 def dp_ghost_norm_clip_layers(layers, sqnorm, C: float, c, norm=None, has_bias=False, mode: int = MODE_MIXED,
                               kappa: int = 1, accumulate: bool = False, workspace=None, stream=None):
     """dp_ghost_norm_layers plus the clip factors (and norms) of the result, in the same pass."""
-    import torch
     dt, B, arr = _layer_table(layers, has_bias)
     for t, nm in ((sqnorm, "sqnorm"), (c, "c")) + (((norm, "norm"),) if norm is not None else ()):
         _f32_vec(t, nm)
         if t.numel() != B:
             raise ValueError(f"{nm} must have B elements")
     if workspace is None:
-        need = int(lib().dp_layers_workspace_bytes(arr, len(layers), dt, B, int(mode), int(kappa)))
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=sqnorm.device)
+        workspace = _scratch(lib().dp_layers_workspace_bytes(arr, len(layers), dt, B, int(mode), int(kappa)),
+                             sqnorm.device, stream)
     paths = (ctypes.c_int32 * len(layers))()
     _check("dp_ghost_norm_clip_layers", lib().dp_ghost_norm_clip_layers(
         _stream(stream), arr, len(layers), dt, B, int(mode), int(kappa), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _ptr(sqnorm), int(bool(accumulate)), float(C), _ptr(c),
+        _ws_bytes(workspace), _ptr(sqnorm), int(bool(accumulate)), float(C), _ptr(c),
         _ptr(norm), paths))
     return list(paths)
 
@@ -314,7 +353,6 @@ def dp_clipped_sum_noise_layers(layers, c, C: float, sigma: float, denom: float,
                                 bias_outs=None, has_bias=False, layer_ids=None, workspace=None, stream=None):
     """Clipped noised means of `layers` (a list of (A, G) pairs) under one c
     into outs[l] ([d_l, p_l]); bias_outs[l] for the layers with a bias."""
-    import torch
     dt, B, arr = _layer_table(layers, has_bias)
     n = len(layers)
     _f32_vec(c, "c")
@@ -324,25 +362,26 @@ def dp_clipped_sum_noise_layers(layers, c, C: float, sigma: float, denom: float,
         _f32_vec(o, "outs[k]")
         if o.numel() != arr[k].d * arr[k].p:
             raise ValueError(f"outs[{k}] must have d*p elements")
-    bptr = None
-    if bias_outs is not None:
-        if len(bias_outs) != n:
-            raise ValueError("one bias output (or None) per layer")
-        bptr = (ctypes.c_void_p * n)(*[None if b is None else b.data_ptr() for b in bias_outs])
-    ids = None if layer_ids is None else (ctypes.c_uint32 * n)(*[int(v) & 0xFFFFFFFF for v in layer_ids])
+    bptr = _bias_ptrs(bias_outs, arr, n, "bias_outs")
+    ids = None
+    if layer_ids is not None:
+        ids_list = [int(v) for v in layer_ids]
+        if len(ids_list) != n:
+            raise ValueError("layer_ids must hold one id per layer")
+        if any(v < 0 or v > 0xFFFFFFFF for v in ids_list) or len(set(ids_list)) != n:
+            raise ValueError("layer_ids must be distinct uint32 values (each layer its own noise stream)")
+        ids = (ctypes.c_uint32 * n)(*ids_list)
     if workspace is None:
-        need = int(lib().dp_layers_workspace_bytes(arr, n, dt, B, MODE_MIXED, 1))
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=c.device)
+        workspace = _scratch(lib().dp_layers_workspace_bytes(arr, n, dt, B, MODE_MIXED, 1), c.device, stream)
     optr = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
     _check("dp_clipped_sum_noise_layers", lib().dp_clipped_sum_noise_layers(
         _stream(stream), arr, n, dt, B, _ptr(c), float(C), float(sigma), float(denom),
         int(seed) & 0xFFFFFFFFFFFFFFFF, ids, int(step) & 0xFFFFFFFF, _ptr(workspace),
-        workspace.numel() * workspace.element_size(), optr, bptr))
+        _ws_bytes(workspace), optr, bptr))
 
 
 def dp_clipped_sum_accumulate(A, G, c, acc, bias_acc=None, accumulate: bool = False, workspace=None, stream=None):
     """acc (+)= the clipped sum of one physical batch (no noise, no mean)."""
-    import torch
     dt, B, T, d, p = _layer(A, G)
     _f32_vec(c, "c")
     _f32_vec(acc, "acc")
@@ -353,17 +392,16 @@ def dp_clipped_sum_accumulate(A, G, c, acc, bias_acc=None, accumulate: bool = Fa
         if bias_acc.numel() != p:
             raise ValueError("bias_acc must have p elements")
     if workspace is None:
-        need = int(lib().dp_accumulate_workspace_bytes(dt, B, T, d, p, int(bias_acc is not None)))
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=A.device)
+        workspace = _scratch(lib().dp_accumulate_workspace_bytes(dt, B, T, d, p, int(bias_acc is not None)),
+                             A.device, stream)
     _check("dp_clipped_sum_accumulate", lib().dp_clipped_sum_accumulate(
         _stream(stream), _ptr(A), _ptr(G), dt, B, T, d, p, _ptr(c), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _ptr(acc), _ptr(bias_acc), int(bool(accumulate))))
+        _ws_bytes(workspace), _ptr(acc), _ptr(bias_acc), int(bool(accumulate))))
 
 
 def dp_clipped_sum_accumulate_layers(layers, c, accs, bias_accs=None, has_bias=False, accumulate: bool = False,
                                      workspace=None, stream=None):
     """accs[l] (+)= the clipped sum of layer l over one physical batch (no noise, no mean)."""
-    import torch
     dt, B, arr = _layer_table(layers, has_bias)
     n = len(layers)
     _f32_vec(c, "c")
@@ -373,17 +411,12 @@ def dp_clipped_sum_accumulate_layers(layers, c, accs, bias_accs=None, has_bias=F
         _f32_vec(a, "accs[k]")
         if a.numel() != arr[k].d * arr[k].p:
             raise ValueError(f"accs[{k}] must have d*p elements")
-    bptr = None
-    if bias_accs is not None:
-        if len(bias_accs) != n:
-            raise ValueError("one bias accumulator (or None) per layer")
-        bptr = (ctypes.c_void_p * n)(*[None if b is None else b.data_ptr() for b in bias_accs])
+    bptr = _bias_ptrs(bias_accs, arr, n, "bias_accs")
     if workspace is None:
-        need = int(lib().dp_layers_accumulate_workspace_bytes(arr, n, dt, B))
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=c.device)
+        workspace = _scratch(lib().dp_layers_accumulate_workspace_bytes(arr, n, dt, B), c.device, stream)
     aptr = (ctypes.c_void_p * n)(*[a.data_ptr() for a in accs])
     _check("dp_clipped_sum_accumulate_layers", lib().dp_clipped_sum_accumulate_layers(
-        _stream(stream), arr, n, dt, B, _ptr(c), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream), arr, n, dt, B, _ptr(c), _ptr(workspace), _ws_bytes(workspace),
         aptr, bptr, int(bool(accumulate))))
 
 
@@ -430,7 +463,7 @@ def dp_clipped_sum_noise(A, G, c, C: float, sigma: float, denom: float, seed: in
         _f32_vec(bias_out, "bias_out")
         if bias_out.numel() != p:
             raise ValueError("bias_out must have p elements")
-    ws, nbytes = _workspace(workspace, dt, B, T, d, p, MODE_MIXED, 1, A.device)
+    ws, nbytes = _workspace(workspace, dt, B, T, d, p, MODE_MIXED, 1, A.device, stream)
     _check("dp_clipped_sum_noise", lib().dp_clipped_sum_noise(
         _stream(stream), _ptr(A), _ptr(G), dt, B, T, d, p, _ptr(c), float(C), float(sigma), float(denom),
         int(seed) & 0xFFFFFFFFFFFFFFFF, int(layer_id) & 0xFFFFFFFF, int(step) & 0xFFFFFFFF, _ptr(ws), nbytes,
@@ -439,6 +472,10 @@ def dp_clipped_sum_noise(A, G, c, C: float, sigma: float, denom: float, seed: in
 
 def dp_adaptive_threshold(norm, C_prev: float, alpha: float, beta: float, sigma_l2: float, init: bool, seed: int,
                           layer_id: int, step: int, C_next, C_l2_out=None, stream=None):
+    """One update of TTP's adaptive per-layer bound into C_next (a device
+    scalar). With init=True, C_l2 is the plain mean of `norm` (no noise): those
+    norms must come from a data-independent batch (TTP: one iteration on
+    random noise), never from private training data."""
     _f32_vec(norm, "norm")
     _f32_vec(C_next, "C_next")
     if C_l2_out is not None:
@@ -471,12 +508,10 @@ def dp_conv_workspace_bytes(conv: DpConv2d, dtype: int, B: int, p: int, has_bias
                                              int(kappa)))
 
 
-def _conv_ws(workspace, conv, dt, B, p, has_bias, mode, kappa, device):
-    import torch
+def _conv_ws(workspace, conv, dt, B, p, has_bias, mode, kappa, device, stream=None):
     if workspace is None:
-        need = dp_conv_workspace_bytes(conv, dt, B, p, has_bias, mode, kappa)
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
-    return workspace, workspace.numel() * workspace.element_size()
+        workspace = _scratch(dp_conv_workspace_bytes(conv, dt, B, p, has_bias, mode, kappa), device, stream)
+    return workspace, _ws_bytes(workspace)
 
 
 def dp_conv_norm(a, G, conv: DpConv2d, sqnorm, has_bias: bool = False, mode: int = MODE_MIXED, kappa: int = 1,
@@ -487,7 +522,7 @@ def dp_conv_norm(a, G, conv: DpConv2d, sqnorm, has_bias: bool = False, mode: int
     _f32_vec(sqnorm, "sqnorm")
     if sqnorm.numel() != B:
         raise ValueError("sqnorm must have B elements")
-    ws, nbytes = _conv_ws(workspace, conv, dt, B, p, has_bias, mode, kappa, a.device)
+    ws, nbytes = _conv_ws(workspace, conv, dt, B, p, has_bias, mode, kappa, a.device, stream)
     path = ctypes.c_int32(0)
     _check("dp_conv_norm", lib().dp_conv_norm(_stream(stream), _ptr(a), _ptr(G), ctypes.byref(conv), dt, B, p,
                                               int(bool(has_bias)), int(mode), int(kappa), _ptr(ws), nbytes,
@@ -507,7 +542,7 @@ def dp_conv_clipped_sum_noise(a, G, conv: DpConv2d, c, C: float, sigma: float, d
         _f32_vec(bias_out, "bias_out")
         if bias_out.numel() != p:
             raise ValueError("bias_out must have p elements")
-    ws, nbytes = _conv_ws(workspace, conv, dt, B, p, bias_out is not None, MODE_MIXED, 1, a.device)
+    ws, nbytes = _conv_ws(workspace, conv, dt, B, p, bias_out is not None, MODE_MIXED, 1, a.device, stream)
     _check("dp_conv_clipped_sum_noise", lib().dp_conv_clipped_sum_noise(
         _stream(stream), _ptr(a), _ptr(G), ctypes.byref(conv), dt, B, p, _ptr(c), float(C), float(sigma),
         float(denom), int(seed) & 0xFFFFFFFFFFFFFFFF, int(layer_id) & 0xFFFFFFFF, int(step) & 0xFFFFFFFF, _ptr(ws),

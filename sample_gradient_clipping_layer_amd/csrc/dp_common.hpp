@@ -306,15 +306,23 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Arrival counter of a group of `total` workgroups: bits 63..16 hold the
 // call's epoch, bits 15..0 the arrivals of that call. A value left by an
 // earlier call (another epoch) counts as zero, so the counters need no
-// clearing between calls. Returns true for the last arrival. The CAS loop
-// retries only when another workgroup's update succeeded.
+// clearing between calls. Returns true for the last arrival, which also puts
+// the counter back to zero arrivals of this epoch: every arrival of the launch
+// has been counted by then, so a later launch with the same epoch (a replay of
+// a captured HIP graph, where the kernel arguments are fixed) starts from zero
+// as well. The CAS loop retries only when another workgroup's update
+// succeeded. Callers order their data with a release fence before the
+// arrival and an acquire fence after the last one.
 __device__ __forceinline__ bool arrive_last(unsigned long long* ctr, uint64_t epoch, uint32_t total) {
   unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (;;) {
     const unsigned long long nv = ((old >> 16) == epoch) ? old + 1ull : ((epoch << 16) | 1ull);
     if (__hip_atomic_compare_exchange_strong(ctr, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT))
-      return (uint32_t)(nv & 0xFFFFull) == total;
+                                             __HIP_MEMORY_SCOPE_AGENT)) {
+      const bool last = (uint32_t)(nv & 0xFFFFull) == total;
+      if (last) __hip_atomic_store(ctr, epoch << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return last;
+    }
   }
 }
 
@@ -380,9 +388,10 @@ inline NormSink make_norm_sink(float* partial, unsigned long long* arrivals, flo
 // Called by ONE thread per tile workgroup with the tile's partial s. The
 // tiles of a sample run on different XCDs, whose L2 caches are not coherent
 // with each other: partials are stored and read with device-scope accesses,
-// which go through to the memory-side cache, and the store is complete
-// (vmcnt 0) before the arrival is counted. The last tile to arrive sums the
-// partials in tile order, so the result does not depend on arrival order.
+// which go through to the memory-side cache; a device-scope release fence
+// orders the store before the arrival is counted, and the last tile to arrive
+// takes an acquire fence before it reads the others' partials. It sums them
+// in tile order, so the result does not depend on arrival order.
 __device__ __forceinline__ void norm_sink_tile(const NormSink& k, int64_t i, int64_t tile, float s) {
   if (k.ntiles == 1) {
     const float tot = 0.f + s;
@@ -393,8 +402,9 @@ __device__ __forceinline__ void norm_sink_tile(const NormSink& k, int64_t i, int
   }
   float* row = k.partial + i * k.ntiles;
   __hip_atomic_store(row + tile, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_vmcnt<0>();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   if (!arrive_last(k.arrivals + i, k.epoch, (uint32_t)k.ntiles)) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   float v = k.accumulate ? k.sqnorm[i] : 0.f;
   for (int l = 0; l < k.nlayers; ++l) {
     float tot = 0.f;

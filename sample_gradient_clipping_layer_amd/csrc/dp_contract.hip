@@ -188,6 +188,17 @@ __device__ __forceinline__ void dl_fixup(const DlLayer& L, uint64_t epoch, int64
 // skipped; a NaN factor still propagates. The partial tile is written to the
 // workspace straight from registers.
 //
+// The units of acc must not drift far from the factors it holds: were a
+// factor 2^-100 to follow factors near 1, acc = sum / c_i would overflow. So
+// when c_i lies outside [ref * 2^-32, ref * 2^32], ref being the factor of
+// the first sample since the last such event, acc * c_prev is flushed into
+// this split's partial tile in the workspace (added to what earlier flushes
+// left there; each lane owns its elements) and acc restarts from zero with
+// ref = c_i. Within the window the rescale factor is at most 2^32 and every
+// term of acc is c_j * P_j / c_i with c_j / c_i <= 2^64 (P_j the unscaled
+// per-sample product), which stays finite for clipped terms |c_j P_j| <= C
+// whenever C / c_i does. The epilogue adds the flushed part first.
+//
 // Work items: XCD x (blockIdx % 8) takes items [x * per_l, (x+1) * per_l) of
 // every layer l in turn, so that each XCD holds a share of every layer and
 // its concurrently running workgroups share operand tiles in its L2.
@@ -339,7 +350,26 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const float* __restr
   int64_t sample = q0 / L.cps;
   int64_t in_sample = q0 - sample * L.cps;
   float cur = 0.0f, prev = 0.0f;  // RATIO: current and last nonzero clip factor
-  bool have_prev = false;
+  float ref = 0.0f;               // RATIO: factor of the first sample since the last flush
+  bool have_prev = false, flushed = false;
+  // RATIO: acc element (bi, bj, j) of this lane sits at row lrow + bi*32 + 8*(j/4) + j%4
+  // and column lcol + bj*32 of the split's partial tile; `f(elem, ptr)` is called for the
+  // elements inside [0, d) x [0, p) (flushes and the epilogue; the offsets past the lane's
+  // base are compile-time constants times p).
+  auto for_tile_elems = [&](auto f) {
+    const int64_t lrow = m0 + wm * C::WM + 4 * (lane >> 5), lcol = n0 + wn * C::WN + (lane & 31);
+    float* const base = L.ws + split * L.d * L.p + lrow * L.p + lcol;
+    const int64_t rem_r = L.d - lrow, rem_c = L.p - lcol;
+#pragma unroll
+    for (int bi = 0; bi < C::NBM; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < C::NBN; ++bj)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int ro = bi * 32 + 8 * (j >> 2) + (j & 3), co = bj * 32;
+          if (ro < rem_r && co < rem_c) f(acc[bi][bj][j], base + ro * L.p + co);
+        }
+  };
 #pragma unroll
   for (int c = 0; c < STAGES - 1; ++c)
     if (c < nq) issue(q0 + c, c);
@@ -356,13 +386,28 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const float* __restr
         cur = c[sample];
         if (cur != 0.0f) {  // a NaN factor is not 0: it propagates
           if (have_prev) {
-            const float r = prev / cur;
+            const float mag = fabsf(cur), rmag = fabsf(ref);
+            float r;
+            if (mag < rmag * 0x1p-32f || mag > rmag * 0x1p32f) {
+              // flush: partial tile (+)= acc * c_prev; acc restarts (times 0) in units of c_i
+              for_tile_elems([&](float a, float* dst) {
+                const float v = a * prev;
+                *dst = flushed ? *dst + v : v;
+              });
+              flushed = true;
+              ref = cur;
+              r = 0.0f;
+            } else {
+              r = prev / cur;
+            }
 #pragma unroll
             for (int bi = 0; bi < C::NBM; ++bi)
 #pragma unroll
               for (int bj = 0; bj < C::NBN; ++bj)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) acc[bi][bj][j] *= r;
+          } else {
+            ref = cur;
           }
           prev = cur;
           have_prev = true;
@@ -399,17 +444,10 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const float* __restr
     // ---- epilogue: undo the last sample's division, write the partial tile
     // [m][n] (m < d, n < p) straight from the accumulators, then the fix-up
     const float last = have_prev ? prev : 0.0f;
-    float* wsp = L.ws + split * L.d * L.p;
-#pragma unroll
-    for (int bi = 0; bi < C::NBM; ++bi)
-#pragma unroll
-      for (int bj = 0; bj < C::NBN; ++bj)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int64_t m = m0 + wm * C::WM + bi * 32 + acc_row(j, lane);
-          const int64_t n = n0 + wn * C::WN + bj * 32 + acc_col(lane);
-          if (m < L.d && n < L.p) wsp[m * L.p + n] = have_prev ? acc[bi][bj][j] * last : 0.0f;
-        }
+    for_tile_elems([&](float a, float* dst) {
+      const float v = have_prev ? a * last : 0.0f;
+      *dst = flushed ? *dst + v : v;
+    });
     if (g.fixup) dl_fixup<BM, BN, C::NT>(L, g.epoch, t, m0, n0, &fix_flag);
     return;
   } else {

@@ -51,11 +51,6 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
   return c;
 }
 
-// Correctly rounded fp32 square root: the fp64 square root is correctly
-// rounded and 53 >= 2*24 + 2 bits, so rounding it to fp32 gives the correctly
-// rounded fp32 result (double rounding is innocuous for sqrt). The bare
-// hardware fp32 square root is not correctly rounded.
-
 // Reciprocal of b in [1.7, 2.5]: three Newton steps (relative error < 2e-7).
 __device__ __forceinline__ float rcp_spec(float b) {
 #pragma clang fp contract(off)

@@ -18,6 +18,11 @@ import workloads as W
 
 TAU_NORM = {"f32": 1e-4, "bf16": 1e-2}
 TAU_SUM = {"f32": 1e-3, "bf16": 2e-2}
+# Diagnostic bound for bf16 norms next to the 1e-2 bar: the oracle reads the
+# exact bf16 input values, so the only error left is the fp32 accumulation
+# (~1e-6 relative); a dropped or doubled tile worth less than 1 % of a norm
+# would pass the bar but not this.
+DIAG_NORM_BF16 = 1e-4
 
 
 def dev():
@@ -67,6 +72,10 @@ def assert_norms(n_gpu, n_or, dtype, what="norm"):
     bound = TAU_NORM[dtype] * np.abs(n_or)
     bad = np.nonzero(~(err <= bound))[0]
     assert bad.size == 0, f"{what}: {bad.size} outside tol, worst rel {np.max(err / np.maximum(np.abs(n_or), 1e-300)):.3e} at {bad[:5]}"
+    if dtype == "bf16":
+        diag = np.nonzero(~(err <= DIAG_NORM_BF16 * np.abs(n_or)))[0]
+        assert diag.size == 0, (f"{what}: {diag.size} norms within the 1e-2 bar but beyond the {DIAG_NORM_BF16:g} "
+                                f"diagnostic bound (worst rel {np.max(err / np.maximum(np.abs(n_or), 1e-300)):.3e})")
 
 
 def assert_clip(c_gpu, c_or, N_or, C, dtype):

@@ -491,3 +491,79 @@ def test_conv_offset_limit_boundary(lib):
     import torch
     if not torch.cuda.is_available():  # fake pointers: only where nothing can launch
         assert _conv(lib, geo=ok, B=2, p=8, mode=dpc.MODE_EXPLICIT, wsb=1 << 40)[0] == dpc.DP_ERR_NO_DEVICE
+
+
+class _FakeGpuTensor:
+    """Stands in for a contiguous GPU tensor in binding-level checks that
+    raise before any library call (its pointer is never used)."""
+
+    def __init__(self, shape, dtype=None):
+        import torch
+        self.shape = tuple(shape)
+        self.dtype = torch.float32 if dtype is None else dtype
+        self.is_cuda = True
+        self.device = "cuda:0"
+
+    def dim(self):
+        return len(self.shape)
+
+    def numel(self):
+        n = 1
+        for s in self.shape:
+            n *= s
+        return n
+
+    def is_contiguous(self):
+        return True
+
+    def data_ptr(self):
+        return FAKE
+
+    def element_size(self):
+        return 4
+
+
+def test_binding_checks_bias_vectors_and_layer_ids(lib, monkeypatch):
+    """The multi-layer binding validates every bias vector (float32, p
+    elements, present for each layer with a bias) and layer_ids (one distinct
+    uint32 per layer) before calling the library: a short or bf16 bias vector
+    would take p fp32 writes past its end, and repeated ids would draw two
+    layers' noise from one stream."""
+    import torch
+
+    def no_call(*a, **k):
+        raise AssertionError("the library must not be called")
+
+    # the stream is fetched as the library call's first argument: reaching it means every check passed
+    monkeypatch.setattr(dpc, "_stream", no_call)
+    monkeypatch.setattr(dpc, "_check", no_call)
+    ws = _FakeGpuTensor((1 << 20,))
+    layers = [(_FakeGpuTensor((4, 2, 8)), _FakeGpuTensor((4, 2, 16))),
+              (_FakeGpuTensor((4, 2, 8)), _FakeGpuTensor((4, 2, 24)))]
+    c = _FakeGpuTensor((4,))
+    outs = [_FakeGpuTensor((8, 16)), _FakeGpuTensor((8, 24))]
+    good_b = [_FakeGpuTensor((16,)), _FakeGpuTensor((24,))]
+    call = lambda **kw: dpc.dp_clipped_sum_noise_layers(layers, c, 1.0, 1.0, 4.0, 0, 0, outs, workspace=ws, **kw)
+    with pytest.raises(ValueError, match="required"):
+        call(has_bias=True)                                            # no bias outputs at all
+    with pytest.raises(ValueError, match="required"):
+        call(has_bias=True, bias_outs=[good_b[0], None])               # one missing
+    with pytest.raises(ValueError, match="p = 24"):
+        call(has_bias=True, bias_outs=[good_b[0], _FakeGpuTensor((16,))])   # short
+    with pytest.raises(ValueError, match="float32"):
+        call(has_bias=True, bias_outs=[good_b[0], _FakeGpuTensor((24,), torch.bfloat16)])
+    with pytest.raises(ValueError, match="one bias_outs entry"):
+        call(has_bias=True, bias_outs=[good_b[0]])
+    with pytest.raises(ValueError, match="one id per layer"):
+        call(layer_ids=[3])
+    with pytest.raises(ValueError, match="distinct"):
+        call(layer_ids=[5, 5])
+    with pytest.raises(ValueError, match="distinct"):
+        call(layer_ids=[1, 1 << 32])
+    accs = [_FakeGpuTensor((8, 16)), _FakeGpuTensor((8, 24))]
+    with pytest.raises(ValueError, match="p = 16"):
+        dpc.dp_clipped_sum_accumulate_layers(layers, c, accs, bias_accs=[_FakeGpuTensor((8,)), good_b[1]],
+                                             has_bias=[True, False], workspace=ws)
+    # entries of layers without a bias are ignored; the checks then pass and the call goes ahead
+    with pytest.raises(AssertionError, match="must not be called"):
+        call(has_bias=[False, True], bias_outs=[None, good_b[1]], layer_ids=[7, 2])

@@ -217,22 +217,26 @@ def device_seed(wl_id: int, layer: int, step: int, tensor: int, base: int = BASE
 
 
 def make_layer_device(wl: Workload, layer: int, device, step: int = 0):
-    """Inputs (A, G) of a transformer layer drawn on the device with torch's
-    generator: the same distributions as ``make_layer`` (N(0, 1)/sqrt(d) and
-    N(0, 1)/sqrt(p) in fp32, rounded to bf16 to nearest even), not the same
-    values. For layer sets too large to draw on the host in reasonable time
-    (the GPT-2-large stack: 48 GB per pass)."""
+    """Inputs (A, G) of a layer drawn on the device with torch's generator:
+    the same distributions as ``make_layer``, not the same values. bf16
+    transformer layers: N(0, 1)/sqrt(d) and N(0, 1)/sqrt(p) in fp32, rounded
+    to bf16 to nearest even; the fp32 MLP: N(0, 1). For layer sets too large
+    to draw on the host in reasonable time (the GPT-2-large stack: 48 GB per
+    pass; the B = 65536 MLP: 4.8 GB per step, fresh every step)."""
     import torch
-    if wl.dtype != "bf16" or wl.conv:
-        raise ValueError("device generation covers the bf16 transformer workloads only")
+    if wl.conv or wl.name == "single-linear-t1":
+        raise ValueError("device generation covers the transformer and MLP workloads only")
     B = wl.B
     T, d, p = wl.layer_shape(layer)
     out = []
-    for tensor, (width, scale) in enumerate(((d, 1.0 / math.sqrt(d)), (p, 1.0 / math.sqrt(p)))):
+    for tensor, width in enumerate((d, p)):
         g = torch.Generator(device=device)
         g.manual_seed(device_seed(wl.wl_id, layer, step, tensor))
         x = torch.randn((B, T, width), generator=g, device=device, dtype=torch.float32)
-        x.mul_(scale)
-        out.append(x.to(torch.bfloat16))
-        del x
+        if wl.dtype == "bf16":
+            x.mul_(1.0 / math.sqrt(width))
+            out.append(x.to(torch.bfloat16))
+            del x
+        else:
+            out.append(x)
     return out[0], out[1]
