@@ -11,9 +11,10 @@
  *    enqueued asynchronously on it; nothing is synchronised. The caller keeps
  *    every buffer alive until the stream has passed the call.
  *  - The caller owns every buffer, including the workspace. The library keeps
- *    no pointer after returning. Its only global state is an atomic call
- *    counter that tags the arrival counters a call keeps in its workspace;
- *    calls are re-entrant. A workspace serves one call at a time: calls that
+ *    no pointer after returning. Its global state is an atomic call counter
+ *    that tags the arrival counters a call keeps in its workspace, and the
+ *    fixed scratch array of dp_ghost_norm_clip_layers_noalloc (with its
+ *    per-device address); calls are re-entrant. A workspace serves one call at a time: calls that
  *    may run concurrently (different streams) need distinct workspaces.
  *    Identical inputs give bitwise-identical outputs (fixed-order reductions,
  *    no floating-point atomics).
@@ -154,6 +155,29 @@ dp_status dp_ghost_norm_clip_layers(void* stream, const dp_layer* layers, int32_
                                     int64_t B, dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes,
                                     float* sqnorm, int32_t accumulate, float C, float* c, float* norm,
                                     int32_t* paths_out);
+
+/*
+ * dp_ghost_norm_clip_layers for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and bitwise the same results, with no
+ * workspace argument. Its scratch (tile partials and arrival counters) is a
+ * fixed 4 MiB device array inside the library, one per GPU, held from the
+ * first call on that GPU until the process ends; the call allocates no
+ * memory (device or host) and makes no memset.
+ *
+ * Every call on one GPU shares that array: calls that may overlap on one GPU
+ * (different streams, or one stream and a graph replay) race and give wrong
+ * results; serialise them. Nothing in the array needs clearing between calls.
+ *
+ *  Arguments as in dp_ghost_norm_clip_layers, with n_layers <= 1024.
+ *  DP_ERR_WORKSPACE when the layers would need more than 4 MiB of scratch
+ *  (dp_layers_workspace_bytes covers it: B * tiles-per-sample * 4 bytes plus
+ *  8 bytes per sample, e.g. 20 KB for eight GPT-2-large layers at B = 32).
+ */
+dp_status dp_ghost_norm_clip_layers_noalloc(void* stream, const dp_layer* layers, int32_t n_layers,
+                                            dp_dtype dtype, int64_t B, dp_mode mode, int32_t kappa,
+                                            float* sqnorm, int32_t accumulate, float C, float* c, float* norm,
+                                            int32_t* paths_out);
 
 /* Workspace bytes that dp_ghost_norm_layers (with this mode and kappa) and
  * dp_clipped_sum_noise_layers need for these layers (the larger of the two).

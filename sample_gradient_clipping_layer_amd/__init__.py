@@ -13,6 +13,8 @@ The functions mirror the C ABI in ``include/dpclip.h``:
                          accumulate=False, workspace=None) -> [path, ...]
     dp_ghost_norm_clip_layers(layers, sqnorm, C, c, norm=None, has_bias=False, mode=MODE_MIXED, kappa=1,
                               accumulate=False, workspace=None) -> [path, ...]
+    dp_ghost_norm_clip_layers_noalloc(layers, sqnorm, C, c, norm=None, has_bias=False, mode=MODE_MIXED,
+                                      kappa=1, accumulate=False) -> [path, ...]   (allocates nothing)
     dp_layers_workspace_bytes(layers, has_bias=False, mode=MODE_MIXED, kappa=1) -> int
     dp_clipped_sum_noise_layers(layers, c, C, sigma, denom, seed, step, outs,
                                 bias_outs=None, has_bias=False, layer_ids=None, workspace=None)
@@ -55,7 +57,8 @@ DP_F32, DP_BF16 = 0, 1
 MODE_MIXED, MODE_GHOST, MODE_EXPLICIT, MODE_TIME = 0, 1, 2, 3
 PATH_GHOST, PATH_EXPLICIT, PATH_T1 = 1, 2, 3
 
-EXPORTS = ("dp_ghost_norm", "dp_ghost_norm_layers", "dp_ghost_norm_clip_layers", "dp_layers_workspace_bytes", "dp_clipped_sum_noise_layers",
+EXPORTS = ("dp_ghost_norm", "dp_ghost_norm_layers", "dp_ghost_norm_clip_layers", "dp_ghost_norm_clip_layers_noalloc",
+           "dp_layers_workspace_bytes", "dp_clipped_sum_noise_layers",
            "dp_clip_factors", "dp_clipped_sum_accumulate", "dp_noise_mean", "dp_accumulate_workspace_bytes",
            "dp_clipped_sum_accumulate_layers", "dp_layers_accumulate_workspace_bytes", "dp_clipped_sum_noise", "dp_adaptive_threshold",
            "dp_workspace_bytes", "dp_choose_path", "dp_status_string", "dp_abi_version",
@@ -109,6 +112,9 @@ def _declare(lib):
     lib.dp_ghost_norm_clip_layers.argtypes = [vp, lp, c_i32, c_i32, c_i64, c_i32, c_i32, vp, ctypes.c_size_t, fp,
                                               c_i32, f, fp, fp, ctypes.POINTER(c_i32)]
     lib.dp_ghost_norm_clip_layers.restype = c_i32
+    lib.dp_ghost_norm_clip_layers_noalloc.argtypes = [vp, lp, c_i32, c_i32, c_i64, c_i32, c_i32, fp, c_i32, f, fp,
+                                                      fp, ctypes.POINTER(c_i32)]
+    lib.dp_ghost_norm_clip_layers_noalloc.restype = c_i32
     lib.dp_clipped_sum_noise_layers.argtypes = [vp, lp, c_i32, c_i32, c_i64, fp, f, f, f, c_u64,
                                                 ctypes.POINTER(c_u32), c_u32, vp, ctypes.c_size_t,
                                                 ctypes.POINTER(vp), ctypes.POINTER(vp)]
@@ -346,6 +352,22 @@ def dp_ghost_norm_clip_layers(layers, sqnorm, C: float, c, norm=None, has_bias=F
         _stream(stream), arr, len(layers), dt, B, int(mode), int(kappa), _ptr(workspace),
         _ws_bytes(workspace), _ptr(sqnorm), int(bool(accumulate)), float(C), _ptr(c),
         _ptr(norm), paths))
+    return list(paths)
+
+
+def dp_ghost_norm_clip_layers_noalloc(layers, sqnorm, C: float, c, norm=None, has_bias=False,
+                                      mode: int = MODE_MIXED, kappa: int = 1, accumulate: bool = False, stream=None):
+    """dp_ghost_norm_clip_layers with the library's fixed scratch array instead
+    of a workspace: allocates nothing. Calls that overlap on one GPU race."""
+    dt, B, arr = _layer_table(layers, has_bias)
+    for t, nm in ((sqnorm, "sqnorm"), (c, "c")) + (((norm, "norm"),) if norm is not None else ()):
+        _f32_vec(t, nm)
+        if t.numel() != B:
+            raise ValueError(f"{nm} must have B elements")
+    paths = (ctypes.c_int32 * len(layers))()
+    _check("dp_ghost_norm_clip_layers_noalloc", lib().dp_ghost_norm_clip_layers_noalloc(
+        _stream(stream), arr, len(layers), dt, B, int(mode), int(kappa), _ptr(sqnorm), int(bool(accumulate)),
+        float(C), _ptr(c), _ptr(norm), paths))
     return list(paths)
 
 

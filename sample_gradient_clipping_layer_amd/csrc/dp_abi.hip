@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/dpclip.h"
@@ -351,6 +352,38 @@ size_t conv_sum_ws_bytes(const dpk::ContractPlan& pl, int64_t d, int64_t p, int 
   return round256((size_t)pl.ks * (size_t)(d + (has_bias ? 1 : 0)) * (size_t)p * sizeof(float));
 }
 
+// ---- scratch of the entry point that allocates nothing
+// (dp_ghost_norm_clip_layers_noalloc): a fixed device array that every call on
+// a GPU shares (each GPU holds its own copy until the process ends). It holds
+// the norm kernels' tile partials and per-sample arrival counters. Nothing in
+// it must start at zero: the counters carry each call's tag and are returned
+// to zero arrivals by their last arrival, and every partial is written before
+// it is read. Calls that overlap on one GPU (different streams) race on it.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+constexpr int32_t kNoAllocMaxLayers = 1024;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device: looked up once per
+// device with that device current, then reused. The array's host-side name
+// is only a stand-in for the symbol and is never passed to a kernel.
+dp_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DP_ERR_NO_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DP_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return DP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -426,15 +459,16 @@ size_t dp_layers_workspace_bytes(const dp_layer* layers, int32_t n_layers, dp_dt
   return w;
 }
 
+// The multi-layer norm calls; `runs` has room for n_layers runs (the caller's
+// buffer, so that an entry point can keep it off the heap).
 static dp_status norm_layers_impl(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B,
                                   dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes, float* sqnorm,
-                                  int32_t accumulate, int32_t* paths_out, const ClipOut* clip) {
+                                  int32_t accumulate, int32_t* paths_out, const ClipOut* clip, NormRun* runs) {
   dp_status s = check_norm_layers(layers, n_layers, dtype, B, mode, kappa);
   if (s != DP_OK) return s;
   if (!sqnorm) return DP_ERR_NULL;
   if (!aligned(sqnorm, 4)) return DP_ERR_ALIGN;
-  std::vector<NormRun> runs((size_t)n_layers);
-  const int nr = plan_norm_runs(layers, n_layers, dtype, B, mode, kappa, runs.data());
+  const int nr = plan_norm_runs(layers, n_layers, dtype, B, mode, kappa, runs);
   size_t need = 0;
   for (int r = 0; r < nr; ++r) need = std::max(need, run_ws_bytes(runs[r], layers, dtype, B, mode, kappa));
   if (need > 0) {
@@ -486,8 +520,10 @@ static dp_status norm_layers_impl(void* stream, const dp_layer* layers, int32_t 
 dp_status dp_ghost_norm_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B,
                                dp_mode mode, int32_t kappa, void* workspace, size_t ws_bytes, float* sqnorm,
                                int32_t accumulate, int32_t* paths_out) {
+  if (n_layers < 1 || n_layers > kMaxNormLayers) return layers ? DP_ERR_SHAPE : DP_ERR_NULL;
+  std::vector<NormRun> runs((size_t)n_layers);
   return norm_layers_impl(stream, layers, n_layers, dtype, B, mode, kappa, workspace, ws_bytes, sqnorm, accumulate,
-                          paths_out, nullptr);
+                          paths_out, nullptr, runs.data());
 }
 
 dp_status dp_ghost_norm_clip_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B,
@@ -496,9 +532,39 @@ dp_status dp_ghost_norm_clip_layers(void* stream, const dp_layer* layers, int32_
   if (!c) return DP_ERR_NULL;
   if (!aligned(c, 4) || (norm && !aligned(norm, 4))) return DP_ERR_ALIGN;
   if (!finite(C) || !(C > 0.0f)) return DP_ERR_VALUE;
+  if (n_layers < 1 || n_layers > kMaxNormLayers) return layers ? DP_ERR_SHAPE : DP_ERR_NULL;
+  std::vector<NormRun> runs((size_t)n_layers);
   const ClipOut clip{C, c, norm};
   return norm_layers_impl(stream, layers, n_layers, dtype, B, mode, kappa, workspace, ws_bytes, sqnorm, accumulate,
-                          paths_out, &clip);
+                          paths_out, &clip, runs.data());
+}
+
+dp_status dp_ghost_norm_clip_layers_noalloc(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype,
+                                            int64_t B, dp_mode mode, int32_t kappa, float* sqnorm,
+                                            int32_t accumulate, float C, float* c, float* norm,
+                                            int32_t* paths_out) {
+  if (!c) return DP_ERR_NULL;
+  if (!aligned(c, 4) || (norm && !aligned(norm, 4))) return DP_ERR_ALIGN;
+  if (!finite(C) || !(C > 0.0f)) return DP_ERR_VALUE;
+  if (!layers) return DP_ERR_NULL;
+  if (n_layers < 1 || n_layers > kNoAllocMaxLayers) return DP_ERR_SHAPE;
+  dp_status s = check_norm_layers(layers, n_layers, dtype, B, mode, kappa);
+  if (s != DP_OK) return s;
+  if (!sqnorm) return DP_ERR_NULL;
+  if (!aligned(sqnorm, 4)) return DP_ERR_ALIGN;
+  NormRun runs[kNoAllocMaxLayers];  // on the stack: no heap either
+  const int nr = plan_norm_runs(layers, n_layers, dtype, B, mode, kappa, runs);
+  size_t need = 0;
+  for (int r = 0; r < nr; ++r) need = std::max(need, run_ws_bytes(runs[r], layers, dtype, B, mode, kappa));
+  if (need > kNoAllocScratchBytes) return DP_ERR_WORKSPACE;
+  s = device_ready();
+  if (s != DP_OK) return s;
+  void* ws = nullptr;
+  s = noalloc_scratch(&ws);
+  if (s != DP_OK) return s;
+  const ClipOut clip{C, c, norm};
+  return norm_layers_impl(stream, layers, n_layers, dtype, B, mode, kappa, ws, kNoAllocScratchBytes, sqnorm,
+                          accumulate, paths_out, &clip, runs);
 }
 
 dp_status dp_clipped_sum_noise_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype,

@@ -567,3 +567,27 @@ def test_binding_checks_bias_vectors_and_layer_ids(lib, monkeypatch):
     # entries of layers without a bias are ignored; the checks then pass and the call goes ahead
     with pytest.raises(AssertionError, match="must not be called"):
         call(has_bias=[False, True], bias_outs=[None, good_b[1]], layer_ids=[7, 2])
+
+
+def test_noalloc_norm_call_validation(lib):
+    """dp_ghost_norm_clip_layers_noalloc validates like the workspace call and
+    refuses, before any HIP call, layer sets whose scratch would exceed its
+    fixed 4 MiB array: four T = 1024 ghost layers (80 tiles per sample) need
+    B * 80 * 4 + B * 8 bytes, over 4 MiB at B = 13000."""
+    def call(layers, n, B=13000, sq=FAKE, c=FAKE, C=1.0):
+        return lib.dp_ghost_norm_clip_layers_noalloc(None, layers, n, dpc.DP_BF16, B, dpc.MODE_MIXED, 1, sq, 0,
+                                                     C, c, None, None)
+    wide = (dpc.DpLayer * 4)(*[dpc.DpLayer(FAKE, FAKE, 1024, 1024, 1024, 0, 0)] * 4)
+    assert lib.dp_layers_workspace_bytes(wide, 4, dpc.DP_BF16, 13000, dpc.MODE_MIXED, 1) > (4 << 20)
+    assert call(wide, 4) == dpc.DP_ERR_WORKSPACE
+    import torch
+    if not torch.cuda.is_available():      # placeholder pointers: only where nothing can be launched
+        assert call(wide, 4, B=12000) == dpc.DP_ERR_NO_DEVICE  # fits: goes on to the device check
+    assert call(wide, 0) == dpc.DP_ERR_SHAPE
+    assert call(wide, 1025) == dpc.DP_ERR_SHAPE
+    assert call(None, 4) == dpc.DP_ERR_NULL
+    assert call(wide, 4, sq=None) == dpc.DP_ERR_NULL
+    assert call(wide, 4, c=None) == dpc.DP_ERR_NULL
+    assert call(wide, 4, C=0.0) == dpc.DP_ERR_VALUE
+    mis = (dpc.DpLayer * 1)(dpc.DpLayer(FAKE_MIS, FAKE, 1024, 1024, 1024, 0, 0))
+    assert call(mis, 1) == dpc.DP_ERR_ALIGN
