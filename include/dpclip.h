@@ -12,9 +12,10 @@
  *    every buffer alive until the stream has passed the call.
  *  - The caller owns every buffer, including the workspace. The library keeps
  *    no pointer after returning. Its global state is an atomic call counter
- *    that tags the arrival counters a call keeps in its workspace, and the
- *    fixed scratch array of dp_ghost_norm_clip_layers_noalloc (with its
- *    per-device address); calls are re-entrant. A workspace serves one call at a time: calls that
+ *    that tags the arrival counters a multi-layer clipped-sum call keeps in
+ *    its workspace, and the fixed scratch array of
+ *    dp_ghost_norm_clip_layers_noalloc (with its per-device address); calls
+ *    are re-entrant. A workspace serves one call at a time: calls that
  *    may run concurrently (different streams) need distinct workspaces.
  *    Identical inputs give bitwise-identical outputs (fixed-order reductions,
  *    no floating-point atomics).
@@ -23,8 +24,9 @@
  *    DP_ERR_HIP; no usable device returns DP_ERR_NO_DEVICE.
  *  - Calls may be captured into a HIP graph and replayed: they enqueue kernel
  *    launches only (no memset, copy or allocation), and each arrival counter
- *    is returned to zero arrivals by the last arrival of its launch, so a
- *    replay with the captured tag counts from zero again. Buffers captured by
+ *    (multi-layer clipped sums) is returned to zero arrivals by the last
+ *    arrival of its launch, so a replay with the captured tag counts from
+ *    zero again. Buffers captured by
  *    pointer keep their addresses across replays, as graphs require.
  *
  * Page keys used in the comments:
@@ -92,11 +94,11 @@ typedef int32_t dp_mode;
  *           unless mode is EXPLICIT.
  *  workspace, ws_bytes  device scratch of at least dp_workspace_bytes(...)
  *           bytes (may be NULL when that is 0). Its contents on entry are
- *           ignored and on return undefined: per-sample arrival counters kept
- *           there carry a 48-bit per-call tag, so values left by earlier calls
- *           (or arbitrary bytes) read as "no arrivals", except with
- *           probability 2^-48 per counter. DP_ERR_SHAPE when a sample would
- *           span more than 65535 tiles (explicit path with d*p beyond ~1e9).
+ *           ignored and on return undefined. When a sample spans several
+ *           tile workgroups, each stores its partial there and a small
+ *           finish kernel on the same stream folds them (no workgroup waits
+ *           for another). DP_ERR_SHAPE when a sample would span more than
+ *           65535 tiles (explicit path with d*p beyond ~1e9).
  *  sqnorm   [B] fp32 device: overwritten (accumulate == 0) or incremented
  *           (accumulate != 0) by the layer's squared norms, so several layers
  *           can be summed in call order into one global norm.
@@ -127,8 +129,8 @@ typedef struct dp_layer {
  * with `accumulate` and the others with accumulate = 1. Runs of up to 8
  * consecutive layers that take the tiled ghost kernel with one tile size
  * share a launch, whose Gram tiles fill the GPU together (a small layer
- * alone leaves most compute units idle); the last tile of a sample to finish
- * adds the layers in order. Other layers (closed form, explicit, the
+ * alone leaves most compute units idle); the launch's finish kernel adds each
+ * sample's tile partials and then the layers in order. Other layers (closed form, explicit, the
  * long-sequence bf16 ghost engine) run one launch each.
  *
  *  layers, n_layers  host array, 1 <= n_layers <= 4096; each layer as in
@@ -160,7 +162,7 @@ dp_status dp_ghost_norm_clip_layers(void* stream, const dp_layer* layers, int32_
  * dp_ghost_norm_clip_layers for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same computation and bitwise the same results, with no
- * workspace argument. Its scratch (tile partials and arrival counters) is a
+ * workspace argument. Its scratch (the norm kernels' tile partials) is a
  * fixed 4 MiB device array inside the library, one per GPU, held from the
  * first call on that GPU until the process ends; the call allocates no
  * memory (device or host) and makes no memset.
@@ -171,8 +173,8 @@ dp_status dp_ghost_norm_clip_layers(void* stream, const dp_layer* layers, int32_
  *
  *  Arguments as in dp_ghost_norm_clip_layers, with n_layers <= 1024.
  *  DP_ERR_WORKSPACE when the layers would need more than 4 MiB of scratch
- *  (dp_layers_workspace_bytes covers it: B * tiles-per-sample * 4 bytes plus
- *  8 bytes per sample, e.g. 20 KB for eight GPT-2-large layers at B = 32).
+ *  (dp_layers_workspace_bytes covers it: B * tiles-per-sample * 4 bytes,
+ *  e.g. 20 KB for eight GPT-2-large layers at B = 32).
  */
 dp_status dp_ghost_norm_clip_layers_noalloc(void* stream, const dp_layer* layers, int32_t n_layers,
                                             dp_dtype dtype, int64_t B, dp_mode mode, int32_t kappa,

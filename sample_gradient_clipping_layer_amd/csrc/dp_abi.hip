@@ -79,13 +79,13 @@ int64_t norm_ntiles(int dtype, int path, int64_t T, int64_t d, int64_t p, int ha
   return (int64_t)pl.mt * pl.nt;
 }
 
-// tile partials [B][ntiles] fp32, then one arrival counter per sample
+// tile partials [B][ntiles] fp32
 size_t norm_partial_bytes(int64_t B, int64_t ntiles) { return round256((size_t)B * (size_t)ntiles * sizeof(float)); }
 
 size_t norm_ws_bytes(int dtype, int path, int64_t B, int64_t T, int64_t d, int64_t p, int has_bias) {
   const int64_t ntiles = norm_ntiles(dtype, path, T, d, p, has_bias);
   if (ntiles == 1) return 0;
-  return norm_partial_bytes(B, ntiles) + round256((size_t)B * sizeof(unsigned long long));
+  return norm_partial_bytes(B, ntiles);
 }
 
 size_t contract_ws_for(const dpk::ContractPlan& pl, int64_t d, int64_t p, int has_bias) {
@@ -119,19 +119,15 @@ hipError_t launch_layer_norm(hipStream_t st, int dtype, const void* A, const voi
     return e;
   }
   const int64_t ntiles = norm_ntiles(dtype, path, T, d, p, hb);
-  dpk::NormSink sink = dpk::make_norm_sink(
-      static_cast<float*>(workspace),
-      ntiles > 1 ? reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(workspace) +
-                                                         norm_partial_bytes(B, ntiles))
-                 : nullptr,
-      sqnorm, (int)ntiles, acc, dpk::next_epoch());
+  dpk::NormSink sink = dpk::make_norm_sink(static_cast<float*>(workspace), sqnorm, (int)ntiles, acc);
   if (clip) {
     sink.clip_c = clip->c;
     sink.clip_norm = clip->norm;
     sink.C = clip->C;
   }
-  if (path == DP_PATH_GHOST) return dpk::launch_ghost(st, dtype, A, G, B, T, d, p, hb, sink);
-  return dpk::launch_explicit(st, dtype, A, G, B, T, d, p, hb, sink);
+  const hipError_t e = path == DP_PATH_GHOST ? dpk::launch_ghost(st, dtype, A, G, B, T, d, p, hb, sink)
+                                             : dpk::launch_explicit(st, dtype, A, G, B, T, d, p, hb, sink);
+  return e == hipSuccess ? dpk::launch_norm_finish(st, sink, B) : e;
 }
 
 // Per-layer limits of dp_ghost_norm: tiles per sample (16-bit arrival count)
@@ -211,7 +207,7 @@ int plan_norm_runs(const dp_layer* layers, int32_t n, dp_dtype dtype, int64_t B,
 size_t run_ws_bytes(const NormRun& r, const dp_layer* layers, int dtype, int64_t B, dp_mode mode, int32_t kappa) {
   if (r.grouped) {
     if (r.ntiles == 1) return 0;
-    return norm_partial_bytes(B, r.ntiles) + round256((size_t)B * sizeof(unsigned long long));
+    return norm_partial_bytes(B, r.ntiles);
   }
   const dp_layer& x = layers[r.first];
   return norm_ws_bytes(dtype, path_of(x.T, x.d, x.p, mode, kappa), B, x.T, x.d, x.p, x.has_bias ? 1 : 0);
@@ -344,7 +340,7 @@ int64_t conv_norm_ntiles(int path, int64_t T, int64_t d, int64_t p, int has_bias
 size_t conv_norm_ws_bytes(int path, int64_t B, int64_t T, int64_t d, int64_t p, int has_bias) {
   const int64_t nt = conv_norm_ntiles(path, T, d, p, has_bias);
   if (nt == 1) return 0;
-  return norm_partial_bytes(B, nt) + round256((size_t)B * sizeof(unsigned long long));
+  return norm_partial_bytes(B, nt);
 }
 
 size_t conv_sum_ws_bytes(const dpk::ContractPlan& pl, int64_t d, int64_t p, int has_bias) {
@@ -355,10 +351,9 @@ size_t conv_sum_ws_bytes(const dpk::ContractPlan& pl, int64_t d, int64_t p, int 
 // ---- scratch of the entry point that allocates nothing
 // (dp_ghost_norm_clip_layers_noalloc): a fixed device array that every call on
 // a GPU shares (each GPU holds its own copy until the process ends). It holds
-// the norm kernels' tile partials and per-sample arrival counters. Nothing in
-// it must start at zero: the counters carry each call's tag and are returned
-// to zero arrivals by their last arrival, and every partial is written before
-// it is read. Calls that overlap on one GPU (different streams) race on it.
+// the norm kernels' tile partials. Nothing in it must start at zero: every
+// partial is written by its tile before the finish kernel reads it. Calls
+// that overlap on one GPU (different streams) race on it.
 constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
 constexpr int32_t kNoAllocMaxLayers = 1024;
 constexpr int kMaxDevices = 64;
@@ -487,12 +482,7 @@ static dp_status norm_layers_impl(void* stream, const dp_layer* layers, int32_t 
     hipError_t e;
     if (run.grouped) {
       dpk::GhostLayerDesc desc[dpk::kNormGroupMax];
-      dpk::NormSink sink = dpk::make_norm_sink(
-          static_cast<float*>(workspace),
-          run.ntiles > 1 ? reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(workspace) +
-                                                                 norm_partial_bytes(B, run.ntiles))
-                         : nullptr,
-          sqnorm, (int)run.ntiles, acc, dpk::next_epoch());
+      dpk::NormSink sink = dpk::make_norm_sink(static_cast<float*>(workspace), sqnorm, (int)run.ntiles, acc);
       sink.nlayers = run.count;
       if (clip && r == nr - 1) {  // the last run's sink holds each sample's final value
         sink.clip_c = clip->c;
@@ -506,6 +496,7 @@ static dp_status norm_layers_impl(void* stream, const dp_layer* layers, int32_t 
         sink.lt[k + 1] = sink.lt[k] + (int)norm_ntiles(dtype, DP_PATH_GHOST, x.T, x.d, x.p, desc[k].has_bias);
       }
       e = dpk::launch_ghost_group(st, dtype, desc, run.count, B, sink);
+      if (e == hipSuccess) e = dpk::launch_norm_finish(st, sink, B);
     } else {
       const dp_layer& x = layers[run.first];
       const int hb = x.has_bias ? 1 : 0;
@@ -718,14 +709,11 @@ dp_status dp_conv_norm(void* stream, const void* a, const void* G, const dp_conv
   s = device_ready();
   if (s != DP_OK) return s;
   if (path_out) *path_out = path;
-  const dpk::NormSink sink = dpk::make_norm_sink(
-      static_cast<float*>(workspace),
-      nt > 1 ? reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(workspace) + norm_partial_bytes(B, nt))
-             : nullptr,
-      sqnorm, (int)nt, accumulate ? 1 : 0, dpk::next_epoch());
+  const dpk::NormSink sink = dpk::make_norm_sink(static_cast<float*>(workspace), sqnorm, (int)nt, accumulate ? 1 : 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (path == DP_PATH_GHOST) return hip_status(dpk::launch_ghost_conv(st, dtype, g, G, B, p, hb, sink));
-  return hip_status(dpk::launch_explicit_conv(st, dtype, g, G, B, p, hb, sink));
+  const hipError_t e = path == DP_PATH_GHOST ? dpk::launch_ghost_conv(st, dtype, g, G, B, p, hb, sink)
+                                             : dpk::launch_explicit_conv(st, dtype, g, G, B, p, hb, sink);
+  return hip_status(e == hipSuccess ? dpk::launch_norm_finish(st, sink, B) : e);
 }
 
 dp_status dp_conv_clipped_sum_noise(void* stream, const void* a, const void* G, const dp_conv2d* conv, dp_dtype dtype,

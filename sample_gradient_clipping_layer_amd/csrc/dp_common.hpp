@@ -355,13 +355,17 @@ constexpr int kNormGroupMax = 8;
 // then takes the layers in order, as calls with accumulate = 1 after the
 // first would: sqnorm[i] = ((start + n_0) + n_1) + ..., start = sqnorm[i]
 // when accumulating, else the first layer's value stands alone.
+//
+// With one tile per sample the tile's workgroup writes sqnorm (and the clip
+// factors) itself. With several, each tile stores its partial and the finish
+// kernel (k_norm_finish), launched after the tiles' kernel on the same stream,
+// folds them: the kernel boundary orders the partials before their reads, so
+// no workgroup waits for or signals another.
 struct NormSink {
   float* partial;                 // [B][ntiles] (unused when ntiles == 1)
-  unsigned long long* arrivals;   // [B] arrival counters (unused when ntiles == 1)
   float* sqnorm;
   int ntiles;
   int accumulate;
-  uint64_t epoch;
   int nlayers;
   int lt[kNormGroupMax + 1];
   float* clip_c;                  // when set: clip factors (and clip_norm, when set) of the final sqnorm
@@ -370,28 +374,19 @@ struct NormSink {
 };
 
 // A sink for one layer of `ntiles` tiles per sample.
-inline NormSink make_norm_sink(float* partial, unsigned long long* arrivals, float* sqnorm, int ntiles,
-                               int accumulate, uint64_t epoch) {
+inline NormSink make_norm_sink(float* partial, float* sqnorm, int ntiles, int accumulate) {
   NormSink k{};
   k.partial = partial;
-  k.arrivals = arrivals;
   k.sqnorm = sqnorm;
   k.ntiles = ntiles;
   k.accumulate = accumulate;
-  k.epoch = epoch;
   k.nlayers = 1;
   k.lt[0] = 0;
   k.lt[1] = ntiles;
   return k;
 }
 
-// Called by ONE thread per tile workgroup with the tile's partial s. The
-// tiles of a sample run on different XCDs, whose L2 caches are not coherent
-// with each other: partials are stored and read with device-scope accesses,
-// which go through to the memory-side cache; a device-scope release fence
-// orders the store before the arrival is counted, and the last tile to arrive
-// takes an acquire fence before it reads the others' partials. It sums them
-// in tile order, so the result does not depend on arrival order.
+// Called by ONE thread per tile workgroup with the tile's partial s.
 __device__ __forceinline__ void norm_sink_tile(const NormSink& k, int64_t i, int64_t tile, float s) {
   if (k.ntiles == 1) {
     const float tot = 0.f + s;
@@ -400,16 +395,17 @@ __device__ __forceinline__ void norm_sink_tile(const NormSink& k, int64_t i, int
     if (k.clip_c) clip_factor_of(v, k.C, k.clip_c + i, k.clip_norm ? k.clip_norm + i : nullptr);
     return;
   }
-  float* row = k.partial + i * k.ntiles;
-  __hip_atomic_store(row + tile, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  if (!arrive_last(k.arrivals + i, k.epoch, (uint32_t)k.ntiles)) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  k.partial[i * k.ntiles + tile] = s;
+}
+
+// The fold of sample i's tile partials (sink with ntiles > 1), in tile order
+// within a layer and layer order across layers, then its clip factor.
+__device__ __forceinline__ void norm_sink_finish(const NormSink& k, int64_t i) {
+  const float* row = k.partial + i * k.ntiles;
   float v = k.accumulate ? k.sqnorm[i] : 0.f;
   for (int l = 0; l < k.nlayers; ++l) {
     float tot = 0.f;
-    for (int t = k.lt[l]; t < k.lt[l + 1]; ++t)
-      tot += __hip_atomic_load(row + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int t = k.lt[l]; t < k.lt[l + 1]; ++t) tot += row[t];
     v = (l == 0 && !k.accumulate) ? tot : v + tot;
   }
   k.sqnorm[i] = v;

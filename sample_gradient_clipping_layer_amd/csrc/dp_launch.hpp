@@ -111,13 +111,16 @@ hipError_t launch_ghost_group(hipStream_t st, int dtype, const GhostLayerDesc* l
                               const NormSink& sink);
 hipError_t launch_ghost_wide_group(hipStream_t st, const GhostLayerDesc* layers, int n, int64_t B,
                                    const NormSink& sink);
-// Norm kernels whose sample spans several tile workgroups finish each
-// sample in its last-arriving tile (NormSink in dp_common.hpp).
+// Norm kernels whose sample spans several tile workgroups store per-tile
+// partials; launch_norm_finish (after the tiles' launch, same stream) folds
+// them per sample (NormSink in dp_common.hpp). A no-op for one tile per sample.
+hipError_t launch_norm_finish(hipStream_t st, const NormSink& sink, int64_t B);
 hipError_t launch_ghost(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
                         int64_t p, int has_bias, const NormSink& sink);
 hipError_t launch_explicit(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
                            int64_t p, int has_bias, const NormSink& sink);
-// Tag of one call for its arrival counters: 48 bits, never 0, distinct per call in the process.
+// Tag of one call for the arrival counters of the contraction's in-kernel
+// split fix-up: 48 bits, never 0, distinct per call in the process.
 uint64_t next_epoch();
 // Weighted contraction + noise + 1/denom: one kernel when pl.ks == 1, else
 // partial tiles in ws and a reduce kernel. bias_out != nullptr <=> bias row.

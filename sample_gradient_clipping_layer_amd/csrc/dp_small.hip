@@ -15,6 +15,20 @@ __global__ __launch_bounds__(256) void k_clip_factors(const float* __restrict__ 
   clip_factor_of(sqnorm[i], C, c + i, norm ? norm + i : nullptr);
 }
 
+// The per-sample fold of a norm launch whose samples span several tiles: one
+// thread per sample (NormSink, norm_sink_finish).
+__global__ __launch_bounds__(256) void k_norm_finish(NormSink sink, int64_t B) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B) return;
+  norm_sink_finish(sink, i);
+}
+
+hipError_t launch_norm_finish(hipStream_t st, const NormSink& sink, int64_t B) {
+  if (sink.ntiles == 1) return hipSuccess;  // the tiles wrote sqnorm themselves
+  hipLaunchKernelGGL(k_norm_finish, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, st, sink, B);
+  return hipGetLastError();
+}
+
 // TTP adaptive clipping, one layer: one workgroup of 1024 threads.
 //   C_l2   = init ? mean(norm) : beta * C_prev
 //   C_next = alpha / B * (sum_i min(norm_i, C_l2) + sigma_l2 * C_l2 * z)

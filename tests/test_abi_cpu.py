@@ -235,23 +235,24 @@ def _norm_need_ok(lib, arr, n, dt, B, mode, need):
 
 def test_layers_workspace_follows_the_runs(lib):
     """Consecutive ghost layers of one tile size share a launch (at most 8)
-    whose partials span all their tiles; other layers need their own."""
+    whose tile partials ([B][tiles of the run] fp32) span all their tiles;
+    other layers need their own."""
     import torch
     if torch.cuda.is_available():
         pytest.skip("checks the no-device validation path")
     B = 64
     # four T = 128 layers: one launch, 3 Gram tiles per layer and sample
-    _norm_need_ok(lib, _layers(GPT_BLOCK), 4, 1, B, 0, _r256(B * 12 * 4) + _r256(B * 8))
+    _norm_need_ok(lib, _layers(GPT_BLOCK), 4, 1, B, 0, _r256(B * 12 * 4))
     # nine layers: runs of 8 and 1
-    _norm_need_ok(lib, _layers([GPT_BLOCK[0]] * 9), 9, 1, B, 0, _r256(B * 24 * 4) + _r256(B * 8))
+    _norm_need_ok(lib, _layers([GPT_BLOCK[0]] * 9), 9, 1, B, 0, _r256(B * 24 * 4))
     # a T = 1 layer in between splits the run; it needs no workspace
     mixed = _layers([GPT_BLOCK[0], (1, 64, 32, 0), GPT_BLOCK[1]])
-    _norm_need_ok(lib, mixed, 3, 1, B, 0, _r256(B * 3 * 4) + _r256(B * 8))
+    _norm_need_ok(lib, mixed, 3, 1, B, 0, _r256(B * 3 * 4))
     # one single-tile ghost layer: nothing
     _norm_need_ok(lib, _layers([(64, 32, 48, 0)]), 1, 0, 5, dpc.MODE_GHOST, 0)
     # two single-tile ghost layers share a launch: two tiles per sample
     two = _layers([(64, 32, 48, 0), (40, 16, 16, 1)])
-    _norm_need_ok(lib, two, 2, 0, 5, dpc.MODE_GHOST, _r256(5 * 2 * 4) + _r256(5 * 8))
+    _norm_need_ok(lib, two, 2, 0, 5, dpc.MODE_GHOST, _r256(5 * 2 * 4))
     # the long-sequence bf16 engine runs alone, with its own tile count
     assert lib.dp_layers_workspace_bytes(_layers([(1024, 1280, 3840, 0)]), 1, 1, 32, 0, 1) > 0
     assert lib.dp_layers_workspace_bytes(None, 1, 1, B, 0, 1) == 0
@@ -573,16 +574,15 @@ def test_noalloc_norm_call_validation(lib):
     """dp_ghost_norm_clip_layers_noalloc validates like the workspace call and
     refuses, before any HIP call, layer sets whose scratch would exceed its
     fixed 4 MiB array: four T = 1024 ghost layers (80 tiles per sample) need
-    B * 80 * 4 + B * 8 bytes, over 4 MiB at B = 13000."""
-    def call(layers, n, B=13000, sq=FAKE, c=FAKE, C=1.0):
+    B * 80 * 4 bytes of tile partials, over 4 MiB from B = 13108 on."""
+    def call(layers, n, B=14000, sq=FAKE, c=FAKE, C=1.0):
         return lib.dp_ghost_norm_clip_layers_noalloc(None, layers, n, dpc.DP_BF16, B, dpc.MODE_MIXED, 1, sq, 0,
                                                      C, c, None, None)
     wide = (dpc.DpLayer * 4)(*[dpc.DpLayer(FAKE, FAKE, 1024, 1024, 1024, 0, 0)] * 4)
-    assert lib.dp_layers_workspace_bytes(wide, 4, dpc.DP_BF16, 13000, dpc.MODE_MIXED, 1) > (4 << 20)
-    assert call(wide, 4) == dpc.DP_ERR_WORKSPACE
+    assert call(wide, 4, B=13108) == dpc.DP_ERR_WORKSPACE
     import torch
     if not torch.cuda.is_available():      # placeholder pointers: only where nothing can be launched
-        assert call(wide, 4, B=12000) == dpc.DP_ERR_NO_DEVICE  # fits: goes on to the device check
+        assert call(wide, 4, B=13107) == dpc.DP_ERR_NO_DEVICE  # fits: goes on to the device check
     assert call(wide, 0) == dpc.DP_ERR_SHAPE
     assert call(wide, 1025) == dpc.DP_ERR_SHAPE
     assert call(None, 4) == dpc.DP_ERR_NULL
