@@ -69,7 +69,7 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 constexpr uint64_t kMaxWorkgroups = (1ull << 32) / 512;
 bool grid_fits(uint64_t workgroups) { return workgroups < kMaxWorkgroups; }
 
-// a sample's tiles are counted in 16 bits of its arrival counter
+// tiles per sample of one norm call (the documented DP_ERR_SHAPE limit)
 constexpr int64_t kMaxTilesPerSample = 65535;
 
 int64_t norm_ntiles(int dtype, int path, int64_t T, int64_t d, int64_t p, int has_bias) {
@@ -130,7 +130,7 @@ hipError_t launch_layer_norm(hipStream_t st, int dtype, const void* A, const voi
   return e == hipSuccess ? dpk::launch_norm_finish(st, sink, B) : e;
 }
 
-// Per-layer limits of dp_ghost_norm: tiles per sample (16-bit arrival count)
+// Per-layer limits of dp_ghost_norm: tiles per sample (kMaxTilesPerSample)
 // and the ghost grid (32-bit workgroup ids).
 bool layer_fits(int dtype, int path, int64_t B, int64_t T, int64_t d, int64_t p, int hb) {
   const int64_t nt = norm_ntiles(dtype, path, T, d, p, hb);

@@ -272,6 +272,18 @@ __device__ __forceinline__ u32x4 conv_row16_walk(const ConvGeo& g, const ConvRow
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// A pointer every lane of the wave holds, taken from lane 0 so that it lives
+// in scalar registers (a scalar base for the direct-to-LDS loads). Each half
+// goes through uint32_t: readfirstlane returns a signed int, and widening it
+// directly would sign-extend a low word with bit 31 set into the high word.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
+}
+
 // D += A * B on one 32x32 output block, K = 16 (bf16 inputs).
 __device__ __forceinline__ f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);

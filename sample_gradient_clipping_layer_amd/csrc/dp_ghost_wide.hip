@@ -27,8 +27,8 @@
 //   Grams' 64-entry accumulators until the epilogue forms
 //   sum_{s,t} w(s,t) (GA + bias) GG with w = 2 (s < t), 1 (s = t), 0 (s > t
 //   or past T).
-// - Three LDS stages, one barrier per chunk; the sample's last-arriving tile
-//   sums the tiles' parts in tile order (NormSink).
+// - Three LDS stages, one barrier per chunk; each tile stores its part and
+//   the finish kernel sums a sample's parts in tile order (NormSink).
 // - Work items are XCD-grouped by sample: the tiles of one sample run on one
 //   XCD and share its rows in that XCD's L2.
 #include "dp_common.hpp"
@@ -59,14 +59,6 @@ struct Cfg {
   static_assert(LPC * 1024 * NW == STAGE, "whole 1 KB loads per wave");
 };
 }  // namespace gw
-
-template <typename T>
-__device__ __forceinline__ const T* uniform_ptr(const T* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
-}
 
 struct GwArgs {
   int64_t B, Tn, d, p;

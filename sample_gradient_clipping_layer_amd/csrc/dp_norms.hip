@@ -583,9 +583,10 @@ static std::atomic<uint64_t> g_epoch{0};
 
 // The call counter through a bijection of 48-bit words (xor-shifts and odd
 // multipliers modulo 2^48), so that epochs differ from call to call but look
-// like no small integer or float pattern: an arrival counter's word may hold
-// data a kernel left there (the workspace is shared with tile partials), and
-// such a word passes for the current epoch only if its top 48 bits match.
+// like no small integer or float pattern: an arrival counter's word of the
+// contraction's split fix-up may hold data a kernel left there (the workspace
+// is shared with partial tiles), and such a word passes for the current epoch
+// only if its top 48 bits match.
 static uint64_t mix48(uint64_t x) {
   constexpr uint64_t M = (1ull << 48) - 1;
   x &= M;
