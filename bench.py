@@ -445,6 +445,41 @@ def copy_probe(reps=5):
     print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "launches": reps}), flush=True)
 
 
+def noise_fill(reps=3):
+    """The noise and the mean alone (dp_noise_mean, k_noise_mean) over the
+    outputs of every layer of the GPT-2-large stack: 144 layers, 708 M fp32
+    elements, out-of-place (read acc, write out: 8 bytes per element). HIP
+    events around each pass; prints one JSON line with the rate."""
+    import torch
+    import sample_gradient_clipping_layer_amd as dpc
+    wl = W.WORKLOADS["gpt2large-t1024"]
+    dev = torch.device("cuda", 0)
+    shapes = [(d, p) for (T, d, p) in wl.layers]
+    accs = [torch.randn(d, p, device=dev) for (d, p) in shapes]
+    outs = [torch.empty_like(a) for a in accs]
+    elems = wl.blocks * sum(d * p for (d, p) in shapes)
+
+    def one_pass(step):
+        for b in range(wl.blocks):
+            for k, (d, p) in enumerate(shapes):
+                dpc.dp_noise_mean(accs[k], wl.C, wl.sigma, float(wl.B), wl.seed, 4 * b + k, step, outs[k])
+
+    one_pass(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r in range(reps):
+        one_pass(r + 1)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    for o in outs:
+        assert torch.isfinite(o).all().item()
+    print(json.dumps({"noise_fill_elements": elems, "launches_per_pass": wl.blocks * len(shapes),
+                      "ms_per_pass": round(ms, 4), "algorithmic_bytes_per_pass": 8 * elems,
+                      "GB_per_s": round(8 * elems / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -472,6 +507,8 @@ def main():
                     help="conv workloads: pass each layer's folded input (dp_conv_* calls) instead of its unfolding")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (HBM counter calibration)")
+    ap.add_argument("--noise-fill", action="store_true",
+                    help="only run the noise and the mean (dp_noise_mean) over all 144 GPT-2-large layer outputs")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library runs the clipping path on a single MI355X "
@@ -479,6 +516,9 @@ def main():
         sys.exit(2)
     if a.copy_probe:
         copy_probe()
+        return
+    if a.noise_fill:
+        noise_fill()
         return
     wl = W.WORKLOADS[a.workload]
     # the multi-layer clipped-sum call shares launches among bf16 layers without bias whose T is a

@@ -15,17 +15,44 @@ __global__ __launch_bounds__(256) void k_clip_factors(const float* __restrict__ 
   clip_factor_of(sqnorm[i], C, c + i, norm ? norm + i : nullptr);
 }
 
-// The per-sample fold of a norm launch whose samples span several tiles: one
-// thread per sample (NormSink, norm_sink_finish).
-__global__ __launch_bounds__(256) void k_norm_finish(NormSink sink, int64_t B) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= B) return;
-  norm_sink_finish(sink, i);
+// The per-sample fold of a norm launch whose samples span several tiles
+// (NormSink): one wave per sample. The lanes load 64 tile partials at a time
+// (one coalesced load instead of a chain of dependent ones), and the fold
+// itself runs in tile order through the lanes' values, the same fp32 additions
+// in the same order as norm_sink_finish: each layer's tiles summed from 0, then
+// the layers in order onto the starting value.
+__global__ __launch_bounds__(64) void k_norm_finish(NormSink sink) {
+  const int64_t i = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int nt = sink.ntiles;
+  const float* row = sink.partial + i * nt;
+  float v = sink.accumulate ? sink.sqnorm[i] : 0.f;
+  float tot = 0.f;
+  int l = 0, next = sink.lt[1];
+  for (int base = 0; base < nt; base += kWave) {
+    const float x = base + lane < nt ? row[base + lane] : 0.f;
+#pragma unroll
+    for (int j = 0; j < kWave; ++j) {
+      const int t = base + j;
+      if (t >= nt) break;
+      if (t == next) {  // layer l ends before tile t (every layer has at least one tile)
+        v = (l == 0 && !sink.accumulate) ? tot : v + tot;
+        tot = 0.f;
+        next = sink.lt[++l + 1];
+      }
+      tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
+    }
+  }
+  v = (l == 0 && !sink.accumulate) ? tot : v + tot;
+  if (lane == 0) {
+    sink.sqnorm[i] = v;
+    if (sink.clip_c) clip_factor_of(v, sink.C, sink.clip_c + i, sink.clip_norm ? sink.clip_norm + i : nullptr);
+  }
 }
 
 hipError_t launch_norm_finish(hipStream_t st, const NormSink& sink, int64_t B) {
   if (sink.ntiles == 1) return hipSuccess;  // the tiles wrote sqnorm themselves
-  hipLaunchKernelGGL(k_norm_finish, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, st, sink, B);
+  hipLaunchKernelGGL(k_norm_finish, dim3((unsigned)B), dim3(kWave), 0, st, sink);
   return hipGetLastError();
 }
 
@@ -95,20 +122,25 @@ __global__ __launch_bounds__(256) void k_accumulate(float* __restrict__ acc, con
 // element (m, n): lane m % 4 of group (m/4)*p + n, word 2*layer; bias element
 // n: lane n % 4 of group n/4, word 2*layer + 1). One thread per Philox block
 // (4 rows of one column); reads its block before writing it, so out may be acc.
+// The group index t = q*p + n is below 2^32 (the host checks ceil(d/4)*p <
+// 2^32), so q and n come from a 32-bit multiply-shift division by p.
 __global__ __launch_bounds__(256) void k_noise_mean(const float* acc, const float* bias_acc, int64_t d, int64_t p,
-                                                    NoiseArgs na, float* out, float* bias_out) {
+                                                    FastDiv by_p, NoiseArgs na, float* out, float* bias_out) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nw = ((d + 3) / 4) * p;
   if (t < nw) {
-    const int64_t q = t / p, n = t % p;
-    const f32x4 z = normals4((uint32_t)t, 2u * na.layer, na.step, 0u, na.k0, na.k1);
+    const uint32_t tt = (uint32_t)t;
+    const uint32_t q = fast_div(tt, by_p), n = tt - q * (uint32_t)p;
+    const f32x4 z = normals4(tt, 2u * na.layer, na.step, 0u, na.k0, na.k1);
+    const int64_t e0 = (int64_t)(4 * (uint64_t)q) * p + n;  // element (4q, n)
+    const int rows = d - 4 * (int64_t)q < 4 ? (int)(d - 4 * (int64_t)q) : 4;
     float v[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (4 * q + r < d) v[r] = acc[(4 * q + r) * p + n];
+      if (r < rows) v[r] = acc[e0 + r * p];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (4 * q + r < d) out[(4 * q + r) * p + n] = noised_mean_spec(v[r], na.sc, z[r], na.inv_denom);
+      if (r < rows) out[e0 + r * p] = noised_mean_spec(v[r], na.sc, z[r], na.inv_denom);
   } else if (bias_acc && t < nw + (p + 3) / 4) {
     const int64_t g = t - nw;
     const f32x4 z = normals4((uint32_t)g, 2u * na.layer + 1u, na.step, 0u, na.k0, na.k1);
@@ -132,8 +164,8 @@ hipError_t launch_accumulate(hipStream_t st, float* acc, const float* s, int64_t
 hipError_t launch_noise_mean(hipStream_t st, const float* acc, const float* bias_acc, int64_t d, int64_t p,
                              const NoiseArgs& na, float* out, float* bias_out) {
   const int64_t threads = ((d + 3) / 4) * p + (bias_acc ? (p + 3) / 4 : 0);
-  hipLaunchKernelGGL(k_noise_mean, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, acc, bias_acc, d, p, na,
-                     out, bias_out);
+  hipLaunchKernelGGL(k_noise_mean, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, acc, bias_acc, d, p,
+                     make_fastdiv((uint32_t)p), na, out, bias_out);
   return hipGetLastError();
 }
 
