@@ -12,7 +12,10 @@
 // columns t in [128 c, 128 c + 128), c >= 2r (every entry with s <= t lies in
 // such a tile). A T x T Gram has sum over r of (ceil(T/128) - 2r) tiles.
 // When the column block lies inside the row block (c = 2r or 2r + 1) its
-// rows are read from the row block's stage instead of being loaded again.
+// rows are read from the row block's stage instead of being loaded again;
+// for c = 2r only the first 128 rows of the row block hold entries s <= t, and
+// only they are loaded. A wave whose 64 x 64 sub-tile lies wholly below the
+// diagonal (or past T) has weight 0 everywhere and skips its reads and MFMAs.
 //
 // gfx950 mapping:
 // - Features are streamed in chunks of 64: a chunk holds the tile's rows
@@ -50,10 +53,12 @@ constexpr int WM = BM / WGM, WN = BN / WGN;  // 64 x 64
 static_assert(WM == 64 && WN == 64, "two 32-blocks per operand and wave");
 static_assert(LDS <= 160 * 1024, "LDS budget");
 
-// TIN: the column block's rows are inside the row block (not loaded twice).
-template <bool TIN>
+// Tile kinds: 0 = column block outside the row block (BM + BN rows loaded);
+// 1 = column block inside it, c = 2r + 1 (BM rows); 2 = c = 2r, where rows
+// past the first BN are wholly below the diagonal (BN rows).
+template <int KIND>
 struct Cfg {
-  static constexpr int ROWS = TIN ? BM : BM + BN;
+  static constexpr int ROWS = KIND == 0 ? BM + BN : (KIND == 1 ? BM : BN);
   static constexpr int STAGE = ROWS * ROWB;
   static constexpr int LPC = STAGE / (1024 * NW);  // 1 KB loads per wave per chunk
   static_assert(LPC * 1024 * NW == STAGE, "whole 1 KB loads per wave");
@@ -78,16 +83,22 @@ __device__ __forceinline__ void gw_tile_rc(int tile, int nbc, int* r, int* c) {
   *c = 2 * rr + rem;
 }
 
-template <bool TIN>
+template <int KIND>
 __device__ __forceinline__ float gw_item(const bf16s* __restrict__ Ai, const bf16s* __restrict__ Gi, const GwArgs& a,
                                          int r, int c, unsigned char* lds) {
-  using C = gw::Cfg<TIN>;
+  using C = gw::Cfg<KIND>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave % gw::WGM, wn = wave / gw::WGM;
+  // sub-tile (wm, wn) of wave w: (0,0) (0,1) (1,1) (1,0) (2,0) (2,1) (3,0) (3,1). Wave w runs
+  // on SIMD w % 4, so the sub-tiles that diagonal tiles keep ((0,0), (0,1), (1,1) for c = 2r,
+  // all but (3,0) for c = 2r + 1) sit on different SIMDs where they can.
+  const int wm = wave >> 1, wn = (wave & 1) ^ (wm == 1 ? 1 : 0);
   const int64_t row0 = (int64_t)r * gw::BM;       // first Gram row of the tile
   const int64_t col0 = (int64_t)c * gw::BN;       // first Gram column of the tile
-  const int toff = TIN ? (int)(col0 - row0) : gw::BM;  // stage row of the column block's first row
+  const int toff = KIND == 0 ? gw::BM : (int)(col0 - row0);  // stage row of the column block's first row
+  // every entry of the wave's sub-tile has s > t or lies past T: weight 0, nothing to compute
+  const int64_t sr0 = row0 + wm * gw::WM, sc0 = col0 + wn * gw::WN;
+  const bool idle = sr0 > sc0 + (gw::WN - 1) || sr0 >= a.Tn || sc0 >= a.Tn;
   const int64_t nA = a.d / gw::KC, nG = a.p / gw::KC, n = nA + nG;
 
   // ---- this lane's 16-byte pieces: load i of the wave covers stage rows
@@ -167,6 +178,10 @@ __device__ __forceinline__ float gw_item(const bf16s* __restrict__ Ai, const bf1
   };
   issue(0, 0);
   if (n > 1) issue(1, 1);
+  if (idle) {  // wave-uniform: the wave still loads its share and meets every barrier
+    for (int64_t q = 0; q < n; ++q) (void)step(q);
+    return 0.0f;
+  }
   for (int64_t q = 0; q < nA; ++q) compute(step(q), accA);
   for (int64_t q = nA; q < n; ++q) compute(step(q), accG);
 
@@ -229,8 +244,8 @@ __global__ __launch_bounds__(gw::NT, 1) void k_ghost_wide(GwGroup g, NormSink si
   // (the direct-to-LDS loads take a scalar base)
   const bf16s* Ai = uniform_ptr(L.A + i * a.Tn * a.d);
   const bf16s* Gi = uniform_ptr(L.G + i * a.Tn * a.p);
-  const bool tin = c < 2 * r + 2;  // column block inside the row block
-  float s = tin ? gw_item<true>(Ai, Gi, a, r, c, lds) : gw_item<false>(Ai, Gi, a, r, c, lds);
+  float s = c >= 2 * r + 2 ? gw_item<0>(Ai, Gi, a, r, c, lds)
+            : (c == 2 * r + 1 ? gw_item<1>(Ai, Gi, a, r, c, lds) : gw_item<2>(Ai, Gi, a, r, c, lds));
   s = block_sum<gw::NT>(s, red);
   if (threadIdx.x == 0) norm_sink_tile(sink, i, L.tile_base + tile, s);
 }

@@ -32,8 +32,15 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
 // Workgroup barrier that orders LDS only: waits for this wave's LDS reads
 // (lgkmcnt) but not for its global loads in flight (vmcnt), which the
 // pipeline waits for explicitly. The memory clobber keeps the compiler from
-// moving memory operations across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// moving memory operations across it. The wait is also given as a builtin,
+// which the compiler's wait insertion sees (it cannot see into the asm):
+// without it the pass keeps assuming that scalar loads from before the loop
+// may be outstanding, and since those return out of order it then waits for
+// every LDS read of a chunk before the chunk's first MFMA.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt(63), expcnt(7): no wait
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // Wait until at most k chunks of `LPC` loads each are still in flight
 // (k <= MAXK); uniform branches down to an immediate vmcnt.
