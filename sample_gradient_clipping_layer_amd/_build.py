@@ -16,6 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdpclip.so")
+CEILINGS_SRC = os.path.join(PKG, "ceilings", "dp_ceilings.hip")
+CEILINGS = os.path.join(PKG, "dp_ceilings")  # stand-alone probe program, not part of the library
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -61,6 +63,13 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources", flush=True)
+    cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f != "-fPIC"], "-o", CEILINGS + ".tmp", CEILINGS_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(CEILINGS + ".tmp", CEILINGS)
+    if verbose:
+        print(f"built {CEILINGS}", flush=True)
     return LIB
 
 

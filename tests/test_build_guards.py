@@ -29,7 +29,8 @@ def _asm(src):
     return out.stdout
 
 
-SOURCES = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+SOURCES = sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [
+    os.path.join(ROOT, "sample_gradient_clipping_layer_amd", "ceilings", "dp_ceilings.hip")]
 
 
 @pytest.mark.parametrize("src", SOURCES, ids=[os.path.basename(s) for s in SOURCES])
