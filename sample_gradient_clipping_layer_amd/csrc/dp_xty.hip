@@ -534,17 +534,25 @@ template <typename T, int BM, int BN, bool FUSED, bool IM2COL>
 __global__ __launch_bounds__(256, (ContractOcc<T, BM, BN>::value)) void k_contract_tiles(const T* __restrict__ A, const T* __restrict__ G,
                                                            const float* __restrict__ c, int64_t B, int64_t Tn,
                                                            int64_t d, int64_t p, int has_bias, int mt, int nt,
-                                                           int64_t units_per_split, int vecA, int vecG,
-                                                           float* __restrict__ ws, NoiseArgs na,
+                                                           int64_t units_per_split, int64_t nitems, int vecA,
+                                                           int vecG, float* __restrict__ ws, NoiseArgs na,
                                                            float* __restrict__ out, float* __restrict__ bias_out,
                                                            ConvGeo geo) {
   using E = Xty<T, BM, BN>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[E::LDS_BYTES];
+  // Work items (split, column block, row block), row block fastest; XCD x
+  // (blockIdx % 8) takes the contiguous items [x * per, (x + 1) * per), so the
+  // row blocks that read one slice of G (one column block and split) run
+  // together on one XCD and share that slice in its L2. The grid is a
+  // multiple of 8; surplus workgroups return before any barrier.
+  const int64_t per = gridDim.x / 8;
+  const int64_t item = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (item >= nitems) return;
   const int ntl = mt * nt;
-  const int tile = (int)(blockIdx.x % ntl);
-  const int64_t split = blockIdx.x / ntl;
-  const int64_t m0 = (tile / nt) * BM;
-  const int64_t n0 = (tile % nt) * BN;
+  const int64_t split = item / ntl;
+  const int tile = (int)(item - split * ntl);
+  const int64_t m0 = (tile % mt) * BM;
+  const int64_t n0 = (tile / mt) * BN;
   const int64_t ones_col = has_bias ? d : -1;
   const int64_t mrows = d + (has_bias ? 1 : 0);
   const bool wide = !IM2COL && vecA && vecG && (m0 + BM <= d) && (n0 + BN <= p);
@@ -984,14 +992,15 @@ static void launch_contract_k(hipStream_t st, dim3 grid, const void* A, const vo
                               int64_t Tn, int64_t d, int64_t p, int has_bias, const ContractPlan& pl, int vecA,
                               int vecG, float* ws, const NoiseArgs& na, float* out, float* bias_out,
                               const ConvGeo* geo) {
+  const int64_t nitems = (int64_t)pl.mt * pl.nt * pl.ks;
   if (geo)
     hipLaunchKernelGGL((k_contract_tiles<T, BM, BN, FUSED, true>), grid, dim3(256), 0, st, static_cast<const T*>(A),
-                       static_cast<const T*>(G), c, B, Tn, d, p, has_bias, pl.mt, pl.nt, pl.units_per_split, 0,
-                       vecG, ws, na, out, bias_out, *geo);
+                       static_cast<const T*>(G), c, B, Tn, d, p, has_bias, pl.mt, pl.nt, pl.units_per_split, nitems,
+                       0, vecG, ws, na, out, bias_out, *geo);
   else
     hipLaunchKernelGGL((k_contract_tiles<T, BM, BN, FUSED, false>), grid, dim3(256), 0, st, static_cast<const T*>(A),
-                       static_cast<const T*>(G), c, B, Tn, d, p, has_bias, pl.mt, pl.nt, pl.units_per_split, vecA,
-                       vecG, ws, na, out, bias_out, ConvGeo{});
+                       static_cast<const T*>(G), c, B, Tn, d, p, has_bias, pl.mt, pl.nt, pl.units_per_split, nitems,
+                       vecA, vecG, ws, na, out, bias_out, ConvGeo{});
 }
 
 template <typename T, int BM, int BN>
@@ -1002,7 +1011,7 @@ static hipError_t launch_contract_t(hipStream_t st, const void* A, const void* G
   const int eb = elem_traits<T>::bytes;
   const int vecA = ((reinterpret_cast<uintptr_t>(A) & 15) == 0) && ((d * eb) % 16 == 0);
   const int vecG = ((reinterpret_cast<uintptr_t>(G) & 15) == 0) && ((p * eb) % 16 == 0);
-  const dim3 grid((unsigned)((int64_t)pl.mt * pl.nt * pl.ks));
+  const dim3 grid((unsigned)(((int64_t)pl.mt * pl.nt * pl.ks + 7) / 8 * 8));  // whole XCD rounds
   if (pl.ks == 1)
     launch_contract_k<T, BM, BN, true>(st, grid, A, G, c, B, Tn, d, p, has_bias, pl, vecA, vecG, ws, na, out,
                                        bias_out, geo);
