@@ -79,6 +79,8 @@ __global__ __launch_bounds__(256) void k_norm_t1(const T* __restrict__ A, const 
 #define GHOST64_GROUPS 2
 #endif
 constexpr int kGhost64Groups = GHOST64_GROUPS;
+// At most this many samples share one Gram tile (samples of T <= TS / 2 rows).
+constexpr int kGhostPackMax = 4;
 
 template <typename T, int TS>
 struct GhostCfg {
@@ -299,6 +301,7 @@ struct GhostLayer {
   const T* A;
   const T* G;
   int64_t Tn, d, p;
+  int pack;  // samples stacked in one tile (T <= TS / 2), else 1
   int64_t wg_begin;
   int nb, ntiles, tile_base, vecA, vecG, has_bias;
 };
@@ -328,9 +331,14 @@ __global__ __launch_bounds__((GhostCfg<T, TS>::NT)) void k_ghost_tiles(GhostGrou
   const int64_t Tn = L.Tn, d = L.d, p = L.p;
   const int nb = L.nb, vecA = L.vecA, vecG = L.vecG, has_bias = L.has_bias;
 
-  int64_t i, tile;
-  xcd_group_map((int64_t)blockIdx.x - L.wg_begin, L.ntiles, &i, &tile);
-  if (i >= B) return;
+  int64_t grp_i, tile;
+  xcd_group_map((int64_t)blockIdx.x - L.wg_begin, L.ntiles, &grp_i, &tile);
+  // samples i0 .. i0 + nvalid - 1 (one unless the layer packs several short samples per tile)
+  const int pack = L.pack;
+  const int64_t i0 = grp_i * pack;
+  if (i0 >= B) return;
+  const int nvalid = (int)(B - i0 < pack ? B - i0 : pack);
+  const int64_t rows = nvalid * Tn;  // valid tile rows: consecutive rows of consecutive samples
   int sb = 0;
   int rem = (int)tile;
   while (rem >= nb - sb) {
@@ -351,10 +359,10 @@ __global__ __launch_bounds__((GhostCfg<T, TS>::NT)) void k_ghost_tiles(GhostGrou
         acc_g[bi][bj][j] = 0.f;
       }
 
-  const T* Ai = IM2COL ? A : A + i * Tn * d;
-  const T* Gi = G + i * Tn * p;
+  const T* Ai = IM2COL ? A : A + i0 * Tn * d;
+  const T* Gi = G + i0 * Tn * p;
   const bool full =
-      !IM2COL && vecA && vecG && (int64_t)(tb + 1) * TS <= Tn && d % Cfg::KC == 0 && p % Cfg::KC == 0;
+      !IM2COL && vecA && vecG && (int64_t)(tb + 1) * TS <= rows && d % Cfg::KC == 0 && p % Cfg::KC == 0;
   if (full && sb == tb) {
     GhostFull<T, TS, true>::run(Ai, Gi, d, p, sb, tb, lds, acc_a, acc_g);
   } else if (full) {
@@ -365,9 +373,9 @@ __global__ __launch_bounds__((GhostCfg<T, TS>::NT)) void k_ghost_tiles(GhostGrou
   const int64_t n = nA + nG;
   typename Cfg::Regs regs;
   if constexpr (IM2COL)
-    ghost_load_conv<T, TS>(regs, grp.conv, i, sb, tb, 0);
+    ghost_load_conv<T, TS>(regs, grp.conv, i0, sb, tb, 0);  // pack == 1
   else
-    ghost_load<T, TS>(regs, Ai, Tn, d, vecA != 0, sb, tb, 0);
+    ghost_load<T, TS>(regs, Ai, rows, d, vecA != 0, sb, tb, 0);
   for (int64_t c = 0; c < n; ++c) {
     unsigned char* buf = lds + (c & 1) * Cfg::BUF;
     ghost_store<T, TS>(regs, buf, diag);
@@ -375,11 +383,11 @@ __global__ __launch_bounds__((GhostCfg<T, TS>::NT)) void k_ghost_tiles(GhostGrou
     const int64_t cn = c + 1;
     if (cn < nA) {
       if constexpr (IM2COL)
-        ghost_load_conv<T, TS>(regs, grp.conv, i, sb, tb, cn);
+        ghost_load_conv<T, TS>(regs, grp.conv, i0, sb, tb, cn);
       else
-        ghost_load<T, TS>(regs, Ai, Tn, d, vecA != 0, sb, tb, cn);
+        ghost_load<T, TS>(regs, Ai, rows, d, vecA != 0, sb, tb, cn);
     } else if (cn < n)
-      ghost_load<T, TS>(regs, Gi, Tn, p, vecG != 0, sb, tb, cn - nA);
+      ghost_load<T, TS>(regs, Gi, rows, p, vecG != 0, sb, tb, cn - nA);
     if (c < nA)
       ghost_compute<T, TS>(buf, diag, acc_a);
     else
@@ -433,6 +441,46 @@ __global__ __launch_bounds__((GhostCfg<T, TS>::NT)) void k_ghost_tiles(GhostGrou
   }
 
   const float one = has_bias ? 1.0f : 0.0f;
+  if (pack > 1) {
+    // one diagonal tile of stacked samples: only entries of two rows of the
+    // same sample count, summed per sample (row r belongs to sample r / T)
+    __shared__ float red4[kGhostPackMax * (Cfg::NT / kWave)];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wq = wave & 3, wm = wq & 1, wn = wq >> 1;
+    float sk[kGhostPackMax];
+#pragma unroll
+    for (int k = 0; k < kGhostPackMax; ++k) sk[k] = 0.f;
+    if (owner) {
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int r = wm * Cfg::WM + bi * 32 + acc_row(j, lane);
+            const int c = wn * Cfg::WM + bj * 32 + acc_col(lane);
+            const int kr = r / (int)Tn, kc = c / (int)Tn;
+            const float v = (acc_a[bi][bj][j] + one) * acc_g[bi][bj][j];
+#pragma unroll
+            for (int k = 0; k < kGhostPackMax; ++k)
+              if (kr == k && kc == k) sk[k] += v;
+          }
+    }
+#pragma unroll
+    for (int k = 0; k < kGhostPackMax; ++k) sk[k] = wave_sum(sk[k]);
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < kGhostPackMax; ++k) red4[k * (Cfg::NT / kWave) + wave] = sk[k];
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < nvalid) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < Cfg::NT / kWave; ++w) v += red4[threadIdx.x * (Cfg::NT / kWave) + w];
+      norm_sink_tile(sink, i0 + threadIdx.x, L.tile_base + tile, v);
+    }
+    return;
+  }
   float s = 0.f;
   if (owner) {
 #pragma unroll
@@ -444,7 +492,7 @@ __global__ __launch_bounds__((GhostCfg<T, TS>::NT)) void k_ghost_tiles(GhostGrou
   }
   if (!diag) s *= 2.0f;
   s = block_sum<Cfg::NT>(s, red);
-  if (threadIdx.x == 0) norm_sink_tile(sink, i, L.tile_base + tile, s);
+  if (threadIdx.x == 0) norm_sink_tile(sink, i0, L.tile_base + tile, s);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -477,7 +525,7 @@ int64_t ghost_ntiles(int dtype, int64_t T, int64_t d, int64_t p) {
 }
 
 template <typename T>
-static GhostLayer<T> ghost_layer(const GhostLayerDesc& x, int ts) {
+static GhostLayer<T> ghost_layer(const GhostLayerDesc& x, int ts, bool folded) {
   const int eb = elem_traits<T>::bytes;
   GhostLayer<T> L{};
   L.A = static_cast<const T*>(x.A);
@@ -487,6 +535,12 @@ static GhostLayer<T> ghost_layer(const GhostLayerDesc& x, int ts) {
   L.p = x.p;
   L.nb = (int)((x.Tn + ts - 1) / ts);
   L.ntiles = L.nb * (L.nb + 1) / 2;
+  // samples of at most half a tile share one tile (up to kGhostPackMax): the
+  // loads then fill the tile's rows instead of one sample's few. Not for
+  // folded convolution inputs: their rows are gathered element by element
+  // whatever the tile holds, and packing only removes workgroups.
+  const int64_t fit = ts / x.Tn;
+  L.pack = !folded && fit >= 2 ? (int)(fit < kGhostPackMax ? fit : kGhostPackMax) : 1;
   L.vecA = ((reinterpret_cast<uintptr_t>(x.A) & 15) == 0) && ((x.d * eb) % 16 == 0);
   L.vecG = ((reinterpret_cast<uintptr_t>(x.G) & 15) == 0) && ((x.p * eb) % 16 == 0);
   L.has_bias = x.has_bias;
@@ -503,7 +557,7 @@ hipError_t launch_ghost_t(hipStream_t st, const GhostLayerDesc* layers, int n, i
   int order[kNormGroupMax];
   int base = 0;
   for (int l = 0; l < n; ++l) {
-    grp.L[l] = ghost_layer<T>(layers[l], TS);
+    grp.L[l] = ghost_layer<T>(layers[l], TS, conv != nullptr);
     grp.L[l].tile_base = base;
     base += grp.L[l].ntiles;
     order[l] = l;
@@ -516,12 +570,12 @@ hipError_t launch_ghost_t(hipStream_t st, const GhostLayerDesc* layers, int n, i
       order[b - 1] = t;
     }
   GhostGroup<T> sorted{};
-  const int64_t groups8 = (B + 7) / 8;
   int64_t wg = 0;
   for (int k = 0; k < n; ++k) {
     sorted.L[k] = grp.L[order[k]];
     sorted.L[k].wg_begin = wg;
-    wg += groups8 * 8 * sorted.L[k].ntiles;
+    const int64_t units = (B + sorted.L[k].pack - 1) / sorted.L[k].pack;  // samples or sample packs
+    wg += (units + 7) / 8 * 8 * sorted.L[k].ntiles;
   }
   sorted.n = n;
   const size_t lds_bytes = 2 * GhostCfg<T, TS>::BUF;
