@@ -26,8 +26,9 @@
 //   of G_i (Gram of G).
 // - A Gram product only needs row-major operands: an MFMA 32x32x16 operand
 //   is 8 consecutive features of one row, one ds_read_b128 (no transposes).
-// - 8 waves in a 4 x 2 grid of 64 x 64 sub-tiles; each lane holds both
-//   Grams' 64-entry accumulators until the epilogue forms
+// - 8 waves on the 4 x 2 grid of 64 x 64 sub-tiles (assignment in
+//   gw_item); each lane holds both Grams' 64-entry accumulators until the
+//   epilogue forms
 //   sum_{s,t} w(s,t) (GA + bias) GG with w = 2 (s < t), 1 (s = t), 0 (s > t
 //   or past T).
 // - Three LDS stages, one barrier per chunk; each tile stores its part and

@@ -74,7 +74,10 @@ __global__ __launch_bounds__(256) void k_norm_t1(const T* __restrict__ A, const 
 // double-buffered LDS, with the next chunk's global loads in flight during
 // the MFMAs of this one: first the chunks of A_i (K = d, Gram of A), then
 // those of G_i (K = p, Gram of G). The epilogue forms sum (GA + bias) .* GG,
-// doubled off the diagonal.
+// doubled off the diagonal. Samples of at most TS/2 rows are stacked, up to
+// kGhostPackMax consecutive samples per tile (their rows are consecutive in
+// memory): the workgroup then takes one diagonal tile of all of them, and the
+// epilogue keeps only the entries of two rows of one sample, per sample.
 #ifndef GHOST64_GROUPS
 #define GHOST64_GROUPS 2
 #endif

@@ -652,8 +652,8 @@ def test_concurrent_streams_bitwise():
 # ------------------------------------------------------------------ ghost path shapes
 # bf16 ghost norms over 64-row tiles (T <= 384), 128-row tiles (T > 384) and
 # 256 x 128 tiles (T >= 512 with d and p multiples of 64): one tile with most
-# rows past T, ragged T, up to 36 tiles per sample, bias on and off,
-# accumulation into sqnorm.
+# rows past T, ragged T, up to 36 tiles per sample, several short samples
+# stacked in one tile, bias on and off, accumulation into sqnorm.
 GHOST_CASES = [
     # B, T, d, p, has_bias
     (3, 5, 128, 256, True),      # 1 tile of 64
@@ -669,6 +669,9 @@ GHOST_CASES = [
     (1, 1100, 192, 64, True),    # 25 tiles, ragged
     (4, 1024, 64, 64, False),    # 20 tiles
     (9, 520, 64, 64, True),      # 9 tiles; samples on two XCD rounds
+    (9, 16, 128, 64, True),      # 4 samples per 64-row tile: packs of 4, 4, 1
+    (5, 32, 64, 128, False),     # 2 samples per tile, the last pack half full
+    (7, 20, 96, 64, True),       # 3 samples per tile (60 of 64 rows), packs of 3, 3, 1
 ]
 
 
