@@ -146,36 +146,61 @@ __device__ __forceinline__ void dl_fixup(const DlLayer& L, uint64_t epoch, int64
   __syncthreads();
   if (*flag == 0u) return;
   const int64_t sstride = L.d * L.p;
-  constexpr int KU = 4;  // splits whose loads are issued together
+  // Work unit: 4 rows x 2 columns (two Philox blocks). A thread takes UB
+  // units at a time and issues the loads of KU splits of all of them
+  // together: the fix-up runs on one CU at the end of an item, and with the
+  // loads of one unit in flight it waited out a memory latency per unit.
+  constexpr int KU = 2;  // splits per pass
+  constexpr int UB = 4;  // units per pass
+  constexpr int NU = (BM / 4) * (BN / 2);
 #pragma unroll 1
-  for (int u = threadIdx.x; u < (BM / 4) * (BN / 2); u += NT) {
-    const int64_t m = m0 + 4 * (u / (BN / 2)), n = n0 + 2 * (u % (BN / 2));
-    if (m >= L.d || n >= L.p) continue;  // d % 8 == 0, p % 8 == 0: all 4 rows and both columns exist
-    const float* base = L.ws + m * L.p + n;
-    float sx[4] = {0.f, 0.f, 0.f, 0.f}, sy[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int u0 = threadIdx.x; u0 < NU; u0 += UB * NT) {
+    int64_t m[UB], n[UB];
+    bool ok[UB];
+    float sx[UB][4], sy[UB][4];
+#pragma unroll
+    for (int b = 0; b < UB; ++b) {
+      const int u = u0 + b * NT;
+      m[b] = m0 + 4 * (u / (BN / 2));
+      n[b] = n0 + 2 * (u % (BN / 2));
+      ok[b] = u < NU && m[b] < L.d && n[b] < L.p;  // d % 8 == 0, p % 8 == 0: all 4 rows and both columns exist
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sx[b][r] = sy[b][r] = 0.f;
+    }
 #pragma unroll 1
     for (int64_t s0 = 0; s0 < L.ks; s0 += KU) {
-      float2 v[KU][4];
+      float2 v[UB][KU][4];
 #pragma unroll
-      for (int j = 0; j < KU; ++j)
+      for (int b = 0; b < UB; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (s0 + j < L.ks) v[j][r] = *reinterpret_cast<const float2*>(base + (s0 + j) * sstride + r * L.p);
+        for (int j = 0; j < KU; ++j)
 #pragma unroll
-      for (int j = 0; j < KU; ++j)
+          for (int r = 0; r < 4; ++r)
+            if (ok[b] && s0 + j < L.ks)
+              v[b][j][r] = *reinterpret_cast<const float2*>(L.ws + (s0 + j) * sstride + (m[b] + r) * L.p + n[b]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (s0 + j < L.ks) {
-            sx[r] += v[j][r].x;
-            sy[r] += v[j][r].y;
-          }
+      for (int b = 0; b < UB; ++b)
+#pragma unroll
+        for (int j = 0; j < KU; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (ok[b] && s0 + j < L.ks) {  // split order: 0 + P_0 + P_1 + ...
+              sx[b][r] += v[b][j][r].x;
+              sy[b][r] += v[b][j][r].y;
+            }
     }
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const f32x4 z = normals4((uint32_t)((m >> 2) * L.p + n + cc), 2u * L.na.layer, L.na.step, 0u, L.na.k0, L.na.k1);
+    for (int b = 0; b < UB; ++b) {
+      if (!ok[b]) continue;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        L.out[(m + r) * L.p + n + cc] = noised_mean_spec(cc ? sy[r] : sx[r], L.na.sc, z[r], L.na.inv_denom);
+      for (int cc = 0; cc < 2; ++cc) {
+        const f32x4 z =
+            normals4((uint32_t)((m[b] >> 2) * L.p + n[b] + cc), 2u * L.na.layer, L.na.step, 0u, L.na.k0, L.na.k1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          L.out[(m[b] + r) * L.p + n[b] + cc] =
+              noised_mean_spec(cc ? sy[b][r] : sx[b][r], L.na.sc, z[r], L.na.inv_denom);
+      }
     }
   }
 }
