@@ -615,6 +615,15 @@ def main():
                          f"steps of the adaptive schedule (step k uses set k mod {n_sets}); the initial bounds "
                          f"from a separate random-noise batch")
         cfg["schedule_steps"] = wl.steps
+    # layer-GB/s: the algorithmic bytes of a step's calls (per layer and physical batch: A and G read by the
+    # norm pass and again by the clipped sum, 4 bytes per norm, the d x p fp32 output) over the step time
+    step_bytes = 0.0
+    for ll, (T, d, p) in enumerate(shapes):
+        a_el = None if geos is None else geos[ll].C_in * geos[ll].H * geos[ll].W
+        step_bytes += _algorithmic(wl, T, d, p, "norm", MODES[a.path_rule], a_el)[1]
+        step_bytes += _algorithmic(wl, T, d, p, "sum", MODES[a.path_rule], a_el)[1]
+    step_bytes *= max(1, a.virtual_steps)
+    layer_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "examples/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -623,6 +632,8 @@ def main():
         "gpu_ms_per_step": round(gpu_ms / a.steps, 4),
         "calls_ms_per_step": round(float(call_ms.sum(axis=1).mean()), 4),
         "breakdown_steps": int(call_ms.shape[0]),
+        "layer_GB_per_s": round(layer_gbs, 1),
+        "layer_GB_per_s_frac_hbm": round(layer_gbs / PEAK_HBM_GBS, 4),
     }
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
