@@ -1,4 +1,5 @@
-// Ghost norm of a bf16 layer with long sequences, direct-to-LDS engine.
+// Ghost norm of a bf16 layer of more than 64 rows per sample, direct-to-LDS
+// engine.
 //
 // The per-example squared norm of "Scalable and Efficient Training of Large
 // CNNs with DP", eq. (2.7) / Sec. 3.1 (ghost clipping):
@@ -6,7 +7,10 @@
 // A_i A_i^T + 1 1^T, without forming A_i^T G_i. Both Grams are symmetric, so
 // only entries s <= t are computed; entries s < t count twice.
 //
-// Eligible layers: bf16, T >= 512, d and p multiples of 64.
+// Eligible layers: bf16, T > 64, d and p multiples of 64 (samples of at most
+// 64 rows are stacked in the tiled kernel's 64-row tiles instead). At
+// T <= 128 a sample is one 128 x 128 tile: each row is read once, by one
+// workgroup.
 //
 // Work item = (sample i, Gram tile (r, c)): rows s in [256 r, 256 r + 256) x
 // columns t in [128 c, 128 c + 128), c >= 2r (every entry with s <= t lies in
@@ -19,7 +23,7 @@
 //
 // gfx950 mapping:
 // - Features are streamed in chunks of 64: a chunk holds the tile's rows
-//   (256 + 128, or 256) x 128 bytes and goes from HBM straight to LDS with
+//   (256 + 128, 256 or 128) x 128 bytes and goes from HBM straight to LDS with
 //   16-byte global_load_lds; the 16-byte pieces of row R are XOR-swizzled by
 //   (R / 2) % 8, so that the 16 rows a ds_read_b128 serves per pass land on
 //   64 distinct banks. The chunks of A_i come first (Gram of A), then those
@@ -31,8 +35,10 @@
 //   epilogue forms
 //   sum_{s,t} w(s,t) (GA + bias) GG with w = 2 (s < t), 1 (s = t), 0 (s > t
 //   or past T).
-// - Three LDS stages, one barrier per chunk; each tile stores its part and
-//   the finish kernel sums a sample's parts in tile order (NormSink).
+// - LDS stages: 3 for the 384- and 256-row tiles, 4 for the 128-row tile
+//   (its chunks are a third the size); one barrier per chunk; each tile
+//   stores its part and the finish kernel sums a sample's parts in tile
+//   order (NormSink).
 // - Work items are XCD-grouped by sample: the tiles of one sample run on one
 //   XCD and share its rows in that XCD's L2.
 #include "dp_common.hpp"
@@ -57,12 +63,26 @@ static_assert(LDS <= 160 * 1024, "LDS budget");
 // Tile kinds: 0 = column block outside the row block (BM + BN rows loaded);
 // 1 = column block inside it, c = 2r + 1 (BM rows); 2 = c = 2r, where rows
 // past the first BN are wholly below the diagonal (BN rows).
+#ifndef GW_STAGES0
+#define GW_STAGES0 3
+#endif
+#ifndef GW_STAGES1
+#define GW_STAGES1 3
+#endif
+#ifndef GW_STAGES2
+#define GW_STAGES2 4
+#endif
 template <int KIND>
 struct Cfg {
   static constexpr int ROWS = KIND == 0 ? BM + BN : (KIND == 1 ? BM : BN);
   static constexpr int STAGE = ROWS * ROWB;
+  // LDS stages of this kind's chunks in the launch's allocation: the smaller
+  // tiles keep more chunks in flight
+  static constexpr int STAGES = KIND == 0 ? GW_STAGES0 : (KIND == 1 ? GW_STAGES1 : GW_STAGES2);
   static constexpr int LPC = STAGE / (1024 * NW);  // 1 KB loads per wave per chunk
   static_assert(LPC * 1024 * NW == STAGE, "whole 1 KB loads per wave");
+  static_assert(STAGES >= 3 && STAGES * STAGE <= LDS, "stages fit the allocation");
+  static_assert(LPC * (STAGES - 2) <= 63, "vmcnt range");
 };
 }  // namespace gw
 
@@ -117,7 +137,7 @@ __device__ __forceinline__ float gw_item(const bf16s* __restrict__ Ai, const bf1
   }
   const uint32_t rowbA = (uint32_t)(a.d * 2), rowbG = (uint32_t)(a.p * 2);  // row bytes
   auto issue = [&](int64_t q, int stage) {
-    const uint32_t sl = lds_addr(lds) + stage * gw::STAGE_MAX + wave * 1024;
+    const uint32_t sl = lds_addr(lds) + stage * C::STAGE + wave * 1024;
     const bool inA = q < nA;
     const bf16s* g = inA ? Ai + q * gw::KC : Gi + (q - nA) * gw::KC;
     const uint32_t rowb = inA ? rowbA : rowbG;
@@ -164,21 +184,22 @@ __device__ __forceinline__ float gw_item(const bf16s* __restrict__ Ai, const bf1
         for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mfma32_bf16(fa[kk][bi], fb[kk][bj], acc[bi][bj]);
   };
 
-  // ---- pipeline: chunk q in stage q % 3; loads for chunk q+2 go out once
+  // ---- pipeline: chunk q in stage q % S; loads for chunk q+S-1 go out once
   // every wave is past chunk q-1 (the barrier), while chunk q is computed.
   // Two loops (A chunks, then G chunks) so that each body updates one
   // accumulator set.
+  constexpr int S = C::STAGES;
   auto step = [&](int64_t q) -> uint32_t {
-    if (q + 1 < n)
-      wait_vmcnt<C::LPC>();
-    else
-      wait_vmcnt<0>();
+    // chunks q+1 .. q+S-2 (those issued) may still be in flight
+    const int later = n - 1 - q < S - 2 ? (int)(n - 1 - q) : S - 2;
+    wait_chunks<C::LPC, S - 2>(later);
     lds_barrier();
-    if (q + 2 < n) issue(q + 2, (int)((q + 2) % 3));
-    return lds_addr(lds) + (uint32_t)((q % 3) * gw::STAGE_MAX);
+    if (q + S - 1 < n) issue(q + S - 1, (int)((q + S - 1) % S));
+    return lds_addr(lds) + (uint32_t)((q % S) * C::STAGE);
   };
-  issue(0, 0);
-  if (n > 1) issue(1, 1);
+#pragma unroll
+  for (int q = 0; q < S - 1; ++q)
+    if (q < n) issue(q, q);
   if (idle) {  // wave-uniform: the wave still loads its share and meets every barrier
     for (int64_t q = 0; q < n; ++q) (void)step(q);
     return 0.0f;
@@ -253,7 +274,7 @@ __global__ __launch_bounds__(gw::NT, 1) void k_ghost_wide(GwGroup g, NormSink si
 
 bool ghost_wide_eligible(int dtype, int64_t Tn, int64_t d, int64_t p) {
   // per-sample byte offsets are 32-bit: T * max(d, p) * 2 < 2^32
-  return dtype == 1 && Tn >= 512 && d % gw::KC == 0 && p % gw::KC == 0 &&
+  return dtype == 1 && Tn > 64 && d % gw::KC == 0 && p % gw::KC == 0 &&
          Tn * (d > p ? d : p) * 2 < (1ll << 32) - 4096;
 }
 

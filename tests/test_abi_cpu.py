@@ -205,7 +205,7 @@ def test_ghost_norm_layers_validation(lib):
     bad = _layers(GPT_BLOCK[:3] + [(128, 0, 768, 0)])  # the last layer's d
     assert call(bad)[0] == dpc.DP_ERR_SHAPE
     assert call(ok, ws=None)[0] == dpc.DP_ERR_NULL
-    st, paths = call(ok, wsb=1024)
+    st, paths = call(ok, wsb=16)
     assert st == dpc.DP_ERR_WORKSPACE and paths[:4] == [-7] * 4
     # an explicit layer beyond the per-sample tile limit fails the whole call
     huge = _layers(GPT_BLOCK[:1] + [(1 << 16, 1 << 15, 1 << 15, 0)])
@@ -241,13 +241,18 @@ def test_layers_workspace_follows_the_runs(lib):
     if torch.cuda.is_available():
         pytest.skip("checks the no-device validation path")
     B = 64
-    # four T = 128 layers: one launch, 3 Gram tiles per layer and sample
-    _norm_need_ok(lib, _layers(GPT_BLOCK), 4, 1, B, 0, _r256(B * 12 * 4))
-    # nine layers: runs of 8 and 1
-    _norm_need_ok(lib, _layers([GPT_BLOCK[0]] * 9), 9, 1, B, 0, _r256(B * 24 * 4))
+    # four T = 128 layers on the long-sequence engine: one launch, one 128 x 128
+    # Gram tile per layer and sample
+    _norm_need_ok(lib, _layers(GPT_BLOCK), 4, 1, B, 0, _r256(B * 4 * 4))
+    # T = 128 layers on the 64-row tiled kernel (d not a multiple of 64): 3 tiles
+    # per layer and sample; nine layers: runs of 8 and 1
+    tiled = (128, 136, 256, 0)
+    _norm_need_ok(lib, _layers([tiled] * 9), 9, 1, B, 0, _r256(B * 24 * 4))
     # a T = 1 layer in between splits the run; it needs no workspace
-    mixed = _layers([GPT_BLOCK[0], (1, 64, 32, 0), GPT_BLOCK[1]])
+    mixed = _layers([tiled, (1, 64, 32, 0), (128, 136, 128, 0)])
     _norm_need_ok(lib, mixed, 3, 1, B, 0, _r256(B * 3 * 4))
+    # runs of one single-tile layer each: nothing
+    _norm_need_ok(lib, _layers([GPT_BLOCK[0], (1, 64, 32, 0), GPT_BLOCK[1]]), 3, 1, B, 0, 0)
     # one single-tile ghost layer: nothing
     _norm_need_ok(lib, _layers([(64, 32, 48, 0)]), 1, 0, 5, dpc.MODE_GHOST, 0)
     # two single-tile ghost layers share a launch: two tiles per sample

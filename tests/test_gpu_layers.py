@@ -73,11 +73,14 @@ CASES = {
                     "bf16", [False, True, False, True, False, True], dpc.MODE_MIXED),
     "ten-layers": (11, [(128, 64 + 8 * k, 128) for k in range(10)], "bf16", [k % 2 == 0 for k in range(10)],
                    dpc.MODE_GHOST),
-    "wide-engine-inside": (3, [(128, 128, 128), (512, 128, 192), (128, 64, 128)], "bf16", [False, False, True],
+    "wide-engine-inside": (3, [(128, 96, 128), (512, 128, 192), (64, 64, 128)], "bf16", [False, False, True],
                            dpc.MODE_GHOST),
     # consecutive long-sequence layers share one launch of that engine
     "wide-group": (3, [(512, 128, 192), (576, 64, 128), (1024, 128, 64), (512, 192, 64)], "bf16",
                    [False, True, False, True], dpc.MODE_GHOST),
+    # short and long samples in one launch of that engine (128 x 128 tiles beside 256 x 128)
+    "wide-short-long": (5, [(128, 128, 192), (100, 64, 64), (512, 64, 128), (65, 128, 64)], "bf16",
+                        [True, False, False, True], dpc.MODE_GHOST),
 }
 
 

@@ -651,20 +651,27 @@ def test_concurrent_streams_bitwise():
 
 # ------------------------------------------------------------------ ghost path shapes
 # bf16 ghost norms over 64-row tiles (T <= 384), 128-row tiles (T > 384) and
-# 256 x 128 tiles (T >= 512 with d and p multiples of 64): one tile with most
-# rows past T, ragged T, up to 36 tiles per sample, several short samples
-# stacked in one tile, bias on and off, accumulation into sqnorm.
+# the long-sequence engine's 256 x 128 tiles (T > 64 with d and p multiples
+# of 64; at T <= 128 one 128 x 128 tile per sample): one tile with most rows
+# past T, ragged T, up to 36 tiles per sample, several short samples stacked
+# in one tile, bias on and off, accumulation into sqnorm.
 GHOST_CASES = [
     # B, T, d, p, has_bias
     (3, 5, 128, 256, True),      # 1 tile of 64
-    (4, 100, 256, 128, False),   # 3 tiles, ragged
-    (5, 128, 384, 128, False),   # 3 tiles: the gpt-block T
+    (4, 100, 200, 128, False),   # 3 tiles, ragged
+    (5, 128, 136, 128, True),    # 3 tiles
     (9, 64, 128, 128, True),     # 1 tile
-    (3, 200, 128, 256, True),    # 10 tiles, ragged
-    (2, 300, 256, 128, False),   # 15 tiles, ragged
-    (2, 385, 64, 192, True),     # 128-row tiles: 10, ragged
-    (1, 1000, 128, 64, False),   # 256 x 128 tiles (T >= 512, d and p multiples of 64): 28, ragged
-    (2, 512, 64, 128, True),     # 256 x 128 tiles: 6
+    (3, 200, 136, 256, True),    # 10 tiles, ragged
+    (2, 300, 232, 128, False),   # 15 tiles, ragged
+    (2, 385, 72, 192, True),     # 128-row tiles: 10, ragged
+    (4, 100, 256, 128, False),   # long-sequence engine: one 128 x 128 tile, 28 rows past T
+    (5, 128, 384, 128, False),   # one 128 x 128 tile: the gpt-block T
+    (3, 65, 64, 192, True),      # one tile, one row of its second half
+    (3, 200, 128, 256, True),    # 2 tiles (128 x 128, 256 x 128), ragged
+    (2, 300, 256, 128, False),   # 4 tiles, ragged
+    (2, 385, 64, 192, True),     # 6 tiles, ragged
+    (1, 1000, 128, 64, False),   # 28 tiles, ragged
+    (2, 512, 64, 128, True),     # 6 tiles
     (3, 600, 128, 192, False),   # 9 tiles, last row block 88 rows
     (1, 1100, 192, 64, True),    # 25 tiles, ragged
     (4, 1024, 64, 64, False),    # 20 tiles
