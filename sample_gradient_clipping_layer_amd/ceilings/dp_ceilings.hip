@@ -19,8 +19,19 @@
 //   (its load-to-read byte ratio), not waited on by the reads.
 // - mix_contract: the bf16 contraction's k-step: 6 operand fragments from
 //   12 ds_read_b64_tr_b16 and 8 MFMAs (random data).
+// - mix_contract_pipe: the same with the next k-step's 12 reads issued ahead
+//   of this k-step's MFMAs.
+// - mix_contract_dma: mix_contract plus 2 direct-to-LDS loads per wave and
+//   k-step (the 256 x 256 tile's load-to-read byte ratio), not waited on by
+//   the reads.
+// - hbm_rows / hbm_contiguous: HBM read rate of one workgroup per CU reading
+//   blocks of 128 rows x 1536 bytes (one sample's rows of a 768-feature bf16
+//   layer) of a 1.5 GiB buffer, 256-byte slices of every row at a time (the
+//   Gram kernels' order), or each block as one contiguous run; 8 loads of 16
+//   bytes in flight per thread.
 // Every LDS address is masked into the kernel's 96 KB allocation and every
-// global offset into the 2 MiB source; each thread stores one float.
+// global offset into the 2 MiB source (1.5 GiB for the HBM probes); each
+// thread stores one float.
 //
 // Build: python -m sample_gradient_clipping_layer_amd._build (writes
 // sample_gradient_clipping_layer_amd/dp_ceilings). Run it with no arguments;
@@ -43,8 +54,13 @@ constexpr int kThreads = 512, kBlocks = 1024, kIters = 4096;
 constexpr int kLdsBytes = 98304;           // forces one workgroup per CU
 constexpr uint32_t kReadMask = 65535;      // reads stay in the first 64 KB
 constexpr uint32_t kSrcBytes = 2u << 20;   // global source of the loads
+constexpr int64_t kHbmBytes = 1536ll << 20; // source of the HBM probes: past the 256 MB last-level cache
+constexpr int kRowBytes = 1536, kRows = 128, kSlice = 256, kHbmUnroll = 8;
 
-enum Mode { MFMA_CONST, MFMA_RANDOM, LDS_B128, LDS_TR, DMA_L2, MIX_GRAM, MIX_GRAM_DMA, MIX_CONTRACT, NMODES };
+enum Mode {
+  MFMA_CONST, MFMA_RANDOM, LDS_B128, LDS_TR, DMA_L2, MIX_GRAM, MIX_GRAM_DMA, MIX_CONTRACT, MIX_CONTRACT_PIPE,
+  MIX_CONTRACT_DMA, NMODES
+};
 
 __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
@@ -106,12 +122,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_probe(const unsigned char* __re
     b0[e] = l32[(lane * 4 + 256 + e) & 16383];
   }
   const uint32_t wsrc = (uint32_t)(blockIdx.x * 8 + wave) * 6144u;
+  // MIX_CONTRACT_PIPE: this k-step's operands, read in the previous iteration
+  u32x4 pa[2], pb[4];
+  if constexpr (MODE == MIX_CONTRACT_PIPE) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pa[i] = rdtr(rbase + i * 8192);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pb[i] = rdtr(rbase + 32768 + i * 4096);
+  }
   for (int it = 0; it < kIters; ++it) {
     asm volatile("" : "+v"(rbase));  // a fresh address each iteration: no read is hoisted
-    if constexpr (MODE == DMA_L2 || MODE == MIX_GRAM_DMA) {
+    if constexpr (MODE == DMA_L2 || MODE == MIX_GRAM_DMA || MODE == MIX_CONTRACT_DMA) {
+      constexpr int N = MODE == MIX_CONTRACT_DMA ? 2 : 6;
       const uint32_t g0 = wsrc + (uint32_t)it * 49152u;
 #pragma unroll
-      for (int i = 0; i < 6; ++i) {
+      for (int i = 0; i < N; ++i) {
         const uint32_t goff = ((g0 + i * 1024u) & (kSrcBytes - 1) & ~1023u) + lane * 16;
         const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane(((it & 1) * 49152 + wave * 6144 + i * 1024) &
                                                                      ~1023);
@@ -151,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_probe(const unsigned char* __re
         for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
           for (int bj = 0; bj < 2; ++bj) acc[bi * 2 + bj] = mfma(fa[kk][bi], fb[kk][bj], acc[bi * 2 + bj]);
-    } else if constexpr (MODE == MIX_CONTRACT) {
+    } else if constexpr (MODE == MIX_CONTRACT || MODE == MIX_CONTRACT_DMA) {
       u32x4 fa[2], fb[4];
 #pragma unroll
       for (int i = 0; i < 2; ++i) fa[i] = rdtr(rbase + i * 8192);
@@ -161,8 +186,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_probe(const unsigned char* __re
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[j] = mfma(fa[i], fb[j], acc[j]);
+    } else if constexpr (MODE == MIX_CONTRACT_PIPE) {
+      u32x4 na[2], nb[4];  // the next k-step's operands, in flight during this one's MFMAs
+#pragma unroll
+      for (int i = 0; i < 2; ++i) na[i] = rdtr(rbase + i * 8192);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) nb[i] = rdtr(rbase + 32768 + i * 4096);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma(pa[i], pb[j], acc[j]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) pa[i] = na[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[i] = nb[i];
     }
     if constexpr (MODE == DMA_L2 || MODE == MIX_GRAM_DMA) wait_vm<12>();  // two iterations of loads in flight
+    if constexpr (MODE == MIX_CONTRACT_DMA) wait_vm<4>();
   }
   wait_vm<0>();
   float s = 0.f;
@@ -171,6 +211,60 @@ __global__ __launch_bounds__(kThreads, 1) void k_probe(const unsigned char* __re
 #pragma unroll
     for (int e = 0; e < 16; ++e) s += acc[j][e];
   out[blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
+// HBM read probe: workgroup b reads block b (kRows rows of kRowBytes) either
+// in 256-byte slices of every row at a time (SLICED) or as one run.
+template <bool SLICED>
+__global__ __launch_bounds__(kThreads, 1) void k_rows(const unsigned char* __restrict__ src, int64_t nblk,
+                                                      float* out) {
+  extern __shared__ unsigned char unused_lds[];  // one workgroup per CU
+  const int64_t blk = blockIdx.x;
+  if (blk >= nblk) return;
+  const unsigned char* b = src + blk * (int64_t)kRows * kRowBytes;
+  constexpr int kPieces = kRows * kRowBytes / 16;  // 16-byte pieces of a block
+  constexpr int kPerSlice = kRows * (kSlice / 16);
+  u32x4 x = {0u, 0u, 0u, 0u};
+  for (int base = 0; base < kPieces; base += kThreads * kHbmUnroll) {
+    u32x4 v[kHbmUnroll];
+#pragma unroll
+    for (int u = 0; u < kHbmUnroll; ++u) {
+      const int i = base + u * kThreads + (int)threadIdx.x;  // < kPieces: kPieces % (kThreads * kHbmUnroll) == 0
+      int off = i * 16;
+      if constexpr (SLICED) {
+        const int sl = i / kPerSlice, r = (i % kPerSlice) / (kSlice / 16), pc = i % (kSlice / 16);
+        off = r * kRowBytes + sl * kSlice + pc * 16;
+      }
+      v[u] = *reinterpret_cast<const u32x4*>(b + off);
+    }
+#pragma unroll
+    for (int u = 0; u < kHbmUnroll; ++u) x ^= v[u];
+  }
+  out[blk * kThreads + threadIdx.x] = (float)(x[0] ^ x[1] ^ x[2] ^ x[3]);
+}
+static_assert((kRows * kRowBytes / 16) % (kThreads * kHbmUnroll) == 0 && kRowBytes % kSlice == 0, "whole passes");
+
+template <bool SLICED>
+int time_rows(const unsigned char* src, float* out, double* seconds) {
+  const int64_t nblk = kHbmBytes / ((int64_t)kRows * kRowBytes);
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_rows<SLICED>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kLdsBytes) != hipSuccess)
+    return 1;
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return 1;
+  hipLaunchKernelGGL(k_rows<SLICED>, dim3((unsigned)nblk), dim3(kThreads), kLdsBytes, 0, src, nblk, out);
+  const int reps = 5;
+  hipEventRecord(e0, 0);
+  for (int r = 0; r < reps; ++r)
+    hipLaunchKernelGGL(k_rows<SLICED>, dim3((unsigned)nblk), dim3(kThreads), kLdsBytes, 0, src, nblk, out);
+  hipEventRecord(e1, 0);
+  if (hipEventSynchronize(e1) != hipSuccess) return 1;
+  float ms = 0.f;
+  hipEventElapsedTime(&ms, e0, e1);
+  *seconds = ms * 1e-3 / reps;
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
 template <int MODE>
@@ -198,34 +292,47 @@ int time_mode(const unsigned char* src, float* out, double* seconds) {
 
 int main() {
   unsigned char* src = nullptr;
+  unsigned char* big = nullptr;
   float* out = nullptr;
-  if (hipMalloc(&src, kSrcBytes) != hipSuccess || hipMalloc(&out, (size_t)kBlocks * kThreads * 4) != hipSuccess ||
-      hipMemset(src, 0x3C, kSrcBytes) != hipSuccess) {
+  const int64_t nblk = kHbmBytes / ((int64_t)kRows * kRowBytes);
+  const size_t nout = (size_t)(nblk > kBlocks ? nblk : kBlocks) * kThreads;
+  if (hipMalloc(&src, kSrcBytes) != hipSuccess || hipMalloc(&big, kHbmBytes) != hipSuccess ||
+      hipMalloc(&out, nout * 4) != hipSuccess || hipMemset(src, 0x3C, kSrcBytes) != hipSuccess ||
+      hipMemset(big, 0x3C, kHbmBytes) != hipSuccess) {
     fprintf(stderr, "dp_ceilings: device allocation failed\n");
     return 1;
   }
-  double t[NMODES] = {};
+  double t[NMODES] = {}, t_rows = 0.0, t_run = 0.0;
   int err = time_mode<MFMA_CONST>(src, out, &t[MFMA_CONST]) | time_mode<MFMA_RANDOM>(src, out, &t[MFMA_RANDOM]) |
             time_mode<LDS_B128>(src, out, &t[LDS_B128]) | time_mode<LDS_TR>(src, out, &t[LDS_TR]) |
             time_mode<DMA_L2>(src, out, &t[DMA_L2]) | time_mode<MIX_GRAM>(src, out, &t[MIX_GRAM]) |
-            time_mode<MIX_GRAM_DMA>(src, out, &t[MIX_GRAM_DMA]) | time_mode<MIX_CONTRACT>(src, out, &t[MIX_CONTRACT]);
+            time_mode<MIX_GRAM_DMA>(src, out, &t[MIX_GRAM_DMA]) | time_mode<MIX_CONTRACT>(src, out, &t[MIX_CONTRACT]) |
+            time_mode<MIX_CONTRACT_PIPE>(src, out, &t[MIX_CONTRACT_PIPE]) |
+            time_mode<MIX_CONTRACT_DMA>(src, out, &t[MIX_CONTRACT_DMA]) | time_rows<true>(big, out, &t_rows) |
+            time_rows<false>(big, out, &t_run);
   if (err || hipDeviceSynchronize() != hipSuccess) {
     fprintf(stderr, "dp_ceilings: a probe failed\n");
     return 1;
   }
   const double waves = (double)kBlocks * kThreads / 64, cu_clk = 256 * 2.4e9, peak = 2.5e15;
   const double fl16 = waves * kIters * 16 * 32768.0, fl8 = waves * kIters * 8 * 32768.0;
+  const double hbm = (double)nblk * kRows * kRowBytes;
   auto tf = [](double fl, double s) { return fl / s / 1e12; };
   printf("{\"probe\": \"dp_ceilings\", \"waves_per_cu\": 8, \"nominal_clock_ghz\": 2.4, \"bf16_peak_tflops\": 2500, "
          "\"mfma_const_tflops\": %.0f, \"mfma_random_tflops\": %.0f, \"mfma_random_frac\": %.3f, "
          "\"lds_b128_bytes_per_clk_cu\": %.1f, \"lds_tr_b16_bytes_per_clk_cu\": %.1f, \"dma_l2_bytes_per_clk_cu\": %.1f, "
          "\"mix_gram_tflops\": %.0f, \"mix_gram_dma_tflops\": %.0f, \"mix_contract_tflops\": %.0f, "
-         "\"mix_contract_frac\": %.3f}\n",
+         "\"mix_contract_frac\": %.3f, \"mix_contract_pipe_tflops\": %.0f, \"mix_contract_pipe_frac\": %.3f, "
+         "\"mix_contract_dma_tflops\": %.0f, \"mix_contract_dma_frac\": %.3f, \"hbm_rows_256B_tbs\": %.2f, "
+         "\"hbm_contiguous_tbs\": %.2f}\n",
          tf(fl16, t[MFMA_CONST]), tf(fl16, t[MFMA_RANDOM]), tf(fl16, t[MFMA_RANDOM]) * 1e12 / peak,
          waves * kIters * 16 * 1024 / t[LDS_B128] / cu_clk, waves * kIters * 16 * 512 / t[LDS_TR] / cu_clk,
          waves * kIters * 6144 / t[DMA_L2] / cu_clk, tf(fl16, t[MIX_GRAM]), tf(fl16, t[MIX_GRAM_DMA]),
-         tf(fl8, t[MIX_CONTRACT]), tf(fl8, t[MIX_CONTRACT]) * 1e12 / peak);
+         tf(fl8, t[MIX_CONTRACT]), tf(fl8, t[MIX_CONTRACT]) * 1e12 / peak, tf(fl8, t[MIX_CONTRACT_PIPE]),
+         tf(fl8, t[MIX_CONTRACT_PIPE]) * 1e12 / peak, tf(fl8, t[MIX_CONTRACT_DMA]),
+         tf(fl8, t[MIX_CONTRACT_DMA]) * 1e12 / peak, hbm / t_rows / 1e12, hbm / t_run / 1e12);
   hipFree(src);
+  hipFree(big);
   hipFree(out);
   return 0;
 }
