@@ -127,11 +127,12 @@ typedef struct dp_layer {
  * The result is bitwise the one of dp_ghost_norm called on layers[0],
  * layers[1], ... in that order (one stream, one workspace), the first call
  * with `accumulate` and the others with accumulate = 1. Runs of up to 8
- * consecutive layers that take the tiled ghost kernel with one tile size
- * share a launch, whose Gram tiles fill the GPU together (a small layer
- * alone leaves most compute units idle); the launch's finish kernel adds each
- * sample's tile partials and then the layers in order. Other layers (closed form, explicit, the
- * long-sequence bf16 ghost engine) run one launch each.
+ * consecutive layers that take the same ghost kernel (the tiled kernel with
+ * one tile size, or the direct-to-LDS bf16 engine: T > 64, d and p multiples
+ * of 64) share a launch, whose Gram tiles fill the GPU together (a small
+ * layer alone leaves most compute units idle); the launch's finish kernel
+ * adds each sample's tile partials and then the layers in order. Other
+ * layers (closed form, explicit) run one launch each.
  *
  *  layers, n_layers  host array, 1 <= n_layers <= 4096; each layer as in
  *           dp_ghost_norm (A, G non-NULL and 16-byte aligned, shape limits),
