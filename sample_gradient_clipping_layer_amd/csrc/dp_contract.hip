@@ -27,7 +27,9 @@
 //   tiles keep one set and rescale it by c_prev / c_i at each sample (one
 //   more fp32 rounding per sample; see RATIO below).
 // - STAGES LDS buffers: loads for chunk q+STAGES-1 are in flight while chunk q
-//   is computed; one barrier per chunk.
+//   is computed; one barrier per chunk. The 256x256 tile (two k-steps per
+//   chunk) reads the next chunk's first k-step right after that chunk's
+//   barrier, while this chunk's second k-step runs on the matrix cores.
 // - One launch takes up to kDlGroupMax layers (one tile shape, a K split per
 //   layer). Each XCD (blockIdx % 8) owns a contiguous range of every layer's
 //   (split, tile) work items, ordered with the shorter tile dimension fastest,
@@ -369,6 +371,23 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const float* __restr
     }
   };
 
+  // RATIO: one k-step's operands of the chunk in stage base sbase, and its MFMAs
+  struct Frags {
+    u32x4 a[C::NBM], g[C::NBN];
+  };
+  auto read_kstep = [&](uint32_t sbase, int k, Frags& f) {
+#pragma unroll
+    for (int bi = 0; bi < C::NBM; ++bi) f.a[bi] = frag_tr(sbase + rdA[bi], k * 16 * C::RA, 4 * C::RA);
+#pragma unroll
+    for (int bj = 0; bj < C::NBN; ++bj) f.g[bj] = frag_tr(sbase + rdG[bj], k * 16 * C::RG, 4 * C::RG);
+  };
+  auto mfma_kstep = [&](const Frags& f) {
+#pragma unroll
+    for (int bi = 0; bi < C::NBM; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < C::NBN; ++bj) acc[bi][bj] = mfma32_bf16(f.a[bi], f.g[bj], acc[bi][bj]);
+  };
+
   // ---- pipeline: chunk q in stage q % STAGES; loads for chunk it+STAGES-1
   // go out once every wave is past chunk it-1 (the barrier), while chunk it
   // is computed.
@@ -382,8 +401,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const float* __restr
   // elements inside [0, d) x [0, p) (flushes and the epilogue; the offsets past the lane's
   // base are compile-time constants times p).
   auto for_tile_elems = [&](auto f) {
+    // an opaque copy of the row stride: the element addresses are formed where
+    // they are used instead of being computed ahead of the (rare) flushes and
+    // held in registers through the whole K loop
+    int64_t ps = L.p;
+    asm volatile("" : "+s"(ps));
     const int64_t lrow = m0 + wm * C::WM + 4 * (lane >> 5), lcol = n0 + wn * C::WN + (lane & 31);
-    float* const base = L.ws + split * L.d * L.p + lrow * L.p + lcol;
+    float* const base = L.ws + split * L.d * ps + lrow * ps + lcol;
     const int64_t rem_r = L.d - lrow, rem_c = L.p - lcol;
 #pragma unroll
     for (int bi = 0; bi < C::NBM; ++bi)
@@ -392,21 +416,31 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const float* __restr
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int ro = bi * 32 + 8 * (j >> 2) + (j & 3), co = bj * 32;
-          if (ro < rem_r && co < rem_c) f(acc[bi][bj][j], base + ro * L.p + co);
+          if (ro < rem_r && co < rem_c) f(acc[bi][bj][j], base + ro * ps + co);
         }
   };
 #pragma unroll
   for (int c = 0; c < STAGES - 1; ++c)
     if (c < nq) issue(q0 + c, c);
-  for (int it = 0; it < nq; ++it) {
-    // chunks it+1 .. it+STAGES-2 (those issued) may still be in flight
-    const int later = nq - 1 - it < STAGES - 2 ? nq - 1 - it : STAGES - 2;
-    wait_chunks<C::LPC, STAGES - 2>(later);
-    lds_barrier();  // chunk it landed for every wave; every wave is done with chunk it-1
-    if (it + STAGES - 1 < nq) issue(q0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
-
-    const uint32_t sb = lds_addr(lds) + (uint32_t)((it % STAGES) * C::STAGE);
-    if constexpr (RATIO) {
+  if constexpr (RATIO) {
+    // Two k-steps per chunk, software-pipelined across chunks: chunk it+1's
+    // first k-step is read right after the barrier that makes it visible,
+    // while chunk it's second k-step runs on the matrix cores. The barrier
+    // for chunk it+1 also finds every wave done reading chunk it, whose stage
+    // then takes the loads of chunk it+STAGES.
+    static_assert(C::KC == 32, "two k-steps per chunk");
+    auto stage_of = [&](int it) { return lds_addr(lds) + (uint32_t)((it % STAGES) * C::STAGE); };
+    auto arrive = [&](int it) {  // chunk it landed for every wave; issue chunk it + STAGES - 1
+      const int later = nq - 1 - it < STAGES - 2 ? nq - 1 - it : STAGES - 2;
+      wait_chunks<C::LPC, STAGES - 2>(later);
+      lds_barrier();
+      if (it + STAGES - 1 < nq) issue(q0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
+    };
+    // The last chunk is peeled off the loop, so that every path into the
+    // second k-step's MFMAs passes the barrier, which waits for this wave's
+    // reads: the compiler's wait insertion then tracks only the next chunk's
+    // first-k-step reads as pending there, and the MFMAs do not wait for them.
+    auto begin_chunk = [&](int it) {  // the chunk's clip factor: rescale (or flush) at a sample's start
       if (it == 0 || in_sample == 0) {
         cur = c[sample];
         if (cur != 0.0f) {  // a NaN factor is not 0: it propagates
@@ -438,18 +472,49 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const float* __restr
           have_prev = true;
         }
       }
-      if (cur != 0.0f) compute(sb, std::false_type{});
+    };
+    auto end_chunk = [&]() {
       if (++in_sample == L.cps) {
         in_sample = 0;
         ++sample;
       }
-      continue;
-    } else {
-      if (it == 0 || in_sample == 0)
-        compute(sb, std::true_type{});
-      else
-        compute(sb, std::false_type{});
+    };
+    Frags f0, f1;
+    if (nq > 0) {
+      arrive(0);
+      read_kstep(stage_of(0), 0, f0);
     }
+    for (int it = 0; it + 1 < nq; ++it) {
+      begin_chunk(it);
+      read_kstep(stage_of(it), 1, f1);
+      if (cur != 0.0f) mfma_kstep(f0);
+      arrive(it + 1);  // also: this wave's reads of chunk it are done (lgkmcnt)
+      read_kstep(stage_of(it + 1), 0, f0);
+      if (cur != 0.0f) mfma_kstep(f1);
+      end_chunk();
+    }
+    if (nq > 0) {
+      begin_chunk(nq - 1);
+      read_kstep(stage_of(nq - 1), 1, f1);
+      if (cur != 0.0f) {
+        mfma_kstep(f0);
+        mfma_kstep(f1);
+      }
+      end_chunk();
+    }
+  } else
+  for (int it = 0; it < nq; ++it) {
+    // chunks it+1 .. it+STAGES-2 (those issued) may still be in flight
+    const int later = nq - 1 - it < STAGES - 2 ? nq - 1 - it : STAGES - 2;
+    wait_chunks<C::LPC, STAGES - 2>(later);
+    lds_barrier();  // chunk it landed for every wave; every wave is done with chunk it-1
+    if (it + STAGES - 1 < nq) issue(q0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
+
+    const uint32_t sb = lds_addr(lds) + (uint32_t)((it % STAGES) * C::STAGE);
+    if (it == 0 || in_sample == 0)
+      compute(sb, std::true_type{});
+    else
+      compute(sb, std::false_type{});
     if (++in_sample == L.cps || it + 1 == nq) {
       const float ci = c[sample];
 #pragma unroll
