@@ -39,6 +39,8 @@
 //   (its chunks are a third the size); one barrier per chunk; each tile
 //   stores its part and the finish kernel sums a sample's parts in tile
 //   order (NormSink).
+// - Operand reads run half a chunk (two k-steps) ahead of the MFMAs, across
+//   the barrier into the next chunk.
 // - Work items are XCD-grouped by sample: the tiles of one sample run on one
 //   XCD and share its rows in that XCD's L2.
 #include "dp_common.hpp"
@@ -165,24 +167,28 @@ __device__ __forceinline__ float gw_item(const bf16s* __restrict__ Ai, const bf1
         accG[bi][bj][e] = 0.f;
       }
 
-  // all operand reads of a chunk are issued before its MFMAs
-  auto compute = [&](uint32_t sb, f32x16 (&acc)[2][2]) {
-    u32x4 fa[gw::KC / 16][2], fb[gw::KC / 16][2];
+  // The operands of half a chunk (k-steps 2 hh and 2 hh + 1), and its MFMAs.
+  struct Half {
+    u32x4 a[2][2], b[2][2];
+  };
+  auto read_half = [&](uint32_t sb, int hh, Half& F) {
 #pragma unroll
-    for (int kk = 0; kk < gw::KC / 16; ++kk)
+    for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        fa[kk][b] = *(const lds_u32x4*)(uintptr_t)(sb + rd[kk] + (ra0 + 32 * b) * gw::ROWB);
-        fb[kk][b] = *(const lds_u32x4*)(uintptr_t)(sb + rd[kk] + (rg0 + 32 * b) * gw::ROWB);
+        F.a[k2][b] = *(const lds_u32x4*)(uintptr_t)(sb + rd[2 * hh + k2] + (ra0 + 32 * b) * gw::ROWB);
+        F.b[k2][b] = *(const lds_u32x4*)(uintptr_t)(sb + rd[2 * hh + k2] + (rg0 + 32 * b) * gw::ROWB);
       }
-    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+  };
+  auto mfma_half = [&](const Half& F, f32x16 (&acc)[2][2]) {
 #pragma unroll
-    for (int kk = 0; kk < gw::KC / 16; ++kk)
+    for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mfma32_bf16(fa[kk][bi], fb[kk][bj], acc[bi][bj]);
+        for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = mfma32_bf16(F.a[k2][bi], F.b[k2][bj], acc[bi][bj]);
   };
+  static_assert(gw::KC == 64, "two halves of two k-steps per chunk");
 
   // ---- pipeline: chunk q in stage q % S; loads for chunk q+S-1 go out once
   // every wave is past chunk q-1 (the barrier), while chunk q is computed.
@@ -204,8 +210,28 @@ __device__ __forceinline__ float gw_item(const bf16s* __restrict__ Ai, const bf1
     for (int64_t q = 0; q < n; ++q) (void)step(q);
     return 0.0f;
   }
-  for (int64_t q = 0; q < nA; ++q) compute(step(q), accA);
-  for (int64_t q = nA; q < n; ++q) compute(step(q), accG);
+  // Software-pipelined by half chunks: the second half of chunk q is read
+  // while the first half's MFMAs run, and the first half of chunk q+1 right
+  // after the barrier that makes it visible, while the second half's MFMAs
+  // run. n >= 2 (d, p >= 64); the last chunk (of G) is peeled off the loops,
+  // so that every path into a half's MFMAs passes the barrier, which waits
+  // for this wave's earlier reads, and the compiler's wait insertion does not
+  // make them wait for the reads just issued.
+  uint32_t sb = step(0);
+  Half h0, h1;
+  read_half(sb, 0, h0);
+  auto body = [&](int64_t q, f32x16 (&acc)[2][2]) {  // chunk q < n - 1
+    read_half(sb, 1, h1);
+    mfma_half(h0, acc);
+    sb = step(q + 1);
+    read_half(sb, 0, h0);
+    mfma_half(h1, acc);
+  };
+  for (int64_t q = 0; q < nA; ++q) body(q, accA);
+  for (int64_t q = nA; q < n - 1; ++q) body(q, accG);
+  read_half(sb, 1, h1);
+  mfma_half(h0, accG);
+  mfma_half(h1, accG);
 
   // ---- epilogue: weighted Frobenius product of the tile
   const float one = a.has_bias ? 1.0f : 0.0f;
