@@ -11,11 +11,9 @@
  *    enqueued asynchronously on it; nothing is synchronised. The caller keeps
  *    every buffer alive until the stream has passed the call.
  *  - The caller owns every buffer, including the workspace. The library keeps
- *    no pointer after returning. Its global state is an atomic call counter
- *    that tags the arrival counters a multi-layer clipped-sum call keeps in
- *    its workspace, and the fixed scratch array of
- *    dp_ghost_norm_clip_layers_noalloc (with its per-device address); calls
- *    are re-entrant. A workspace serves one call at a time: calls that
+ *    no pointer after returning. Its only global state is the fixed scratch
+ *    array of dp_ghost_norm_clip_layers_noalloc (with its per-device
+ *    address); calls are re-entrant. A workspace serves one call at a time: calls that
  *    may run concurrently (different streams) need distinct workspaces.
  *    Identical inputs give bitwise-identical outputs (fixed-order reductions,
  *    no floating-point atomics).
@@ -23,10 +21,8 @@
  *    returns its code and touches nothing. HIP launch failures return
  *    DP_ERR_HIP; no usable device returns DP_ERR_NO_DEVICE.
  *  - Calls may be captured into a HIP graph and replayed: they enqueue kernel
- *    launches only (no memset, copy or allocation), and each arrival counter
- *    (multi-layer clipped sums) is returned to zero arrivals by the last
- *    arrival of its launch, so a replay with the captured tag counts from
- *    zero again. Buffers captured by
+ *    launches only (no memset, copy or allocation), and a call's kernels read
+ *    from the workspace only what the same call wrote there before. Buffers captured by
  *    pointer keep their addresses across replays, as graphs require.
  *
  * Page keys used in the comments:
@@ -250,8 +246,9 @@ dp_status dp_clipped_sum_noise(void* stream, const void* A, const void* G, dp_dt
  * Layers that the bf16 direct-to-LDS engine takes (bf16, no bias, T a
  * multiple of 64, d and p multiples of 8) share kernel launches of up to 8
  * layers: one tile shape and a K split per layer chosen for the set, so that
- * the work items of all of them fill the GPU together; a split output tile
- * is finished by the last of its splits inside the same launch. Other layers
+ * the work items of all of them fill the GPU together; the partial tiles of
+ * split layers are added by a reduce kernel per layer after the launch, in
+ * split order, with the noise and the mean. Other layers
  * run one dp_clipped_sum_noise-like launch each. Results are deterministic
  * for a given set of layer shapes; the K split of a layer may differ from the
  * one a single-layer call picks, which changes the fp32 rounding of the sum

@@ -262,7 +262,7 @@ dpk::DlGroupPlan group_plan_of(const SumLaunch& g, const dp_layer* layers, int64
     dv[k] = x.d;
     pv[k] = x.p;
   }
-  return dpk::dl_group_plan(Bv, Tv, dv, pv, g.count, g.count > 1);
+  return dpk::dl_group_plan(Bv, Tv, dv, pv, g.count);
 }
 
 size_t sum_launch_ws_bytes(const SumLaunch& g, const dp_layer* layers, dp_dtype dtype, int64_t B) {
@@ -624,7 +624,11 @@ dp_status dp_clipped_sum_noise_layers(void* stream, const dp_layer* layers, int3
         ll[k] = dpk::DlLaunchLayer{x.A, x.G, B, x.T, x.d, x.p, wsl, outs[l],
                                    dpk::make_noise_args(sc, denom, seed, lid(l), step)};
       }
-      e = dpk::launch_contract_dl_group(st, ll, g.count, c, pl, dpk::next_epoch());
+      e = dpk::launch_contract_dl_group(st, ll, g.count, c, pl);
+      // the split tiles' partials (and the 256x256 tiles') -> outputs
+      for (int k = 0; e == hipSuccess && k < g.count; ++k)
+        if (pl.ks[k] > 1 || pl.bn == 256)
+          e = dpk::launch_split_reduce(st, pl.ks[k], ll[k].ws, ll[k].d, ll[k].p, ll[k].na, ll[k].out);
     } else {
       const int l = g.first[0];
       const dp_layer& x = layers[l];

@@ -315,29 +315,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Arrival counter of a group of `total` workgroups: bits 63..16 hold the
-// call's epoch, bits 15..0 the arrivals of that call. A value left by an
-// earlier call (another epoch) counts as zero, so the counters need no
-// clearing between calls. Returns true for the last arrival, which also puts
-// the counter back to zero arrivals of this epoch: every arrival of the launch
-// has been counted by then, so a later launch with the same epoch (a replay of
-// a captured HIP graph, where the kernel arguments are fixed) starts from zero
-// as well. The CAS loop retries only when another workgroup's update
-// succeeded. Callers order their data with a release fence before the
-// arrival and an acquire fence after the last one.
-__device__ __forceinline__ bool arrive_last(unsigned long long* ctr, uint64_t epoch, uint32_t total) {
-  unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (;;) {
-    const unsigned long long nv = ((old >> 16) == epoch) ? old + 1ull : ((epoch << 16) | 1ull);
-    if (__hip_atomic_compare_exchange_strong(ctr, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT)) {
-      const bool last = (uint32_t)(nv & 0xFFFFull) == total;
-      if (last) __hip_atomic_store(ctr, epoch << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return last;
-    }
-  }
-}
-
 // Correctly rounded fp32 square root (through the double-precision one).
 __device__ __forceinline__ float sqrt_rn_f32(float x) { return (float)__dsqrt_rn((double)x); }
 

@@ -35,9 +35,9 @@
 //   (split, tile) work items, ordered with the shorter tile dimension fastest,
 //   so concurrently running workgroups of one XCD share operand tiles in its
 //   L2.
-// - A split output tile is finished either by the reduce kernel (single-layer
-//   launches) or, in multi-layer launches, by its last split inside the kernel
-//   (dl_fixup).
+// - A split output tile (or any 256x256 tile) leaves its partial in the
+//   workspace; the reduce kernel adds the partials in split order and applies
+//   the noise and the mean.
 #include "dp_common.hpp"
 #include "dp_launch.hpp"
 #include "dp_lds.hpp"
@@ -105,7 +105,6 @@ struct DlLayer {
   const bf16s* A;
   const bf16s* G;
   float* ws;                  // partial tiles [ks][d][p] (when ks > 1 or the tile always writes partials)
-  unsigned long long* ctr;    // [mt * nt] arrival counters of each output tile's K splits
   float* out;
   int64_t d, p;
   int64_t cps;                // chunks per sample (T / KC)
@@ -117,95 +116,11 @@ struct DlLayer {
   int m_fast;                 // work-item order: tile row index fastest
   NoiseArgs na;
 };
-// The layers of one launch, in dispatch order, and the call's tag for the
-// arrival counters of the in-kernel fix-up.
+// The layers of one launch, in dispatch order.
 struct DlGroup {
   DlLayer L[kDlGroupMax];
   int n;
-  int fixup;       // split tiles finished in-kernel; else left in ws for the reduce kernel
-  uint64_t epoch;
 };
-
-// K-split fix-up of output tile `tile` (rows m0.., columns n0..): called by
-// every thread of each split's workgroup after its partial tile went to
-// ws[split] with plain stores. The barrier orders them before thread 0's
-// device-scope release fence (the XCDs' L2 caches are not coherent with each
-// other: the fence writes this L2's dirty lines back) and the arrival count;
-// the last split to arrive takes an acquire fence, then adds the ks partials
-// in split order (0 + P_0 + P_1 + ...), the noise and 1/denom, and writes the
-// output. Which split arrives last does not change the result. Rows are
-// taken in groups of 4 (one Philox block per column), columns in pairs.
-template <int BM, int BN, int NT>
-__device__ __forceinline__ void dl_fixup(const DlLayer& L, uint64_t epoch, int64_t tile, int64_t m0, int64_t n0,
-                                         unsigned* flag) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const bool last = arrive_last(L.ctr + tile, epoch, (uint32_t)L.ks);
-    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    *flag = last ? 1u : 0u;
-  }
-  __syncthreads();
-  if (*flag == 0u) return;
-  const int64_t sstride = L.d * L.p;
-  // Work unit: 4 rows x 2 columns (two Philox blocks). A thread takes UB
-  // units at a time and issues the loads of KU splits of all of them
-  // together: the fix-up runs on one CU at the end of an item, and with the
-  // loads of one unit in flight it waited out a memory latency per unit.
-  constexpr int KU = 2;  // splits per pass
-  constexpr int UB = 4;  // units per pass
-  constexpr int NU = (BM / 4) * (BN / 2);
-#pragma unroll 1
-  for (int u0 = threadIdx.x; u0 < NU; u0 += UB * NT) {
-    int64_t m[UB], n[UB];
-    bool ok[UB];
-    float sx[UB][4], sy[UB][4];
-#pragma unroll
-    for (int b = 0; b < UB; ++b) {
-      const int u = u0 + b * NT;
-      m[b] = m0 + 4 * (u / (BN / 2));
-      n[b] = n0 + 2 * (u % (BN / 2));
-      ok[b] = u < NU && m[b] < L.d && n[b] < L.p;  // d % 8 == 0, p % 8 == 0: all 4 rows and both columns exist
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sx[b][r] = sy[b][r] = 0.f;
-    }
-#pragma unroll 1
-    for (int64_t s0 = 0; s0 < L.ks; s0 += KU) {
-      float2 v[UB][KU][4];
-#pragma unroll
-      for (int b = 0; b < UB; ++b)
-#pragma unroll
-        for (int j = 0; j < KU; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (ok[b] && s0 + j < L.ks)
-              v[b][j][r] = *reinterpret_cast<const float2*>(L.ws + (s0 + j) * sstride + (m[b] + r) * L.p + n[b]);
-#pragma unroll
-      for (int b = 0; b < UB; ++b)
-#pragma unroll
-        for (int j = 0; j < KU; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (ok[b] && s0 + j < L.ks) {  // split order: 0 + P_0 + P_1 + ...
-              sx[b][r] += v[b][j][r].x;
-              sy[b][r] += v[b][j][r].y;
-            }
-    }
-#pragma unroll
-    for (int b = 0; b < UB; ++b) {
-      if (!ok[b]) continue;
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const f32x4 z =
-            normals4((uint32_t)((m[b] >> 2) * L.p + n[b] + cc), 2u * L.na.layer, L.na.step, 0u, L.na.k0, L.na.k1);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          L.out[(m[b] + r) * L.p + n[b] + cc] =
-              noised_mean_spec(cc ? sy[b][r] : sx[b][r], L.na.sc, z[r], L.na.inv_denom);
-      }
-    }
-  }
-}
 
 // RATIO (one accumulator set, for wave tiles too large for two): acc holds
 // the clipped sum so far divided by the current sample's clip factor; at the
@@ -233,7 +148,6 @@ template <int BM, int BN, int STAGES, int NW, int KCK = kDlKC, bool RATIO = fals
 __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const float* __restrict__ c, DlGroup g) {
   using C = DlCfg<BM, BN, STAGES, NW, KCK>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
-  __shared__ unsigned fix_flag;
 
   // ---- layer and work item
   const int64_t xcd = blockIdx.x & 7;
@@ -532,13 +446,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const float* __restr
 
   if constexpr (RATIO) {
     // ---- epilogue: undo the last sample's division, write the partial tile
-    // [m][n] (m < d, n < p) straight from the accumulators, then the fix-up
+    // [m][n] (m < d, n < p) straight from the accumulators (for the reduce)
     const float last = have_prev ? prev : 0.0f;
     for_tile_elems([&](float a, float* dst) {
       const float v = have_prev ? a * last : 0.0f;
       *dst = flushed ? *dst + v : v;
     });
-    if (g.fixup) dl_fixup<BM, BN, C::NT>(L, g.epoch, t, m0, n0, &fix_flag);
     return;
   } else {
   // ---- epilogue: the output tile goes through LDS ([BM][BN + 8] fp32; the
@@ -546,7 +459,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const float* __restr
   // noise and the mean are applied here: each thread takes whole Philox
   // blocks (4 rows of one column), consecutive threads on consecutive
   // columns. Otherwise the partial tile goes to ws[split] (16-byte pieces
-  // of consecutive columns) and the fix-up follows.
+  // of consecutive columns) for the reduce kernel.
   constexpr int TP = BN + 8;
   static_assert(BM * TP * 4 <= C::LDS, "epilogue tile fits the stages");
   float* tile = reinterpret_cast<float*>(lds);
@@ -582,7 +495,6 @@ __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const float* __restr
     // p % 8 == 0 and n % 4 == 0: the four columns are all in range and 16-byte aligned
     *reinterpret_cast<float4*>(wsp + m * L.p + n) = *reinterpret_cast<const float4*>(tile + row * TP + 4 * c4);
   }
-  if (g.fixup) dl_fixup<BM, BN, C::NT>(L, g.epoch, t, m0, n0, &fix_flag);
   }
 }
 
@@ -601,10 +513,6 @@ constexpr int kDlWideKC = 32, kDlWideStages = 4;
 #ifndef DL_TILE_MASK
 #define DL_TILE_MASK 7
 #endif
-// bytes per second one CU reads back split partials at in the fix-up
-#ifndef DL_FIXUP_BW
-#define DL_FIXUP_BW 1.0e11
-#endif
 
 namespace {
 constexpr int kTiles = 3;
@@ -612,14 +520,12 @@ const int kTileBM[kTiles] = {128, 256, 256}, kTileBN[kTiles] = {128, 128, 256};
 const int kTileKC[kTiles] = {kDlKC, kDlKC, kDlWideKC};
 // Cost model fitted to MI355X measurements of this engine: a work item runs
 // its chunks at a sustained fraction of the bf16 MFMA peak of one CU, plus a
-// fixed cost (pipeline fill, epilogue); one workgroup per CU (LDS). A split
-// tile's partials are written by every split and read back by the last one
-// (the fix-up) at the bandwidth one CU achieves.
+// fixed cost (pipeline fill, epilogue); one workgroup per CU (LDS). Split
+// tiles cost the reduce kernel that follows the launch: it reads every
+// partial and writes the output.
 const double kTileEff[kTiles] = {0.30, 0.35, 0.47};
 const double kTileFixed[kTiles] = {6e-6, 8e-6, 13.5e-6};
 constexpr double kCuPeak = 2.5e15 / 256.0;
-constexpr double kFixupBytesPerS = DL_FIXUP_BW;
-constexpr double kFixupFixed = 1.0e-6;
 constexpr int kCusPerXcd = 32;
 
 struct LayerChoice {
@@ -629,8 +535,7 @@ struct LayerChoice {
 
 // Split of one layer into items of about `target` chunks; false when the
 // tile cannot take it.
-bool choose_split(int ti, int64_t B, int64_t Tn, int64_t d, int64_t p, int64_t target, bool fixup,
-                  LayerChoice* o) {
+bool choose_split(int ti, int64_t B, int64_t Tn, int64_t d, int64_t p, int64_t target, LayerChoice* o) {
   const int kc = kTileKC[ti];
   if (Tn % kc != 0) return false;
   const int64_t nchunks = B * Tn / kc;
@@ -647,11 +552,9 @@ bool choose_split(int ti, int64_t B, int64_t Tn, int64_t d, int64_t p, int64_t t
   o->per = (o->mt * o->nt * ks + 7) / 8;
   const double chunk_s = 2.0 * kTileBM[ti] * kTileBN[ti] * kc / (kCuPeak * kTileEff[ti]);
   const bool partials = ks > 1 || kTileBN[ti] == 256;
-  const double fix_s =
-      partials && fixup ? (double)ks * kTileBM[ti] * kTileBN[ti] * 4.0 / kFixupBytesPerS + kFixupFixed : 0.0;
-  o->item_s = (double)cps * chunk_s + kTileFixed[ti] + fix_s / (double)ks;  // the fix-up, spread over the splits
-  // without the fix-up: the reduce kernel writes the output after reading every partial
-  o->reduce_s = partials && !fixup ? (2.0 * ks + 1.0) * (double)d * (double)p * 4.0 / 8.0e12 + 4.0e-6 : 0.0;
+  o->item_s = (double)cps * chunk_s + kTileFixed[ti];
+  // the reduce kernel writes the output after reading every partial
+  o->reduce_s = partials ? (2.0 * ks + 1.0) * (double)d * (double)p * 4.0 / 8.0e12 + 4.0e-6 : 0.0;
   return true;
 }
 
@@ -680,8 +583,7 @@ double xcd_makespan(const LayerChoice* ch, const int* order, int n) {
 // Tile (shared by the launch) and per-layer K splits: over the three tiles
 // and a range of target item lengths, the smallest simulated makespan.
 // Layers go in dispatch order by decreasing item time.
-DlGroupPlan dl_group_plan(const int64_t* B, const int64_t* Tn, const int64_t* d, const int64_t* p, int n,
-                          bool fixup) {
+DlGroupPlan dl_group_plan(const int64_t* B, const int64_t* Tn, const int64_t* d, const int64_t* p, int n) {
   static const int64_t targets[] = {4, 6, 8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256, 384, 512, 768, 1024,
                                     1536, 2048, 4096, 8192, 1ll << 40};
   DlGroupPlan best{};
@@ -693,7 +595,7 @@ DlGroupPlan dl_group_plan(const int64_t* B, const int64_t* Tn, const int64_t* d,
     for (int64_t target : targets) {
       LayerChoice ch[kDlGroupMax];
       bool ok = true;
-      for (int l = 0; l < n && ok; ++l) ok = choose_split(ti, B[l], Tn[l], d[l], p[l], target, fixup, &ch[l]);
+      for (int l = 0; l < n && ok; ++l) ok = choose_split(ti, B[l], Tn[l], d[l], p[l], target, &ch[l]);
       if (!ok) continue;
       bool same = true;  // the splits of the previous target: nothing new
       for (int l = 0; l < n; ++l) {
@@ -718,7 +620,6 @@ DlGroupPlan dl_group_plan(const int64_t* B, const int64_t* Tn, const int64_t* d,
         best.bn = kTileBN[ti];
         best.kc = kTileKC[ti];
         best.seconds = t;
-        best.fixup = fixup ? 1 : 0;
         for (int l = 0; l < n; ++l) {
           best.ks[l] = ch[l].ks;
           best.cps[l] = ch[l].cps;
@@ -732,11 +633,8 @@ DlGroupPlan dl_group_plan(const int64_t* B, const int64_t* Tn, const int64_t* d,
   return best;
 }
 
-// One layer alone fills the GPU with a single round of items at best: the
-// last split of a tile would finish it alone at the end, so its partials go
-// to the reduce kernel instead.
 ContractPlan dl_plan(int64_t B, int64_t Tn, int64_t d, int64_t p) {
-  const DlGroupPlan g = dl_group_plan(&B, &Tn, &d, &p, 1, false);
+  const DlGroupPlan g = dl_group_plan(&B, &Tn, &d, &p, 1);
   ContractPlan pl{};
   pl.bm = g.bm;
   pl.bn = g.bn;
@@ -760,15 +658,13 @@ DlGroupPlan dl_single_plan(const ContractPlan& pl) {
   g.mt[0] = pl.mt;
   g.nt[0] = pl.nt;
   g.order[0] = 0;
-  g.fixup = 0;
   return g;
 }
 
 size_t dl_layer_ws_bytes(const DlGroupPlan& g, int l, int64_t d, int64_t p) {
   if (g.ks[l] == 1 && g.bn != 256) return 0;
   const size_t part = (size_t)g.ks[l] * (size_t)d * (size_t)p * sizeof(float);
-  const size_t ctr = g.fixup ? (size_t)g.mt[l] * (size_t)g.nt[l] * sizeof(unsigned long long) : 0;
-  return (part + 255) / 256 * 256 + (ctr + 255) / 256 * 256;
+  return (part + 255) / 256 * 256;
 }
 
 // ---------------------------------------------------------------- launch
@@ -786,11 +682,9 @@ static hipError_t launch_dl_t(hipStream_t st, const float* c, const DlGroup& grp
 }
 
 hipError_t launch_contract_dl_group(hipStream_t st, const DlLaunchLayer* layers, int n, const float* c,
-                                    const DlGroupPlan& g, uint64_t epoch) {
+                                    const DlGroupPlan& g) {
   DlGroup grp{};
   grp.n = n;
-  grp.fixup = g.fixup;
-  grp.epoch = epoch;
   int64_t per_sum = 0;
   for (int k = 0; k < n; ++k) {
     const int l = g.order[k];
@@ -811,10 +705,6 @@ hipError_t launch_contract_dl_group(hipStream_t st, const DlLaunchLayer* layers,
     L.m_fast = L.mt <= L.nt ? 1 : 0;
     L.na = x.na;
     L.ws = x.ws;
-    const size_t part = (size_t)L.ks * (size_t)L.d * (size_t)L.p * sizeof(float);
-    L.ctr = x.ws && g.fixup ? reinterpret_cast<unsigned long long*>(reinterpret_cast<unsigned char*>(x.ws) +
-                                                                    (part + 255) / 256 * 256)
-                            : nullptr;
     per_sum += L.per;
   }
   const int64_t wgs = 8 * per_sum;
@@ -829,7 +719,7 @@ hipError_t launch_contract_dl(hipStream_t st, const void* A, const void* G, cons
                               float* out) {
   const DlGroupPlan g = dl_single_plan(pl);
   const DlLaunchLayer x{A, G, B, Tn, d, p, ws, out, na};
-  return launch_contract_dl_group(st, &x, 1, c, g, next_epoch());
+  return launch_contract_dl_group(st, &x, 1, c, g);
 }
 
 }  // namespace dpk

@@ -45,8 +45,8 @@ hipError_t launch_contract_dl(hipStream_t st, const void* A, const void* G, cons
                               float* out);
 // Launches of the direct-to-LDS bf16 engine: up to kDlGroupMax eligible
 // layers in one kernel launch, one tile shape for all of them, K splits per
-// layer. In a multi-layer launch split tiles are finished inside the kernel
-// by their last split; a single-layer launch leaves them to the reduce kernel.
+// layer. Split tiles (and the 256x256 tile's) leave partials in the layer's
+// workspace region for the reduce kernel (launch_split_reduce).
 constexpr int kDlGroupMax = 8;
 struct DlLaunchLayer {
   const void* A;
@@ -63,16 +63,18 @@ struct DlGroupPlan {
   int64_t cps[kDlGroupMax];       // chunks per split
   int mt[kDlGroupMax], nt[kDlGroupMax];
   int order[kDlGroupMax];         // dispatch order (layer indices)
-  int fixup;                      // split tiles finished in-kernel (else by the reduce kernel)
   double seconds;                 // modelled time
 };
-DlGroupPlan dl_group_plan(const int64_t* B, const int64_t* Tn, const int64_t* d, const int64_t* p, int n,
-                          bool fixup);
+DlGroupPlan dl_group_plan(const int64_t* B, const int64_t* Tn, const int64_t* d, const int64_t* p, int n);
 size_t dl_layer_ws_bytes(const DlGroupPlan& g, int l, int64_t d, int64_t p);
 // The one-layer group plan of a single-layer engine-1 plan.
 DlGroupPlan dl_single_plan(const ContractPlan& pl);
 hipError_t launch_contract_dl_group(hipStream_t st, const DlLaunchLayer* layers, int n, const float* c,
-                                    const DlGroupPlan& g, uint64_t epoch);
+                                    const DlGroupPlan& g);
+// The split partials [ks][d][p] a launch left in ws (no bias row) -> out,
+// with the noise and the mean: the reduce kernel of the split contractions.
+hipError_t launch_split_reduce(hipStream_t st, int64_t ks, float* ws, int64_t d, int64_t p, const NoiseArgs& na,
+                               float* out);
 // direct-to-LDS fp32 engine (bias row accumulated on the side, partials [ks][d + bias][p] in ws)
 bool dl32_eligible(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias);
 ContractPlan dl32_plan(int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias);
@@ -119,9 +121,6 @@ hipError_t launch_ghost(hipStream_t st, int dtype, const void* A, const void* G,
                         int64_t p, int has_bias, const NormSink& sink);
 hipError_t launch_explicit(hipStream_t st, int dtype, const void* A, const void* G, int64_t B, int64_t Tn, int64_t d,
                            int64_t p, int has_bias, const NormSink& sink);
-// Tag of one call for the arrival counters of the contraction's in-kernel
-// split fix-up: 48 bits, never 0, distinct per call in the process.
-uint64_t next_epoch();
 // Weighted contraction + noise + 1/denom: one kernel when pl.ks == 1, else
 // partial tiles in ws and a reduce kernel. bias_out != nullptr <=> bias row.
 // Convolution layers given by their folded input (ConvGeo): the unfolded

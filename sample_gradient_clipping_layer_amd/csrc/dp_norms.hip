@@ -12,7 +12,6 @@
 // reproducible.
 #include "dp_common.hpp"
 
-#include <atomic>
 #include "dp_launch.hpp"
 
 namespace dpk {
@@ -634,33 +633,6 @@ hipError_t launch_ghost_conv(hipStream_t st, int dtype, const ConvGeo& geo, cons
   }
   if (ts == 64) return launch_ghost_t<float, 64>(st, &x, 1, B, sink, &geo);
   return launch_ghost_t<float, 128>(st, &x, 1, B, sink, &geo);
-}
-
-static std::atomic<uint64_t> g_epoch{0};
-
-// The call counter through a bijection of 48-bit words (xor-shifts and odd
-// multipliers modulo 2^48), so that epochs differ from call to call but look
-// like no small integer or float pattern: an arrival counter's word of the
-// contraction's split fix-up may hold data a kernel left there (the workspace
-// is shared with partial tiles), and such a word passes for the current epoch
-// only if its top 48 bits match.
-static uint64_t mix48(uint64_t x) {
-  constexpr uint64_t M = (1ull << 48) - 1;
-  x &= M;
-  x ^= x >> 24;
-  x = (x * 0x9E3779B97F4Bull) & M;
-  x ^= x >> 21;
-  x = (x * 0xD6E8FEB86659ull) & M;
-  x ^= x >> 24;
-  return x;
-}
-
-uint64_t next_epoch() {
-  uint64_t e;
-  do {
-    e = mix48(g_epoch.fetch_add(1, std::memory_order_relaxed) + 1);
-  } while (e == 0);
-  return e;
 }
 
 }  // namespace dpk

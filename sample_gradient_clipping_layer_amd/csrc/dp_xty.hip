@@ -1059,6 +1059,13 @@ static hipError_t launch_reduce_noise(hipStream_t st, const ContractPlan& pl, fl
   return hipGetLastError();
 }
 
+hipError_t launch_split_reduce(hipStream_t st, int64_t ks, float* ws, int64_t d, int64_t p, const NoiseArgs& na,
+                               float* out) {
+  ContractPlan pl{};
+  pl.ks = ks;
+  return launch_reduce_noise(st, pl, ws, d, p, 0, na, out, nullptr);
+}
+
 hipError_t launch_clipped_sum_conv(hipStream_t st, int dtype, const ConvGeo& geo, const void* G, const float* c,
                                    int64_t B, int64_t p, const ContractPlan& pl, float* ws, float sc, float denom,
                                    uint64_t seed, uint32_t layer, uint32_t step, float* out, float* bias_out) {

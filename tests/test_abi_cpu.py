@@ -65,7 +65,7 @@ def test_ghost_norm_validation(lib):
     assert _ghost(lib, A=FAKE_MIS)[0] == dpc.DP_ERR_ALIGN
     assert _ghost(lib, mode=4)[0] == dpc.DP_ERR_VALUE
     assert _ghost(lib, kappa=0)[0] == dpc.DP_ERR_VALUE
-    # T = 100 spans 3 Gram tiles per sample: partials + arrival counters in the workspace
+    # T = 100 spans 3 Gram tiles per sample: tile partials in the workspace
     assert _ghost(lib, ws=None, T=100, mode=dpc.MODE_GHOST)[0] == dpc.DP_ERR_NULL
     assert _ghost(lib, wsb=4, T=100, mode=dpc.MODE_GHOST)[0] == dpc.DP_ERR_WORKSPACE
     st, path = _ghost(lib, wsb=4, T=100, mode=dpc.MODE_GHOST)
@@ -449,7 +449,7 @@ def test_conv_validation(lib):
     if no_gpu:
         st, path = _conv(lib, ws=None, mode=dpc.MODE_GHOST)                     # T = 64: 1 tile, no workspace
         assert st == dpc.DP_ERR_NO_DEVICE
-    big = g(3, 32, 32, 3, 1, 1)                                                 # T = 1024: partials + counters
+    big = g(3, 32, 32, 3, 1, 1)                                                 # T = 1024: tile partials
     assert _conv(lib, geo=big, ws=None, mode=dpc.MODE_GHOST)[0] == dpc.DP_ERR_NULL
     st, path = _conv(lib, geo=big, wsb=4, mode=dpc.MODE_GHOST)
     assert st == dpc.DP_ERR_WORKSPACE and path == -7

@@ -114,8 +114,8 @@ def test_conv_clipped_sum(name, dtype):
 
 
 def test_conv_workspace_reuse_and_errors():
-    """Consecutive calls share one workspace (the arrival counters are tagged
-    per call); a short workspace and a mismatched geometry are refused."""
+    """Consecutive calls share one workspace (each call's partials overwrite the
+    last call's); a short workspace and a mismatched geometry are refused."""
     geo, (U, Go), (a, G) = _case("stem-3x3", "f32")  # T = 1024: 36 Gram tiles per sample
     B = U.shape[0]
     need = dpc.dp_conv_workspace_bytes(geo, dpc.DP_F32, B, Go.shape[2], False, dpc.MODE_GHOST)

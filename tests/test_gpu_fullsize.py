@@ -5,9 +5,9 @@ The benchmark's step is two calls: dp_ghost_norm_clip_layers (every layer's
 norm, the cross-layer sum and the clip factors) and
 dp_clipped_sum_noise_layers (every layer's clipped noised mean under one c).
 At gpt-block-t128 the four layers share one ghost launch and one contraction
-launch (256 x 256 tiles with the per-sample rescale, K split with the split
-tiles finished in-kernel); at gpt2large-t1024 eight consecutive layers (two
-decoder blocks) share each launch. The oracle computes each layer's
+launch (256 x 256 tiles with the per-sample rescale, K split, the split
+tiles' partials added by a reduce kernel per layer); at gpt2large-t1024 eight
+consecutive layers (two decoder blocks) share each launch. The oracle computes each layer's
 per-example gradients in fp64 and everything from them ("Scalable and
 Efficient Training of Large CNNs with DP", eq. (2.1) and Sec. 3.2; "Scaling up
 DP Deep Learning with Fast Per-Example Gradient Clipping", clipped mean plus
@@ -141,7 +141,7 @@ def test_wide_tile_extreme_clip_factors():
     out = torch.empty(d, p, dtype=torch.float32, device=dev())
     C, denom = 0.25, float(B)
     dpc.dp_clipped_sum_noise(A, G, f32(c_np), C, 0.0, denom, 5, 0, 0, out)
-    # the multi-layer call with this layer twice shares a launch (in-kernel split fix-up)
+    # the multi-layer call with this layer twice shares a launch (and its plan)
     outs2 = [torch.empty_like(out), torch.empty_like(out)]
     dpc.dp_clipped_sum_noise_layers([(A, G), (A, G)], f32(c_np), C, 0.0, denom, 5, 0, outs2)
     torch.cuda.synchronize()
@@ -158,9 +158,8 @@ def test_graph_capture_replays_match_eager_calls():
     """The benchmark's two calls captured in a HIP graph (torch.cuda.CUDAGraph)
     and replayed three times with new inputs copied in, eager work and
     synchronisations in between: every replay gives the eager calls' bits
-    (norms, clip factors, noised means). The arrival counters of the launches
-    go back to zero arrivals at the end of each launch, so replays with the
-    captured tags count from zero."""
+    (norms, clip factors, noised means): a call's kernels read from the
+    workspace only what the same call wrote there."""
     wl = W.WORKLOADS["gpt-block-t128"]
     B = 16
     specs = [(128, 256, 384), (128, 256, 256), (128, 384, 256)]

@@ -130,8 +130,8 @@ def test_layers_zero_and_nan_samples():
 
 
 def test_layers_repeated_calls_share_a_workspace():
-    """Calls of different layer lists on one workspace (arrival counters of
-    other shapes, partials left in it) give the same results as fresh ones."""
+    """Calls of different layer lists on one workspace (partials of other
+    shapes left in it) give the same results as fresh ones."""
     B = 12
     lists = [CASES["ten-layers"][1][:5], GPT_BLOCK[:2], [(100, 96, 80), (37, 72, 72)]]
     ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev())
@@ -227,7 +227,7 @@ def test_sum_layers_against_oracle_and_single_calls(name):
 
 def test_sum_layers_repeatable_bitwise():
     """Two calls with the same inputs give the same bits, also when the
-    workspace holds another call's partials and counters in between."""
+    workspace holds another call's partials in between."""
     B, specs, _ = SUM_CASES["ten-layers"]
     _, devs = _inputs(B, specs, "bf16", seed=8)
     c_np = np.linspace(0.1, 0.9, B).astype(np.float32)

@@ -395,10 +395,9 @@ def test_dl_engine_noise_bit_exact(B):
 
 
 def test_dl_engine_workspace_reuse():
-    """Split-K tiles are finished by the last-arriving split, found through
-    per-tile counters in the workspace that carry a per-call tag. A workspace
-    full of arbitrary bytes, and one reused by earlier calls, must both give
-    the oracle's sums, bit-identically for identical inputs."""
+    """Split-K tiles leave partials in the workspace for the reduce kernel. A
+    workspace full of arbitrary bytes, and one reused by earlier calls, must
+    both give the oracle's sums, bit-identically for identical inputs."""
     B, T, d, p = 40, 128, 264, 136
     rng = np.random.default_rng(5)
     A = W.f32_to_bf16_bits((rng.standard_normal((B, T, d)) / math.sqrt(d)).astype(np.float32))

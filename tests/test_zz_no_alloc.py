@@ -2,7 +2,7 @@
 allocate) against dp_ghost_norm_clip_layers with a caller's workspace, through
 the C ABI: bitwise equal squared norms, norms and clip factors on two calls
 in a row, the second with a smaller input (fewer samples and layers, so the
-scratch array still holds the first call's partials and counters); a request
+scratch array still holds the first call's partials); a request
 beyond the fixed scratch is refused before any work (a CPU test in
 test_abi_cpu.py)."""
 import ctypes
