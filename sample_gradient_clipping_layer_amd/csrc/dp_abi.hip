@@ -625,10 +625,13 @@ dp_status dp_clipped_sum_noise_layers(void* stream, const dp_layer* layers, int3
                                    dpk::make_noise_args(sc, denom, seed, lid(l), step)};
       }
       e = dpk::launch_contract_dl_group(st, ll, g.count, c, pl);
-      // the split tiles' partials (and the 256x256 tiles') -> outputs
-      for (int k = 0; e == hipSuccess && k < g.count; ++k)
+      // the split tiles' partials (and the 256x256 tiles') -> outputs, one launch for the group
+      dpk::SplitReduceLayer rl[dpk::kDlGroupMax];
+      int nr = 0;
+      for (int k = 0; k < g.count; ++k)
         if (pl.ks[k] > 1 || pl.bn == 256)
-          e = dpk::launch_split_reduce(st, pl.ks[k], ll[k].ws, ll[k].d, ll[k].p, ll[k].na, ll[k].out);
+          rl[nr++] = dpk::SplitReduceLayer{ll[k].ws, pl.ks[k], ll[k].d, ll[k].p, ll[k].na, ll[k].out};
+      if (e == hipSuccess && nr > 0) e = dpk::launch_split_reduce_group(st, rl, nr);
     } else {
       const int l = g.first[0];
       const dp_layer& x = layers[l];

@@ -75,6 +75,17 @@ hipError_t launch_contract_dl_group(hipStream_t st, const DlLaunchLayer* layers,
 // with the noise and the mean: the reduce kernel of the split contractions.
 hipError_t launch_split_reduce(hipStream_t st, int64_t ks, float* ws, int64_t d, int64_t p, const NoiseArgs& na,
                                float* out);
+// One layer's split partials [ks][d][p] (no bias row) and its output.
+struct SplitReduceLayer {
+  const float* ws;
+  int64_t ks, d, p;
+  NoiseArgs na;
+  float* out;
+};
+// The split reduces of up to kDlGroupMax layers, each layer's output the same
+// as launch_split_reduce's: one launch for the layers the vectorised reduce
+// takes, a launch of their own for the others.
+hipError_t launch_split_reduce_group(hipStream_t st, const SplitReduceLayer* layers, int n);
 // direct-to-LDS fp32 engine (bias row accumulated on the side, partials [ks][d + bias][p] in ws)
 bool dl32_eligible(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias);
 ContractPlan dl32_plan(int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias);

@@ -703,66 +703,75 @@ __global__ __launch_bounds__(256) void k_reduce_noise(const float* __restrict__ 
   }
 }
 
-// Same result as k_reduce_noise (splits summed in split order per element)
-// for d % 4 == 0, p % 4 == 0 and 16-byte aligned out: every load is a float4
-// and each thread keeps 4 splits x 4 rows of loads in flight.
+// The 4 x 4 output block (rows 4 q.., columns 4 cq..) of a split reduce: the
+// partials summed in split order per element, then the noise and the mean.
+// Same result as k_reduce_noise for d % 4 == 0, p % 4 == 0 and 16-byte
+// aligned ws and out: every load is a float4 and the thread keeps 4 splits x
+// 4 rows of loads in flight.
+__device__ __forceinline__ void reduce_noise_block4(const float* __restrict__ ws, int64_t ks, int64_t p,
+                                                    int64_t split_stride, int64_t q, int64_t cq, const NoiseArgs& na,
+                                                    float* __restrict__ out) {
+  constexpr int U = 4;
+  const float* base = ws + 4 * q * p + 4 * cq;
+  float4 s[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+  int64_t sp = 0;
+  for (; sp + U <= ks; sp += U) {
+    float4 v[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[u][r] = *reinterpret_cast<const float4*>(base + (sp + u) * split_stride + r * p);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s[r].x += v[u][r].x;
+        s[r].y += v[u][r].y;
+        s[r].z += v[u][r].z;
+        s[r].w += v[u][r].w;
+      }
+  }
+  for (; sp < ks; ++sp) {
+    float4 v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = *reinterpret_cast<const float4*>(base + sp * split_stride + r * p);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s[r].x += v[r].x;
+      s[r].y += v[r].y;
+      s[r].z += v[r].z;
+      s[r].w += v[r].w;
+    }
+  }
+  float o[4][4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t n = 4 * cq + k;
+    const f32x4 z = normals4((uint32_t)(q * p + n), 2u * na.layer, na.step, 0u, na.k0, na.k1);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float sv = k == 0 ? s[r].x : k == 1 ? s[r].y : k == 2 ? s[r].z : s[r].w;
+      o[r][k] = noised_mean_spec(sv, na.sc, z[r], na.inv_denom);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    *reinterpret_cast<float4*>(out + (4 * q + r) * p + 4 * cq) = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
+}
+
+// One thread per 4 x 4 output block (reduce_noise_block4), then one per 4
+// bias columns.
 __global__ __launch_bounds__(256) void k_reduce_noise_vec(const float* __restrict__ ws, int64_t ks, int64_t d,
                                                           int64_t p, int has_bias, NoiseArgs na,
                                                           float* __restrict__ out, float* __restrict__ bias_out) {
-  constexpr int U = 4;
   const int64_t nq = d / 4, nc = p / 4;
   const int64_t nw = nq * nc;
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t split_stride = (d + (has_bias ? 1 : 0)) * p;
   if (t < nw) {
-    const int64_t q = t / nc, cq = t % nc;
-    const float* base = ws + 4 * q * p + 4 * cq;
-    float4 s[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-    int64_t sp = 0;
-    for (; sp + U <= ks; sp += U) {
-      float4 v[U][4];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[u][r] = *reinterpret_cast<const float4*>(base + (sp + u) * split_stride + r * p);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s[r].x += v[u][r].x;
-          s[r].y += v[u][r].y;
-          s[r].z += v[u][r].z;
-          s[r].w += v[u][r].w;
-        }
-    }
-    for (; sp < ks; ++sp) {
-      float4 v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = *reinterpret_cast<const float4*>(base + sp * split_stride + r * p);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[r].x += v[r].x;
-        s[r].y += v[r].y;
-        s[r].z += v[r].z;
-        s[r].w += v[r].w;
-      }
-    }
-    float o[4][4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t n = 4 * cq + k;
-      const f32x4 z = normals4((uint32_t)(q * p + n), 2u * na.layer, na.step, 0u, na.k0, na.k1);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float sv = k == 0 ? s[r].x : k == 1 ? s[r].y : k == 2 ? s[r].z : s[r].w;
-        o[r][k] = noised_mean_spec(sv, na.sc, z[r], na.inv_denom);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      *reinterpret_cast<float4*>(out + (4 * q + r) * p + 4 * cq) = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
+    reduce_noise_block4(ws, ks, p, split_stride, t / nc, t % nc, na, out);
   } else if (has_bias && t < nw + nc) {
     const int64_t cq = t - nw;
     const float* base = ws + d * p + 4 * cq;
@@ -780,6 +789,27 @@ __global__ __launch_bounds__(256) void k_reduce_noise_vec(const float* __restric
     bias_out[4 * cq + 2] = noised_mean_spec(s.z, na.sc, z[2], na.inv_denom);
     bias_out[4 * cq + 3] = noised_mean_spec(s.w, na.sc, z[3], na.inv_denom);
   }
+}
+
+// The split reduces of several layers in one launch: each layer owns a
+// contiguous range of workgroups, one thread per 4 x 4 output block, with the
+// arithmetic of k_reduce_noise_vec (no bias rows).
+struct RedGroup {
+  SplitReduceLayer L[kDlGroupMax];
+  int64_t blk_begin[kDlGroupMax];
+  int n;
+};
+
+__global__ __launch_bounds__(256) void k_reduce_noise_group(RedGroup g) {
+  int k = 0;
+#pragma unroll
+  for (int j = 1; j < kDlGroupMax; ++j)
+    if (j < g.n && (int64_t)blockIdx.x >= g.blk_begin[j]) k = j;
+  const SplitReduceLayer L = g.L[k];
+  const int64_t nc = L.p / 4, nw = (L.d / 4) * nc;
+  const int64_t t = ((int64_t)blockIdx.x - g.blk_begin[k]) * blockDim.x + threadIdx.x;
+  if (t >= nw) return;
+  reduce_noise_block4(L.ws, L.ks, L.p, L.d * L.p, t / nc, t % nc, L.na, L.out);
 }
 
 // Many splits, small output. A workgroup takes a block of 4 weight rows x 16
@@ -1064,6 +1094,32 @@ hipError_t launch_split_reduce(hipStream_t st, int64_t ks, float* ws, int64_t d,
   ContractPlan pl{};
   pl.ks = ks;
   return launch_reduce_noise(st, pl, ws, d, p, 0, na, out, nullptr);
+}
+
+hipError_t launch_split_reduce_group(hipStream_t st, const SplitReduceLayer* layers, int n) {
+  if (n < 0 || n > kDlGroupMax) return hipErrorInvalidValue;
+  RedGroup g{};
+  int64_t blocks = 0;
+  for (int l = 0; l < n; ++l) {
+    const SplitReduceLayer& x = layers[l];
+    const int64_t blocks_l = ((x.d / 4) * (x.p / 4) + 255) / 256;
+    // layers the one-layer launch would not give to the vectorised kernel keep that launch
+    const bool vec = x.d % 4 == 0 && x.p % 4 == 0 && (reinterpret_cast<uintptr_t>(x.out) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(x.ws) & 15) == 0 && !(x.ks >= 64 && (x.d / 4) * (x.p / 4) < 32768);
+    if (!vec || blocks_l == 0) {
+      const hipError_t e = launch_split_reduce(st, x.ks, const_cast<float*>(x.ws), x.d, x.p, x.na, x.out);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    g.L[g.n] = x;
+    g.blk_begin[g.n] = blocks;
+    blocks += blocks_l;
+    ++g.n;
+  }
+  if (g.n == 0) return hipSuccess;
+  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_reduce_noise_group, dim3((unsigned)blocks), dim3(256), 0, st, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_clipped_sum_conv(hipStream_t st, int dtype, const ConvGeo& geo, const void* G, const float* c,
