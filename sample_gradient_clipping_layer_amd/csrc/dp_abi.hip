@@ -558,10 +558,14 @@ dp_status dp_ghost_norm_clip_layers_noalloc(void* stream, const dp_layer* layers
                           accumulate, paths_out, &clip, runs);
 }
 
-dp_status dp_clipped_sum_noise_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype,
-                                      int64_t B, const float* c, float C, float sigma, float denom, uint64_t seed,
-                                      const uint32_t* layer_ids, uint32_t step, void* workspace, size_t ws_bytes,
-                                      float* const* outs, float* const* bias_outs) {
+// The multi-layer clipped sums. With accs, a layer whose split partials go
+// through the grouped reduce has them added to accs[l] there (acc = acc + S,
+// no noise, outs[l] untouched) and acc_done[l] is set; the caller adds the
+// other layers' outs[l].
+static dp_status sum_layers_impl(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype, int64_t B,
+                                 const float* c, float C, float sigma, float denom, uint64_t seed,
+                                 const uint32_t* layer_ids, uint32_t step, void* workspace, size_t ws_bytes,
+                                 float* const* outs, float* const* bias_outs, float* const* accs, char* acc_done) {
   dp_status s = check_layer_list(layers, n_layers, dtype, B);
   if (s != DP_OK) return s;
   if (!c || !outs) return DP_ERR_NULL;
@@ -629,8 +633,11 @@ dp_status dp_clipped_sum_noise_layers(void* stream, const dp_layer* layers, int3
       dpk::SplitReduceLayer rl[dpk::kDlGroupMax];
       int nr = 0;
       for (int k = 0; k < g.count; ++k)
-        if (pl.ks[k] > 1 || pl.bn == 256)
-          rl[nr++] = dpk::SplitReduceLayer{ll[k].ws, pl.ks[k], ll[k].d, ll[k].p, ll[k].na, ll[k].out};
+        if (pl.ks[k] > 1 || pl.bn == 256) {
+          float* acc = accs ? accs[g.first[k]] : nullptr;
+          rl[nr++] = dpk::SplitReduceLayer{ll[k].ws, pl.ks[k], ll[k].d, ll[k].p, ll[k].na, ll[k].out, acc};
+          if (acc) acc_done[g.first[k]] = 1;
+        }
       if (e == hipSuccess && nr > 0) e = dpk::launch_split_reduce_group(st, rl, nr);
     } else {
       const int l = g.first[0];
@@ -642,6 +649,14 @@ dp_status dp_clipped_sum_noise_layers(void* stream, const dp_layer* layers, int3
     if (e != hipSuccess) return DP_ERR_HIP;
   }
   return DP_OK;
+}
+
+dp_status dp_clipped_sum_noise_layers(void* stream, const dp_layer* layers, int32_t n_layers, dp_dtype dtype,
+                                      int64_t B, const float* c, float C, float sigma, float denom, uint64_t seed,
+                                      const uint32_t* layer_ids, uint32_t step, void* workspace, size_t ws_bytes,
+                                      float* const* outs, float* const* bias_outs) {
+  return sum_layers_impl(stream, layers, n_layers, dtype, B, c, C, sigma, denom, seed, layer_ids, step, workspace,
+                         ws_bytes, outs, bias_outs, nullptr, nullptr);
 }
 
 dp_status dp_clip_factors(void* stream, const float* sqnorm, int64_t B, float C, float* c, float* norm) {
@@ -788,12 +803,14 @@ dp_status dp_clipped_sum_accumulate_layers(void* stream, const dp_layer* layers,
     if (layers[l].has_bias) bsums[l] = base + layers[l].d * layers[l].p;
     off += round256((size_t)(layers[l].d + (layers[l].has_bias ? 1 : 0)) * (size_t)layers[l].p * sizeof(float));
   }
-  s = dp_clipped_sum_noise_layers(stream, layers, n_layers, dtype, B, c, 1.0f, 0.0f, 1.0f, 0, nullptr, 0, workspace,
-                                  sum_ws, sums.data(), bsums.data());
+  // split partials that go through the grouped reduce are added to accs there
+  std::vector<char> done((size_t)n_layers, 0);
+  s = sum_layers_impl(stream, layers, n_layers, dtype, B, c, 1.0f, 0.0f, 1.0f, 0, nullptr, 0, workspace, sum_ws,
+                      sums.data(), bsums.data(), accs, done.data());
   if (s != DP_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   for (int32_t l = 0; l < n_layers; ++l) {
-    hipError_t e = dpk::launch_accumulate(st, accs[l], sums[l], layers[l].d * layers[l].p);
+    hipError_t e = done[l] ? hipSuccess : dpk::launch_accumulate(st, accs[l], sums[l], layers[l].d * layers[l].p);
     if (e == hipSuccess && layers[l].has_bias) e = dpk::launch_accumulate(st, bias_accs[l], bsums[l], layers[l].p);
     if (e != hipSuccess) return DP_ERR_HIP;
   }

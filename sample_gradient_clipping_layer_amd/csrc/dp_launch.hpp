@@ -75,16 +75,21 @@ hipError_t launch_contract_dl_group(hipStream_t st, const DlLaunchLayer* layers,
 // with the noise and the mean: the reduce kernel of the split contractions.
 hipError_t launch_split_reduce(hipStream_t st, int64_t ks, float* ws, int64_t d, int64_t p, const NoiseArgs& na,
                                float* out);
-// One layer's split partials [ks][d][p] (no bias row) and its output.
+// One layer's split partials [ks][d][p] (no bias row) and its output; with
+// acc set, the partials' sum S is added to acc instead (acc = acc + S, no
+// noise) and out is left alone.
 struct SplitReduceLayer {
   const float* ws;
   int64_t ks, d, p;
   NoiseArgs na;
   float* out;
+  float* acc;
 };
 // The split reduces of up to kDlGroupMax layers, each layer's output the same
-// as launch_split_reduce's: one launch for the layers the vectorised reduce
-// takes, a launch of their own for the others.
+// as launch_split_reduce's (for an acc layer: as launch_split_reduce with no
+// noise and a mean of 1, then launch_accumulate): one launch for the layers
+// the vectorised reduce takes, launches of their own for the others. Either
+// every layer has acc set or none.
 hipError_t launch_split_reduce_group(hipStream_t st, const SplitReduceLayer* layers, int n);
 // direct-to-LDS fp32 engine (bias row accumulated on the side, partials [ks][d + bias][p] in ws)
 bool dl32_eligible(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias);

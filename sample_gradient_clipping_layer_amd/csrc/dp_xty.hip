@@ -708,6 +708,9 @@ __global__ __launch_bounds__(256) void k_reduce_noise(const float* __restrict__ 
 // Same result as k_reduce_noise for d % 4 == 0, p % 4 == 0 and 16-byte
 // aligned ws and out: every load is a float4 and the thread keeps 4 splits x
 // 4 rows of loads in flight.
+// With ACC the block's sums are added to out (out = out + S) instead: no
+// noise, no mean.
+template <bool ACC = false>
 __device__ __forceinline__ void reduce_noise_block4(const float* __restrict__ ws, int64_t ks, int64_t p,
                                                     int64_t split_stride, int64_t q, int64_t cq, const NoiseArgs& na,
                                                     float* __restrict__ out) {
@@ -744,6 +747,19 @@ __device__ __forceinline__ void reduce_noise_block4(const float* __restrict__ ws
       s[r].z += v[r].z;
       s[r].w += v[r].w;
     }
+  }
+  if (ACC) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float4* po = reinterpret_cast<float4*>(out + (4 * q + r) * p + 4 * cq);
+      float4 a = *po;
+      a.x = a.x + s[r].x;
+      a.y = a.y + s[r].y;
+      a.z = a.z + s[r].z;
+      a.w = a.w + s[r].w;
+      *po = a;
+    }
+    return;
   }
   float o[4][4];
 #pragma unroll
@@ -800,6 +816,7 @@ struct RedGroup {
   int n;
 };
 
+template <bool ACC>
 __global__ __launch_bounds__(256) void k_reduce_noise_group(RedGroup g) {
   int k = 0;
 #pragma unroll
@@ -809,7 +826,7 @@ __global__ __launch_bounds__(256) void k_reduce_noise_group(RedGroup g) {
   const int64_t nc = L.p / 4, nw = (L.d / 4) * nc;
   const int64_t t = ((int64_t)blockIdx.x - g.blk_begin[k]) * blockDim.x + threadIdx.x;
   if (t >= nw) return;
-  reduce_noise_block4(L.ws, L.ks, L.p, L.d * L.p, t / nc, t % nc, L.na, L.out);
+  reduce_noise_block4<ACC>(L.ws, L.ks, L.p, L.d * L.p, t / nc, t % nc, L.na, ACC ? L.acc : L.out);
 }
 
 // Many splits, small output. A workgroup takes a block of 4 weight rows x 16
@@ -1100,14 +1117,18 @@ hipError_t launch_split_reduce_group(hipStream_t st, const SplitReduceLayer* lay
   if (n < 0 || n > kDlGroupMax) return hipErrorInvalidValue;
   RedGroup g{};
   int64_t blocks = 0;
+  const bool acc = n > 0 && layers[0].acc != nullptr;
   for (int l = 0; l < n; ++l) {
     const SplitReduceLayer& x = layers[l];
+    if ((x.acc != nullptr) != acc) return hipErrorInvalidValue;  // one kind of reduce per group
     const int64_t blocks_l = ((x.d / 4) * (x.p / 4) + 255) / 256;
     // layers the one-layer launch would not give to the vectorised kernel keep that launch
-    const bool vec = x.d % 4 == 0 && x.p % 4 == 0 && (reinterpret_cast<uintptr_t>(x.out) & 15) == 0 &&
+    float* const dst = x.acc ? x.acc : x.out;
+    const bool vec = x.d % 4 == 0 && x.p % 4 == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0 &&
                      (reinterpret_cast<uintptr_t>(x.ws) & 15) == 0 && !(x.ks >= 64 && (x.d / 4) * (x.p / 4) < 32768);
     if (!vec || blocks_l == 0) {
-      const hipError_t e = launch_split_reduce(st, x.ks, const_cast<float*>(x.ws), x.d, x.p, x.na, x.out);
+      hipError_t e = launch_split_reduce(st, x.ks, const_cast<float*>(x.ws), x.d, x.p, x.na, x.out);
+      if (e == hipSuccess && x.acc) e = launch_accumulate(st, x.acc, x.out, x.d * x.p);
       if (e != hipSuccess) return e;
       continue;
     }
@@ -1118,7 +1139,10 @@ hipError_t launch_split_reduce_group(hipStream_t st, const SplitReduceLayer* lay
   }
   if (g.n == 0) return hipSuccess;
   if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_reduce_noise_group, dim3((unsigned)blocks), dim3(256), 0, st, g);
+  if (acc)
+    hipLaunchKernelGGL(k_reduce_noise_group<true>, dim3((unsigned)blocks), dim3(256), 0, st, g);
+  else
+    hipLaunchKernelGGL(k_reduce_noise_group<false>, dim3((unsigned)blocks), dim3(256), 0, st, g);
   return hipGetLastError();
 }
 

@@ -157,3 +157,37 @@ def test_virtual_step_multi_layer():
         assert_noised(out.cpu().numpy(), r["out"], r["sum"], np.zeros((d, p)), "bf16", n, what=f"layer {l}")
         if hb:
             assert_noised(bout.cpu().numpy(), r["bias_out"], r["bias_sum"], np.zeros(p), "bf16", n, what="bias")
+
+
+def test_virtual_step_gpt_block_accumulates_bit_for_bit():
+    """The transformer-block layers at B = 64, T = 128 (one shared bf16
+    launch whose split partials are added to the accumulators by the reduce
+    kernel itself): after each physical batch the accumulators equal, bit for
+    bit, the previous accumulators plus that batch's multi-layer clipped sum at
+    sigma = 0, denom = 1, added in fp32."""
+    wl = W.WORKLOADS["gpt-block-t128"]
+    B = wl.B
+    rng = np.random.default_rng(21)
+    batches = []
+    for k in range(3):
+        batch = []
+        for (T, d, p) in wl.layers:
+            A = W.f32_to_bf16_bits((rng.standard_normal((B, T, d)) / np.sqrt(d)).astype(np.float32))
+            G = W.f32_to_bf16_bits((rng.standard_normal((B, T, p)) / np.sqrt(p)).astype(np.float32))
+            batch.append((upload(A, "bf16"), upload(G, "bf16")))
+        batches.append(batch)
+    cs = [rng.uniform(0.0, 1.0, B).astype(np.float32) for _ in batches]
+    accs = [torch.full((d, p), float("nan"), dtype=torch.float32, device=dev()) for (T, d, p) in wl.layers]
+    sums = [torch.empty_like(a) for a in accs]
+    prev = None
+    for k, batch in enumerate(batches):
+        dpc.dp_clipped_sum_accumulate_layers(batch, f32(cs[k]), accs, accumulate=k > 0)
+        dpc.dp_clipped_sum_noise_layers(batch, f32(cs[k]), 1.0, 0.0, 1.0, 0, 0, sums)
+        torch.cuda.synchronize()
+        got = [a.cpu().numpy() for a in accs]
+        s = [x.cpu().numpy() for x in sums]
+        want = s if prev is None else [np.add(a, b, dtype=np.float32) for a, b in zip(prev, s)]
+        for l, (x, y) in enumerate(zip(got, want)):
+            assert np.isfinite(x).all(), f"batch {k} layer {l}"
+            np.testing.assert_array_equal(x.view(np.uint32), y.view(np.uint32), err_msg=f"batch {k} layer {l}")
+        prev = got
