@@ -583,7 +583,7 @@ def main():
     roof["algorithmic_bytes_per_call"] = round(byts / ndom)
     roof["kernel"] = ("dp_ghost_norm[_layers]: k_ghost_tiles / k_ghost_wide / k_explicit_tiles / k_norm_t1"
                       if dom == "norm"
-                      else "dp_clipped_sum_noise[_layers]: k_contract_dl (+ k_reduce_noise_vec for split tiles), "
+                      else "dp_clipped_sum_noise[_layers]: k_contract_dl (+ k_reduce_noise_group / _vec for split tiles), "
                            "k_contract_dl32 / k_contract_tiles (+ k_reduce_noise[_vec|_wide] when K is split)")
     if a.implicit_conv:
         roof["kernel"] = ("dp_conv_norm: k_ghost_tiles / k_explicit_tiles on folded inputs" if dom == "norm" else

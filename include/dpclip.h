@@ -247,7 +247,7 @@ dp_status dp_clipped_sum_noise(void* stream, const void* A, const void* G, dp_dt
  * multiple of 64, d and p multiples of 8) share kernel launches of up to 8
  * layers: one tile shape and a K split per layer chosen for the set, so that
  * the work items of all of them fill the GPU together; the partial tiles of
- * split layers are added by a reduce kernel per layer after the launch, in
+ * split layers are added by one reduce launch for the group after it, in
  * split order, with the noise and the mean. Other layers
  * run one dp_clipped_sum_noise-like launch each. Results are deterministic
  * for a given set of layer shapes; the K split of a layer may differ from the
