@@ -240,6 +240,36 @@ def test_sum_layers_repeatable_bitwise():
         np.testing.assert_array_equal(x.view(np.uint32), y.view(np.uint32))
 
 
+def test_sum_layers_unaligned_outputs_bitwise():
+    """Outputs (and accumulators) only 4-byte aligned take the scalar reduce
+    for their layer while the others share the grouped one: every layer's
+    result equals, bit for bit, that of the call with 16-byte aligned
+    outputs, with noise and in the accumulating form."""
+    B, specs, dtype, _, _ = CASES["gpt-block"]
+    _, devs = _inputs(B, specs, dtype, seed=41)
+    c_np = np.random.default_rng(6).uniform(0.0, 1.0, B).astype(np.float32)
+    want, _ = _sum_layers(devs, c_np, 0.9, 1.2, float(B), 77, 2)
+    # layers 1 and 3 written at a 4-byte offset into a larger buffer
+    bufs = [torch.empty(A.shape[2] * G.shape[2] + 4, dtype=torch.float32, device=dev()) for (A, G) in devs]
+    outs = [b[1:1 + A.shape[2] * G.shape[2]].view(A.shape[2], G.shape[2]) if l % 2 else
+            b[:A.shape[2] * G.shape[2]].view(A.shape[2], G.shape[2]) for l, (b, (A, G)) in enumerate(zip(bufs, devs))]
+    assert outs[1].data_ptr() % 16 == 4
+    dpc.dp_clipped_sum_noise_layers(devs, f32(c_np), 0.9, 1.2, float(B), 77, 2, outs)
+    torch.cuda.synchronize()
+    for l, (x, y) in enumerate(zip(outs, want)):
+        np.testing.assert_array_equal(x.cpu().numpy().view(np.uint32), y.view(np.uint32), err_msg=f"layer {l}")
+    # accumulating form: acc + sum at sigma = 0, denom = 1, against fp32 adds of the plain sums
+    plain, _ = _sum_layers(devs, c_np, 1.0, 0.0, 1.0, 0, 0)
+    start = [np.random.default_rng(50 + l).standard_normal(x.shape).astype(np.float32) for l, x in enumerate(plain)]
+    for l, o in enumerate(outs):
+        o.copy_(torch.from_numpy(start[l]))
+    dpc.dp_clipped_sum_accumulate_layers(devs, f32(c_np), outs, accumulate=True)
+    torch.cuda.synchronize()
+    for l, (x, s0, s) in enumerate(zip(outs, start, plain)):
+        np.testing.assert_array_equal(x.cpu().numpy().view(np.uint32), np.add(s0, s, dtype=np.float32).view(np.uint32),
+                                      err_msg=f"accumulated layer {l}")
+
+
 def test_time_rule_on_conv_layers():
     """The time rule (DP_MODE_TIME) on the conv layer set (B = 5): the paths
     the oracle's rule picks (explicit on the four early layers), and the norm
