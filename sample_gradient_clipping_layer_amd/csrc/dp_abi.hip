@@ -276,11 +276,37 @@ size_t sum_launch_ws_bytes(const SumLaunch& g, const dp_layer* layers, dp_dtype 
   return w;
 }
 
+// Workspace of a multi-layer clipped-sum call: the split partials of the
+// shared launches take two regions in turn, each as large as the largest
+// launch's (a launch's partials stay intact while the next launch reduces
+// them on its idle CUs); a single-layer launch uses the start.
+struct SumWsLayout {
+  size_t region = 0;  // one region of the shared launches' partials
+  bool two = false;   // at least two shared launches leave partials
+  size_t total = 0;
+};
+static SumWsLayout sum_ws_layout(const std::vector<size_t>& grouped_ws, size_t single_ws) {
+  SumWsLayout o;
+  int n_part = 0;
+  for (size_t w : grouped_ws) {
+    o.region = std::max(o.region, round256(w));
+    if (w > 0) ++n_part;
+  }
+  o.two = n_part >= 2;
+  o.total = std::max(single_ws, o.two ? 2 * o.region : o.region);
+  return o;
+}
+
 size_t sum_layers_ws_bytes(const dp_layer* layers, int32_t n, dp_dtype dtype, int64_t B) {
-  size_t w = 0;
-  for (const SumLaunch& g : plan_sum_launches(layers, n, dtype, B))
-    w = std::max(w, sum_launch_ws_bytes(g, layers, dtype, B));
-  return w;
+  std::vector<size_t> grouped;
+  size_t single = 0;
+  for (const SumLaunch& g : plan_sum_launches(layers, n, dtype, B)) {
+    if (g.grouped)
+      grouped.push_back(sum_launch_ws_bytes(g, layers, dtype, B));
+    else
+      single = std::max(single, sum_launch_ws_bytes(g, layers, dtype, B));
+  }
+  return sum_ws_layout(grouped, single).total;
 }
 
 // ---- convolution layers given by their folded input
@@ -585,7 +611,8 @@ static dp_status sum_layers_impl(void* stream, const dp_layer* layers, int32_t n
   const std::vector<SumLaunch> launches = plan_sum_launches(layers, n_layers, dtype, B);
   std::vector<dpk::DlGroupPlan> gplans(launches.size());
   std::vector<dpk::ContractPlan> splans(launches.size());
-  size_t need = 0;
+  std::vector<size_t> grouped_ws;
+  size_t single_ws = 0;
   for (size_t k = 0; k < launches.size(); ++k) {
     const SumLaunch& g = launches[k];
     const dp_layer& x0 = layers[g.first[0]];
@@ -594,14 +621,16 @@ static dp_status sum_layers_impl(void* stream, const dp_layer* layers, int32_t n
       size_t w = 0;
       for (int j = 0; j < g.count; ++j)
         w += dpk::dl_layer_ws_bytes(gplans[k], j, layers[g.first[j]].d, layers[g.first[j]].p);
-      need = std::max(need, w);
+      grouped_ws.push_back(w);
     } else {
       const int hb = x0.has_bias ? 1 : 0;
       splans[k] = dpk::contract_plan(dtype, B, x0.T, x0.d, x0.p, hb);
       if (!grid_fits((uint64_t)splans[k].mt * splans[k].nt * splans[k].ks)) return DP_ERR_SHAPE;
-      need = std::max(need, contract_ws_for(splans[k], x0.d, x0.p, hb));
+      single_ws = std::max(single_ws, contract_ws_for(splans[k], x0.d, x0.p, hb));
     }
   }
+  const SumWsLayout wl = sum_ws_layout(grouped_ws, single_ws);
+  const size_t need = wl.total;
   if (need > 0) {
     if (!workspace) return DP_ERR_NULL;
     if (ws_bytes < need) return DP_ERR_WORKSPACE;
@@ -612,24 +641,40 @@ static dp_status sum_layers_impl(void* stream, const dp_layer* layers, int32_t n
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float sc = sigma * C;
   auto lid = [&](int l) { return layer_ids ? layer_ids[l] : (uint32_t)l; };
+  // The split reduce of the last shared launch, not yet issued (noise form):
+  // the next shared launch runs it on its idle CUs when it can, else it is
+  // issued on its own before the workspace region it reads is written again.
+  dpk::SplitReduceLayer pend[dpk::kDlGroupMax];
+  int npend = 0;
+  auto flush = [&]() -> hipError_t {
+    const hipError_t e = npend > 0 ? dpk::launch_split_reduce_group(st, pend, npend) : hipSuccess;
+    npend = 0;
+    return e;
+  };
+  int parts = 0;  // shared launches so far that left partials
   for (size_t k = 0; k < launches.size(); ++k) {
     const SumLaunch& g = launches[k];
     hipError_t e;
     if (g.grouped) {
       const dpk::DlGroupPlan& pl = gplans[k];
       dpk::DlLaunchLayer ll[dpk::kDlGroupMax];
+      unsigned char* base = static_cast<unsigned char*>(workspace) + (wl.two ? (size_t)(parts % 2) * wl.region : 0);
       size_t off = 0;
       for (int k = 0; k < g.count; ++k) {
         const int l = g.first[k];
         const dp_layer& x = layers[l];
         const size_t wb = dpk::dl_layer_ws_bytes(pl, k, x.d, x.p);
-        float* wsl = wb ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + off) : nullptr;
+        float* wsl = wb ? reinterpret_cast<float*>(base + off) : nullptr;
         off += wb;
         ll[k] = dpk::DlLaunchLayer{x.A, x.G, B, x.T, x.d, x.p, wsl, outs[l],
                                    dpk::make_noise_args(sc, denom, seed, lid(l), step)};
       }
-      e = dpk::launch_contract_dl_group(st, ll, g.count, c, pl);
-      // the split tiles' partials (and the 256x256 tiles') -> outputs, one launch for the group
+      bool taken = false;
+      e = dpk::launch_contract_dl_group(st, ll, g.count, c, pl, npend > 0 ? pend : nullptr, npend, &taken);
+      if (taken) npend = 0;
+      if (e == hipSuccess) e = flush();  // not taken: the pending reduce reads the other region
+      // the split tiles' partials (and the 256x256 tiles') -> outputs, one reduce launch for the
+      // group: issued now in the accumulating form, else left pending for the next launch
       dpk::SplitReduceLayer rl[dpk::kDlGroupMax];
       int nr = 0;
       for (int k = 0; k < g.count; ++k)
@@ -638,8 +683,18 @@ static dp_status sum_layers_impl(void* stream, const dp_layer* layers, int32_t n
           rl[nr++] = dpk::SplitReduceLayer{ll[k].ws, pl.ks[k], ll[k].d, ll[k].p, ll[k].na, ll[k].out, acc};
           if (acc) acc_done[g.first[k]] = 1;
         }
-      if (e == hipSuccess && nr > 0) e = dpk::launch_split_reduce_group(st, rl, nr);
+      if (nr > 0) ++parts;
+      if (e == hipSuccess && nr > 0) {
+        if (accs) {
+          e = dpk::launch_split_reduce_group(st, rl, nr);
+        } else {
+          for (int r = 0; r < nr; ++r) pend[r] = rl[r];
+          npend = nr;
+        }
+      }
     } else {
+      e = flush();  // the single-layer launch writes the start of the workspace
+      if (e != hipSuccess) return DP_ERR_HIP;
       const int l = g.first[0];
       const dp_layer& x = layers[l];
       const int hb = x.has_bias ? 1 : 0;
@@ -648,6 +703,7 @@ static dp_status sum_layers_impl(void* stream, const dp_layer* layers, int32_t n
     }
     if (e != hipSuccess) return DP_ERR_HIP;
   }
+  if (flush() != hipSuccess) return DP_ERR_HIP;
   return DP_OK;
 }
 

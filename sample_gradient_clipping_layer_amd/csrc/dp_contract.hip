@@ -42,6 +42,7 @@
 #include "dp_launch.hpp"
 #include "dp_lds.hpp"
 #include "dp_noise.hpp"
+#include "dp_reduce.hpp"
 
 #include <type_traits>
 
@@ -116,10 +117,16 @@ struct DlLayer {
   int m_fast;                 // work-item order: tile row index fastest
   NoiseArgs na;
 };
-// The layers of one launch, in dispatch order.
+// The layers of one launch, in dispatch order, and the tail work: the split
+// reduce of the previous launch of the same call, which the workgroups past
+// the work items (ids >= wgs_main) run on the CUs that the last round of
+// items leaves idle.
 struct DlGroup {
   DlLayer L[kDlGroupMax];
   int n;
+  int64_t wgs_main;
+  int64_t tail_blocks;  // 256-thread blocks of the tail reduce (0: none)
+  RedGroup tail;
 };
 
 // RATIO (one accumulator set, for wave tiles too large for two): acc holds
@@ -148,6 +155,25 @@ template <int BM, int BN, int STAGES, int NW, int KCK = kDlKC, bool RATIO = fals
 __global__ __launch_bounds__(64 * NW, 1) void k_contract_dl(const float* __restrict__ c, DlGroup g) {
   using C = DlCfg<BM, BN, STAGES, NW, KCK>;
   extern __shared__ __attribute__((aligned(1024))) unsigned char lds[];
+
+  // ---- tail workgroups: the previous launch's split reduce, two 256-thread
+  // blocks per pass, blocks strided over the tail workgroups
+  if ((int64_t)blockIdx.x >= g.wgs_main) {
+    const int64_t ntail = (int64_t)gridDim.x - g.wgs_main, e = (int64_t)blockIdx.x - g.wgs_main;
+    const int64_t half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8);
+    const int tid = threadIdx.x & 255;
+    for (int64_t vb = 2 * e + half; vb < g.tail_blocks; vb += 2 * ntail) {
+      int k = 0;
+#pragma unroll
+      for (int j = 1; j < kDlGroupMax; ++j)
+        if (j < g.tail.n && vb >= g.tail.blk_begin[j]) k = j;
+      const SplitReduceLayer R = g.tail.L[k];
+      const int64_t nc = R.p / 4, nw = (R.d / 4) * nc;
+      const int64_t t = (vb - g.tail.blk_begin[k]) * 256 + tid;
+      if (t < nw) reduce_noise_block4(R.ws, R.ks, R.p, R.d * R.p, t / nc, t % nc, R.na, R.out);
+    }
+    return;  // whole workgroup, no barrier
+  }
 
   // ---- layer and work item
   const int64_t xcd = blockIdx.x & 7;
@@ -670,6 +696,7 @@ size_t dl_layer_ws_bytes(const DlGroupPlan& g, int l, int64_t d, int64_t p) {
 // ---------------------------------------------------------------- launch
 template <int BM, int BN, int S, int KC, bool RATIO>
 static hipError_t launch_dl_t(hipStream_t st, const float* c, const DlGroup& grp, int64_t wgs) {
+  static_assert(8 * 64 == 512, "tail workgroups run two 256-thread reduce blocks");
   using C = DlCfg<BM, BN, S, 8, KC>;
   auto kern = &k_contract_dl<BM, BN, S, 8, KC, RATIO>;
   // more than 64 KB of dynamic LDS must be allowed per kernel (per call:
@@ -682,7 +709,8 @@ static hipError_t launch_dl_t(hipStream_t st, const float* c, const DlGroup& grp
 }
 
 hipError_t launch_contract_dl_group(hipStream_t st, const DlLaunchLayer* layers, int n, const float* c,
-                                    const DlGroupPlan& g) {
+                                    const DlGroupPlan& g, const SplitReduceLayer* tail, int ntail, bool* tail_taken) {
+  if (tail_taken) *tail_taken = false;
   DlGroup grp{};
   grp.n = n;
   int64_t per_sum = 0;
@@ -708,10 +736,36 @@ hipError_t launch_contract_dl_group(hipStream_t st, const DlLaunchLayer* layers,
     per_sum += L.per;
   }
   const int64_t wgs = 8 * per_sum;
-  if (wgs * 512 >= ((int64_t)1 << 32)) return hipErrorInvalidValue;  // work-items counted in 32 bits
-  if (g.bn == 256) return launch_dl_t<256, 256, kDlWideStages, kDlWideKC, true>(st, c, grp, wgs);
-  if (g.bm == 256) return launch_dl_t<256, 128, kDlStages, kDlKC, false>(st, c, grp, wgs);
-  return launch_dl_t<128, 128, kDlStages, kDlKC, false>(st, c, grp, wgs);
+  grp.wgs_main = wgs;
+  int64_t extra = 0;
+  if (tail && ntail > 0 && ntail <= kDlGroupMax && tail_taken) {
+    // the CUs of each XCD (32) that the last round of items leaves idle take the
+    // tail, when its vectorised reduce (VALU-bound: about 5 us per pass of two
+    // blocks on a CU) fits in about 80 % of that round
+    const int64_t rounds = (per_sum + kCusPerXcd - 1) / kCusPerXcd;
+    const int64_t idle = 8 * (rounds * kCusPerXcd - per_sum);
+    bool ok = idle > 0 && tail[0].acc == nullptr;
+    int64_t blocks = 0;
+    for (int k = 0; ok && k < ntail; ++k) {
+      ok = tail[k].acc == nullptr && split_reduce_vec_ok(tail[k]) && split_reduce_blocks(tail[k]) > 0;
+      grp.tail.L[k] = tail[k];
+      grp.tail.blk_begin[k] = blocks;
+      blocks += split_reduce_blocks(tail[k]);
+    }
+    const double round_s = g.seconds / (double)(rounds > 0 ? rounds : 1);
+    const double tail_s = (double)((blocks + 2 * idle - 1) / (2 * (idle > 0 ? idle : 1))) * 5.0e-6;
+    if (ok && tail_s <= 0.8 * round_s) {
+      grp.tail.n = ntail;
+      grp.tail_blocks = blocks;
+      extra = idle;
+      *tail_taken = true;
+    }
+  }
+  if ((wgs + extra) * 512 >= ((int64_t)1 << 32)) return hipErrorInvalidValue;  // work-items counted in 32 bits
+  const int64_t grid = wgs + extra;
+  if (g.bn == 256) return launch_dl_t<256, 256, kDlWideStages, kDlWideKC, true>(st, c, grp, grid);
+  if (g.bm == 256) return launch_dl_t<256, 128, kDlStages, kDlKC, false>(st, c, grp, grid);
+  return launch_dl_t<128, 128, kDlStages, kDlKC, false>(st, c, grp, grid);
 }
 
 hipError_t launch_contract_dl(hipStream_t st, const void* A, const void* G, const float* c, int64_t B, int64_t Tn,
@@ -719,7 +773,7 @@ hipError_t launch_contract_dl(hipStream_t st, const void* A, const void* G, cons
                               float* out) {
   const DlGroupPlan g = dl_single_plan(pl);
   const DlLaunchLayer x{A, G, B, Tn, d, p, ws, out, na};
-  return launch_contract_dl_group(st, &x, 1, c, g);
+  return launch_contract_dl_group(st, &x, 1, c, g, nullptr, 0, nullptr);
 }
 
 }  // namespace dpk

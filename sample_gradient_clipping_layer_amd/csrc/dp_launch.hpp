@@ -69,8 +69,13 @@ DlGroupPlan dl_group_plan(const int64_t* B, const int64_t* Tn, const int64_t* d,
 size_t dl_layer_ws_bytes(const DlGroupPlan& g, int l, int64_t d, int64_t p);
 // The one-layer group plan of a single-layer engine-1 plan.
 DlGroupPlan dl_single_plan(const ContractPlan& pl);
+struct SplitReduceLayer;
+// tail (may be null): the split reduce of the previous launch of the same
+// call (noise form, ntail layers); the launch takes it on its idle CUs when it
+// fits, and says so in *tail_taken; else the caller launches that reduce.
 hipError_t launch_contract_dl_group(hipStream_t st, const DlLaunchLayer* layers, int n, const float* c,
-                                    const DlGroupPlan& g);
+                                    const DlGroupPlan& g, const SplitReduceLayer* tail, int ntail,
+                                    bool* tail_taken);
 // The split partials [ks][d][p] a launch left in ws (no bias row) -> out,
 // with the noise and the mean: the reduce kernel of the split contractions.
 hipError_t launch_split_reduce(hipStream_t st, int64_t ks, float* ws, int64_t d, int64_t p, const NoiseArgs& na,

@@ -28,6 +28,7 @@
 #include "dp_common.hpp"
 #include "dp_launch.hpp"
 #include "dp_noise.hpp"
+#include "dp_reduce.hpp"
 
 namespace dpk {
 
@@ -703,80 +704,6 @@ __global__ __launch_bounds__(256) void k_reduce_noise(const float* __restrict__ 
   }
 }
 
-// The 4 x 4 output block (rows 4 q.., columns 4 cq..) of a split reduce: the
-// partials summed in split order per element, then the noise and the mean.
-// Same result as k_reduce_noise for d % 4 == 0, p % 4 == 0 and 16-byte
-// aligned ws and out: every load is a float4 and the thread keeps 4 splits x
-// 4 rows of loads in flight.
-// With ACC the block's sums are added to out (out = out + S) instead: no
-// noise, no mean.
-template <bool ACC = false>
-__device__ __forceinline__ void reduce_noise_block4(const float* __restrict__ ws, int64_t ks, int64_t p,
-                                                    int64_t split_stride, int64_t q, int64_t cq, const NoiseArgs& na,
-                                                    float* __restrict__ out) {
-  constexpr int U = 4;
-  const float* base = ws + 4 * q * p + 4 * cq;
-  float4 s[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) s[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-  int64_t sp = 0;
-  for (; sp + U <= ks; sp += U) {
-    float4 v[U][4];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[u][r] = *reinterpret_cast<const float4*>(base + (sp + u) * split_stride + r * p);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[r].x += v[u][r].x;
-        s[r].y += v[u][r].y;
-        s[r].z += v[u][r].z;
-        s[r].w += v[u][r].w;
-      }
-  }
-  for (; sp < ks; ++sp) {
-    float4 v[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = *reinterpret_cast<const float4*>(base + sp * split_stride + r * p);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s[r].x += v[r].x;
-      s[r].y += v[r].y;
-      s[r].z += v[r].z;
-      s[r].w += v[r].w;
-    }
-  }
-  if (ACC) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float4* po = reinterpret_cast<float4*>(out + (4 * q + r) * p + 4 * cq);
-      float4 a = *po;
-      a.x = a.x + s[r].x;
-      a.y = a.y + s[r].y;
-      a.z = a.z + s[r].z;
-      a.w = a.w + s[r].w;
-      *po = a;
-    }
-    return;
-  }
-  float o[4][4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t n = 4 * cq + k;
-    const f32x4 z = normals4((uint32_t)(q * p + n), 2u * na.layer, na.step, 0u, na.k0, na.k1);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float sv = k == 0 ? s[r].x : k == 1 ? s[r].y : k == 2 ? s[r].z : s[r].w;
-      o[r][k] = noised_mean_spec(sv, na.sc, z[r], na.inv_denom);
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    *reinterpret_cast<float4*>(out + (4 * q + r) * p + 4 * cq) = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
-}
-
 // One thread per 4 x 4 output block (reduce_noise_block4), then one per 4
 // bias columns.
 __global__ __launch_bounds__(256) void k_reduce_noise_vec(const float* __restrict__ ws, int64_t ks, int64_t d,
@@ -810,12 +737,6 @@ __global__ __launch_bounds__(256) void k_reduce_noise_vec(const float* __restric
 // The split reduces of several layers in one launch: each layer owns a
 // contiguous range of workgroups, one thread per 4 x 4 output block, with the
 // arithmetic of k_reduce_noise_vec (no bias rows).
-struct RedGroup {
-  SplitReduceLayer L[kDlGroupMax];
-  int64_t blk_begin[kDlGroupMax];
-  int n;
-};
-
 template <bool ACC>
 __global__ __launch_bounds__(256) void k_reduce_noise_group(RedGroup g) {
   int k = 0;
@@ -1121,12 +1042,9 @@ hipError_t launch_split_reduce_group(hipStream_t st, const SplitReduceLayer* lay
   for (int l = 0; l < n; ++l) {
     const SplitReduceLayer& x = layers[l];
     if ((x.acc != nullptr) != acc) return hipErrorInvalidValue;  // one kind of reduce per group
-    const int64_t blocks_l = ((x.d / 4) * (x.p / 4) + 255) / 256;
+    const int64_t blocks_l = split_reduce_blocks(x);
     // layers the one-layer launch would not give to the vectorised kernel keep that launch
-    float* const dst = x.acc ? x.acc : x.out;
-    const bool vec = x.d % 4 == 0 && x.p % 4 == 0 && (reinterpret_cast<uintptr_t>(dst) & 15) == 0 &&
-                     (reinterpret_cast<uintptr_t>(x.ws) & 15) == 0 && !(x.ks >= 64 && (x.d / 4) * (x.p / 4) < 32768);
-    if (!vec || blocks_l == 0) {
+    if (!split_reduce_vec_ok(x) || blocks_l == 0) {
       hipError_t e = launch_split_reduce(st, x.ks, const_cast<float*>(x.ws), x.d, x.p, x.na, x.out);
       if (e == hipSuccess && x.acc) e = launch_accumulate(st, x.acc, x.out, x.d * x.p);
       if (e != hipSuccess) return e;

@@ -6,8 +6,9 @@ norm, the cross-layer sum and the clip factors) and
 dp_clipped_sum_noise_layers (every layer's clipped noised mean under one c).
 At gpt-block-t128 the four layers share one ghost launch and one contraction
 launch (256 x 256 tiles with the per-sample rescale, K split, the split
-tiles' partials added by a reduce kernel per layer); at gpt2large-t1024 eight
-consecutive layers (two decoder blocks) share each launch. The oracle computes each layer's
+tiles' partials added by one reduce launch); at gpt2large-t1024 eight
+consecutive layers (two decoder blocks) share each launch, and each launch's
+split reduce runs on the next launch's idle CUs. The oracle computes each layer's
 per-example gradients in fp64 and everything from them ("Scalable and
 Efficient Training of Large CNNs with DP", eq. (2.1) and Sec. 3.2; "Scaling up
 DP Deep Learning with Fast Per-Example Gradient Clipping", clipped mean plus
@@ -110,6 +111,29 @@ def test_gpt2large_block_pair_benched_launches():
         out_or = D.noised_mean(S_or, z, wl.C, wl.sigma, B)
         assert_noised(out.cpu().numpy()[rows, cols], out_or, S_or, wl.sigma * wl.C * z / B, "bf16", B,
                       what=f"out[{l}]")
+
+
+def test_gpt2large_reduce_in_next_launch_bitwise():
+    """Six GPT-2-large decoder blocks (24 layers: three shared contraction
+    launches) in one call, where each launch's split reduce runs on the idle
+    CUs of the next launch and the last one's on its own: every layer's noised
+    mean equals, bit for bit, that of one call per block pair (whose reduce
+    runs on its own), with the same layer ids."""
+    wl = W.WORKLOADS["gpt2large-t1024"]
+    layers = [W.make_layer_device(wl, l, dev()) for l in range(24)]
+    B = wl.B
+    gen = torch.Generator(device=dev()).manual_seed(3)
+    c = torch.rand(B, device=dev(), generator=gen) * 0.8 + 0.2
+    outs = [torch.empty(A.shape[2], G.shape[2], dtype=torch.float32, device=dev()) for (A, G) in layers]
+    dpc.dp_clipped_sum_noise_layers(layers, c, 1.0, 1.0, float(B), 7, 2, outs)
+    for k in range(3):
+        ids = list(range(8 * k, 8 * k + 8))
+        ref = [torch.empty_like(outs[l]) for l in ids]
+        dpc.dp_clipped_sum_noise_layers([layers[l] for l in ids], c, 1.0, 1.0, float(B), 7, 2, ref, layer_ids=ids)
+        torch.cuda.synchronize()
+        for l, r in zip(ids, ref):
+            assert torch.equal(outs[l].view(torch.int32), r.view(torch.int32)), f"layer {l}"
+    del layers
 
 
 def test_wide_tile_extreme_clip_factors():
