@@ -13,12 +13,57 @@ namespace dpk {
 // Same result as k_reduce_noise for d % 4 == 0, p % 4 == 0 and 16-byte
 // aligned ws and out: every load is a float4 and the thread keeps 4 splits x
 // 4 rows of loads in flight.
+// The noise form for a known split count: the partials' loads are issued
+// first and the normals drawn while they are in flight; the same operations
+// as the general form.
+template <int KS>
+__device__ __forceinline__ void reduce_noise_block4_ks(const float* __restrict__ ws, int64_t p, int64_t split_stride,
+                                                       int64_t q, int64_t cq, const NoiseArgs& na,
+                                                       float* __restrict__ out) {
+  const float* base = ws + 4 * q * p + 4 * cq;
+  float4 v[KS][4];
+#pragma unroll
+  for (int u = 0; u < KS; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[u][r] = *reinterpret_cast<const float4*>(base + u * split_stride + r * p);
+  f32x4 z[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) z[k] = normals4((uint32_t)(q * p + 4 * cq + k), 2u * na.layer, na.step, 0u, na.k0, na.k1);
+  float4 s[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int u = 0; u < KS; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s[r].x += v[u][r].x;
+      s[r].y += v[u][r].y;
+      s[r].z += v[u][r].z;
+      s[r].w += v[u][r].w;
+    }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    *reinterpret_cast<float4*>(out + (4 * q + r) * p + 4 * cq) =
+        make_float4(noised_mean_spec(s[r].x, na.sc, z[0][r], na.inv_denom),
+                    noised_mean_spec(s[r].y, na.sc, z[1][r], na.inv_denom),
+                    noised_mean_spec(s[r].z, na.sc, z[2][r], na.inv_denom),
+                    noised_mean_spec(s[r].w, na.sc, z[3][r], na.inv_denom));
+}
+
 // With ACC the block's sums are added to out (out = out + S) instead: no
 // noise, no mean.
 template <bool ACC = false>
 __device__ __forceinline__ void reduce_noise_block4(const float* __restrict__ ws, int64_t ks, int64_t p,
                                                     int64_t split_stride, int64_t q, int64_t cq, const NoiseArgs& na,
                                                     float* __restrict__ out) {
+  if (!ACC && ks >= 1 && ks <= 4) {
+    switch (ks) {
+      case 1: reduce_noise_block4_ks<1>(ws, p, split_stride, q, cq, na, out); return;
+      case 2: reduce_noise_block4_ks<2>(ws, p, split_stride, q, cq, na, out); return;
+      case 3: reduce_noise_block4_ks<3>(ws, p, split_stride, q, cq, na, out); return;
+      default: reduce_noise_block4_ks<4>(ws, p, split_stride, q, cq, na, out); return;
+    }
+  }
   constexpr int U = 4;
   const float* base = ws + 4 * q * p + 4 * cq;
   float4 s[4];
