@@ -248,7 +248,10 @@ dp_status dp_clipped_sum_noise(void* stream, const void* A, const void* G, dp_dt
  * layers: one tile shape and a K split per layer chosen for the set, so that
  * the work items of all of them fill the GPU together; the partial tiles of
  * split layers are added by one reduce launch for the group after it, in
- * split order, with the noise and the mean. Other layers
+ * split order, with the noise and the mean (in a call with several shared
+ * launches, by workgroups of the next launch that run on the CUs its last
+ * round of work leaves idle; the partials of consecutive launches then take
+ * two workspace regions in turn). Other layers
  * run one dp_clipped_sum_noise-like launch each. Results are deterministic
  * for a given set of layer shapes; the K split of a layer may differ from the
  * one a single-layer call picks, which changes the fp32 rounding of the sum
