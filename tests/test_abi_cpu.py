@@ -264,6 +264,30 @@ def test_layers_workspace_follows_the_runs(lib):
     assert lib.dp_layers_workspace_bytes(_layers(GPT_BLOCK), 0, 1, B, 0, 1) == 0
 
 
+GPT2L_BLOCK = [(1024, 1280, 3840, 0), (1024, 1280, 1280, 0), (1024, 1280, 5120, 0), (1024, 5120, 1280, 0)]
+
+
+def test_sum_layers_workspace_two_regions(lib):
+    """A call with several shared contraction launches keeps each launch's
+    split partials intact while the next launch reduces them: two regions,
+    each as large as one launch's, used in turn; one launch needs one."""
+    import torch
+    B = 32
+    one = lib.dp_layers_workspace_bytes(_layers(GPT2L_BLOCK * 2), 8, 1, B, 0, 1)
+    two = lib.dp_layers_workspace_bytes(_layers(GPT2L_BLOCK * 4), 16, 1, B, 0, 1)
+    three = lib.dp_layers_workspace_bytes(_layers(GPT2L_BLOCK * 6), 24, 1, B, 0, 1)
+    assert one > 0 and one % 256 == 0
+    assert two == 2 * one
+    assert three == two
+    fn = lib.dp_clipped_sum_noise_layers
+    outs = (ctypes.c_void_p * 16)(*([FAKE] * 16))
+    call = lambda wsb: fn(None, _layers(GPT2L_BLOCK * 4), 16, 1, B, FAKE, 1.0, 1.0, float(B), 0, None, 0, FAKE, wsb,
+                          outs, None)
+    assert call(two - 256) == dpc.DP_ERR_WORKSPACE
+    if not torch.cuda.is_available():
+        assert call(two) == dpc.DP_ERR_NO_DEVICE
+
+
 def test_clipped_sum_layers_validation(lib):
     """The multi-layer clipped-sum call validates everything before any HIP
     call; its workspace need is covered by dp_layers_workspace_bytes."""
