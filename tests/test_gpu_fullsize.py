@@ -226,6 +226,51 @@ def test_graph_capture_replays_match_eager_calls():
         assert (want[1] < 1.0).any()
 
 
+def test_graph_capture_of_a_multi_launch_sum_call():
+    """A clipped-sum call of four GPT-2-large decoder blocks (two shared
+    launches: the second runs the first one's split reduce in its tail, the
+    last reduce runs on its own) captured in a HIP graph and replayed three
+    times with new inputs copied in: every replay gives the eager call's bits."""
+    wl = W.WORKLOADS["gpt2large-t1024"]
+    B = wl.B
+    static = [W.make_layer_device(wl, l, dev(), step=0) for l in range(16)]
+    gen = torch.Generator(device=dev()).manual_seed(5)
+    c = torch.rand(B, device=dev(), generator=gen) * 0.8 + 0.2
+    ws = torch.empty(dpc.dp_layers_workspace_bytes(static) + 256, dtype=torch.uint8, device=dev())
+    outs = [torch.empty(A.shape[2], G.shape[2], dtype=torch.float32, device=dev()) for (A, G) in static]
+
+    def call(layers, o, stream=None):
+        dpc.dp_clipped_sum_noise_layers(layers, c, wl.C, wl.sigma, float(B), wl.seed, 3, o, workspace=ws,
+                                        stream=stream)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up on the capture stream
+        call(static, outs, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(static, outs, stream=torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    eager_outs = [torch.empty_like(o) for o in outs]
+    for rep in range(3):
+        for l, (A, G) in enumerate(static):
+            A2, G2 = W.make_layer_device(wl, l, dev(), step=rep + 1)
+            A.copy_(A2)
+            G.copy_(G2)
+            del A2, G2
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs]
+        call(static, eager_outs)
+        torch.cuda.synchronize()
+        for l, (x, y) in enumerate(zip(got, eager_outs)):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32)), f"replay {rep}, layer {l}"
+    del static
+
+
 def test_side_stream_call_keeps_its_workspace():
     """A call on a side stream with a workspace the binding allocates, then an
     allocation on the current stream written with garbage right away: the
