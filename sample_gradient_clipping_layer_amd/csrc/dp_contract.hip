@@ -696,8 +696,8 @@ size_t dl_layer_ws_bytes(const DlGroupPlan& g, int l, int64_t d, int64_t p) {
 // ---------------------------------------------------------------- launch
 template <int BM, int BN, int S, int KC, bool RATIO>
 static hipError_t launch_dl_t(hipStream_t st, const float* c, const DlGroup& grp, int64_t wgs) {
-  static_assert(8 * 64 == 512, "tail workgroups run two 256-thread reduce blocks");
   using C = DlCfg<BM, BN, S, 8, KC>;
+  static_assert(C::NT == 512, "tail workgroups run two 256-thread reduce blocks");
   auto kern = &k_contract_dl<BM, BN, S, 8, KC, RATIO>;
   // more than 64 KB of dynamic LDS must be allowed per kernel (per call:
   // cheap, and correct whichever device is current)
@@ -744,7 +744,7 @@ hipError_t launch_contract_dl_group(hipStream_t st, const DlLaunchLayer* layers,
     // blocks on a CU) fits in about 80 % of that round
     const int64_t rounds = (per_sum + kCusPerXcd - 1) / kCusPerXcd;
     const int64_t idle = 8 * (rounds * kCusPerXcd - per_sum);
-    bool ok = idle > 0 && tail[0].acc == nullptr;
+    bool ok = idle > 0 && (wgs + idle) * 512 < ((int64_t)1 << 32);
     int64_t blocks = 0;
     for (int k = 0; ok && k < ntail; ++k) {
       ok = tail[k].acc == nullptr && split_reduce_vec_ok(tail[k]) && split_reduce_blocks(tail[k]) > 0;
