@@ -113,18 +113,27 @@ def test_gpt2large_block_pair_benched_launches():
                       what=f"out[{l}]")
 
 
-def test_gpt2large_reduce_in_next_launch_bitwise():
+@pytest.mark.parametrize("unaligned", [False, True])
+def test_gpt2large_reduce_in_next_launch_bitwise(unaligned):
     """Six GPT-2-large decoder blocks (24 layers: three shared contraction
     launches) in one call, where each launch's split reduce runs on the idle
     CUs of the next launch and the last one's on its own: every layer's noised
     mean equals, bit for bit, that of one call per block pair (whose reduce
-    runs on its own), with the same layer ids."""
+    runs on its own), with the same layer ids. With one output of the first
+    launch only 4-byte aligned, that launch's reduce cannot go to the next
+    launch (it runs on its own after it, the odd layer in the scalar reduce):
+    the same bits."""
     wl = W.WORKLOADS["gpt2large-t1024"]
     layers = [W.make_layer_device(wl, l, dev()) for l in range(24)]
     B = wl.B
     gen = torch.Generator(device=dev()).manual_seed(3)
     c = torch.rand(B, device=dev(), generator=gen) * 0.8 + 0.2
     outs = [torch.empty(A.shape[2], G.shape[2], dtype=torch.float32, device=dev()) for (A, G) in layers]
+    if unaligned:
+        d, p = outs[3].shape
+        buf = torch.empty(d * p + 4, dtype=torch.float32, device=dev())
+        outs[3] = buf[1:1 + d * p].view(d, p)
+        assert outs[3].data_ptr() % 16 == 4
     dpc.dp_clipped_sum_noise_layers(layers, c, 1.0, 1.0, float(B), 7, 2, outs)
     for k in range(3):
         ids = list(range(8 * k, 8 * k + 8))
