@@ -95,7 +95,7 @@ BREAKDOWN_STEPS = 50
 
 
 def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums=False, virtual_steps=1,
-            mode=0, implicit_conv=False):
+            mode=0, implicit_conv=False, unfold_in_step=False):
     """Times `steps` whole steps of the workload after `warmup` untimed ones.
 
     Global clipping (one norm per example over all layers): every layer's
@@ -113,7 +113,11 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
     the number of rotated input sets and whether inputs were drawn on the
     device. implicit_conv (conv workloads): the layers are given by their
     folded inputs, one dp_conv_norm per layer into the global norm, the clip
-    factors, one dp_conv_clipped_sum_noise per layer."""
+    factors, one dp_conv_clipped_sum_noise per layer. unfold_in_step (conv
+    workloads): the layers are given by their folded inputs too, and each step
+    first unfolds every one with torch (F.unfold, laid out [B, T, D]) into a
+    buffer, then runs the unfolded path on the buffers: what a caller holding
+    only folded inputs pays for the unfolded path."""
     import torch
     import sample_gradient_clipping_layer_amd as dpc
 
@@ -136,7 +140,8 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
         return torch.from_numpy(x).to(dev)
 
     geos = None
-    if implicit_conv:
+    folded = implicit_conv or unfold_in_step
+    if folded:
         geos = [dpc.conv_geometry(cin, h, w, 3, st, 1) for (cin, h, w, st) in wl.conv]
         set_bytes = sum(B * (g.C_in * g.H * g.W + T * p) * eb for g, (T, d, p) in zip(geos, shapes))
         n_sets = max(1, min(4, math.ceil(2 * CACHE_BYTES / set_bytes) + 1))
@@ -145,7 +150,7 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
     for s in range(n_sets):
         layers = []
         for l in range(len(shapes)):
-            if implicit_conv:
+            if folded:
                 fm, G = W.make_folded(wl, l, step=s)
                 layers.append((up(fm), up(G)))
                 del fm, G
@@ -156,6 +161,10 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
                 layers.append((up(A), up(G)))
                 del A, G
         sets.append(layers)
+    unf = None
+    if unfold_in_step:
+        # the unfolded inputs U(a) [B, T, D], rewritten every step
+        unf = [torch.empty(B, T, d, dtype=sets[0][l][0].dtype, device=dev) for l, (T, d, p) in enumerate(shapes)]
     torch.cuda.synchronize()
     dt = dpc.DP_BF16 if wl.dtype == "bf16" else dpc.DP_F32
     # one workspace per distinct shape (calls on one stream run one at a time)
@@ -209,8 +218,11 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
             kinds = [("norm", l) for l in range(L)] + [("clip", -1)] + [("sum", l) for l in range(L)]
         # one workspace for the multi-layer calls (they run one after another on the stream)
         ws_layers = None if implicit_conv else torch.empty(
-            max(256, dpc.dp_layers_workspace_bytes(sets[0], has_bias=wl.has_bias, mode=mode)), dtype=torch.uint8,
-            device=dev)
+            max(256, dpc.dp_layers_workspace_bytes(
+                [(unf[l], G) for l, (_, G) in enumerate(sets[0])] if unfold_in_step else sets[0],
+                has_bias=wl.has_bias, mode=mode)), dtype=torch.uint8, device=dev)
+        if unfold_in_step:
+            kinds = [("unfold", l) for l in range(L)] + kinds
         if virtual_steps > 1:
             # a logical batch of `virtual_steps` physical batches: per physical batch the norms, the
             # clip factors and each layer's clipped sum added to its accumulator; once per logical
@@ -235,6 +247,10 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
     ready = torch.cuda.Event()
     done_ev = [torch.cuda.Event() for _ in shapes]
 
+    def unfold_into(l, a):
+        cin, h, w, st = wl.conv[l]
+        unf[l].copy_(torch.nn.functional.unfold(a, 3, padding=1, stride=st).transpose(1, 2))
+
     def step(k, e=None):
         nonlocal C_t
         layers = sets[k % n_sets]
@@ -247,6 +263,12 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
             fn(*args, **kw)
             if e: e[j][1].record(stream)
             j += 1
+
+        if unfold_in_step:
+            join()  # the previous step's clipped sums still read the buffers
+            for l, (a, G) in enumerate(layers):
+                call(unfold_into, l, a)
+            layers = [(unf[l], G) for l, (a, G) in enumerate(layers)]
 
         if wl.per_layer:
             for l, (A, G) in enumerate(layers):
@@ -505,6 +527,9 @@ def main():
                          "default 3 for layer sets of at most 8 layers, else 1")
     ap.add_argument("--implicit-conv", action="store_true",
                     help="conv workloads: pass each layer's folded input (dp_conv_* calls) instead of its unfolding")
+    ap.add_argument("--unfold-in-step", action="store_true",
+                    help="conv workloads: the layers given by their folded inputs, unfolded by torch inside every "
+                         "step before the unfolded path runs (the alternative to --implicit-conv)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (HBM counter calibration)")
     ap.add_argument("--noise-fill", action="store_true",
@@ -542,9 +567,13 @@ def main():
             print("--implicit-conv applies to conv workloads, alone", file=sys.stderr)
             sys.exit(2)
         nstreams, per_layer_sums = 1, True
+    if a.unfold_in_step and (not wl.conv or a.implicit_conv or a.virtual_steps > 1):
+        print("--unfold-in-step applies to conv workloads, without --implicit-conv or --virtual-steps",
+              file=sys.stderr)
+        sys.exit(2)
     wall, gpu_ms, call_ms, shapes, kinds, n_sets, on_device, geos = run_gpu(
         wl, a.steps, a.warmup, nstreams, a.per_layer_norms, per_layer_sums, a.virtual_steps, MODES[a.path_rule],
-        a.implicit_conv)
+        a.implicit_conv, a.unfold_in_step)
     L = len(shapes)
     ms_per_step = 1e3 * wall / a.steps
     value = wl.B * a.virtual_steps * a.steps / wall
@@ -605,6 +634,8 @@ def main():
     if a.implicit_conv:
         cfg["conv_input"] = "folded [B, C_in, H, W]; unfolded rows formed in the kernels"
         cfg["norm_call"] = cfg["sum_call"] = "per-layer (dp_conv_*)"
+    if a.unfold_in_step:
+        cfg["conv_input"] = "folded [B, C_in, H, W], unfolded by torch (F.unfold to [B, T, D]) inside every step"
     if a.virtual_steps > 1:
         cfg["virtual_steps"] = a.virtual_steps
         cfg["logical_batch"] = wl.B * a.virtual_steps

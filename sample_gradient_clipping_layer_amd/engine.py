@@ -8,10 +8,13 @@ layer's input a and output gradient dL/ds during one ordinary forward and
 backward pass of the summed per-sample loss; step() then runs the library's
 path over all layers -- the per-sample norm over every layer, the clip
 factors, and each layer's clipped noised mean -- and writes the results into
-the parameters' .grad. A convolution's input is unfolded first (U(a) of the
-same page, Sec. 2.2: D = C_in * kH * kW features per output position), in
-torch, on the GPU; with conv_input="folded" the library takes the folded
-input instead and forms U(a)'s rows inside its kernels (dp_conv_* calls).
+the parameters' .grad. A convolution is taken by its folded input: the
+library forms the rows of its unfolding U(a) (same page, Sec. 2.2: D =
+C_in * kH * kW features per output position) inside its kernels (dp_conv_*
+calls); with conv_input="unfolded" torch unfolds each input on the GPU first
+and the conv layers share the multi-layer calls with the linear ones (at
+ResNet-18 shapes torch's unfold alone takes several times the whole
+clipping path).
 
 Only argument marshalling and layout changes happen here; every step of the
 clipping path runs in libdpclip.
@@ -51,14 +54,14 @@ class PrivacyEngine:
     its per-sample gradient would go unclipped.
 
     mode: the per-layer path rule ('ghost-mixed', 'ghost', 'explicit',
-    'time'). conv_input: 'unfolded' (torch unfolds each Conv2d input; the
-    layers share the multi-layer calls) or 'folded' (the library takes the
-    folded input and forms the unfolded rows in its kernels, one call per
-    Conv2d layer).
+    'time'). conv_input: 'folded' (the default: the library takes each
+    Conv2d input as it is and forms the unfolded rows in its kernels, one
+    call per Conv2d layer) or 'unfolded' (torch unfolds each Conv2d input
+    and the layers share the multi-layer calls).
     """
 
     def __init__(self, model: torch.nn.Module, C: float, sigma: float, seed: int = 0, mode: str = "ghost-mixed",
-                 kappa: int = 1, conv_input: str = "unfolded"):
+                 kappa: int = 1, conv_input: str = "folded"):
         if mode not in MODES:
             raise ValueError(f"mode must be one of {sorted(MODES)}")
         if conv_input not in ("unfolded", "folded"):
