@@ -249,7 +249,10 @@ def run_gpu(wl, steps, warmup, nstreams=1, per_layer_norms=False, per_layer_sums
 
     def unfold_into(l, a):
         cin, h, w, st = wl.conv[l]
-        unf[l].copy_(torch.nn.functional.unfold(a, 3, padding=1, stride=st).transpose(1, 2))
+        if unfold_in_step == "library":
+            dpc.dp_unfold2d(a, geos[l], out=unf[l])
+        else:
+            unf[l].copy_(torch.nn.functional.unfold(a, 3, padding=1, stride=st).transpose(1, 2))
 
     def step(k, e=None):
         nonlocal C_t
@@ -527,9 +530,10 @@ def main():
                          "default 3 for layer sets of at most 8 layers, else 1")
     ap.add_argument("--implicit-conv", action="store_true",
                     help="conv workloads: pass each layer's folded input (dp_conv_* calls) instead of its unfolding")
-    ap.add_argument("--unfold-in-step", action="store_true",
-                    help="conv workloads: the layers given by their folded inputs, unfolded by torch inside every "
-                         "step before the unfolded path runs (the alternative to --implicit-conv)")
+    ap.add_argument("--unfold-in-step", nargs="?", const="torch", default=None, choices=("torch", "library"),
+                    help="conv workloads: the layers given by their folded inputs, unfolded inside every step "
+                         "(by torch's F.unfold, or by the library's dp_unfold2d) before the unfolded path runs "
+                         "(the alternatives to --implicit-conv)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (HBM counter calibration)")
     ap.add_argument("--noise-fill", action="store_true",
@@ -635,7 +639,8 @@ def main():
         cfg["conv_input"] = "folded [B, C_in, H, W]; unfolded rows formed in the kernels"
         cfg["norm_call"] = cfg["sum_call"] = "per-layer (dp_conv_*)"
     if a.unfold_in_step:
-        cfg["conv_input"] = "folded [B, C_in, H, W], unfolded by torch (F.unfold to [B, T, D]) inside every step"
+        cfg["conv_input"] = ("folded [B, C_in, H, W], unfolded inside every step to [B, T, D] by "
+                             + ("torch's F.unfold" if a.unfold_in_step == "torch" else "the library's dp_unfold2d"))
     if a.virtual_steps > 1:
         cfg["virtual_steps"] = a.virtual_steps
         cfg["logical_batch"] = wl.B * a.virtual_steps

@@ -402,6 +402,21 @@ dp_status dp_conv_clipped_sum_noise(void* stream, const void* a, const void* G, 
                                     float denom, uint64_t seed, uint32_t layer_id, uint32_t step,
                                     void* workspace, size_t ws_bytes, float* out, float* bias_out);
 
+/*
+ * dp_unfold2d: U(a) [B, T, d] itself, written to U in the layout above (dtype
+ * of a; row t of sample b at U + (b*T + t)*d elements), for callers that run
+ * the unfolded path (dp_ghost_norm[_layers], dp_clipped_sum_noise[_layers])
+ * on a layer they hold folded, sharing launches with other layers. The
+ * conv-as-linear unfolding of SEDP Sec. 2.2, eqs. (2.5)-(2.6) (FPC Alg. 3
+ * works on the same unfolded patches). Every element is copied or set to 0:
+ * U equals torch's unfold(a).transpose(1, 2) bit for bit.
+ *
+ *  a, conv, dtype, B  as in dp_conv_norm.
+ *  U        [B, T, d] device buffer of the caller (B*T*d elements of dtype),
+ *           16-byte aligned; T*d < 2^31.
+ */
+dp_status dp_unfold2d(void* stream, const void* a, const dp_conv2d* conv, dp_dtype dtype, int64_t B, void* U);
+
 /* Workspace bytes that dp_conv_norm (with this mode and kappa) and
  * dp_conv_clipped_sum_noise need for this layer (the larger of the two).
  * Returns 0 for invalid arguments. */

@@ -34,10 +34,12 @@ The functions mirror the C ABI in ``include/dpclip.h``:
     dp_conv_clipped_sum_noise(a, G, conv, c, C, sigma, denom, seed, layer_id, step, out,
                               bias_out=None, workspace=None)
     dp_conv_workspace_bytes(conv, dtype, B, p, has_bias=False, mode=MODE_MIXED, kappa=1) -> int
+    dp_unfold2d(a, conv, out=None) -> U [B, T, d]
 
 The dp_conv_* calls take a convolution layer's folded input a [B, C_in, H, W]
 and its geometry (``conv_geometry(C_in, H, W, kernel_size, stride, padding,
-dilation)``); the unfolded rows are formed inside the kernels.
+dilation)``); the unfolded rows are formed inside the kernels. dp_unfold2d
+writes the unfolding U(a) itself, for the unfolded (multi-layer) calls.
 
 A and G are contiguous [B, T, d] / [B, T, p] tensors (float32 or bfloat16) on
 the current GPU; norm, factor and output vectors are float32. Every call also
@@ -62,7 +64,7 @@ EXPORTS = ("dp_ghost_norm", "dp_ghost_norm_layers", "dp_ghost_norm_clip_layers",
            "dp_clip_factors", "dp_clipped_sum_accumulate", "dp_noise_mean", "dp_accumulate_workspace_bytes",
            "dp_clipped_sum_accumulate_layers", "dp_layers_accumulate_workspace_bytes", "dp_clipped_sum_noise", "dp_adaptive_threshold",
            "dp_workspace_bytes", "dp_choose_path", "dp_status_string", "dp_abi_version",
-           "dp_conv_norm", "dp_conv_clipped_sum_noise", "dp_conv_workspace_bytes")
+           "dp_conv_norm", "dp_conv_clipped_sum_noise", "dp_conv_workspace_bytes", "dp_unfold2d")
 
 _lib = None
 
@@ -155,6 +157,8 @@ def _declare(lib):
     lib.dp_conv_clipped_sum_noise.restype = c_i32
     lib.dp_conv_workspace_bytes.argtypes = [cp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32]
     lib.dp_conv_workspace_bytes.restype = ctypes.c_size_t
+    lib.dp_unfold2d.argtypes = [vp, vp, cp, c_i32, c_i64, vp]
+    lib.dp_unfold2d.restype = c_i32
     lib.dp_abi_version.argtypes = []
     lib.dp_abi_version.restype = c_i32
     return lib
@@ -550,6 +554,26 @@ def dp_conv_norm(a, G, conv: DpConv2d, sqnorm, has_bias: bool = False, mode: int
                                               int(bool(has_bias)), int(mode), int(kappa), _ptr(ws), nbytes,
                                               _ptr(sqnorm), int(bool(accumulate)), ctypes.byref(path)))
     return path.value
+
+
+def dp_unfold2d(a, conv: DpConv2d, out=None, stream=None):
+    """U(a) [B, T, d] of a conv layer's folded input a [B, C_in, H, W] (torch's
+    unfold(a).transpose(1, 2) layout), written by the library into `out`
+    (allocated when None); returns it."""
+    if a.dim() != 4 or tuple(a.shape[1:]) != (conv.C_in, conv.H, conv.W):
+        raise ValueError("a [B, C_in, H, W] matching the geometry expected")
+    if not (a.is_contiguous() and a.is_cuda):
+        raise ValueError("a must be a contiguous GPU tensor")
+    T, d = conv_out_shape(conv)
+    B = int(a.shape[0])
+    if out is None:
+        import torch
+        out = torch.empty(B, T, d, dtype=a.dtype, device=a.device)
+    elif tuple(out.shape) != (B, T, d) or out.dtype != a.dtype or not (out.is_contiguous() and out.is_cuda):
+        raise ValueError(f"out must be a contiguous GPU tensor [B, T, d] = {(B, T, d)} of a's dtype")
+    _check("dp_unfold2d", lib().dp_unfold2d(_stream(stream), _ptr(a), ctypes.byref(conv), _dtype_code(a), B,
+                                            _ptr(out)))
+    return out
 
 
 def dp_conv_clipped_sum_noise(a, G, conv: DpConv2d, c, C: float, sigma: float, denom: float, seed: int,

@@ -794,6 +794,17 @@ dp_status dp_conv_norm(void* stream, const void* a, const void* G, const dp_conv
   return hip_status(e == hipSuccess ? dpk::launch_norm_finish(st, sink, B) : e);
 }
 
+dp_status dp_unfold2d(void* stream, const void* a, const dp_conv2d* conv, dp_dtype dtype, int64_t B, void* U) {
+  dpk::ConvGeo g;
+  // U stands where the conv calls take G: non-NULL and 16-byte aligned
+  dp_status s = check_conv(a, U, conv, dtype, B, 1, &g);
+  if (s != DP_OK) return s;
+  if ((int64_t)g.T * g.d >= kMaxConv || (((int64_t)g.T * g.d + 255) / 256) * B >= kMaxConv) return DP_ERR_SHAPE;
+  s = device_ready();
+  if (s != DP_OK) return s;
+  return hip_status(dpk::launch_unfold2d(static_cast<hipStream_t>(stream), dtype, g, B, U));
+}
+
 dp_status dp_conv_clipped_sum_noise(void* stream, const void* a, const void* G, const dp_conv2d* conv, dp_dtype dtype,
                                     int64_t B, int64_t p, const float* c, float C, float sigma, float denom,
                                     uint64_t seed, uint32_t layer_id, uint32_t step, void* workspace, size_t ws_bytes,

@@ -149,6 +149,8 @@ hipError_t launch_explicit(hipStream_t st, int dtype, const void* A, const void*
 // contraction kernels; G is [B, geo.T, p]. The contraction plan is tiles_plan.
 // `folded`: the plan of a folded-input convolution.
 ContractPlan tiles_plan(int dtype, int64_t B, int64_t Tn, int64_t d, int64_t p, int has_bias, bool folded);
+// U(a) [B, T, d] of a folded input a (geometry g) written to U: the unfolding of dp_conv_*.
+hipError_t launch_unfold2d(hipStream_t st, int dtype, const ConvGeo& g, int64_t B, void* U);
 hipError_t launch_ghost_conv(hipStream_t st, int dtype, const ConvGeo& geo, const void* G, int64_t B, int64_t p,
                              int has_bias, const NormSink& sink);
 hipError_t launch_explicit_conv(hipStream_t st, int dtype, const ConvGeo& geo, const void* G, int64_t B, int64_t p,

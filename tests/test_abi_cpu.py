@@ -264,6 +264,24 @@ def test_layers_workspace_follows_the_runs(lib):
     assert lib.dp_layers_workspace_bytes(_layers(GPT_BLOCK), 0, 1, B, 0, 1) == 0
 
 
+def test_unfold2d_validation(lib):
+    """dp_unfold2d checks its arguments before any HIP call: NULL pointers,
+    the dtype, geometry limits and U's 16-byte alignment."""
+    import torch
+    geo = dpc.conv_geometry(3, 8, 8, 3, 1, 1)
+    fn = lib.dp_unfold2d
+    assert fn(None, None, ctypes.byref(geo), 0, 2, FAKE) == dpc.DP_ERR_NULL
+    assert fn(None, FAKE, ctypes.byref(geo), 0, 2, None) == dpc.DP_ERR_NULL
+    assert fn(None, FAKE, None, 0, 2, FAKE) == dpc.DP_ERR_NULL
+    assert fn(None, FAKE, ctypes.byref(geo), 7, 2, FAKE) == dpc.DP_ERR_DTYPE
+    assert fn(None, FAKE, ctypes.byref(geo), 0, 2, FAKE + 4) == dpc.DP_ERR_ALIGN
+    assert fn(None, FAKE, ctypes.byref(geo), 0, 0, FAKE) == dpc.DP_ERR_SHAPE
+    bad = dpc.conv_geometry(3, 2, 2, 5, 1, 0)  # a kernel larger than the input
+    assert fn(None, FAKE, ctypes.byref(bad), 0, 2, FAKE) == dpc.DP_ERR_SHAPE
+    if not torch.cuda.is_available():
+        assert fn(None, FAKE, ctypes.byref(geo), 0, 2, FAKE) == dpc.DP_ERR_NO_DEVICE
+
+
 GPT2L_BLOCK = [(1024, 1280, 3840, 0), (1024, 1280, 1280, 0), (1024, 1280, 5120, 0), (1024, 5120, 1280, 0)]
 
 

@@ -220,3 +220,51 @@ def test_conv_calls_deterministic_and_on_a_given_stream():
     for x, y, z in zip(r0, r1, r2):
         np.testing.assert_array_equal(x, y)
         np.testing.assert_array_equal(x, z)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", sorted(GEOMS))
+def test_unfold2d_bit_exact(name, dtype):
+    """dp_unfold2d writes U(a) itself: bit for bit the oracle's fp64 unfolding
+    (every element a copy of an input element or 0) and torch's
+    unfold(a).transpose(1, 2); the unfolded calls on it give dp_conv_norm's
+    norms within the norm tolerance."""
+    geo, (U64, G64), (a, G) = _case(name, dtype)
+    U = dpc.dp_unfold2d(a, geo)
+    torch.cuda.synchronize()
+    want = U64.astype(np.float32)
+    if dtype == "bf16":
+        want = W.f32_to_bf16_bits(want).view(np.uint16)
+        got = U.view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        got = U.cpu().numpy().view(np.uint32)
+        want = want.view(np.uint32)
+    np.testing.assert_array_equal(got.reshape(want.shape), want)
+    B, cin, H, Wd, k, s, pad, dil, p = GEOMS[name]
+    ref = torch.nn.functional.unfold(a.float(), k, dilation=dil, padding=pad, stride=s).transpose(1, 2)
+    assert torch.equal(U.float(), ref)
+    sq = torch.empty(B, dtype=torch.float32, device=dev())
+    dpc.dp_ghost_norm(U, G, sq)
+    torch.cuda.synchronize()
+    assert_norms(sq.cpu().numpy(), D.layer_sqnorms(U64, G64), dtype, what=f"{name} unfolded")
+
+
+def test_unfold2d_resnet_layers_and_errors():
+    """The ResNet-18 layers of the benchmark at B = 256 (strides 1 and 2):
+    dp_unfold2d against torch's unfold, bit for bit; and the binding's checks."""
+    wl = W.WORKLOADS["resnet18-conv-t1024"]
+    for l, (cin, h, w, st) in enumerate(wl.conv):
+        fm, _ = W.make_folded(wl, l, step=0)
+        a = torch.from_numpy(fm).to(dev())
+        geo = dpc.conv_geometry(cin, h, w, 3, st, 1)
+        U = dpc.dp_unfold2d(a, geo)
+        ref = torch.nn.functional.unfold(a, 3, padding=1, stride=st).transpose(1, 2)
+        torch.cuda.synchronize()
+        assert torch.equal(U.view(torch.int32), ref.contiguous().view(torch.int32)), f"layer {l}"
+        del a, U, ref
+    a = torch.zeros(2, 3, 8, 8, device=dev())
+    geo = dpc.conv_geometry(3, 8, 8, 3, 1, 1)
+    with pytest.raises(ValueError):
+        dpc.dp_unfold2d(a, geo, out=torch.empty(2, 64, 26, device=dev()))
+    with pytest.raises(ValueError):
+        dpc.dp_unfold2d(a[:, :2].contiguous(), geo)
