@@ -8,11 +8,12 @@ layer's input a and output gradient dL/ds during one ordinary forward and
 backward pass of the summed per-sample loss; step() then runs the library's
 path over all layers -- the per-sample norm over every layer, the clip
 factors, and each layer's clipped noised mean -- and writes the results into
-the parameters' .grad. A convolution is taken by its folded input: the
-library forms the rows of its unfolding U(a) (same page, Sec. 2.2: D =
-C_in * kH * kW features per output position) inside its kernels (dp_conv_*
-calls); with conv_input="unfolded" torch unfolds each input on the GPU first
-and the conv layers share the multi-layer calls with the linear ones (at
+the parameters' .grad. A convolution's input is unfolded into U(a) (same
+page, Sec. 2.2: D = C_in * kH * kW features per output position) by the
+library (dp_unfold2d), and the conv layers share the multi-layer calls with
+the linear ones; with conv_input="folded" the library instead forms U(a)'s
+rows inside its kernels (dp_conv_* calls, one per layer; nothing unfolded is
+stored), and with conv_input="unfolded" torch unfolds each input (at
 ResNet-18 shapes torch's unfold alone takes several times the whole
 clipping path).
 
@@ -26,7 +27,7 @@ import torch.nn.functional as F
 
 from . import (DP_BF16, DP_F32, MODE_EXPLICIT, MODE_GHOST, MODE_MIXED, MODE_TIME, conv_geometry, dp_clip_factors,
                dp_clipped_sum_noise_layers, dp_conv_clipped_sum_noise, dp_conv_norm, dp_conv_workspace_bytes,
-               dp_ghost_norm_layers, dp_layers_workspace_bytes)
+               dp_ghost_norm_layers, dp_layers_workspace_bytes, dp_unfold2d)
 
 MODES = {"ghost-mixed": MODE_MIXED, "ghost": MODE_GHOST, "explicit": MODE_EXPLICIT, "time": MODE_TIME}
 
@@ -54,19 +55,21 @@ class PrivacyEngine:
     its per-sample gradient would go unclipped.
 
     mode: the per-layer path rule ('ghost-mixed', 'ghost', 'explicit',
-    'time'). conv_input: 'folded' (the default: the library takes each
-    Conv2d input as it is and forms the unfolded rows in its kernels, one
-    call per Conv2d layer) or 'unfolded' (torch unfolds each Conv2d input
-    and the layers share the multi-layer calls).
+    'time'). conv_input: 'library-unfold' (the default: the library writes
+    each Conv2d input's unfolding, and the layers share the multi-layer
+    calls), 'folded' (the library takes each Conv2d input as it is and forms
+    the unfolded rows in its kernels, one call per Conv2d layer; no unfolded
+    copy in memory) or 'unfolded' (torch unfolds each Conv2d input).
     """
 
     def __init__(self, model: torch.nn.Module, C: float, sigma: float, seed: int = 0, mode: str = "ghost-mixed",
-                 kappa: int = 1, conv_input: str = "folded"):
+                 kappa: int = 1, conv_input: str = "library-unfold"):
         if mode not in MODES:
             raise ValueError(f"mode must be one of {sorted(MODES)}")
-        if conv_input not in ("unfolded", "folded"):
-            raise ValueError("conv_input must be 'unfolded' or 'folded'")
+        if conv_input not in ("library-unfold", "unfolded", "folded"):
+            raise ValueError("conv_input must be 'library-unfold', 'unfolded' or 'folded'")
         self.folded = conv_input == "folded"
+        self.library_unfold = conv_input == "library-unfold"
         self.C, self.sigma, self.seed = float(C), float(sigma), int(seed)
         self.mode, self.kappa = MODES[mode], int(kappa)
         self.layers: list[_Layer] = []
@@ -138,6 +141,11 @@ class PrivacyEngine:
                                 m.dilation)
             G = g.reshape(B, g.shape[1], -1).transpose(1, 2)
             return a.to(dt).contiguous(), G.to(dt).contiguous(), geo
+        elif self.library_unfold:
+            geo = conv_geometry(a.shape[1], a.shape[2], a.shape[3], m.kernel_size, m.stride, self._padding(m),
+                                m.dilation)
+            A = dp_unfold2d(a.to(dt).contiguous(), geo)  # [B, T, D], written by the library
+            G = g.reshape(B, g.shape[1], -1).transpose(1, 2)
         else:
             U = F.unfold(a, m.kernel_size, dilation=m.dilation, padding=self._padding(m), stride=m.stride)  # [B, D, L]
             A = U.transpose(1, 2)

@@ -66,7 +66,8 @@ def _reference(model, x, y, C, scale_grad_of=None):
     return dict(zip(names, mean)), norms
 
 
-@pytest.mark.parametrize("kind", ["mlp-sequence", "conv", "conv-folded", "dilated", "dilated-folded-time"])
+@pytest.mark.parametrize("kind", ["mlp-sequence", "conv", "conv-folded", "conv-torch", "dilated", "dilated-folded-time",
+                                  "dilated-torch"])
 def test_engine_matches_per_example_backprop(kind):
     dev = torch.device("cuda", 0)
     g = torch.Generator().manual_seed(5)
@@ -88,7 +89,8 @@ def test_engine_matches_per_example_backprop(kind):
     ref, norms = _reference(model, x, y, C)
     model = model.to(dev)
     engine = PrivacyEngine(model, C=C, sigma=0.0, seed=9, mode="time" if kind.endswith("time") else "ghost-mixed",
-                           conv_input="folded" if "folded" in kind else "unfolded")
+                           conv_input=("folded" if "folded" in kind else "unfolded" if "torch" in kind
+                                       else "library-unfold"))
     _per_sample_loss(model(x.to(dev)), y.to(dev)).sum().backward()
     n_gpu = engine.step(0)
     np.testing.assert_allclose(n_gpu.cpu().numpy(), norms.numpy(), rtol=1e-4)
@@ -125,13 +127,14 @@ def test_engine_noise_matches_the_stream():
 
 
 def test_engine_folded_conv_noise_matches_unfolded():
-    """Folded and unfolded conv inputs give the same noise (each layer's
-    stream is its index in the engine) and the same clipped means."""
+    """Folded and unfolded (by torch or the library) conv inputs give the
+    same noise (each layer's stream is its index in the engine) and the same
+    clipped means; the two unfoldings give the same bits."""
     dev = torch.device("cuda", 0)
     g = torch.Generator().manual_seed(8)
     x, y = torch.randn(6, 3, 8, 8, generator=g), torch.randn(6, 3, generator=g)
     grads = {}
-    for conv_input in ("unfolded", "folded"):
+    for conv_input in ("unfolded", "folded", "library-unfold"):
         model = _ConvNet(4).to(dev)
         engine = PrivacyEngine(model, C=3.0, sigma=1.5, seed=33, conv_input=conv_input)
         _per_sample_loss(model(x.to(dev)), y.to(dev)).sum().backward()
@@ -140,3 +143,4 @@ def test_engine_folded_conv_noise_matches_unfolded():
         engine.detach()
     for n, want in grads["unfolded"].items():
         np.testing.assert_allclose(grads["folded"][n], want, rtol=1e-4, atol=1e-5 * np.abs(want).max(), err_msg=n)
+        np.testing.assert_array_equal(grads["library-unfold"][n], want, err_msg=n)
