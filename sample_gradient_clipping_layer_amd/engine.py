@@ -27,7 +27,7 @@ import torch.nn.functional as F
 
 from . import (DP_BF16, DP_F32, MODE_EXPLICIT, MODE_GHOST, MODE_MIXED, MODE_TIME, conv_geometry, dp_clip_factors,
                dp_clipped_sum_noise_layers, dp_conv_clipped_sum_noise, dp_conv_norm, dp_conv_workspace_bytes,
-               dp_ghost_norm_layers, dp_layers_workspace_bytes, dp_unfold2d)
+               dp_ghost_norm_clip_layers, dp_ghost_norm_layers, dp_layers_workspace_bytes, dp_unfold2d)
 
 MODES = {"ghost-mixed": MODE_MIXED, "ghost": MODE_GHOST, "explicit": MODE_EXPLICIT, "time": MODE_TIME}
 
@@ -169,12 +169,18 @@ class PrivacyEngine:
         dense = [k for k, op in enumerate(ops) if len(op) == 2]   # [B, T, d] operands: multi-layer calls
         folded = [k for k, op in enumerate(ops) if len(op) == 3]  # folded conv inputs: dp_conv_* calls
         sq = torch.empty(B, dtype=torch.float32, device=dev)
+        c = torch.empty(B, dtype=torch.float32, device=dev)
+        norms = torch.empty(B, dtype=torch.float32, device=dev)
         ws = None
         if dense:
             dops, dhb = [ops[k] for k in dense], [has_bias[k] for k in dense]
             ws = torch.empty(max(256, dp_layers_workspace_bytes(dops, has_bias=dhb, mode=self.mode,
                                                                 kappa=self.kappa)), dtype=torch.uint8, device=dev)
-            dp_ghost_norm_layers(dops, sq, has_bias=dhb, mode=self.mode, kappa=self.kappa, workspace=ws)
+            if folded:
+                dp_ghost_norm_layers(dops, sq, has_bias=dhb, mode=self.mode, kappa=self.kappa, workspace=ws)
+            else:  # every layer in this call: its kernels form the clip factors too (the same bits)
+                dp_ghost_norm_clip_layers(dops, sq, self.C, c, norms, has_bias=dhb, mode=self.mode,
+                                          kappa=self.kappa, workspace=ws)
         wsc = {}
         for k in folded:
             a, G, geo = ops[k]
@@ -182,9 +188,8 @@ class PrivacyEngine:
                                                                   self.kappa)), dtype=torch.uint8, device=dev)
             dp_conv_norm(a, G, geo, sq, has_bias=has_bias[k], mode=self.mode, kappa=self.kappa,
                          accumulate=bool(dense) or k != folded[0], workspace=wsc[k])
-        c = torch.empty(B, dtype=torch.float32, device=dev)
-        norms = torch.empty(B, dtype=torch.float32, device=dev)
-        dp_clip_factors(sq, self.C, c, norms)
+        if folded:
+            dp_clip_factors(sq, self.C, c, norms)
         d_of = [op[2].C_in * op[2].kh * op[2].kw if len(op) == 3 else op[0].shape[2] for op in ops]
         outs = [torch.empty(d_of[k], op[1].shape[2], dtype=torch.float32, device=dev) for k, op in enumerate(ops)]
         bouts = [torch.empty(op[1].shape[2], dtype=torch.float32, device=dev) if hb else None
